@@ -1,0 +1,13 @@
+"""CPU oracle for the OneTrans block stack (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package. The product path (the HIP library and its
+Python binding) never imports, calls or links anything here.
+"""
+
+from .onetrans_oracle import (rms_norm, layer_norm, norm, gelu, weight_group, block_forward,
+                              forward, forward_batch, prefill_user, score_candidate,
+                              append_events, BlockTrace)
+
+__all__ = ["rms_norm", "layer_norm", "norm", "gelu", "weight_group", "block_forward", "forward",
+           "forward_batch", "prefill_user", "score_candidate", "append_events", "BlockTrace"]

@@ -1,0 +1,318 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix (no GPU).
+
+Each test names the property it checks and where it comes from; the oracle is
+only trusted because these hold.
+"""
+
+import math
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle as O
+import synth
+from oracle_refs import gelu_scalar, torch_encoder_layer_stack, torch_functional_forward
+
+TINY = synth.workload("tiny")
+T3 = synth.test_workload("tiny3_fwd")
+
+
+def _rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.sqrt(np.mean(b * b)), 1e-300))
+
+
+def _shared_weights(ws):
+    """Every NS parameter set replaced by the shared S set (W_NS,j = W_S)."""
+    out = []
+    for p in ws:
+        q = p.copy()
+        for f in ("wq", "wk", "wv", "wo", "w1", "b1", "w2", "b2"):
+            a = getattr(q, f)
+            a[1:] = a[0]
+        out.append(q)
+    return out
+
+
+# --- elementary pieces against library routines ------------------------------------------------
+
+def test_norms_and_gelu_match_torch():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((7, 64)) * 3 + 0.5
+    g = 1 + 0.1 * rng.standard_normal(64)
+    b = 0.1 * rng.standard_normal(64)
+    t = torch.as_tensor
+    assert _rel(O.rms_norm(x, g, 1e-6), F.rms_norm(t(x), (64,), weight=t(g), eps=1e-6).numpy()) < 1e-14
+    assert _rel(O.layer_norm(x, g, b, 1e-5),
+                F.layer_norm(t(x), (64,), weight=t(g), bias=t(b), eps=1e-5).numpy()) < 1e-14
+    z = np.linspace(-6, 6, 1001)
+    assert _rel(O.gelu(z), F.gelu(t(z), approximate="none").numpy()) < 1e-15
+    # GELU special values: phi(0) = 0, phi(x) -> x for large x, phi(-x) -> 0
+    assert O.gelu(np.array([0.0]))[0] == 0.0
+    assert abs(O.gelu(np.array([10.0]))[0] - 10.0) < 1e-12
+    assert abs(O.gelu(np.array([-10.0]))[0]) < 1e-12
+
+
+def test_weight_group_indexing():
+    # [en] 7.5.1: rows 0..L_S-1 share set 0; NS token j (row L_S + j) owns set 1 + j.
+    assert [O.weight_group(t, 5) for t in range(8)] == [0, 0, 0, 0, 0, 1, 2, 3]
+
+
+# --- P5: reduction to a textbook pre-norm causal Transformer ----------------------------------
+
+def test_textbook_reduction_torch_encoder_layer():
+    """W_NS,j = W_S and no pyramid: the stack is torch's own pre-LN causal encoder layer."""
+    m = TINY.model
+    ws = _shared_weights(synth.make_weights(m))
+    for b in range(3):
+        x0 = synth.forward_sample(TINY, b)
+        got = O.forward(x0, ws, m, TINY.s_queries)
+        ref = torch_encoder_layer_stack(x0, ws, m)
+        assert _rel(got, ref) < 1e-12
+
+
+def test_textbook_reduction_multiblock_layernorm():
+    m = replace(T3.model, norm="layer", norm_eps=1e-5)
+    w = replace(T3, model=m, s_queries=(32, 32, 32))
+    ws = _shared_weights(synth.make_weights(m))
+    x0 = synth.forward_sample(w, 0)
+    assert _rel(O.forward(x0, ws, m, w.s_queries), torch_encoder_layer_stack(x0, ws, m)) < 1e-12
+
+
+@pytest.mark.parametrize("norm_kind", ["rms", "layer"])
+def test_mixed_stack_matches_torch_functional(norm_kind):
+    """Distinct NS parameter sets, pyramid 32 -> 20 -> 8: library attention with a bottom-right mask."""
+    m = replace(T3.model, norm=norm_kind)
+    w = replace(T3, model=m)
+    ws = synth.make_weights(m)
+    for b in range(2):
+        x0 = synth.forward_sample(w, b)
+        got = O.forward(x0, ws, m, w.s_queries)
+        ref = torch_functional_forward(x0, ws, m, w.s_queries)
+        assert got.shape == (w.s_queries[-1] + m.l_ns, m.d_model)
+        assert _rel(got, ref) < 1e-12
+
+
+# --- P1: S rows never see NS rows ------------------------------------------------------------
+
+def test_s_rows_invariant_to_ns_inputs_and_weights():
+    m = T3.model
+    w = replace(T3, s_queries=(32, 32, 32))
+    ws = synth.make_weights(m)
+    x0 = synth.forward_sample(w, 0)
+    base = O.forward(x0, ws, m, w.s_queries)
+    rng = np.random.default_rng(5)
+    x1 = x0.copy()
+    x1[w.l_s:] = rng.standard_normal(x1[w.l_s:].shape).astype(np.float32)
+    ws1 = [p.copy() for p in ws]
+    for p in ws1:
+        for f in ("wq", "wk", "wv", "wo", "w1", "b1", "w2", "b2"):
+            a = getattr(p, f)
+            a[1:] = rng.standard_normal(a[1:].shape).astype(np.float32) * 0.05
+    pert = O.forward(x1, ws1, m, w.s_queries)
+    np.testing.assert_array_equal(pert[: w.l_s], base[: w.l_s])
+    assert np.max(np.abs(pert[w.l_s:] - base[w.l_s:])) > 1e-3     # NS rows do change
+
+
+# --- P2: pyramid tail equality per block ------------------------------------------------------
+
+def test_pyramid_tail_equals_full_query_block():
+    m = T3.model
+    ws = synth.make_weights(m)
+    x0 = synth.forward_sample(T3, 1)
+    s = T3.l_s
+    for q in (32, 20, 8, 1):
+        tail = O.block_forward(x0, s, q, ws[0], m)
+        full = O.block_forward(x0, s, s, ws[0], m)
+        assert tail.shape[0] == q + m.l_ns
+        assert _rel(tail, full[s - q:]) < 1e-13
+
+
+# --- P3: two-stage serving equals the monolithic forward ---------------------------------------
+
+def test_two_stage_equals_forward():
+    w = synth.test_workload("tiny3_two_stage")
+    m = w.model
+    ws = synth.make_weights(m)
+    for u in range(w.n_users):
+        xs = synth.user_sequence(w, u)
+        cache, s_out = O.prefill_user(xs, ws, m, w.s_queries)
+        assert [c["k"].shape[0] for c in cache] == [32, 32, 20]
+        for c in range(w.n_cand):
+            xn = synth.candidate_tokens(w, u, c)
+            mono = O.forward(np.concatenate([xs, xn]), ws, m, w.s_queries)
+            assert _rel(O.score_candidate(cache, xn, ws, m), mono[-m.l_ns:]) < 1e-12
+            assert _rel(s_out, mono[: -m.l_ns]) < 1e-12
+
+
+# --- P4: cross-request append equals full recompute ---------------------------------------------
+
+def test_append_equals_recompute():
+    w = synth.test_workload("tiny3_append")
+    m = w.model
+    ws = synth.make_weights(m)
+    for u in range(w.n_users):
+        old, new = synth.append_rows(w, u)
+        full_cache, full_out = O.prefill_user(np.concatenate([old, new]), ws, m, w.s_queries)
+        old_cache, _ = O.prefill_user(old, ws, m, (w.l_old,) * m.n_blocks)
+        new_cache, new_out = O.append_events(old_cache, new, ws, m)
+        for a, b in zip(new_cache, full_cache):
+            assert _rel(a["k"], b["k"]) < 1e-12 and _rel(a["v"], b["v"]) < 1e-12
+        assert _rel(new_out, full_out[w.l_old:]) < 1e-12
+        xn = synth.candidate_tokens(w, u, 0)
+        assert _rel(O.score_candidate(new_cache, xn, ws, m), O.score_candidate(full_cache, xn, ws, m)) < 1e-12
+
+
+def test_append_refuses_pyramided_cache():
+    w = synth.test_workload("tiny3_two_stage")
+    ws = synth.make_weights(w.model)
+    cache, _ = O.prefill_user(synth.user_sequence(w, 0), ws, w.model, w.s_queries)
+    with pytest.raises(ValueError):
+        O.append_events(cache, np.zeros((2, w.model.d_model), np.float32), ws, w.model)
+
+
+# --- P6 / P7: closed forms of the mask ---------------------------------------------------------
+
+def test_equal_scores_give_mean_of_visible_values():
+    """W^K = 0 makes every score equal, so each query returns the mean of the V rows it may see.
+    This fixes the visible key count of every query: causal S, NS behind all S, pyramid tail."""
+    m = T3.model
+    ws = synth.make_weights(m)
+    for p in ws:
+        p.wk[:] = 0
+    x0 = synth.forward_sample(T3, 2)
+    traces = []
+    O.forward(x0, ws, m, T3.s_queries, traces)
+    s = T3.l_s
+    for n, tr in enumerate(traces):
+        q = T3.s_queries[n]
+        csum = np.cumsum(tr.v, axis=0) / np.arange(1, tr.v.shape[0] + 1)[:, None]
+        assert _rel(tr.o, csum[s - q:]) < 1e-13
+        s = q
+
+
+def test_single_token_attention_returns_value():
+    m = replace(T3.model, l_ns=0, n_blocks=1)
+    ws = synth.make_weights(m)
+    x = np.random.default_rng(1).standard_normal((1, m.d_model)).astype(np.float32)
+    traces = []
+    O.forward(x, ws, m, (1,), traces)
+    assert _rel(traces[0].o, traces[0].v) < 1e-15
+
+
+# --- mixed-parameter indexing through the pyramid: closed form --------------------------------
+
+def test_mixed_indexing_closed_form():
+    """W^V = 0 and W^1 = 0: the attention adds nothing and the FFN adds W2_g phi(b1_g) + b2_g.
+
+    So each output row equals its input row plus, for every block, the term of the
+    parameter set it belongs to: set 0 for S rows, set 1 + j for NS token j. The
+    expectation is computed with scalar erf, independent of the oracle's code.
+    """
+    m = T3.model
+    ws = synth.make_weights(m)
+    for p in ws:
+        p.wv[:] = 0
+        p.w1[:] = 0
+    x0 = synth.forward_sample(T3, 3).astype(np.float64)
+    out = O.forward(x0, ws, m, T3.s_queries)
+    expect = x0[T3.l_s - T3.s_queries[-1]:].copy()
+    for p in ws:
+        for r in range(expect.shape[0]):
+            g = 0 if r < T3.s_queries[-1] else 1 + (r - T3.s_queries[-1])
+            ph = np.array([gelu_scalar(float(z)) for z in p.b1[g]])
+            expect[r] += np.asarray(p.w2[g], np.float64) @ ph + p.b2[g]
+    assert _rel(out, expect) < 1e-13
+
+
+# --- P8: brute force with scalar loops on a tiny block ----------------------------------------
+
+def _brute_block(x, s, q_keep, p, m):
+    p = p.__class__(**{f: np.asarray(getattr(p, f), np.float64).tolist() for f in p.FIELDS})
+    T, d = len(x), len(x[0])
+    H = m.n_heads
+    dh = d // H
+
+    def grp(t):
+        return 0 if t < s else 1 + t - s
+
+    def nrm(row, g, b):
+        ms = sum(v * v for v in row) / d
+        return [row[i] / math.sqrt(ms + m.norm_eps) * g[i] for i in range(d)]
+
+    def mv(W, vec, bias=None):
+        return [sum(W[o][i] * vec[i] for i in range(len(vec))) + (bias[o] if bias is not None else 0.0)
+                for o in range(len(W))]
+
+    xh = [nrm(x[t], p.norm1_g, p.norm1_b) for t in range(T)]
+    K = [mv(p.wk[grp(t)], xh[t]) for t in range(T)]
+    V = [mv(p.wv[grp(t)], xh[t]) for t in range(T)]
+    out = []
+    for t in range(s - q_keep, T):
+        qv = mv(p.wq[grp(t)], xh[t])
+        o = [0.0] * d
+        for h in range(H):
+            sc = [sum(qv[h * dh + c] * K[u][h * dh + c] for c in range(dh)) / math.sqrt(dh)
+                  for u in range(t + 1)]
+            mx = max(sc)
+            e = [math.exp(z - mx) for z in sc]
+            z = sum(e)
+            for c in range(dh):
+                o[h * dh + c] = sum(e[u] * V[u][h * dh + c] for u in range(t + 1)) / z
+        y = [x[t][i] + v for i, v in enumerate(mv(p.wo[grp(t)], o))]
+        yh = nrm(y, p.norm2_g, p.norm2_b)
+        hid = [gelu_scalar(v) for v in mv(p.w1[grp(t)], yh, p.b1[grp(t)])]
+        out.append([y[i] + v for i, v in enumerate(mv(p.w2[grp(t)], hid, p.b2[grp(t)]))])
+    return out
+
+
+def test_brute_force_scalar_block():
+    m = replace(T3.model, d_model=8, n_heads=2, d_ff=16, l_ns=2, n_blocks=1)
+    ws = synth.make_weights(m)
+    x = np.random.default_rng(3).standard_normal((6, 8))
+    got = O.block_forward(x, 4, 2, ws[0], m)
+    ref = _brute_block(x.tolist(), 4, 2, ws[0], m)
+    assert _rel(got, ref) < 1e-13
+
+
+# --- P9: samples are independent ---------------------------------------------------------------
+
+def test_batch_independence_and_permutation():
+    m = TINY.model
+    ws = synth.make_weights(m)
+    x = synth.forward_batch(TINY, [0, 1, 2, 3])
+    out = O.forward_batch(x, ws, m, TINY.s_queries)
+    perm = [2, 0, 3, 1]
+    out_p = O.forward_batch(x[perm], ws, m, TINY.s_queries)
+    np.testing.assert_array_equal(out_p, out[perm])
+
+
+# --- generator sanity (inputs only) ------------------------------------------------------------
+
+def test_generators_are_seeded_and_regenerable():
+    w = synth.workload("onetrans_s")
+    a = synth.forward_sample(w, 7)
+    b = synth.forward_batch(w, [6, 7])[1]
+    np.testing.assert_array_equal(a, b)
+    # bf16 storage: every value is a bf16 number
+    assert np.all((a.view(np.uint32) & 0xFFFF) == 0)
+    # [SEP] rows are shared across samples
+    c = synth.forward_sample(w, 8)
+    for r in w.sep_rows:
+        np.testing.assert_array_equal(a[r], c[r])
+    assert w.sep_rows == (187, 388, 1189) and w.l_s == 1190
+
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, -2.5, 3.0e-3], np.float32)
+    r = synth.round_bf16(x)
+    assert r[0] == 1.0
+    assert r[1] == 1.0                       # halfway, even mantissa kept
+    assert r[2] == 1.0 + 4 * 2 ** -8         # halfway, rounds up to even
+    assert r[3] == 1.0
+    assert r[4] == -2.5
+    assert abs(r[5] - 3.0e-3) <= 3.0e-3 * 2 ** -8

@@ -1,0 +1,106 @@
+"""Algorithmic work of the OneTrans hot path (host-side arithmetic only, no device code).
+
+FLOPs count 2 per useful multiply-add of the projections and the FFN, and 4 * d
+per *visible* (query, key) pair of the causal attention (2 * d_head for Q.K and
+2 * d_head for P.V, summed over the heads). Masked pairs, exponentials and norms
+are not counted.
+
+The complexity statements follow fun-rec-mdbook (English) chapter 7.5:
+section 7.5.2 (the Pyramid Stack takes attention from O(L^2 d) to O(L L' d) and the
+FFN from O(L d^2) to O(L' d^2)) and section 7.5.3 (KV caching takes per-request
+sequence work from O(C L_S) to O(L_S + C L_NS), and cross-request append from
+O(L_S) to O(dL_S)). The worked problems 7.5.3 and 7.5.4 of the Chinese edition
+print numeric answers for two of these estimates; ``pyramid_attention_ratio``
+and ``kv_cache_saving`` reproduce them.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Sequence, Tuple
+
+
+@dataclass
+class Work:
+    gemm: float = 0.0        # projection + FFN flops
+    attn: float = 0.0        # attention flops (visible pairs only)
+
+    @property
+    def total(self) -> float:
+        return self.gemm + self.attn
+
+    def __add__(self, o: "Work") -> "Work":
+        return Work(self.gemm + o.gemm, self.attn + o.attn)
+
+    def scale(self, k: float) -> "Work":
+        return Work(self.gemm * k, self.attn * k)
+
+
+def visible_pairs(first_query_pos: int, n_queries: int) -> int:
+    """Visible (query, key) pairs when queries sit at consecutive positions p0..p0+R-1 and
+    each sees keys 0..p (key position <= query position)."""
+    p0, r = first_query_pos, n_queries
+    return r * (p0 + 1) + r * (r - 1) // 2
+
+
+def block_work(d: int, d_ff: int, kv_rows: int, q_rows: int, first_query_pos: int) -> Work:
+    """One block: K/V for ``kv_rows`` rows, Q / W^O / FFN for ``q_rows`` tail rows."""
+    gemm = 2.0 * d * d * (2 * kv_rows + 2 * q_rows) + 2.0 * 2 * d * d_ff * q_rows
+    attn = 4.0 * d * visible_pairs(first_query_pos, q_rows)
+    return Work(gemm, attn)
+
+
+def forward_work(d: int, d_ff: int, l_ns: int, l_s: int, s_queries: Sequence[int]) -> Work:
+    """Per candidate (one sample) of the monolithic forward over [S; NS]."""
+    w, s = Work(), l_s
+    for q in s_queries:
+        w = w + block_work(d, d_ff, s + l_ns, q + l_ns, s - q)
+        s = q
+    return w
+
+
+def prefill_work(d: int, d_ff: int, l_s: int, s_queries: Sequence[int]) -> Work:
+    """Stage I per user: S rows only."""
+    w, s = Work(), l_s
+    for q in s_queries:
+        w = w + block_work(d, d_ff, s, q, s - q)
+        s = q
+    return w
+
+
+def score_work(d: int, d_ff: int, l_ns: int, l_s: int, s_queries: Sequence[int]) -> Work:
+    """Stage II per candidate: NS rows against the cached S keys of every block."""
+    w, s = Work(), l_s
+    for q in s_queries:
+        w = w + block_work(d, d_ff, l_ns, l_ns, s)
+        s = q
+    return w
+
+
+def append_work(d: int, d_ff: int, n_blocks: int, l_old: int, d_l: int) -> Work:
+    """Cross-request append per user (unpyramided): only the d_l new rows per block."""
+    return block_work(d, d_ff, d_l, d_l, l_old).scale(n_blocks)
+
+
+# --- the pages' order-of-magnitude estimates -------------------------------------------------
+
+def pyramid_attention_ratio(query_fractions: Sequence[float]) -> float:
+    """Worked problem 7.5.3: attention of a pyramid whose layer k keeps L * f_k queries
+    against a fixed full-length K/V, relative to the same number of full layers.
+
+    Cost of layer k ~ L * (L f_k); standard ~ L * L per layer."""
+    return sum(query_fractions) / len(query_fractions)
+
+
+def kv_cache_saving(n_cand: int, l_s: int, l_ns: int) -> Tuple[int, int, float]:
+    """Worked problem 7.5.4: (per-candidate sequence work C*L_S, cached work L_S + C*L_NS, ratio)."""
+    plain = n_cand * l_s
+    cached = l_s + n_cand * l_ns
+    return plain, cached, plain / cached
+
+
+def mixed_param_count(d: int, d_ff: int, l_ns: int, with_wo: bool = True) -> int:
+    """Parameters of one block under mixed parameterization: one S set plus one set per NS token,
+    O(L_NS d^2 + d^2) ([en] 7.5.1, comparison with a per-token FFN)."""
+    per_set = (4 if with_wo else 3) * d * d + 2 * d * d_ff + d_ff + d
+    return (1 + l_ns) * per_set
