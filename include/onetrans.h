@@ -1,0 +1,158 @@
+/*
+ * onetrans.h — C ABI of the MI355X (gfx950) OneTrans hot path.
+ *
+ * The method (fun-rec-mdbook, chapter 7.5 "OneTrans: Unifying Sequence Modeling and Feature
+ * Interaction"; paper-daily deep reading of the OneTrans paper, section 2):
+ *   X(0) = [S-tokens; NS-tokens], S rows first (section 7.5.0, equation for X(0));
+ *   each block is a pre-norm causal Transformer block whose Q/K/V/O and FFN parameters are
+ *   mixed: all S rows share one set, NS token j owns set 1 + j (section 7.5.1, conditional
+ *   parameterization and Mixed FFN);
+ *   the Pyramid Stack keeps only the tail S rows as queries (keys/values span all rows of the
+ *   block) and the block output keeps only those rows (section 7.5.2);
+ *   serving splits into Stage I (S side once per user, K/V cached per block) and Stage II
+ *   (NS rows per candidate against the cache), and an append-only user sequence extends the
+ *   cache by the new rows only (section 7.5.3).
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer is a DEVICE pointer unless marked "host". Device pointers must be 16-byte
+ *     aligned. The caller owns all memory (inputs, outputs, weights, workspace, K/V cache); the
+ *     library never allocates or frees device memory.
+ *   - Calls are asynchronous on `stream` (NULL = the null stream). Buffers must stay alive until
+ *     the stream has passed the call. Argument validation happens on the host before anything is
+ *     enqueued; a call that returns an error other than ONETRANS_ERR_HIP has enqueued nothing.
+ *     Device faults surface at the caller's synchronisation or as ONETRANS_ERR_HIP of a later call.
+ *   - Storage dtype (config.dtype) applies to X(0) / x_s / x_ns / x_new, all weights and norm
+ *     parameters, and the K/V cache. Arithmetic accumulates in fp32; the residual stream between
+ *     blocks is fp32; every output buffer (out, out_s, out_ns, out_new) is fp32.
+ *   - Weight matrices are (out, in) row-major, like torch.nn.Linear: y = W x. Each matrix is
+ *     stored as [1 + l_ns][rows][cols]: index 0 is the shared S set, 1 + j is NS token j.
+ *   - No exceptions cross the boundary; every entry point returns an onetrans_status.
+ *   - Supported shapes: d_head = d_model / n_heads in {16, 32}; d_model and d_ff multiples of 64,
+ *     d_model <= 1024; 0 <= l_ns <= 32 (>= 1 for score_candidates).
+ */
+#ifndef ONETRANS_H_
+#define ONETRANS_H_
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ONETRANS_OK = 0,
+  ONETRANS_ERR_INVALID_ARG = -1,    /* null pointer, bad enum, non-positive size */
+  ONETRANS_ERR_SHAPE = -2,          /* inconsistent sizes or pyramid schedule */
+  ONETRANS_ERR_UNSUPPORTED = -3,    /* valid but not implemented (d_head, dims, pyramided append) */
+  ONETRANS_ERR_WORKSPACE = -4,      /* ws_bytes smaller than onetrans_workspace_bytes() */
+  ONETRANS_ERR_CACHE_CAPACITY = -5, /* cache too small for the rows to be written */
+  ONETRANS_ERR_ALIGNMENT = -6,      /* a device pointer is not 16-byte aligned */
+  ONETRANS_ERR_HIP = -7             /* a HIP runtime call or kernel launch failed */
+} onetrans_status;
+
+typedef enum { ONETRANS_F32 = 0, ONETRANS_BF16 = 1 } onetrans_dtype;
+typedef enum { ONETRANS_RMSNORM = 0, ONETRANS_LAYERNORM = 1 } onetrans_norm;
+typedef enum {
+  ONETRANS_OP_FORWARD = 0, ONETRANS_OP_PREFILL = 1, ONETRANS_OP_SCORE = 2, ONETRANS_OP_APPEND = 3
+} onetrans_op;
+
+typedef struct {
+  int n_blocks;           /* N */
+  int d_model;            /* d */
+  int n_heads;            /* H; head h owns columns [h*d_head, (h+1)*d_head) of q, k, v, o */
+  int d_ff;               /* FFN width */
+  int l_ns;               /* NS tokens per sample / candidate */
+  int norm;               /* onetrans_norm. RMSNorm: x / sqrt(mean(x^2) + eps) * g.
+                             LayerNorm: (x - mean) / sqrt(var + eps) * g + b (population var) */
+  float norm_eps;
+  int dtype;              /* onetrans_dtype (storage) */
+  const int *s_queries;   /* host [n_blocks]: q_n, the S rows block n keeps as queries (pyramid,
+                             section 7.5.2). Non-increasing, 1 <= q_n <= s_n where s_0 = l_s and
+                             s_{n+1} = q_n. q_n = s_n for every block means no pyramid. */
+} onetrans_config;
+
+typedef struct {          /* one per block, storage dtype */
+  const void *norm1_g, *norm1_b;   /* [d]; *_b is ignored by RMSNorm (may be NULL then) */
+  const void *norm2_g, *norm2_b;   /* [d] */
+  const void *wq, *wk, *wv, *wo;   /* [1+l_ns][d][d] */
+  const void *w1, *b1;             /* [1+l_ns][d_ff][d], [1+l_ns][d_ff] */
+  const void *w2, *b2;             /* [1+l_ns][d][d_ff], [1+l_ns][d] */
+} onetrans_block_weights;
+
+typedef struct {
+  void *k, *v;            /* device, onetrans_kv_cache_bytes() bytes each, storage dtype,
+                             layout [user][block][head][capacity][d_head] */
+  int n_users;
+  int capacity;           /* rows per (user, block) */
+  int *layer_len;         /* host [n_blocks]: valid rows of block n (same for every user); written
+                             by prefill_user (s_n) and advanced by append_events (+d_l) */
+} onetrans_kv_cache;
+
+/* Workspace bytes needed by one call of `op`.
+ *   FORWARD: n_seq = batch, l_s = S rows per sample (n_cand, d_l ignored)
+ *   PREFILL: n_seq = users, l_s = S rows per user
+ *   SCORE:   n_seq = users, n_cand = candidates per user (l_s ignored)
+ *   APPEND:  n_seq = users, d_l = appended rows per user
+ * Returns 0 for an invalid configuration. */
+size_t onetrans_workspace_bytes(const onetrans_config *cfg, int op, int n_seq, int l_s, int n_cand,
+                                int d_l);
+
+/* Bytes of ONE of the two cache arrays (K or V): n_users * n_blocks * n_heads * capacity * d_head
+ * elements of the storage dtype. Returns 0 for an invalid configuration. */
+size_t onetrans_kv_cache_bytes(const onetrans_config *cfg, int n_users, int capacity);
+
+/* Monolithic forward of the block stack (sections 7.5.1-7.5.2) over `batch` independent samples.
+ *   x0  [batch][l_s + l_ns][d] storage dtype: S rows then NS rows of each sample.
+ *   out [batch][q_last + l_ns][d] fp32: final block rows (tail S rows then NS rows).
+ * Errors: INVALID_ARG, SHAPE, UNSUPPORTED, WORKSPACE, ALIGNMENT, HIP. */
+int onetrans_forward(const onetrans_config *cfg, const onetrans_block_weights *blk /* host [n_blocks] */,
+                     const void *x0, int batch, int l_s, void *out, void *ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* Stage I (section 7.5.3): run the S rows of `n_users` users through every block (pyramid
+ * included, no NS rows: S rows never attend to NS rows) and write each block's K/V rows into the
+ * cache: block n gets s_n rows at positions 0..s_n-1. Sets cache->layer_len[n] = s_n.
+ *   x_s   [n_users][l_s][d] storage dtype.
+ *   out_s [n_users][q_last][d] fp32 final S rows, or NULL.
+ * Errors: as forward, plus CACHE_CAPACITY (capacity < l_s or n_users > cache->n_users). */
+int onetrans_prefill_user(const onetrans_config *cfg, const onetrans_block_weights *blk,
+                          const void *x_s, int n_users, int l_s, onetrans_kv_cache *cache, void *out_s,
+                          void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Stage II (section 7.5.3): score `n_cand` candidates per user. At block n the NS rows of a
+ * candidate sit behind the user's layer_len[n] cached S rows; NS query j attends over those cached
+ * keys and its own NS keys 0..j in one softmax, then goes through its token-specific FFN.
+ *   x_ns   [n_users][n_cand][l_ns][d] storage dtype.
+ *   out_ns [n_users][n_cand][l_ns][d] fp32 final NS rows.
+ * The cache is read only. Errors: as forward, plus SHAPE if n_users > cache->n_users or a
+ * layer_len is out of range. */
+int onetrans_score_candidates(const onetrans_config *cfg, const onetrans_block_weights *blk,
+                              const onetrans_kv_cache *cache, const void *x_ns, int n_users,
+                              int n_cand, void *out_ns, void *ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+/* Cross-request append (section 7.5.3): `d_l` new S rows per user at positions L_old..L_old+d_l-1
+ * behind the L_old cached rows. Only the new rows are computed (shared S parameters, keys = cached
+ * rows plus new rows up to themselves); their K/V are written at offset L_old of every block and
+ * layer_len[n] becomes L_old + d_l. Needs an unpyramided cache (every layer_len equal), otherwise
+ * UNSUPPORTED: with a tail-count pyramid the key window of later blocks would slide with every
+ * append, so appending could not equal recomputation. cfg->s_queries is not read by this call.
+ *   x_new   [n_users][d_l][d] storage dtype.
+ *   out_new [n_users][d_l][d] fp32 final rows of the new events, or NULL.
+ * Errors: as forward, plus CACHE_CAPACITY (L_old + d_l > capacity), UNSUPPORTED (pyramided cache). */
+int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weights *blk,
+                           onetrans_kv_cache *cache, const void *x_new, int n_users, int d_l,
+                           void *out_new, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Static text for a status code. */
+const char *onetrans_status_string(int status);
+
+/* Library version string, e.g. "onetrans-gfx950 0.1". */
+const char *onetrans_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ONETRANS_H_ */

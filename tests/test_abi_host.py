@@ -1,0 +1,149 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared symbol, sizes its
+buffers as documented, and rejects bad arguments on the host before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from unified_transformer_recommender_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "onetrans.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH), reason="libonetrans.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(onetrans_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert "onetrans_forward" in names and len(names) == 8
+    lib = L.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in L.SIGNATURES, f"binding lacks {n}"
+    assert lib.onetrans_version().decode().startswith("onetrans-gfx950")
+
+
+def _cfg(d=256, H=8, dff=1024, lns=16, N=2, sq=(100, 50), dtype=L.BF16, norm=L.RMSNORM):
+    sqa = (ctypes.c_int * N)(*sq)
+    c = L.Config(N, d, H, dff, lns, norm, 1e-6, dtype, sqa)
+    c._keep = sqa
+    return c
+
+
+def _blocks(N, base=0x100000):
+    b = (L.BlockWeights * N)()
+    for i in range(N):
+        for j, f in enumerate(L.WEIGHT_FIELDS):
+            setattr(b[i], f, base + (i * 16 + j) * 4096)
+    return b
+
+
+FAKE = 0x7000000      # aligned, never dereferenced: every call below fails validation first
+
+
+def test_workspace_and_cache_sizes():
+    lib = L.lib()
+    c = _cfg()
+    B, l_s = 4, 120
+    got = lib.onetrans_workspace_bytes(ctypes.byref(c), L.OP_FORWARD, B, l_s, 0, 0)
+    d, dff, T, R = 256, 1024, 136, 116
+    al = lambda n: (n + 255) // 256 * 256
+    expect = (al(B * R * d * 4) + al(B * T * d * 2) + al(B * R * d * 2) + 2 * al(B * T * d * 2)
+              + al(B * R * d * 2) + al(B * R * d * 4) + al(B * R * d * 2) + al(B * R * dff * 2))
+    assert got == expect
+    assert lib.onetrans_kv_cache_bytes(ctypes.byref(c), 3, 200) == 3 * 2 * 8 * 200 * 32 * 2
+    assert lib.onetrans_workspace_bytes(ctypes.byref(c), L.OP_SCORE, 2, 0, 5, 0) > 0
+    assert lib.onetrans_workspace_bytes(ctypes.byref(c), 9, 2, 10, 0, 0) == 0
+    assert lib.onetrans_workspace_bytes(None, L.OP_FORWARD, 2, 10, 0, 0) == 0
+    # pyramid longer than the sequence
+    assert lib.onetrans_workspace_bytes(ctypes.byref(c), L.OP_FORWARD, 2, 60, 0, 0) == 0
+
+
+def _fwd(c, blocks, x0=FAKE, B=2, l_s=120, out=FAKE, ws=FAKE, wsb=1 << 40):
+    return L.lib().onetrans_forward(ctypes.byref(c) if c is not None else None, blocks, x0, B, l_s, out, ws, wsb,
+                                    None)
+
+
+def test_forward_validation_errors():
+    c, b = _cfg(), _blocks(2)
+    assert _fwd(None, b) == L.ERR_INVALID_ARG
+    assert _fwd(c, None) == L.ERR_INVALID_ARG
+    assert _fwd(c, b, x0=None) == L.ERR_INVALID_ARG
+    assert _fwd(c, b, x0=FAKE + 2) == L.ERR_ALIGNMENT
+    assert _fwd(c, b, out=FAKE + 8) == L.ERR_ALIGNMENT
+    assert _fwd(c, b, wsb=1024) == L.ERR_WORKSPACE
+    assert _fwd(c, b, ws=None) == L.ERR_INVALID_ARG
+    assert _fwd(c, b, B=0) == L.ERR_SHAPE
+    assert _fwd(c, b, l_s=60) == L.ERR_SHAPE                       # q_0 = 100 > s_0 = 60
+    assert _fwd(_cfg(sq=(100, 120)), b) == L.ERR_SHAPE               # schedule must not grow
+    assert _fwd(_cfg(sq=(100, 0)), b) == L.ERR_SHAPE
+    assert _fwd(_cfg(d=256, H=4), b) == L.ERR_UNSUPPORTED            # d_head 64
+    assert _fwd(_cfg(d=96, H=3), b) == L.ERR_UNSUPPORTED             # d not a multiple of 64
+    assert _fwd(_cfg(d=256, H=7), b) == L.ERR_SHAPE                  # d % H != 0
+    assert _fwd(_cfg(lns=40), b) == L.ERR_UNSUPPORTED
+    assert _fwd(_cfg(dtype=7), b) == L.ERR_INVALID_ARG
+    assert _fwd(_cfg(norm=5), b) == L.ERR_INVALID_ARG
+    nb = _blocks(2)
+    nb[1].w2 = None
+    assert _fwd(c, nb) == L.ERR_INVALID_ARG
+    nb[1].w2 = FAKE + 4
+    assert _fwd(c, nb) == L.ERR_ALIGNMENT
+    # RMSNorm ignores the shift vectors, LayerNorm needs them
+    nb = _blocks(2)
+    nb[0].norm1_b = None
+    assert _fwd(c, nb, wsb=1024) == L.ERR_WORKSPACE
+    assert _fwd(_cfg(norm=L.LAYERNORM), nb) == L.ERR_INVALID_ARG
+
+
+def _cache(n_users=2, cap=200, lens=(120, 100)):
+    ll = (ctypes.c_int * len(lens))(*lens)
+    kc = L.KVCache(FAKE, FAKE, n_users, cap, ll)
+    kc._keep = ll
+    return kc
+
+
+def test_serving_validation_errors():
+    lib = L.lib()
+    c, b = _cfg(), _blocks(2)
+    kc = _cache()
+    # prefill: capacity and user count
+    assert lib.onetrans_prefill_user(ctypes.byref(c), b, FAKE, 2, 120, ctypes.byref(_cache(cap=100)), None, FAKE,
+                                     1 << 40, None) == L.ERR_CACHE_CAPACITY
+    assert lib.onetrans_prefill_user(ctypes.byref(c), b, FAKE, 3, 120, ctypes.byref(kc), None, FAKE, 1 << 40,
+                                     None) == L.ERR_CACHE_CAPACITY
+    assert lib.onetrans_prefill_user(ctypes.byref(c), b, FAKE, 2, 120, None, None, FAKE, 1 << 40,
+                                     None) == L.ERR_INVALID_ARG
+    assert lib.onetrans_prefill_user(ctypes.byref(c), b, FAKE, 2, 120, ctypes.byref(kc), None, FAKE, 16,
+                                     None) == L.ERR_WORKSPACE
+    # score: users beyond the cache, bad layer length, NS-free model
+    assert lib.onetrans_score_candidates(ctypes.byref(c), b, ctypes.byref(kc), FAKE, 3, 4, FAKE, FAKE, 1 << 40,
+                                         None) == L.ERR_SHAPE
+    assert lib.onetrans_score_candidates(ctypes.byref(c), b, ctypes.byref(_cache(lens=(120, 300))), FAKE, 2, 4,
+                                         FAKE, FAKE, 1 << 40, None) == L.ERR_SHAPE
+    assert lib.onetrans_score_candidates(ctypes.byref(_cfg(lns=0)), b, ctypes.byref(kc), FAKE, 2, 4, FAKE, FAKE,
+                                         1 << 40, None) == L.ERR_SHAPE
+    assert lib.onetrans_score_candidates(ctypes.byref(c), b, ctypes.byref(kc), FAKE, 2, 4, FAKE, FAKE, 64,
+                                         None) == L.ERR_WORKSPACE
+    # append: pyramided cache, capacity
+    assert lib.onetrans_append_events(ctypes.byref(c), b, ctypes.byref(kc), FAKE, 2, 8, None, FAKE, 1 << 40,
+                                      None) == L.ERR_UNSUPPORTED
+    full = _cache(cap=128, lens=(124, 124))
+    assert lib.onetrans_append_events(ctypes.byref(c), b, ctypes.byref(full), FAKE, 2, 8, None, FAKE, 1 << 40,
+                                      None) == L.ERR_CACHE_CAPACITY
+    assert list(full._keep) == [124, 124]            # nothing advanced on error
+    assert lib.onetrans_append_events(ctypes.byref(c), b, ctypes.byref(full), FAKE, 2, 0, None, FAKE, 1 << 40,
+                                      None) == L.ERR_SHAPE
+
+
+def test_status_strings():
+    for s in range(-7, 1):
+        assert L.status_string(s) not in ("", "unknown status")
+    assert L.status_string(-99) == "unknown status"

@@ -1,0 +1,197 @@
+"""GPU parity of the four C-ABI entry points against the CPU oracle.
+
+Every comparison is element by element on the same seeded inputs; the bar is
+max |gpu - oracle| / rms(oracle) <= 1e-4 in fp32 mode and <= 2e-2 in bf16 mode. Full-size
+workloads run in the launch configuration the benchmark times and compare a seeded subset of
+samples / users / candidates (samples are independent).
+"""
+
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from gpu_util import TOL, cache_to_host, dev, model, rel_err, say, weights
+from unified_transformer_recommender_amd import binding as ob
+
+pytestmark = pytest.mark.gpu
+
+
+def _forward_case(w, samples=None):
+    say(f"[forward] {w.key} dtype={w.model.dtype} B={w.batch} L_S={w.l_s} q={w.s_queries}")
+    mdl = model(w)
+    x = synth.forward_batch(w)
+    out = ob.onetrans_forward(mdl, dev(x, mdl))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    idx = range(w.batch) if samples is None else samples
+    ws = weights(w.model)
+    for b in idx:
+        ref = O.forward(x[b], ws, w.model, w.s_queries)
+        e = rel_err(got[b], ref)
+        say(f"  sample {b}: err {e:.3e}")
+        assert e <= TOL[w.model.dtype], (w.key, b, e)
+    return got
+
+
+# --- small shapes: several tiles, ragged tails, both precisions -------------------------------
+
+def test_tiny_config_fp32_all_samples():
+    _forward_case(synth.workload("tiny"))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_tiny3_pyramid_forward(dtype):
+    _forward_case(synth.test_workload("tiny3_fwd", dtype))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_tiny_layernorm_bf16_and_f32(dtype):
+    _forward_case(synth.workload("tiny", dtype))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mid_shape_ragged_tiles(dtype):
+    """d=256 / 8 heads (d_head 32, 128x128 GEMM tiles) with lengths that leave ragged tiles."""
+    m = replace(synth.workload("onetrans_s").model, n_blocks=3, dtype=dtype)
+    w = replace(synth.workload("onetrans_s"), model=m, l_s=203, s_queries=(203, 131, 5), seq_lens=(60, 70, 70),
+                batch=5, key="mid_ragged")
+    _forward_case(w)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_two_stage_small(dtype):
+    w = synth.test_workload("tiny3_two_stage", dtype)
+    say(f"[two_stage] {w.key} dtype={dtype}")
+    mdl = model(w)
+    m, ws = w.model, weights(w.model)
+    xs = synth.user_sequences(w)
+    xn = synth.candidate_batch(w)
+    cache = ob.KVCache(mdl, w.n_users, w.l_s)
+    out_s = torch.empty((w.n_users, w.s_queries[-1], m.d_model), dtype=torch.float32, device=mdl.device)
+    ob.onetrans_prefill_user(mdl, dev(xs, mdl), cache, out_s)
+    out = ob.onetrans_score_candidates(mdl, cache, dev(xn, mdl))
+    torch.cuda.synchronize()
+    assert cache.lengths == [32, 32, 20]
+    for u in range(w.n_users):
+        rc, rs = O.prefill_user(xs[u], ws, m, w.s_queries)
+        assert rel_err(out_s[u].cpu().numpy(), rs) <= TOL[dtype]
+        for n, (k, v) in enumerate(cache_to_host(cache, u, m.n_blocks, cache.lengths)):
+            assert rel_err(k, rc[n]["k"]) <= TOL[dtype] and rel_err(v, rc[n]["v"]) <= TOL[dtype], (u, n)
+        for c in range(w.n_cand):
+            e = rel_err(out[u, c].cpu().numpy(), O.score_candidate(rc, xn[u, c], ws, m))
+            say(f"  user {u} cand {c}: err {e:.3e}")
+            assert e <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_append_small(dtype):
+    w = synth.test_workload("tiny3_append", dtype)
+    say(f"[append] {w.key} dtype={dtype}")
+    m, ws = w.model, weights(w.model)
+    mdl = model(w, s_queries=(w.l_old,) * m.n_blocks)
+    old, new = synth.append_batch(w)
+    xn = np.stack([synth.candidate_tokens(w, u, 0) for u in range(w.n_users)])[:, None]
+    cache = ob.KVCache(mdl, w.n_users, w.l_old + w.d_l)
+    ob.onetrans_prefill_user(mdl, dev(old, mdl), cache)
+    out_new = torch.empty((w.n_users, w.d_l, m.d_model), dtype=torch.float32, device=mdl.device)
+    ob.onetrans_append_events(mdl, cache, dev(new, mdl), out_new)
+    sc = ob.onetrans_score_candidates(mdl, cache, dev(xn, mdl))
+    torch.cuda.synchronize()
+    assert cache.lengths == [w.l_old + w.d_l] * m.n_blocks
+    for u in range(w.n_users):
+        oc, _ = O.prefill_user(old[u], ws, m, (w.l_old,) * m.n_blocks)
+        nc, ref_new = O.append_events(oc, new[u], ws, m)
+        assert rel_err(out_new[u].cpu().numpy(), ref_new) <= TOL[dtype]
+        for n, (k, v) in enumerate(cache_to_host(cache, u, m.n_blocks, cache.lengths)):
+            assert rel_err(k, nc[n]["k"]) <= TOL[dtype] and rel_err(v, nc[n]["v"]) <= TOL[dtype]
+        e = rel_err(sc[u, 0].cpu().numpy(), O.score_candidate(nc, xn[u, 0], ws, m))
+        say(f"  user {u}: score err {e:.3e}")
+        assert e <= TOL[dtype]
+
+
+def test_edge_cases_forward():
+    """batch 1, no NS tokens, pyramid down to one S query."""
+    base = synth.test_workload("tiny3_fwd", "bf16")
+    _forward_case(replace(base, batch=1, s_queries=(32, 7, 1), key="b1_q1"))
+    m0 = replace(base.model, l_ns=0)
+    _forward_case(replace(base, model=m0, batch=3, key="no_ns"))
+
+
+# --- full workloads (the benchmark's launch configurations) -----------------------------------
+
+def test_onetrans_s_forward_bf16_full_batch():
+    w = synth.workload("onetrans_s")
+    _forward_case(w, samples=w.parity_subset)
+
+
+def test_onetrans_s_forward_f32_mode():
+    w = replace(synth.workload("onetrans_s", "f32"), batch=12)
+    _forward_case(w, samples=(0, 5, 11))
+
+
+def test_two_stage_full():
+    w = synth.workload("two_stage")
+    say(f"[two_stage full] U={w.n_users} C={w.n_cand}")
+    m, ws = w.model, weights(w.model)
+    mdl = model(w)
+    xs = synth.user_sequences(w)
+    xn = synth.candidate_batch(w)
+    cache = ob.KVCache(mdl, w.n_users, w.l_s)
+    ob.onetrans_prefill_user(mdl, dev(xs, mdl), cache)
+    out = ob.onetrans_score_candidates(mdl, cache, dev(xn, mdl))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    for u in w.parity_subset:
+        rc, _ = O.prefill_user(xs[u], ws, m, w.s_queries)
+        for c in sorted(rng.choice(w.n_cand, 16, replace=False)):
+            e = rel_err(out[u, c].cpu().numpy(), O.score_candidate(rc, xn[u, c], ws, m))
+            assert e <= TOL["bf16"], (u, c, e)
+        say(f"  user {u}: 16 candidates ok")
+
+
+def test_append_full():
+    w = synth.workload("append")
+    say(f"[append full] U={w.n_users} L_old={w.l_old} dL={w.d_l}")
+    m, ws = w.model, weights(w.model)
+    mdl = model(w, s_queries=(w.l_old,) * m.n_blocks)
+    old, new = synth.append_batch(w)
+    xn = np.stack([synth.candidate_tokens(w, u, 0) for u in range(w.n_users)])[:, None]
+    cache = ob.KVCache(mdl, w.n_users, w.l_s)
+    ob.onetrans_prefill_user(mdl, dev(old, mdl), cache)
+    out_new = torch.empty((w.n_users, w.d_l, m.d_model), dtype=torch.float32, device=mdl.device)
+    ob.onetrans_append_events(mdl, cache, dev(new, mdl), out_new)
+    sc = ob.onetrans_score_candidates(mdl, cache, dev(xn, mdl))
+    torch.cuda.synchronize()
+    for u in w.parity_subset:
+        oc, _ = O.prefill_user(old[u], ws, m, (w.l_old,) * m.n_blocks)
+        nc, ref_new = O.append_events(oc, new[u], ws, m)
+        e1 = rel_err(out_new[u].cpu().numpy(), ref_new)
+        e2 = rel_err(sc[u, 0].cpu().numpy(), O.score_candidate(nc, xn[u, 0], ws, m))
+        say(f"  user {u}: new rows {e1:.3e} score {e2:.3e}")
+        assert e1 <= TOL["bf16"] and e2 <= TOL["bf16"]
+
+
+def test_onetrans_l_forward_bf16_full_batch():
+    w = synth.workload("onetrans_l")
+    _forward_case(w, samples=w.parity_subset)
+
+
+# --- GPU-side invariants ----------------------------------------------------------------------
+
+def test_gpu_two_stage_matches_gpu_forward():
+    w = synth.test_workload("tiny3_two_stage", "f32")
+    mdl = model(w)
+    xs = synth.user_sequences(w)
+    xn = synth.candidate_batch(w)
+    cache = ob.KVCache(mdl, w.n_users, w.l_s)
+    ob.onetrans_prefill_user(mdl, dev(xs, mdl), cache)
+    sc = ob.onetrans_score_candidates(mdl, cache, dev(xn, mdl)).cpu().numpy()
+    x0 = np.concatenate([np.repeat(xs[:, None], w.n_cand, 1), xn], axis=2).reshape(-1, w.l_s + w.model.l_ns,
+                                                                                   w.model.d_model)
+    fw = ob.onetrans_forward(mdl, dev(x0, mdl)).cpu().numpy()
+    ns = fw[:, -w.model.l_ns:].reshape(sc.shape)
+    assert rel_err(sc, ns) <= 1e-5

@@ -1,0 +1,178 @@
+"""Python binding of the C ABI: the same four entry points, torch tensors in and out.
+
+Only argument marshalling happens here. torch provides device memory and the current stream;
+every step of the computation runs in the HIP library (libonetrans.so). If the library is
+missing, every call raises: there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import torch
+
+from . import _lib as L
+
+DTYPES = {"f32": (L.F32, torch.float32, 4), "bf16": (L.BF16, torch.bfloat16, 2)}
+NORMS = {"rms": L.RMSNORM, "layer": L.LAYERNORM}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev: torch.device, stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    return s.cuda_stream
+
+
+class Model:
+    """Configuration plus per-block device weights of a OneTrans stack.
+
+    ``blocks`` is a sequence (one per block) of mappings or objects providing the twelve
+    parameter tensors named in ``_lib.WEIGHT_FIELDS`` on the device, in the storage dtype,
+    contiguous, shaped as documented in include/onetrans.h.
+    """
+
+    def __init__(self, *, n_blocks: int, d_model: int, n_heads: int, d_ff: int, l_ns: int, norm: str,
+                 norm_eps: float, dtype: str, s_queries: Sequence[int], blocks):
+        self.n_blocks, self.d_model, self.n_heads, self.d_ff, self.l_ns = n_blocks, d_model, n_heads, d_ff, l_ns
+        self.dtype = dtype
+        self.dt_code, self.torch_dtype, self.esz = DTYPES[dtype]
+        self.s_queries = tuple(int(q) for q in s_queries)
+        self._sq = (ctypes.c_int * n_blocks)(*self.s_queries)
+        self.cfg = L.Config(n_blocks, d_model, n_heads, d_ff, l_ns, NORMS[norm], float(norm_eps), self.dt_code,
+                            self._sq)
+        self._tensors = []
+        self.blocks = (L.BlockWeights * n_blocks)()
+        for i, b in enumerate(blocks):
+            for f in L.WEIGHT_FIELDS:
+                t = b[f] if isinstance(b, dict) else getattr(b, f)
+                if not (t.is_contiguous() and t.dtype == self.torch_dtype):
+                    raise ValueError(f"block {i} {f}: need a contiguous {self.torch_dtype} tensor")
+                self._tensors.append(t)
+                setattr(self.blocks[i], f, t.data_ptr())
+        self.device = self._tensors[0].device
+
+    @classmethod
+    def from_host(cls, shape, s_queries: Sequence[int], host_blocks, device="cuda") -> "Model":
+        """Upload host weights (numpy float32 arrays, already representable in the storage dtype)."""
+        _, tdt, _ = DTYPES[shape.dtype]
+        blocks = [{f: torch.from_numpy(getattr(b, f)).to(device=device, dtype=tdt).contiguous()
+                   for f in L.WEIGHT_FIELDS} for b in host_blocks]
+        return cls(n_blocks=shape.n_blocks, d_model=shape.d_model, n_heads=shape.n_heads, d_ff=shape.d_ff,
+                   l_ns=shape.l_ns, norm=shape.norm, norm_eps=shape.norm_eps, dtype=shape.dtype,
+                   s_queries=s_queries, blocks=blocks)
+
+    def with_schedule(self, s_queries: Sequence[int]) -> "Model":
+        """Same weights, another pyramid schedule."""
+        m = Model.__new__(Model)
+        m.__dict__.update(self.__dict__)
+        m.s_queries = tuple(int(q) for q in s_queries)
+        m._sq = (ctypes.c_int * self.n_blocks)(*m.s_queries)
+        m.cfg = L.Config(self.cfg.n_blocks, self.cfg.d_model, self.cfg.n_heads, self.cfg.d_ff, self.cfg.l_ns,
+                         self.cfg.norm, self.cfg.norm_eps, self.cfg.dtype, m._sq)
+        return m
+
+    def workspace_bytes(self, op: int, n_seq: int, l_s: int = 0, n_cand: int = 0, d_l: int = 0) -> int:
+        return int(L.lib().onetrans_workspace_bytes(ctypes.byref(self.cfg), op, n_seq, l_s, n_cand, d_l))
+
+    def workspace(self, op: int, n_seq: int, l_s: int = 0, n_cand: int = 0, d_l: int = 0) -> torch.Tensor:
+        n = self.workspace_bytes(op, n_seq, l_s, n_cand, d_l)
+        if n == 0:
+            raise ValueError("invalid configuration for a workspace")
+        return torch.empty(n, dtype=torch.uint8, device=self.device)
+
+
+class KVCache:
+    """Caller-owned K/V cache [user][block][head][capacity][d_head] in the storage dtype."""
+
+    def __init__(self, model: Model, n_users: int, capacity: int):
+        nbytes = int(L.lib().onetrans_kv_cache_bytes(ctypes.byref(model.cfg), n_users, capacity))
+        if nbytes == 0:
+            raise ValueError("invalid cache shape")
+        shape = (n_users, model.n_blocks, model.n_heads, capacity, model.d_model // model.n_heads)
+        self.k = torch.empty(shape, dtype=model.torch_dtype, device=model.device)
+        self.v = torch.empty(shape, dtype=model.torch_dtype, device=model.device)
+        assert self.k.numel() * model.esz == nbytes
+        self.layer_len = (ctypes.c_int * model.n_blocks)()
+        self.c = L.KVCache(self.k.data_ptr(), self.v.data_ptr(), n_users, capacity, self.layer_len)
+
+    @property
+    def lengths(self):
+        return list(self.layer_len)
+
+    def copy_(self, other: "KVCache") -> "KVCache":
+        self.k.copy_(other.k)
+        self.v.copy_(other.v)
+        for i, n in enumerate(other.layer_len):
+            self.layer_len[i] = n
+        return self
+
+
+def _check_input(model: Model, x: torch.Tensor, ndim: int, name: str):
+    if x.dtype != model.torch_dtype or not x.is_contiguous() or x.dim() != ndim or x.shape[-1] != model.d_model:
+        raise ValueError(f"{name}: need a contiguous {model.torch_dtype} tensor of rank {ndim} and width d_model")
+
+
+def onetrans_forward(model: Model, x0: torch.Tensor, out: Optional[torch.Tensor] = None,
+                     ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """x0 [B][L_S + l_ns][d] (storage dtype) -> out [B][q_last + l_ns][d] fp32."""
+    _check_input(model, x0, 3, "x0")
+    B, T, d = x0.shape
+    l_s = T - model.l_ns
+    if out is None:
+        out = torch.empty((B, model.s_queries[-1] + model.l_ns, d), dtype=torch.float32, device=x0.device)
+    if ws is None:
+        ws = model.workspace(L.OP_FORWARD, B, l_s)
+    st = L.lib().onetrans_forward(ctypes.byref(model.cfg), model.blocks, x0.data_ptr(), B, l_s, out.data_ptr(),
+                                  ws.data_ptr(), ws.numel(), _stream(x0.device, stream))
+    L.check(st, "onetrans_forward")
+    return out
+
+
+def onetrans_prefill_user(model: Model, x_s: torch.Tensor, cache: KVCache, out_s: Optional[torch.Tensor] = None,
+                          ws: Optional[torch.Tensor] = None, stream=None) -> Optional[torch.Tensor]:
+    """Stage I: x_s [U][L_S][d] -> cache K/V per block (and optionally out_s [U][q_last][d] fp32)."""
+    _check_input(model, x_s, 3, "x_s")
+    U, l_s, _ = x_s.shape
+    if ws is None:
+        ws = model.workspace(L.OP_PREFILL, U, l_s)
+    st = L.lib().onetrans_prefill_user(ctypes.byref(model.cfg), model.blocks, x_s.data_ptr(), U, l_s,
+                                       ctypes.byref(cache.c), _ptr(out_s), ws.data_ptr(), ws.numel(),
+                                       _stream(x_s.device, stream))
+    L.check(st, "onetrans_prefill_user")
+    return out_s
+
+
+def onetrans_score_candidates(model: Model, cache: KVCache, x_ns: torch.Tensor,
+                              out_ns: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                              stream=None) -> torch.Tensor:
+    """Stage II: x_ns [U][C][l_ns][d] -> out_ns [U][C][l_ns][d] fp32."""
+    _check_input(model, x_ns, 4, "x_ns")
+    U, C, _, d = x_ns.shape
+    if out_ns is None:
+        out_ns = torch.empty((U, C, model.l_ns, d), dtype=torch.float32, device=x_ns.device)
+    if ws is None:
+        ws = model.workspace(L.OP_SCORE, U, n_cand=C)
+    st = L.lib().onetrans_score_candidates(ctypes.byref(model.cfg), model.blocks, ctypes.byref(cache.c),
+                                           x_ns.data_ptr(), U, C, out_ns.data_ptr(), ws.data_ptr(), ws.numel(),
+                                           _stream(x_ns.device, stream))
+    L.check(st, "onetrans_score_candidates")
+    return out_ns
+
+
+def onetrans_append_events(model: Model, cache: KVCache, x_new: torch.Tensor,
+                           out_new: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                           stream=None) -> Optional[torch.Tensor]:
+    """Cross-request append: x_new [U][dL][d] -> cache extended by dL rows per block (+ out_new fp32)."""
+    _check_input(model, x_new, 3, "x_new")
+    U, dl, _ = x_new.shape
+    if ws is None:
+        ws = model.workspace(L.OP_APPEND, U, d_l=dl)
+    st = L.lib().onetrans_append_events(ctypes.byref(model.cfg), model.blocks, ctypes.byref(cache.c),
+                                        x_new.data_ptr(), U, dl, _ptr(out_new), ws.data_ptr(), ws.numel(),
+                                        _stream(x_new.device, stream))
+    L.check(st, "onetrans_append_events")
+    return out_new

@@ -1,0 +1,252 @@
+// Causal mixed attention with pyramid tail queries and the Stage II two-segment key set.
+//
+// What is computed (fun-rec-mdbook 7.5.1 causal mask, 7.5.2 Pyramid Stack, 7.5.3 two-stage
+// serving): for every head h and query row at position p,
+//     o = sum_{key u <= p} softmax_u(q . k_u / sqrt(d_head)) v_u
+// Keys span every row of the block input; queries are only the tail rows. In Stage II the keys
+// of a candidate's NS query j are the user's cached S rows followed by the candidate's own NS
+// rows 0..j, one softmax over both.
+//
+// Work layout: a workgroup (4 waves) handles one (sequence or user, head) and up to 128 query
+// rows; a wave owns 32 query rows. Scores are formed transposed, S^T = K Q^T, with one MFMA
+// 32x32 tile per 32 keys, so a lane holds 16 of the 32 keys of ONE query (its column) and the
+// softmax statistics of that query stay in the lane (one cross-half shuffle per tile). The
+// probabilities are then already laid out as the B operand of O^T += V^T P^T: the k index of that
+// product is a permutation of the 32 keys, and the V^T operand is read with the same permutation
+// from an LDS copy of V stored transposed ([d_head][key]). K/V tiles of 64 keys are staged in LDS
+// once per workgroup and shared by its four waves. Online softmax in base 2 with the 1/sqrt(dh)
+// scale folded into one FMA per score; fully masked tiles are skipped per wave.
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ot {
+
+namespace {
+
+constexpr float NEG_INF = -__builtin_inff();
+
+template <typename T> struct VtFrag;
+
+// bf16: the 8 k elements of lane-group g in k-chunk mc are keys {16mc + 4g + 0..3, 16mc + 8 + 4g + 0..3}
+template <> struct VtFrag<bf16> {
+  static __device__ __forceinline__ bf16x8 load(const bf16 *row, int mc, int g) {
+    const bf16x4 lo = *(const bf16x4 *)(row + 16 * mc + 4 * g);
+    const bf16x4 hi = *(const bf16x4 *)(row + 16 * mc + 8 + 4 * g);
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  static __device__ __forceinline__ bf16x8 pfrag(const float *p, int mc) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (bf16)p[8 * mc + e];
+    return r;
+  }
+};
+
+template <> struct VtFrag<float> {
+  static __device__ __forceinline__ float load(const float *row, int mc, int g) { return row[acc_row(mc, g)]; }
+  static __device__ __forceinline__ float pfrag(const float *p, int mc) { return p[mc]; }
+};
+
+// One 32-key tile: fold masked scores s (already -inf where invisible) into the running state.
+template <typename T, int DH>
+__device__ __forceinline__ void softmax_pv(const f32x16 &s, float scale, float &m, float &lsum, f32x16 &o,
+                                           const T *vt_row /* this lane's V^T row, or null if lc >= DH */,
+                                           int g) {
+  using M = Mma<T>;
+  float mt = s[0];
+#pragma unroll
+  for (int v = 1; v < 16; ++v) mt = fmaxf(mt, s[v]);
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  const float mn = fmaxf(m, mt);
+  const float alpha = __builtin_amdgcn_exp2f((m - mn) * scale);
+  const float nb = -mn * scale;
+  m = mn;
+  float p[16];
+  float ps = 0.0f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    p[v] = __builtin_amdgcn_exp2f(fmaf(s[v], scale, nb));
+    ps += p[v];
+  }
+  lsum = lsum * alpha + ps;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) o[v] *= alpha;
+#pragma unroll
+  for (int mc = 0; mc < 32 / M::KSTEP; ++mc) {
+    typename M::frag vf = vt_row ? VtFrag<T>::load(vt_row, mc, g) : M::zero();
+    o = M::mma(vf, VtFrag<T>::pfrag(p, mc), o);
+  }
+}
+
+template <typename T, int DH, bool STAGE2>
+__global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
+  using M = Mma<T>;
+  using frag = typename M::frag;
+  constexpr int EPC = 16 / (int)sizeof(T);
+  constexpr int KT = 64;             // keys per shared tile
+  constexpr int LDK = DH + EPC;      // padded K row (elements)
+  constexpr int LDV = KT + EPC;      // padded V^T row (keys)
+  constexpr int LDW = 32 + EPC;      // padded V^T row of a wave's own-key tile
+  constexpr int CPK = DH / EPC;      // 16-byte chunks per key row
+  __shared__ __attribute__((aligned(16))) T sK[KT * LDK];
+  __shared__ __attribute__((aligned(16))) T sVt[DH * LDV];
+  __shared__ __attribute__((aligned(16))) T sKw[STAGE2 ? 4 * 32 * LDK : EPC];
+  __shared__ __attribute__((aligned(16))) T sVw[STAGE2 ? 4 * DH * LDW : EPC];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, lc = lane & 31;
+  const int H = a.n_heads;
+  const int per_q = a.n_seq_grp * H;
+  const int qb = a.n_qblocks - 1 - (int)(blockIdx.x / per_q);   // longest query blocks first
+  const int rem = blockIdx.x - (int)(blockIdx.x / per_q) * per_q;
+  const int h = rem % H, grp = rem / H;
+
+  // ---- this lane's query --------------------------------------------------------------------
+  int z, qi, cslot = 0, cpw = 0, c_first = 0;
+  bool valid;
+  if constexpr (!STAGE2) {
+    z = grp;
+    qi = qb * ATTN_QBLOCK + wave * 32 + lc;
+    valid = qi < a.R;
+  } else {
+    cpw = 32 / a.R;
+    cslot = lc / a.R;
+    qi = lc - cslot * a.R;
+    c_first = qb * 4 * cpw + wave * cpw;
+    const int c = c_first + cslot;
+    valid = cslot < cpw && c < a.n_cand;
+    z = grp * a.n_cand + (valid ? c : 0);
+  }
+  const int qpos = a.p0 + qi;
+
+  frag qf[DH / M::KSTEP];
+  {
+    const T *qrow = (const T *)a.q + z * a.q_sb + h * a.q_sh + (long long)(valid ? qi : 0) * DH + g * M::KPL;
+#pragma unroll
+    for (int kk = 0; kk < DH / M::KSTEP; ++kk) qf[kk] = valid ? *(const frag *)(qrow + kk * M::KSTEP) : M::zero();
+  }
+
+  // ---- key range of the shared (prefix) segment --------------------------------------------
+  int n_keys, wave_min = 0, wave_max = 0;
+  if constexpr (!STAGE2) {
+    const int wg_last = min(a.R, (qb + 1) * ATTN_QBLOCK) - 1;
+    n_keys = min(a.n_pre, a.p0 + wg_last + 1);
+    const int wf = qb * ATTN_QBLOCK + wave * 32;
+    const int wl = min(a.R, wf + 32) - 1;
+    wave_min = a.p0 + wf;
+    wave_max = wf < a.R ? a.p0 + wl : -1;
+  } else {
+    n_keys = a.n_pre;
+  }
+  const T *kp = (const T *)a.k_pre + grp * a.pre_sb + h * a.pre_sh;
+  const T *vp = (const T *)a.v_pre + grp * a.pre_sb + h * a.pre_sh;
+
+  f32x16 o = f32x16{};
+  float m = -1e30f, lsum = 0.0f;
+  const float scale = a.scale_log2;
+
+  for (int k0 = 0; k0 < n_keys; k0 += KT) {
+    __syncthreads();
+    for (int ch = tid; ch < KT * CPK; ch += 256) {
+      const int key = ch / CPK, c0 = (ch - key * CPK) * EPC;
+      const int kg = k0 + key;
+      u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+      if (kg < n_keys) {
+        kv = ld16(kp + (long long)kg * DH + c0);
+        vv = ld16(vp + (long long)kg * DH + c0);
+      }
+      st16(&sK[key * LDK + c0], kv);
+      const T *ve = (const T *)&vv;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) sVt[(c0 + e) * LDV + key] = ve[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int sub = 0; sub < KT / 32; ++sub) {
+      const int kb = k0 + sub * 32;
+      if (kb >= n_keys) break;
+      if (!STAGE2 && kb > wave_max) break;
+      f32x16 s = f32x16{};
+      const T *krow = &sK[(sub * 32 + lc) * LDK + g * M::KPL];
+#pragma unroll
+      for (int kk = 0; kk < DH / M::KSTEP; ++kk) s = M::mma(*(const frag *)(krow + kk * M::KSTEP), qf[kk], s);
+      const bool need_mask = STAGE2 ? (kb + 32 > n_keys) : (kb + 31 > wave_min || kb + 32 > n_keys);
+      if (need_mask) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = kb + acc_row(v, g);
+          if (key >= n_keys || (!STAGE2 && key > qpos)) s[v] = NEG_INF;
+        }
+      }
+      softmax_pv<T, DH>(s, scale, m, lsum, o, lc < DH ? &sVt[lc * LDV + sub * 32] : nullptr, g);
+    }
+  }
+
+  // ---- Stage II: the candidates' own NS keys (block-diagonal causal) -----------------------
+  if constexpr (STAGE2) {
+    T *kw = sKw + wave * 32 * LDK;
+    T *vw = sVw + wave * DH * LDW;
+    const int n_own = cpw * a.R;
+    for (int ch = lane; ch < 32 * CPK; ch += 64) {
+      const int ks = ch / CPK, c0 = (ch - ks * CPK) * EPC;
+      const int kc = ks / a.R, j2 = ks - kc * a.R;
+      const int c = c_first + kc;
+      u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+      if (ks < n_own && c < a.n_cand) {
+        const long long off = (long long)(grp * a.n_cand + c) * a.own_sb + h * a.own_sh + (long long)j2 * DH + c0;
+        kv = ld16((const T *)a.k_own + off);
+        vv = ld16((const T *)a.v_own + off);
+      }
+      st16(&kw[ks * LDK + c0], kv);
+      const T *ve = (const T *)&vv;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) vw[(c0 + e) * LDW + ks] = ve[e];
+    }
+    __syncthreads();
+    f32x16 s = f32x16{};
+    const T *krow = &kw[lc * LDK + g * M::KPL];
+#pragma unroll
+    for (int kk = 0; kk < DH / M::KSTEP; ++kk) s = M::mma(*(const frag *)(krow + kk * M::KSTEP), qf[kk], s);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int ks = acc_row(v, g);
+      const int kc = ks / a.R, j2 = ks - kc * a.R;
+      const bool vis = ks < n_own && kc == cslot && j2 <= qi && c_first + kc < a.n_cand;
+      if (!vis) s[v] = NEG_INF;
+    }
+    softmax_pv<T, DH>(s, scale, m, lsum, o, lc < DH ? &vw[lc * LDW] : nullptr, g);
+  }
+
+  // ---- normalise and store O[b][i][h*dh + c] ----------------------------------------------
+  const float lt = lsum + __shfl_xor(lsum, 32, 64);
+  if (valid) {
+    const float inv = 1.0f / lt;
+    T *orow = (T *)a.o + z * a.o_sb + (long long)qi * a.d_model + h * DH;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int c = acc_row(v, g);
+      if (c < DH) orow[c] = from_f32<T>(o[v] * inv);
+    }
+  }
+}
+
+template <typename T, int DH>
+hipError_t launch_dh(int stage2, const AttnArgs &a, hipStream_t s) {
+  dim3 gd(a.n_qblocks * a.n_seq_grp * a.n_heads), bd(256);
+  if (stage2)
+    hipLaunchKernelGGL((attn_kernel<T, DH, true>), gd, bd, 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_kernel<T, DH, false>), gd, bd, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn(int dtype, int d_head, int stage2, const AttnArgs &a, hipStream_t s) {
+  if (a.n_qblocks * a.n_seq_grp * a.n_heads == 0) return hipSuccess;
+  if (dtype == 1) return d_head == 16 ? launch_dh<bf16, 16>(stage2, a, s) : launch_dh<bf16, 32>(stage2, a, s);
+  return d_head == 16 ? launch_dh<float, 16>(stage2, a, s) : launch_dh<float, 32>(stage2, a, s);
+}
+
+}  // namespace ot

@@ -1,0 +1,26 @@
+// Host-side launchers of the device kernels (one translation unit per kernel family).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+
+namespace ot {
+
+// dtype: 0 = fp32 storage, 1 = bf16 storage. tile: 0 = 64x64, 1 = 128x128 workgroup tile.
+// resid_f32: residual operand of EPI_RESID is fp32 (1) or storage dtype (0).
+hipError_t launch_gemm(int dtype, int epi, int resid_f32, int tile, const GemmArgs &a, int grid,
+                       hipStream_t s);
+
+// in_f32: input rows are fp32 (1) or storage dtype (0); output is the storage dtype.
+hipError_t launch_norm(int dtype, int in_f32, const NormArgs &a, hipStream_t s);
+
+hipError_t launch_attn(int dtype, int d_head, int stage2, const AttnArgs &a, hipStream_t s);
+
+// Workgroup tile edge of the GEMM for a given tile selector.
+inline int gemm_bm(int tile) { return tile ? 128 : 64; }
+inline int gemm_bn(int tile) { return tile ? 128 : 64; }
+constexpr int GEMM_BK = 32;
+constexpr int ATTN_QBLOCK = 128;   // forward-mode queries per attention workgroup
+
+}  // namespace ot

@@ -1,0 +1,657 @@
+// C ABI and host planner of the OneTrans hot path.
+//
+// Every operation is the same per-block launch sequence over a different set of rows
+// (fun-rec-mdbook 7.5.1-7.5.3):
+//   norm1 -> mixed Q/K/V projection -> causal attention -> W^O + residual -> norm2
+//   -> FFN up + GELU -> FFN down + bias + residual
+// forward   : S and NS rows of each sample, K/V of all block rows, queries = tail S rows + NS rows
+// prefill   : S rows only, K/V written into the user's cache (Stage I)
+// score     : NS rows of each candidate, keys = user's cached S rows + own NS rows (Stage II)
+// append    : the new rows only, K/V appended to the cache, keys = cached + new rows
+//
+// Rows are addressed by (sequence b, position t) where t is the row's position in the current
+// block's input; the pyramid re-indexes the kept tail rows from 0 for the next block (the tail is
+// contiguous per sequence, so no copy is made).
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <vector>
+
+#include "onetrans.h"
+#include "common.hpp"
+#include "launch.hpp"
+
+using namespace ot;
+
+namespace {
+
+struct Dims {
+  int N, d, H, dh, dff, lns, dt;
+  size_t esz;
+  int layer;
+  float eps;
+  int tile;
+};
+
+inline bool misaligned(const void *p) { return ((uintptr_t)p & 15u) != 0; }
+
+int check_cfg(const onetrans_config *c, Dims &D) {
+  if (!c) return ONETRANS_ERR_INVALID_ARG;
+  if (c->n_blocks < 1 || c->d_model < 1 || c->n_heads < 1 || c->d_ff < 1 || c->l_ns < 0)
+    return ONETRANS_ERR_INVALID_ARG;
+  if (c->norm != ONETRANS_RMSNORM && c->norm != ONETRANS_LAYERNORM) return ONETRANS_ERR_INVALID_ARG;
+  if (c->dtype != ONETRANS_F32 && c->dtype != ONETRANS_BF16) return ONETRANS_ERR_INVALID_ARG;
+  if (!(c->norm_eps >= 0.0f) || !(c->norm_eps < 1.0f)) return ONETRANS_ERR_INVALID_ARG;
+  if (c->d_model % c->n_heads) return ONETRANS_ERR_SHAPE;
+  D.N = c->n_blocks;
+  D.d = c->d_model;
+  D.H = c->n_heads;
+  D.dh = c->d_model / c->n_heads;
+  D.dff = c->d_ff;
+  D.lns = c->l_ns;
+  D.dt = c->dtype;
+  D.esz = c->dtype == ONETRANS_BF16 ? 2 : 4;
+  D.layer = c->norm == ONETRANS_LAYERNORM;
+  D.eps = c->norm_eps;
+  if (D.dh != 16 && D.dh != 32) return ONETRANS_ERR_UNSUPPORTED;
+  if (D.d % 64 || D.d > 1024 || D.dff % 64) return ONETRANS_ERR_UNSUPPORTED;
+  if (D.lns > 32) return ONETRANS_ERR_UNSUPPORTED;
+  D.tile = (D.d % 128 == 0 && D.dff % 128 == 0) ? 1 : 0;
+  return ONETRANS_OK;
+}
+
+int check_schedule(const onetrans_config *c, int l_s) {
+  if (!c->s_queries) return ONETRANS_ERR_INVALID_ARG;
+  int s = l_s;
+  for (int n = 0; n < c->n_blocks; ++n) {
+    const int q = c->s_queries[n];
+    if (q < 1 || q > s) return ONETRANS_ERR_SHAPE;
+    s = q;
+  }
+  return ONETRANS_OK;
+}
+
+int check_weights(const onetrans_block_weights *blk, const Dims &D) {
+  if (!blk) return ONETRANS_ERR_INVALID_ARG;
+  for (int n = 0; n < D.N; ++n) {
+    const onetrans_block_weights &w = blk[n];
+    const void *req[] = {w.norm1_g, w.norm2_g, w.wq, w.wk, w.wv, w.wo, w.w1, w.b1, w.w2, w.b2};
+    for (const void *p : req) {
+      if (!p) return ONETRANS_ERR_INVALID_ARG;
+      if (misaligned(p)) return ONETRANS_ERR_ALIGNMENT;
+    }
+    if (D.layer) {
+      if (!w.norm1_b || !w.norm2_b) return ONETRANS_ERR_INVALID_ARG;
+      if (misaligned(w.norm1_b) || misaligned(w.norm2_b)) return ONETRANS_ERR_ALIGNMENT;
+    }
+  }
+  return ONETRANS_OK;
+}
+
+// ---- workspace -------------------------------------------------------------------------------
+struct Ws {
+  size_t x, xh, q, k, v, o, y, yh, hb, total;
+};
+
+inline size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// n: sequences; tin: max block input rows; rq: max query rows; kv: K/V buffers needed
+Ws ws_layout(const Dims &D, size_t n, size_t tin, size_t rq, bool kv) {
+  Ws w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += al(bytes);
+    return o;
+  };
+  const size_t d = D.d, es = D.esz;
+  w.x = take(n * rq * d * 4);
+  w.xh = take(n * tin * d * es);
+  w.q = take(n * rq * d * es);
+  w.k = kv ? take(n * tin * d * es) : 0;
+  w.v = kv ? take(n * tin * d * es) : 0;
+  w.o = take(n * rq * d * es);
+  w.y = take(n * rq * d * 4);
+  w.yh = take(n * rq * d * es);
+  w.hb = take(n * rq * (size_t)D.dff * es);
+  w.total = off;
+  return w;
+}
+
+bool ws_dims(const onetrans_config *c, const Dims &D, int op, int n_seq, int l_s, int n_cand, int d_l, size_t &n,
+             size_t &tin, size_t &rq, bool &kv) {
+  switch (op) {
+    case ONETRANS_OP_FORWARD:
+      if (n_seq < 1 || l_s < 1 || !c->s_queries) return false;
+      n = n_seq; tin = (size_t)l_s + D.lns; rq = (size_t)c->s_queries[0] + D.lns; kv = true;
+      return true;
+    case ONETRANS_OP_PREFILL:
+      if (n_seq < 1 || l_s < 1 || !c->s_queries) return false;
+      n = n_seq; tin = l_s; rq = c->s_queries[0]; kv = false;
+      return true;
+    case ONETRANS_OP_SCORE:
+      if (n_seq < 1 || n_cand < 1 || D.lns < 1) return false;
+      n = (size_t)n_seq * n_cand; tin = rq = D.lns; kv = true;
+      return true;
+    case ONETRANS_OP_APPEND:
+      if (n_seq < 1 || d_l < 1) return false;
+      n = n_seq; tin = rq = d_l; kv = false;
+      return true;
+    default:
+      return false;
+  }
+}
+
+// ---- launches ------------------------------------------------------------------------------
+struct JobSpec {
+  RowSet rs;
+  int n_seg;
+  const void *w[3];
+  HeadView oh[3];
+};
+
+int run_gemm(const Dims &D, int epi, int resid_f32, int N, int K, const JobSpec *jobs, int n_jobs, RowView a,
+             RowView out, RowView resid, const void *bias, hipStream_t st) {
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.N = N;
+  g.K = K;
+  g.d_head = D.dh;
+  g.a = a;
+  g.out = out;
+  g.resid = resid;
+  g.bias = bias;
+  const int BM = gemm_bm(D.tile), BN = gemm_bn(D.tile);
+  long long tiles = 0;
+  int nj = 0;
+  for (int i = 0; i < n_jobs; ++i) {
+    const JobSpec &j = jobs[i];
+    const long long m = (long long)j.rs.n_seq * j.rs.rows;
+    if (m == 0 || j.rs.n_groups == 0 || j.n_seg == 0) continue;
+    GemmJob &gj = g.job[nj++];
+    gj.rs = j.rs;
+    gj.n_seg = j.n_seg;
+    for (int s = 0; s < 3; ++s) {
+      gj.w[s] = j.w[s];
+      gj.out_heads[s] = j.oh[s];
+    }
+    gj.m_tiles = (int)((m + BM - 1) / BM);
+    gj.tile_start = (int)tiles;
+    tiles += (long long)gj.m_tiles * j.rs.n_groups * j.n_seg * (N / BN);
+  }
+  g.n_jobs = nj;
+  if (tiles == 0) return ONETRANS_OK;
+  if (tiles > 0x7fffffffLL) return ONETRANS_ERR_UNSUPPORTED;
+  return launch_gemm(D.dt, epi, resid_f32, D.tile, g, (int)tiles, st) == hipSuccess ? ONETRANS_OK
+                                                                                   : ONETRANS_ERR_HIP;
+}
+
+// One block over one operation's rows.
+struct Step {
+  int n_seq;
+  int s, q;            // S rows in the key range (positions 0..s-1); S query rows (tail)
+  int kv_t0, kv_n;     // S rows whose K/V are computed here
+  int ns;              // NS rows (positions s..s+ns-1), 0 if none
+  int in_t0, in_n;     // input rows present (positions)
+  RowView x;           // block input by position
+  int x_f32;
+  HeadView kS, vS, kN, vN;
+  int stage2, n_grp, n_cand, n_pre;
+  const void *kp, *vp;
+  long long pre_sb, pre_sh;
+  long long own_sb, own_sh;
+  RowView out;         // X' (fp32), t_off = first query position
+  bool need_out;
+};
+
+int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, char *ws, const Ws &L,
+             hipStream_t stream) {
+  const int d = D.d, H = D.H, dh = D.dh;
+  const int p0 = st.s - st.q;
+  const int R = st.q + st.ns;
+  char *xh = ws + L.xh, *qb = ws + L.q, *ob = ws + L.o, *yb = ws + L.y, *yhb = ws + L.yh, *hb = ws + L.hb;
+  int rc;
+
+  // norm1 over the input rows
+  {
+    NormArgs na;
+    na.n_seq = st.n_seq;
+    na.rows = st.in_n;
+    na.d = d;
+    na.in = st.x.base;
+    na.in_sb = st.x.sb;
+    na.in_i0 = st.in_t0 - st.x.t_off;
+    na.out = xh;
+    na.out_sb = (long long)st.in_n * d;
+    na.out_i0 = 0;
+    na.gamma = w.norm1_g;
+    na.beta = w.norm1_b;
+    na.layer = D.layer;
+    na.eps = D.eps;
+    if (launch_norm(D.dt, st.x_f32, na, stream) != hipSuccess) return ONETRANS_ERR_HIP;
+  }
+  const RowView xh_v{xh, (long long)st.in_n * d, st.in_t0, d};
+  const HeadView q_v{qb, (long long)H * R * dh, (long long)R * dh, p0};
+
+  // mixed Q/K/V projection
+  {
+    JobSpec jobs[3];
+    int nj = 0;
+    if (st.kv_n > 0) {
+      JobSpec &j = jobs[nj++];
+      j = JobSpec{};
+      j.rs = RowSet{st.n_seq, st.kv_n, 1, st.kv_t0, 0, 0};
+      j.n_seg = 2;
+      j.w[0] = w.wk; j.oh[0] = st.kS;
+      j.w[1] = w.wv; j.oh[1] = st.vS;
+    }
+    if (st.need_out && st.q > 0) {
+      JobSpec &j = jobs[nj++];
+      j = JobSpec{};
+      j.rs = RowSet{st.n_seq, st.q, 1, p0, 0, 0};
+      j.n_seg = 1;
+      j.w[0] = w.wq; j.oh[0] = q_v;
+    }
+    if (st.ns > 0) {
+      JobSpec &j = jobs[nj++];
+      j = JobSpec{};
+      j.rs = RowSet{st.n_seq, 1, st.ns, st.s, 1, 1};
+      j.n_seg = st.need_out ? 3 : 2;
+      j.w[0] = w.wk; j.oh[0] = st.kN;
+      j.w[1] = w.wv; j.oh[1] = st.vN;
+      j.w[2] = w.wq; j.oh[2] = q_v;
+    }
+    rc = run_gemm(D, EPI_HEADS, 0, d, d, jobs, nj, xh_v, RowView{}, RowView{}, nullptr, stream);
+    if (rc) return rc;
+  }
+  if (!st.need_out) return ONETRANS_OK;
+
+  // attention
+  {
+    AttnArgs a;
+    memset(&a, 0, sizeof(a));
+    a.n_heads = H;
+    a.d_model = d;
+    a.R = R;
+    a.p0 = p0;
+    a.n_pre = st.n_pre;
+    a.q = qb;
+    a.q_sb = q_v.sb;
+    a.q_sh = q_v.sh;
+    a.k_pre = st.kp;
+    a.v_pre = st.vp;
+    a.pre_sb = st.pre_sb;
+    a.pre_sh = st.pre_sh;
+    a.o = ob;
+    a.o_sb = (long long)R * d;
+    a.scale_log2 = 1.4426950408889634f / sqrtf((float)dh);
+    if (st.stage2) {
+      a.n_seq_grp = st.n_grp;
+      a.n_cand = st.n_cand;
+      a.k_own = st.kN.base;
+      a.v_own = st.vN.base;
+      a.own_sb = st.own_sb;
+      a.own_sh = st.own_sh;
+      const int cpw = 32 / st.ns;
+      a.n_qblocks = (st.n_cand + 4 * cpw - 1) / (4 * cpw);
+    } else {
+      a.n_seq_grp = st.n_seq;
+      a.n_qblocks = (R + ATTN_QBLOCK - 1) / ATTN_QBLOCK;
+    }
+    if (launch_attn(D.dt, dh, st.stage2, a, stream) != hipSuccess) return ONETRANS_ERR_HIP;
+  }
+
+  // projections of the query rows: S tail rows use set 0, NS token j uses set 1 + j
+  JobSpec pj[2];
+  int npj = 0;
+  if (st.q > 0) {
+    pj[npj] = JobSpec{};
+    pj[npj].rs = RowSet{st.n_seq, st.q, 1, p0, 0, 0};
+    pj[npj].n_seg = 1;
+    ++npj;
+  }
+  if (st.ns > 0) {
+    pj[npj] = JobSpec{};
+    pj[npj].rs = RowSet{st.n_seq, 1, st.ns, st.s, 1, 1};
+    pj[npj].n_seg = 1;
+    ++npj;
+  }
+  auto set_w = [&](const void *wp) {
+    for (int i = 0; i < npj; ++i) pj[i].w[0] = wp;
+  };
+  const RowView o_v{ob, (long long)R * d, p0, d};
+  const RowView y_v{yb, (long long)R * d, p0, d};
+  const RowView yh_v{yhb, (long long)R * d, p0, d};
+  const RowView h_v{hb, (long long)R * D.dff, p0, D.dff};
+
+  set_w(w.wo);
+  rc = run_gemm(D, EPI_RESID, st.x_f32, d, d, pj, npj, o_v, y_v, st.x, nullptr, stream);
+  if (rc) return rc;
+  {
+    NormArgs na;
+    na.n_seq = st.n_seq;
+    na.rows = R;
+    na.d = d;
+    na.in = yb;
+    na.in_sb = (long long)R * d;
+    na.in_i0 = 0;
+    na.out = yhb;
+    na.out_sb = (long long)R * d;
+    na.out_i0 = 0;
+    na.gamma = w.norm2_g;
+    na.beta = w.norm2_b;
+    na.layer = D.layer;
+    na.eps = D.eps;
+    if (launch_norm(D.dt, 1, na, stream) != hipSuccess) return ONETRANS_ERR_HIP;
+  }
+  set_w(w.w1);
+  rc = run_gemm(D, EPI_GELU, 0, D.dff, d, pj, npj, yh_v, h_v, RowView{}, w.b1, stream);
+  if (rc) return rc;
+  set_w(w.w2);
+  return run_gemm(D, EPI_RESID_BIAS, 1, d, D.dff, pj, npj, h_v, st.out, y_v, w.b2, stream);
+}
+
+int check_ws(const Dims &D, const Ws &L, void *ws, size_t ws_bytes) {
+  if (!ws) return ONETRANS_ERR_INVALID_ARG;
+  if (misaligned(ws)) return ONETRANS_ERR_ALIGNMENT;
+  if (ws_bytes < L.total) return ONETRANS_ERR_WORKSPACE;
+  (void)D;
+  return ONETRANS_OK;
+}
+
+int check_cache(const onetrans_kv_cache *c) {
+  if (!c || !c->k || !c->v || !c->layer_len) return ONETRANS_ERR_INVALID_ARG;
+  if (c->n_users < 1 || c->capacity < 1) return ONETRANS_ERR_INVALID_ARG;
+  if (misaligned(c->k) || misaligned(c->v)) return ONETRANS_ERR_ALIGNMENT;
+  return ONETRANS_OK;
+}
+
+// Cache views of block n: layout [user][block][head][capacity][d_head].
+inline HeadView cache_view(const Dims &D, const onetrans_kv_cache *c, void *base, int n) {
+  const long long per_head = (long long)c->capacity * D.dh;
+  return HeadView{(char *)base + (size_t)n * D.H * per_head * D.esz, (long long)D.N * D.H * per_head, per_head, 0};
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t onetrans_workspace_bytes(const onetrans_config *cfg, int op, int n_seq, int l_s, int n_cand, int d_l) {
+  Dims D;
+  if (check_cfg(cfg, D)) return 0;
+  size_t n, tin, rq;
+  bool kv;
+  if (!ws_dims(cfg, D, op, n_seq, l_s, n_cand, d_l, n, tin, rq, kv)) return 0;
+  if ((op == ONETRANS_OP_FORWARD || op == ONETRANS_OP_PREFILL) && check_schedule(cfg, l_s)) return 0;
+  return ws_layout(D, n, tin, rq, kv).total;
+}
+
+size_t onetrans_kv_cache_bytes(const onetrans_config *cfg, int n_users, int capacity) {
+  Dims D;
+  if (check_cfg(cfg, D) || n_users < 1 || capacity < 1) return 0;
+  return (size_t)n_users * D.N * D.H * (size_t)capacity * D.dh * D.esz;
+}
+
+int onetrans_forward(const onetrans_config *cfg, const onetrans_block_weights *blk, const void *x0, int batch,
+                     int l_s, void *out, void *ws, size_t ws_bytes, hipStream_t stream) {
+  Dims D;
+  int rc;
+  if ((rc = check_cfg(cfg, D))) return rc;
+  if (batch < 1 || l_s < 1) return ONETRANS_ERR_SHAPE;
+  if ((rc = check_schedule(cfg, l_s))) return rc;
+  if ((rc = check_weights(blk, D))) return rc;
+  if (!x0 || !out) return ONETRANS_ERR_INVALID_ARG;
+  if (misaligned(x0) || misaligned(out)) return ONETRANS_ERR_ALIGNMENT;
+  size_t n, tin, rq;
+  bool kv;
+  ws_dims(cfg, D, ONETRANS_OP_FORWARD, batch, l_s, 0, 0, n, tin, rq, kv);
+  const Ws L = ws_layout(D, n, tin, rq, kv);
+  if ((rc = check_ws(D, L, ws, ws_bytes))) return rc;
+
+  char *w = (char *)ws;
+  const int d = D.d, H = D.H, dh = D.dh;
+  int s = l_s;
+  RowView x{const_cast<void *>(x0), (long long)(l_s + D.lns) * d, 0, d};
+  int x_f32 = D.dt == ONETRANS_F32;
+  for (int n = 0; n < D.N; ++n) {
+    const int q = cfg->s_queries[n];
+    const int T = s + D.lns, R = q + D.lns, p0 = s - q;
+    Step st{};
+    st.n_seq = batch;
+    st.s = s;
+    st.q = q;
+    st.kv_t0 = 0;
+    st.kv_n = s;
+    st.ns = D.lns;
+    st.in_t0 = 0;
+    st.in_n = T;
+    st.x = x;
+    st.x_f32 = x_f32;
+    st.kS = HeadView{w + L.k, (long long)H * T * dh, (long long)T * dh, 0};
+    st.vS = HeadView{w + L.v, (long long)H * T * dh, (long long)T * dh, 0};
+    st.kN = st.kS;
+    st.vN = st.vS;
+    st.stage2 = 0;
+    st.n_pre = T;
+    st.kp = w + L.k;
+    st.vp = w + L.v;
+    st.pre_sb = (long long)H * T * dh;
+    st.pre_sh = (long long)T * dh;
+    st.out = RowView{n + 1 == D.N ? out : (void *)(w + L.x), (long long)R * d, p0, d};
+    st.need_out = true;
+    if ((rc = run_step(D, blk[n], st, w, L, stream))) return rc;
+    x = RowView{w + L.x, (long long)R * d, 0, d};
+    x_f32 = 1;
+    s = q;
+  }
+  return ONETRANS_OK;
+}
+
+int onetrans_prefill_user(const onetrans_config *cfg, const onetrans_block_weights *blk, const void *x_s,
+                          int n_users, int l_s, onetrans_kv_cache *cache, void *out_s, void *ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  Dims D;
+  int rc;
+  if ((rc = check_cfg(cfg, D))) return rc;
+  if (n_users < 1 || l_s < 1) return ONETRANS_ERR_SHAPE;
+  if ((rc = check_schedule(cfg, l_s))) return rc;
+  if ((rc = check_weights(blk, D))) return rc;
+  if (!x_s) return ONETRANS_ERR_INVALID_ARG;
+  if (misaligned(x_s) || (out_s && misaligned(out_s))) return ONETRANS_ERR_ALIGNMENT;
+  if ((rc = check_cache(cache))) return rc;
+  if (n_users > cache->n_users || l_s > cache->capacity) return ONETRANS_ERR_CACHE_CAPACITY;
+  size_t n, tin, rq;
+  bool kv;
+  ws_dims(cfg, D, ONETRANS_OP_PREFILL, n_users, l_s, 0, 0, n, tin, rq, kv);
+  const Ws L = ws_layout(D, n, tin, rq, kv);
+  if ((rc = check_ws(D, L, ws, ws_bytes))) return rc;
+
+  char *w = (char *)ws;
+  const int d = D.d;
+  int s = l_s;
+  RowView x{const_cast<void *>(x_s), (long long)l_s * d, 0, d};
+  int x_f32 = D.dt == ONETRANS_F32;
+  for (int n = 0; n < D.N; ++n) {
+    const int q = cfg->s_queries[n];
+    const int p0 = s - q;
+    const bool last = n + 1 == D.N;
+    Step st{};
+    st.n_seq = n_users;
+    st.s = s;
+    st.q = q;
+    st.kv_t0 = 0;
+    st.kv_n = s;
+    st.ns = 0;
+    st.in_t0 = 0;
+    st.in_n = s;
+    st.x = x;
+    st.x_f32 = x_f32;
+    st.kS = cache_view(D, cache, cache->k, n);
+    st.vS = cache_view(D, cache, cache->v, n);
+    st.kN = st.kS;
+    st.vN = st.vS;
+    st.stage2 = 0;
+    st.n_pre = s;
+    st.kp = st.kS.base;
+    st.vp = st.vS.base;
+    st.pre_sb = st.kS.sb;
+    st.pre_sh = st.kS.sh;
+    st.out = RowView{last ? out_s : (void *)(w + L.x), (long long)q * d, p0, d};
+    st.need_out = !last || out_s != nullptr;
+    if ((rc = run_step(D, blk[n], st, w, L, stream))) return rc;
+    x = RowView{w + L.x, (long long)q * d, 0, d};
+    x_f32 = 1;
+    s = q;
+  }
+  s = l_s;
+  for (int n = 0; n < D.N; ++n) {
+    cache->layer_len[n] = s;
+    s = cfg->s_queries[n];
+  }
+  return ONETRANS_OK;
+}
+
+int onetrans_score_candidates(const onetrans_config *cfg, const onetrans_block_weights *blk,
+                              const onetrans_kv_cache *cache, const void *x_ns, int n_users, int n_cand,
+                              void *out_ns, void *ws, size_t ws_bytes, hipStream_t stream) {
+  Dims D;
+  int rc;
+  if ((rc = check_cfg(cfg, D))) return rc;
+  if (n_users < 1 || n_cand < 1) return ONETRANS_ERR_SHAPE;
+  if (D.lns < 1) return ONETRANS_ERR_SHAPE;
+  if ((rc = check_weights(blk, D))) return rc;
+  if (!x_ns || !out_ns) return ONETRANS_ERR_INVALID_ARG;
+  if (misaligned(x_ns) || misaligned(out_ns)) return ONETRANS_ERR_ALIGNMENT;
+  if ((rc = check_cache(cache))) return rc;
+  if (n_users > cache->n_users) return ONETRANS_ERR_SHAPE;
+  for (int n = 0; n < D.N; ++n)
+    if (cache->layer_len[n] < 0 || cache->layer_len[n] > cache->capacity) return ONETRANS_ERR_SHAPE;
+  size_t n, tin, rq;
+  bool kv;
+  ws_dims(cfg, D, ONETRANS_OP_SCORE, n_users, 0, n_cand, 0, n, tin, rq, kv);
+  const Ws L = ws_layout(D, n, tin, rq, kv);
+  if ((rc = check_ws(D, L, ws, ws_bytes))) return rc;
+
+  char *w = (char *)ws;
+  const int d = D.d, H = D.H, dh = D.dh, ns = D.lns;
+  const int nseq = n_users * n_cand;
+  RowView x{const_cast<void *>(x_ns), (long long)ns * d, cache->layer_len[0], d};
+  int x_f32 = D.dt == ONETRANS_F32;
+  for (int n = 0; n < D.N; ++n) {
+    const int s = cache->layer_len[n];
+    Step st{};
+    st.n_seq = nseq;
+    st.s = s;
+    st.q = 0;
+    st.kv_t0 = 0;
+    st.kv_n = 0;
+    st.ns = ns;
+    st.in_t0 = s;
+    st.in_n = ns;
+    x.t_off = s;
+    st.x = x;
+    st.x_f32 = x_f32;
+    st.kN = HeadView{w + L.k, (long long)H * ns * dh, (long long)ns * dh, s};
+    st.vN = HeadView{w + L.v, (long long)H * ns * dh, (long long)ns * dh, s};
+    st.kS = st.kN;
+    st.vS = st.vN;
+    const HeadView cv = cache_view(D, cache, cache->k, n);
+    st.stage2 = 1;
+    st.n_grp = n_users;
+    st.n_cand = n_cand;
+    st.n_pre = s;
+    st.kp = cv.base;
+    st.vp = cache_view(D, cache, cache->v, n).base;
+    st.pre_sb = cv.sb;
+    st.pre_sh = cv.sh;
+    st.own_sb = st.kN.sb;
+    st.own_sh = st.kN.sh;
+    st.out = RowView{n + 1 == D.N ? out_ns : (void *)(w + L.x), (long long)ns * d, s, d};
+    st.need_out = true;
+    if ((rc = run_step(D, blk[n], st, w, L, stream))) return rc;
+    x = RowView{w + L.x, (long long)ns * d, 0, d};
+    x_f32 = 1;
+  }
+  return ONETRANS_OK;
+}
+
+int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weights *blk, onetrans_kv_cache *cache,
+                           const void *x_new, int n_users, int d_l, void *out_new, void *ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  Dims D;
+  int rc;
+  if ((rc = check_cfg(cfg, D))) return rc;
+  if (n_users < 1 || d_l < 1) return ONETRANS_ERR_SHAPE;
+  if ((rc = check_weights(blk, D))) return rc;
+  if (!x_new) return ONETRANS_ERR_INVALID_ARG;
+  if (misaligned(x_new) || (out_new && misaligned(out_new))) return ONETRANS_ERR_ALIGNMENT;
+  if ((rc = check_cache(cache))) return rc;
+  if (n_users > cache->n_users) return ONETRANS_ERR_SHAPE;
+  const int l_old = cache->layer_len[0];
+  for (int n = 0; n < D.N; ++n) {
+    if (cache->layer_len[n] < 0 || cache->layer_len[n] > cache->capacity) return ONETRANS_ERR_SHAPE;
+    if (cache->layer_len[n] != l_old) return ONETRANS_ERR_UNSUPPORTED;
+  }
+  if ((long long)l_old + d_l > cache->capacity) return ONETRANS_ERR_CACHE_CAPACITY;
+  size_t n, tin, rq;
+  bool kv;
+  ws_dims(cfg, D, ONETRANS_OP_APPEND, n_users, 0, 0, d_l, n, tin, rq, kv);
+  const Ws L = ws_layout(D, n, tin, rq, kv);
+  if ((rc = check_ws(D, L, ws, ws_bytes))) return rc;
+
+  char *w = (char *)ws;
+  const int d = D.d;
+  RowView x{const_cast<void *>(x_new), (long long)d_l * d, l_old, d};
+  int x_f32 = D.dt == ONETRANS_F32;
+  for (int n = 0; n < D.N; ++n) {
+    const bool last = n + 1 == D.N;
+    Step st{};
+    st.n_seq = n_users;
+    st.s = l_old + d_l;
+    st.q = d_l;
+    st.kv_t0 = l_old;
+    st.kv_n = d_l;
+    st.ns = 0;
+    st.in_t0 = l_old;
+    st.in_n = d_l;
+    st.x = x;
+    st.x_f32 = x_f32;
+    st.kS = cache_view(D, cache, cache->k, n);
+    st.vS = cache_view(D, cache, cache->v, n);
+    st.kN = st.kS;
+    st.vN = st.vS;
+    st.stage2 = 0;
+    st.n_pre = l_old + d_l;
+    st.kp = st.kS.base;
+    st.vp = st.vS.base;
+    st.pre_sb = st.kS.sb;
+    st.pre_sh = st.kS.sh;
+    st.out = RowView{last && out_new ? out_new : (void *)(w + L.x), (long long)d_l * d, l_old, d};
+    st.need_out = !last || out_new != nullptr;
+    if ((rc = run_step(D, blk[n], st, w, L, stream))) return rc;
+    x = RowView{w + L.x, (long long)d_l * d, l_old, d};
+    x_f32 = 1;
+  }
+  for (int n = 0; n < D.N; ++n) cache->layer_len[n] = l_old + d_l;
+  return ONETRANS_OK;
+}
+
+const char *onetrans_status_string(int status) {
+  switch (status) {
+    case ONETRANS_OK: return "ok";
+    case ONETRANS_ERR_INVALID_ARG: return "invalid argument";
+    case ONETRANS_ERR_SHAPE: return "inconsistent shape or pyramid schedule";
+    case ONETRANS_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ONETRANS_ERR_WORKSPACE: return "workspace too small";
+    case ONETRANS_ERR_CACHE_CAPACITY: return "kv cache capacity exceeded";
+    case ONETRANS_ERR_ALIGNMENT: return "device pointer not 16-byte aligned";
+    case ONETRANS_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char *onetrans_version(void) { return "onetrans-gfx950 0.1"; }
+
+}  // extern "C"
