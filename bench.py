@@ -1,0 +1,299 @@
+"""Benchmark of the OneTrans hot path on one MI355X.
+
+Default workload: the OneTransS-shaped forward (6 blocks, d=256, 8 heads, FFN 1024, L_S=1190,
+L_NS=16, pyramid 1190 -> 12, batch 256, bf16 storage with fp32 accumulation). One step is one
+onetrans_forward call over the whole batch: every block's norm, mixed Q/K/V projection, causal
+pyramid attention, output projection and mixed FFN. The metric is candidates scored per second
+(each batch row is one candidate carrying its own user sequence) plus the fraction of bf16 MFMA
+peak that the algorithmic FLOPs reach.
+
+Other workloads (--workload two_stage | append | onetrans_l) print their own line; they are
+parity cases of the same kernels and are measured for the design notes, not as the headline.
+
+Timing: W untimed warm-up steps, then K timed steps between a device synchronisation on both
+sides (one GPU, so no barrier is needed). Inputs and weights are resident in HBM before the
+timed region starts. Per-kernel device time comes from hipEvents the library records around each
+launch on the call's stream during the timed region. The CPU baseline times the fp64 oracle on a
+bounded sample of the same workload on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 (matrix and packed vector)
+PEAK_HBM_GBS = 8000.0
+METRIC = "candidates scored/sec at 1 GPU (OneTransS shape) + % bf16 MFMA peak"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="onetrans_s",
+                   choices=["onetrans_s", "two_stage", "append", "onetrans_l"])
+    p.add_argument("--dtype", default=None, choices=[None, "bf16", "f32"])
+    p.add_argument("--no-trace", action="store_true", help="no per-kernel events in the timed region")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline (0: skip)")
+    return p.parse_args()
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def roofline_entry(name, work, ms, launches, peak, unit, bound):
+    achieved = work / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
+    return {"kernel": name, "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": None, "avg_launch_us": round(1e3 * ms / max(launches, 1), 2),
+            "launches": launches}
+
+
+def kernel_table(classes, timing, steps, n_units, peak_tflops, store_bytes):
+    """Per class: algorithmic work per step over measured time per step."""
+    out = {}
+    for k, (ms, cnt) in timing.items():
+        if cnt == 0:
+            continue
+        ms_step = ms / steps
+        if k == "norm":
+            gbs = classes["norm_bytes"] * n_units / (ms_step * 1e-3) / 1e9
+            out[k] = {"ms_per_step": round(ms_step, 4), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                      "launches_per_step": cnt // steps}
+        else:
+            tf = classes[k] * n_units / (ms_step * 1e-3) / 1e12
+            out[k] = {"ms_per_step": round(ms_step, 4), "TFLOP/s": round(tf, 2), "frac_mfma": round(tf / peak_tflops, 4),
+                      "launches_per_step": cnt // steps}
+    return out
+
+
+def dominant(classes, timing, steps, n_units, peak_tflops):
+    k = max((c for c in timing if timing[c][1] > 0), key=lambda c: timing[c][0])
+    ms, cnt = timing[k]
+    if k == "norm":
+        return roofline_entry(k, classes["norm_bytes"] * n_units * steps, ms, cnt, PEAK_HBM_GBS, "GB/s", "hbm")
+    return roofline_entry(k, classes[k] * n_units * steps, ms, cnt, peak_tflops, "TFLOP/s", "mfma")
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {a.gpus}); samples are independent, "
+              "so N GPUs would each run this same per-GPU step on their own share of the batch.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from unified_transformer_recommender_amd import binding as ob
+    from unified_transformer_recommender_amd import costmodel as cm
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = synth.workload(a.workload, a.dtype)
+    m = w.model
+    store_bytes = 2 if m.dtype == "bf16" else 4
+    peak = PEAK_BF16_TFLOPS if m.dtype == "bf16" else PEAK_FP32_TFLOPS
+    t_setup = time.time()
+    host_w = synth.make_weights(m)
+    sched = w.s_queries if w.kind != "append" else (w.l_old,) * m.n_blocks
+    model = ob.Model.from_host(m, sched, host_w, device=dev)
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev, dtype=model.torch_dtype)
+
+    stream = torch.cuda.current_stream(dev)
+    extra = {}
+    if w.kind == "forward":
+        x0 = up(synth.forward_batch(w))
+        out = torch.empty((w.batch, w.s_queries[-1] + m.l_ns, m.d_model), dtype=torch.float32, device=dev)
+        wsp = model.workspace(ob.L.OP_FORWARD, w.batch, w.l_s)
+        n_units = w.batch
+        classes = cm.forward_classes(m.d_model, m.d_ff, m.l_ns, w.l_s, w.s_queries, store_bytes)
+
+        def step():
+            ob.onetrans_forward(model, x0, out, wsp)
+    elif w.kind == "two_stage":
+        xs = up(synth.user_sequences(w))
+        xn = up(synth.candidate_batch(w))
+        cache = ob.KVCache(model, w.n_users, w.l_s)
+        out = torch.empty((w.n_users, w.n_cand, m.l_ns, m.d_model), dtype=torch.float32, device=dev)
+        ws1 = model.workspace(ob.L.OP_PREFILL, w.n_users, w.l_s)
+        ws2 = model.workspace(ob.L.OP_SCORE, w.n_users, n_cand=w.n_cand)
+        n_units = w.n_users * w.n_cand
+        pre = cm.prefill_classes(m.d_model, m.d_ff, w.l_s, w.s_queries, store_bytes)
+        sc = cm.score_classes(m.d_model, m.d_ff, m.l_ns, w.l_s, w.s_queries, store_bytes)
+        classes = {k: (pre[k] * w.n_users + sc[k] * n_units) / n_units for k in sc}
+
+        def step():
+            ob.onetrans_prefill_user(model, xs, cache, None, ws1)
+            ob.onetrans_score_candidates(model, cache, xn, out, ws2)
+    else:   # append: restore the pristine cache (untimed), then append + score the user's NS tokens
+        old, new = synth.append_batch(w)
+        xo, xnw = up(old), up(new)
+        xn = up(np.stack([synth.candidate_tokens(w, u, 0) for u in range(w.n_users)])[:, None])
+        pristine = ob.KVCache(model, w.n_users, w.l_s)
+        ob.onetrans_prefill_user(model, xo, pristine)
+        cache = ob.KVCache(model, w.n_users, w.l_s)
+        out_new = torch.empty((w.n_users, w.d_l, m.d_model), dtype=torch.float32, device=dev)
+        out = torch.empty((w.n_users, 1, m.l_ns, m.d_model), dtype=torch.float32, device=dev)
+        ws1 = model.workspace(ob.L.OP_APPEND, w.n_users, d_l=w.d_l)
+        ws2 = model.workspace(ob.L.OP_SCORE, w.n_users, n_cand=1)
+        n_units = w.n_users
+        ap = cm.append_classes(m.d_model, m.d_ff, m.n_blocks, w.l_old, w.d_l, store_bytes)
+        sc = cm.score_classes(m.d_model, m.d_ff, m.l_ns, w.l_old + w.d_l, (w.l_old + w.d_l,) * m.n_blocks,
+                              store_bytes)
+        classes = {k: ap[k] + sc[k] for k in sc}
+        restore_ms = []
+
+        def step():
+            ob.onetrans_append_events(model, cache, xnw, out_new, ws1)
+            ob.onetrans_score_candidates(model, cache, xn, out, ws2)
+
+        def restore():
+            cache.copy_(pristine)
+
+    torch.cuda.synchronize()
+    t_setup = time.time() - t_setup
+
+    # warm-up
+    for _ in range(a.warmup):
+        if w.kind == "append":
+            restore()
+        step()
+    torch.cuda.synchronize()
+    ob.timing_read()                        # drop anything recorded so far
+
+    # timed region
+    ob.timing_enable(not a.no_trace)
+    total_ms = 0.0
+    if w.kind == "append":
+        # the cache restore between steps is outside the timed intervals
+        for _ in range(a.steps):
+            restore()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            total_ms += e0.elapsed_time(e1)
+    else:
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(a.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3
+        total_ms = max(e0.elapsed_time(e1), 0.0)
+        extra["wall_ms_per_step"] = round(wall / a.steps, 4)
+    ob.timing_enable(False)
+    timing = ob.timing_read()
+    ms_step = total_ms / a.steps
+    if a.no_trace:
+        # per-kernel table from a separate traced pass after the timed region
+        ob.timing_enable(True)
+        for _ in range(a.steps):
+            if w.kind == "append":
+                restore()
+            step()
+        torch.cuda.synchronize()
+        ob.timing_enable(False)
+        timing = ob.timing_read()
+        if w.kind == "append":     # the restores are copies outside the library: not in the table
+            pass
+    value = n_units / (ms_step * 1e-3)
+
+    flops_unit = sum(v for k, v in classes.items() if k != "norm_bytes")
+    mfma_frac = flops_unit * n_units / (ms_step * 1e-3) / 1e12 / peak
+    kernels = kernel_table(classes, timing, a.steps, n_units, peak, store_bytes)
+    roof = dominant(classes, timing, a.steps, n_units, peak)
+
+    # CPU baseline: the oracle on a bounded sample of the same workload
+    cpu = None
+    if a.cpu_seconds > 0:
+        import oracle as O
+        t0 = time.perf_counter()
+        done = 0
+        if w.kind == "forward":
+            while done < 64 and (time.perf_counter() - t0 < a.cpu_seconds or done < 2):
+                O.forward(synth.forward_sample(w, done), host_w, m, w.s_queries)
+                done += 1
+            sample = f"{done} samples of the same workload, one at a time"
+            units = done
+        elif w.kind == "two_stage":
+            cache_o, _ = O.prefill_user(synth.user_sequence(w, 0), host_w, m, w.s_queries)
+            while done < 2048 and (time.perf_counter() - t0 < a.cpu_seconds or done < 4):
+                O.score_candidate(cache_o, synth.candidate_tokens(w, 0, done), host_w, m)
+                done += 1
+            sample = f"Stage I of user 0 plus Stage II of {done} of its candidates, both timed"
+            units = done
+        else:
+            t_app = 0.0
+            while done < 64 and (time.perf_counter() - t0 < a.cpu_seconds or done < 2):
+                o, nw = synth.append_rows(w, done)
+                co, _ = O.prefill_user(o, host_w, m, (w.l_old,) * m.n_blocks)
+                t1 = time.perf_counter()
+                O.append_events(co, nw, host_w, m)
+                t_app += time.perf_counter() - t1
+                done += 1
+            sample = f"{done} users' appends (their Stage I prefill runs untimed)"
+            units = done
+        cpu_s = time.perf_counter() - t0 if w.kind != "append" else t_app
+        cpu = {"value": round(units / cpu_s, 4), "unit": "candidates/s" if w.kind != "append" else "users/s",
+               "cores": blas_threads(), "kind": "oracle", "sample": sample, "seconds": round(cpu_s, 2)}
+
+    unit = "candidates/s" if w.kind != "append" else "user appends/s"
+    line = {
+        "metric": METRIC if w.key == "onetrans_s" else f"{unit} at 1 GPU ({w.key})",
+        "value": round(value, 2),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": m.dtype,
+        "data": "synthetic (seeded N(0,1) inputs with shared [SEP] rows, N(0,0.02^2) weights)",
+        "config": {"workload": w.description, "batch": w.batch or None, "n_users": w.n_users or None,
+                   "n_cand": w.n_cand or None, "l_s": w.l_s, "l_ns": m.l_ns, "s_queries": list(sched),
+                   "n_blocks": m.n_blocks, "d_model": m.d_model, "n_heads": m.n_heads, "d_ff": m.d_ff},
+        "mfma_frac": round(mfma_frac, 4),
+        "tflops": round(flops_unit * n_units / (ms_step * 1e-3) / 1e12, 2),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "trace_in_timed_region": not a.no_trace,
+        "setup_s": round(t_setup, 1),
+        **extra,
+    }
+    if w.kind == "append":
+        byts = cm.append_cache_bytes(m.d_model, m.n_blocks, w.l_old, w.d_l, store_bytes) * n_units
+        line["cache_GB/s"] = round(byts / (ms_step * 1e-3) / 1e9, 1)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

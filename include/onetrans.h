@@ -27,8 +27,8 @@
  *   - Weight matrices are (out, in) row-major, like torch.nn.Linear: y = W x. Each matrix is
  *     stored as [1 + l_ns][rows][cols]: index 0 is the shared S set, 1 + j is NS token j.
  *   - No exceptions cross the boundary; every entry point returns an onetrans_status.
- *   - Supported shapes: d_head = d_model / n_heads in {16, 32}; d_model and d_ff multiples of 64,
- *     d_model <= 1024; 0 <= l_ns <= 32 (>= 1 for score_candidates).
+ *   - Supported shapes: d_head = d_model / n_heads in {16, 32}; d_model in {64, 128, 256, 512};
+ *     d_ff a multiple of 64; 0 <= l_ns <= 32 (>= 1 for score_candidates).
  */
 #ifndef ONETRANS_H_
 #define ONETRANS_H_
@@ -144,6 +144,23 @@ int onetrans_score_candidates(const onetrans_config *cfg, const onetrans_block_w
 int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weights *blk,
                            onetrans_kv_cache *cache, const void *x_new, int n_users, int d_l,
                            void *out_new, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Kernel classes of the per-launch timing below. */
+typedef enum {
+  ONETRANS_K_NORM = 0,       /* pre-norm 1 and 2 */
+  ONETRANS_K_QKV = 1,        /* mixed Q/K/V projection */
+  ONETRANS_K_ATTN = 2,       /* causal / Stage II attention */
+  ONETRANS_K_POST = 3,       /* fused W^O + residual + pre-norm 2 + mixed FFN + residual */
+  ONETRANS_K_COUNT = 4
+} onetrans_kernel_class;
+
+/* Per-launch device timing (tracing aid). While enabled, the library brackets every kernel launch
+ * with a pair of hipEvents recorded on the call's stream. onetrans_timing_read() waits for the
+ * recorded events, adds each pair's elapsed time to ms[class] and counts launches[class]
+ * (arrays of ONETRANS_K_COUNT entries, host), then forgets the pairs. Off by default; not
+ * thread-safe (one caller at a time). Returns ONETRANS_ERR_HIP if an event call fails. */
+int onetrans_timing_enable(int on);
+int onetrans_timing_read(double *ms, long long *launches);
 
 /* Static text for a status code. */
 const char *onetrans_status_string(int status);

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert "onetrans_forward" in names and len(names) == 8
+    assert "onetrans_forward" in names and len(names) == 10
     lib = L.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -54,10 +54,10 @@ def test_workspace_and_cache_sizes():
     c = _cfg()
     B, l_s = 4, 120
     got = lib.onetrans_workspace_bytes(ctypes.byref(c), L.OP_FORWARD, B, l_s, 0, 0)
-    d, dff, T, R = 256, 1024, 136, 116
+    d, T, R = 256, 136, 116
     al = lambda n: (n + 255) // 256 * 256
-    expect = (al(B * R * d * 4) + al(B * T * d * 2) + al(B * R * d * 2) + 2 * al(B * T * d * 2)
-              + al(B * R * d * 2) + al(B * R * d * 4) + al(B * R * d * 2) + al(B * R * dff * 2))
+    expect = (2 * al(B * R * d * 4) + al(B * T * d * 2) + al(B * R * d * 2) + 2 * al(B * T * d * 2)
+              + al(B * R * d * 2))
     assert got == expect
     assert lib.onetrans_kv_cache_bytes(ctypes.byref(c), 3, 200) == 3 * 2 * 8 * 200 * 32 * 2
     assert lib.onetrans_workspace_bytes(ctypes.byref(c), L.OP_SCORE, 2, 0, 5, 0) > 0
@@ -87,6 +87,7 @@ def test_forward_validation_errors():
     assert _fwd(_cfg(sq=(100, 0)), b) == L.ERR_SHAPE
     assert _fwd(_cfg(d=256, H=4), b) == L.ERR_UNSUPPORTED            # d_head 64
     assert _fwd(_cfg(d=96, H=3), b) == L.ERR_UNSUPPORTED             # d not a multiple of 64
+    assert _fwd(_cfg(d=192, H=6), b) == L.ERR_UNSUPPORTED            # d outside {64, 128, 256, 512}
     assert _fwd(_cfg(d=256, H=7), b) == L.ERR_SHAPE                  # d % H != 0
     assert _fwd(_cfg(lns=40), b) == L.ERR_UNSUPPORTED
     assert _fwd(_cfg(dtype=7), b) == L.ERR_INVALID_ARG

@@ -73,3 +73,12 @@ def test_mixed_parameter_count_order():
     a = cm.mixed_param_count(256, 1024, 16)
     b = cm.mixed_param_count(256, 1024, 32)
     assert b / a == pytest.approx(33 / 17)
+
+
+def test_kernel_classes_sum_to_forward_work():
+    w = synth.workload("onetrans_s")
+    m = w.model
+    c = cm.forward_classes(m.d_model, m.d_ff, m.l_ns, w.l_s, w.s_queries, 2)
+    fw = cm.forward_work(m.d_model, m.d_ff, m.l_ns, w.l_s, w.s_queries)
+    assert c["qkv"] + c["post"] == pytest.approx(fw.gemm)
+    assert c["attn"] == pytest.approx(fw.attn)

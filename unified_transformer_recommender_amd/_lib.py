@@ -20,6 +20,7 @@ ERR_HIP = -7
 F32, BF16 = 0, 1
 RMSNORM, LAYERNORM = 0, 1
 OP_FORWARD, OP_PREFILL, OP_SCORE, OP_APPEND = 0, 1, 2, 3
+KERNEL_CLASSES = ("norm", "qkv", "attn", "post")
 
 WEIGHT_FIELDS = ("norm1_g", "norm1_b", "norm2_g", "norm2_b", "wq", "wk", "wv", "wo", "w1", "b1", "w2", "b2")
 
@@ -49,6 +50,8 @@ SIGNATURES = {
                                           c_int, c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
     "onetrans_append_events": (c_int, [POINTER(Config), POINTER(BlockWeights), POINTER(KVCache), c_void_p,
                                        c_int, c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "onetrans_timing_enable": (c_int, [c_int]),
+    "onetrans_timing_read": (c_int, [POINTER(ctypes.c_double), POINTER(ctypes.c_longlong)]),
     "onetrans_status_string": (c_char_p, [c_int]),
     "onetrans_version": (c_char_p, []),
 }

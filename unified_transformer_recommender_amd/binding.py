@@ -176,3 +176,17 @@ def onetrans_append_events(model: Model, cache: KVCache, x_new: torch.Tensor,
                                         _stream(x_new.device, stream))
     L.check(st, "onetrans_append_events")
     return out_new
+
+
+def timing_enable(on: bool = True) -> None:
+    """Bracket every library kernel launch with hipEvents on its stream (tracing aid)."""
+    L.check(L.lib().onetrans_timing_enable(1 if on else 0), "onetrans_timing_enable")
+
+
+def timing_read() -> dict:
+    """{class: (total device ms, launches)} accumulated since the last read."""
+    n = len(L.KERNEL_CLASSES)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_longlong * n)()
+    L.check(L.lib().onetrans_timing_read(ms, cnt), "onetrans_timing_read")
+    return {k: (ms[i], int(cnt[i])) for i, k in enumerate(L.KERNEL_CLASSES)}

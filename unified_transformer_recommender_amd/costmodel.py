@@ -104,3 +104,68 @@ def mixed_param_count(d: int, d_ff: int, l_ns: int, with_wo: bool = True) -> int
     O(L_NS d^2 + d^2) ([en] 7.5.1, comparison with a per-token FFN)."""
     per_set = (4 if with_wo else 3) * d * d + 2 * d * d_ff + d_ff + d
     return (1 + l_ns) * per_set
+
+
+# --- per kernel class (the launch sequence of one block) --------------------------------------
+
+KERNEL_CLASSES = ("norm", "qkv", "attn", "post")
+
+
+def _block_classes(d, d_ff, kv_rows, q_rows, first_query_pos, in_rows, in_bytes, store_bytes):
+    """Algorithmic flops (GEMM/attention classes) and bytes (norm) of one block for one sequence.
+
+    "post" is the fused tail of the block: W^O projection plus both FFN projections."""
+    return {
+        "qkv": 2.0 * d * d * (2 * kv_rows + q_rows),
+        "attn": 4.0 * d * visible_pairs(first_query_pos, q_rows),
+        "post": 2.0 * d * d * q_rows + 2.0 * 2 * d * d_ff * q_rows,
+        # pre-norm 1 reads every input row and writes it normalised in the storage dtype
+        "norm_bytes": float(d * in_rows * (in_bytes + store_bytes)),
+    }
+
+
+def forward_classes(d, d_ff, l_ns, l_s, s_queries, store_bytes):
+    """Per-candidate work of the monolithic forward split by kernel class (norm in bytes)."""
+    tot, s = {}, l_s
+    for n, q in enumerate(s_queries):
+        in_bytes = store_bytes if n == 0 else 4
+        c = _block_classes(d, d_ff, s + l_ns, q + l_ns, s - q, s + l_ns, in_bytes, store_bytes)
+        for k, v in c.items():
+            tot[k] = tot.get(k, 0.0) + v
+        s = q
+    return tot
+
+
+def prefill_classes(d, d_ff, l_s, s_queries, store_bytes):
+    tot, s = {}, l_s
+    for n, q in enumerate(s_queries):
+        c = _block_classes(d, d_ff, s, q, s - q, s, store_bytes if n == 0 else 4, store_bytes)
+        for k, v in c.items():
+            tot[k] = tot.get(k, 0.0) + v
+        s = q
+    return tot
+
+
+def score_classes(d, d_ff, l_ns, l_s, s_queries, store_bytes):
+    tot, s = {}, l_s
+    for n, q in enumerate(s_queries):
+        c = _block_classes(d, d_ff, l_ns, l_ns, s, l_ns, store_bytes if n == 0 else 4, store_bytes)
+        for k, v in c.items():
+            tot[k] = tot.get(k, 0.0) + v
+        s = q
+    return tot
+
+
+def append_classes(d, d_ff, n_blocks, l_old, d_l, store_bytes):
+    tot = {}
+    for n in range(n_blocks):
+        c = _block_classes(d, d_ff, d_l, d_l, l_old, d_l, store_bytes if n == 0 else 4, store_bytes)
+        for k, v in c.items():
+            tot[k] = tot.get(k, 0.0) + v
+    return tot
+
+
+def append_cache_bytes(d, n_blocks, l_old, d_l, store_bytes):
+    """K/V cache bytes one user's append must read (every cached row of every block, K and V)
+    plus the new rows it writes: the HBM floor of the append path."""
+    return float(n_blocks * 2 * d * store_bytes * (l_old + d_l) + n_blocks * 2 * d * store_bytes * d_l)

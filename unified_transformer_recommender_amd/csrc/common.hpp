@@ -91,31 +91,48 @@ struct HeadView {
 };
 
 // ---------------------------------------------------------------------------------------------
-// Mixed-parameter GEMM launch: C[r][n] = sum_k A[r][k] * W_g[n][k] for each job's rows,
+// Mixed-parameter GEMM launch (Q/K/V): C[r][n] = sum_k A[r][k] * W_g[n][k] for each job's rows,
 // with W_g the parameter set of the row's group. N columns per segment; a job has up to three
 // segments (Q, K, V) that share the A rows and differ in weights and output.
 // ---------------------------------------------------------------------------------------------
-enum EpiKind { EPI_HEADS = 0, EPI_RESID = 1, EPI_GELU = 2, EPI_RESID_BIAS = 3 };
-
 struct GemmJob {
   RowSet rs;
   int n_seg;
   int tile_start;          // first workgroup of this job
   int m_tiles;             // per group
   const void *w[3];        // segment weight base: [G][N][K] storage dtype
-  HeadView out_heads[3];   // EPI_HEADS outputs per segment
+  HeadView out_heads[3];   // head-split output per segment
 };
 
 struct GemmArgs {
   int n_jobs;
   int N, K;
-  int d_head;              // EPI_HEADS: columns per head
+  int d_head;              // columns per head of the outputs
   GemmJob job[3];
   RowView a;               // A operand rows (storage dtype)
-  // epilogue operands
-  RowView out;             // EPI_RESID / EPI_GELU / EPI_RESID_BIAS output
-  RowView resid;           // residual input (EPI_RESID: TR dtype; EPI_RESID_BIAS: fp32)
-  const void *bias;        // [G][N] storage dtype (EPI_GELU, EPI_RESID_BIAS)
+};
+
+// ---------------------------------------------------------------------------------------------
+// Fused post-attention launch (W^O + residual + norm2 + mixed FFN + residual) over the query rows
+// of a block: job 0 = tail S rows (parameter set 0), job 1 = NS rows (sets 1..l_ns).
+// ---------------------------------------------------------------------------------------------
+struct PostJob {
+  RowSet rs;
+  int tile_start;          // first workgroup of this job
+  int m_tiles;             // token tiles per group
+};
+
+struct PostArgs {
+  int n_jobs;
+  PostJob job[2];
+  int d_model, d_ff;
+  RowView o;               // attention output rows (storage dtype)
+  RowView resid;           // block input rows (storage dtype in block 0, else fp32)
+  RowView out;             // X' rows (fp32)
+  const void *wo, *w1, *b1, *w2, *b2;   // [G][..] storage dtype
+  const void *gamma, *beta;             // norm2 [d]
+  int layer;
+  float eps;
 };
 
 // ---------------------------------------------------------------------------------------------

@@ -13,11 +13,8 @@
 // kt+1 are issued before the MFMAs of k-tile kt, stored to the other buffer afterwards, and one
 // barrier per k-tile separates the two.
 //
-// Epilogues (per element of the fp32 accumulator):
-//   EPI_HEADS      -> head-split Q/K/V (or K/V cache) rows in the storage dtype
-//   EPI_RESID      -> y = acc + x_residual (fp32 out)                       attention output proj.
-//   EPI_GELU       -> h = GELU(acc + b1_g) (storage dtype out), exact erf   FFN up
-//   EPI_RESID_BIAS -> x' = acc + b2_g + y (fp32 out)                        FFN down
+// Epilogue: each fp32 accumulator is rounded to the storage dtype and written to its head-split
+// Q/K/V (or K/V cache) row.
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -39,7 +36,7 @@ struct GemmTile {
 
 __device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
 
-template <typename T, int BM, int BN, int BK, int EPI, typename TR>
+template <typename T, int BM, int BN, int BK>
 __global__ __launch_bounds__(256) void mixed_gemm_kernel(const GemmArgs args) {
   using G = GemmTile<T, BM, BN, BK>;
   using M = Mma<T>;
@@ -154,8 +151,7 @@ __global__ __launch_bounds__(256) void mixed_gemm_kernel(const GemmArgs args) {
     __syncthreads();
   }
 
-  // ---- epilogue ---------------------------------------------------------------------------
-  const T *bias = (const T *)args.bias + (size_t)wgrp * N;
+  // ---- epilogue: head-split rows ------------------------------------------------------------
 #pragma unroll
   for (int i = 0; i < G::TM; ++i) {
 #pragma unroll
@@ -164,64 +160,26 @@ __global__ __launch_bounds__(256) void mixed_gemm_kernel(const GemmArgs args) {
       const int b = s_b[row];
       if (b < 0) continue;
       const int t = s_t[row];
+      const HeadView &hv = jb.out_heads[seg];
 #pragma unroll
       for (int j = 0; j < G::TN; ++j) {
         const int col = n0 + wn * G::WN + j * 32 + lc;
-        const float val = acc[i][j][v];
-        if constexpr (EPI == EPI_HEADS) {
-          const HeadView &hv = jb.out_heads[seg];
-          const int h = col / d_head, c = col - h * d_head;
-          ((T *)hv.base)[b * hv.sb + h * hv.sh + (long long)(t - hv.t_off) * d_head + c] = from_f32<T>(val);
-        } else if constexpr (EPI == EPI_RESID) {
-          const TR *xr = (const TR *)args.resid.base + b * args.resid.sb + (long long)(t - args.resid.t_off) * args.resid.rs;
-          ((float *)args.out.base)[b * args.out.sb + (long long)(t - args.out.t_off) * args.out.rs + col] =
-              val + to_f32(xr[col]);
-        } else if constexpr (EPI == EPI_GELU) {
-          ((T *)args.out.base)[b * args.out.sb + (long long)(t - args.out.t_off) * args.out.rs + col] =
-              from_f32<T>(gelu_erf(val + to_f32(bias[col])));
-        } else {
-          const float *yr = (const float *)args.resid.base + b * args.resid.sb + (long long)(t - args.resid.t_off) * args.resid.rs;
-          ((float *)args.out.base)[b * args.out.sb + (long long)(t - args.out.t_off) * args.out.rs + col] =
-              val + to_f32(bias[col]) + yr[col];
-        }
+        const int h = col / d_head, c = col - h * d_head;
+        ((T *)hv.base)[b * hv.sb + h * hv.sh + (long long)(t - hv.t_off) * d_head + c] = from_f32<T>(acc[i][j][v]);
       }
     }
   }
 }
 
 template <typename T, int BM, int BN>
-static hipError_t launch_t(int epi, int resid_f32, const GemmArgs &a, int grid, hipStream_t s) {
-  constexpr int BK = GEMM_BK;
-  dim3 gd(grid), bd(256);
-  switch (epi) {
-    case EPI_HEADS:
-      hipLaunchKernelGGL((mixed_gemm_kernel<T, BM, BN, BK, EPI_HEADS, T>), gd, bd, 0, s, a);
-      break;
-    case EPI_RESID:
-      if (resid_f32)
-        hipLaunchKernelGGL((mixed_gemm_kernel<T, BM, BN, BK, EPI_RESID, float>), gd, bd, 0, s, a);
-      else
-        hipLaunchKernelGGL((mixed_gemm_kernel<T, BM, BN, BK, EPI_RESID, T>), gd, bd, 0, s, a);
-      break;
-    case EPI_GELU:
-      hipLaunchKernelGGL((mixed_gemm_kernel<T, BM, BN, BK, EPI_GELU, T>), gd, bd, 0, s, a);
-      break;
-    case EPI_RESID_BIAS:
-      hipLaunchKernelGGL((mixed_gemm_kernel<T, BM, BN, BK, EPI_RESID_BIAS, float>), gd, bd, 0, s, a);
-      break;
-    default:
-      return hipErrorInvalidValue;
-  }
+static hipError_t launch_t(const GemmArgs &a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((mixed_gemm_kernel<T, BM, BN, GEMM_BK>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(int dtype, int epi, int resid_f32, int tile, const GemmArgs &a, int grid, hipStream_t s) {
-  if (dtype == 1) {
-    return tile ? launch_t<bf16, 128, 128>(epi, resid_f32, a, grid, s)
-                : launch_t<bf16, 64, 64>(epi, resid_f32, a, grid, s);
-  }
-  return tile ? launch_t<float, 128, 128>(epi, resid_f32, a, grid, s)
-              : launch_t<float, 64, 64>(epi, resid_f32, a, grid, s);
+hipError_t launch_gemm(int dtype, int tile, const GemmArgs &a, int grid, hipStream_t s) {
+  if (dtype == 1) return tile ? launch_t<bf16, 128, 128>(a, grid, s) : launch_t<bf16, 64, 64>(a, grid, s);
+  return tile ? launch_t<float, 128, 128>(a, grid, s) : launch_t<float, 64, 64>(a, grid, s);
 }
 
 }  // namespace ot

@@ -8,14 +8,16 @@
 namespace ot {
 
 // dtype: 0 = fp32 storage, 1 = bf16 storage. tile: 0 = 64x64, 1 = 128x128 workgroup tile.
-// resid_f32: residual operand of EPI_RESID is fp32 (1) or storage dtype (0).
-hipError_t launch_gemm(int dtype, int epi, int resid_f32, int tile, const GemmArgs &a, int grid,
-                       hipStream_t s);
+hipError_t launch_gemm(int dtype, int tile, const GemmArgs &a, int grid, hipStream_t s);
 
 // in_f32: input rows are fp32 (1) or storage dtype (0); output is the storage dtype.
 hipError_t launch_norm(int dtype, int in_f32, const NormArgs &a, hipStream_t s);
 
 hipError_t launch_attn(int dtype, int d_head, int stage2, const AttnArgs &a, hipStream_t s);
+
+// Fused post-attention kernel; tokens per workgroup tile for a dtype / d_model.
+hipError_t launch_post(int dtype, int resid_f32, const PostArgs &a, int grid, hipStream_t s);
+int post_tokens_per_tile(int dtype, int d_model);
 
 // Workgroup tile edge of the GEMM for a given tile selector.
 inline int gemm_bm(int tile) { return tile ? 128 : 64; }

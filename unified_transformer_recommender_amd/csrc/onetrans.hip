@@ -27,6 +27,39 @@ using namespace ot;
 
 namespace {
 
+// ---- per-launch timing (off unless enabled) ---------------------------------------------------
+struct TimedLaunch {
+  int cls;
+  hipEvent_t a, b;
+};
+bool g_timing = false;
+std::vector<TimedLaunch> g_timed;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `launch` (returning hipError_t); with timing on, brackets it with events on `s`.
+template <class F>
+hipError_t timed(int cls, hipStream_t s, F &&launch) {
+  if (!g_timing) return launch();
+  hipEvent_t a = take_event(), b = take_event();
+  if (!a || !b) return hipErrorOutOfMemory;
+  if (hipEventRecord(a, s) != hipSuccess) return hipErrorInvalidValue;
+  const hipError_t e = launch();
+  if (hipEventRecord(b, s) != hipSuccess) return hipErrorInvalidValue;
+  g_timed.push_back(TimedLaunch{cls, a, b});
+  return e;
+}
+
 struct Dims {
   int N, d, H, dh, dff, lns, dt;
   size_t esz;
@@ -56,7 +89,7 @@ int check_cfg(const onetrans_config *c, Dims &D) {
   D.layer = c->norm == ONETRANS_LAYERNORM;
   D.eps = c->norm_eps;
   if (D.dh != 16 && D.dh != 32) return ONETRANS_ERR_UNSUPPORTED;
-  if (D.d % 64 || D.d > 1024 || D.dff % 64) return ONETRANS_ERR_UNSUPPORTED;
+  if ((D.d != 64 && D.d != 128 && D.d != 256 && D.d != 512) || D.dff % 64) return ONETRANS_ERR_UNSUPPORTED;
   if (D.lns > 32) return ONETRANS_ERR_UNSUPPORTED;
   D.tile = (D.d % 128 == 0 && D.dff % 128 == 0) ? 1 : 0;
   return ONETRANS_OK;
@@ -92,7 +125,7 @@ int check_weights(const onetrans_block_weights *blk, const Dims &D) {
 
 // ---- workspace -------------------------------------------------------------------------------
 struct Ws {
-  size_t x, xh, q, k, v, o, y, yh, hb, total;
+  size_t x[2], xh, q, k, v, o, total;
 };
 
 inline size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -107,15 +140,15 @@ Ws ws_layout(const Dims &D, size_t n, size_t tin, size_t rq, bool kv) {
     return o;
   };
   const size_t d = D.d, es = D.esz;
-  w.x = take(n * rq * d * 4);
+  // block outputs alternate between two buffers: the fused tail reads its block input as the
+  // residual while writing the block output, so the two must not alias
+  w.x[0] = take(n * rq * d * 4);
+  w.x[1] = take(n * rq * d * 4);
   w.xh = take(n * tin * d * es);
   w.q = take(n * rq * d * es);
   w.k = kv ? take(n * tin * d * es) : 0;
   w.v = kv ? take(n * tin * d * es) : 0;
   w.o = take(n * rq * d * es);
-  w.y = take(n * rq * d * 4);
-  w.yh = take(n * rq * d * es);
-  w.hb = take(n * rq * (size_t)D.dff * es);
   w.total = off;
   return w;
 }
@@ -152,17 +185,13 @@ struct JobSpec {
   HeadView oh[3];
 };
 
-int run_gemm(const Dims &D, int epi, int resid_f32, int N, int K, const JobSpec *jobs, int n_jobs, RowView a,
-             RowView out, RowView resid, const void *bias, hipStream_t st) {
+int run_gemm(int cls, const Dims &D, int N, int K, const JobSpec *jobs, int n_jobs, RowView a, hipStream_t st) {
   GemmArgs g;
   memset(&g, 0, sizeof(g));
   g.N = N;
   g.K = K;
   g.d_head = D.dh;
   g.a = a;
-  g.out = out;
-  g.resid = resid;
-  g.bias = bias;
   const int BM = gemm_bm(D.tile), BN = gemm_bn(D.tile);
   long long tiles = 0;
   int nj = 0;
@@ -184,8 +213,8 @@ int run_gemm(const Dims &D, int epi, int resid_f32, int N, int K, const JobSpec 
   g.n_jobs = nj;
   if (tiles == 0) return ONETRANS_OK;
   if (tiles > 0x7fffffffLL) return ONETRANS_ERR_UNSUPPORTED;
-  return launch_gemm(D.dt, epi, resid_f32, D.tile, g, (int)tiles, st) == hipSuccess ? ONETRANS_OK
-                                                                                   : ONETRANS_ERR_HIP;
+  const hipError_t e = timed(cls, st, [&] { return launch_gemm(D.dt, D.tile, g, (int)tiles, st); });
+  return e == hipSuccess ? ONETRANS_OK : ONETRANS_ERR_HIP;
 }
 
 // One block over one operation's rows.
@@ -211,7 +240,7 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
   const int d = D.d, H = D.H, dh = D.dh;
   const int p0 = st.s - st.q;
   const int R = st.q + st.ns;
-  char *xh = ws + L.xh, *qb = ws + L.q, *ob = ws + L.o, *yb = ws + L.y, *yhb = ws + L.yh, *hb = ws + L.hb;
+  char *xh = ws + L.xh, *qb = ws + L.q, *ob = ws + L.o;
   int rc;
 
   // norm1 over the input rows
@@ -230,7 +259,8 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
     na.beta = w.norm1_b;
     na.layer = D.layer;
     na.eps = D.eps;
-    if (launch_norm(D.dt, st.x_f32, na, stream) != hipSuccess) return ONETRANS_ERR_HIP;
+    if (timed(ONETRANS_K_NORM, stream, [&] { return launch_norm(D.dt, st.x_f32, na, stream); }) != hipSuccess)
+      return ONETRANS_ERR_HIP;
   }
   const RowView xh_v{xh, (long long)st.in_n * d, st.in_t0, d};
   const HeadView q_v{qb, (long long)H * R * dh, (long long)R * dh, p0};
@@ -263,7 +293,7 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
       j.w[1] = w.wv; j.oh[1] = st.vN;
       j.w[2] = w.wq; j.oh[2] = q_v;
     }
-    rc = run_gemm(D, EPI_HEADS, 0, d, d, jobs, nj, xh_v, RowView{}, RowView{}, nullptr, stream);
+    rc = run_gemm(ONETRANS_K_QKV, D, d, d, jobs, nj, xh_v, stream);
     if (rc) return rc;
   }
   if (!st.need_out) return ONETRANS_OK;
@@ -300,57 +330,49 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
       a.n_seq_grp = st.n_seq;
       a.n_qblocks = (R + ATTN_QBLOCK - 1) / ATTN_QBLOCK;
     }
-    if (launch_attn(D.dt, dh, st.stage2, a, stream) != hipSuccess) return ONETRANS_ERR_HIP;
+    if (timed(ONETRANS_K_ATTN, stream, [&] { return launch_attn(D.dt, dh, st.stage2, a, stream); }) != hipSuccess)
+      return ONETRANS_ERR_HIP;
   }
 
-  // projections of the query rows: S tail rows use set 0, NS token j uses set 1 + j
-  JobSpec pj[2];
-  int npj = 0;
-  if (st.q > 0) {
-    pj[npj] = JobSpec{};
-    pj[npj].rs = RowSet{st.n_seq, st.q, 1, p0, 0, 0};
-    pj[npj].n_seg = 1;
-    ++npj;
-  }
-  if (st.ns > 0) {
-    pj[npj] = JobSpec{};
-    pj[npj].rs = RowSet{st.n_seq, 1, st.ns, st.s, 1, 1};
-    pj[npj].n_seg = 1;
-    ++npj;
-  }
-  auto set_w = [&](const void *wp) {
-    for (int i = 0; i < npj; ++i) pj[i].w[0] = wp;
-  };
-  const RowView o_v{ob, (long long)R * d, p0, d};
-  const RowView y_v{yb, (long long)R * d, p0, d};
-  const RowView yh_v{yhb, (long long)R * d, p0, d};
-  const RowView h_v{hb, (long long)R * D.dff, p0, D.dff};
-
-  set_w(w.wo);
-  rc = run_gemm(D, EPI_RESID, st.x_f32, d, d, pj, npj, o_v, y_v, st.x, nullptr, stream);
-  if (rc) return rc;
+  // W^O + residual + norm2 + mixed FFN + residual, fused, over the query rows:
+  // tail S rows use parameter set 0, NS token j uses set 1 + j
   {
-    NormArgs na;
-    na.n_seq = st.n_seq;
-    na.rows = R;
-    na.d = d;
-    na.in = yb;
-    na.in_sb = (long long)R * d;
-    na.in_i0 = 0;
-    na.out = yhb;
-    na.out_sb = (long long)R * d;
-    na.out_i0 = 0;
-    na.gamma = w.norm2_g;
-    na.beta = w.norm2_b;
-    na.layer = D.layer;
-    na.eps = D.eps;
-    if (launch_norm(D.dt, 1, na, stream) != hipSuccess) return ONETRANS_ERR_HIP;
+    PostArgs pa;
+    memset(&pa, 0, sizeof(pa));
+    const int bm = post_tokens_per_tile(D.dt, d);
+    int nj = 0;
+    long long tiles = 0;
+    auto add_job = [&](RowSet rs) {
+      const long long m = (long long)rs.n_seq * rs.rows;
+      if (m == 0 || rs.n_groups == 0) return;
+      PostJob &j = pa.job[nj++];
+      j.rs = rs;
+      j.m_tiles = (int)((m + bm - 1) / bm);
+      j.tile_start = (int)tiles;
+      tiles += (long long)j.m_tiles * rs.n_groups;
+    };
+    if (st.q > 0) add_job(RowSet{st.n_seq, st.q, 1, p0, 0, 0});
+    if (st.ns > 0) add_job(RowSet{st.n_seq, 1, st.ns, st.s, 1, 1});
+    pa.n_jobs = nj;
+    pa.d_model = d;
+    pa.d_ff = D.dff;
+    pa.o = RowView{ob, (long long)R * d, p0, d};
+    pa.resid = st.x;
+    pa.out = st.out;
+    pa.wo = w.wo;
+    pa.w1 = w.w1;
+    pa.b1 = w.b1;
+    pa.w2 = w.w2;
+    pa.b2 = w.b2;
+    pa.gamma = w.norm2_g;
+    pa.beta = w.norm2_b;
+    pa.layer = D.layer;
+    pa.eps = D.eps;
+    if (tiles > 0x7fffffffLL) return ONETRANS_ERR_UNSUPPORTED;
+    const hipError_t e = timed(ONETRANS_K_POST, stream, [&] { return launch_post(D.dt, st.x_f32, pa, (int)tiles, stream); });
+    if (e != hipSuccess) return ONETRANS_ERR_HIP;
   }
-  set_w(w.w1);
-  rc = run_gemm(D, EPI_GELU, 0, D.dff, d, pj, npj, yh_v, h_v, RowView{}, w.b1, stream);
-  if (rc) return rc;
-  set_w(w.w2);
-  return run_gemm(D, EPI_RESID_BIAS, 1, d, D.dff, pj, npj, h_v, st.out, y_v, w.b2, stream);
+  return ONETRANS_OK;
 }
 
 int check_ws(const Dims &D, const Ws &L, void *ws, size_t ws_bytes) {
@@ -439,10 +461,10 @@ int onetrans_forward(const onetrans_config *cfg, const onetrans_block_weights *b
     st.vp = w + L.v;
     st.pre_sb = (long long)H * T * dh;
     st.pre_sh = (long long)T * dh;
-    st.out = RowView{n + 1 == D.N ? out : (void *)(w + L.x), (long long)R * d, p0, d};
+    st.out = RowView{n + 1 == D.N ? out : (void *)(w + L.x[n & 1]), (long long)R * d, p0, d};
     st.need_out = true;
     if ((rc = run_step(D, blk[n], st, w, L, stream))) return rc;
-    x = RowView{w + L.x, (long long)R * d, 0, d};
+    x = RowView{w + L.x[n & 1], (long long)R * d, 0, d};
     x_f32 = 1;
     s = q;
   }
@@ -498,10 +520,10 @@ int onetrans_prefill_user(const onetrans_config *cfg, const onetrans_block_weigh
     st.vp = st.vS.base;
     st.pre_sb = st.kS.sb;
     st.pre_sh = st.kS.sh;
-    st.out = RowView{last ? out_s : (void *)(w + L.x), (long long)q * d, p0, d};
+    st.out = RowView{last ? out_s : (void *)(w + L.x[n & 1]), (long long)q * d, p0, d};
     st.need_out = !last || out_s != nullptr;
     if ((rc = run_step(D, blk[n], st, w, L, stream))) return rc;
-    x = RowView{w + L.x, (long long)q * d, 0, d};
+    x = RowView{w + L.x[n & 1], (long long)q * d, 0, d};
     x_f32 = 1;
     s = q;
   }
@@ -568,10 +590,10 @@ int onetrans_score_candidates(const onetrans_config *cfg, const onetrans_block_w
     st.pre_sh = cv.sh;
     st.own_sb = st.kN.sb;
     st.own_sh = st.kN.sh;
-    st.out = RowView{n + 1 == D.N ? out_ns : (void *)(w + L.x), (long long)ns * d, s, d};
+    st.out = RowView{n + 1 == D.N ? out_ns : (void *)(w + L.x[n & 1]), (long long)ns * d, s, d};
     st.need_out = true;
     if ((rc = run_step(D, blk[n], st, w, L, stream))) return rc;
-    x = RowView{w + L.x, (long long)ns * d, 0, d};
+    x = RowView{w + L.x[n & 1], (long long)ns * d, 0, d};
     x_f32 = 1;
   }
   return ONETRANS_OK;
@@ -628,10 +650,10 @@ int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weig
     st.vp = st.vS.base;
     st.pre_sb = st.kS.sb;
     st.pre_sh = st.kS.sh;
-    st.out = RowView{last && out_new ? out_new : (void *)(w + L.x), (long long)d_l * d, l_old, d};
+    st.out = RowView{last && out_new ? out_new : (void *)(w + L.x[n & 1]), (long long)d_l * d, l_old, d};
     st.need_out = !last || out_new != nullptr;
     if ((rc = run_step(D, blk[n], st, w, L, stream))) return rc;
-    x = RowView{w + L.x, (long long)d_l * d, l_old, d};
+    x = RowView{w + L.x[n & 1], (long long)d_l * d, l_old, d};
     x_f32 = 1;
   }
   for (int n = 0; n < D.N; ++n) cache->layer_len[n] = l_old + d_l;
@@ -653,5 +675,24 @@ const char *onetrans_status_string(int status) {
 }
 
 const char *onetrans_version(void) { return "onetrans-gfx950 0.1"; }
+
+int onetrans_timing_enable(int on) {
+  g_timing = on != 0;
+  return ONETRANS_OK;
+}
+
+int onetrans_timing_read(double *ms, long long *launches) {
+  int rc = ONETRANS_OK;
+  for (const TimedLaunch &t : g_timed) {
+    float e = 0.0f;
+    if (hipEventSynchronize(t.b) != hipSuccess || hipEventElapsedTime(&e, t.a, t.b) != hipSuccess) rc = ONETRANS_ERR_HIP;
+    if (ms && t.cls >= 0 && t.cls < ONETRANS_K_COUNT) ms[t.cls] += e;
+    if (launches && t.cls >= 0 && t.cls < ONETRANS_K_COUNT) launches[t.cls] += 1;
+    g_event_pool.push_back(t.a);
+    g_event_pool.push_back(t.b);
+  }
+  g_timed.clear();
+  return rc;
+}
 
 }  // extern "C"
