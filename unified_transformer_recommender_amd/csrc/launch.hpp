@@ -24,5 +24,6 @@ inline int gemm_bm(int tile) { return tile ? 128 : 64; }
 inline int gemm_bn(int tile) { return tile ? 128 : 64; }
 constexpr int GEMM_BK = 32;
 constexpr int ATTN_QBLOCK = 128;   // forward-mode queries per attention workgroup
+constexpr int POST_MAX_DFF = 2048; // widest FFN the fused post-attention kernel stages
 
 }  // namespace ot

@@ -89,7 +89,9 @@ int check_cfg(const onetrans_config *c, Dims &D) {
   D.layer = c->norm == ONETRANS_LAYERNORM;
   D.eps = c->norm_eps;
   if (D.dh != 16 && D.dh != 32) return ONETRANS_ERR_UNSUPPORTED;
-  if ((D.d != 64 && D.d != 128 && D.d != 256 && D.d != 512) || D.dff % 64) return ONETRANS_ERR_UNSUPPORTED;
+  if ((D.d != 64 && D.d != 128 && D.d != 256 && D.d != 512) || D.dff % 64 || D.dff > POST_MAX_DFF)
+    return ONETRANS_ERR_UNSUPPORTED;
+  if (D.dt == ONETRANS_F32 && D.d > 256) return ONETRANS_ERR_UNSUPPORTED;
   if (D.lns > 32) return ONETRANS_ERR_UNSUPPORTED;
   D.tile = (D.d % 128 == 0 && D.dff % 128 == 0) ? 1 : 0;
   return ONETRANS_OK;

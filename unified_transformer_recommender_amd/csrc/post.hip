@@ -7,12 +7,18 @@
 // MFMA 32x32 tile are 32 tokens and each lane owns ONE token. Per token the wave keeps
 //   Y^T   (d x 32 fp32 accumulators)          -> becomes X'^T after the FFN adds into it
 //   Yh^T  (norm2 output, bf16 B fragments)   -> B operand of the FFN up-projection
-// and streams the weights (A operand) through LDS in chunks of 32 rows shared by all waves.
-// An accumulator tile's lane holds k-indices {4g + r + 8j}; using it directly as the next
-// product's B fragment permutes the k order inside every 16-block (bits 2 and 3 of k swap), so the
-// W1 and W2 chunks are written to LDS with the same permutation. The hidden activations of a
-// 32-unit chunk never leave registers: up-projection tile -> +b1 -> GELU -> bf16 -> B fragments of
-// the down-projection, which accumulates straight into X'^T.
+// and streams the weights (A operand) through LDS in chunks of 32 rows (W^O, W1) or 32 columns
+// (W2) shared by the workgroup's waves. The hidden activations of a 32-unit chunk never leave
+// registers: up-projection tile -> +b1 -> GELU -> bf16 -> B fragments of the down-projection,
+// which accumulates straight into X'^T. An accumulator tile's lane holds the k-indices
+// {4g + r + 8j}; two cross-half lane swaps (v_permlane32_swap) turn it into a natural B fragment.
+//
+// Weight streaming: chunks flow through NB = 2 LDS buffers with direct global->LDS loads
+// (each wave instruction writes 64 x 16 bytes), issued one chunk ahead; a chunk is consumed
+// after the issuing waves' own vmcnt wait and one workgroup barrier. Rows are stored unpadded
+// with their 16-byte pieces XOR-swizzled so that 16 lanes reading 16 consecutive rows touch 16
+// distinct bank groups. The FFN is software-pipelined: while the up-projection of hidden chunk
+// c+1 runs on the matrix cores, the VALU evaluates GELU of chunk c.
 //
 // GELU is the exact erf form 0.5 x (1 + erf(x / sqrt 2)); erf is evaluated with Abramowitz &
 // Stegun 7.1.26 (|error| <= 1.5e-7): with z = |x|/sqrt2, t = 1/(1 + p z),
@@ -38,33 +44,63 @@ __device__ __forceinline__ float gelu_as(float x) {
   return fmaf(-ax * q, e, fmaxf(x, 0.0f));
 }
 
-// Index of k inside LDS for an accumulator-fed B operand (bf16): bits 2 and 3 of k swapped.
-__device__ __forceinline__ constexpr int kperm(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
-
-// Waves per workgroup: two per SIMD where the per-token state (d/32 accumulator tiles plus the
-// norm2 fragments) fits in half the register file, else one.
+// Waves per workgroup (every chunk is split into whole 1 KB wave loads).
 template <typename T, int D>
-constexpr int post_nw() { return (sizeof(T) == 2 && D <= 128) ? 8 : 4; }
+constexpr int post_nw() { return (sizeof(T) == 2 && D == 128) ? 8 : 4; }
 
-template <typename T, typename TR, int D>
+// Row layout of a weight chunk in LDS: RP 16-byte pieces per row; piece q of row r is stored at
+// slot q ^ swz(r). `rpb` = rows sharing one 256-byte bank line.
+template <int RP, int RB>
+__device__ __forceinline__ constexpr int chunk_swz(int r) {
+  constexpr int rpb = RB >= 256 ? 1 : 256 / RB;
+  constexpr int P = RP < 16 / rpb ? RP : 16 / rpb;
+  return (r / rpb) & (P - 1);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// bf16 accumulator-fed B fragment: lane half g holds k {4g..4g+3, 8+4g..8+4g+3} of a 16-block;
+// exchange the middle 8-byte halves between the lane halves to get k {8g .. 8g+7}.
+__device__ __forceinline__ bf16x8 natural_kfrag(bf16x8 f) {
+  u32x4 u = __builtin_bit_cast(u32x4, f);
+  const auto s0 = __builtin_amdgcn_permlane32_swap(u[0], u[2], false, false);
+  const auto s1 = __builtin_amdgcn_permlane32_swap(u[1], u[3], false, false);
+  u[0] = s0[0]; u[2] = s0[1];
+  u[1] = s1[0]; u[3] = s1[1];
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+template <typename T, typename TR, int D, bool LAYER>
 __global__ __launch_bounds__((post_nw<T, D>() * 64)) void post_kernel(const PostArgs a) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int NW = post_nw<T, D>();
-  constexpr int NT = NW * 64;
   constexpr int EPC = 16 / (int)sizeof(T);
   constexpr int DT = D / 32;                    // feature tiles
   constexpr int KC = D / M::KSTEP;              // k-chunks over d
-  constexpr int LDA = D + EPC;                  // LDS row of a 32 x d chunk (Wo, W1)
-  constexpr int LDB = 32 + EPC;                 // LDS row of a d x 32 chunk (W2)
-  constexpr int BUF = (32 * LDA > D * LDB) ? 32 * LDA : D * LDB;
-  constexpr int PIECES = 32 * D / EPC;          // 16-byte pieces per chunk
-  constexpr int PPT = (PIECES + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) T lds[2][BUF];
+  constexpr int HKC = 32 / M::KSTEP;            // k-chunks over a 32-unit hidden chunk
+  constexpr int RPA = D / EPC;                  // pieces per row of a 32 x d chunk (W^O, W1)
+  constexpr int RPB = 32 / EPC;                 // pieces per row of a d x 32 chunk (W2)
+  constexpr int CH = 32 * D;                    // elements per chunk
+  constexpr int BLOCKS = CH / EPC / 64;         // 1 KB wave loads per chunk
+  constexpr int LPW = BLOCKS / NW;              // wave loads per chunk per wave
+  static_assert(BLOCKS % NW == 0 && LPW >= 1, "chunk must split into whole wave loads");
+  constexpr int NB = 2;                         // chunk buffers; loads run NB - 1 chunks ahead
+  constexpr bool BF = sizeof(T) == 2;
+  __shared__ __attribute__((aligned(16))) T lds[NB][CH];
+  // per-feature / per-hidden-unit vectors of this parameter set, fp32: gamma, beta, b2 [d], b1 [d_ff]
+  __shared__ __attribute__((aligned(16))) float svec[3 * D + POST_MAX_DFF];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lc = lane & 31;
   const int DFF = a.d_ff;
+  const int NC = DFF / 32;                      // hidden chunks
+  const int NCH = DT + 1 + 2 * NC;              // chunks in the stream
 
   // ---- job / group / token tile --------------------------------------------------------------
   const int bid = blockIdx.x;
@@ -84,80 +120,102 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64)) void post_kernel(const Post
   const T *w2 = (const T *)a.w2 + (size_t)wg * D * DFF;
   const T *b1 = (const T *)a.b1 + (size_t)wg * DFF;
   const T *b2 = (const T *)a.b2 + (size_t)wg * D;
-  const int n_wo = DT;
-  const int n_chunks = n_wo + 2 * (DFF / 32);
 
-  // ---- chunk staging: global -> registers -> LDS ------------------------------------------
-  u32x4 pre[PPT];
-  auto prefetch = [&](int id) {
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int p = tid + i * NT;
-      if (p >= PIECES) break;
-      const T *src;
-      if (id < n_wo || ((id - n_wo) & 1) == 0) {      // Wo or W1 chunk: 32 rows x d
-        const int row = p / (D / EPC), kp = (p - row * (D / EPC)) * EPC;
-        const T *base = id < n_wo ? wo + (size_t)(id * 32) * D : w1 + (size_t)(((id - n_wo) >> 1) * 32) * D;
-        src = base + (size_t)row * D + kp;
-      } else {                                          // W2 chunk: d rows x 32 hidden
-        const int row = p / (32 / EPC), kp = (p - row * (32 / EPC)) * EPC;
-        src = w2 + (size_t)row * DFF + ((id - n_wo) >> 1) * 32 + kp;
-      }
-      pre[i] = ld16(src);
-    }
-  };
-  auto commit = [&](int id, int buf) {
-    T *dst = lds[buf];
-    const bool permute = sizeof(T) == 2 && id >= n_wo;
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int p = tid + i * NT;
-      if (p >= PIECES) break;
-      int row, kp, ld;
-      if (id < n_wo || ((id - n_wo) & 1) == 0) {
-        row = p / (D / EPC); kp = (p - row * (D / EPC)) * EPC; ld = LDA;
-      } else {
-        row = p / (32 / EPC); kp = (p - row * (32 / EPC)) * EPC; ld = LDB;
-      }
-      T *d = dst + row * ld;
-      if (permute) {
-        // 8 consecutive k (k0 = 16m + 8a): first half to 16m + 4a, second half to 16m + 8 + 4a
-        const uint2 lo = {pre[i][0], pre[i][1]}, hi = {pre[i][2], pre[i][3]};
-        *(uint2 *)(d + kperm(kp)) = lo;
-        *(uint2 *)(d + kperm(kp + 4)) = hi;
-      } else {
-        st16(d + kp, pre[i]);
-      }
-    }
-  };
-
-  // A fragment of row `row` (LDS, leading dim ld) for k-chunk kc; `perm` = accumulator-fed B.
-  auto afrag = [&](const T *base, int ld, int row, int kc, bool perm) -> frag {
-    if constexpr (sizeof(T) == 2) {
-      (void)perm;
-      return *(const frag *)(base + row * ld + kc * 16 + g * 8);
+  // ---- weight chunk stream --------------------------------------------------------------------
+  // chunk i: i < DT            -> W^O rows 32i..32i+31
+  //          i == DT           -> W1 rows 0..31 (hidden chunk 0)
+  //          i == DT + 1 + 2c  -> W1 rows of hidden chunk (c + 1) mod NC   (up-projection one ahead)
+  //          i == DT + 2 + 2c  -> W2 columns of hidden chunk c
+  // This lane's piece of wave load j sits at LDS piece P = (j * NW + wave) * 64 + lane.
+  auto issue = [&](int i) {
+    const T *base;
+    bool cols = false;
+    if (i < DT) {
+      base = wo + (size_t)(32 * i) * D;
+    } else if (i == DT) {
+      base = w1;
     } else {
-      const int k = perm ? 32 * (kc >> 4) + acc_row(kc & 15, g) : kc * 2 + g;
-      return base[row * ld + k];
+      const int c = (i - DT - 1) >> 1;
+      if (((i - DT - 1) & 1) == 0) {
+        base = w1 + (size_t)(32 * ((c + 1) % NC)) * D;
+      } else {
+        base = w2 + 32 * c;
+        cols = true;
+      }
+    }
+    T *dst = lds[i % NB];
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int blk = j * NW + wave;
+      const int P = blk * 64 + lane;
+      const T *src;
+      if (!cols) {
+        const int row = P / RPA, q = P % RPA;
+        src = base + row * D + (q ^ chunk_swz<RPA, RPA * 16>(row)) * EPC;
+      } else {
+        const int row = P / RPB, q = P % RPB;
+        src = base + (size_t)row * DFF + (q ^ chunk_swz<RPB, RPB * 16>(row)) * EPC;
+      }
+      __builtin_amdgcn_global_load_lds((const void *)src, (__attribute__((address_space(3))) void *)(dst + blk * 64 * EPC),
+                                       16, 0, 0);
+    }
+  };
+  // Make chunk i visible: this wave's loads of chunk i are done (loads of later chunks may still
+  // be in flight), then every wave's.
+  auto arrive = [&](int i) {
+    const int later = min(NB - 2, NCH - 1 - i);
+    if (later >= 2) wait_vm<2 * LPW>();
+    else if (later == 1) wait_vm<LPW>();
+    else wait_vm<0>();
+    __syncthreads();
+  };
+
+  // A fragment of chunk row `row` for k-chunk kc (row chunks: k = feature; column chunks: k = hidden).
+  auto afrag_rows = [&](const T *base, int row, int kc, bool accfed) -> frag {
+    if constexpr (BF) {
+      (void)accfed;
+      const int q = (2 * kc + g) ^ chunk_swz<RPA, RPA * 16>(row);
+      return *(const frag *)(base + row * D + q * EPC);
+    } else {
+      const int k = accfed ? 32 * (kc >> 4) + acc_row(kc & 15, g) : kc * 2 + g;
+      return base[row * D + ((k / EPC) ^ chunk_swz<RPA, RPA * 16>(row)) * EPC + k % EPC];
+    }
+  };
+  auto afrag_cols = [&](const T *base, int row, int kc) -> frag {
+    if constexpr (BF) {
+      const int q = (2 * kc + g) ^ chunk_swz<RPB, RPB * 16>(row);
+      return *(const frag *)(base + row * 32 + q * EPC);
+    } else {
+      const int k = acc_row(kc, g);
+      return base[row * 32 + ((k / EPC) ^ chunk_swz<RPB, RPB * 16>(row)) * EPC + k % EPC];
     }
   };
 
-  // ---- B fragments of O^T (attention output of this lane's token) -----------------------------
+  // prologue: start the weight stream, then the per-token loads
+#pragma unroll
+  for (int i = 0; i < NB - 1; ++i) issue(i);
+
+  float *s_gm = svec, *s_bt = svec + D, *s_b2 = svec + 2 * D, *s_b1 = svec + 3 * D;
+  for (int i = tid; i < 3 * D + DFF; i += NW * 64) {
+    float v;
+    if (i < D) v = to_f32(((const T *)a.gamma)[i]);
+    else if (i < 2 * D) v = LAYER ? to_f32(((const T *)a.beta)[i - D]) : 0.0f;
+    else if (i < 3 * D) v = to_f32(b2[i - 2 * D]);
+    else v = to_f32(b1[i - 3 * D]);
+    svec[i] = v;
+  }
+
   frag ofr[KC];
   {
     const T *orow = (const T *)a.o.base + b * a.o.sb + (long long)(t - a.o.t_off) * a.o.rs;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      if constexpr (sizeof(T) == 2)
+      if constexpr (BF)
         ofr[kc] = *(const frag *)(orow + kc * 16 + g * 8);
       else
         ofr[kc] = orow[kc * 2 + g];
     }
   }
-
-  prefetch(0);
-  commit(0, 0);
-  __syncthreads();
 
   f32x16 acc[DT];
 #pragma unroll
@@ -166,29 +224,36 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64)) void post_kernel(const Post
   // ---- W^O: Y^T = Wo O^T, one 32-feature tile per chunk ---------------------------------------
 #pragma unroll
   for (int ti = 0; ti < DT; ++ti) {
-    const int cur = ti & 1;
-    prefetch(ti + 1);
-    const T *base = lds[cur];
+    arrive(ti);
+    if (ti + NB - 1 < NCH) issue(ti + NB - 1);
+    const T *base = lds[ti % NB];
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) acc[ti] = M::mma(afrag(base, LDA, lc, kc, false), ofr[kc], acc[ti]);
-    commit(ti + 1, cur ^ 1);
-    __syncthreads();
+    for (int kc = 0; kc < KC; ++kc) acc[ti] = M::mma(afrag_rows(base, lc, kc, false), ofr[kc], acc[ti]);
   }
 
   // ---- residual, norm2, + b2 ------------------------------------------------------------------
   {
-    const TR *xr = (const TR *)a.resid.base + b * a.resid.sb + (long long)(t - a.resid.t_off) * a.resid.rs;
+    const TR *xr = (const TR *)a.resid.base + b * a.resid.sb + (long long)(t - a.resid.t_off) * a.resid.rs + 4 * g;
 #pragma unroll
     for (int ti = 0; ti < DT; ++ti)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j) {
+        float xv[4];
+        if constexpr (sizeof(TR) == 4) {
+          const f32x4 v4 = *(const f32x4 *)(xr + 32 * ti + 8 * j);
+          xv[0] = v4[0]; xv[1] = v4[1]; xv[2] = v4[2]; xv[3] = v4[3];
+        } else {
+          const bf16x4 v4 = *(const bf16x4 *)(xr + 32 * ti + 8 * j);
+          xv[0] = (float)v4[0]; xv[1] = (float)v4[1]; xv[2] = (float)v4[2]; xv[3] = (float)v4[3];
+        }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[ti][4 * j + q] += to_f32(xr[32 * ti + 8 * j + 4 * g + q]);
+        for (int q = 0; q < 4; ++q) acc[ti][4 * j + q] += xv[q];
+      }
   }
   frag yfr[KC];
   {
     float mean = 0.0f;
-    if (a.layer) {
+    if constexpr (LAYER) {
       float s = 0.0f;
 #pragma unroll
       for (int ti = 0; ti < DT; ++ti)
@@ -207,26 +272,24 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64)) void post_kernel(const Post
       }
     ss += __shfl_xor(ss, 32, 64);
     const float rstd = 1.0f / sqrtf(ss * (1.0f / D) + a.eps);
-    const T *gm = (const T *)a.gamma;
-    const T *bt = (const T *)a.beta;
 #pragma unroll
     for (int ti = 0; ti < DT; ++ti) {
       float yh[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int f = 32 * ti + acc_row(v, g);
-        float y = (acc[ti][v] - mean) * rstd * to_f32(gm[f]);
-        if (a.layer) y += to_f32(bt[f]);
+        float y = (acc[ti][v] - mean) * rstd * s_gm[f];
+        if constexpr (LAYER) y += s_bt[f];
         yh[v] = y;
-        acc[ti][v] += to_f32(b2[f]);
+        acc[ti][v] += s_b2[f];
       }
-      if constexpr (sizeof(T) == 2) {
+      if constexpr (BF) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           frag fr;
 #pragma unroll
           for (int e = 0; e < 8; ++e) fr[e] = (bf16)yh[8 * h + e];
-          yfr[2 * ti + h] = fr;
+          yfr[2 * ti + h] = natural_kfrag(fr);
         }
       } else {
 #pragma unroll
@@ -235,50 +298,58 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64)) void post_kernel(const Post
     }
   }
 
-  // ---- FFN: per 32 hidden units, up (+b1, GELU) then down into X'^T ---------------------------
-  for (int c = 0; c < DFF / 32; ++c) {
-    const int id = n_wo + 2 * c;
-    // up-projection chunk (LDS buffer (id & 1))
-    prefetch(id + 1);
-    f32x16 h = f32x16{};
+  // ---- FFN prologue: up-projection of hidden chunk 0 (chunk DT) --------------------------------
+  f32x16 hacc = f32x16{};
+  {
+    arrive(DT);
+    if (DT + NB - 1 < NCH) issue(DT + NB - 1);
+    const T *base = lds[DT % NB];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) hacc = M::mma(afrag_rows(base, lc, kc, true), yfr[kc], hacc);
+  }
+
+  // ---- FFN: stage A (W1 chunk c+1): up(c+1) interleaved with GELU(c); stage B (W2 chunk c): down(c)
+  constexpr int NI = KC > 16 ? KC : 16;
+  for (int c = 0; c < NC; ++c) {
+    const int ia = DT + 1 + 2 * c;
+    // stage A
+    arrive(ia);
+    if (ia + NB - 1 < NCH) issue(ia + NB - 1);
+    f32x16 hn = f32x16{};
+    float hv[16];
     {
-      const T *base = lds[id & 1];
+      const T *base = lds[ia % NB];
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) h = M::mma(afrag(base, LDA, lc, kc, true), yfr[kc], h);
-    }
-    commit(id + 1, (id + 1) & 1);
-    __syncthreads();
-    // bias + GELU -> B fragments of the down-projection
-    constexpr int HKC = 32 / M::KSTEP;
-    frag hfr[HKC];
-    {
-      float hv[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) hv[v] = gelu_as(h[v] + to_f32(b1[32 * c + acc_row(v, g)]));
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          frag fr;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) fr[e] = (bf16)hv[8 * hh + e];
-          hfr[hh] = fr;
-        }
-      } else {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) hfr[v] = hv[v];
+      for (int i = 0; i < NI; ++i) {
+        // the last chunk's look-ahead multiplies W1 chunk 0 again; the result is discarded
+        if (i < KC) hn = M::mma(afrag_rows(base, lc, i, true), yfr[i], hn);
+        if (i < 16) hv[i] = gelu_as(hacc[i] + s_b1[32 * c + acc_row(i, g)]);
       }
     }
-    // down-projection chunk (LDS buffer ((id + 1) & 1))
-    if (id + 2 < n_chunks) prefetch(id + 2);
+    frag hfr[HKC];
+    if constexpr (BF) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        frag fr;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fr[e] = (bf16)hv[8 * hh + e];
+        hfr[hh] = natural_kfrag(fr);
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) hfr[v] = hv[v];
+    }
+    // stage B
+    arrive(ia + 1);
+    if (ia + NB < NCH) issue(ia + NB);
     {
-      const T *base = lds[(id + 1) & 1];
+      const T *base = lds[(ia + 1) % NB];
 #pragma unroll
       for (int ti = 0; ti < DT; ++ti)
 #pragma unroll
-        for (int kc = 0; kc < HKC; ++kc) acc[ti] = M::mma(afrag(base, LDB, 32 * ti + lc, kc, true), hfr[kc], acc[ti]);
+        for (int kc = 0; kc < HKC; ++kc) acc[ti] = M::mma(afrag_cols(base, 32 * ti + lc, kc), hfr[kc], acc[ti]);
     }
-    if (id + 2 < n_chunks) commit(id + 2, id & 1);
-    __syncthreads();
+    hacc = hn;
   }
 
   // ---- store X' (fp32, this lane's token) -----------------------------------------------------
@@ -292,28 +363,33 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64)) void post_kernel(const Post
   }
 }
 
+template <typename T, typename TR, int D>
+hipError_t launch_dl(const PostArgs &a, int grid, hipStream_t s) {
+  if (a.layer)
+    hipLaunchKernelGGL((post_kernel<T, TR, D, true>), dim3(grid), dim3(post_nw<T, D>() * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((post_kernel<T, TR, D, false>), dim3(grid), dim3(post_nw<T, D>() * 64), 0, s, a);
+  return hipGetLastError();
+}
+
 template <typename T, typename TR>
 hipError_t launch_d(const PostArgs &a, int grid, hipStream_t s) {
   switch (a.d_model) {
-#define OT_POST_CASE(DV)                                                                         \
-  case DV:                                                                                        \
-    hipLaunchKernelGGL((post_kernel<T, TR, DV>), dim3(grid), dim3(post_nw<T, DV>() * 64), 0, s, a); \
-    break;
-    OT_POST_CASE(64)
-    OT_POST_CASE(128)
-    OT_POST_CASE(256)
-    OT_POST_CASE(512)
-#undef OT_POST_CASE
+    case 64: return launch_dl<T, TR, 64>(a, grid, s);
+    case 128: return launch_dl<T, TR, 128>(a, grid, s);
+    case 256: return launch_dl<T, TR, 256>(a, grid, s);
+    case 512:
+      if constexpr (sizeof(T) == 2) return launch_dl<T, TR, 512>(a, grid, s);
+      return hipErrorInvalidValue;   // fp32 storage at d = 512 is not supported
     default:
       return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace
 
 int post_tokens_per_tile(int dtype, int d_model) {
-  if (dtype == 1) return (d_model <= 128 ? post_nw<bf16, 128>() : post_nw<bf16, 512>()) * 32;
+  if (dtype == 1) return (d_model == 128 ? post_nw<bf16, 128>() : post_nw<bf16, 256>()) * 32;
   return post_nw<float, 256>() * 32;
 }
 
