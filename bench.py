@@ -65,29 +65,22 @@ def roofline_entry(name, work, ms, launches, peak, unit, bound):
             "launches": launches}
 
 
-def kernel_table(classes, timing, steps, n_units, peak_tflops, store_bytes):
-    """Per class: algorithmic work per step over measured time per step."""
+def kernel_table(classes, timing, steps, n_units, peak_tflops):
+    """Per class: algorithmic flops per step over measured device time per step."""
     out = {}
     for k, (ms, cnt) in timing.items():
         if cnt == 0:
             continue
         ms_step = ms / steps
-        if k == "norm":
-            gbs = classes["norm_bytes"] * n_units / (ms_step * 1e-3) / 1e9
-            out[k] = {"ms_per_step": round(ms_step, 4), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
-                      "launches_per_step": cnt // steps}
-        else:
-            tf = classes[k] * n_units / (ms_step * 1e-3) / 1e12
-            out[k] = {"ms_per_step": round(ms_step, 4), "TFLOP/s": round(tf, 2), "frac_mfma": round(tf / peak_tflops, 4),
-                      "launches_per_step": cnt // steps}
+        tf = classes[k] * n_units / (ms_step * 1e-3) / 1e12
+        out[k] = {"ms_per_step": round(ms_step, 4), "TFLOP/s": round(tf, 2), "frac_mfma": round(tf / peak_tflops, 4),
+                  "launches_per_step": cnt // steps}
     return out
 
 
 def dominant(classes, timing, steps, n_units, peak_tflops):
     k = max((c for c in timing if timing[c][1] > 0), key=lambda c: timing[c][0])
     ms, cnt = timing[k]
-    if k == "norm":
-        return roofline_entry(k, classes["norm_bytes"] * n_units * steps, ms, cnt, PEAK_HBM_GBS, "GB/s", "hbm")
     return roofline_entry(k, classes[k] * n_units * steps, ms, cnt, peak_tflops, "TFLOP/s", "mfma")
 
 
@@ -224,9 +217,9 @@ def main():
             pass
     value = n_units / (ms_step * 1e-3)
 
-    flops_unit = sum(v for k, v in classes.items() if k != "norm_bytes")
+    flops_unit = sum(classes.values())
     mfma_frac = flops_unit * n_units / (ms_step * 1e-3) / 1e12 / peak
-    kernels = kernel_table(classes, timing, a.steps, n_units, peak, store_bytes)
+    kernels = kernel_table(classes, timing, a.steps, n_units, peak)
     roof = dominant(classes, timing, a.steps, n_units, peak)
 
     # CPU baseline: the oracle on a bounded sample of the same workload

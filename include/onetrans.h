@@ -148,11 +148,10 @@ int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weig
 
 /* Kernel classes of the per-launch timing below. */
 typedef enum {
-  ONETRANS_K_NORM = 0,       /* pre-norm 1 and 2 */
-  ONETRANS_K_QKV = 1,        /* mixed Q/K/V projection */
-  ONETRANS_K_ATTN = 2,       /* causal / Stage II attention */
-  ONETRANS_K_POST = 3,       /* fused W^O + residual + pre-norm 2 + mixed FFN + residual */
-  ONETRANS_K_COUNT = 4
+  ONETRANS_K_QKV = 0,        /* fused pre-norm 1 + mixed Q/K/V projection */
+  ONETRANS_K_ATTN = 1,       /* causal / Stage II attention */
+  ONETRANS_K_POST = 2,       /* fused W^O + residual + pre-norm 2 + mixed FFN + residual */
+  ONETRANS_K_COUNT = 3
 } onetrans_kernel_class;
 
 /* Per-launch device timing (tracing aid). While enabled, the library brackets every kernel launch

@@ -20,7 +20,7 @@ ERR_HIP = -7
 F32, BF16 = 0, 1
 RMSNORM, LAYERNORM = 0, 1
 OP_FORWARD, OP_PREFILL, OP_SCORE, OP_APPEND = 0, 1, 2, 3
-KERNEL_CLASSES = ("norm", "qkv", "attn", "post")
+KERNEL_CLASSES = ("qkv", "attn", "post")
 
 WEIGHT_FIELDS = ("norm1_g", "norm1_b", "norm2_g", "norm2_b", "wq", "wk", "wv", "wo", "w1", "b1", "w2", "b2")
 

@@ -108,24 +108,23 @@ def mixed_param_count(d: int, d_ff: int, l_ns: int, with_wo: bool = True) -> int
 
 # --- per kernel class (the launch sequence of one block) --------------------------------------
 
-KERNEL_CLASSES = ("norm", "qkv", "attn", "post")
+KERNEL_CLASSES = ("qkv", "attn", "post")
 
 
 def _block_classes(d, d_ff, kv_rows, q_rows, first_query_pos, in_rows, in_bytes, store_bytes):
-    """Algorithmic flops (GEMM/attention classes) and bytes (norm) of one block for one sequence.
+    """Algorithmic flops of one block for one sequence, by kernel class.
 
-    "post" is the fused tail of the block: W^O projection plus both FFN projections."""
+    "qkv" is the fused pre-norm 1 + Q/K/V projection, "post" the fused tail of the block
+    (W^O projection plus both FFN projections)."""
     return {
         "qkv": 2.0 * d * d * (2 * kv_rows + q_rows),
         "attn": 4.0 * d * visible_pairs(first_query_pos, q_rows),
         "post": 2.0 * d * d * q_rows + 2.0 * 2 * d * d_ff * q_rows,
-        # pre-norm 1 reads every input row and writes it normalised in the storage dtype
-        "norm_bytes": float(d * in_rows * (in_bytes + store_bytes)),
     }
 
 
 def forward_classes(d, d_ff, l_ns, l_s, s_queries, store_bytes):
-    """Per-candidate work of the monolithic forward split by kernel class (norm in bytes)."""
+    """Per-candidate work of the monolithic forward split by kernel class."""
     tot, s = {}, l_s
     for n, q in enumerate(s_queries):
         in_bytes = store_bytes if n == 0 else 4

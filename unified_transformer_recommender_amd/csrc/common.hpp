@@ -91,25 +91,27 @@ struct HeadView {
 };
 
 // ---------------------------------------------------------------------------------------------
-// Mixed-parameter GEMM launch (Q/K/V): C[r][n] = sum_k A[r][k] * W_g[n][k] for each job's rows,
-// with W_g the parameter set of the row's group. N columns per segment; a job has up to three
-// segments (Q, K, V) that share the A rows and differ in weights and output.
+// Fused pre-norm 1 + mixed Q/K/V launch over the rows of a block: job 0 = S rows (parameter set
+// 0), job 1 = NS rows (sets 1..l_ns). K and V are produced for every row, Q for rows at
+// positions >= q_from.
 // ---------------------------------------------------------------------------------------------
-struct GemmJob {
+struct QkvJob {
   RowSet rs;
-  int n_seg;
   int tile_start;          // first workgroup of this job
-  int m_tiles;             // per group
-  const void *w[3];        // segment weight base: [G][N][K] storage dtype
-  HeadView out_heads[3];   // head-split output per segment
+  int m_tiles;             // token tiles per group
+  int q_from;              // first position that issues a query
+  HeadView k, v, q;        // head-split outputs
 };
 
-struct GemmArgs {
+struct QkvArgs {
   int n_jobs;
-  int N, K;
-  int d_head;              // columns per head of the outputs
-  GemmJob job[3];
-  RowView a;               // A operand rows (storage dtype)
+  QkvJob job[2];
+  int d_model, d_head;
+  RowView x;               // block input rows (storage dtype in block 0, else fp32)
+  const void *wq, *wk, *wv;   // [G][d][d] storage dtype
+  const void *gamma, *beta;   // norm1 [d]
+  int layer;
+  float eps;
 };
 
 // ---------------------------------------------------------------------------------------------
@@ -132,18 +134,6 @@ struct PostArgs {
   const void *wo, *w1, *b1, *w2, *b2;   // [G][..] storage dtype
   const void *gamma, *beta;             // norm2 [d]
   int layer;
-  float eps;
-};
-
-// ---------------------------------------------------------------------------------------------
-// Row norm launch: rows (b, i) for b < n_seq, i < rows; input row at in.base + b*sb + (i0+i)*d.
-// ---------------------------------------------------------------------------------------------
-struct NormArgs {
-  int n_seq, rows, d;
-  const void *in; long long in_sb; int in_i0;
-  void *out; long long out_sb; int out_i0;
-  const void *gamma, *beta;
-  int layer;               // 0 = RMSNorm, 1 = LayerNorm
   float eps;
 };
 

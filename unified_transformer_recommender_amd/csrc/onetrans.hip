@@ -65,7 +65,6 @@ struct Dims {
   size_t esz;
   int layer;
   float eps;
-  int tile;
 };
 
 inline bool misaligned(const void *p) { return ((uintptr_t)p & 15u) != 0; }
@@ -93,7 +92,6 @@ int check_cfg(const onetrans_config *c, Dims &D) {
     return ONETRANS_ERR_UNSUPPORTED;
   if (D.dt == ONETRANS_F32 && D.d > 256) return ONETRANS_ERR_UNSUPPORTED;
   if (D.lns > 32) return ONETRANS_ERR_UNSUPPORTED;
-  D.tile = (D.d % 128 == 0 && D.dff % 128 == 0) ? 1 : 0;
   return ONETRANS_OK;
 }
 
@@ -127,7 +125,7 @@ int check_weights(const onetrans_block_weights *blk, const Dims &D) {
 
 // ---- workspace -------------------------------------------------------------------------------
 struct Ws {
-  size_t x[2], xh, q, k, v, o, total;
+  size_t x[2], q, k, v, o, total;
 };
 
 inline size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -146,7 +144,6 @@ Ws ws_layout(const Dims &D, size_t n, size_t tin, size_t rq, bool kv) {
   // residual while writing the block output, so the two must not alias
   w.x[0] = take(n * rq * d * 4);
   w.x[1] = take(n * rq * d * 4);
-  w.xh = take(n * tin * d * es);
   w.q = take(n * rq * d * es);
   w.k = kv ? take(n * tin * d * es) : 0;
   w.v = kv ? take(n * tin * d * es) : 0;
@@ -180,45 +177,6 @@ bool ws_dims(const onetrans_config *c, const Dims &D, int op, int n_seq, int l_s
 }
 
 // ---- launches ------------------------------------------------------------------------------
-struct JobSpec {
-  RowSet rs;
-  int n_seg;
-  const void *w[3];
-  HeadView oh[3];
-};
-
-int run_gemm(int cls, const Dims &D, int N, int K, const JobSpec *jobs, int n_jobs, RowView a, hipStream_t st) {
-  GemmArgs g;
-  memset(&g, 0, sizeof(g));
-  g.N = N;
-  g.K = K;
-  g.d_head = D.dh;
-  g.a = a;
-  const int BM = gemm_bm(D.tile), BN = gemm_bn(D.tile);
-  long long tiles = 0;
-  int nj = 0;
-  for (int i = 0; i < n_jobs; ++i) {
-    const JobSpec &j = jobs[i];
-    const long long m = (long long)j.rs.n_seq * j.rs.rows;
-    if (m == 0 || j.rs.n_groups == 0 || j.n_seg == 0) continue;
-    GemmJob &gj = g.job[nj++];
-    gj.rs = j.rs;
-    gj.n_seg = j.n_seg;
-    for (int s = 0; s < 3; ++s) {
-      gj.w[s] = j.w[s];
-      gj.out_heads[s] = j.oh[s];
-    }
-    gj.m_tiles = (int)((m + BM - 1) / BM);
-    gj.tile_start = (int)tiles;
-    tiles += (long long)gj.m_tiles * j.rs.n_groups * j.n_seg * (N / BN);
-  }
-  g.n_jobs = nj;
-  if (tiles == 0) return ONETRANS_OK;
-  if (tiles > 0x7fffffffLL) return ONETRANS_ERR_UNSUPPORTED;
-  const hipError_t e = timed(cls, st, [&] { return launch_gemm(D.dt, D.tile, g, (int)tiles, st); });
-  return e == hipSuccess ? ONETRANS_OK : ONETRANS_ERR_HIP;
-}
-
 // One block over one operation's rows.
 struct Step {
   int n_seq;
@@ -242,61 +200,49 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
   const int d = D.d, H = D.H, dh = D.dh;
   const int p0 = st.s - st.q;
   const int R = st.q + st.ns;
-  char *xh = ws + L.xh, *qb = ws + L.q, *ob = ws + L.o;
+  char *qb = ws + L.q, *ob = ws + L.o;
   int rc;
 
-  // norm1 over the input rows
-  {
-    NormArgs na;
-    na.n_seq = st.n_seq;
-    na.rows = st.in_n;
-    na.d = d;
-    na.in = st.x.base;
-    na.in_sb = st.x.sb;
-    na.in_i0 = st.in_t0 - st.x.t_off;
-    na.out = xh;
-    na.out_sb = (long long)st.in_n * d;
-    na.out_i0 = 0;
-    na.gamma = w.norm1_g;
-    na.beta = w.norm1_b;
-    na.layer = D.layer;
-    na.eps = D.eps;
-    if (timed(ONETRANS_K_NORM, stream, [&] { return launch_norm(D.dt, st.x_f32, na, stream); }) != hipSuccess)
-      return ONETRANS_ERR_HIP;
-  }
-  const RowView xh_v{xh, (long long)st.in_n * d, st.in_t0, d};
   const HeadView q_v{qb, (long long)H * R * dh, (long long)R * dh, p0};
 
-  // mixed Q/K/V projection
+  // pre-norm 1 + mixed Q/K/V: K/V for the S rows [kv_t0, kv_t0 + kv_n) and the NS rows, Q for the
+  // rows at positions >= p0 (tail S rows and NS rows)
   {
-    JobSpec jobs[3];
+    QkvArgs qa;
+    memset(&qa, 0, sizeof(qa));
+    const int bm = qkv_tokens_per_tile();
+    const int no_q = 0x7fffffff;
     int nj = 0;
-    if (st.kv_n > 0) {
-      JobSpec &j = jobs[nj++];
-      j = JobSpec{};
-      j.rs = RowSet{st.n_seq, st.kv_n, 1, st.kv_t0, 0, 0};
-      j.n_seg = 2;
-      j.w[0] = w.wk; j.oh[0] = st.kS;
-      j.w[1] = w.wv; j.oh[1] = st.vS;
-    }
-    if (st.need_out && st.q > 0) {
-      JobSpec &j = jobs[nj++];
-      j = JobSpec{};
-      j.rs = RowSet{st.n_seq, st.q, 1, p0, 0, 0};
-      j.n_seg = 1;
-      j.w[0] = w.wq; j.oh[0] = q_v;
-    }
-    if (st.ns > 0) {
-      JobSpec &j = jobs[nj++];
-      j = JobSpec{};
-      j.rs = RowSet{st.n_seq, 1, st.ns, st.s, 1, 1};
-      j.n_seg = st.need_out ? 3 : 2;
-      j.w[0] = w.wk; j.oh[0] = st.kN;
-      j.w[1] = w.wv; j.oh[1] = st.vN;
-      j.w[2] = w.wq; j.oh[2] = q_v;
-    }
-    rc = run_gemm(ONETRANS_K_QKV, D, d, d, jobs, nj, xh_v, stream);
-    if (rc) return rc;
+    long long tiles = 0;
+    auto add_job = [&](RowSet rs, int q_from, HeadView k, HeadView v) {
+      const long long m = (long long)rs.n_seq * rs.rows;
+      if (m == 0 || rs.n_groups == 0) return;
+      QkvJob &j = qa.job[nj++];
+      j.rs = rs;
+      j.q_from = q_from;
+      j.k = k;
+      j.v = v;
+      j.q = q_v;
+      j.m_tiles = (int)((m + bm - 1) / bm);
+      j.tile_start = (int)tiles;
+      tiles += (long long)j.m_tiles * rs.n_groups;
+    };
+    if (st.kv_n > 0) add_job(RowSet{st.n_seq, st.kv_n, 1, st.kv_t0, 0, 0}, st.need_out ? p0 : no_q, st.kS, st.vS);
+    if (st.ns > 0) add_job(RowSet{st.n_seq, 1, st.ns, st.s, 1, 1}, st.need_out ? st.s : no_q, st.kN, st.vN);
+    qa.n_jobs = nj;
+    qa.d_model = d;
+    qa.d_head = dh;
+    qa.x = st.x;
+    qa.wq = w.wq;
+    qa.wk = w.wk;
+    qa.wv = w.wv;
+    qa.gamma = w.norm1_g;
+    qa.beta = w.norm1_b;
+    qa.layer = D.layer;
+    qa.eps = D.eps;
+    if (tiles > 0x7fffffffLL) return ONETRANS_ERR_UNSUPPORTED;
+    const hipError_t e = timed(ONETRANS_K_QKV, stream, [&] { return launch_qkv(D.dt, st.x_f32, qa, (int)tiles, stream); });
+    if (e != hipSuccess) return ONETRANS_ERR_HIP;
   }
   if (!st.need_out) return ONETRANS_OK;
 

@@ -1,0 +1,219 @@
+// Fused pre-norm 1 + mixed-parameter Q/K/V projection (fun-rec-mdbook 7.5.1: q_i, k_i, v_i =
+// W_i x_i with W_i = W_S for S rows and W_NS,j for NS token j; pre-norm before the sub-layer;
+// 7.5.2: keys/values from every row of the block, queries only from the tail rows).
+//
+// Orientation as in the post-attention kernel: products are formed transposed, C^T = W Xh^T, so
+// each lane owns one token. A lane loads its token's input row, forms the norm statistics with
+// one cross-half shuffle, and keeps the normalised row as bf16 B fragments in registers. The
+// projection weights stream through LDS in chunks of 32 output features x d (direct global->LDS
+// loads, XOR-swizzled rows, double-buffered): with d_head = 32 a chunk is exactly one head, and
+// each accumulator tile is written straight into the head-major Q/K/V (or K/V cache) rows.
+// Chunks of W_Q are skipped by workgroups holding no query row, and Q stores are masked per token.
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ot {
+
+namespace {
+
+template <int RP, int RB>
+__device__ __forceinline__ constexpr int chunk_swz(int r) {
+  constexpr int rpb = RB >= 256 ? 1 : 256 / RB;
+  constexpr int P = RP < 16 / rpb ? RP : 16 / rpb;
+  return (r / rpb) & (P - 1);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+constexpr int QKV_NW = 4;
+
+template <typename T, typename TI, int D, bool LAYER>
+__global__ __launch_bounds__(QKV_NW * 64) void qkv_kernel(const QkvArgs a) {
+  using M = Mma<T>;
+  using frag = typename M::frag;
+  constexpr int NW = QKV_NW;
+  constexpr int EPC = 16 / (int)sizeof(T);
+  constexpr int DT = D / 32;                    // 32-feature chunks per projection
+  constexpr int KC = D / M::KSTEP;
+  constexpr int RPA = D / EPC;                  // 16-byte pieces per weight row
+  constexpr int CH = 32 * D;
+  constexpr int BLOCKS = CH / EPC / 64;
+  constexpr int LPW = BLOCKS / NW;
+  static_assert(BLOCKS % NW == 0 && LPW >= 1, "chunk must split into whole wave loads");
+  constexpr bool BF = sizeof(T) == 2;
+  __shared__ __attribute__((aligned(16))) T lds[2][CH];
+  __shared__ float s_gm[D], s_bt[D];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, lc = lane & 31;
+  const int dh = a.d_head;
+
+  // ---- job / group / token tile --------------------------------------------------------------
+  const int bid = blockIdx.x;
+  const QkvJob &jb = (a.n_jobs > 1 && bid >= a.job[1].tile_start) ? a.job[1] : a.job[0];
+  const int local = bid - jb.tile_start;
+  const int tm = local % jb.m_tiles, grp = local / jb.m_tiles;
+  const int wg = jb.rs.wg0 + grp;
+  const int M_rows = jb.rs.n_seq * jb.rs.rows;
+  const int r0 = tm * (NW * 32) + wave * 32 + lc;
+  const bool valid = r0 < M_rows;
+  const int r = valid ? r0 : 0;
+  const int b = r / jb.rs.rows;
+  const int t = jb.rs.t0 + grp * jb.rs.t_step + (r - b * jb.rs.rows);
+  const bool lane_q = valid && t >= jb.q_from;
+  const bool tile_q = __syncthreads_or(lane_q);   // does any token of this workgroup issue a query?
+
+  // chunk stream: K chunks 0..DT-1, V chunks, then (if any query row) Q chunks
+  const int n_chunks = tile_q ? 3 * DT : 2 * DT;
+  const T *wk = (const T *)a.wk + (size_t)wg * D * D;
+  const T *wv = (const T *)a.wv + (size_t)wg * D * D;
+  const T *wq = (const T *)a.wq + (size_t)wg * D * D;
+  auto issue = [&](int i) {
+    const int seg = i / DT, ci = i - seg * DT;
+    const T *base = (seg == 0 ? wk : seg == 1 ? wv : wq) + (size_t)(32 * ci) * D;
+    T *dst = lds[i & 1];
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int blk = j * NW + wave;
+      const int P = blk * 64 + lane;
+      const int row = P / RPA, q = P % RPA;
+      __builtin_amdgcn_global_load_lds((const void *)(base + row * D + (q ^ chunk_swz<RPA, RPA * 16>(row)) * EPC),
+                                       (__attribute__((address_space(3))) void *)(dst + blk * 64 * EPC), 16, 0, 0);
+    }
+  };
+  issue(0);
+
+  for (int i = tid; i < D; i += NW * 64) {
+    s_gm[i] = to_f32(((const T *)a.gamma)[i]);
+    s_bt[i] = LAYER ? to_f32(((const T *)a.beta)[i]) : 0.0f;
+  }
+
+  // ---- norm1 of this lane's token -> bf16 B fragments (k = 16 kc + 8 g + e) ------------------
+  frag xfr[KC];
+  {
+    const TI *xr = (const TI *)a.x.base + b * a.x.sb + (long long)(t - a.x.t_off) * a.x.rs;
+    constexpr int PER = D / 2;                 // features held by this lane
+    float xv[PER];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      if constexpr (BF) {
+        const TI *p = xr + 16 * kc + 8 * g;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xv[8 * kc + e] = to_f32(p[e]);
+      } else {
+        xv[kc] = to_f32(xr[2 * kc + g]);
+      }
+    }
+    float mean = 0.0f;
+    if constexpr (LAYER) {
+      float s = 0.0f;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) s += xv[e];
+      s += __shfl_xor(s, 32, 64);
+      mean = s * (1.0f / D);
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const float c = xv[e] - mean;
+      ss += c * c;
+    }
+    ss += __shfl_xor(ss, 32, 64);
+    const float rstd = 1.0f / sqrtf(ss * (1.0f / D) + a.eps);
+    __syncthreads();                           // gamma / beta staged
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      if constexpr (BF) {
+        frag fr;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int f = 16 * kc + 8 * g + e;
+          fr[e] = (bf16)((xv[8 * kc + e] - mean) * rstd * s_gm[f] + s_bt[f]);
+        }
+        xfr[kc] = fr;
+      } else {
+        const int f = 2 * kc + g;
+        xfr[kc] = (xv[kc] - mean) * rstd * s_gm[f] + s_bt[f];
+      }
+    }
+  }
+
+  // ---- chunk loop -----------------------------------------------------------------------------
+  for (int i = 0; i < n_chunks; ++i) {
+    wait_vm<0>();
+    __syncthreads();
+    if (i + 1 < n_chunks) issue(i + 1);
+    const T *base = lds[i & 1];
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      frag af;
+      if constexpr (BF) {
+        const int q = (2 * kc + g) ^ chunk_swz<RPA, RPA * 16>(lc);
+        af = *(const frag *)(base + lc * D + q * EPC);
+      } else {
+        const int k = 2 * kc + g;
+        af = base[lc * D + ((k / EPC) ^ chunk_swz<RPA, RPA * 16>(lc)) * EPC + k % EPC];
+      }
+      acc = M::mma(af, xfr[kc], acc);
+    }
+    // output features 32 ci + 8 j + 4 g + r (r = 0..3) of this lane's token
+    const int seg = i / DT, ci = i - seg * DT;
+    const HeadView &hv = seg == 0 ? jb.k : seg == 1 ? jb.v : jb.q;
+    const bool st = seg < 2 ? valid : lane_q;
+    if (st) {
+      T *ob = (T *)hv.base + b * hv.sb + (long long)(t - hv.t_off) * dh;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int f = 32 * ci + 8 * j + 4 * g;       // 4 consecutive features, same head
+        const int h = f / dh, c = f - h * dh;
+        T *o = ob + h * hv.sh + c;
+        if constexpr (BF) {
+          *(bf16x4 *)o = bf16x4{(bf16)acc[4 * j], (bf16)acc[4 * j + 1], (bf16)acc[4 * j + 2], (bf16)acc[4 * j + 3]};
+        } else {
+          *(f32x4 *)o = f32x4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]};
+        }
+      }
+    }
+  }
+}
+
+template <typename T, typename TI, int D>
+hipError_t launch_dl(const QkvArgs &a, int grid, hipStream_t s) {
+  if (a.layer)
+    hipLaunchKernelGGL((qkv_kernel<T, TI, D, true>), dim3(grid), dim3(QKV_NW * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((qkv_kernel<T, TI, D, false>), dim3(grid), dim3(QKV_NW * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, typename TI>
+hipError_t launch_d(const QkvArgs &a, int grid, hipStream_t s) {
+  switch (a.d_model) {
+    case 64: return launch_dl<T, TI, 64>(a, grid, s);
+    case 128: return launch_dl<T, TI, 128>(a, grid, s);
+    case 256: return launch_dl<T, TI, 256>(a, grid, s);
+    case 512:
+      if constexpr (sizeof(T) == 2) return launch_dl<T, TI, 512>(a, grid, s);
+      return hipErrorInvalidValue;
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+int qkv_tokens_per_tile() { return QKV_NW * 32; }
+
+hipError_t launch_qkv(int dtype, int in_f32, const QkvArgs &a, int grid, hipStream_t s) {
+  if (grid == 0) return hipSuccess;
+  if (dtype == 1) return in_f32 ? launch_d<bf16, float>(a, grid, s) : launch_d<bf16, bf16>(a, grid, s);
+  return launch_d<float, float>(a, grid, s);
+}
+
+}  // namespace ot
