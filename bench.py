@@ -44,7 +44,23 @@ def parse():
     p.add_argument("--dtype", default=None, choices=[None, "bf16", "f32"])
     p.add_argument("--no-trace", action="store_true", help="no per-kernel events in the timed region")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline (0: skip)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain elementwise copy of MIB MiB (fp32 negate: reads and writes MIB MiB "
+                        "once each), to scale the FETCH_SIZE / WRITE_SIZE counters of a profiler run")
     return p.parse_args()
+
+
+def copy_calibration(mib: int) -> None:
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"kernel": "torch neg (fp32, elementwise)", "launches": 3,
+                                           "read_bytes_per_launch": n * 4, "write_bytes_per_launch": n * 4}}))
 
 
 def blas_threads() -> int:
@@ -90,6 +106,9 @@ def main():
         print(f"bench.py: this build runs on one GPU only (got --gpus {a.gpus}); samples are independent, "
               "so N GPUs would each run this same per-GPU step on their own share of the batch.", file=sys.stderr)
         sys.exit(2)
+    if a.copy_calibration:
+        copy_calibration(a.copy_calibration)
+        return
 
     import numpy as np
     import torch

@@ -93,6 +93,8 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) T sVt[DH * LDV];
   __shared__ __attribute__((aligned(16))) T sKw[STAGE2 ? 4 * 32 * LDK : EPC];
   __shared__ __attribute__((aligned(16))) T sVw[STAGE2 ? 4 * DH * LDW : EPC];
+  using TS = TileStage<T>;
+  __shared__ __attribute__((aligned(16))) T stage[4][TS::SIZE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lc = lane & 31;
@@ -218,16 +220,21 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
     softmax_pv<T, DH>(s, scale, m, lsum, o, lc < DH ? &vw[lc * LDW] : nullptr, g);
   }
 
-  // ---- normalise and store O[b][i][h*dh + c] ----------------------------------------------
+  // ---- normalise and store O[b][i][h*dh + c] through the wave's LDS staging tile ---------------
   const float lt = lsum + __shfl_xor(lsum, 32, 64);
-  if (valid) {
-    const float inv = 1.0f / lt;
-    T *orow = (T *)a.o + z * a.o_sb + (long long)qi * a.d_model + h * DH;
+  const float inv = valid ? 1.0f / lt : 0.0f;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int c = acc_row(v, g);
-      if (c < DH) orow[c] = from_f32<T>(o[v] * inv);
-    }
+  for (int v = 0; v < 16; ++v) o[v] *= inv;
+  T *stg = stage[wave];
+  TS::put(stg, o, lc, g);
+#pragma unroll
+  for (int k = 0; k < TS::NI; ++k) {
+    const int tok = TS::token(k, lane);
+    const int tz = __shfl(z, tok, 64), tq = __shfl(qi, tok, 64);
+    const bool tv = __shfl((int)valid, tok, 64) != 0;
+    const u32x4 piece = TS::get(stg, k, lane);
+    const int f = TS::feature(lane);
+    if (tv && f < DH) st16((T *)a.o + tz * a.o_sb + (long long)tq * a.d_model + h * DH + f, piece);
   }
 }
 

@@ -50,6 +50,48 @@ template <> struct Mma<float> {
 __device__ __forceinline__ constexpr int acc_row(int v, int g) { return 8 * (v >> 2) + 4 * g + (v & 3); }
 
 // ---------------------------------------------------------------------------------------------
+// synchronisation and instruction-scheduling helpers
+// ---------------------------------------------------------------------------------------------
+// s_waitcnt constraining only the vector-memory counter (gfx9 encoding: vmcnt bits [3:0] and
+// [15:14]). Vector-memory loads complete in issue order, so waiting for <= N outstanding means
+// every load but the last N issued has landed (for direct-to-LDS loads: its LDS bytes are written).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// s_waitcnt lgkmcnt(0): this wave's LDS reads and writes have completed.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier with no memory fence. __syncthreads() also waits for every outstanding
+// vector-memory access of the wave (vmcnt(0)), which would drain loads issued several chunks
+// ahead; here the caller states exactly what must have completed (wait_vm / wait_lgkm0) before
+// arriving. The empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Instruction order for an unrolled block of NR LDS reads feeding NM MFMAs: PD reads first, then
+// one read after every MFMA, then the remaining MFMAs. Each MFMA's operand was requested PD
+// instructions earlier, which hides the LDS latency behind the matrix pipe (the default schedule
+// keeps only one read in flight to save registers). Place after the block, in the same basic block.
+template <int NR, int NM, int PD>
+__device__ __forceinline__ void sched_lds_mfma() {
+  constexpr int P = PD < NR ? PD : NR;   // never more reads ahead than the block has
+  static_assert(NR - P <= NM, "schedule shape");
+  __builtin_amdgcn_sched_group_barrier(0x100, P, 0);
+#pragma unroll
+  for (int i = 0; i < NR - P; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, NM - (NR - P), 0);
+}
+
+// ---------------------------------------------------------------------------------------------
 // conversions
 // ---------------------------------------------------------------------------------------------
 __device__ __forceinline__ float to_f32(float x) { return x; }
@@ -61,6 +103,44 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf
 // 16-byte vector load / store (both pointers 16-byte aligned).
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+
+// ---------------------------------------------------------------------------------------------
+// Coalesced store of a 32 x 32 accumulator tile whose 32 columns are tokens (lane l % 32) and
+// whose 32 rows are consecutive output features. In registers a lane holds 16 features of its
+// own token spread over the row, so storing straight from registers scatters 4-16 byte pieces
+// over 32 rows. Instead the wave writes the tile into its own LDS staging area and reads it back
+// as row-major 16-byte pieces: store instruction k of lane l writes piece (l % PPR) of token
+// k * TPI + l / PPR, so each instruction covers TPI complete 32-feature runs.
+// ---------------------------------------------------------------------------------------------
+template <typename T>
+struct TileStage {
+  static constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte piece
+  static constexpr int PPR = 32 / EPC;               // pieces per token run of 32 features
+  static constexpr int TPI = 64 / PPR;               // tokens per store instruction
+  static constexpr int NI = 32 / TPI;                // store instructions per tile
+  static constexpr int LD = 32 + EPC;                // staging row (elements), padded by 16 bytes
+  static constexpr int SIZE = 32 * LD;               // staging elements per wave
+
+  // Token (0..31) whose piece this lane stores in instruction k, and that piece's first feature.
+  static __device__ __forceinline__ int token(int k, int lane) { return k * TPI + lane / PPR; }
+  static __device__ __forceinline__ int feature(int lane) { return (lane % PPR) * EPC; }
+
+  // acc element v of lane (lc, g) is feature acc_row(v, g) of token lc.
+  static __device__ __forceinline__ void put(T *stg, const f32x16 &acc, int lc, int g) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      T *d = stg + lc * LD + 8 * j + 4 * g;
+      if constexpr (sizeof(T) == 2) {
+        *(bf16x4 *)d = bf16x4{(bf16)acc[4 * j], (bf16)acc[4 * j + 1], (bf16)acc[4 * j + 2], (bf16)acc[4 * j + 3]};
+      } else {
+        *(f32x4 *)d = f32x4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]};
+      }
+    }
+  }
+  static __device__ __forceinline__ u32x4 get(const T *stg, int k, int lane) {
+    return *(const u32x4 *)(stg + token(k, lane) * LD + feature(lane));
+  }
+};
 
 // ---------------------------------------------------------------------------------------------
 // Row sets. A row set enumerates (sequence b, position t, parameter group) triples:

@@ -13,9 +13,11 @@
 // which accumulates straight into X'^T. An accumulator tile's lane holds the k-indices
 // {4g + r + 8j}; two cross-half lane swaps (v_permlane32_swap) turn it into a natural B fragment.
 //
-// Weight streaming: chunks flow through NB = 2 LDS buffers with direct global->LDS loads
-// (each wave instruction writes 64 x 16 bytes), issued one chunk ahead; a chunk is consumed
-// after the issuing waves' own vmcnt wait and one workgroup barrier. Rows are stored unpadded
+// Weight streaming: chunks flow through a ring of NB = 4 LDS buffers with direct global->LDS
+// loads (each wave instruction writes 64 x 16 bytes), issued three chunks ahead; a chunk is consumed
+// after the issuing waves' own partial vmcnt wait and one fence-free workgroup barrier, so the
+// next chunk's loads stay in flight across it. Within a chunk, LDS operand reads are issued a
+// few MFMAs ahead of their use, and long dependent accumulation chains are split in two. Rows are stored unpadded
 // with their 16-byte pieces XOR-swizzled so that 16 lanes reading 16 consecutive rows touch 16
 // distinct bank groups. The FFN is software-pipelined: while the up-projection of hidden chunk
 // c+1 runs on the matrix cores, the VALU evaluates GELU of chunk c.
@@ -23,6 +25,8 @@
 // GELU is the exact erf form 0.5 x (1 + erf(x / sqrt 2)); erf is evaluated with Abramowitz &
 // Stegun 7.1.26 (|error| <= 1.5e-7): with z = |x|/sqrt2, t = 1/(1 + p z),
 //   GELU(x) = max(x, 0) - |x| * 0.5 t (a1 + t(a2 + t(a3 + t(a4 + t a5)))) * exp(-x^2 / 2).
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -57,13 +61,6 @@ __device__ __forceinline__ constexpr int chunk_swz(int r) {
   return (r / rpb) & (P - 1);
 }
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 // bf16 accumulator-fed B fragment: lane half g holds k {4g..4g+3, 8+4g..8+4g+3} of a 16-block;
 // exchange the middle 8-byte halves between the lane halves to get k {8g .. 8g+7}.
 __device__ __forceinline__ bf16x8 natural_kfrag(bf16x8 f) {
@@ -91,8 +88,11 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64)) void post_kernel(const Post
   constexpr int LPW = BLOCKS / NW;              // wave loads per chunk per wave
   static_assert(BLOCKS % NW == 0 && LPW >= 1, "chunk must split into whole wave loads");
   constexpr int NB = 2;                         // chunk buffers; loads run NB - 1 chunks ahead
+  constexpr int PD = 4;                         // LDS operand reads in flight ahead of the MFMAs
   constexpr bool BF = sizeof(T) == 2;
   __shared__ __attribute__((aligned(16))) T lds[NB][CH];
+  using TS = TileStage<float>;
+  __shared__ __attribute__((aligned(16))) float stage[NW][TS::SIZE];
   // per-feature / per-hidden-unit vectors of this parameter set, fp32: gamma, beta, b2 [d], b1 [d_ff]
   __shared__ __attribute__((aligned(16))) float svec[3 * D + POST_MAX_DFF];
 
@@ -161,13 +161,15 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64)) void post_kernel(const Post
     }
   };
   // Make chunk i visible: this wave's loads of chunk i are done (loads of later chunks may still
-  // be in flight), then every wave's.
+  // be in flight) and its LDS accesses so far have completed (so the buffer of chunk i - 1 may be
+  // refilled), then every wave's.
   auto arrive = [&](int i) {
-    const int later = min(NB - 2, NCH - 1 - i);
+    const int later = min(NB - 2, NCH - 1 - i);   // chunks issued after chunk i so far
     if (later >= 2) wait_vm<2 * LPW>();
     else if (later == 1) wait_vm<LPW>();
     else wait_vm<0>();
-    __syncthreads();
+    wait_lgkm0();
+    bare_barrier();
   };
 
   // A fragment of chunk row `row` for k-chunk kc (row chunks: k = feature; column chunks: k = hidden).
@@ -217,39 +219,45 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64)) void post_kernel(const Post
     }
   }
 
+  // Y^T accumulators start from the residual rows X^T (fp32, or storage dtype in block 0): the
+  // loads are issued here, ahead of the W^O chunks, and each tile's values are needed only by its
+  // own chunk's first MFMA, so their latency hides behind the weight stream.
   f32x16 acc[DT];
-#pragma unroll
-  for (int i = 0; i < DT; ++i) acc[i] = f32x16{};
-
-  // ---- W^O: Y^T = Wo O^T, one 32-feature tile per chunk ---------------------------------------
-#pragma unroll
-  for (int ti = 0; ti < DT; ++ti) {
-    arrive(ti);
-    if (ti + NB - 1 < NCH) issue(ti + NB - 1);
-    const T *base = lds[ti % NB];
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) acc[ti] = M::mma(afrag_rows(base, lc, kc, false), ofr[kc], acc[ti]);
-  }
-
-  // ---- residual, norm2, + b2 ------------------------------------------------------------------
   {
     const TR *xr = (const TR *)a.resid.base + b * a.resid.sb + (long long)(t - a.resid.t_off) * a.resid.rs + 4 * g;
 #pragma unroll
     for (int ti = 0; ti < DT; ++ti)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float xv[4];
         if constexpr (sizeof(TR) == 4) {
           const f32x4 v4 = *(const f32x4 *)(xr + 32 * ti + 8 * j);
-          xv[0] = v4[0]; xv[1] = v4[1]; xv[2] = v4[2]; xv[3] = v4[3];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[ti][4 * j + q] = v4[q];
         } else {
           const bf16x4 v4 = *(const bf16x4 *)(xr + 32 * ti + 8 * j);
-          xv[0] = (float)v4[0]; xv[1] = (float)v4[1]; xv[2] = (float)v4[2]; xv[3] = (float)v4[3];
-        }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[ti][4 * j + q] += xv[q];
+          for (int q = 0; q < 4; ++q) acc[ti][4 * j + q] = (float)v4[q];
+        }
       }
   }
+
+  // ---- W^O: Y^T = X^T + Wo O^T, one 32-feature tile per chunk ---------------------------------
+#pragma unroll
+  for (int ti = 0; ti < DT; ++ti) {
+    arrive(ti);
+    if (ti + NB - 1 < NCH) issue(ti + NB - 1);
+    const T *base = lds[ti % NB];
+    f32x16 odd = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      if (kc & 1) odd = M::mma(afrag_rows(base, lc, kc, false), ofr[kc], odd);
+      else acc[ti] = M::mma(afrag_rows(base, lc, kc, false), ofr[kc], acc[ti]);
+    }
+    sched_lds_mfma<KC, KC, PD>();
+    acc[ti] += odd;
+  }
+
+  // ---- norm2, + b2 ----------------------------------------------------------------------------
   frag yfr[KC];
   {
     float mean = 0.0f;
@@ -304,28 +312,43 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64)) void post_kernel(const Post
     arrive(DT);
     if (DT + NB - 1 < NCH) issue(DT + NB - 1);
     const T *base = lds[DT % NB];
+    f32x16 odd = f32x16{};
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) hacc = M::mma(afrag_rows(base, lc, kc, true), yfr[kc], hacc);
+    for (int kc = 0; kc < KC; ++kc) {
+      if (kc & 1) odd = M::mma(afrag_rows(base, lc, kc, true), yfr[kc], odd);
+      else hacc = M::mma(afrag_rows(base, lc, kc, true), yfr[kc], hacc);
+    }
+    sched_lds_mfma<KC, KC, PD>();
+    hacc += odd;
   }
 
   // ---- FFN: stage A (W1 chunk c+1): up(c+1) interleaved with GELU(c); stage B (W2 chunk c): down(c)
   constexpr int NI = KC > 16 ? KC : 16;
-  for (int c = 0; c < NC; ++c) {
+  // One hidden chunk c: stage A consumes ring slot SA (W1 chunk c + 1), stage B slot SB (W2 chunk
+  // c). The slots are compile-time constants (the loop below handles two chunks per iteration,
+  // NC is even), so every LDS operand address is a fixed per-lane offset.
+  auto ffn_step = [&](int c, auto sa, auto sb) {
+    constexpr int SA = decltype(sa)::value, SB = decltype(sb)::value;
     const int ia = DT + 1 + 2 * c;
     // stage A
     arrive(ia);
     if (ia + NB - 1 < NCH) issue(ia + NB - 1);
-    f32x16 hn = f32x16{};
+    f32x16 hn = f32x16{}, hn_odd = f32x16{};
     float hv[16];
     {
-      const T *base = lds[ia % NB];
+      const T *base = lds[SA];
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         // the last chunk's look-ahead multiplies W1 chunk 0 again; the result is discarded
-        if (i < KC) hn = M::mma(afrag_rows(base, lc, i, true), yfr[i], hn);
+        if (i < KC) {
+          if (i & 1) hn_odd = M::mma(afrag_rows(base, lc, i, true), yfr[i], hn_odd);
+          else hn = M::mma(afrag_rows(base, lc, i, true), yfr[i], hn);
+        }
         if (i < 16) hv[i] = gelu_as(hacc[i] + s_b1[32 * c + acc_row(i, g)]);
       }
+      sched_lds_mfma<KC, KC, PD>();
     }
+    hn += hn_odd;
     frag hfr[HKC];
     if constexpr (BF) {
 #pragma unroll
@@ -343,23 +366,42 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64)) void post_kernel(const Post
     arrive(ia + 1);
     if (ia + NB < NCH) issue(ia + NB);
     {
-      const T *base = lds[(ia + 1) % NB];
+      const T *base = lds[SB];
 #pragma unroll
       for (int ti = 0; ti < DT; ++ti)
 #pragma unroll
         for (int kc = 0; kc < HKC; ++kc) acc[ti] = M::mma(afrag_cols(base, 32 * ti + lc, kc), hfr[kc], acc[ti]);
+      sched_lds_mfma<DT * HKC, DT * HKC, PD>();
     }
     hacc = hn;
+  };
+  static_assert(NB % 2 == 0, "two hidden chunks per iteration need an even ring");
+  for (int c = 0; c < NC; c += 2) {
+    ffn_step(c, std::integral_constant<int, (DT + 1) % NB>{}, std::integral_constant<int, (DT + 2) % NB>{});
+    ffn_step(c + 1, std::integral_constant<int, (DT + 3) % NB>{}, std::integral_constant<int, (DT + 4) % NB>{});
   }
 
-  // ---- store X' (fp32, this lane's token) -----------------------------------------------------
-  if (valid) {
-    float *xo = (float *)a.out.base + b * a.out.sb + (long long)(t - a.out.t_off) * a.out.rs;
+  // ---- store X' (fp32) tile by tile through the wave's LDS staging area ------------------------
+  {
+    float *stg = stage[wave];
+    float *rowp[TS::NI];
+    bool rv[TS::NI];
 #pragma unroll
-    for (int ti = 0; ti < DT; ++ti)
+    for (int k = 0; k < TS::NI; ++k) {
+      const int tok = TS::token(k, lane);
+      const int tb = __shfl(b, tok, 64), tt = __shfl(t, tok, 64);
+      rv[k] = __shfl((int)valid, tok, 64) != 0;
+      rowp[k] = (float *)a.out.base + tb * a.out.sb + (long long)(tt - a.out.t_off) * a.out.rs + TS::feature(lane);
+    }
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *(f32x4 *)(xo + 32 * ti + 8 * j + 4 * g) = f32x4{acc[ti][4 * j], acc[ti][4 * j + 1], acc[ti][4 * j + 2], acc[ti][4 * j + 3]};
+    for (int ti = 0; ti < DT; ++ti) {
+      TS::put(stg, acc[ti], lc, g);
+#pragma unroll
+      for (int k = 0; k < TS::NI; ++k) {
+        const u32x4 piece = TS::get(stg, k, lane);
+        if (rv[k]) st16(rowp[k] + 32 * ti, piece);
+      }
+    }
   }
 }
 

@@ -7,8 +7,15 @@
 // one cross-half shuffle, and keeps the normalised row as bf16 B fragments in registers. The
 // projection weights stream through LDS in chunks of 32 output features x d (direct global->LDS
 // loads, XOR-swizzled rows, double-buffered): with d_head = 32 a chunk is exactly one head, and
-// each accumulator tile is written straight into the head-major Q/K/V (or K/V cache) rows.
-// Chunks of W_Q are skipped by workgroups holding no query row, and Q stores are masked per token.
+// each accumulator tile is written into the head-major Q/K/V (or K/V cache) rows through a
+// per-wave LDS staging tile. Chunks of W_Q are skipped by workgroups holding no query row, and Q
+// stores are masked per token.
+//
+// Roles: the four compute waves never wait for their own stores. A fifth, loader wave issues
+// every weight-chunk load and waits for its own vector-memory counter; the chunk handoff is a
+// plain s_barrier (no memory fence), so output stores stay in flight across chunks. (One
+// counter covers both loads and stores on this architecture, so a compute wave waiting for a
+// chunk would otherwise also wait for its previous chunk's stores.)
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -24,16 +31,10 @@ __device__ __forceinline__ constexpr int chunk_swz(int r) {
   return (r / rpb) & (P - 1);
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-constexpr int QKV_NW = 4;
+constexpr int QKV_NW = 4;                 // compute waves; one loader wave more per workgroup
 
 template <typename T, typename TI, int D, bool LAYER>
-__global__ __launch_bounds__(QKV_NW * 64) void qkv_kernel(const QkvArgs a) {
+__global__ __launch_bounds__((QKV_NW + 1) * 64) void qkv_kernel(const QkvArgs a) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int NW = QKV_NW;
@@ -42,16 +43,17 @@ __global__ __launch_bounds__(QKV_NW * 64) void qkv_kernel(const QkvArgs a) {
   constexpr int KC = D / M::KSTEP;
   constexpr int RPA = D / EPC;                  // 16-byte pieces per weight row
   constexpr int CH = 32 * D;
-  constexpr int BLOCKS = CH / EPC / 64;
-  constexpr int LPW = BLOCKS / NW;
-  static_assert(BLOCKS % NW == 0 && LPW >= 1, "chunk must split into whole wave loads");
+  constexpr int BLOCKS = CH / EPC / 64;         // 1 KB loads per chunk, all issued by the loader wave
   constexpr bool BF = sizeof(T) == 2;
+  using TS = TileStage<T>;
   __shared__ __attribute__((aligned(16))) T lds[2][CH];
+  __shared__ __attribute__((aligned(16))) T stage[NW][TS::SIZE];
   __shared__ float s_gm[D], s_bt[D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lc = lane & 31;
   const int dh = a.d_head;
+  const bool loader = wave == NW;
 
   // ---- job / group / token tile --------------------------------------------------------------
   const int bid = blockIdx.x;
@@ -61,34 +63,45 @@ __global__ __launch_bounds__(QKV_NW * 64) void qkv_kernel(const QkvArgs a) {
   const int wg = jb.rs.wg0 + grp;
   const int M_rows = jb.rs.n_seq * jb.rs.rows;
   const int r0 = tm * (NW * 32) + wave * 32 + lc;
-  const bool valid = r0 < M_rows;
+  const bool valid = !loader && r0 < M_rows;
   const int r = valid ? r0 : 0;
   const int b = r / jb.rs.rows;
   const int t = jb.rs.t0 + grp * jb.rs.t_step + (r - b * jb.rs.rows);
   const bool lane_q = valid && t >= jb.q_from;
   const bool tile_q = __syncthreads_or(lane_q);   // does any token of this workgroup issue a query?
+  // tokens whose 16-byte output pieces this lane stores (one per store instruction)
+  int sb[TS::NI], stt[TS::NI];
+  bool sval[TS::NI], sq[TS::NI];
+#pragma unroll
+  for (int k = 0; k < TS::NI; ++k) {
+    const int tok = TS::token(k, lane);
+    sb[k] = __shfl(b, tok, 64);
+    stt[k] = __shfl(t, tok, 64);
+    sval[k] = __shfl((int)valid, tok, 64) != 0;
+    sq[k] = __shfl((int)lane_q, tok, 64) != 0;
+  }
+  T *stg = stage[loader ? 0 : wave];
 
   // chunk stream: K chunks 0..DT-1, V chunks, then (if any query row) Q chunks
   const int n_chunks = tile_q ? 3 * DT : 2 * DT;
   const T *wk = (const T *)a.wk + (size_t)wg * D * D;
   const T *wv = (const T *)a.wv + (size_t)wg * D * D;
   const T *wq = (const T *)a.wq + (size_t)wg * D * D;
-  auto issue = [&](int i) {
+  auto issue = [&](int i) {   // loader wave only
     const int seg = i / DT, ci = i - seg * DT;
     const T *base = (seg == 0 ? wk : seg == 1 ? wv : wq) + (size_t)(32 * ci) * D;
     T *dst = lds[i & 1];
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-      const int blk = j * NW + wave;
+    for (int blk = 0; blk < BLOCKS; ++blk) {
       const int P = blk * 64 + lane;
       const int row = P / RPA, q = P % RPA;
       __builtin_amdgcn_global_load_lds((const void *)(base + row * D + (q ^ chunk_swz<RPA, RPA * 16>(row)) * EPC),
                                        (__attribute__((address_space(3))) void *)(dst + blk * 64 * EPC), 16, 0, 0);
     }
   };
-  issue(0);
+  if (loader) issue(0);
 
-  for (int i = tid; i < D; i += NW * 64) {
+  for (int i = tid; i < D; i += (NW + 1) * 64) {
     s_gm[i] = to_f32(((const T *)a.gamma)[i]);
     s_bt[i] = LAYER ? to_f32(((const T *)a.beta)[i]) : 0.0f;
   }
@@ -143,11 +156,21 @@ __global__ __launch_bounds__(QKV_NW * 64) void qkv_kernel(const QkvArgs a) {
     }
   }
 
-  // ---- chunk loop -----------------------------------------------------------------------------
-  for (int i = 0; i < n_chunks; ++i) {
+  // ---- chunk loop: barrier B_i makes chunk i visible and frees buffer (i + 1) & 1 -------------
+  if (loader) {
     wait_vm<0>();
-    __syncthreads();
-    if (i + 1 < n_chunks) issue(i + 1);
+    bare_barrier();                  // B_0
+    for (int i = 0; i < n_chunks; ++i) {
+      if (i + 1 < n_chunks) {
+        issue(i + 1);
+        wait_vm<0>();
+      }
+      bare_barrier();                // B_{i+1}
+    }
+    return;
+  }
+  bare_barrier();                    // B_0
+  for (int i = 0; i < n_chunks; ++i) {
     const T *base = lds[i & 1];
     f32x16 acc = f32x16{};
 #pragma unroll
@@ -162,33 +185,31 @@ __global__ __launch_bounds__(QKV_NW * 64) void qkv_kernel(const QkvArgs a) {
       }
       acc = M::mma(af, xfr[kc], acc);
     }
-    // output features 32 ci + 8 j + 4 g + r (r = 0..3) of this lane's token
+    // 32 output features 32 ci .. 32 ci + 31 of every token: stage through LDS, store whole runs
     const int seg = i / DT, ci = i - seg * DT;
     const HeadView &hv = seg == 0 ? jb.k : seg == 1 ? jb.v : jb.q;
-    const bool st = seg < 2 ? valid : lane_q;
-    if (st) {
-      T *ob = (T *)hv.base + b * hv.sb + (long long)(t - hv.t_off) * dh;
+    TS::put(stg, acc, lc, g);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int f = 32 * ci + 8 * j + 4 * g;       // 4 consecutive features, same head
+    for (int k = 0; k < TS::NI; ++k) {
+      const u32x4 piece = TS::get(stg, k, lane);
+      if (seg < 2 ? sval[k] : sq[k]) {
+        const int f = 32 * ci + TS::feature(lane);
         const int h = f / dh, c = f - h * dh;
-        T *o = ob + h * hv.sh + c;
-        if constexpr (BF) {
-          *(bf16x4 *)o = bf16x4{(bf16)acc[4 * j], (bf16)acc[4 * j + 1], (bf16)acc[4 * j + 2], (bf16)acc[4 * j + 3]};
-        } else {
-          *(f32x4 *)o = f32x4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]};
-        }
+        st16((T *)hv.base + sb[k] * hv.sb + h * hv.sh + (long long)(stt[k] - hv.t_off) * dh + c, piece);
       }
     }
+    // this wave's LDS reads of chunk i are complete once their data fed the MFMAs above
+    wait_lgkm0();
+    bare_barrier();                  // B_{i+1}
   }
 }
 
 template <typename T, typename TI, int D>
 hipError_t launch_dl(const QkvArgs &a, int grid, hipStream_t s) {
   if (a.layer)
-    hipLaunchKernelGGL((qkv_kernel<T, TI, D, true>), dim3(grid), dim3(QKV_NW * 64), 0, s, a);
+    hipLaunchKernelGGL((qkv_kernel<T, TI, D, true>), dim3(grid), dim3((QKV_NW + 1) * 64), 0, s, a);
   else
-    hipLaunchKernelGGL((qkv_kernel<T, TI, D, false>), dim3(grid), dim3(QKV_NW * 64), 0, s, a);
+    hipLaunchKernelGGL((qkv_kernel<T, TI, D, false>), dim3(grid), dim3((QKV_NW + 1) * 64), 0, s, a);
   return hipGetLastError();
 }
 
