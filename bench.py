@@ -94,10 +94,18 @@ def kernel_table(classes, timing, steps, n_units, peak_tflops):
     return out
 
 
-def dominant(classes, timing, steps, n_units, peak_tflops):
+def dominant(classes, timing, steps, n_units, peak_tflops, workload):
     k = max((c for c in timing if timing[c][1] > 0), key=lambda c: timing[c][0])
     ms, cnt = timing[k]
-    return roofline_entry(k, classes[k] * n_units * steps, ms, cnt, peak_tflops, "TFLOP/s", "mfma")
+    entry = roofline_entry(k, classes[k] * n_units * steps, ms, cnt, peak_tflops, "TFLOP/s", "mfma")
+    # HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary of this
+    # kernel and workload, scaled by the copy-kernel calibration; null when that record was taken
+    # on a different version of the kernel source.
+    from unified_transformer_recommender_amd import profsummary
+    rec = profsummary.read_traffic(os.path.join(ROOT, "profiles", f"traffic_{k}_{workload}.txt"))
+    if rec is not None:
+        entry["traffic"] = float(rec["traffic_bytes_per_launch"])
+    return entry
 
 
 def main():
@@ -239,7 +247,7 @@ def main():
     flops_unit = sum(classes.values())
     mfma_frac = flops_unit * n_units / (ms_step * 1e-3) / 1e12 / peak
     kernels = kernel_table(classes, timing, a.steps, n_units, peak)
-    roof = dominant(classes, timing, a.steps, n_units, peak)
+    roof = dominant(classes, timing, a.steps, n_units, peak, w.key)
 
     # CPU baseline: the oracle on a bounded sample of the same workload
     cpu = None

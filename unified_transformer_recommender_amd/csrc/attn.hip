@@ -99,10 +99,22 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lc = lane & 31;
   const int H = a.n_heads;
-  const int per_q = a.n_seq_grp * H;
-  const int qb = a.n_qblocks - 1 - (int)(blockIdx.x / per_q);   // longest query blocks first
-  const int rem = blockIdx.x - (int)(blockIdx.x / per_q) * per_q;
-  const int h = rem % H, grp = rem / H;
+  // Work order. Workgroups are dispatched round-robin over the 8 XCDs (block b runs on XCD b % 8),
+  // and each XCD has its own L2. XCD x takes a contiguous range of logical work items lg, and lg
+  // walks groups of ATTN_GROUP (sequence/user, head) pairs: within a group the longest query
+  // blocks of all its pairs go first, then the shorter ones. All query blocks of a pair thus run on
+  // one XCD close together in time (its K/V rows come from HBM once), and each group still starts
+  // with its heaviest workgroups.
+  constexpr int ATTN_GROUP = 8;
+  const int total = gridDim.x, nq = a.n_qblocks, n_pairs = a.n_seq_grp * H;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int lg = xcd * (total >> 3) + min(xcd, total & 7) + slot;
+  const int group = lg / (ATTN_GROUP * nq);
+  const int r = lg - group * ATTN_GROUP * nq;
+  const int gp = min(ATTN_GROUP, n_pairs - group * ATTN_GROUP);   // pairs in this group
+  const int qb = nq - 1 - r / gp;
+  const int pair = group * ATTN_GROUP + r % gp;
+  const int h = pair % H, grp = pair / H;
 
   // ---- this lane's query --------------------------------------------------------------------
   int z, qi, cslot = 0, cpw = 0, c_first = 0;

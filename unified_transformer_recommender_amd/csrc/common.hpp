@@ -74,6 +74,19 @@ __device__ __forceinline__ void bare_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Direct global->LDS load of 16 bytes per lane: lane i's bytes land at LDS byte address
+// lds_base + 16 i (lds_base is wave-uniform). Written as inline assembly so that the compiler's
+// wait-count bookkeeping does not see an outstanding LDS write: with the builtin, every later LDS
+// read waits for lgkmcnt(0), which serialises the operand reads of the MFMA loops. The caller
+// waits for completion explicitly (wait_vm) before the data is read; the asm has no outputs.
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(src) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) void *)p;
+}
+
 // Instruction order for an unrolled block of NR LDS reads feeding NM MFMAs: PD reads first, then
 // one read after every MFMA, then the remaining MFMAs. Each MFMA's operand was requested PD
 // instructions earlier, which hides the LDS latency behind the matrix pipe (the default schedule

@@ -156,8 +156,7 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64)) void post_kernel(const Post
         const int row = P / RPB, q = P % RPB;
         src = base + (size_t)row * DFF + (q ^ chunk_swz<RPB, RPB * 16>(row)) * EPC;
       }
-      __builtin_amdgcn_global_load_lds((const void *)src, (__attribute__((address_space(3))) void *)(dst + blk * 64 * EPC),
-                                       16, 0, 0);
+      dma16(src, lds_addr(dst + blk * 64 * EPC));
     }
   };
   // Make chunk i visible: this wave's loads of chunk i are done (loads of later chunks may still
@@ -368,9 +367,9 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64)) void post_kernel(const Post
     {
       const T *base = lds[SB];
 #pragma unroll
-      for (int ti = 0; ti < DT; ++ti)
+      for (int kc = 0; kc < HKC; ++kc)
 #pragma unroll
-        for (int kc = 0; kc < HKC; ++kc) acc[ti] = M::mma(afrag_cols(base, 32 * ti + lc, kc), hfr[kc], acc[ti]);
+        for (int ti = 0; ti < DT; ++ti) acc[ti] = M::mma(afrag_cols(base, 32 * ti + lc, kc), hfr[kc], acc[ti]);
       sched_lds_mfma<DT * HKC, DT * HKC, PD>();
     }
     hacc = hn;
