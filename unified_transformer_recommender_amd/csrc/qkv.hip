@@ -32,9 +32,10 @@ __device__ __forceinline__ constexpr int chunk_swz(int r) {
 }
 
 constexpr int QKV_NW = 4;                 // compute waves; one loader wave more per workgroup
+constexpr int QKV_NB = 2;                 // weight-chunk ring slots; the loader runs QKV_NB - 1 chunks ahead
 
 template <typename T, typename TI, int D, bool LAYER>
-__global__ __launch_bounds__((QKV_NW + 1) * 64) void qkv_kernel(const QkvArgs a) {
+__global__ __launch_bounds__((QKV_NW + 1) * 64, 2) void qkv_kernel(const QkvArgs a) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int NW = QKV_NW;
@@ -46,7 +47,8 @@ __global__ __launch_bounds__((QKV_NW + 1) * 64) void qkv_kernel(const QkvArgs a)
   constexpr int BLOCKS = CH / EPC / 64;         // 1 KB loads per chunk, all issued by the loader wave
   constexpr bool BF = sizeof(T) == 2;
   using TS = TileStage<T>;
-  __shared__ __attribute__((aligned(16))) T lds[2][CH];
+  constexpr int NB = CH * (int)sizeof(T) <= 16384 ? QKV_NB : 2;   // 32 KB chunks: two slots
+  __shared__ __attribute__((aligned(16))) T lds[NB][CH];
   __shared__ __attribute__((aligned(16))) T stage[NW][TS::SIZE];
   __shared__ float s_gm[D], s_bt[D];
 
@@ -90,7 +92,7 @@ __global__ __launch_bounds__((QKV_NW + 1) * 64) void qkv_kernel(const QkvArgs a)
   auto issue = [&](int i) {   // loader wave only
     const int seg = i / DT, ci = i - seg * DT;
     const T *base = (seg == 0 ? wk : seg == 1 ? wv : wq) + (size_t)(32 * ci) * D;
-    T *dst = lds[i & 1];
+    T *dst = lds[i % NB];
 #pragma unroll
     for (int blk = 0; blk < BLOCKS; ++blk) {
       const int P = blk * 64 + lane;
@@ -99,7 +101,10 @@ __global__ __launch_bounds__((QKV_NW + 1) * 64) void qkv_kernel(const QkvArgs a)
                                        (__attribute__((address_space(3))) void *)(dst + blk * 64 * EPC), 16, 0, 0);
     }
   };
-  if (loader) issue(0);
+  if (loader) {
+#pragma unroll
+    for (int i = 0; i < NB - 1; ++i) issue(i);   // n_chunks >= 2 * (d / 32) >= NB - 1
+  }
 
   for (int i = tid; i < D; i += (NW + 1) * 64) {
     s_gm[i] = to_f32(((const T *)a.gamma)[i]);
@@ -107,71 +112,129 @@ __global__ __launch_bounds__((QKV_NW + 1) * 64) void qkv_kernel(const QkvArgs a)
   }
 
   // ---- norm1 of this lane's token -> bf16 B fragments (k = 16 kc + 8 g + e) ------------------
+  // A lane holds half of its token's row (the other half sits in lane +- 32). For bf16 storage at
+  // d >= 256 the row is read twice: once for the statistics, in two halves, and once more (from
+  // cache) to normalise. That keeps at most a quarter row live in registers, so two workgroups fit
+  // on a CU and one's row loads overlap the other's chunk loop. LayerNorm statistics are taken
+  // about the row's first element, which keeps the one-pass variance free of cancellation.
   frag xfr[KC];
   {
     const TI *xr = (const TI *)a.x.base + b * a.x.sb + (long long)(t - a.x.t_off) * a.x.rs;
-    constexpr int PER = D / 2;                 // features held by this lane
-    float xv[PER];
+    if constexpr (BF && D >= 256) {
+      constexpr int HALF = KC / 2;
+      const float shift = LAYER ? to_f32(xr[0]) : 0.0f;
+      float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      if constexpr (BF) {
-        const TI *p = xr + 16 * kc + 8 * g;
+      for (int part = 0; part < 2; ++part) {
+        float xv[8 * HALF];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) xv[8 * kc + e] = to_f32(p[e]);
-      } else {
-        xv[kc] = to_f32(xr[2 * kc + g]);
+        for (int k = 0; k < HALF; ++k) {
+          const TI *p = xr + 16 * (part * HALF + k) + 8 * g;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xv[8 * k + e] = to_f32(p[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8 * HALF; ++e) {
+          const float c = xv[e] - shift;
+          s1 += c;
+          s2 += c * c;
+        }
       }
-    }
-    float mean = 0.0f;
-    if constexpr (LAYER) {
-      float s = 0.0f;
+      s1 += __shfl_xor(s1, 32, 64);
+      s2 += __shfl_xor(s2, 32, 64);
+      const float m1 = s1 * (1.0f / D);
+      const float mean = LAYER ? shift + m1 : 0.0f;
+      const float var = LAYER ? fmaxf(s2 * (1.0f / D) - m1 * m1, 0.0f) : s2 * (1.0f / D);
+      const float rstd = 1.0f / sqrtf(var + a.eps);
+      __syncthreads();                           // gamma / beta staged
+      asm volatile("" ::: "memory");             // read the row again rather than keep it live
 #pragma unroll
-      for (int e = 0; e < PER; ++e) s += xv[e];
-      s += __shfl_xor(s, 32, 64);
-      mean = s * (1.0f / D);
-    }
-    float ss = 0.0f;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const float c = xv[e] - mean;
-      ss += c * c;
-    }
-    ss += __shfl_xor(ss, 32, 64);
-    const float rstd = 1.0f / sqrtf(ss * (1.0f / D) + a.eps);
-    __syncthreads();                           // gamma / beta staged
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      if constexpr (BF) {
+      for (int kc = 0; kc < KC; ++kc) {
+        const TI *p = xr + 16 * kc + 8 * g;
         frag fr;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int f = 16 * kc + 8 * g + e;
-          fr[e] = (bf16)((xv[8 * kc + e] - mean) * rstd * s_gm[f] + s_bt[f]);
+          fr[e] = (bf16)((to_f32(p[e]) - mean) * rstd * s_gm[f] + s_bt[f]);
         }
         xfr[kc] = fr;
-      } else {
-        const int f = 2 * kc + g;
-        xfr[kc] = (xv[kc] - mean) * rstd * s_gm[f] + s_bt[f];
+      }
+    } else {
+      constexpr int PER = D / 2;                 // features held by this lane
+      float xv[PER];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        if constexpr (BF) {
+          const TI *p = xr + 16 * kc + 8 * g;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xv[8 * kc + e] = to_f32(p[e]);
+        } else {
+          xv[kc] = to_f32(xr[2 * kc + g]);
+        }
+      }
+      float mean = 0.0f;
+      if constexpr (LAYER) {
+        float s = 0.0f;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) s += xv[e];
+        s += __shfl_xor(s, 32, 64);
+        mean = s * (1.0f / D);
+      }
+      float ss = 0.0f;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const float c = xv[e] - mean;
+        ss += c * c;
+      }
+      ss += __shfl_xor(ss, 32, 64);
+      const float rstd = 1.0f / sqrtf(ss * (1.0f / D) + a.eps);
+      __syncthreads();                           // gamma / beta staged
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        if constexpr (BF) {
+          frag fr;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int f = 16 * kc + 8 * g + e;
+            fr[e] = (bf16)((xv[8 * kc + e] - mean) * rstd * s_gm[f] + s_bt[f]);
+          }
+          xfr[kc] = fr;
+        } else {
+          const int f = 2 * kc + g;
+          xfr[kc] = (xv[kc] - mean) * rstd * s_gm[f] + s_bt[f];
+        }
       }
     }
   }
 
-  // ---- chunk loop: barrier B_i makes chunk i visible and frees buffer (i + 1) & 1 -------------
+  // ---- chunk loop: barrier B_i makes chunk i visible and frees the slot of chunk i - 1 ----------
+  // Loader: before B_i, chunk i has landed; after B_i every compute wave has finished reading
+  // chunk i - 1, so its slot takes chunk i + NB - 1. Loads complete in issue order, so waiting for
+  // "at most k * BLOCKS outstanding" leaves exactly the k most recently issued chunks in flight.
+  auto wait_chunk = [&](int later) {   // later = chunks issued after the awaited one
+    if constexpr (2 * BLOCKS < 64) {
+      if (later >= 2) wait_vm<2 * BLOCKS>();
+      else if (later == 1) wait_vm<BLOCKS>();
+      else wait_vm<0>();
+      return;
+    }
+    if (later >= 1) wait_vm<BLOCKS>();
+    else wait_vm<0>();
+  };
   if (loader) {
-    wait_vm<0>();
+    static_assert(NB <= 4 && BLOCKS < 64 && (NB <= 2 || 2 * BLOCKS < 64), "wait counts cover at most two chunks in flight");
+    wait_chunk(min(NB - 2, n_chunks - 1));
     bare_barrier();                  // B_0
     for (int i = 0; i < n_chunks; ++i) {
-      if (i + 1 < n_chunks) {
-        issue(i + 1);
-        wait_vm<0>();
-      }
+      if (i + NB - 1 < n_chunks) issue(i + NB - 1);
+      if (i + 1 < n_chunks) wait_chunk(min(NB - 2, n_chunks - 2 - i));
       bare_barrier();                // B_{i+1}
     }
     return;
   }
   bare_barrier();                    // B_0
   for (int i = 0; i < n_chunks; ++i) {
-    const T *base = lds[i & 1];
+    const T *base = lds[i % NB];
     f32x16 acc = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
