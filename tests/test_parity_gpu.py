@@ -62,6 +62,18 @@ def test_mid_shape_ragged_tiles(dtype):
     _forward_case(w)
 
 
+@pytest.mark.parametrize("norm", ["rms", "layer"])
+def test_d128_shape_both_norms(norm):
+    """d=128 / 4 heads in bf16 (the wave-pair post-attention kernel at its narrower width), with
+    RMSNorm and LayerNorm, ragged tiles and a pyramid."""
+    base = synth.workload("onetrans_s")
+    m = replace(base.model, n_blocks=3, d_model=128, n_heads=4, d_ff=512, norm=norm,
+                norm_eps=1e-6 if norm == "rms" else 1e-5, dtype="bf16")
+    w = replace(base, model=m, l_s=181, s_queries=(181, 97, 3), seq_lens=(50, 60, 68), batch=5,
+                key=f"d128_{norm}")
+    _forward_case(w)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_two_stage_small(dtype):
     w = synth.test_workload("tiny3_two_stage", dtype)

@@ -7,15 +7,17 @@
 // of a candidate's NS query j are the user's cached S rows followed by the candidate's own NS
 // rows 0..j, one softmax over both.
 //
-// Work layout: a workgroup (4 waves) handles one (sequence or user, head) and up to 128 query
-// rows; a wave owns 32 query rows. Scores are formed transposed, S^T = K Q^T, with one MFMA
-// 32x32 tile per 32 keys, so a lane holds 16 of the 32 keys of ONE query (its column) and the
-// softmax statistics of that query stay in the lane (one cross-half shuffle per tile). The
-// probabilities are then already laid out as the B operand of O^T += V^T P^T: the k index of that
-// product is a permutation of the 32 keys, and the V^T operand is read with the same permutation
-// from an LDS copy of V stored transposed ([d_head][key]). K/V tiles of 64 keys are staged in LDS
-// once per workgroup and shared by its four waves. Online softmax in base 2 with the 1/sqrt(dh)
-// scale folded into one FMA per score; fully masked tiles are skipped per wave.
+// Work layout: a workgroup (ATTN_WAVES waves) handles one (sequence or user, head) and up to
+// 32 * ATTN_WAVES query rows; a wave owns 32 query rows. Scores are formed transposed,
+// S^T = K Q^T, with one MFMA 32x32 tile per 32 keys, so a lane holds 16 of the 32 keys of ONE
+// query (its column) and the softmax statistics of that query stay in the lane (one cross-half
+// swap per tile). The probabilities are then already laid out as the B operand of
+// O^T += V^T P^T: the k index of that product is a permutation of the 32 keys, and the V^T
+// operand is read with the same permutation from an LDS copy of V stored transposed
+// ([d_head][key]). K/V tiles of 16 * ATTN_WAVES keys are staged in LDS once per workgroup and
+// shared by all its waves. Online softmax in base 2 with the 1/sqrt(dh) scale folded into one FMA
+// per score; fully masked tiles are skipped per wave; the accumulator is rescaled only when a
+// tile raises the running maximum by more than a fixed headroom.
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -48,6 +50,20 @@ template <> struct VtFrag<float> {
   static __device__ __forceinline__ float pfrag(const float *p, int mc) { return p[mc]; }
 };
 
+// The value x of the lane in the other half of the wave (lane ^ 32), by one cross-half swap.
+__device__ __forceinline__ float other_half(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  // sw[0]: upper lanes now hold the lower lanes' x; sw[1]: lower lanes hold the upper lanes' x
+  return __uint_as_float((threadIdx.x & 32) ? sw[0] : sw[1]);
+}
+
+// Headroom (in base-2 exponent units) of the running maximum: a tile whose maximum exceeds the
+// running one by at most this much is folded in against the stale maximum, so its probabilities
+// are at most 2^8 and the accumulator need not be rescaled. The final division by the running
+// sum, taken against the same maximum, gives the same softmax.
+constexpr float RESCALE_HEADROOM = 8.0f;
+
 // One 32-key tile: fold masked scores s (already -inf where invisible) into the running state.
 template <typename T, int DH>
 __device__ __forceinline__ void softmax_pv(const f32x16 &s, float scale, float &m, float &lsum, f32x16 &o,
@@ -57,11 +73,16 @@ __device__ __forceinline__ void softmax_pv(const f32x16 &s, float scale, float &
   float mt = s[0];
 #pragma unroll
   for (int v = 1; v < 16; ++v) mt = fmaxf(mt, s[v]);
-  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-  const float mn = fmaxf(m, mt);
-  const float alpha = __builtin_amdgcn_exp2f((m - mn) * scale);
-  const float nb = -mn * scale;
-  m = mn;
+  mt = fmaxf(mt, other_half(mt));
+  if (__any((mt - m) * scale > RESCALE_HEADROOM)) {   // wave-uniform: raise the maximum and rescale
+    const float mn = fmaxf(m, mt);
+    const float alpha = __builtin_amdgcn_exp2f((m - mn) * scale);
+    m = mn;
+    lsum *= alpha;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o[v] *= alpha;
+  }
+  const float nb = -m * scale;
   float p[16];
   float ps = 0.0f;
 #pragma unroll
@@ -69,9 +90,7 @@ __device__ __forceinline__ void softmax_pv(const f32x16 &s, float scale, float &
     p[v] = __builtin_amdgcn_exp2f(fmaf(s[v], scale, nb));
     ps += p[v];
   }
-  lsum = lsum * alpha + ps;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) o[v] *= alpha;
+  lsum += ps;
 #pragma unroll
   for (int mc = 0; mc < 32 / M::KSTEP; ++mc) {
     typename M::frag vf = vt_row ? VtFrag<T>::load(vt_row, mc, g) : M::zero();
@@ -80,21 +99,22 @@ __device__ __forceinline__ void softmax_pv(const f32x16 &s, float scale, float &
 }
 
 template <typename T, int DH, bool STAGE2>
-__global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(ATTN_WAVES * 64) void attn_kernel(const AttnArgs a) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int EPC = 16 / (int)sizeof(T);
-  constexpr int KT = 64;             // keys per shared tile
+  constexpr int NWA = ATTN_WAVES;
+  constexpr int KT = 16 * NWA;       // keys per shared tile (one K and one V piece per thread at d_head 32)
   constexpr int LDK = DH + EPC;      // padded K row (elements)
   constexpr int LDV = KT + EPC;      // padded V^T row (keys)
   constexpr int LDW = 32 + EPC;      // padded V^T row of a wave's own-key tile
   constexpr int CPK = DH / EPC;      // 16-byte chunks per key row
   __shared__ __attribute__((aligned(16))) T sK[KT * LDK];
   __shared__ __attribute__((aligned(16))) T sVt[DH * LDV];
-  __shared__ __attribute__((aligned(16))) T sKw[STAGE2 ? 4 * 32 * LDK : EPC];
-  __shared__ __attribute__((aligned(16))) T sVw[STAGE2 ? 4 * DH * LDW : EPC];
+  __shared__ __attribute__((aligned(16))) T sKw[STAGE2 ? NWA * 32 * LDK : EPC];
+  __shared__ __attribute__((aligned(16))) T sVw[STAGE2 ? NWA * DH * LDW : EPC];
   using TS = TileStage<T>;
-  __shared__ __attribute__((aligned(16))) T stage[4][TS::SIZE];
+  __shared__ __attribute__((aligned(16))) T stage[NWA][TS::SIZE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lc = lane & 31;
@@ -127,7 +147,7 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
     cpw = 32 / a.R;
     cslot = lc / a.R;
     qi = lc - cslot * a.R;
-    c_first = qb * 4 * cpw + wave * cpw;
+    c_first = qb * NWA * cpw + wave * cpw;
     const int c = c_first + cslot;
     valid = cslot < cpw && c < a.n_cand;
     z = grp * a.n_cand + (valid ? c : 0);
@@ -162,7 +182,7 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
 
   for (int k0 = 0; k0 < n_keys; k0 += KT) {
     __syncthreads();
-    for (int ch = tid; ch < KT * CPK; ch += 256) {
+    for (int ch = tid; ch < KT * CPK; ch += NWA * 64) {
       const int key = ch / CPK, c0 = (ch - key * CPK) * EPC;
       const int kg = k0 + key;
       u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
@@ -233,7 +253,7 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
   }
 
   // ---- normalise and store O[b][i][h*dh + c] through the wave's LDS staging tile ---------------
-  const float lt = lsum + __shfl_xor(lsum, 32, 64);
+  const float lt = lsum + other_half(lsum);
   const float inv = valid ? 1.0f / lt : 0.0f;
 #pragma unroll
   for (int v = 0; v < 16; ++v) o[v] *= inv;
@@ -252,7 +272,7 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
 
 template <typename T, int DH>
 hipError_t launch_dh(int stage2, const AttnArgs &a, hipStream_t s) {
-  dim3 gd(a.n_qblocks * a.n_seq_grp * a.n_heads), bd(256);
+  dim3 gd(a.n_qblocks * a.n_seq_grp * a.n_heads), bd(ATTN_WAVES * 64);
   if (stage2)
     hipLaunchKernelGGL((attn_kernel<T, DH, true>), gd, bd, 0, s, a);
   else

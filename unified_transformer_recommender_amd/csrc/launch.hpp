@@ -17,7 +17,8 @@ hipError_t launch_attn(int dtype, int d_head, int stage2, const AttnArgs &a, hip
 hipError_t launch_post(int dtype, int resid_f32, const PostArgs &a, int grid, hipStream_t s);
 int post_tokens_per_tile(int dtype, int d_model);
 
-constexpr int ATTN_QBLOCK = 128;   // forward-mode queries per attention workgroup
+constexpr int ATTN_WAVES = 8;                    // waves per attention workgroup
+constexpr int ATTN_QBLOCK = 32 * ATTN_WAVES;     // forward-mode queries per attention workgroup
 constexpr int POST_MAX_DFF = 2048; // widest FFN the fused post-attention kernel stages
 
 }  // namespace ot

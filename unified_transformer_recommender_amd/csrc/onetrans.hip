@@ -273,7 +273,7 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
       a.own_sb = st.own_sb;
       a.own_sh = st.own_sh;
       const int cpw = 32 / st.ns;
-      a.n_qblocks = (st.n_cand + 4 * cpw - 1) / (4 * cpw);
+      a.n_qblocks = (st.n_cand + ATTN_WAVES * cpw - 1) / (ATTN_WAVES * cpw);
     } else {
       a.n_seq_grp = st.n_seq;
       a.n_qblocks = (R + ATTN_QBLOCK - 1) / ATTN_QBLOCK;
