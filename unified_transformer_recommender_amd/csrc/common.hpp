@@ -203,6 +203,7 @@ struct QkvArgs {
   RowView x;               // block input rows (storage dtype in block 0, else fp32)
   const void *wq, *wk, *wv;   // [G][d][d] storage dtype
   const void *gamma, *beta;   // norm1 [d]
+  RowView stats;           // per-row (mean, rstd) of x from the previous block's tail, fp32; base null if absent
   int layer;
   float eps;
 };
@@ -226,6 +227,7 @@ struct PostArgs {
   RowView out;             // X' rows (fp32)
   const void *wo, *w1, *b1, *w2, *b2;   // [G][..] storage dtype
   const void *gamma, *beta;             // norm2 [d]
+  RowView stats;           // where to write per-row (mean, rstd) of X' for the next block's norm 1; base null: none
   int layer;
   float eps;
 };

@@ -125,7 +125,7 @@ int check_weights(const onetrans_block_weights *blk, const Dims &D) {
 
 // ---- workspace -------------------------------------------------------------------------------
 struct Ws {
-  size_t x[2], q, k, v, o, total;
+  size_t x[2], st[2], q, k, v, o, total;
 };
 
 inline size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -144,6 +144,10 @@ Ws ws_layout(const Dims &D, size_t n, size_t tin, size_t rq, bool kv) {
   // residual while writing the block output, so the two must not alias
   w.x[0] = take(n * rq * d * 4);
   w.x[1] = take(n * rq * d * 4);
+  // per-row (mean, rstd) of the block output in x[i], written by the post-attention kernel for the
+  // next block's norm 1
+  w.st[0] = take(n * rq * 8);
+  w.st[1] = take(n * rq * 8);
   w.q = take(n * rq * d * es);
   w.k = kv ? take(n * tin * d * es) : 0;
   w.v = kv ? take(n * tin * d * es) : 0;
@@ -193,6 +197,8 @@ struct Step {
   long long own_sb, own_sh;
   RowView out;         // X' (fp32), t_off = first query position
   bool need_out;
+  void *stats_in;      // (mean, rstd) per row of x, laid out like x; null: norm 1 computes them
+  void *stats_out;     // where the post kernel writes (mean, rstd) per row of out; null: none
 };
 
 int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, char *ws, const Ws &L,
@@ -238,6 +244,10 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
     qa.wv = w.wv;
     qa.gamma = w.norm1_g;
     qa.beta = w.norm1_b;
+    // only the bf16 norm at d >= 256 consumes row statistics (the other shapes keep the whole row
+    // in registers and take them in the kernel)
+    const bool row_stats = D.dt == ONETRANS_BF16 && d >= 256;
+    if (row_stats && st.stats_in) qa.stats = RowView{st.stats_in, st.x.sb / d * 2, st.x.t_off, 2};
     qa.layer = D.layer;
     qa.eps = D.eps;
     if (tiles > 0x7fffffffLL) return ONETRANS_ERR_UNSUPPORTED;
@@ -314,6 +324,7 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
     pa.b2 = w.b2;
     pa.gamma = w.norm2_g;
     pa.beta = w.norm2_b;
+    if (D.dt == ONETRANS_BF16 && d >= 256 && st.stats_out) pa.stats = RowView{st.stats_out, st.out.sb / d * 2, st.out.t_off, 2};
     pa.layer = D.layer;
     pa.eps = D.eps;
     if (tiles > 0x7fffffffLL) return ONETRANS_ERR_UNSUPPORTED;
@@ -385,6 +396,7 @@ int onetrans_forward(const onetrans_config *cfg, const onetrans_block_weights *b
   int s = l_s;
   RowView x{const_cast<void *>(x0), (long long)(l_s + D.lns) * d, 0, d};
   int x_f32 = D.dt == ONETRANS_F32;
+  void *stats = nullptr;   // (mean, rstd) rows of x when the previous block wrote them
   for (int n = 0; n < D.N; ++n) {
     const int q = cfg->s_queries[n];
     const int T = s + D.lns, R = q + D.lns, p0 = s - q;
@@ -411,8 +423,11 @@ int onetrans_forward(const onetrans_config *cfg, const onetrans_block_weights *b
     st.pre_sh = (long long)T * dh;
     st.out = RowView{n + 1 == D.N ? out : (void *)(w + L.x[n & 1]), (long long)R * d, p0, d};
     st.need_out = true;
+    st.stats_in = stats;
+    st.stats_out = n + 1 == D.N ? nullptr : (void *)(w + L.st[n & 1]);
     if ((rc = run_step(D, blk[n], st, w, L, stream))) return rc;
     x = RowView{w + L.x[n & 1], (long long)R * d, 0, d};
+    stats = st.stats_out;
     x_f32 = 1;
     s = q;
   }
@@ -443,6 +458,7 @@ int onetrans_prefill_user(const onetrans_config *cfg, const onetrans_block_weigh
   int s = l_s;
   RowView x{const_cast<void *>(x_s), (long long)l_s * d, 0, d};
   int x_f32 = D.dt == ONETRANS_F32;
+  void *stats = nullptr;   // (mean, rstd) rows of x when the previous block wrote them
   for (int n = 0; n < D.N; ++n) {
     const int q = cfg->s_queries[n];
     const int p0 = s - q;
@@ -470,8 +486,11 @@ int onetrans_prefill_user(const onetrans_config *cfg, const onetrans_block_weigh
     st.pre_sh = st.kS.sh;
     st.out = RowView{last ? out_s : (void *)(w + L.x[n & 1]), (long long)q * d, p0, d};
     st.need_out = !last || out_s != nullptr;
+    st.stats_in = stats;
+    st.stats_out = last ? nullptr : (void *)(w + L.st[n & 1]);
     if ((rc = run_step(D, blk[n], st, w, L, stream))) return rc;
     x = RowView{w + L.x[n & 1], (long long)q * d, 0, d};
+    stats = st.stats_out;
     x_f32 = 1;
     s = q;
   }
@@ -509,6 +528,7 @@ int onetrans_score_candidates(const onetrans_config *cfg, const onetrans_block_w
   const int nseq = n_users * n_cand;
   RowView x{const_cast<void *>(x_ns), (long long)ns * d, cache->layer_len[0], d};
   int x_f32 = D.dt == ONETRANS_F32;
+  void *stats = nullptr;   // (mean, rstd) rows of x when the previous block wrote them
   for (int n = 0; n < D.N; ++n) {
     const int s = cache->layer_len[n];
     Step st{};
@@ -540,8 +560,11 @@ int onetrans_score_candidates(const onetrans_config *cfg, const onetrans_block_w
     st.own_sh = st.kN.sh;
     st.out = RowView{n + 1 == D.N ? out_ns : (void *)(w + L.x[n & 1]), (long long)ns * d, s, d};
     st.need_out = true;
+    st.stats_in = stats;
+    st.stats_out = n + 1 == D.N ? nullptr : (void *)(w + L.st[n & 1]);
     if ((rc = run_step(D, blk[n], st, w, L, stream))) return rc;
     x = RowView{w + L.x[n & 1], (long long)ns * d, 0, d};
+    stats = st.stats_out;
     x_f32 = 1;
   }
   return ONETRANS_OK;
@@ -575,6 +598,7 @@ int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weig
   const int d = D.d;
   RowView x{const_cast<void *>(x_new), (long long)d_l * d, l_old, d};
   int x_f32 = D.dt == ONETRANS_F32;
+  void *stats = nullptr;   // (mean, rstd) rows of x when the previous block wrote them
   for (int n = 0; n < D.N; ++n) {
     const bool last = n + 1 == D.N;
     Step st{};
@@ -599,9 +623,12 @@ int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weig
     st.pre_sb = st.kS.sb;
     st.pre_sh = st.kS.sh;
     st.out = RowView{last && out_new ? out_new : (void *)(w + L.x[n & 1]), (long long)d_l * d, l_old, d};
+    st.stats_in = stats;
+    st.stats_out = last ? nullptr : (void *)(w + L.st[n & 1]);
     st.need_out = !last || out_new != nullptr;
     if ((rc = run_step(D, blk[n], st, w, L, stream))) return rc;
     x = RowView{w + L.x[n & 1], (long long)d_l * d, l_old, d};
+    stats = st.stats_out;
     x_f32 = 1;
   }
   for (int n = 0; n < D.N; ++n) cache->layer_len[n] = l_old + d_l;

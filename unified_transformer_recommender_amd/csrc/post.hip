@@ -380,6 +380,34 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64)) void post_kernel(const Post
     ffn_step(c + 1, std::integral_constant<int, (DT + 3) % NB>{}, std::integral_constant<int, (DT + 4) % NB>{});
   }
 
+  // ---- statistics of X' for the next block's norm 1 (exact two-pass over the registers) --------
+  if (a.stats.base != nullptr) {
+    float mean = 0.0f;
+    if constexpr (LAYER) {
+      float s = 0.0f;
+#pragma unroll
+      for (int ti = 0; ti < DT; ++ti)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s += acc[ti][v];
+      s += __shfl_xor(s, 32, 64);
+      mean = s * (1.0f / D);
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int ti = 0; ti < DT; ++ti)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float c = acc[ti][v] - mean;
+        ss += c * c;
+      }
+    ss += __shfl_xor(ss, 32, 64);
+    if (g == 0 && valid) {
+      float *sp = (float *)a.stats.base + b * a.stats.sb + (long long)(t - a.stats.t_off) * a.stats.rs;
+      sp[0] = mean;
+      sp[1] = 1.0f / sqrtf(ss * (1.0f / D) + a.eps);
+    }
+  }
+
   // ---- store X' (fp32) tile by tile through the wave's LDS staging area ------------------------
   {
     float *stg = stage[wave];

@@ -113,14 +113,34 @@ __global__ __launch_bounds__((QKV_NW + 1) * 64, 2) void qkv_kernel(const QkvArgs
 
   // ---- norm1 of this lane's token -> bf16 B fragments (k = 16 kc + 8 g + e) ------------------
   // A lane holds half of its token's row (the other half sits in lane +- 32). For bf16 storage at
-  // d >= 256 the row is read twice: once for the statistics, in two halves, and once more (from
-  // cache) to normalise. That keeps at most a quarter row live in registers, so two workgroups fit
+  // d >= 256 the row's statistics come from the previous block's post-attention kernel when it
+  // wrote them (one read of the row); otherwise the row is read twice: once for the statistics, in
+  // two halves, and once more (from cache) to normalise. That keeps at most a quarter row live in registers, so two workgroups fit
   // on a CU and one's row loads overlap the other's chunk loop. LayerNorm statistics are taken
   // about the row's first element, which keeps the one-pass variance free of cancellation.
   frag xfr[KC];
   {
     const TI *xr = (const TI *)a.x.base + b * a.x.sb + (long long)(t - a.x.t_off) * a.x.rs;
-    if constexpr (BF && D >= 256) {
+    if (BF && D >= 256 && a.stats.base != nullptr) {
+      // statistics of this row were written by the previous block's post-attention kernel:
+      // one read of the row, normalised on the fly
+      const float *sp = (const float *)a.stats.base + b * a.stats.sb + (long long)(t - a.stats.t_off) * a.stats.rs;
+      const float mean = LAYER ? sp[0] : 0.0f, rstd = sp[1];
+      __syncthreads();                           // gamma / beta staged
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        if constexpr (BF) {
+          const TI *p = xr + 16 * kc + 8 * g;
+          frag fr;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int f = 16 * kc + 8 * g + e;
+            fr[e] = (bf16)((to_f32(p[e]) - mean) * rstd * s_gm[f] + s_bt[f]);
+          }
+          xfr[kc] = fr;
+        }
+      }
+    } else if constexpr (BF && D >= 256) {
       constexpr int HALF = KC / 2;
       const float shift = LAYER ? to_f32(xr[0]) : 0.0f;
       float s1 = 0.0f, s2 = 0.0f;
