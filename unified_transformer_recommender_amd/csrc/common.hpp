@@ -83,6 +83,12 @@ __device__ __forceinline__ void dma16(const void *src, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                :: "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(src) : "memory", "m0");
 }
+// The same with a wave-uniform base address in SGPRs and a 32-bit per-lane byte offset (the
+// load's scalar-base form): no per-lane 64-bit address arithmetic per load.
+__device__ __forceinline__ void dma16s(const void *sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds_base), "v"(voff), "s"(sbase) : "memory", "m0");
+}
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(size_t)(const __attribute__((address_space(3))) void *)p;
 }

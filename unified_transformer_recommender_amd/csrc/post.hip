@@ -22,9 +22,11 @@
 // distinct bank groups. The FFN is software-pipelined: while the up-projection of hidden chunk
 // c+1 runs on the matrix cores, the VALU evaluates GELU of chunk c.
 //
-// GELU is the exact erf form 0.5 x (1 + erf(x / sqrt 2)); erf is evaluated with Abramowitz &
+// GELU is the erf form 0.5 x (1 + erf(x / sqrt 2)). The fp32 path evaluates erf with Abramowitz &
 // Stegun 7.1.26 (|error| <= 1.5e-7): with z = |x|/sqrt2, t = 1/(1 + p z),
 //   GELU(x) = max(x, 0) - |x| * 0.5 t (a1 + t(a2 + t(a3 + t(a4 + t a5)))) * exp(-x^2 / 2).
+// The bf16 path, which rounds the activations to bf16 right after, uses a fitted sigmoid form with
+// half the instructions (gelu_fit below, |error| <= 7.9e-5).
 
 #include <type_traits>
 
@@ -46,6 +48,22 @@ __device__ __forceinline__ float gelu_as(float x) {
   const float q = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, a5, a4), a3), a2), a1);
   const float e = __builtin_amdgcn_exp2f(x * x * neg_half_log2e);
   return fmaf(-ax * q, e, fmaxf(x, 0.0f));
+}
+
+// GELU for the bf16 path, whose hidden activations are rounded to bf16 (relative step 2^-8)
+// before the down-projection: x sigma(z) with z = x (A1 + x^2 (A3 + A5 x^2)), the coefficients a
+// minimax fit to the erf form on [-12, 12] (max |error| 7.9e-5). z uses x clamped to [-10, 10]:
+// beyond, sigma(z) is 1 or 0 to fp32 precision (z(10) > 35), and the clamp keeps the quintic's
+// turn past |x| = 11.7 out of reach. sigma(z) = 1 / (1 + 2^(-z log2 e)).
+constexpr float GELU_FIT_A1 = 1.5965385145315985f;
+constexpr float GELU_FIT_A3 = 0.07282272755159432f;
+constexpr float GELU_FIT_A5 = -0.0005347158153885608f;
+__device__ __forceinline__ float gelu_fit(float x) {
+  constexpr float L = -1.4426950408889634f;   // -log2(e)
+  const float xc = __builtin_amdgcn_fmed3f(x, -10.0f, 10.0f);
+  const float x2 = xc * xc;
+  const float z = xc * fmaf(x2, fmaf(x2, GELU_FIT_A5 * L, GELU_FIT_A3 * L), GELU_FIT_A1 * L);
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z));
 }
 
 // Waves per workgroup (every chunk is split into whole 1 KB wave loads).
@@ -122,6 +140,18 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64)) void post_kernel(const Post
   const T *b2 = (const T *)a.b2 + (size_t)wg * D;
 
   // ---- weight chunk stream --------------------------------------------------------------------
+  // Byte offsets of this lane's 16-byte pieces within a row chunk (W^O, W1: 32 rows of d) and a
+  // column chunk (W2: d rows of 32 hidden units); piece j of the wave lands at LDS piece
+  // (j * NW + wave) * 64 + lane of the chunk buffer.
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t off_r[LPW], off_c[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int P = (j * NW + wave) * 64 + lane;
+    const int rr = P / RPA, qr = P % RPA, rc = P / RPB, qc = P % RPB;
+    off_r[j] = (uint32_t)((rr * D + (qr ^ chunk_swz<RPA, RPA * 16>(rr)) * EPC) * (int)sizeof(T));
+    off_c[j] = (uint32_t)((rc * DFF + (qc ^ chunk_swz<RPB, RPB * 16>(rc)) * EPC) * (int)sizeof(T));
+  }
   // chunk i: i < DT            -> W^O rows 32i..32i+31
   //          i == DT           -> W1 rows 0..31 (hidden chunk 0)
   //          i == DT + 1 + 2c  -> W1 rows of hidden chunk (c + 1) mod NC   (up-projection one ahead)
@@ -143,21 +173,10 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64)) void post_kernel(const Post
         cols = true;
       }
     }
-    T *dst = lds[i % NB];
+    const uint32_t dst = lds_addr(lds[i % NB]);
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-      const int blk = j * NW + wave;
-      const int P = blk * 64 + lane;
-      const T *src;
-      if (!cols) {
-        const int row = P / RPA, q = P % RPA;
-        src = base + row * D + (q ^ chunk_swz<RPA, RPA * 16>(row)) * EPC;
-      } else {
-        const int row = P / RPB, q = P % RPB;
-        src = base + (size_t)row * DFF + (q ^ chunk_swz<RPB, RPB * 16>(row)) * EPC;
-      }
-      dma16(src, lds_addr(dst + blk * 64 * EPC));
-    }
+    for (int j = 0; j < LPW; ++j)
+      dma16s(base, cols ? off_c[j] : off_r[j], dst + (uint32_t)((j * NW + wave_s) * 64 * 16));
   };
   // Make chunk i visible: this wave's loads of chunk i are done (loads of later chunks may still
   // be in flight) and its LDS accesses so far have completed (so the buffer of chunk i - 1 may be
@@ -320,9 +339,20 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64)) void post_kernel(const Post
     sched_lds_mfma<KC, KC, PD>();
     hacc += odd;
   }
+  auto gelu = [](float x) -> float {
+    if constexpr (BF) return gelu_fit(x);
+    else return gelu_as(x);
+  };
+  // GELU of a hidden chunk is split over two stages so that both carry VALU work beside their
+  // MFMAs: values 0..7 of the chunk's 16 per lane during the previous chunk's down-projection,
+  // values 8..15 during the next chunk's up-projection.
+  float hv[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) hv[i] = gelu(hacc[i] + s_b1[acc_row(i, g)]);
 
-  // ---- FFN: stage A (W1 chunk c+1): up(c+1) interleaved with GELU(c); stage B (W2 chunk c): down(c)
-  constexpr int NI = KC > 16 ? KC : 16;
+  // ---- FFN: stage A (W1 chunk c+1): up(c+1) + second half of GELU(c); stage B (W2 chunk c):
+  // down(c) + first half of GELU(c+1)
+  constexpr int NI = KC > 8 ? KC : 8;
   // One hidden chunk c: stage A consumes ring slot SA (W1 chunk c + 1), stage B slot SB (W2 chunk
   // c). The slots are compile-time constants (the loop below handles two chunks per iteration,
   // NC is even), so every LDS operand address is a fixed per-lane offset.
@@ -333,7 +363,6 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64)) void post_kernel(const Post
     arrive(ia);
     if (ia + NB - 1 < NCH) issue(ia + NB - 1);
     f32x16 hn = f32x16{}, hn_odd = f32x16{};
-    float hv[16];
     {
       const T *base = lds[SA];
 #pragma unroll
@@ -343,7 +372,7 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64)) void post_kernel(const Post
           if (i & 1) hn_odd = M::mma(afrag_rows(base, lc, i, true), yfr[i], hn_odd);
           else hn = M::mma(afrag_rows(base, lc, i, true), yfr[i], hn);
         }
-        if (i < 16) hv[i] = gelu_as(hacc[i] + s_b1[32 * c + acc_row(i, g)]);
+        if (i < 8) hv[8 + i] = gelu(hacc[8 + i] + s_b1[32 * c + acc_row(8 + i, g)]);
       }
       sched_lds_mfma<KC, KC, PD>();
     }
@@ -366,11 +395,18 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64)) void post_kernel(const Post
     if (ia + NB < NCH) issue(ia + NB);
     {
       const T *base = lds[SB];
+      const int cn = c + 1 < NC ? c + 1 : 0;   // after the last chunk: discarded look-ahead
 #pragma unroll
       for (int kc = 0; kc < HKC; ++kc)
 #pragma unroll
-        for (int ti = 0; ti < DT; ++ti) acc[ti] = M::mma(afrag_cols(base, 32 * ti + lc, kc), hfr[kc], acc[ti]);
+        for (int ti = 0; ti < DT; ++ti) {
+          acc[ti] = M::mma(afrag_cols(base, 32 * ti + lc, kc), hfr[kc], acc[ti]);
+          const int i = kc * DT + ti;
+          if (i < 8) hv[i] = gelu(hn[i] + s_b1[32 * cn + acc_row(i, g)]);
+        }
       sched_lds_mfma<DT * HKC, DT * HKC, PD>();
+#pragma unroll
+      for (int i = DT * HKC; i < 8; ++i) hv[i] = gelu(hn[i] + s_b1[32 * cn + acc_row(i, g)]);
     }
     hacc = hn;
   };
