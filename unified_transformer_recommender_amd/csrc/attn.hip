@@ -15,9 +15,13 @@
 // O^T += V^T P^T: the k index of that product is a permutation of the 32 keys, and the V^T
 // operand is read with the same permutation from an LDS copy of V stored transposed
 // ([d_head][key]). K/V tiles of 16 * ATTN_WAVES keys are staged in LDS once per workgroup and
-// shared by all its waves. Online softmax in base 2 with the 1/sqrt(dh) scale folded into one FMA
-// per score; fully masked tiles are skipped per wave; the accumulator is rescaled only when a
-// tile raises the running maximum by more than a fixed headroom.
+// shared by all its waves.
+//
+// Online softmax in base 2: queries arrive multiplied by log2(e)/sqrt(dh), so a probability is
+// exp2 of the score minus the running maximum. For bf16 the row sums are packed bf16 dot products
+// of the probabilities as rounded for the P.V product (two per instruction). Fully masked tiles
+// are skipped per wave; the accumulator is rescaled only when a tile raises the running maximum
+// by more than a fixed headroom.
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -64,37 +68,65 @@ __device__ __forceinline__ float other_half(float x) {
 // sum, taken against the same maximum, gives the same softmax.
 constexpr float RESCALE_HEADROOM = 8.0f;
 
-// One 32-key tile: fold masked scores s (already -inf where invisible) into the running state.
+// Running softmax state of the lane's query: maximum m (base-2 units), output accumulator o, and
+// this lane's partial row sum (its 16 of every 32 keys; the other half sits in lane +- 32).
+struct SoftmaxState {
+  float m, lsum;
+  f32x16 o;
+};
+
+// Scores of one 32-key tile against the lane's query: K rows from LDS (krow = this lane's key row
+// at its k offset), Q fragments in registers.
 template <typename T, int DH>
-__device__ __forceinline__ void softmax_pv(const f32x16 &s, float scale, float &m, float &lsum, f32x16 &o,
+__device__ __forceinline__ f32x16 score_tile(const T *krow, const typename Mma<T>::frag *qf) {
+  using M = Mma<T>;
+  f32x16 s = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < DH / M::KSTEP; ++kk) s = M::mma(*(const typename M::frag *)(krow + kk * M::KSTEP), qf[kk], s);
+  return s;
+}
+
+// One 32-key tile: fold the scores s (base-2 units, -inf where invisible) into the running state.
+template <typename T, int DH>
+__device__ __forceinline__ void softmax_pv(const f32x16 &s, SoftmaxState &st,
                                            const T *vt_row /* this lane's V^T row, or null if lc >= DH */,
                                            int g) {
   using M = Mma<T>;
   float mt = s[0];
 #pragma unroll
-  for (int v = 1; v < 16; ++v) mt = fmaxf(mt, s[v]);
+  for (int v = 1; v < 15; v += 2) mt = fmaxf(fmaxf(mt, s[v]), s[v + 1]);   // three-operand max
+  mt = fmaxf(mt, s[15]);
   mt = fmaxf(mt, other_half(mt));
-  if (__any((mt - m) * scale > RESCALE_HEADROOM)) {   // wave-uniform: raise the maximum and rescale
-    const float mn = fmaxf(m, mt);
-    const float alpha = __builtin_amdgcn_exp2f((m - mn) * scale);
-    m = mn;
-    lsum *= alpha;
+  if (__any(mt > st.m + RESCALE_HEADROOM)) {   // wave-uniform: raise the maximum and rescale
+    const float mn = fmaxf(st.m, mt);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - mn);
+    st.m = mn;
+    st.lsum *= alpha;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) o[v] *= alpha;
+    for (int v = 0; v < 16; ++v) st.o[v] *= alpha;
   }
-  const float nb = -m * scale;
   float p[16];
-  float ps = 0.0f;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    p[v] = __builtin_amdgcn_exp2f(fmaf(s[v], scale, nb));
-    ps += p[v];
+  for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(s[v] - st.m);
+  if constexpr (sizeof(T) == 4) {
+    float ps = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) ps += p[v];
+    st.lsum += ps;
   }
-  lsum += ps;
 #pragma unroll
   for (int mc = 0; mc < 32 / M::KSTEP; ++mc) {
-    typename M::frag vf = vt_row ? VtFrag<T>::load(vt_row, mc, g) : M::zero();
-    o = M::mma(vf, VtFrag<T>::pfrag(p, mc), o);
+    typename M::frag vf = (DH == 32 || vt_row) ? VtFrag<T>::load(vt_row, mc, g) : M::zero();
+    const typename M::frag pf = VtFrag<T>::pfrag(p, mc);
+    st.o = M::mma(vf, pf, st.o);
+    if constexpr (sizeof(T) == 2) {
+      // row sum of the probabilities as rounded for the product: packed bf16 dot products
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      const bf16x2_t one2 = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+      for (int e = 0; e < 8; e += 2)
+        st.lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{pf[e], pf[e + 1]}, one2, st.lsum, false);
+    }
   }
 }
 
@@ -176,9 +208,10 @@ __global__ __launch_bounds__(ATTN_WAVES * 64) void attn_kernel(const AttnArgs a)
   const T *kp = (const T *)a.k_pre + grp * a.pre_sb + h * a.pre_sh;
   const T *vp = (const T *)a.v_pre + grp * a.pre_sb + h * a.pre_sh;
 
-  f32x16 o = f32x16{};
-  float m = -1e30f, lsum = 0.0f;
-  const float scale = a.scale_log2;
+  SoftmaxState st;
+  st.m = -1e30f;
+  st.lsum = 0.0f;
+  st.o = f32x16{};
 
   for (int k0 = 0; k0 < n_keys; k0 += KT) {
     __syncthreads();
@@ -201,19 +234,18 @@ __global__ __launch_bounds__(ATTN_WAVES * 64) void attn_kernel(const AttnArgs a)
       const int kb = k0 + sub * 32;
       if (kb >= n_keys) break;
       if (!STAGE2 && kb > wave_max) break;
-      f32x16 s = f32x16{};
-      const T *krow = &sK[(sub * 32 + lc) * LDK + g * M::KPL];
-#pragma unroll
-      for (int kk = 0; kk < DH / M::KSTEP; ++kk) s = M::mma(*(const frag *)(krow + kk * M::KSTEP), qf[kk], s);
+      f32x16 s = score_tile<T, DH>(&sK[(sub * 32 + lc) * LDK + g * M::KPL], qf);
       const bool need_mask = STAGE2 ? (kb + 32 > n_keys) : (kb + 31 > wave_min || kb + 32 > n_keys);
       if (need_mask) {
+        // key kb + acc_row(v, g) is visible iff it is at most min(qpos, n_keys - 1) (Stage II: no
+        // causal limit within the prefix); compare element v's constant row offset with one
+        // per-lane bound
+        const int lim = (STAGE2 ? n_keys - 1 : min(qpos, n_keys - 1)) - kb - 4 * g;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = kb + acc_row(v, g);
-          if (key >= n_keys || (!STAGE2 && key > qpos)) s[v] = NEG_INF;
-        }
+        for (int v = 0; v < 16; ++v)
+          if (acc_row(v, 0) > lim) s[v] = NEG_INF;
       }
-      softmax_pv<T, DH>(s, scale, m, lsum, o, lc < DH ? &sVt[lc * LDV + sub * 32] : nullptr, g);
+      softmax_pv<T, DH>(s, st, lc < DH ? &sVt[lc * LDV + sub * 32] : nullptr, g);
     }
   }
 
@@ -238,10 +270,7 @@ __global__ __launch_bounds__(ATTN_WAVES * 64) void attn_kernel(const AttnArgs a)
       for (int e = 0; e < EPC; ++e) vw[(c0 + e) * LDW + ks] = ve[e];
     }
     __syncthreads();
-    f32x16 s = f32x16{};
-    const T *krow = &kw[lc * LDK + g * M::KPL];
-#pragma unroll
-    for (int kk = 0; kk < DH / M::KSTEP; ++kk) s = M::mma(*(const frag *)(krow + kk * M::KSTEP), qf[kk], s);
+    f32x16 s = score_tile<T, DH>(&kw[lc * LDK + g * M::KPL], qf);
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int ks = acc_row(v, g);
@@ -249,12 +278,13 @@ __global__ __launch_bounds__(ATTN_WAVES * 64) void attn_kernel(const AttnArgs a)
       const bool vis = ks < n_own && kc == cslot && j2 <= qi && c_first + kc < a.n_cand;
       if (!vis) s[v] = NEG_INF;
     }
-    softmax_pv<T, DH>(s, scale, m, lsum, o, lc < DH ? &vw[lc * LDW] : nullptr, g);
+    softmax_pv<T, DH>(s, st, lc < DH ? &vw[lc * LDW] : nullptr, g);
   }
 
   // ---- normalise and store O[b][i][h*dh + c] through the wave's LDS staging tile ---------------
-  const float lt = lsum + other_half(lsum);
+  const float lt = st.lsum + other_half(st.lsum);
   const float inv = valid ? 1.0f / lt : 0.0f;
+  f32x16 o = st.o;
 #pragma unroll
   for (int v = 0; v < 16; ++v) o[v] *= inv;
   T *stg = stage[wave];

@@ -212,6 +212,7 @@ struct QkvArgs {
   RowView stats;           // per-row (mean, rstd) of x from the previous block's tail, fp32; base null if absent
   int layer;
   float eps;
+  float q_scale;           // queries are stored multiplied by this (log2(e) / sqrt(d_head))
 };
 
 // ---------------------------------------------------------------------------------------------
@@ -260,7 +261,6 @@ struct AttnArgs {
   const void *k_pre, *v_pre; long long pre_sb, pre_sh;
   const void *k_own, *v_own; long long own_sb, own_sh;
   void *o; long long o_sb;
-  float scale_log2;        // log2(e) / sqrt(d_head)
 };
 
 }  // namespace ot

@@ -250,6 +250,7 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
     if (row_stats && st.stats_in) qa.stats = RowView{st.stats_in, st.x.sb / d * 2, st.x.t_off, 2};
     qa.layer = D.layer;
     qa.eps = D.eps;
+    qa.q_scale = 1.4426950408889634f / sqrtf((float)dh);
     if (tiles > 0x7fffffffLL) return ONETRANS_ERR_UNSUPPORTED;
     const hipError_t e = timed(ONETRANS_K_QKV, stream, [&] { return launch_qkv(D.dt, st.x_f32, qa, (int)tiles, stream); });
     if (e != hipSuccess) return ONETRANS_ERR_HIP;
@@ -274,7 +275,6 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
     a.pre_sh = st.pre_sh;
     a.o = ob;
     a.o_sb = (long long)R * d;
-    a.scale_log2 = 1.4426950408889634f / sqrtf((float)dh);
     if (st.stage2) {
       a.n_seq_grp = st.n_grp;
       a.n_cand = st.n_cand;

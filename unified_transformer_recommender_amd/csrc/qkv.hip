@@ -271,6 +271,10 @@ __global__ __launch_bounds__((QKV_NW + 1) * 64, 2) void qkv_kernel(const QkvArgs
     // 32 output features 32 ci .. 32 ci + 31 of every token: stage through LDS, store whole runs
     const int seg = i / DT, ci = i - seg * DT;
     const HeadView &hv = seg == 0 ? jb.k : seg == 1 ? jb.v : jb.q;
+    if (seg == 2) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[v] *= a.q_scale;
+    }
     TS::put(stg, acc, lc, g);
 #pragma unroll
     for (int k = 0; k < TS::NI; ++k) {
