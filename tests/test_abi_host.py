@@ -56,7 +56,7 @@ def test_workspace_and_cache_sizes():
     got = lib.onetrans_workspace_bytes(ctypes.byref(c), L.OP_FORWARD, B, l_s, 0, 0)
     d, T, R = 256, 136, 116
     al = lambda n: (n + 255) // 256 * 256
-    expect = 2 * al(B * R * d * 4) + 2 * al(B * R * 8) + al(B * R * d * 2) + 2 * al(B * T * d * 2) + al(B * R * d * 2)
+    expect = 2 * al(B * R * d * 4) + 2 * al(B * R * 8) + al(B * R * d * 2) + 2 * al(B * T * d * 2) + al(B * R * d * 2) + al(16)
     assert got == expect
     assert lib.onetrans_kv_cache_bytes(ctypes.byref(c), 3, 200) == 3 * 2 * 8 * 200 * 32 * 2
     assert lib.onetrans_workspace_bytes(ctypes.byref(c), L.OP_SCORE, 2, 0, 5, 0) > 0

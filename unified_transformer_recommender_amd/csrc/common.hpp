@@ -213,6 +213,7 @@ struct QkvArgs {
   int layer;
   float eps;
   float q_scale;           // queries are stored multiplied by this (log2(e) / sqrt(d_head))
+  void *trash;             // 16 bytes that masked-off output pieces are written to
 };
 
 // ---------------------------------------------------------------------------------------------

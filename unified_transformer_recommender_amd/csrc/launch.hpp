@@ -9,7 +9,7 @@ namespace ot {
 
 // dtype: 0 = fp32 storage, 1 = bf16 storage. in_f32: block input rows are fp32 (1) or storage (0).
 hipError_t launch_qkv(int dtype, int in_f32, const QkvArgs &a, int grid, hipStream_t s);
-int qkv_tokens_per_tile();
+int qkv_tokens_per_tile(int dtype, int d_model);
 
 hipError_t launch_attn(int dtype, int d_head, int stage2, const AttnArgs &a, hipStream_t s);
 

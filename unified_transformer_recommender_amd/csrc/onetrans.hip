@@ -125,7 +125,7 @@ int check_weights(const onetrans_block_weights *blk, const Dims &D) {
 
 // ---- workspace -------------------------------------------------------------------------------
 struct Ws {
-  size_t x[2], st[2], q, k, v, o, total;
+  size_t x[2], st[2], q, k, v, o, trash, total;
 };
 
 inline size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -152,6 +152,8 @@ Ws ws_layout(const Dims &D, size_t n, size_t tin, size_t rq, bool kv) {
   w.k = kv ? take(n * tin * d * es) : 0;
   w.v = kv ? take(n * tin * d * es) : 0;
   w.o = take(n * rq * d * es);
+  // 16 bytes that the QKV kernel's masked-off lanes store to (its store count stays fixed)
+  w.trash = take(16);
   w.total = off;
   return w;
 }
@@ -216,7 +218,7 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
   {
     QkvArgs qa;
     memset(&qa, 0, sizeof(qa));
-    const int bm = qkv_tokens_per_tile();
+    const int bm = qkv_tokens_per_tile(D.dt, d);
     const int no_q = 0x7fffffff;
     int nj = 0;
     long long tiles = 0;
@@ -251,6 +253,7 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
     qa.layer = D.layer;
     qa.eps = D.eps;
     qa.q_scale = 1.4426950408889634f / sqrtf((float)dh);
+    qa.trash = ws + L.trash;
     if (tiles > 0x7fffffffLL) return ONETRANS_ERR_UNSUPPORTED;
     const hipError_t e = timed(ONETRANS_K_QKV, stream, [&] { return launch_qkv(D.dt, st.x_f32, qa, (int)tiles, stream); });
     if (e != hipSuccess) return ONETRANS_ERR_HIP;

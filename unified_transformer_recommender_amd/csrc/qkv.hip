@@ -31,23 +31,35 @@ __device__ __forceinline__ constexpr int chunk_swz(int r) {
   return (r / rpb) & (P - 1);
 }
 
-constexpr int QKV_NW = 4;                 // compute waves; one loader wave more per workgroup
-constexpr int QKV_NB = 2;                 // weight-chunk ring slots; the loader runs QKV_NB - 1 chunks ahead
+constexpr int QKV_NW = 4;                 // waves per workgroup
+constexpr int QKV_NB = 2;                 // weight-chunk ring slots; loads run QKV_NB - 1 chunks ahead
+
+// Token groups of 32 per wave: with two, every weight fragment read from LDS feeds two MFMAs
+// (half the LDS operand traffic and half the weight stream per token). The normalised rows of
+// both groups stay in registers, which bounds it to bf16 at d <= 256.
+template <typename T, int D>
+constexpr int qkv_tg() { return (sizeof(T) == 2 && D <= 256) ? 2 : 1; }
 
 template <typename T, typename TI, int D, bool LAYER>
-__global__ __launch_bounds__((QKV_NW + 1) * 64, 2) void qkv_kernel(const QkvArgs a) {
+__global__ __launch_bounds__(QKV_NW * 64, 2) void qkv_kernel(const QkvArgs a) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int NW = QKV_NW;
+  constexpr int TG = qkv_tg<T, D>();
   constexpr int EPC = 16 / (int)sizeof(T);
   constexpr int DT = D / 32;                    // 32-feature chunks per projection
   constexpr int KC = D / M::KSTEP;
   constexpr int RPA = D / EPC;                  // 16-byte pieces per weight row
   constexpr int CH = 32 * D;
-  constexpr int BLOCKS = CH / EPC / 64;         // 1 KB loads per chunk, all issued by the loader wave
+  constexpr int BLOCKS = CH / EPC / 64;         // 1 KB wave loads per chunk
+  constexpr int LPW = BLOCKS / NW;              // wave loads per chunk per wave
+  static_assert(BLOCKS % NW == 0 && LPW >= 1, "chunk must split into whole wave loads");
   constexpr bool BF = sizeof(T) == 2;
   using TS = TileStage<T>;
-  constexpr int NB = CH * (int)sizeof(T) <= 16384 ? QKV_NB : 2;   // 32 KB chunks: two slots
+  constexpr int NS = TS::NI * TG;               // output stores per chunk per wave
+  constexpr int NB = QKV_NB;
+  constexpr int PD = 4;                         // LDS operand reads in flight ahead of the MFMAs
+  static_assert(NB == 2, "the chunk waits below assume one chunk in flight");
   __shared__ __attribute__((aligned(16))) T lds[NB][CH];
   __shared__ __attribute__((aligned(16))) T stage[NW][TS::SIZE];
   __shared__ float s_gm[D], s_bt[D];
@@ -55,78 +67,93 @@ __global__ __launch_bounds__((QKV_NW + 1) * 64, 2) void qkv_kernel(const QkvArgs
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lc = lane & 31;
   const int dh = a.d_head;
-  const bool loader = wave == NW;
 
   // ---- job / group / token tile --------------------------------------------------------------
+  // The workgroup's tile is NW * TG * 32 rows of one parameter group; wave w holds token groups
+  // w * TG .. w * TG + TG - 1 of it, and the lane's token lc of each.
   const int bid = blockIdx.x;
   const QkvJob &jb = (a.n_jobs > 1 && bid >= a.job[1].tile_start) ? a.job[1] : a.job[0];
   const int local = bid - jb.tile_start;
   const int tm = local % jb.m_tiles, grp = local / jb.m_tiles;
   const int wg = jb.rs.wg0 + grp;
   const int M_rows = jb.rs.n_seq * jb.rs.rows;
-  const int r0 = tm * (NW * 32) + wave * 32 + lc;
-  const bool valid = !loader && r0 < M_rows;
-  const int r = valid ? r0 : 0;
-  const int b = r / jb.rs.rows;
-  const int t = jb.rs.t0 + grp * jb.rs.t_step + (r - b * jb.rs.rows);
-  const bool lane_q = valid && t >= jb.q_from;
-  const bool tile_q = __syncthreads_or(lane_q);   // does any token of this workgroup issue a query?
-  // tokens whose 16-byte output pieces this lane stores (one per store instruction)
-  int sb[TS::NI], stt[TS::NI];
-  bool sval[TS::NI], sq[TS::NI];
+  int b[TG], t[TG];
+  bool valid[TG], lane_q[TG];
+  bool any_q = false;
 #pragma unroll
-  for (int k = 0; k < TS::NI; ++k) {
-    const int tok = TS::token(k, lane);
-    sb[k] = __shfl(b, tok, 64);
-    stt[k] = __shfl(t, tok, 64);
-    sval[k] = __shfl((int)valid, tok, 64) != 0;
-    sq[k] = __shfl((int)lane_q, tok, 64) != 0;
+  for (int tg = 0; tg < TG; ++tg) {
+    const int r0 = (tm * NW + wave) * (TG * 32) + tg * 32 + lc;
+    valid[tg] = r0 < M_rows;
+    const int r = valid[tg] ? r0 : 0;
+    b[tg] = r / jb.rs.rows;
+    t[tg] = jb.rs.t0 + grp * jb.rs.t_step + (r - b[tg] * jb.rs.rows);
+    lane_q[tg] = valid[tg] && t[tg] >= jb.q_from;
+    any_q = any_q || lane_q[tg];
   }
-  T *stg = stage[loader ? 0 : wave];
+  const bool tile_q = __syncthreads_or(any_q);   // does any token of this workgroup issue a query?
+  // Output pieces this lane stores (one per store instruction): the piece's token within its
+  // group, and whether it is written at all. Every store instruction is issued; a lane with
+  // nothing to write sends its piece to a trash slot, so the number of outstanding vector-memory
+  // operations after each chunk is a constant the chunk waits rely on.
+  int sb[TG][TS::NI], stt[TG][TS::NI];
+  bool sval[TG][TS::NI], sq[TG][TS::NI];
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+    for (int k = 0; k < TS::NI; ++k) {
+      const int tok = TS::token(k, lane);
+      sb[tg][k] = __shfl(b[tg], tok, 64);
+      stt[tg][k] = __shfl(t[tg], tok, 64);
+      sval[tg][k] = __shfl((int)valid[tg], tok, 64) != 0;
+      sq[tg][k] = __shfl((int)lane_q[tg], tok, 64) != 0;
+    }
+  T *stg = stage[wave];
 
-  // chunk stream: K chunks 0..DT-1, V chunks, then (if any query row) Q chunks
+  // ---- weight chunk stream: K chunks 0..DT-1, V chunks, then (if any query row) Q chunks -------
   const int n_chunks = tile_q ? 3 * DT : 2 * DT;
   const T *wk = (const T *)a.wk + (size_t)wg * D * D;
   const T *wv = (const T *)a.wv + (size_t)wg * D * D;
   const T *wq = (const T *)a.wq + (size_t)wg * D * D;
-  auto issue = [&](int i) {   // loader wave only
+  // byte offset of this lane's 16-byte piece j within a chunk (32 rows of d, pieces XOR-swizzled);
+  // piece j of the wave lands at LDS piece (j * NW + wave) * 64 + lane of the chunk buffer
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t off[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int P = (j * NW + wave) * 64 + lane;
+    const int row = P / RPA, q = P % RPA;
+    off[j] = (uint32_t)((row * D + (q ^ chunk_swz<RPA, RPA * 16>(row)) * EPC) * (int)sizeof(T));
+  }
+  auto issue = [&](int i) {
     const int seg = i / DT, ci = i - seg * DT;
     const T *base = (seg == 0 ? wk : seg == 1 ? wv : wq) + (size_t)(32 * ci) * D;
-    T *dst = lds[i % NB];
+    const uint32_t dst = lds_addr(lds[i % NB]);
 #pragma unroll
-    for (int blk = 0; blk < BLOCKS; ++blk) {
-      const int P = blk * 64 + lane;
-      const int row = P / RPA, q = P % RPA;
-      __builtin_amdgcn_global_load_lds((const void *)(base + row * D + (q ^ chunk_swz<RPA, RPA * 16>(row)) * EPC),
-                                       (__attribute__((address_space(3))) void *)(dst + blk * 64 * EPC), 16, 0, 0);
-    }
+    for (int j = 0; j < LPW; ++j) dma16s(base, off[j], dst + (uint32_t)((j * NW + wave_s) * 64 * 16));
   };
-  if (loader) {
-#pragma unroll
-    for (int i = 0; i < NB - 1; ++i) issue(i);   // n_chunks >= 2 * (d / 32) >= NB - 1
-  }
+  issue(0);                                      // n_chunks >= 2 * DT >= 2
 
-  for (int i = tid; i < D; i += (NW + 1) * 64) {
+  for (int i = tid; i < D; i += NW * 64) {
     s_gm[i] = to_f32(((const T *)a.gamma)[i]);
     s_bt[i] = LAYER ? to_f32(((const T *)a.beta)[i]) : 0.0f;
   }
+  __syncthreads();                               // gamma / beta staged
 
-  // ---- norm1 of this lane's token -> bf16 B fragments (k = 16 kc + 8 g + e) ------------------
+  // ---- norm1 of this lane's tokens -> bf16 B fragments (k = 16 kc + 8 g + e) -----------------
   // A lane holds half of its token's row (the other half sits in lane +- 32). For bf16 storage at
   // d >= 256 the row's statistics come from the previous block's post-attention kernel when it
   // wrote them (one read of the row); otherwise the row is read twice: once for the statistics, in
-  // two halves, and once more (from cache) to normalise. That keeps at most a quarter row live in registers, so two workgroups fit
-  // on a CU and one's row loads overlap the other's chunk loop. LayerNorm statistics are taken
-  // about the row's first element, which keeps the one-pass variance free of cancellation.
-  frag xfr[KC];
-  {
-    const TI *xr = (const TI *)a.x.base + b * a.x.sb + (long long)(t - a.x.t_off) * a.x.rs;
+  // two halves, and once more (from cache) to normalise, which keeps at most a quarter row live in
+  // registers. LayerNorm statistics are taken about the row's first element, which keeps the
+  // one-pass variance free of cancellation. Token groups are normalised one after the other.
+  frag xfr[TG][KC];
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg) {
+    asm volatile("" ::: "memory");               // one group's row in flight at a time
+    const TI *xr = (const TI *)a.x.base + b[tg] * a.x.sb + (long long)(t[tg] - a.x.t_off) * a.x.rs;
     if (BF && D >= 256 && a.stats.base != nullptr) {
-      // statistics of this row were written by the previous block's post-attention kernel:
-      // one read of the row, normalised on the fly
-      const float *sp = (const float *)a.stats.base + b * a.stats.sb + (long long)(t - a.stats.t_off) * a.stats.rs;
+      const float *sp = (const float *)a.stats.base + b[tg] * a.stats.sb + (long long)(t[tg] - a.stats.t_off) * a.stats.rs;
       const float mean = LAYER ? sp[0] : 0.0f, rstd = sp[1];
-      __syncthreads();                           // gamma / beta staged
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
         if constexpr (BF) {
@@ -137,7 +164,7 @@ __global__ __launch_bounds__((QKV_NW + 1) * 64, 2) void qkv_kernel(const QkvArgs
             const int f = 16 * kc + 8 * g + e;
             fr[e] = (bf16)((to_f32(p[e]) - mean) * rstd * s_gm[f] + s_bt[f]);
           }
-          xfr[kc] = fr;
+          xfr[tg][kc] = fr;
         }
       }
     } else if constexpr (BF && D >= 256) {
@@ -166,7 +193,6 @@ __global__ __launch_bounds__((QKV_NW + 1) * 64, 2) void qkv_kernel(const QkvArgs
       const float mean = LAYER ? shift + m1 : 0.0f;
       const float var = LAYER ? fmaxf(s2 * (1.0f / D) - m1 * m1, 0.0f) : s2 * (1.0f / D);
       const float rstd = 1.0f / sqrtf(var + a.eps);
-      __syncthreads();                           // gamma / beta staged
       asm volatile("" ::: "memory");             // read the row again rather than keep it live
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
@@ -177,7 +203,7 @@ __global__ __launch_bounds__((QKV_NW + 1) * 64, 2) void qkv_kernel(const QkvArgs
           const int f = 16 * kc + 8 * g + e;
           fr[e] = (bf16)((to_f32(p[e]) - mean) * rstd * s_gm[f] + s_bt[f]);
         }
-        xfr[kc] = fr;
+        xfr[tg][kc] = fr;
       }
     } else {
       constexpr int PER = D / 2;                 // features held by this lane
@@ -208,7 +234,6 @@ __global__ __launch_bounds__((QKV_NW + 1) * 64, 2) void qkv_kernel(const QkvArgs
       }
       ss += __shfl_xor(ss, 32, 64);
       const float rstd = 1.0f / sqrtf(ss * (1.0f / D) + a.eps);
-      __syncthreads();                           // gamma / beta staged
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
         if constexpr (BF) {
@@ -218,44 +243,31 @@ __global__ __launch_bounds__((QKV_NW + 1) * 64, 2) void qkv_kernel(const QkvArgs
             const int f = 16 * kc + 8 * g + e;
             fr[e] = (bf16)((xv[8 * kc + e] - mean) * rstd * s_gm[f] + s_bt[f]);
           }
-          xfr[kc] = fr;
+          xfr[tg][kc] = fr;
         } else {
           const int f = 2 * kc + g;
-          xfr[kc] = (xv[kc] - mean) * rstd * s_gm[f] + s_bt[f];
+          xfr[tg][kc] = (xv[kc] - mean) * rstd * s_gm[f] + s_bt[f];
         }
       }
     }
   }
 
-  // ---- chunk loop: barrier B_i makes chunk i visible and frees the slot of chunk i - 1 ----------
-  // Loader: before B_i, chunk i has landed; after B_i every compute wave has finished reading
-  // chunk i - 1, so its slot takes chunk i + NB - 1. Loads complete in issue order, so waiting for
-  // "at most k * BLOCKS outstanding" leaves exactly the k most recently issued chunks in flight.
-  auto wait_chunk = [&](int later) {   // later = chunks issued after the awaited one
-    if constexpr (2 * BLOCKS < 64) {
-      if (later >= 2) wait_vm<2 * BLOCKS>();
-      else if (later == 1) wait_vm<BLOCKS>();
-      else wait_vm<0>();
-      return;
-    }
-    if (later >= 1) wait_vm<BLOCKS>();
-    else wait_vm<0>();
-  };
-  if (loader) {
-    static_assert(NB <= 4 && BLOCKS < 64 && (NB <= 2 || 2 * BLOCKS < 64), "wait counts cover at most two chunks in flight");
-    wait_chunk(min(NB - 2, n_chunks - 1));
-    bare_barrier();                  // B_0
-    for (int i = 0; i < n_chunks; ++i) {
-      if (i + NB - 1 < n_chunks) issue(i + NB - 1);
-      if (i + 1 < n_chunks) wait_chunk(min(NB - 2, n_chunks - 2 - i));
-      bare_barrier();                // B_{i+1}
-    }
-    return;
-  }
-  bare_barrier();                    // B_0
+  // ---- chunk loop ----------------------------------------------------------------------------
+  // Before the barrier of chunk i this wave waits for its own loads of chunk i: after those it
+  // has issued only the NS stores of chunk i - 1 (for chunk 0: nothing that is still in flight,
+  // the rows above were consumed), and operations complete in issue order. After the barrier
+  // every wave has also finished reading chunk i - 1, so its slot takes chunk i + 1.
+  T *trash = (T *)a.trash;
   for (int i = 0; i < n_chunks; ++i) {
+    if (i == 0) wait_vm<0>();
+    else wait_vm<NS>();
+    wait_lgkm0();
+    bare_barrier();
+    if (i + 1 < n_chunks) issue(i + 1);
     const T *base = lds[i % NB];
-    f32x16 acc = f32x16{};
+    f32x16 acc[TG];
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg) acc[tg] = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
       frag af;
@@ -266,37 +278,38 @@ __global__ __launch_bounds__((QKV_NW + 1) * 64, 2) void qkv_kernel(const QkvArgs
         const int k = 2 * kc + g;
         af = base[lc * D + ((k / EPC) ^ chunk_swz<RPA, RPA * 16>(lc)) * EPC + k % EPC];
       }
-      acc = M::mma(af, xfr[kc], acc);
+#pragma unroll
+      for (int tg = 0; tg < TG; ++tg) acc[tg] = M::mma(af, xfr[tg][kc], acc[tg]);
     }
+    if constexpr (BF) sched_lds_mfma<KC, KC * TG, PD>();
     // 32 output features 32 ci .. 32 ci + 31 of every token: stage through LDS, store whole runs
     const int seg = i / DT, ci = i - seg * DT;
     const HeadView &hv = seg == 0 ? jb.k : seg == 1 ? jb.v : jb.q;
-    if (seg == 2) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[v] *= a.q_scale;
-    }
-    TS::put(stg, acc, lc, g);
+    for (int tg = 0; tg < TG; ++tg) {
+      if (seg == 2) {
 #pragma unroll
-    for (int k = 0; k < TS::NI; ++k) {
-      const u32x4 piece = TS::get(stg, k, lane);
-      if (seg < 2 ? sval[k] : sq[k]) {
+        for (int v = 0; v < 16; ++v) acc[tg][v] *= a.q_scale;
+      }
+      TS::put(stg, acc[tg], lc, g);
+#pragma unroll
+      for (int k = 0; k < TS::NI; ++k) {
+        const u32x4 piece = TS::get(stg, k, lane);
         const int f = 32 * ci + TS::feature(lane);
         const int h = f / dh, c = f - h * dh;
-        st16((T *)hv.base + sb[k] * hv.sb + h * hv.sh + (long long)(stt[k] - hv.t_off) * dh + c, piece);
+        T *dst = (T *)hv.base + sb[tg][k] * hv.sb + h * hv.sh + (long long)(stt[tg][k] - hv.t_off) * dh + c;
+        st16((seg < 2 ? sval[tg][k] : sq[tg][k]) ? dst : trash, piece);
       }
     }
-    // this wave's LDS reads of chunk i are complete once their data fed the MFMAs above
-    wait_lgkm0();
-    bare_barrier();                  // B_{i+1}
   }
 }
 
 template <typename T, typename TI, int D>
 hipError_t launch_dl(const QkvArgs &a, int grid, hipStream_t s) {
   if (a.layer)
-    hipLaunchKernelGGL((qkv_kernel<T, TI, D, true>), dim3(grid), dim3((QKV_NW + 1) * 64), 0, s, a);
+    hipLaunchKernelGGL((qkv_kernel<T, TI, D, true>), dim3(grid), dim3(QKV_NW * 64), 0, s, a);
   else
-    hipLaunchKernelGGL((qkv_kernel<T, TI, D, false>), dim3(grid), dim3((QKV_NW + 1) * 64), 0, s, a);
+    hipLaunchKernelGGL((qkv_kernel<T, TI, D, false>), dim3(grid), dim3(QKV_NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -316,7 +329,10 @@ hipError_t launch_d(const QkvArgs &a, int grid, hipStream_t s) {
 
 }  // namespace
 
-int qkv_tokens_per_tile() { return QKV_NW * 32; }
+int qkv_tokens_per_tile(int dtype, int d_model) {
+  if (dtype == 1) return QKV_NW * 32 * (d_model <= 256 ? qkv_tg<bf16, 256>() : qkv_tg<bf16, 512>());
+  return QKV_NW * 32 * qkv_tg<float, 256>();
+}
 
 hipError_t launch_qkv(int dtype, int in_f32, const QkvArgs &a, int grid, hipStream_t s) {
   if (grid == 0) return hipSuccess;
