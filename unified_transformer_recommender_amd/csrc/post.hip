@@ -13,14 +13,16 @@
 // which accumulates straight into X'^T. An accumulator tile's lane holds the k-indices
 // {4g + r + 8j}; two cross-half lane swaps (v_permlane32_swap) turn it into a natural B fragment.
 //
-// Weight streaming: chunks flow through a ring of NB = 4 LDS buffers with direct global->LDS
-// loads (each wave instruction writes 64 x 16 bytes), issued three chunks ahead; a chunk is consumed
+// Weight streaming: chunks flow through a ring of NB = 2 LDS buffers with direct global->LDS
+// loads (each wave instruction writes 64 x 16 bytes), issued one chunk ahead; a chunk is consumed
 // after the issuing waves' own partial vmcnt wait and one fence-free workgroup barrier, so the
 // next chunk's loads stay in flight across it. Within a chunk, LDS operand reads are issued a
-// few MFMAs ahead of their use, and long dependent accumulation chains are split in two. Rows are stored unpadded
-// with their 16-byte pieces XOR-swizzled so that 16 lanes reading 16 consecutive rows touch 16
-// distinct bank groups. The FFN is software-pipelined: while the up-projection of hidden chunk
-// c+1 runs on the matrix cores, the VALU evaluates GELU of chunk c.
+// few MFMAs ahead of their use. Rows are stored unpadded with their 16-byte pieces XOR-swizzled so
+// that 16 lanes reading 16 consecutive rows touch 16 distinct bank groups.
+//
+// Occupancy: the kernel is held to 256 registers per lane so that two workgroups share a CU. Each
+// hidden chunk then runs plainly in order (up-projection, GELU, down-projection): the other
+// workgroup's MFMAs fill this one's VALU phases, waits and activation loads.
 //
 // GELU is the erf form 0.5 x (1 + erf(x / sqrt 2)). The fp32 path evaluates erf with Abramowitz &
 // Stegun 7.1.26 (|error| <= 1.5e-7): with z = |x|/sqrt2, t = 1/(1 + p z),
@@ -91,7 +93,7 @@ __device__ __forceinline__ bf16x8 natural_kfrag(bf16x8 f) {
 }
 
 template <typename T, typename TR, int D, bool LAYER>
-__global__ __launch_bounds__((post_nw<T, D>() * 64)) void post_kernel(const PostArgs a) {
+__global__ __launch_bounds__((post_nw<T, D>() * 64), 2) void post_kernel(const PostArgs a) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int NW = post_nw<T, D>();
@@ -118,7 +120,7 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64)) void post_kernel(const Post
   const int g = lane >> 5, lc = lane & 31;
   const int DFF = a.d_ff;
   const int NC = DFF / 32;                      // hidden chunks
-  const int NCH = DT + 1 + 2 * NC;              // chunks in the stream
+  const int NCH = DT + 2 * NC;                  // chunks in the stream
 
   // ---- job / group / token tile --------------------------------------------------------------
   const int bid = blockIdx.x;
@@ -153,21 +155,18 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64)) void post_kernel(const Post
     off_c[j] = (uint32_t)((rc * DFF + (qc ^ chunk_swz<RPB, RPB * 16>(rc)) * EPC) * (int)sizeof(T));
   }
   // chunk i: i < DT            -> W^O rows 32i..32i+31
-  //          i == DT           -> W1 rows 0..31 (hidden chunk 0)
-  //          i == DT + 1 + 2c  -> W1 rows of hidden chunk (c + 1) mod NC   (up-projection one ahead)
-  //          i == DT + 2 + 2c  -> W2 columns of hidden chunk c
+  //          i == DT + 2c      -> W1 rows of hidden chunk c
+  //          i == DT + 2c + 1  -> W2 columns of hidden chunk c
   // This lane's piece of wave load j sits at LDS piece P = (j * NW + wave) * 64 + lane.
   auto issue = [&](int i) {
     const T *base;
     bool cols = false;
     if (i < DT) {
       base = wo + (size_t)(32 * i) * D;
-    } else if (i == DT) {
-      base = w1;
     } else {
-      const int c = (i - DT - 1) >> 1;
-      if (((i - DT - 1) & 1) == 0) {
-        base = w1 + (size_t)(32 * ((c + 1) % NC)) * D;
+      const int c = (i - DT) >> 1;
+      if (((i - DT) & 1) == 0) {
+        base = w1 + (size_t)(32 * c) * D;
       } else {
         base = w2 + 32 * c;
         cols = true;
@@ -265,14 +264,9 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64)) void post_kernel(const Post
     arrive(ti);
     if (ti + NB - 1 < NCH) issue(ti + NB - 1);
     const T *base = lds[ti % NB];
-    f32x16 odd = f32x16{};
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      if (kc & 1) odd = M::mma(afrag_rows(base, lc, kc, false), ofr[kc], odd);
-      else acc[ti] = M::mma(afrag_rows(base, lc, kc, false), ofr[kc], acc[ti]);
-    }
+    for (int kc = 0; kc < KC; ++kc) acc[ti] = M::mma(afrag_rows(base, lc, kc, false), ofr[kc], acc[ti]);
     sched_lds_mfma<KC, KC, PD>();
-    acc[ti] += odd;
   }
 
   // ---- norm2, + b2 ----------------------------------------------------------------------------
@@ -324,96 +318,55 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64)) void post_kernel(const Post
     }
   }
 
-  // ---- FFN prologue: up-projection of hidden chunk 0 (chunk DT) --------------------------------
-  f32x16 hacc = f32x16{};
-  {
-    arrive(DT);
-    if (DT + NB - 1 < NCH) issue(DT + NB - 1);
-    const T *base = lds[DT % NB];
-    f32x16 odd = f32x16{};
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      if (kc & 1) odd = M::mma(afrag_rows(base, lc, kc, true), yfr[kc], odd);
-      else hacc = M::mma(afrag_rows(base, lc, kc, true), yfr[kc], hacc);
-    }
-    sched_lds_mfma<KC, KC, PD>();
-    hacc += odd;
-  }
-  auto gelu = [](float x) -> float {
-    if constexpr (BF) return gelu_fit(x);
-    else return gelu_as(x);
-  };
-  // GELU of a hidden chunk is split over two stages so that both carry VALU work beside their
-  // MFMAs: values 0..7 of the chunk's 16 per lane during the previous chunk's down-projection,
-  // values 8..15 during the next chunk's up-projection.
-  float hv[16];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) hv[i] = gelu(hacc[i] + s_b1[acc_row(i, g)]);
-
-  // ---- FFN: stage A (W1 chunk c+1): up(c+1) + second half of GELU(c); stage B (W2 chunk c):
-  // down(c) + first half of GELU(c+1)
-  constexpr int NI = KC > 8 ? KC : 8;
-  // One hidden chunk c: stage A consumes ring slot SA (W1 chunk c + 1), stage B slot SB (W2 chunk
-  // c). The slots are compile-time constants (the loop below handles two chunks per iteration,
-  // NC is even), so every LDS operand address is a fixed per-lane offset.
-  auto ffn_step = [&](int c, auto sa, auto sb) {
-    constexpr int SA = decltype(sa)::value, SB = decltype(sb)::value;
-    const int ia = DT + 1 + 2 * c;
-    // stage A
+  // ---- FFN: per hidden chunk c, stage A (W1 chunk c): up-projection; GELU; stage B (W2 chunk
+  // c): down-projection into X'^T. Two workgroups share a CU, so the VALU work and the waits of
+  // one overlap the MFMAs of the other. With two ring slots every W1 chunk sits in slot SA and
+  // every W2 chunk in slot SB, so each LDS operand address is a fixed per-lane offset.
+  constexpr int SA = DT % NB, SB = (DT + 1) % NB;
+  static_assert(NB == 2, "fixed stage slots assume a two-slot ring");
+  for (int c = 0; c < NC; ++c) {
+    const int ia = DT + 2 * c;
     arrive(ia);
     if (ia + NB - 1 < NCH) issue(ia + NB - 1);
-    f32x16 hn = f32x16{}, hn_odd = f32x16{};
+    f32x16 h = f32x16{};
     {
       const T *base = lds[SA];
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        // the last chunk's look-ahead multiplies W1 chunk 0 again; the result is discarded
-        if (i < KC) {
-          if (i & 1) hn_odd = M::mma(afrag_rows(base, lc, i, true), yfr[i], hn_odd);
-          else hn = M::mma(afrag_rows(base, lc, i, true), yfr[i], hn);
-        }
-        if (i < 8) hv[8 + i] = gelu(hacc[8 + i] + s_b1[32 * c + acc_row(8 + i, g)]);
-      }
+      for (int kc = 0; kc < KC; ++kc) h = M::mma(afrag_rows(base, lc, kc, true), yfr[kc], h);
       sched_lds_mfma<KC, KC, PD>();
     }
-    hn += hn_odd;
     frag hfr[HKC];
-    if constexpr (BF) {
+    {
+      float hv[16];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        frag fr;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) fr[e] = (bf16)hv[8 * hh + e];
-        hfr[hh] = natural_kfrag(fr);
+      for (int v = 0; v < 16; ++v) {
+        const float hx = h[v] + s_b1[32 * c + acc_row(v, g)];
+        if constexpr (BF) hv[v] = gelu_fit(hx);
+        else hv[v] = gelu_as(hx);
       }
-    } else {
+      if constexpr (BF) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) hfr[v] = hv[v];
+        for (int hh = 0; hh < 2; ++hh) {
+          frag fr;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) fr[e] = (bf16)hv[8 * hh + e];
+          hfr[hh] = natural_kfrag(fr);
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) hfr[v] = hv[v];
+      }
     }
-    // stage B
     arrive(ia + 1);
     if (ia + NB < NCH) issue(ia + NB);
     {
       const T *base = lds[SB];
-      const int cn = c + 1 < NC ? c + 1 : 0;   // after the last chunk: discarded look-ahead
 #pragma unroll
       for (int kc = 0; kc < HKC; ++kc)
 #pragma unroll
-        for (int ti = 0; ti < DT; ++ti) {
-          acc[ti] = M::mma(afrag_cols(base, 32 * ti + lc, kc), hfr[kc], acc[ti]);
-          const int i = kc * DT + ti;
-          if (i < 8) hv[i] = gelu(hn[i] + s_b1[32 * cn + acc_row(i, g)]);
-        }
+        for (int ti = 0; ti < DT; ++ti) acc[ti] = M::mma(afrag_cols(base, 32 * ti + lc, kc), hfr[kc], acc[ti]);
       sched_lds_mfma<DT * HKC, DT * HKC, PD>();
-#pragma unroll
-      for (int i = DT * HKC; i < 8; ++i) hv[i] = gelu(hn[i] + s_b1[32 * cn + acc_row(i, g)]);
     }
-    hacc = hn;
-  };
-  static_assert(NB % 2 == 0, "two hidden chunks per iteration need an even ring");
-  for (int c = 0; c < NC; c += 2) {
-    ffn_step(c, std::integral_constant<int, (DT + 1) % NB>{}, std::integral_constant<int, (DT + 2) % NB>{});
-    ffn_step(c + 1, std::integral_constant<int, (DT + 3) % NB>{}, std::integral_constant<int, (DT + 4) % NB>{});
   }
 
   // ---- statistics of X' for the next block's norm 1 (exact two-pass over the registers) --------
