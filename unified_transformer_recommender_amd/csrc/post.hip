@@ -20,9 +20,10 @@
 // few MFMAs ahead of their use. Rows are stored unpadded with their 16-byte pieces XOR-swizzled so
 // that 16 lanes reading 16 consecutive rows touch 16 distinct bank groups.
 //
-// Occupancy: the kernel is held to 256 registers per lane so that two workgroups share a CU. Each
-// hidden chunk then runs plainly in order (up-projection, GELU, down-projection): the other
-// workgroup's MFMAs fill this one's VALU phases, waits and activation loads.
+// Occupancy: for bf16 at d <= 256 the kernel is held to 256 registers per lane so that two
+// workgroups share a CU. Each hidden chunk then runs plainly in order (up-projection, GELU,
+// down-projection): the other workgroup's MFMAs fill this one's VALU phases, waits and activation
+// loads.
 //
 // GELU is the erf form 0.5 x (1 + erf(x / sqrt 2)). The fp32 path evaluates erf with Abramowitz &
 // Stegun 7.1.26 (|error| <= 1.5e-7): with z = |x|/sqrt2, t = 1/(1 + p z),
@@ -72,6 +73,11 @@ __device__ __forceinline__ float gelu_fit(float x) {
 template <typename T, int D>
 constexpr int post_nw() { return (sizeof(T) == 2 && D == 128) ? 8 : 4; }
 
+// Workgroups per CU the register budget is set for: two where a lane's d-wide accumulators and
+// operand fragments fit in 256 registers (bf16, d <= 256), else one (512 registers).
+template <typename T, int D>
+constexpr int post_wgs_per_cu() { return (sizeof(T) == 2 && D <= 256) ? 2 : 1; }
+
 // Row layout of a weight chunk in LDS: RP 16-byte pieces per row; piece q of row r is stored at
 // slot q ^ swz(r). `rpb` = rows sharing one 256-byte bank line.
 template <int RP, int RB>
@@ -93,7 +99,7 @@ __device__ __forceinline__ bf16x8 natural_kfrag(bf16x8 f) {
 }
 
 template <typename T, typename TR, int D, bool LAYER>
-__global__ __launch_bounds__((post_nw<T, D>() * 64), 2) void post_kernel(const PostArgs a) {
+__global__ __launch_bounds__((post_nw<T, D>() * 64), (post_wgs_per_cu<T, D>())) void post_kernel(const PostArgs a) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int NW = post_nw<T, D>();
