@@ -7,7 +7,7 @@ pyramid attention, output projection and mixed FFN. The metric is candidates sco
 (each batch row is one candidate carrying its own user sequence) plus the fraction of bf16 MFMA
 peak that the algorithmic FLOPs reach.
 
-Other workloads (--workload two_stage | append | onetrans_l) print their own line; they are
+Other workloads (--workload two_stage | append | append_ragged | onetrans_l) print their own line; they are
 parity cases of the same kernels and are measured for the design notes, not as the headline.
 
 Timing: W untimed warm-up steps, then K timed steps between a device synchronisation on both
@@ -40,7 +40,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="onetrans_s",
-                   choices=["onetrans_s", "two_stage", "append", "onetrans_l"])
+                   choices=["onetrans_s", "two_stage", "append", "append_ragged", "onetrans_l"])
     p.add_argument("--dtype", default=None, choices=[None, "bf16", "f32"])
     p.add_argument("--no-trace", action="store_true", help="no per-kernel events in the timed region")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline (0: skip)")
@@ -169,18 +169,23 @@ def main():
         old, new = synth.append_batch(w)
         xo, xnw = up(old), up(new)
         xn = up(np.stack([synth.candidate_tokens(w, u, 0) for u in range(w.n_users)])[:, None])
-        pristine = ob.KVCache(model, w.n_users, w.l_s)
+        # ragged users: user u's cached rows are the first lens[u] rows (the rest of `old` pads)
+        lens = synth.user_cached_lengths(w) if w.l_old_min else None
+        pristine = ob.KVCache(model, w.n_users, w.l_s, user_len=lens)
         ob.onetrans_prefill_user(model, xo, pristine)
-        cache = ob.KVCache(model, w.n_users, w.l_s)
+        cache = ob.KVCache(model, w.n_users, w.l_s, user_len=lens)
         out_new = torch.empty((w.n_users, w.d_l, m.d_model), dtype=torch.float32, device=dev)
         out = torch.empty((w.n_users, 1, m.l_ns, m.d_model), dtype=torch.float32, device=dev)
         ws1 = model.workspace(ob.L.OP_APPEND, w.n_users, d_l=w.d_l)
         ws2 = model.workspace(ob.L.OP_SCORE, w.n_users, n_cand=1)
         n_units = w.n_users
-        ap = cm.append_classes(m.d_model, m.d_ff, m.n_blocks, w.l_old, w.d_l, store_bytes)
-        sc = cm.score_classes(m.d_model, m.d_ff, m.l_ns, w.l_old + w.d_l, (w.l_old + w.d_l,) * m.n_blocks,
-                              store_bytes)
-        classes = {k: ap[k] + sc[k] for k in sc}
+        classes = {}
+        for l_old in (lens or [w.l_old]):   # per-user work, averaged over the users
+            ap = cm.append_classes(m.d_model, m.d_ff, m.n_blocks, l_old, w.d_l, store_bytes)
+            sc = cm.score_classes(m.d_model, m.d_ff, m.l_ns, l_old + w.d_l, (l_old + w.d_l,) * m.n_blocks,
+                                  store_bytes)
+            for k in sc:
+                classes[k] = classes.get(k, 0.0) + (ap[k] + sc[k]) / len(lens or [w.l_old])
         restore_ms = []
 
         def step():
@@ -270,9 +275,11 @@ def main():
             units = done
         else:
             t_app = 0.0
-            while done < 64 and (time.perf_counter() - t0 < a.cpu_seconds or done < 2):
+            ul = synth.user_cached_lengths(w)
+            while done < min(64, w.n_users) and (time.perf_counter() - t0 < a.cpu_seconds or done < 2):
                 o, nw = synth.append_rows(w, done)
-                co, _ = O.prefill_user(o, host_w, m, (w.l_old,) * m.n_blocks)
+                o = o[: ul[done]]
+                co, _ = O.prefill_user(o, host_w, m, (ul[done],) * m.n_blocks)
                 t1 = time.perf_counter()
                 O.append_events(co, nw, host_w, m)
                 t_app += time.perf_counter() - t1
@@ -310,7 +317,8 @@ def main():
         **extra,
     }
     if w.kind == "append":
-        byts = cm.append_cache_bytes(m.d_model, m.n_blocks, w.l_old, w.d_l, store_bytes) * n_units
+        byts = sum(cm.append_cache_bytes(m.d_model, m.n_blocks, l_old, w.d_l, store_bytes)
+                   for l_old in (synth.user_cached_lengths(w)))
         line["cache_GB/s"] = round(byts / (ms_step * 1e-3) / 1e9, 1)
     print(json.dumps(line))
 

@@ -88,6 +88,10 @@ typedef struct {
   int capacity;           /* rows per (user, block) */
   int *layer_len;         /* host [n_blocks]: valid rows of block n (same for every user); written
                              by prefill_user (s_n) and advanced by append_events (+d_l) */
+  int *user_len;          /* host [n_users] or NULL. Ragged users: when set, user u's valid rows are
+                             the first user_len[u] rows of every block (an unpyramided cache) and
+                             the calls below read and advance it per user; layer_len then holds the
+                             largest user_len. NULL: every user has layer_len[n] rows. */
 } onetrans_kv_cache;
 
 /* Workspace bytes needed by one call of `op`.
@@ -116,14 +120,21 @@ int onetrans_forward(const onetrans_config *cfg, const onetrans_block_weights *b
  * cache: block n gets s_n rows at positions 0..s_n-1. Sets cache->layer_len[n] = s_n.
  *   x_s   [n_users][l_s][d] storage dtype.
  *   out_s [n_users][q_last][d] fp32 final S rows, or NULL.
- * Errors: as forward, plus CACHE_CAPACITY (capacity < l_s or n_users > cache->n_users). */
+ * Ragged users (cache->user_len set by the caller, 0 <= user_len[u] <= l_s): user u's sequence is
+ * the first user_len[u] rows of x_s[u]; the rows after it are padding. Row t only attends to rows
+ * <= t, so the first user_len[u] rows of every block, in the cache and in out_s, are exactly those
+ * of user u's own sequence (the padding rows hold values no later call reads). Needs an
+ * unpyramided schedule (every s_queries[n] = l_s), otherwise UNSUPPORTED.
+ * Errors: as forward, plus CACHE_CAPACITY (capacity < l_s or n_users > cache->n_users), SHAPE (a
+ * user_len outside [0, l_s]). */
 int onetrans_prefill_user(const onetrans_config *cfg, const onetrans_block_weights *blk,
                           const void *x_s, int n_users, int l_s, onetrans_kv_cache *cache, void *out_s,
                           void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Stage II (section 7.5.3): score `n_cand` candidates per user. At block n the NS rows of a
- * candidate sit behind the user's layer_len[n] cached S rows; NS query j attends over those cached
- * keys and its own NS keys 0..j in one softmax, then goes through its token-specific FFN.
+ * candidate sit behind the user's layer_len[n] (ragged: user_len[u]) cached S rows; NS query j
+ * attends over those cached keys and its own NS keys 0..j in one softmax, then goes through its
+ * token-specific FFN.
  *   x_ns   [n_users][n_cand][l_ns][d] storage dtype.
  *   out_ns [n_users][n_cand][l_ns][d] fp32 final NS rows.
  * The cache is read only. Errors: as forward, plus SHAPE if n_users > cache->n_users or a
@@ -139,9 +150,12 @@ int onetrans_score_candidates(const onetrans_config *cfg, const onetrans_block_w
  * layer_len[n] becomes L_old + d_l. Needs an unpyramided cache (every layer_len equal), otherwise
  * UNSUPPORTED: with a tail-count pyramid the key window of later blocks would slide with every
  * append, so appending could not equal recomputation. cfg->s_queries is not read by this call.
+ * Ragged users (cache->user_len set): L_old is user_len[u] for user u, and user_len[u] advances by
+ * d_l (the lengths are read and advanced on the host at enqueue time).
  *   x_new   [n_users][d_l][d] storage dtype.
  *   out_new [n_users][d_l][d] fp32 final rows of the new events, or NULL.
- * Errors: as forward, plus CACHE_CAPACITY (L_old + d_l > capacity), UNSUPPORTED (pyramided cache). */
+ * Errors: as forward, plus CACHE_CAPACITY (L_old + d_l > capacity for some user), UNSUPPORTED
+ * (pyramided cache), SHAPE (a user_len outside [0, capacity]). */
 int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weights *blk,
                            onetrans_kv_cache *cache, const void *x_new, int n_users, int d_l,
                            void *out_new, void *ws, size_t ws_bytes, hipStream_t stream);

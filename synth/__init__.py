@@ -24,11 +24,12 @@ from .shapes import (ModelShape, Workload, WORKLOADS, TEST_SHAPES, linear_pyrami
                      workload, test_workload)
 from .gen import (round_bf16, bf16_bits, BlockWeights, make_weights, sep_vectors,
                   forward_sample, forward_batch, user_sequence, user_sequences,
-                  candidate_tokens, candidate_batch, append_rows, append_batch)
+                  candidate_tokens, candidate_batch, append_rows, append_batch,
+                  user_cached_lengths)
 
 __all__ = [
     "ModelShape", "Workload", "WORKLOADS", "TEST_SHAPES", "linear_pyramid", "workload",
     "test_workload", "round_bf16", "bf16_bits", "BlockWeights", "make_weights", "sep_vectors",
     "forward_sample", "forward_batch", "user_sequence", "user_sequences", "candidate_tokens",
-    "candidate_batch", "append_rows", "append_batch",
+    "candidate_batch", "append_rows", "append_batch", "user_cached_lengths",
 ]

@@ -168,6 +168,15 @@ def append_rows(w: Workload, u: int):
     return s[: w.l_old], s[w.l_old:]
 
 
+def user_cached_lengths(w: Workload) -> list:
+    """Ragged append: each user's cached rows before the append, uniform in [l_old_min, l_old]
+    (every user has l_old when l_old_min is 0)."""
+    if not w.l_old_min:
+        return [w.l_old] * w.n_users
+    rng = _rng(w.input_seed, (2,))
+    return [int(x) for x in rng.integers(w.l_old_min, w.l_old + 1, size=w.n_users)]
+
+
 def append_batch(w: Workload, users: Optional[Sequence[int]] = None):
     us = range(w.n_users) if users is None else users
     s = np.stack([user_sequence(w, u) for u in us])

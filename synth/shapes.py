@@ -65,6 +65,8 @@ class Workload:
     n_cand: int = 0                    # candidates per user
     l_old: int = 0                     # append: cached rows before the append
     d_l: int = 0                       # append: new rows
+    l_old_min: int = 0                 # ragged append: users' cached rows drawn uniformly from
+                                       # [l_old_min, l_old] (0: every user has l_old)
     input_seed: int = 0
     parity_subset: Tuple[int, ...] = field(default_factory=tuple)
 
@@ -119,6 +121,12 @@ WORKLOADS = {
                     "1158 cached rows, append 32 new rows, 1 candidate/user; bf16",
         model=_ONETRANS_S, kind="append", l_s=1190, s_queries=(1190,) * 6, n_users=128, n_cand=1,
         l_old=1158, d_l=32, input_seed=2004, parity_subset=(0, 1, 64, 127)),
+    "append_ragged": Workload(
+        key="append_ragged",
+        description="Cross-request append with ragged users on the OneTransS-shaped model without pyramid: "
+                    "128 users with 579..1158 cached rows (uniform), append 32 new rows, 1 candidate/user; bf16",
+        model=_ONETRANS_S, kind="append", l_s=1190, s_queries=(1190,) * 6, n_users=128, n_cand=1,
+        l_old=1158, d_l=32, l_old_min=579, input_seed=2005, parity_subset=(0, 1, 64, 127)),
     "onetrans_l": Workload(
         key="onetrans_l",
         description="OneTransL-shaped forward: 8 blocks, d=512, 16 heads, FFN 2048; L_S=2048, L_NS=16; "

@@ -56,7 +56,7 @@ def test_workspace_and_cache_sizes():
     got = lib.onetrans_workspace_bytes(ctypes.byref(c), L.OP_FORWARD, B, l_s, 0, 0)
     d, T, R = 256, 136, 116
     al = lambda n: (n + 255) // 256 * 256
-    expect = 2 * al(B * R * d * 4) + 2 * al(B * R * 8) + al(B * R * d * 2) + 2 * al(B * T * d * 2) + al(B * R * d * 2) + al(16)
+    expect = 2 * al(B * R * d * 4) + 2 * al(B * R * 8) + al(B * R * d * 2) + 2 * al(B * T * d * 2) + al(B * R * d * 2) + al(16) + al(B * 4)
     assert got == expect
     assert lib.onetrans_kv_cache_bytes(ctypes.byref(c), 3, 200) == 3 * 2 * 8 * 200 * 32 * 2
     assert lib.onetrans_workspace_bytes(ctypes.byref(c), L.OP_SCORE, 2, 0, 5, 0) > 0
@@ -141,6 +141,38 @@ def test_serving_validation_errors():
     assert list(full._keep) == [124, 124]            # nothing advanced on error
     assert lib.onetrans_append_events(ctypes.byref(c), b, ctypes.byref(full), FAKE, 2, 0, None, FAKE, 1 << 40,
                                       None) == L.ERR_SHAPE
+
+
+def _ragged_cache(user_len, n_users=2, cap=200, lens=(120, 120)):
+    kc = _cache(n_users, cap, lens)
+    ul = (ctypes.c_int * len(user_len))(*user_len)
+    kc.user_len = ul
+    kc._keep_ul = ul
+    return kc
+
+
+def test_ragged_user_validation_errors():
+    """Ragged users (per-user cached lengths): every check returns before any HIP call."""
+    lib = L.lib()
+    flat = _cfg(sq=(120, 120))
+    b = _blocks(2)
+    # prefill: padding rows are only harmless without pruning; lengths within [0, l_s]
+    assert lib.onetrans_prefill_user(ctypes.byref(_cfg()), b, FAKE, 2, 120, ctypes.byref(_ragged_cache((50, 120))),
+                                     None, FAKE, 1 << 40, None) == L.ERR_UNSUPPORTED
+    assert lib.onetrans_prefill_user(ctypes.byref(flat), b, FAKE, 2, 120, ctypes.byref(_ragged_cache((50, 121))),
+                                     None, FAKE, 1 << 40, None) == L.ERR_SHAPE
+    assert lib.onetrans_prefill_user(ctypes.byref(flat), b, FAKE, 2, 120, ctypes.byref(_ragged_cache((-1, 7))),
+                                     None, FAKE, 1 << 40, None) == L.ERR_SHAPE
+    # append: each user's own capacity, lengths within the cache; nothing advanced on error
+    kc = _ragged_cache((100, 125), cap=128)
+    assert lib.onetrans_append_events(ctypes.byref(flat), b, ctypes.byref(kc), FAKE, 2, 8, None, FAKE, 1 << 40,
+                                      None) == L.ERR_CACHE_CAPACITY
+    assert list(kc._keep_ul) == [100, 125] and list(kc._keep) == [120, 120]
+    assert lib.onetrans_append_events(ctypes.byref(flat), b, ctypes.byref(_ragged_cache((100, 201))), FAKE, 2, 8,
+                                      None, FAKE, 1 << 40, None) == L.ERR_SHAPE
+    # score: lengths within the cache
+    assert lib.onetrans_score_candidates(ctypes.byref(flat), b, ctypes.byref(_ragged_cache((10, 201))), FAKE, 2, 4,
+                                         FAKE, FAKE, 1 << 40, None) == L.ERR_SHAPE
 
 
 def test_status_strings():

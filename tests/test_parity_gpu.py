@@ -125,6 +125,44 @@ def test_append_small(dtype):
         assert e <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ragged_users_prefill_append_score(dtype):
+    """Users with different cached lengths in one call (cache.user_len): padded prefill, append
+    behind each user's own length, then Stage II scoring against each user's own keys. Each user
+    is checked against the oracle run on that user's own rows alone; a user with no cached rows
+    appends onto an empty cache (the oracle then is Stage I of the new rows by themselves)."""
+    w = replace(synth.test_workload("tiny3_append", dtype), n_users=5, n_cand=2, input_seed=2117)
+    m, ws = w.model, weights(w.model)
+    lens = [24, 1, 17, 0, 9]                    # cached rows per user before the append
+    say(f"[ragged] {w.key} dtype={dtype} lens={lens} d_l={w.d_l}")
+    mdl = model(w, s_queries=(w.l_old,) * m.n_blocks)
+    seq = synth.user_sequences(w)               # [U][l_old + d_l][d]; rows past a user's length pad
+    old = np.ascontiguousarray(seq[:, : w.l_old])
+    new = np.ascontiguousarray(seq[:, w.l_old:])
+    xn = synth.candidate_batch(w)
+    cache = ob.KVCache(mdl, w.n_users, w.l_old + w.d_l, user_len=lens)
+    ob.onetrans_prefill_user(mdl, dev(old, mdl), cache)
+    assert cache.user_lengths == lens
+    out_new = torch.empty((w.n_users, w.d_l, m.d_model), dtype=torch.float32, device=mdl.device)
+    ob.onetrans_append_events(mdl, cache, dev(new, mdl), out_new)
+    sc = ob.onetrans_score_candidates(mdl, cache, dev(xn, mdl))
+    torch.cuda.synchronize()
+    assert cache.user_lengths == [n + w.d_l for n in lens]
+    for u, n_old in enumerate(lens):
+        if n_old:
+            oc, _ = O.prefill_user(old[u, :n_old], ws, m, (n_old,) * m.n_blocks)
+            nc, ref_new = O.append_events(oc, new[u], ws, m)
+        else:
+            nc, ref_new = O.prefill_user(new[u], ws, m, (w.d_l,) * m.n_blocks)
+        e_new = rel_err(out_new[u].cpu().numpy(), ref_new)
+        n_all = n_old + w.d_l
+        for n, (k, v) in enumerate(cache_to_host(cache, u, m.n_blocks, [n_all] * m.n_blocks)):
+            assert rel_err(k, nc[n]["k"]) <= TOL[dtype] and rel_err(v, nc[n]["v"]) <= TOL[dtype], (u, n)
+        e_sc = max(rel_err(sc[u, c].cpu().numpy(), O.score_candidate(nc, xn[u, c], ws, m)) for c in range(w.n_cand))
+        say(f"  user {u} (L_old {n_old}): new rows {e_new:.3e} scores {e_sc:.3e}")
+        assert e_new <= TOL[dtype] and e_sc <= TOL[dtype], (u, e_new, e_sc)
+
+
 def test_edge_cases_forward():
     """batch 1, no NS tokens, pyramid down to one S query."""
     base = synth.test_workload("tiny3_fwd", "bf16")
@@ -184,6 +222,32 @@ def test_append_full():
         e1 = rel_err(out_new[u].cpu().numpy(), ref_new)
         e2 = rel_err(sc[u, 0].cpu().numpy(), O.score_candidate(nc, xn[u, 0], ws, m))
         say(f"  user {u}: new rows {e1:.3e} score {e2:.3e}")
+        assert e1 <= TOL["bf16"] and e2 <= TOL["bf16"]
+
+
+def test_append_ragged_full():
+    """The ragged append workload in the launch configuration the benchmark times: 128 users
+    with their own cached lengths, each checked user recomputed alone by the oracle."""
+    w = synth.workload("append_ragged")
+    lens = synth.user_cached_lengths(w)
+    say(f"[append ragged full] U={w.n_users} L_old {min(lens)}..{max(lens)} dL={w.d_l}")
+    m, ws = w.model, weights(w.model)
+    mdl = model(w, s_queries=(w.l_old,) * m.n_blocks)
+    old, new = synth.append_batch(w)
+    xn = np.stack([synth.candidate_tokens(w, u, 0) for u in range(w.n_users)])[:, None]
+    cache = ob.KVCache(mdl, w.n_users, w.l_s, user_len=lens)
+    ob.onetrans_prefill_user(mdl, dev(old, mdl), cache)
+    out_new = torch.empty((w.n_users, w.d_l, m.d_model), dtype=torch.float32, device=mdl.device)
+    ob.onetrans_append_events(mdl, cache, dev(new, mdl), out_new)
+    sc = ob.onetrans_score_candidates(mdl, cache, dev(xn, mdl))
+    torch.cuda.synchronize()
+    assert cache.user_lengths == [n + w.d_l for n in lens]
+    for u in w.parity_subset:
+        oc, _ = O.prefill_user(old[u, : lens[u]], ws, m, (lens[u],) * m.n_blocks)
+        nc, ref_new = O.append_events(oc, new[u], ws, m)
+        e1 = rel_err(out_new[u].cpu().numpy(), ref_new)
+        e2 = rel_err(sc[u, 0].cpu().numpy(), O.score_candidate(nc, xn[u, 0], ws, m))
+        say(f"  user {u} (L_old {lens[u]}): new rows {e1:.3e} score {e2:.3e}")
         assert e1 <= TOL["bf16"] and e2 <= TOL["bf16"]
 
 

@@ -86,9 +86,13 @@ class Model:
 
 
 class KVCache:
-    """Caller-owned K/V cache [user][block][head][capacity][d_head] in the storage dtype."""
+    """Caller-owned K/V cache [user][block][head][capacity][d_head] in the storage dtype.
 
-    def __init__(self, model: Model, n_users: int, capacity: int):
+    `user_len` (one int per user) makes the users ragged: user u's valid rows are its first
+    user_len[u] rows of every block, and prefill / append / score read (and append advances) these
+    per-user lengths."""
+
+    def __init__(self, model: Model, n_users: int, capacity: int, user_len=None):
         nbytes = int(L.lib().onetrans_kv_cache_bytes(ctypes.byref(model.cfg), n_users, capacity))
         if nbytes == 0:
             raise ValueError("invalid cache shape")
@@ -97,17 +101,30 @@ class KVCache:
         self.v = torch.empty(shape, dtype=model.torch_dtype, device=model.device)
         assert self.k.numel() * model.esz == nbytes
         self.layer_len = (ctypes.c_int * model.n_blocks)()
-        self.c = L.KVCache(self.k.data_ptr(), self.v.data_ptr(), n_users, capacity, self.layer_len)
+        self.user_len = None
+        if user_len is not None:
+            if len(user_len) != n_users:
+                raise ValueError("user_len needs one length per user")
+            self.user_len = (ctypes.c_int * n_users)(*[int(x) for x in user_len])
+        self.c = L.KVCache(self.k.data_ptr(), self.v.data_ptr(), n_users, capacity, self.layer_len,
+                           self.user_len)
 
     @property
     def lengths(self):
         return list(self.layer_len)
+
+    @property
+    def user_lengths(self):
+        return None if self.user_len is None else list(self.user_len)
 
     def copy_(self, other: "KVCache") -> "KVCache":
         self.k.copy_(other.k)
         self.v.copy_(other.v)
         for i, n in enumerate(other.layer_len):
             self.layer_len[i] = n
+        if self.user_len is not None and other.user_len is not None:
+            for i, n in enumerate(other.user_len):
+                self.user_len[i] = n
         return self
 
 

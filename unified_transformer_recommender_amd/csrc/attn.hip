@@ -184,7 +184,10 @@ __global__ __launch_bounds__(ATTN_WAVES * 64) void attn_kernel(const AttnArgs a)
     valid = cslot < cpw && c < a.n_cand;
     z = grp * a.n_cand + (valid ? c : 0);
   }
-  const int qpos = a.p0 + qi;
+  // ragged cached lengths: this sequence's positions and prefix keys start `shift` rows later
+  const int shift = a.seq_shift ? a.seq_shift[grp] : 0;
+  const int p0 = a.p0 + shift, n_pre = a.n_pre + shift;
+  const int qpos = p0 + qi;
 
   frag qf[DH / M::KSTEP];
   {
@@ -197,13 +200,13 @@ __global__ __launch_bounds__(ATTN_WAVES * 64) void attn_kernel(const AttnArgs a)
   int n_keys, wave_min = 0, wave_max = 0;
   if constexpr (!STAGE2) {
     const int wg_last = min(a.R, (qb + 1) * ATTN_QBLOCK) - 1;
-    n_keys = min(a.n_pre, a.p0 + wg_last + 1);
+    n_keys = min(n_pre, p0 + wg_last + 1);
     const int wf = qb * ATTN_QBLOCK + wave * 32;
     const int wl = min(a.R, wf + 32) - 1;
-    wave_min = a.p0 + wf;
-    wave_max = wf < a.R ? a.p0 + wl : -1;
+    wave_min = p0 + wf;
+    wave_max = wf < a.R ? p0 + wl : -1;
   } else {
-    n_keys = a.n_pre;
+    n_keys = n_pre;
   }
   const T *kp = (const T *)a.k_pre + grp * a.pre_sb + h * a.pre_sh;
   const T *vp = (const T *)a.v_pre + grp * a.pre_sb + h * a.pre_sh;

@@ -214,6 +214,7 @@ struct QkvArgs {
   float eps;
   float q_scale;           // queries are stored multiplied by this (log2(e) / sqrt(d_head))
   void *trash;             // 16 bytes that masked-off output pieces are written to
+  const int *kv_shift;     // [n_seq] or null: K/V row t of sequence b is stored at row t + kv_shift[b]
 };
 
 // ---------------------------------------------------------------------------------------------
@@ -262,6 +263,8 @@ struct AttnArgs {
   const void *k_pre, *v_pre; long long pre_sb, pre_sh;
   const void *k_own, *v_own; long long own_sb, own_sh;
   void *o; long long o_sb;
+  const int *seq_shift;    // [n_seq_grp] or null: sequence z's query positions and prefix keys
+                           // start seq_shift[z] rows later (ragged cached lengths)
 };
 
 }  // namespace ot

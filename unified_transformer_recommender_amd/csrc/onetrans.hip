@@ -125,7 +125,7 @@ int check_weights(const onetrans_block_weights *blk, const Dims &D) {
 
 // ---- workspace -------------------------------------------------------------------------------
 struct Ws {
-  size_t x[2], st[2], q, k, v, o, trash, total;
+  size_t x[2], st[2], q, k, v, o, trash, seq, total;
 };
 
 inline size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -154,6 +154,8 @@ Ws ws_layout(const Dims &D, size_t n, size_t tin, size_t rq, bool kv) {
   w.o = take(n * rq * d * es);
   // 16 bytes that the QKV kernel's masked-off lanes store to (its store count stays fixed)
   w.trash = take(16);
+  // per-sequence row offsets of ragged cached users (int32)
+  w.seq = take(n * 4);
   w.total = off;
   return w;
 }
@@ -201,6 +203,9 @@ struct Step {
   bool need_out;
   void *stats_in;      // (mean, rstd) per row of x, laid out like x; null: norm 1 computes them
   void *stats_out;     // where the post kernel writes (mean, rstd) per row of out; null: none
+  const int *kv_shift; // device [n_seq] or null: K/V rows of sequence b go kv_shift[b] rows later
+  const int *seq_shift;   // device [n_grp] or null: attention positions / prefix keys of sequence
+                          // (or user) z start seq_shift[z] rows later
 };
 
 int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, char *ws, const Ws &L,
@@ -254,6 +259,7 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
     qa.eps = D.eps;
     qa.q_scale = 1.4426950408889634f / sqrtf((float)dh);
     qa.trash = ws + L.trash;
+    qa.kv_shift = st.kv_shift;
     if (tiles > 0x7fffffffLL) return ONETRANS_ERR_UNSUPPORTED;
     const hipError_t e = timed(ONETRANS_K_QKV, stream, [&] { return launch_qkv(D.dt, st.x_f32, qa, (int)tiles, stream); });
     if (e != hipSuccess) return ONETRANS_ERR_HIP;
@@ -278,6 +284,7 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
     a.pre_sh = st.pre_sh;
     a.o = ob;
     a.o_sb = (long long)R * d;
+    a.seq_shift = st.seq_shift;
     if (st.stage2) {
       a.n_seq_grp = st.n_grp;
       a.n_cand = st.n_cand;
@@ -349,6 +356,21 @@ int check_cache(const onetrans_kv_cache *c) {
   if (!c || !c->k || !c->v || !c->layer_len) return ONETRANS_ERR_INVALID_ARG;
   if (c->n_users < 1 || c->capacity < 1) return ONETRANS_ERR_INVALID_ARG;
   if (misaligned(c->k) || misaligned(c->v)) return ONETRANS_ERR_ALIGNMENT;
+  return ONETRANS_OK;
+}
+
+// Ragged users: every user_len within [0, limit].
+int check_user_len(const onetrans_kv_cache *c, int n_users, int limit) {
+  for (int u = 0; u < n_users; ++u)
+    if (c->user_len[u] < 0 || c->user_len[u] > limit) return ONETRANS_ERR_SHAPE;
+  return ONETRANS_OK;
+}
+
+// Copy the users' cached lengths into the workspace (read on the host at enqueue time).
+int upload_user_len(const onetrans_kv_cache *c, int n_users, char *ws, const Ws &L, hipStream_t stream) {
+  if (hipMemcpyAsync(ws + L.seq, c->user_len, (size_t)n_users * sizeof(int), hipMemcpyHostToDevice, stream) !=
+      hipSuccess)
+    return ONETRANS_ERR_HIP;
   return ONETRANS_OK;
 }
 
@@ -450,6 +472,12 @@ int onetrans_prefill_user(const onetrans_config *cfg, const onetrans_block_weigh
   if (misaligned(x_s) || (out_s && misaligned(out_s))) return ONETRANS_ERR_ALIGNMENT;
   if ((rc = check_cache(cache))) return rc;
   if (n_users > cache->n_users || l_s > cache->capacity) return ONETRANS_ERR_CACHE_CAPACITY;
+  if (cache->user_len) {
+    // ragged users: padding rows behind each user's sequence are only harmless without pruning
+    for (int n = 0; n < D.N; ++n)
+      if (cfg->s_queries[n] != l_s) return ONETRANS_ERR_UNSUPPORTED;
+    if ((rc = check_user_len(cache, n_users, l_s))) return rc;
+  }
   size_t n, tin, rq;
   bool kv;
   ws_dims(cfg, D, ONETRANS_OP_PREFILL, n_users, l_s, 0, 0, n, tin, rq, kv);
@@ -520,6 +548,8 @@ int onetrans_score_candidates(const onetrans_config *cfg, const onetrans_block_w
   if (n_users > cache->n_users) return ONETRANS_ERR_SHAPE;
   for (int n = 0; n < D.N; ++n)
     if (cache->layer_len[n] < 0 || cache->layer_len[n] > cache->capacity) return ONETRANS_ERR_SHAPE;
+  const bool ragged = cache->user_len != nullptr;
+  if (ragged && (rc = check_user_len(cache, n_users, cache->capacity))) return rc;
   size_t n, tin, rq;
   bool kv;
   ws_dims(cfg, D, ONETRANS_OP_SCORE, n_users, 0, n_cand, 0, n, tin, rq, kv);
@@ -527,13 +557,15 @@ int onetrans_score_candidates(const onetrans_config *cfg, const onetrans_block_w
   if ((rc = check_ws(D, L, ws, ws_bytes))) return rc;
 
   char *w = (char *)ws;
+  if (ragged && (rc = upload_user_len(cache, n_users, w, L, stream))) return rc;
   const int d = D.d, H = D.H, dh = D.dh, ns = D.lns;
   const int nseq = n_users * n_cand;
-  RowView x{const_cast<void *>(x_ns), (long long)ns * d, cache->layer_len[0], d};
+  // ragged users: positions are relative to each user's own cached length (the attention adds it)
+  RowView x{const_cast<void *>(x_ns), (long long)ns * d, ragged ? 0 : cache->layer_len[0], d};
   int x_f32 = D.dt == ONETRANS_F32;
   void *stats = nullptr;   // (mean, rstd) rows of x when the previous block wrote them
   for (int n = 0; n < D.N; ++n) {
-    const int s = cache->layer_len[n];
+    const int s = ragged ? 0 : cache->layer_len[n];
     Step st{};
     st.n_seq = nseq;
     st.s = s;
@@ -561,6 +593,7 @@ int onetrans_score_candidates(const onetrans_config *cfg, const onetrans_block_w
     st.pre_sh = cv.sh;
     st.own_sb = st.kN.sb;
     st.own_sh = st.kN.sh;
+    st.seq_shift = ragged ? (const int *)(w + L.seq) : nullptr;
     st.out = RowView{n + 1 == D.N ? out_ns : (void *)(w + L.x[n & 1]), (long long)ns * d, s, d};
     st.need_out = true;
     st.stats_in = stats;
@@ -585,12 +618,18 @@ int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weig
   if (misaligned(x_new) || (out_new && misaligned(out_new))) return ONETRANS_ERR_ALIGNMENT;
   if ((rc = check_cache(cache))) return rc;
   if (n_users > cache->n_users) return ONETRANS_ERR_SHAPE;
-  const int l_old = cache->layer_len[0];
   for (int n = 0; n < D.N; ++n) {
     if (cache->layer_len[n] < 0 || cache->layer_len[n] > cache->capacity) return ONETRANS_ERR_SHAPE;
-    if (cache->layer_len[n] != l_old) return ONETRANS_ERR_UNSUPPORTED;
+    if (cache->layer_len[n] != cache->layer_len[0]) return ONETRANS_ERR_UNSUPPORTED;
   }
-  if ((long long)l_old + d_l > cache->capacity) return ONETRANS_ERR_CACHE_CAPACITY;
+  const bool ragged = cache->user_len != nullptr;
+  if (ragged) {
+    if ((rc = check_user_len(cache, n_users, cache->capacity))) return rc;
+    for (int u = 0; u < n_users; ++u)
+      if ((long long)cache->user_len[u] + d_l > cache->capacity) return ONETRANS_ERR_CACHE_CAPACITY;
+  } else if ((long long)cache->layer_len[0] + d_l > cache->capacity) {
+    return ONETRANS_ERR_CACHE_CAPACITY;
+  }
   size_t n, tin, rq;
   bool kv;
   ws_dims(cfg, D, ONETRANS_OP_APPEND, n_users, 0, 0, d_l, n, tin, rq, kv);
@@ -598,6 +637,11 @@ int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weig
   if ((rc = check_ws(D, L, ws, ws_bytes))) return rc;
 
   char *w = (char *)ws;
+  if (ragged && (rc = upload_user_len(cache, n_users, w, L, stream))) return rc;
+  // ragged users: positions are relative to each user's own cached length, which the QKV kernel
+  // adds to the cache rows it writes and the attention to its query positions and key count
+  const int l_old = ragged ? 0 : cache->layer_len[0];
+  const int *shift = ragged ? (const int *)(w + L.seq) : nullptr;
   const int d = D.d;
   RowView x{const_cast<void *>(x_new), (long long)d_l * d, l_old, d};
   int x_f32 = D.dt == ONETRANS_F32;
@@ -626,6 +670,8 @@ int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weig
     st.pre_sb = st.kS.sb;
     st.pre_sh = st.kS.sh;
     st.out = RowView{last && out_new ? out_new : (void *)(w + L.x[n & 1]), (long long)d_l * d, l_old, d};
+    st.kv_shift = shift;
+    st.seq_shift = shift;
     st.stats_in = stats;
     st.stats_out = last ? nullptr : (void *)(w + L.st[n & 1]);
     st.need_out = !last || out_new != nullptr;
@@ -634,7 +680,13 @@ int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weig
     stats = st.stats_out;
     x_f32 = 1;
   }
-  for (int n = 0; n < D.N; ++n) cache->layer_len[n] = l_old + d_l;
+  if (ragged) {
+    int longest = 0;
+    for (int u = 0; u < n_users; ++u) longest = max(longest, cache->user_len[u] += d_l);
+    for (int n = 0; n < D.N; ++n) cache->layer_len[n] = max(cache->layer_len[n], longest);
+  } else {
+    for (int n = 0; n < D.N; ++n) cache->layer_len[n] = l_old + d_l;
+  }
   return ONETRANS_OK;
 }
 

@@ -95,7 +95,7 @@ __global__ __launch_bounds__(QKV_NW * 64, 2) void qkv_kernel(const QkvArgs a) {
   // group, and whether it is written at all. Every store instruction is issued; a lane with
   // nothing to write sends its piece to a trash slot, so the number of outstanding vector-memory
   // operations after each chunk is a constant the chunk waits rely on.
-  int sb[TG][TS::NI], stt[TG][TS::NI];
+  int sb[TG][TS::NI], stt[TG][TS::NI], ssh[TG][TS::NI];
   bool sval[TG][TS::NI], sq[TG][TS::NI];
 #pragma unroll
   for (int tg = 0; tg < TG; ++tg)
@@ -106,6 +106,7 @@ __global__ __launch_bounds__(QKV_NW * 64, 2) void qkv_kernel(const QkvArgs a) {
       stt[tg][k] = __shfl(t[tg], tok, 64);
       sval[tg][k] = __shfl((int)valid[tg], tok, 64) != 0;
       sq[tg][k] = __shfl((int)lane_q[tg], tok, 64) != 0;
+      ssh[tg][k] = a.kv_shift ? a.kv_shift[sb[tg][k]] : 0;   // ragged cache: the sequence's row offset
     }
   T *stg = stage[wave];
 
@@ -297,7 +298,8 @@ __global__ __launch_bounds__(QKV_NW * 64, 2) void qkv_kernel(const QkvArgs a) {
         const u32x4 piece = TS::get(stg, k, lane);
         const int f = 32 * ci + TS::feature(lane);
         const int h = f / dh, c = f - h * dh;
-        T *dst = (T *)hv.base + sb[tg][k] * hv.sb + h * hv.sh + (long long)(stt[tg][k] - hv.t_off) * dh + c;
+        const int row = stt[tg][k] - hv.t_off + (seg < 2 ? ssh[tg][k] : 0);
+        T *dst = (T *)hv.base + sb[tg][k] * hv.sb + h * hv.sh + (long long)row * dh + c;
         st16((seg < 2 ? sval[tg][k] : sq[tg][k]) ? dst : trash, piece);
       }
     }
