@@ -167,6 +167,29 @@ def test_append_equals_recompute():
         assert _rel(O.score_candidate(new_cache, xn, ws, m), O.score_candidate(full_cache, xn, ws, m)) < 1e-12
 
 
+def test_padded_prefill_caches_each_users_own_rows():
+    """Ragged users (reading R25): with the causal mask, rows past a user's own length (padding in
+    a shared-length prefill) change none of the rows before them, so the first L rows of every
+    block's cache and output equal those of the user's own L-row sequence. Rows of the padded
+    run past L do differ from the unpadded ones (there are none), so the check is on the prefix."""
+    w = synth.test_workload("tiny3_append")
+    m = w.model
+    ws = synth.make_weights(m)
+    seq = synth.user_sequence(w, 0)                       # 32 rows
+    full = seq.shape[0]
+    pad_cache, pad_out = O.prefill_user(seq, ws, m, (full,) * m.n_blocks)
+    for n_rows in (1, 9, 24):
+        own_cache, own_out = O.prefill_user(seq[:n_rows], ws, m, (n_rows,) * m.n_blocks)
+        for a, b in zip(own_cache, pad_cache):
+            assert _rel(a["k"], b["k"][:n_rows]) < 1e-12 and _rel(a["v"], b["v"][:n_rows]) < 1e-12
+        assert _rel(own_out, pad_out[:n_rows]) < 1e-12
+    # the padding does matter to the rows after it: a changed padding row moves the last row
+    alt = seq.copy()
+    alt[24] += 1.0
+    _, alt_out = O.prefill_user(alt, ws, m, (full,) * m.n_blocks)
+    assert _rel(alt_out[:24], pad_out[:24]) < 1e-12 and _rel(alt_out[24:], pad_out[24:]) > 1e-6
+
+
 def test_append_refuses_pyramided_cache():
     w = synth.test_workload("tiny3_two_stage")
     ws = synth.make_weights(w.model)
