@@ -87,46 +87,64 @@ __device__ __forceinline__ f32x16 score_tile(const T *krow, const typename Mma<T
 }
 
 // One 32-key tile: fold the scores s (base-2 units, -inf where invisible) into the running state.
+// The probabilities are first taken against the running maximum m as it stands. Any one of them
+// above 2^RESCALE_HEADROOM makes the lane's tile sum exceed that bound too, so the tile maximum is
+// only searched (and the state rescaled, the probabilities retaken) when some lane's sum does: on
+// the first tile (m starts far below every score) and when the scores climb by more than the
+// headroom. A tile whose sum crosses the bound with no single probability above it costs one
+// needless rescale, which changes nothing in the result.
 template <typename T, int DH>
 __device__ __forceinline__ void softmax_pv(const f32x16 &s, SoftmaxState &st,
                                            const T *vt_row /* this lane's V^T row, or null if lc >= DH */,
                                            int g) {
   using M = Mma<T>;
-  float mt = s[0];
+  using frag = typename M::frag;
+  constexpr int MC = 32 / M::KSTEP;
+  frag pf[MC];
+  float tsum;
+  // probabilities of the tile against the current maximum, as the P.V operand, and their sum
+  auto take = [&]() {
+    float p[16];
 #pragma unroll
-  for (int v = 1; v < 15; v += 2) mt = fmaxf(fmaxf(mt, s[v]), s[v + 1]);   // three-operand max
-  mt = fmaxf(mt, s[15]);
-  mt = fmaxf(mt, other_half(mt));
-  if (__any(mt > st.m + RESCALE_HEADROOM)) {   // wave-uniform: raise the maximum and rescale
+    for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(s[v] - st.m);
+    tsum = 0.0f;
+#pragma unroll
+    for (int mc = 0; mc < MC; ++mc) {
+      pf[mc] = VtFrag<T>::pfrag(p, mc);
+      if constexpr (sizeof(T) == 2) {
+        // sum of the probabilities as rounded for the product: packed bf16 dot products
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        const bf16x2_t one2 = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+        for (int e = 0; e < 8; e += 2)
+          tsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{pf[mc][e], pf[mc][e + 1]}, one2, tsum, false);
+      } else {
+        tsum += pf[mc];
+      }
+    }
+  };
+  take();
+  constexpr float BOUND = 256.0f;   // 2^RESCALE_HEADROOM
+  static_assert(RESCALE_HEADROOM == 8.0f, "bound is 2^headroom");
+  if (__any(!(tsum <= BOUND))) {    // wave-uniform; also catches an infinite sum
+    float mt = s[0];
+#pragma unroll
+    for (int v = 1; v < 15; v += 2) mt = fmaxf(fmaxf(mt, s[v]), s[v + 1]);   // three-operand max
+    mt = fmaxf(mt, s[15]);
+    mt = fmaxf(mt, other_half(mt));
     const float mn = fmaxf(st.m, mt);
     const float alpha = __builtin_amdgcn_exp2f(st.m - mn);
     st.m = mn;
     st.lsum *= alpha;
 #pragma unroll
     for (int v = 0; v < 16; ++v) st.o[v] *= alpha;
+    take();
   }
-  float p[16];
+  st.lsum += tsum;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(s[v] - st.m);
-  if constexpr (sizeof(T) == 4) {
-    float ps = 0.0f;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) ps += p[v];
-    st.lsum += ps;
-  }
-#pragma unroll
-  for (int mc = 0; mc < 32 / M::KSTEP; ++mc) {
-    typename M::frag vf = (DH == 32 || vt_row) ? VtFrag<T>::load(vt_row, mc, g) : M::zero();
-    const typename M::frag pf = VtFrag<T>::pfrag(p, mc);
-    st.o = M::mma(vf, pf, st.o);
-    if constexpr (sizeof(T) == 2) {
-      // row sum of the probabilities as rounded for the product: packed bf16 dot products
-      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-      const bf16x2_t one2 = {(bf16)1.0f, (bf16)1.0f};
-#pragma unroll
-      for (int e = 0; e < 8; e += 2)
-        st.lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{pf[e], pf[e + 1]}, one2, st.lsum, false);
-    }
+  for (int mc = 0; mc < MC; ++mc) {
+    frag vf = (DH == 32 || vt_row) ? VtFrag<T>::load(vt_row, mc, g) : M::zero();
+    st.o = M::mma(vf, pf[mc], st.o);
   }
 }
 
