@@ -5,7 +5,8 @@
 //     o = sum_{key u <= p} softmax_u(q . k_u / sqrt(d_head)) v_u
 // Keys span every row of the block input; queries are only the tail rows. In Stage II the keys
 // of a candidate's NS query j are the user's cached S rows followed by the candidate's own NS
-// rows 0..j, one softmax over both.
+// rows 0..j, one softmax over both. With ragged cached users every sequence's query positions
+// and prefix key count move by that user's own cached length.
 //
 // Work layout: a workgroup (ATTN_WAVES waves) handles one (sequence or user, head) and up to
 // 32 * ATTN_WAVES query rows; a wave owns 32 query rows. Scores are formed transposed,

@@ -3,19 +3,20 @@
 // 7.5.2: keys/values from every row of the block, queries only from the tail rows).
 //
 // Orientation as in the post-attention kernel: products are formed transposed, C^T = W Xh^T, so
-// each lane owns one token. A lane loads its token's input row, forms the norm statistics with
-// one cross-half shuffle, and keeps the normalised row as bf16 B fragments in registers. The
-// projection weights stream through LDS in chunks of 32 output features x d (direct global->LDS
-// loads, XOR-swizzled rows, double-buffered): with d_head = 32 a chunk is exactly one head, and
-// each accumulator tile is written into the head-major Q/K/V (or K/V cache) rows through a
-// per-wave LDS staging tile. Chunks of W_Q are skipped by workgroups holding no query row, and Q
-// stores are masked per token.
+// each lane owns one token of each of its wave's token groups (two groups of 32 for bf16 at
+// d <= 256: every weight fragment read from LDS then feeds two MFMAs). A lane loads its token's
+// input row, forms the norm statistics with one cross-half shuffle (or reads them from the
+// previous block's post kernel), and keeps the normalised row as bf16 B fragments in registers.
+// The projection weights stream through LDS in chunks of 32 output features x d (direct
+// global->LDS loads by all four waves, XOR-swizzled rows, double-buffered): with d_head = 32 a
+// chunk is exactly one head, and each accumulator tile is written into the head-major Q/K/V (or
+// K/V cache) rows through a per-wave LDS staging tile. Chunks of W_Q are skipped by workgroups
+// holding no query row.
 //
-// Roles: the four compute waves never wait for their own stores. A fifth, loader wave issues
-// every weight-chunk load and waits for its own vector-memory counter; the chunk handoff is a
-// plain s_barrier (no memory fence), so output stores stay in flight across chunks. (One
-// counter covers both loads and stores on this architecture, so a compute wave waiting for a
-// chunk would otherwise also wait for its previous chunk's stores.)
+// Waits: loads and stores share one vector-memory counter on this architecture. Every wave
+// issues exactly NS output stores per chunk (lanes with nothing to store write their piece to a
+// trash slot), so waiting for a chunk's weights is a fixed partial wait that leaves the previous
+// chunk's stores in flight; the chunk handoff is a plain s_barrier (no memory fence).
 
 #include "common.hpp"
 #include "launch.hpp"
