@@ -1,0 +1,81 @@
+"""Plain, slow fp64 CPU oracle of the tokenizers that build the first block's input X(0).
+
+TEST INFRASTRUCTURE. Only tests, the smoke check and the benchmark's CPU-baseline leg use this
+module; the HIP product path shares no code with it.
+
+Source: fun-rec-mdbook (English), chapter 7.5 "OneTrans", section 7.5.0 "Unified Tokenization"
+(the equations for the aligned sequences, S-tokens, NS-tokens and X(0)); the Chinese edition's
+section 2.1 names the Auto-Split tokenizer as the one that saves kernel launches.
+
+What is computed, per sample and independently:
+
+  S~_i      = [MLP_i(e_i1), ..., MLP_i(e_iL_i)]       one behaviour-specific MLP per sequence type,
+                                                      applied to every event of that sequence
+  S-tokens  = Merge(S~_1, ..., S~_n)                  timestamp-agnostic merge: the sequences in the
+                                                      given (intent) order, each followed by its own
+                                                      learnable [SEP] row; L_S = sum L_i + n
+  NS-tokens = Split(MLP(Concat(NS)), L_NS)            one MLP over the concatenated non-sequential
+                                                      features, its output cut into L_NS rows of d
+  X(0)      = [S-tokens; NS-tokens]
+
+Readings of points the section leaves open (each listed in the design notes):
+  * an MLP is two linear layers with biases and the exact erf GELU between them:
+    MLP(x) = W2 GELU(W1 x + b1) + b2, weights stored (out, in) like nn.Linear;
+  * the hidden width of each MLP is a free parameter of the model;
+  * the merge puts one [SEP] row after every sequence (so L_SEP = n), sequences in the order the
+    caller gives them (highest intent first);
+  * Split cuts the MLP output into consecutive pieces of width d: NS token j is output elements
+    [j d, (j + 1) d).
+"""
+
+from __future__ import annotations
+
+from typing import Sequence
+
+import numpy as np
+
+from .onetrans_oracle import gelu
+
+F64 = np.float64
+
+
+def mlp(x: np.ndarray, w1: np.ndarray, b1: np.ndarray, w2: np.ndarray, b2: np.ndarray) -> np.ndarray:
+    """Two-layer MLP on the last axis: W2 GELU(W1 x + b1) + b2 (weights (out, in))."""
+    x = np.asarray(x, F64)
+    h = gelu(x @ np.asarray(w1, F64).T + np.asarray(b1, F64))
+    return h @ np.asarray(w2, F64).T + np.asarray(b2, F64)
+
+
+def s_tokens(events: Sequence[np.ndarray], seq_mlps: Sequence[dict], sep: np.ndarray) -> np.ndarray:
+    """Aligned and merged behaviour sequences of one sample: [S~_1; SEP_1; S~_2; SEP_2; ...]."""
+    rows = []
+    for i, (e, p) in enumerate(zip(events, seq_mlps)):
+        rows.append(mlp(e, p["w1"], p["b1"], p["w2"], p["b2"]))
+        rows.append(np.asarray(sep[i], F64)[None, :])
+    return np.concatenate(rows, axis=0)
+
+
+def ns_tokens(ns_feat: np.ndarray, ns_mlp: dict, l_ns: int) -> np.ndarray:
+    """Auto-Split tokenizer of one sample: Split(MLP(Concat(NS)), l_ns) -> [l_ns][d]."""
+    y = mlp(ns_feat, ns_mlp["w1"], ns_mlp["b1"], ns_mlp["w2"], ns_mlp["b2"])
+    assert y.shape[-1] % l_ns == 0
+    return y.reshape(l_ns, y.shape[-1] // l_ns)
+
+
+def tokenize(events: Sequence[np.ndarray], ns_feat: np.ndarray, tw: dict, l_ns: int) -> np.ndarray:
+    """X(0) = [S-tokens; NS-tokens] of one sample.
+
+    events[i]: [L_i][D_i] raw event embeddings of behaviour type i; ns_feat: [F] concatenated
+    non-sequential features; tw: {"seq": [ {w1, b1, w2, b2} per type ], "sep": [n][d],
+    "ns": {w1, b1, w2, b2}}.
+    """
+    s = s_tokens(events, tw["seq"], tw["sep"])
+    if l_ns == 0:
+        return s
+    return np.concatenate([s, ns_tokens(ns_feat, tw["ns"], l_ns)], axis=0)
+
+
+def tokenize_batch(events: Sequence[np.ndarray], ns_feat: np.ndarray, tw: dict, l_ns: int) -> np.ndarray:
+    """Batched form: events[i] is [B][L_i][D_i], ns_feat [B][F]; returns X(0) [B][L_S + l_ns][d]."""
+    B = ns_feat.shape[0]
+    return np.stack([tokenize([e[b] for e in events], ns_feat[b], tw, l_ns) for b in range(B)])
