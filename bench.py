@@ -7,8 +7,9 @@ pyramid attention, output projection and mixed FFN. The metric is candidates sco
 (each batch row is one candidate carrying its own user sequence) plus the fraction of bf16 MFMA
 peak that the algorithmic FLOPs reach.
 
-Other workloads (--workload two_stage | append | append_ragged | onetrans_l) print their own line; they are
-parity cases of the same kernels and are measured for the design notes, not as the headline.
+Other workloads (--workload two_stage | append | append_ragged | onetrans_l | tokenize_s) print their
+own line; they are parity cases of the same kernels (tokenize_s: the tokenizers that build X(0)) and
+are measured for the design notes, not as the headline.
 
 Timing: W untimed warm-up steps, then K timed steps between a device synchronisation on both
 sides (one GPU, so no barrier is needed). Inputs and weights are resident in HBM before the
@@ -40,7 +41,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="onetrans_s",
-                   choices=["onetrans_s", "two_stage", "append", "append_ragged", "onetrans_l"])
+                   choices=["onetrans_s", "two_stage", "append", "append_ragged", "onetrans_l", "tokenize_s"])
     p.add_argument("--dtype", default=None, choices=[None, "bf16", "f32"])
     p.add_argument("--no-trace", action="store_true", help="no per-kernel events in the timed region")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline (0: skip)")
@@ -108,6 +109,100 @@ def dominant(classes, timing, steps, n_units, peak_tflops, workload):
     return entry
 
 
+def bench_tokenize(a):
+    """The tokenizers ahead of block 1 (behaviour MLPs, [SEP] merge, Auto-Split): samples/s, HBM-bound."""
+    from dataclasses import replace
+
+    import numpy as np
+    import torch
+
+    import synth
+    from unified_transformer_recommender_amd import binding as ob
+    from unified_transformer_recommender_amd import costmodel as cm
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = synth.tok_workload(a.workload, a.dtype)
+    m = w.model
+    store_bytes = 2 if m.dtype == "bf16" else 4
+    t_setup = time.time()
+    one = replace(m, n_blocks=1)
+    model = ob.Model.from_host(one, (w.l_s,), synth.make_weights(one), device=dev)
+    tw = synth.tokenizer_weights(w)
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev, dtype=model.torch_dtype)
+    tok = ob.Tokenizer(model, w.seq_lens, [{k: up(v) for k, v in p.items()} for p in tw["seq"]], up(tw["sep"]),
+                       {k: up(v) for k, v in tw["ns"].items()} if tw["ns"] is not None else None)
+    ev, ns = synth.tokenizer_batch(w)
+    evd, nsd = [up(e) for e in ev], up(ns)
+    x0 = torch.empty((w.batch, w.l_s + m.l_ns, m.d_model), dtype=model.torch_dtype, device=dev)
+    wsp = tok.workspace(w.batch)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ob.onetrans_tokenize(tok, evd, nsd, x0, wsp)
+
+    torch.cuda.synchronize()
+    t_setup = time.time() - t_setup
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    ob.timing_read()
+    ob.timing_enable(not a.no_trace)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(a.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    ob.timing_enable(False)
+    timing = ob.timing_read()
+    ms_step = e0.elapsed_time(e1) / a.steps
+    flops, act, wts = cm.tokenize_work(m.d_model, m.l_ns, w.seq_lens, w.seq_dims, w.seq_hidden, w.ns_dim,
+                                       w.ns_hidden, store_bytes)
+    lin_ms, lin_n = timing["lin"]
+    lin_bytes = (act * w.batch + wts) * a.steps           # every linear launch of the timed steps
+    roof = roofline_entry("lin", lin_bytes, lin_ms, lin_n, PEAK_HBM_GBS, "GB/s", "hbm") if lin_n else None
+    if roof is not None:
+        from unified_transformer_recommender_amd import profsummary
+        rec = profsummary.read_traffic(os.path.join(ROOT, "profiles", f"traffic_lin_{w.key}.txt"))
+        if rec is not None:
+            roof["traffic"] = float(rec["traffic_bytes_per_launch"])
+        roof["tflops"] = round(flops * w.batch * a.steps / (lin_ms * 1e-3) / 1e12, 2)
+    cpu = None
+    if a.cpu_seconds > 0:
+        import oracle as O
+        t0 = time.perf_counter()
+        done = 0
+        while done < 256 and (time.perf_counter() - t0 < a.cpu_seconds or done < 2):
+            e_b, n_b = synth.tokenizer_sample(w, done)
+            O.tokenize(e_b, n_b, tw, m.l_ns)
+            done += 1
+        cpu_s = time.perf_counter() - t0
+        cpu = {"value": round(done / cpu_s, 4), "unit": "samples/s", "cores": blas_threads(), "kind": "oracle",
+               "sample": f"{done} samples of the same workload, one at a time (input generation included)",
+               "seconds": round(cpu_s, 2)}
+    kernels = {k: {"ms_per_step": round(ms / a.steps, 4), "launches_per_step": n // a.steps}
+               for k, (ms, n) in timing.items() if n}
+    print(json.dumps({
+        "metric": f"samples tokenized/sec at 1 GPU ({w.key})",
+        "value": round(w.batch / (ms_step * 1e-3), 2),
+        "unit": "samples/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": m.dtype,
+        "data": "synthetic (seeded N(0,1) raw events and NS features, N(0,1/fan_in) MLP weights)",
+        "config": {"workload": w.description, "batch": w.batch, "seq_lens": list(w.seq_lens),
+                   "seq_dims": list(w.seq_dims), "seq_hidden": list(w.seq_hidden), "ns_dim": w.ns_dim,
+                   "ns_hidden": w.ns_hidden, "l_ns": m.l_ns, "d_model": m.d_model},
+        "tflops": round(flops * w.batch / (ms_step * 1e-3) / 1e12, 2),
+        "hbm_GB/s": round((act * w.batch + wts) / (ms_step * 1e-3) / 1e9, 1),
+        "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
+        "trace_in_timed_region": not a.no_trace, "setup_s": round(t_setup, 1),
+        "wall_ms_per_step": round(wall / a.steps, 4),
+    }))
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -116,6 +211,9 @@ def main():
         sys.exit(2)
     if a.copy_calibration:
         copy_calibration(a.copy_calibration)
+        return
+    if a.workload == "tokenize_s":
+        bench_tokenize(a)
         return
 
     import numpy as np

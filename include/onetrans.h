@@ -160,12 +160,63 @@ int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weig
                            onetrans_kv_cache *cache, const void *x_new, int n_users, int d_l,
                            void *out_new, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---- Tokenizers ahead of block 1 (section 7.5.0, "Unified Tokenization") -------------------
+ *
+ * S-tokens: n_seq behaviour sequences (types), given in merge order (highest intent first).
+ * Event e of type i is a raw embedding of width seq_dim[i]; the behaviour-specific MLP_i maps it
+ * to width d. The timestamp-agnostic merge concatenates the aligned sequences, each followed by
+ * its own learnable [SEP] row, so L_S = sum_i seq_len[i] + n_seq and sequence i starts at row
+ * off_i = sum_{j<i} (seq_len[j] + 1).
+ * NS-tokens (Auto-Split tokenizer): one MLP maps a sample's concatenated non-sequential features
+ * (width ns_dim) to l_ns * d values; NS token j is values [j d, (j + 1) d).
+ * Every MLP here is MLP(x) = W2 GELU(W1 x + b1) + b2 with the exact erf GELU, weights (out, in)
+ * row-major like the blocks' matrices.
+ */
+typedef struct {
+  int n_seq;              /* behaviour types, 1..7 */
+  const int *seq_len;     /* host [n_seq]: events per sample of type i (>= 0) */
+  const int *seq_dim;     /* host [n_seq]: raw event width, a multiple of 64 */
+  const int *seq_hidden;  /* host [n_seq]: hidden width of MLP_i, a multiple of 64 */
+  int ns_dim;             /* width of Concat(NS), a multiple of 64 (ignored when l_ns = 0) */
+  int ns_hidden;          /* hidden width of the Auto-Split MLP, a multiple of 64 (same) */
+} onetrans_tokenizer_config;
+
+typedef struct {          /* storage dtype */
+  const void *w1, *b1;    /* [hidden][in], [hidden] */
+  const void *w2, *b2;    /* [out][hidden], [out] */
+} onetrans_mlp_weights;
+
+/* Workspace bytes of onetrans_tokenize for `batch` samples (the hidden activations of every MLP,
+ * in the storage dtype). Returns 0 for an invalid configuration. */
+size_t onetrans_tokenize_workspace_bytes(const onetrans_config *cfg, const onetrans_tokenizer_config *tc,
+                                         int batch);
+
+/* Builds X(0) = [S-tokens; NS-tokens] for `batch` samples: the input of onetrans_forward.
+ *   seq_mlp  host [n_seq]: MLP_i, in = seq_dim[i], hidden = seq_hidden[i], out = d.
+ *   sep      [n_seq][d]: the [SEP] row written after sequence i.
+ *   ns_mlp   host pointer to the Auto-Split MLP (in = ns_dim, hidden = ns_hidden, out = l_ns * d);
+ *            NULL when l_ns = 0.
+ *   events   host [n_seq] of device pointers: events[i] is [batch][seq_len[i]][seq_dim[i]]
+ *            (may be NULL when seq_len[i] = 0).
+ *   ns_feat  [batch][ns_dim] (NULL when l_ns = 0).
+ *   x0       [batch][L_S + l_ns][d] storage dtype, written entirely.
+ * Hidden activations are rounded to the storage dtype; accumulation is fp32.
+ * Errors: INVALID_ARG (null pointer, bad dtype), SHAPE (n_seq, a negative length, L_S < 1),
+ * UNSUPPORTED (a width not a multiple of 64, n_seq > 7), WORKSPACE, ALIGNMENT, HIP. */
+int onetrans_tokenize(const onetrans_config *cfg, const onetrans_tokenizer_config *tc,
+                      const onetrans_mlp_weights *seq_mlp, const void *sep,
+                      const onetrans_mlp_weights *ns_mlp, const void *const *events,
+                      const void *ns_feat, int batch, void *x0, void *ws, size_t ws_bytes,
+                      hipStream_t stream);
+
 /* Kernel classes of the per-launch timing below. */
 typedef enum {
   ONETRANS_K_QKV = 0,        /* fused pre-norm 1 + mixed Q/K/V projection */
   ONETRANS_K_ATTN = 1,       /* causal / Stage II attention */
   ONETRANS_K_POST = 2,       /* fused W^O + residual + pre-norm 2 + mixed FFN + residual */
-  ONETRANS_K_COUNT = 3
+  ONETRANS_K_LIN = 3,        /* tokenizer linear layers (grouped MLP layers) */
+  ONETRANS_K_SEP = 4,        /* tokenizer [SEP] rows */
+  ONETRANS_K_COUNT = 5
 } onetrans_kernel_class;
 
 /* Per-launch device timing (tracing aid). While enabled, the library brackets every kernel launch

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert "onetrans_forward" in names and len(names) == 10
+    assert "onetrans_forward" in names and "onetrans_tokenize" in names and len(names) == 12
     lib = L.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -173,6 +173,72 @@ def test_ragged_user_validation_errors():
     # score: lengths within the cache
     assert lib.onetrans_score_candidates(ctypes.byref(flat), b, ctypes.byref(_ragged_cache((10, 201))), FAKE, 2, 4,
                                          FAKE, FAKE, 1 << 40, None) == L.ERR_SHAPE
+
+
+def _tok_cfg(lens=(15, 15), dims=(64, 128), hid=(128, 64), ns_dim=192, ns_hidden=128):
+    n = len(lens)
+    arrs = [(ctypes.c_int * n)(*v) for v in (lens, dims, hid)]
+    tc = L.TokenizerConfig(n, *arrs, ns_dim, ns_hidden)
+    tc._keep = arrs
+    return tc
+
+
+def _mlps(n, base=0x200000):
+    m = (L.MlpWeights * n)()
+    for i in range(n):
+        for j, f in enumerate(L.MLP_FIELDS):
+            setattr(m[i], f, base + (i * 4 + j) * 4096)
+    return m
+
+
+def test_tokenize_workspace_bytes():
+    lib = L.lib()
+    c = _cfg(d=64, H=4, dff=256, lns=4, N=1, sq=(32,), dtype=L.F32)
+    al = lambda n: (n + 255) // 256 * 256
+    B = 8
+    got = lib.onetrans_tokenize_workspace_bytes(ctypes.byref(c), ctypes.byref(_tok_cfg()), B)
+    assert got == al(B * 15 * 128 * 4) + al(B * 15 * 64 * 4) + al(B * 128 * 4)
+    assert lib.onetrans_tokenize_workspace_bytes(ctypes.byref(c), ctypes.byref(_tok_cfg(dims=(64, 96))), B) == 0
+    assert lib.onetrans_tokenize_workspace_bytes(ctypes.byref(c), None, B) == 0
+
+
+def test_tokenize_validation_errors():
+    """Every check returns before any HIP call."""
+    lib = L.lib()
+    c = _cfg(d=64, H=4, dff=256, lns=4, N=1, sq=(32,), dtype=L.BF16)
+    ev = (ctypes.c_void_p * 2)(FAKE, FAKE)
+
+    def call(tc=None, seq=None, sep=FAKE, ns=True, events=ev, ns_feat=FAKE, B=8, x0=FAKE, ws=FAKE, wsb=1 << 40,
+             cfg=c):
+        tc = tc or _tok_cfg()
+        seq = seq if seq is not None else _mlps(tc.n_seq)
+        nsm = _mlps(1, 0x400000) if ns else None
+        return lib.onetrans_tokenize(ctypes.byref(cfg), ctypes.byref(tc), seq, sep, nsm, events, ns_feat, B, x0, ws,
+                                     wsb, None)
+
+    assert call(sep=None) == L.ERR_INVALID_ARG
+    assert call(x0=None) == L.ERR_INVALID_ARG
+    assert call(ns=False) == L.ERR_INVALID_ARG                       # l_ns > 0 needs the Auto-Split MLP
+    assert call(ns_feat=None) == L.ERR_INVALID_ARG
+    assert call(events=(ctypes.c_void_p * 2)(FAKE, None)) == L.ERR_INVALID_ARG
+    assert call(x0=FAKE + 8) == L.ERR_ALIGNMENT
+    assert call(events=(ctypes.c_void_p * 2)(FAKE, FAKE + 4)) == L.ERR_ALIGNMENT
+    bad = _mlps(2)
+    bad[1].b2 = FAKE + 2
+    assert call(seq=bad) == L.ERR_ALIGNMENT
+    bad[1].b2 = None
+    assert call(seq=bad) == L.ERR_INVALID_ARG
+    assert call(B=0) == L.ERR_SHAPE
+    assert call(tc=_tok_cfg(lens=(15, -1))) == L.ERR_SHAPE
+    assert call(tc=_tok_cfg(dims=(64, 100))) == L.ERR_UNSUPPORTED    # widths are multiples of 64
+    assert call(tc=_tok_cfg(hid=(32, 64))) == L.ERR_UNSUPPORTED
+    assert call(tc=_tok_cfg(ns_hidden=130)) == L.ERR_UNSUPPORTED
+    assert call(tc=_tok_cfg(lens=(1,) * 8, dims=(64,) * 8, hid=(64,) * 8),
+                events=(ctypes.c_void_p * 8)(*[FAKE] * 8)) == L.ERR_UNSUPPORTED   # at most 7 types
+    assert call(wsb=64) == L.ERR_WORKSPACE
+    assert call(cfg=_cfg(d=64, H=4, dff=256, lns=4, N=1, sq=(32,), dtype=5)) == L.ERR_INVALID_ARG
+    # an empty sequence needs no event buffer
+    assert call(tc=_tok_cfg(lens=(15, 0)), events=(ctypes.c_void_p * 2)(FAKE, None), wsb=64) == L.ERR_WORKSPACE
 
 
 def test_status_strings():

@@ -1,4 +1,4 @@
-"""Python binding of the C ABI: the same four entry points, torch tensors in and out.
+"""Python binding of the C ABI: the same entry points, torch tensors in and out.
 
 Only argument marshalling happens here. torch provides device memory and the current stream;
 every step of the computation runs in the HIP library (libonetrans.so). If the library is
@@ -193,6 +193,80 @@ def onetrans_append_events(model: Model, cache: KVCache, x_new: torch.Tensor,
                                         _stream(x_new.device, stream))
     L.check(st, "onetrans_append_events")
     return out_new
+
+
+class Tokenizer:
+    """Device weights of the tokenizers ahead of block 1 for one model (see onetrans_tokenize).
+
+    ``seq_mlps``: one mapping per behaviour type (merge order) with w1 [hidden][D_i], b1 [hidden],
+    w2 [d][hidden], b2 [d]; ``sep`` [n_seq][d]; ``ns_mlp``: the Auto-Split MLP (w1 [hidden][ns_dim],
+    b1, w2 [l_ns * d][hidden], b2) or None when l_ns = 0. All contiguous, storage dtype, on device.
+    """
+
+    def __init__(self, model: Model, seq_lens: Sequence[int], seq_mlps, sep: torch.Tensor, ns_mlp=None):
+        self.model = model
+        self.seq_lens = tuple(int(v) for v in seq_lens)
+        n = len(self.seq_lens)
+        if len(seq_mlps) != n:
+            raise ValueError("one MLP per behaviour type")
+        self._tensors = [sep]
+        self._mlps = (L.MlpWeights * n)()
+        dims, hidden = [], []
+        for i, p in enumerate(seq_mlps):
+            self._fill(self._mlps[i], p)
+            hidden.append(int(p["w1"].shape[0]))
+            dims.append(int(p["w1"].shape[1]))
+        self._ns = None
+        ns_dim = ns_hidden = 0
+        if ns_mlp is not None:
+            self._ns = L.MlpWeights()
+            self._fill(self._ns, ns_mlp)
+            ns_hidden, ns_dim = int(ns_mlp["w1"].shape[0]), int(ns_mlp["w1"].shape[1])
+        self.seq_dims, self.seq_hidden, self.ns_dim = tuple(dims), tuple(hidden), ns_dim
+        self._len = (ctypes.c_int * n)(*self.seq_lens)
+        self._dim = (ctypes.c_int * n)(*dims)
+        self._hid = (ctypes.c_int * n)(*hidden)
+        self.tc = L.TokenizerConfig(n, self._len, self._dim, self._hid, ns_dim, ns_hidden)
+        self.sep = sep
+        self.l_s = sum(self.seq_lens) + n
+
+    def _fill(self, c, p):
+        for f in L.MLP_FIELDS:
+            t = p[f]
+            if not (t.is_contiguous() and t.dtype == self.model.torch_dtype):
+                raise ValueError(f"tokenizer {f}: need a contiguous {self.model.torch_dtype} tensor")
+            self._tensors.append(t)
+            setattr(c, f, t.data_ptr())
+
+    def workspace(self, batch: int) -> torch.Tensor:
+        n = int(L.lib().onetrans_tokenize_workspace_bytes(ctypes.byref(self.model.cfg), ctypes.byref(self.tc), batch))
+        if n == 0:
+            raise ValueError("invalid tokenizer configuration")
+        return torch.empty(n, dtype=torch.uint8, device=self.model.device)
+
+
+def onetrans_tokenize(tok: Tokenizer, events: Sequence[torch.Tensor], ns_feat: Optional[torch.Tensor],
+                      x0: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """events[i] [B][L_i][D_i], ns_feat [B][ns_dim] -> X(0) [B][L_S + l_ns][d] (storage dtype)."""
+    m = tok.model
+    B = int(ns_feat.shape[0]) if ns_feat is not None else int(events[0].shape[0])
+    for i, e in enumerate(events):
+        if e.dtype != m.torch_dtype or not e.is_contiguous() or tuple(e.shape) != (B, tok.seq_lens[i], tok.seq_dims[i]):
+            raise ValueError(f"events[{i}]: need a contiguous {m.torch_dtype} tensor [B][L_i][D_i]")
+    if ns_feat is not None and (ns_feat.dtype != m.torch_dtype or not ns_feat.is_contiguous()):
+        raise ValueError(f"ns_feat: need a contiguous {m.torch_dtype} tensor")
+    dev = m.device
+    if x0 is None:
+        x0 = torch.empty((B, tok.l_s + m.l_ns, m.d_model), dtype=m.torch_dtype, device=dev)
+    if ws is None:
+        ws = tok.workspace(B)
+    ev = (ctypes.c_void_p * len(events))(*[e.data_ptr() for e in events])
+    st = L.lib().onetrans_tokenize(ctypes.byref(m.cfg), ctypes.byref(tok.tc), tok._mlps, tok.sep.data_ptr(),
+                                   ctypes.byref(tok._ns) if tok._ns is not None else None, ev, _ptr(ns_feat), B,
+                                   x0.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev, stream))
+    L.check(st, "onetrans_tokenize")
+    return x0
 
 
 def timing_enable(on: bool = True) -> None:

@@ -267,4 +267,33 @@ struct AttnArgs {
                            // start seq_shift[z] rows later (ragged cached lengths)
 };
 
+// ---------------------------------------------------------------------------------------------
+// Grouped linear layer of the tokenizers: per group, y = act(x W^T + b) over m rows.
+// Input row r at x + r * x_ld elements; output row r at
+//   y + (r / y_rps) * y_ss + (r % y_rps) * y_rs elements
+// (y_rps rows per sample, so a group can write its rows straight into X(0)).
+// Workgroups [tile0, tile0 + m_tiles * n / 64) belong to the group, output tile fastest.
+// ---------------------------------------------------------------------------------------------
+constexpr int LIN_MAX_GROUPS = 8;
+struct LinGroup {
+  const void *x; long long x_ld;
+  const void *w, *b;       // W [n][k] (out, in), b [n]
+  void *y; long long y_ss, y_rs; int y_rps;
+  int m, n, k;
+  int gelu;                // exact erf GELU after the bias
+  int tile0;
+};
+struct LinArgs {
+  LinGroup g[LIN_MAX_GROUPS];
+  int n_groups;
+};
+
+// [SEP] rows: row j of sep [n_sep][d] to row sep_row[j] of each sample (sample_stride elements).
+struct SepArgs {
+  const void *sep;
+  void *x0; long long sample_stride;
+  int d, n_sep, batch;
+  int sep_row[LIN_MAX_GROUPS];
+};
+
 }  // namespace ot

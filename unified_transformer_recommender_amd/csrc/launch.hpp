@@ -17,6 +17,12 @@ hipError_t launch_attn(int dtype, int d_head, int stage2, const AttnArgs &a, hip
 hipError_t launch_post(int dtype, int resid_f32, const PostArgs &a, int grid, hipStream_t s);
 int post_tokens_per_tile(int dtype, int d_model);
 
+// Tokenizer kernels: grouped linear layer (rows / output features per workgroup) and [SEP] copy.
+hipError_t launch_lin(int dtype, const LinArgs &a, int grid, hipStream_t s);
+int lin_rows_per_tile();
+int lin_features_per_tile();
+hipError_t launch_sep(int dtype, const SepArgs &a, hipStream_t s);
+
 constexpr int ATTN_WAVES = 8;                    // waves per attention workgroup
 constexpr int ATTN_QBLOCK = 32 * ATTN_WAVES;     // forward-mode queries per attention workgroup
 constexpr int POST_MAX_DFF = 2048; // widest FFN the fused post-attention kernel stages

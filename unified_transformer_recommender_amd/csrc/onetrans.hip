@@ -380,6 +380,56 @@ inline HeadView cache_view(const Dims &D, const onetrans_kv_cache *c, void *base
   return HeadView{(char *)base + (size_t)n * D.H * per_head * D.esz, (long long)D.N * D.H * per_head, per_head, 0};
 }
 
+// ---- tokenizers (section 7.5.0) ----------------------------------------------------------------
+// Workspace: the hidden activations of every MLP, [batch * rows][hidden] each, storage dtype.
+struct TokPlan {
+  int l_s, T;
+  size_t hid[LIN_MAX_GROUPS];
+  size_t total;
+};
+
+int check_tok(const onetrans_config *cfg, const onetrans_tokenizer_config *tc, int batch, Dims &D, TokPlan &P) {
+  int rc;
+  if ((rc = check_cfg(cfg, D))) return rc;
+  if (!tc || !tc->seq_len || !tc->seq_dim || !tc->seq_hidden) return ONETRANS_ERR_INVALID_ARG;
+  if (batch < 1 || tc->n_seq < 1) return ONETRANS_ERR_SHAPE;
+  if (tc->n_seq > LIN_MAX_GROUPS - 1) return ONETRANS_ERR_UNSUPPORTED;
+  auto width_ok = [](int w) { return w >= 64 && w % 64 == 0; };
+  long long l_s = 0, tiles1 = 0, tiles2 = 0;
+  const long long rt = lin_rows_per_tile(), nt = lin_features_per_tile();
+  size_t off = 0;
+  for (int i = 0; i < tc->n_seq; ++i) {
+    const int L = tc->seq_len[i];
+    if (L < 0) return ONETRANS_ERR_SHAPE;
+    if (!width_ok(tc->seq_dim[i]) || !width_ok(tc->seq_hidden[i])) return ONETRANS_ERR_UNSUPPORTED;
+    const long long m = (long long)batch * L;
+    if (m > (1LL << 30)) return ONETRANS_ERR_SHAPE;
+    l_s += L + 1;
+    tiles1 += (m + rt - 1) / rt * (tc->seq_hidden[i] / nt);
+    tiles2 += (m + rt - 1) / rt * (D.d / nt);
+    P.hid[i] = off;
+    off += al((size_t)m * tc->seq_hidden[i] * D.esz);
+  }
+  if (D.lns > 0) {
+    if (!width_ok(tc->ns_dim) || !width_ok(tc->ns_hidden)) return ONETRANS_ERR_UNSUPPORTED;
+    tiles1 += (batch + rt - 1) / rt * (tc->ns_hidden / nt);
+    tiles2 += (batch + rt - 1) / rt * ((long long)D.lns * D.d / nt);
+    P.hid[tc->n_seq] = off;
+    off += al((size_t)batch * tc->ns_hidden * D.esz);
+  }
+  if (l_s + D.lns > (1 << 24) || tiles1 >= (1LL << 31) || tiles2 >= (1LL << 31)) return ONETRANS_ERR_SHAPE;
+  P.l_s = (int)l_s;
+  P.T = P.l_s + D.lns;
+  P.total = off > 0 ? off : 256;
+  return ONETRANS_OK;
+}
+
+int check_mlp(const onetrans_mlp_weights *m) {
+  if (!m || !m->w1 || !m->b1 || !m->w2 || !m->b2) return ONETRANS_ERR_INVALID_ARG;
+  if (misaligned(m->w1) || misaligned(m->b1) || misaligned(m->w2) || misaligned(m->b2)) return ONETRANS_ERR_ALIGNMENT;
+  return ONETRANS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -687,6 +737,83 @@ int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weig
   } else {
     for (int n = 0; n < D.N; ++n) cache->layer_len[n] = l_old + d_l;
   }
+  return ONETRANS_OK;
+}
+
+size_t onetrans_tokenize_workspace_bytes(const onetrans_config *cfg, const onetrans_tokenizer_config *tc,
+                                         int batch) {
+  Dims D;
+  TokPlan P;
+  if (check_tok(cfg, tc, batch, D, P)) return 0;
+  return P.total;
+}
+
+int onetrans_tokenize(const onetrans_config *cfg, const onetrans_tokenizer_config *tc,
+                      const onetrans_mlp_weights *seq_mlp, const void *sep, const onetrans_mlp_weights *ns_mlp,
+                      const void *const *events, const void *ns_feat, int batch, void *x0, void *ws,
+                      size_t ws_bytes, hipStream_t stream) {
+  Dims D;
+  TokPlan P;
+  int rc;
+  if ((rc = check_tok(cfg, tc, batch, D, P))) return rc;
+  if (!seq_mlp || !sep || !events || !x0 || !ws) return ONETRANS_ERR_INVALID_ARG;
+  if (misaligned(sep) || misaligned(x0) || misaligned(ws)) return ONETRANS_ERR_ALIGNMENT;
+  const int n_seq = tc->n_seq;
+  for (int i = 0; i < n_seq; ++i) {
+    if ((rc = check_mlp(&seq_mlp[i]))) return rc;
+    if (tc->seq_len[i] > 0 && !events[i]) return ONETRANS_ERR_INVALID_ARG;
+    if (misaligned(events[i])) return ONETRANS_ERR_ALIGNMENT;
+  }
+  if (D.lns > 0) {
+    if ((rc = check_mlp(ns_mlp))) return rc;
+    if (!ns_feat) return ONETRANS_ERR_INVALID_ARG;
+    if (misaligned(ns_feat)) return ONETRANS_ERR_ALIGNMENT;
+  }
+  if (ws_bytes < P.total) return ONETRANS_ERR_WORKSPACE;
+
+  const int rt = lin_rows_per_tile(), nt = lin_features_per_tile();
+  const long long d = D.d, sample = (long long)P.T * d;
+  char *w = (char *)ws;
+  char *x = (char *)x0;
+  LinArgs l1{}, l2{};
+  int tiles1 = 0, tiles2 = 0;
+  auto add = [&](LinArgs &A, int &tiles, LinGroup g) {
+    if (g.m == 0) return;
+    g.tile0 = tiles;
+    A.g[A.n_groups++] = g;
+    tiles += (g.m + rt - 1) / rt * (g.n / nt);
+  };
+  SepArgs sa{};
+  sa.sep = sep;
+  sa.x0 = x0;
+  sa.sample_stride = sample;
+  sa.d = D.d;
+  sa.n_sep = n_seq;
+  sa.batch = batch;
+  int off = 0;   // first row of sequence i inside the S-tokens
+  for (int i = 0; i < n_seq; ++i) {
+    const int L = tc->seq_len[i], h = tc->seq_hidden[i], m = batch * L;
+    const onetrans_mlp_weights &p = seq_mlp[i];
+    // MLP_i, layer 1: events -> hidden (GELU); layer 2: hidden -> rows off..off+L-1 of each sample
+    add(l1, tiles1, LinGroup{events[i], tc->seq_dim[i], p.w1, p.b1, w + P.hid[i], h, 0, 1, m, h, tc->seq_dim[i], 1, 0});
+    add(l2, tiles2, LinGroup{w + P.hid[i], h, p.w2, p.b2, x + (size_t)off * d * D.esz, sample, d, L, m, D.d, h, 0, 0});
+    sa.sep_row[i] = off + L;
+    off += L + 1;
+  }
+  if (D.lns > 0) {
+    // Auto-Split: one row per sample, its l_ns * d outputs are the sample's NS rows in order
+    const int h = tc->ns_hidden;
+    add(l1, tiles1, LinGroup{ns_feat, tc->ns_dim, ns_mlp->w1, ns_mlp->b1, w + P.hid[n_seq], h, 0, 1, batch, h,
+                             tc->ns_dim, 1, 0});
+    add(l2, tiles2, LinGroup{w + P.hid[n_seq], h, ns_mlp->w2, ns_mlp->b2, x + (size_t)P.l_s * d * D.esz, sample, 0, 1,
+                             batch, D.lns * D.d, h, 0, 0});
+  }
+  if (tiles1 > 0 && timed(ONETRANS_K_LIN, stream, [&] { return launch_lin(D.dt, l1, tiles1, stream); }) != hipSuccess)
+    return ONETRANS_ERR_HIP;
+  if (tiles2 > 0 && timed(ONETRANS_K_LIN, stream, [&] { return launch_lin(D.dt, l2, tiles2, stream); }) != hipSuccess)
+    return ONETRANS_ERR_HIP;
+  if (timed(ONETRANS_K_SEP, stream, [&] { return launch_sep(D.dt, sa, stream); }) != hipSuccess)
+    return ONETRANS_ERR_HIP;
   return ONETRANS_OK;
 }
 

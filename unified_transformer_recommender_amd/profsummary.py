@@ -29,6 +29,7 @@ KERNELS = {
     "qkv": ("qkv_kernel", "qkv.hip"),
     "attn": ("attn_kernel", "attn.hip"),
     "post": ("post_kernel", "post.hip"),
+    "lin": ("lin_kernel", "tok.hip"),
 }
 COPY_KERNEL = "neg"
 
