@@ -1,4 +1,4 @@
-"""The bf16 post-attention kernel evaluates GELU with a fitted sigmoid form instead of the erf
+"""The bf16 kernels (post-attention FFN, tokenizer MLPs) evaluate GELU with a fitted sigmoid form instead of the erf
 form. This reads the fit's coefficients from the kernel source, evaluates the same expression in
 fp32 on the CPU, and checks it against the erf form over the range the hidden activations can
 take and far beyond (host-only: no GPU, no oracle)."""
@@ -10,7 +10,7 @@ import numpy as np
 from scipy.special import erf
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-POST = os.path.join(ROOT, "unified_transformer_recommender_amd", "csrc", "post.hip")
+POST = os.path.join(ROOT, "unified_transformer_recommender_amd", "csrc", "common.hpp")
 
 # the bf16 activation this feeds is rounded to 8 significant bits right after; the fit's error
 # stays below half a bf16 step of every activation of magnitude >= 0.14

@@ -124,6 +124,41 @@ __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<
 __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
 
 // ---------------------------------------------------------------------------------------------
+// GELU, the erf form 0.5 x (1 + erf(x / sqrt 2)).
+// gelu_as (fp32 paths): erf by Abramowitz & Stegun 7.1.26 (|error| <= 1.5e-7): with
+// z = |x| / sqrt 2, t = 1 / (1 + p z),
+//   GELU(x) = max(x, 0) - |x| * 0.5 t (a1 + t(a2 + t(a3 + t(a4 + t a5)))) * exp(-x^2 / 2).
+// gelu_fit (bf16 paths, whose activations are rounded to bf16 right after): a fitted sigmoid form
+// with half the instructions (|error| <= 2.71e-4).
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ float gelu_as(float x) {
+  // Abramowitz & Stegun 7.1.26 coefficients, halved so that q = 0.5 t P(t)
+  constexpr float p = 0.3275911f * 0.70710678118654752f;   // p / sqrt(2): t = 1 / (1 + p |x| / sqrt 2)
+  constexpr float a1 = 0.5f * 0.254829592f, a2 = 0.5f * -0.284496736f, a3 = 0.5f * 1.421413741f,
+                  a4 = 0.5f * -1.453152027f, a5 = 0.5f * 1.061405429f;
+  constexpr float neg_half_log2e = -0.72134752044448170f;   // -0.5 * log2(e)
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(p, ax, 1.0f));
+  const float q = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, a5, a4), a3), a2), a1);
+  const float e = __builtin_amdgcn_exp2f(x * x * neg_half_log2e);
+  return fmaf(-ax * q, e, fmaxf(x, 0.0f));
+}
+
+// GELU for the bf16 path, whose hidden activations are rounded to bf16 (relative step 2^-8)
+// before the down-projection: x sigma(z) with z = x (A1 + A3 x^2), the two coefficients a minimax
+// fit to the erf form on [-12, 12] (max |error| 2.71e-4 there; z is monotone in x, so the limits
+// x -> +-inf give x and 0). sigma(z) = 1 / (1 + 2^(-z log2 e)): 5 VALU and 2 transcendental
+// instructions per value.
+constexpr float GELU_FIT_A1 = 1.6003141571088118f;
+constexpr float GELU_FIT_A3 = 0.06940178685506644f;
+__device__ __forceinline__ float gelu_fit(float x) {
+  constexpr float L = -1.4426950408889634f;   // -log2(e)
+  const float x2 = x * x;
+  const float z = x * fmaf(x2, GELU_FIT_A3 * L, GELU_FIT_A1 * L);
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z));
+}
+
+// ---------------------------------------------------------------------------------------------
 // Coalesced store of a 32 x 32 accumulator tile whose 32 columns are tokens (lane l % 32) and
 // whose 32 rows are consecutive output features. In registers a lane holds 16 features of its
 // own token spread over the row, so storing straight from registers scatters 4-16 byte pieces

@@ -7,13 +7,16 @@
 // once per layer for every MLP together:
 //   launch 1: H_i = GELU(E_i W1_i^T + b1_i) for every sequence type, and the same for NS;
 //   launch 2: rows of X(0) = H_i W2_i^T + b2_i, written straight into their merged positions;
-// plus a copy of the [SEP] rows into theirs.
+// plus a copy of the [SEP] rows into theirs. GELU: the shared erf-form evaluations (bf16: the fitted
+// sigmoid form, whose error is below the bf16 rounding of the hidden activation it produces).
 //
 // Work unit: one workgroup of LIN_NW waves computes a tile of LIN_NW * 32 rows by LIN_NT output
 // features. Orientation as in the block kernels (C^T = W X^T): an accumulator column is a row
 // of the input (lane % 32), its rows are output features. k is consumed in chunks of 128 bytes
 // per row; the weight rows of the tile and the wave's own input rows of a chunk are brought into
-// LDS by direct global->LDS loads, LIN_NB chunks in flight.
+// LDS by direct global->LDS loads into LIN_NB chunk buffers. Two buffers (the next chunk loads
+// while the current one is multiplied) measured faster than three: with K of 64..256 a tile has
+// few chunks, and the smaller LDS footprint lets three workgroups share a CU.
 //
 // LDS layout of a chunk: 16-byte pieces p = 0..7 of row r sit at slot r * 8 + (p ^ (r & 7)), so a
 // fragment read (one piece of 32 consecutive rows) touches every bank once.
@@ -21,8 +24,6 @@
 // k order inside a chunk: lane group g (lane / 32) owns the chunk's k elements
 // [g * KC / 2, (g + 1) * KC / 2), in MFMA steps of KPL. Both operands use that same order, so the
 // contraction is unchanged and every fragment is one 16-byte piece.
-
-#include <math.h>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -33,16 +34,23 @@ namespace {
 constexpr int LIN_NW = 4;      // waves per workgroup, 32 input rows each
 constexpr int LIN_NT = 64;     // output features per workgroup
 constexpr int LIN_CB = 128;    // bytes of k per row and chunk
-constexpr int LIN_NB = 3;      // chunks in flight
+constexpr int LIN_NB = 2;      // chunk buffers (2: 48 KB of LDS, three workgroups per CU)
 constexpr int LIN_W_BYTES = LIN_NT * LIN_CB;             // weight rows of one chunk
 constexpr int LIN_X_BYTES = LIN_NW * 32 * LIN_CB;        // input rows of one chunk
 constexpr int LIN_STAGE_BYTES = LIN_W_BYTES + LIN_X_BYTES;
-static_assert(LIN_NB == 3, "the wait counts below assume one chunk in flight behind the current one");
+static_assert(LIN_NB == 2 || LIN_NB == 3, "chunks in flight behind the current one: LIN_NB - 2");
 static_assert(LIN_NT == 64 && LIN_NW == 4, "direct-to-LDS load split: 2 weight and 4 input loads per wave");
 
 __device__ __forceinline__ uint32_t slot_byte(int r, int p) { return (uint32_t)(r * 8 + (p ^ (r & 7))) * 16u; }
 
-__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+// Workgroup b of a launch of n runs on XCD b % 8. Tile t = (b % 8) * (n / 8) + b / 8 (for the first
+// 8 * (n / 8) workgroups) gives each XCD a contiguous run of tiles, so the output tiles of one row
+// tile, which read the same input rows, share that XCD's L2 instead of fetching the rows from HBM
+// once per XCD.
+__device__ __forceinline__ int xcd_tile(int b, int n) {
+  const int per = n / 8;
+  return b < 8 * per ? (b % 8) * per + b / 8 : b;
+}
 
 template <typename T>
 __global__ __launch_bounds__(LIN_NW * 64, 2) void lin_kernel(const LinArgs a) {
@@ -56,13 +64,14 @@ __global__ __launch_bounds__(LIN_NW * 64, 2) void lin_kernel(const LinArgs a) {
   static_assert(LIN_NW * TS::SIZE * ESZ <= LIN_NB * LIN_STAGE_BYTES, "staging fits in the ring");
   __shared__ __attribute__((aligned(16))) char ring[LIN_NB * LIN_STAGE_BYTES];
 
-  // group of this workgroup (uniform)
+  // tile and group of this workgroup (uniform)
+  const int tile = xcd_tile((int)blockIdx.x, (int)gridDim.x);
   int gi = 0;
 #pragma unroll
   for (int i = 1; i < LIN_MAX_GROUPS; ++i)
-    if (i < a.n_groups && (int)blockIdx.x >= a.g[i].tile0) gi = i;
+    if (i < a.n_groups && tile >= a.g[i].tile0) gi = i;
   const LinGroup &G = a.g[gi];
-  const int local = (int)blockIdx.x - G.tile0;
+  const int local = tile - G.tile0;
   const int n_tiles = G.n / LIN_NT;
   const int n0 = (local % n_tiles) * LIN_NT;
   const int mw0 = (local / n_tiles) * (LIN_NW * 32);   // first row of the workgroup
@@ -133,7 +142,7 @@ __global__ __launch_bounds__(LIN_NW * 64, 2) void lin_kernel(const LinArgs a) {
 
   for (int c = 0; c < n_chunks; ++c) {
     // chunk c has landed once at most the loads of the chunks issued after it are outstanding
-    if (c + 1 < n_chunks) wait_vm<PER_CHUNK * (LIN_NB - 2)>();
+    if (LIN_NB == 3 && c + 1 < n_chunks) wait_vm<PER_CHUNK * (LIN_NB - 2)>();
     else wait_vm<0>();
     wait_lgkm0();
     bare_barrier();
@@ -155,6 +164,7 @@ __global__ __launch_bounds__(LIN_NW * 64, 2) void lin_kernel(const LinArgs a) {
         if constexpr (ESZ == 2) {
           acc[t] = MM::mma(__builtin_bit_cast(bf16x8, wa[q][t]), __builtin_bit_cast(bf16x8, xb[q]), acc[t]);
         } else {
+          // reinterpret the whole piece, then take its lanes (4 k-steps of the fp32 MFMA)
           const f32x4 af = __builtin_bit_cast(f32x4, wa[q][t]), bf = __builtin_bit_cast(f32x4, xb[q]);
 #pragma unroll
           for (int e = 0; e < SPP; ++e) acc[t] = MM::mma(af[e], bf[e], acc[t]);
@@ -173,7 +183,7 @@ __global__ __launch_bounds__(LIN_NW * 64, 2) void lin_kernel(const LinArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       float y = v[e] + bv[t][e];
-      if (G.gelu) y = gelu_erf(y);
+      if (G.gelu) y = ESZ == 2 ? gelu_fit(y) : gelu_as(y);
       v[e] = y;
     }
     TS::put(stg, v, lc, g);
