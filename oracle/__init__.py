@@ -8,7 +8,7 @@ Python binding) never imports, calls or links anything here.
 from .onetrans_oracle import (rms_norm, layer_norm, norm, gelu, weight_group, block_forward,
                               forward, forward_batch, prefill_user, score_candidate,
                               append_events, BlockTrace)
-from .tokenizer_oracle import mlp, s_tokens, ns_tokens, tokenize, tokenize_batch
+from .tokenizer_oracle import mlp, s_tokens, s_tokens_by_time, ns_tokens, tokenize, tokenize_batch
 
-__all__ = ["mlp", "s_tokens", "ns_tokens", "tokenize", "tokenize_batch","rms_norm", "layer_norm", "norm", "gelu", "weight_group", "block_forward", "forward",
+__all__ = ["mlp", "s_tokens", "s_tokens_by_time", "ns_tokens", "tokenize", "tokenize_batch","rms_norm", "layer_norm", "norm", "gelu", "weight_group", "block_forward", "forward",
            "forward_batch", "prefill_user", "score_candidate", "append_events", "BlockTrace"]

@@ -14,6 +14,9 @@ What is computed, per sample and independently:
   S-tokens  = Merge(S~_1, ..., S~_n)                  timestamp-agnostic merge: the sequences in the
                                                       given (intent) order, each followed by its own
                                                       learnable [SEP] row; L_S = sum L_i + n
+                                                      timestamp-aware merge: every event row plus its
+                                                      behaviour type's embedding, all events in time
+                                                      order; L_S = sum L_i
   NS-tokens = Split(MLP(Concat(NS)), L_NS)            one MLP over the concatenated non-sequential
                                                       features, its output cut into L_NS rows of d
   X(0)      = [S-tokens; NS-tokens]
@@ -25,7 +28,11 @@ Readings of points the section leaves open (each listed in the design notes):
   * the merge puts one [SEP] row after every sequence (so L_SEP = n), sequences in the order the
     caller gives them (highest intent first);
   * Split cuts the MLP output into consecutive pieces of width d: NS token j is output elements
-    [j d, (j + 1) d).
+    [j d, (j + 1) d);
+  * timestamp-aware merge: the behaviour-type identifier is a learnable vector per type added to
+    each of its event rows; events go in ascending time (oldest first, so the newest events are
+    the tail the pyramid keeps); equal times keep the intent order of the types, then the order
+    within the sequence; no [SEP] rows.
 """
 
 from __future__ import annotations
@@ -55,6 +62,18 @@ def s_tokens(events: Sequence[np.ndarray], seq_mlps: Sequence[dict], sep: np.nda
     return np.concatenate(rows, axis=0)
 
 
+def s_tokens_by_time(events: Sequence[np.ndarray], times: Sequence[np.ndarray], seq_mlps: Sequence[dict],
+                     type_emb: np.ndarray) -> np.ndarray:
+    """Timestamp-aware merge of one sample: aligned event rows plus their type's embedding, sorted by
+    (time, type index, position in the sequence)."""
+    rows, keys = [], []
+    for i, (e, t, p) in enumerate(zip(events, times, seq_mlps)):
+        rows.append(mlp(e, p["w1"], p["b1"], p["w2"], p["b2"]) + np.asarray(type_emb[i], F64))
+        keys += [(int(t[l]), i, l) for l in range(len(t))]
+    order = sorted(range(len(keys)), key=lambda r: keys[r])
+    return np.concatenate(rows, axis=0)[order]
+
+
 def ns_tokens(ns_feat: np.ndarray, ns_mlp: dict, l_ns: int) -> np.ndarray:
     """Auto-Split tokenizer of one sample: Split(MLP(Concat(NS)), l_ns) -> [l_ns][d]."""
     y = mlp(ns_feat, ns_mlp["w1"], ns_mlp["b1"], ns_mlp["w2"], ns_mlp["b2"])
@@ -62,20 +81,26 @@ def ns_tokens(ns_feat: np.ndarray, ns_mlp: dict, l_ns: int) -> np.ndarray:
     return y.reshape(l_ns, y.shape[-1] // l_ns)
 
 
-def tokenize(events: Sequence[np.ndarray], ns_feat: np.ndarray, tw: dict, l_ns: int) -> np.ndarray:
+def tokenize(events: Sequence[np.ndarray], ns_feat: np.ndarray, tw: dict, l_ns: int, times=None) -> np.ndarray:
     """X(0) = [S-tokens; NS-tokens] of one sample.
 
     events[i]: [L_i][D_i] raw event embeddings of behaviour type i; ns_feat: [F] concatenated
     non-sequential features; tw: {"seq": [ {w1, b1, w2, b2} per type ], "sep": [n][d],
-    "ns": {w1, b1, w2, b2}}.
+    "ns": {w1, b1, w2, b2}}. With times (times[i]: [L_i] integer timestamps) the merge is the
+    timestamp-aware one and tw["sep"] holds the behaviour-type embeddings.
     """
-    s = s_tokens(events, tw["seq"], tw["sep"])
+    if times is None:
+        s = s_tokens(events, tw["seq"], tw["sep"])
+    else:
+        s = s_tokens_by_time(events, times, tw["seq"], tw["sep"])
     if l_ns == 0:
         return s
     return np.concatenate([s, ns_tokens(ns_feat, tw["ns"], l_ns)], axis=0)
 
 
-def tokenize_batch(events: Sequence[np.ndarray], ns_feat: np.ndarray, tw: dict, l_ns: int) -> np.ndarray:
-    """Batched form: events[i] is [B][L_i][D_i], ns_feat [B][F]; returns X(0) [B][L_S + l_ns][d]."""
+def tokenize_batch(events: Sequence[np.ndarray], ns_feat: np.ndarray, tw: dict, l_ns: int, times=None) -> np.ndarray:
+    """Batched form: events[i] is [B][L_i][D_i], ns_feat [B][F] (times[i] [B][L_i]); returns X(0)
+    [B][L_S + l_ns][d]."""
     B = ns_feat.shape[0]
-    return np.stack([tokenize([e[b] for e in events], ns_feat[b], tw, l_ns) for b in range(B)])
+    return np.stack([tokenize([e[b] for e in events], ns_feat[b], tw, l_ns,
+                              None if times is None else [t[b] for t in times]) for b in range(B)])

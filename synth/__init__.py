@@ -28,10 +28,11 @@ from .gen import (round_bf16, bf16_bits, BlockWeights, make_weights, sep_vectors
                   user_cached_lengths)
 
 from .tokenizer import (TokWorkload, TOK_WORKLOADS, tok_workload, tokenizer_weights, tokenizer_sample,
-                        tokenizer_batch)
+                        tokenizer_batch, tokenizer_times, tokenizer_times_batch)
 
 __all__ = [
     "TokWorkload", "TOK_WORKLOADS", "tok_workload", "tokenizer_weights", "tokenizer_sample", "tokenizer_batch",
+    "tokenizer_times", "tokenizer_times_batch",
     "ModelShape", "Workload", "WORKLOADS", "TEST_SHAPES", "linear_pyramid", "workload",
     "test_workload", "round_bf16", "bf16_bits", "BlockWeights", "make_weights", "sep_vectors",
     "forward_sample", "forward_batch", "user_sequence", "user_sequences", "candidate_tokens",

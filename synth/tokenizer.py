@@ -7,9 +7,14 @@ raw widths or hidden widths, so the workloads below choose them (multiples of 64
 item-ID plus side-information embeddings); the behaviour sequence lengths and L_NS are those of
 the block workloads.
 
+Timestamps (timestamp-aware merge): each behaviour type logs events at its own rate; a sample's
+sequence of type i starts at a uniform offset in [0, 1000) s and advances by geometric gaps of mean
+about (i + 1) * 20 s, clipped at 0 so that some events share a time (ties across and within types).
+
 Value distributions: raw event embeddings and NS features ~ N(0, 1); MLP matrices
 ~ N(0, 1 / fan_in) so that pre-activations are O(1) and the GELU works in its curved range;
-biases ~ N(0, 0.1^2); the [SEP] rows are the model's seeded [SEP] vectors (one per sequence).
+biases ~ N(0, 0.1^2); the [SEP] rows are the model's seeded [SEP] vectors (one per sequence); in the
+timestamp-aware merge the same vectors serve as the behaviour-type embeddings.
 """
 
 from __future__ import annotations
@@ -37,10 +42,11 @@ class TokWorkload:
     input_seed: int
     weight_seed: int
     parity_subset: Tuple[int, ...] = field(default_factory=tuple)
+    merge: str = "intent"          # "intent": [SEP] after each sequence; "time": interleaved by time
 
     @property
     def l_s(self) -> int:
-        return sum(self.seq_lens) + len(self.seq_lens)
+        return sum(self.seq_lens) + (len(self.seq_lens) if self.merge == "intent" else 0)
 
     @property
     def n_seq(self) -> int:
@@ -75,6 +81,12 @@ TOK_WORKLOADS = {
         seq_hidden=(256, 256, 256), ns_dim=1024, ns_hidden=1024, batch=256, input_seed=2202,
         weight_seed=1302, parity_subset=(0, 77, 255)),
 }
+TOK_WORKLOADS["tok_mid_time"] = replace(TOK_WORKLOADS["tok_mid"], key="tok_mid_time", merge="time",
+                                        description="tok_mid with the timestamp-aware merge")
+TOK_WORKLOADS["tokenize_s_time"] = replace(
+    TOK_WORKLOADS["tokenize_s"], key="tokenize_s_time", merge="time",
+    description=TOK_WORKLOADS["tokenize_s"].description + "; timestamp-aware merge (events interleaved by "
+                                                          "time, type embeddings added, no [SEP])")
 
 
 def tok_workload(key: str, dtype: Optional[str] = None) -> TokWorkload:
@@ -110,6 +122,23 @@ def tokenizer_sample(w: TokWorkload, b: int):
     ev = [_maybe_round(_normal(rng, (w.seq_lens[i], w.seq_dims[i])), w.model.dtype) for i in range(w.n_seq)]
     ns = _maybe_round(_normal(rng, (w.ns_dim,)), w.model.dtype)
     return ev, ns
+
+
+def tokenizer_times(w: TokWorkload, b: int):
+    """Timestamps of sample b: [times_i [L_i] int64, non-decreasing within each type]."""
+    rng = _rng(w.input_seed, (b, 7))
+    out = []
+    for i, L in enumerate(w.seq_lens):
+        start = int(rng.integers(0, 1000))
+        gaps = np.maximum(rng.geometric(1.0 / (20.0 * (i + 1)), size=L) - 2, 0)
+        out.append((start + np.cumsum(gaps)).astype(np.int64))
+    return out
+
+
+def tokenizer_times_batch(w: TokWorkload, samples: Optional[Sequence[int]] = None):
+    samples = range(w.batch) if samples is None else samples
+    per = [tokenizer_times(w, b) for b in samples]
+    return [np.stack([p[i] for p in per]) for i in range(w.n_seq)]
 
 
 def tokenizer_batch(w: TokWorkload, samples: Optional[Sequence[int]] = None):

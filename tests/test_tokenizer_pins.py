@@ -108,3 +108,61 @@ def test_no_ns_tokens():
     w, tw, (ev, ns) = _tok("tok_tiny")
     x = oracle.tokenize(ev, ns, tw, 0)
     assert x.shape == (w.l_s, w.model.d_model)
+
+
+# --- timestamp-aware merge (events interleaved by time, type embedding added, no [SEP]) ---------
+
+def _identity_mlp():
+    # D_in = hidden = 1, d = 2: in the linear regime (b1 = +40) MLP(x) = [x, 0] to within 1e-12
+    return {"w1": np.array([[1.0]]), "b1": np.array([40.0]), "w2": np.array([[1.0], [0.0]]),
+            "b2": np.array([-40.0, 0.0])}
+
+
+def test_time_merge_hand_example():
+    # A: values 10, 11, 12 at times 1, 4, 9; B: values 20, 21, 22 at times 2, 3, 10. The type
+    # embeddings [0, 1] and [0, 2] mark the type in the second column. Worked by hand: time order
+    # 1 (A0), 2 (B0), 3 (B1), 4 (A1), 9 (A2), 10 (B2).
+    ev = [np.array([[10.0], [11.0], [12.0]]), np.array([[20.0], [21.0], [22.0]])]
+    t = [np.array([1, 4, 9]), np.array([2, 3, 10])]
+    emb = np.array([[0.0, 1.0], [0.0, 2.0]])
+    got = oracle.s_tokens_by_time(ev, t, [_identity_mlp(), _identity_mlp()], emb)
+    expect = [[10, 1], [20, 2], [21, 2], [11, 1], [12, 1], [22, 2]]
+    np.testing.assert_allclose(got, expect, atol=1e-12)
+
+
+def test_time_merge_ties_keep_type_then_position_order():
+    # equal times: type order first (A before B), then the order inside the sequence
+    ev = [np.array([[1.0], [2.0]]), np.array([[3.0], [4.0]])]
+    t = [np.array([5, 5]), np.array([5, 7])]
+    emb = np.zeros((2, 2))
+    got = oracle.s_tokens_by_time(ev, t, [_identity_mlp(), _identity_mlp()], emb)
+    np.testing.assert_allclose(got[:, 0], [1, 2, 3, 4], atol=1e-12)
+    t = [np.array([6, 6]), np.array([5, 6])]
+    got = oracle.s_tokens_by_time(ev, t, [_identity_mlp(), _identity_mlp()], emb)
+    np.testing.assert_allclose(got[:, 0], [3, 1, 2, 4], atol=1e-12)
+
+
+def test_time_merge_disjoint_ranges_concatenate():
+    w, tw, (ev, ns) = _tok("tok_mid")
+    times = [np.arange(L) + 10_000 * (w.n_seq - i) for i, L in enumerate(w.seq_lens)]   # last type oldest
+    x = oracle.tokenize(ev, ns, tw, w.model.l_ns, times=times)
+    parts = [oracle.mlp(e, p["w1"], p["b1"], p["w2"], p["b2"]) + tw["sep"][i]
+             for i, (e, p) in enumerate(zip(ev, tw["seq"]))]
+    np.testing.assert_array_equal(x[:sum(w.seq_lens)], np.concatenate(parts[::-1], axis=0))
+
+
+def test_time_merge_is_a_sorted_permutation():
+    w = synth.tok_workload("tok_mid_time")
+    tw = synth.tokenizer_weights(w)
+    ev, ns = synth.tokenizer_sample(w, 2)
+    times = synth.tokenizer_times(w, 2)
+    x = oracle.tokenize(ev, ns, tw, w.model.l_ns, times=times)
+    assert w.l_s == sum(w.seq_lens) and x.shape[0] == w.l_s + w.model.l_ns
+    rows = np.concatenate([oracle.mlp(e, p["w1"], p["b1"], p["w2"], p["b2"]) + tw["sep"][i]
+                           for i, (e, p) in enumerate(zip(ev, tw["seq"]))], axis=0)
+    t_all = np.concatenate(times)
+    # every merged row is one aligned row, each used once, and the times along the merge never fall
+    idx = [int(np.argmin(np.abs(rows - r).sum(axis=1))) for r in x[:w.l_s]]
+    np.testing.assert_array_equal(x[:w.l_s], rows[idx])
+    assert sorted(idx) == list(range(w.l_s))
+    assert np.all(np.diff(t_all[idx]) >= 0)
