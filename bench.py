@@ -41,7 +41,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="onetrans_s",
-                   choices=["onetrans_s", "two_stage", "append", "append_ragged", "onetrans_l", "tokenize_s"])
+                   choices=["onetrans_s", "two_stage", "append", "append_ragged", "onetrans_l", "tokenize_s",
+                            "tokenize_s_time"])
     p.add_argument("--dtype", default=None, choices=[None, "bf16", "f32"])
     p.add_argument("--no-trace", action="store_true", help="no per-kernel events in the timed region")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline (0: skip)")
@@ -131,15 +132,16 @@ def bench_tokenize(a):
     tw = synth.tokenizer_weights(w)
     up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev, dtype=model.torch_dtype)
     tok = ob.Tokenizer(model, w.seq_lens, [{k: up(v) for k, v in p.items()} for p in tw["seq"]], up(tw["sep"]),
-                       {k: up(v) for k, v in tw["ns"].items()} if tw["ns"] is not None else None)
+                       {k: up(v) for k, v in tw["ns"].items()} if tw["ns"] is not None else None, merge=w.merge)
     ev, ns = synth.tokenizer_batch(w)
     evd, nsd = [up(e) for e in ev], up(ns)
+    tmd = [torch.from_numpy(t).to(dev) for t in synth.tokenizer_times_batch(w)] if w.merge == "time" else None
     x0 = torch.empty((w.batch, w.l_s + m.l_ns, m.d_model), dtype=model.torch_dtype, device=dev)
     wsp = tok.workspace(w.batch)
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        ob.onetrans_tokenize(tok, evd, nsd, x0, wsp)
+        ob.onetrans_tokenize(tok, evd, nsd, x0, wsp, times=tmd)
 
     torch.cuda.synchronize()
     t_setup = time.time() - t_setup
@@ -160,7 +162,7 @@ def bench_tokenize(a):
     timing = ob.timing_read()
     ms_step = e0.elapsed_time(e1) / a.steps
     flops, act, wts = cm.tokenize_work(m.d_model, m.l_ns, w.seq_lens, w.seq_dims, w.seq_hidden, w.ns_dim,
-                                       w.ns_hidden, store_bytes)
+                                       w.ns_hidden, store_bytes, w.merge)
     lin_ms, lin_n = timing["lin"]
     lin_bytes = (act * w.batch + wts) * a.steps           # every linear launch of the timed steps
     roof = roofline_entry("lin", lin_bytes, lin_ms, lin_n, PEAK_HBM_GBS, "GB/s", "hbm") if lin_n else None
@@ -177,7 +179,7 @@ def bench_tokenize(a):
         done = 0
         while done < 256 and (time.perf_counter() - t0 < a.cpu_seconds or done < 2):
             e_b, n_b = synth.tokenizer_sample(w, done)
-            O.tokenize(e_b, n_b, tw, m.l_ns)
+            O.tokenize(e_b, n_b, tw, m.l_ns, times=synth.tokenizer_times(w, done) if w.merge == "time" else None)
             done += 1
         cpu_s = time.perf_counter() - t0
         cpu = {"value": round(done / cpu_s, 4), "unit": "samples/s", "cores": blas_threads(), "kind": "oracle",
@@ -212,7 +214,7 @@ def main():
     if a.copy_calibration:
         copy_calibration(a.copy_calibration)
         return
-    if a.workload == "tokenize_s":
+    if a.workload.startswith("tokenize_s"):
         bench_tokenize(a)
         return
 

@@ -162,16 +162,22 @@ int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weig
 
 /* ---- Tokenizers ahead of block 1 (section 7.5.0, "Unified Tokenization") -------------------
  *
- * S-tokens: n_seq behaviour sequences (types), given in merge order (highest intent first).
+ * S-tokens: n_seq behaviour sequences (types), given in intent order (highest intent first).
  * Event e of type i is a raw embedding of width seq_dim[i]; the behaviour-specific MLP_i maps it
- * to width d. The timestamp-agnostic merge concatenates the aligned sequences, each followed by
- * its own learnable [SEP] row, so L_S = sum_i seq_len[i] + n_seq and sequence i starts at row
- * off_i = sum_{j<i} (seq_len[j] + 1).
+ * to width d. Two merges:
+ *   ONETRANS_MERGE_INTENT (timestamp-agnostic): the aligned sequences in the given order, each
+ *     followed by its own learnable [SEP] row, so L_S = sum_i seq_len[i] + n_seq and sequence i
+ *     starts at row off_i = sum_{j<i} (seq_len[j] + 1).
+ *   ONETRANS_MERGE_TIME (timestamp-aware): every aligned event row plus the learnable embedding of
+ *     its behaviour type, all events of a sample in ascending time; equal times keep the type
+ *     order, then the order inside the sequence. No [SEP] rows: L_S = sum_i seq_len[i].
  * NS-tokens (Auto-Split tokenizer): one MLP maps a sample's concatenated non-sequential features
  * (width ns_dim) to l_ns * d values; NS token j is values [j d, (j + 1) d).
  * Every MLP here is MLP(x) = W2 GELU(W1 x + b1) + b2 with the exact erf GELU, weights (out, in)
  * row-major like the blocks' matrices.
  */
+typedef enum { ONETRANS_MERGE_INTENT = 0, ONETRANS_MERGE_TIME = 1 } onetrans_merge;
+
 typedef struct {
   int n_seq;              /* behaviour types, 1..7 */
   const int *seq_len;     /* host [n_seq]: events per sample of type i (>= 0) */
@@ -179,6 +185,7 @@ typedef struct {
   const int *seq_hidden;  /* host [n_seq]: hidden width of MLP_i, a multiple of 64 */
   int ns_dim;             /* width of Concat(NS), a multiple of 64 (ignored when l_ns = 0) */
   int ns_hidden;          /* hidden width of the Auto-Split MLP, a multiple of 64 (same) */
+  int merge;              /* onetrans_merge */
 } onetrans_tokenizer_config;
 
 typedef struct {          /* storage dtype */
@@ -187,27 +194,34 @@ typedef struct {          /* storage dtype */
 } onetrans_mlp_weights;
 
 /* Workspace bytes of onetrans_tokenize for `batch` samples (the hidden activations of every MLP,
- * in the storage dtype). Returns 0 for an invalid configuration. */
+ * in the storage dtype; with the timestamp-aware merge also one int32 row index per event).
+ * Returns 0 for an invalid configuration. */
 size_t onetrans_tokenize_workspace_bytes(const onetrans_config *cfg, const onetrans_tokenizer_config *tc,
                                          int batch);
 
 /* Builds X(0) = [S-tokens; NS-tokens] for `batch` samples: the input of onetrans_forward.
  *   seq_mlp  host [n_seq]: MLP_i, in = seq_dim[i], hidden = seq_hidden[i], out = d.
- *   sep      [n_seq][d]: the [SEP] row written after sequence i.
+ *   seq_vec  [n_seq][d]: INTENT: the [SEP] row written after sequence i; TIME: the embedding of
+ *            behaviour type i, added to each of its event rows.
  *   ns_mlp   host pointer to the Auto-Split MLP (in = ns_dim, hidden = ns_hidden, out = l_ns * d);
  *            NULL when l_ns = 0.
  *   events   host [n_seq] of device pointers: events[i] is [batch][seq_len[i]][seq_dim[i]]
  *            (may be NULL when seq_len[i] = 0).
+ *   times    TIME: host [n_seq] of device pointers, times[i] is int64 [batch][seq_len[i]] (may be
+ *            NULL when seq_len[i] = 0). Any order is merged exactly; chronological sequences
+ *            (non-decreasing per type) take the fast path (binary search instead of an all-pairs
+ *            count per sample). INTENT: ignored (NULL).
  *   ns_feat  [batch][ns_dim] (NULL when l_ns = 0).
  *   x0       [batch][L_S + l_ns][d] storage dtype, written entirely.
  * Hidden activations are rounded to the storage dtype; accumulation is fp32.
- * Errors: INVALID_ARG (null pointer, bad dtype), SHAPE (n_seq, a negative length, L_S < 1),
- * UNSUPPORTED (a width not a multiple of 64, n_seq > 7), WORKSPACE, ALIGNMENT, HIP. */
+ * Errors: INVALID_ARG (null pointer, bad dtype or merge), SHAPE (n_seq, a negative length,
+ * L_S < 1), UNSUPPORTED (a width not a multiple of 64, n_seq > 7, TIME with more than 8192 events
+ * per sample), WORKSPACE, ALIGNMENT, HIP. */
 int onetrans_tokenize(const onetrans_config *cfg, const onetrans_tokenizer_config *tc,
-                      const onetrans_mlp_weights *seq_mlp, const void *sep,
+                      const onetrans_mlp_weights *seq_mlp, const void *seq_vec,
                       const onetrans_mlp_weights *ns_mlp, const void *const *events,
-                      const void *ns_feat, int batch, void *x0, void *ws, size_t ws_bytes,
-                      hipStream_t stream);
+                      const void *const *times, const void *ns_feat, int batch, void *x0, void *ws,
+                      size_t ws_bytes, hipStream_t stream);
 
 /* Kernel classes of the per-launch timing below. */
 typedef enum {
@@ -215,7 +229,7 @@ typedef enum {
   ONETRANS_K_ATTN = 1,       /* causal / Stage II attention */
   ONETRANS_K_POST = 2,       /* fused W^O + residual + pre-norm 2 + mixed FFN + residual */
   ONETRANS_K_LIN = 3,        /* tokenizer linear layers (grouped MLP layers) */
-  ONETRANS_K_SEP = 4,        /* tokenizer [SEP] rows */
+  ONETRANS_K_MERGE = 4,      /* tokenizer merge: [SEP] rows, or time-order ranks */
   ONETRANS_K_COUNT = 5
 } onetrans_kernel_class;
 

@@ -175,10 +175,10 @@ def test_ragged_user_validation_errors():
                                          FAKE, FAKE, 1 << 40, None) == L.ERR_SHAPE
 
 
-def _tok_cfg(lens=(15, 15), dims=(64, 128), hid=(128, 64), ns_dim=192, ns_hidden=128):
+def _tok_cfg(lens=(15, 15), dims=(64, 128), hid=(128, 64), ns_dim=192, ns_hidden=128, merge=L.MERGE_INTENT):
     n = len(lens)
     arrs = [(ctypes.c_int * n)(*v) for v in (lens, dims, hid)]
-    tc = L.TokenizerConfig(n, *arrs, ns_dim, ns_hidden)
+    tc = L.TokenizerConfig(n, *arrs, ns_dim, ns_hidden, merge)
     tc._keep = arrs
     return tc
 
@@ -200,6 +200,14 @@ def test_tokenize_workspace_bytes():
     assert got == al(B * 15 * 128 * 4) + al(B * 15 * 64 * 4) + al(B * 128 * 4)
     assert lib.onetrans_tokenize_workspace_bytes(ctypes.byref(c), ctypes.byref(_tok_cfg(dims=(64, 96))), B) == 0
     assert lib.onetrans_tokenize_workspace_bytes(ctypes.byref(c), None, B) == 0
+    # timestamp-aware merge: plus one int32 row index per event
+    got = lib.onetrans_tokenize_workspace_bytes(ctypes.byref(c), ctypes.byref(_tok_cfg(merge=L.MERGE_TIME)), B)
+    assert got == (al(B * 15 * 128 * 4) + al(B * 15 * 64 * 4) + al(B * 128 * 4) + 2 * al(B * 15 * 4))
+    assert lib.onetrans_tokenize_workspace_bytes(ctypes.byref(c), ctypes.byref(_tok_cfg(merge=2)), B) == 0
+    assert lib.onetrans_tokenize_workspace_bytes(ctypes.byref(c), ctypes.byref(
+        _tok_cfg(lens=(4096, 4097), merge=L.MERGE_TIME)), B) == 0      # more than 8192 events per sample
+    assert lib.onetrans_tokenize_workspace_bytes(ctypes.byref(c), ctypes.byref(
+        _tok_cfg(lens=(0, 0), merge=L.MERGE_TIME)), B) == 0            # no S rows at all
 
 
 def test_tokenize_validation_errors():
@@ -209,12 +217,12 @@ def test_tokenize_validation_errors():
     ev = (ctypes.c_void_p * 2)(FAKE, FAKE)
 
     def call(tc=None, seq=None, sep=FAKE, ns=True, events=ev, ns_feat=FAKE, B=8, x0=FAKE, ws=FAKE, wsb=1 << 40,
-             cfg=c):
+             cfg=c, times=None):
         tc = tc or _tok_cfg()
         seq = seq if seq is not None else _mlps(tc.n_seq)
         nsm = _mlps(1, 0x400000) if ns else None
-        return lib.onetrans_tokenize(ctypes.byref(cfg), ctypes.byref(tc), seq, sep, nsm, events, ns_feat, B, x0, ws,
-                                     wsb, None)
+        return lib.onetrans_tokenize(ctypes.byref(cfg), ctypes.byref(tc), seq, sep, nsm, events, times, ns_feat, B,
+                                     x0, ws, wsb, None)
 
     assert call(sep=None) == L.ERR_INVALID_ARG
     assert call(x0=None) == L.ERR_INVALID_ARG
@@ -237,6 +245,13 @@ def test_tokenize_validation_errors():
                 events=(ctypes.c_void_p * 8)(*[FAKE] * 8)) == L.ERR_UNSUPPORTED   # at most 7 types
     assert call(wsb=64) == L.ERR_WORKSPACE
     assert call(cfg=_cfg(d=64, H=4, dff=256, lns=4, N=1, sq=(32,), dtype=5)) == L.ERR_INVALID_ARG
+    # timestamp-aware merge: timestamps required (8-byte aligned) for every non-empty type
+    tt = _tok_cfg(merge=L.MERGE_TIME)
+    assert call(tc=tt) == L.ERR_INVALID_ARG
+    assert call(tc=tt, times=(ctypes.c_void_p * 2)(FAKE, None)) == L.ERR_INVALID_ARG
+    assert call(tc=tt, times=(ctypes.c_void_p * 2)(FAKE, FAKE + 4)) == L.ERR_ALIGNMENT
+    assert call(tc=tt, times=(ctypes.c_void_p * 2)(FAKE, FAKE), wsb=64) == L.ERR_WORKSPACE
+    assert call(tc=_tok_cfg(merge=3)) == L.ERR_INVALID_ARG
     # an empty sequence needs no event buffer
     assert call(tc=_tok_cfg(lens=(15, 0)), events=(ctypes.c_void_p * 2)(FAKE, None), wsb=64) == L.ERR_WORKSPACE
 

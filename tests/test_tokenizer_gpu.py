@@ -28,29 +28,39 @@ def _setup(w, device="cuda"):
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device, dtype=mdl.torch_dtype)
     seq = [{k: t(v) for k, v in p.items()} for p in tw["seq"]]
     ns = {k: t(v) for k, v in tw["ns"].items()} if tw["ns"] is not None else None
-    tok = ob.Tokenizer(mdl, w.seq_lens, seq, t(tw["sep"]), ns)
+    tok = ob.Tokenizer(mdl, w.seq_lens, seq, t(tw["sep"]), ns, merge=w.merge)
     return mdl, tok, tw, t
 
 
 def _case(w, samples=None):
     say(f"[tokenize] {w.key} dtype={w.model.dtype} B={w.batch} L={w.seq_lens} D={w.seq_dims} "
-        f"H={w.seq_hidden} F={w.ns_dim} l_ns={w.model.l_ns}")
+        f"H={w.seq_hidden} F={w.ns_dim} l_ns={w.model.l_ns} merge={w.merge}")
     mdl, tok, tw, t = _setup(w)
     ev, ns = synth.tokenizer_batch(w)
-    x0 = ob.onetrans_tokenize(tok, [t(e) for e in ev], t(ns) if w.model.l_ns > 0 else None)
+    times = synth.tokenizer_times_batch(w) if w.merge == "time" else None
+    x0 = ob.onetrans_tokenize(tok, [t(e) for e in ev], t(ns) if w.model.l_ns > 0 else None,
+                              times=[torch.from_numpy(x).to("cuda") for x in times] if times else None)
     torch.cuda.synchronize()
     got = x0.float().cpu().numpy()
     assert got.shape == (w.batch, w.l_s + w.model.l_ns, w.model.d_model)
     for b in (range(w.batch) if samples is None else samples):
-        ref = O.tokenize([e[b] for e in ev], ns[b], tw, w.model.l_ns)
+        tb = [x[b] for x in times] if times else None
+        ref = O.tokenize([e[b] for e in ev], ns[b], tw, w.model.l_ns, times=tb)
         e = rel_err(got[b], ref)
         say(f"  sample {b}: err {e:.3e}")
         assert e <= TOL[w.model.dtype], (w.key, b, e)
-        # [SEP] rows are copies: bit-exact
-        off = 0
-        for i, L in enumerate(w.seq_lens):
-            np.testing.assert_array_equal(got[b, off + L], tw["sep"][i])
-            off += L + 1
+        if times is None:
+            # [SEP] rows are copies: bit-exact
+            off = 0
+            for i, L in enumerate(w.seq_lens):
+                np.testing.assert_array_equal(got[b, off + L], tw["sep"][i])
+                off += L + 1
+        else:
+            # the merge order is index work: every GPU row is nearest to the oracle row at its own
+            # position, far ahead of any other row
+            g, r = got[b, :w.l_s].astype(np.float64), ref[:w.l_s]
+            d2 = (g * g).sum(1)[:, None] + (r * r).sum(1)[None, :] - 2.0 * g @ r.T
+            np.testing.assert_array_equal(np.argmin(d2, axis=1), np.arange(w.l_s))
     return got
 
 
@@ -72,6 +82,48 @@ def test_tokenize_without_ns_tokens(dtype):
 def test_tokenize_sep_rows_only():
     w = replace(synth.tok_workload("tok_mid", "bf16"), seq_lens=(0, 0, 0, 0))
     _case(w)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_tokenize_time_merge(dtype):
+    _case(synth.tok_workload("tok_mid_time", dtype))
+
+
+def test_tokenize_time_merge_ties_everywhere():
+    """All events of a sample at one time: the merge is the intent order without [SEP] rows."""
+    w = synth.tok_workload("tok_mid_time", "f32")
+    mdl, tok, tw, t = _setup(w)
+    ev, ns = synth.tokenizer_batch(w)
+    times = [np.full((w.batch, L), 42, dtype=np.int64) for L in w.seq_lens]
+    x0 = ob.onetrans_tokenize(tok, [t(e) for e in ev], t(ns), times=[torch.from_numpy(x).to("cuda") for x in times])
+    torch.cuda.synchronize()
+    got = x0.float().cpu().numpy()
+    for b in range(w.batch):
+        ref = O.tokenize([e[b] for e in ev], ns[b], tw, w.model.l_ns, times=[x[b] for x in times])
+        assert rel_err(got[b], ref) <= TOL["f32"]
+
+
+def test_tokenize_time_merge_unsorted_timestamps():
+    """Timestamps shuffled inside each type (not chronological): the exact all-pairs path."""
+    w = synth.tok_workload("tok_mid_time", "bf16")
+    mdl, tok, tw, t = _setup(w)
+    ev, ns = synth.tokenizer_batch(w)
+    rng = np.random.default_rng(11)
+    times = [np.ascontiguousarray(rng.permuted(x, axis=1)) for x in synth.tokenizer_times_batch(w)]
+    x0 = ob.onetrans_tokenize(tok, [t(e) for e in ev], t(ns), times=[torch.from_numpy(x).to("cuda") for x in times])
+    torch.cuda.synchronize()
+    got = x0.float().cpu().numpy()
+    for b in range(w.batch):
+        ref = O.tokenize([e[b] for e in ev], ns[b], tw, w.model.l_ns, times=[x[b] for x in times])
+        assert rel_err(got[b], ref) <= TOL["bf16"]
+        g, r = got[b, :w.l_s].astype(np.float64), ref[:w.l_s]
+        d2 = (g * g).sum(1)[:, None] + (r * r).sum(1)[None, :] - 2.0 * g @ r.T
+        np.testing.assert_array_equal(np.argmin(d2, axis=1), np.arange(w.l_s))
+
+
+def test_tokenize_time_merge_full_size_sampled():
+    w = synth.tok_workload("tokenize_s_time")
+    _case(w, samples=w.parity_subset)
 
 
 def test_tokenize_full_size_sampled():

@@ -20,7 +20,8 @@ ERR_HIP = -7
 F32, BF16 = 0, 1
 RMSNORM, LAYERNORM = 0, 1
 OP_FORWARD, OP_PREFILL, OP_SCORE, OP_APPEND = 0, 1, 2, 3
-KERNEL_CLASSES = ("qkv", "attn", "post", "lin", "sep")
+KERNEL_CLASSES = ("qkv", "attn", "post", "lin", "merge")
+MERGE_INTENT, MERGE_TIME = 0, 1
 
 WEIGHT_FIELDS = ("norm1_g", "norm1_b", "norm2_g", "norm2_b", "wq", "wk", "wv", "wo", "w1", "b1", "w2", "b2")
 
@@ -41,7 +42,7 @@ class KVCache(ctypes.Structure):
 
 class TokenizerConfig(ctypes.Structure):
     _fields_ = [("n_seq", c_int), ("seq_len", POINTER(c_int)), ("seq_dim", POINTER(c_int)),
-                ("seq_hidden", POINTER(c_int)), ("ns_dim", c_int), ("ns_hidden", c_int)]
+                ("seq_hidden", POINTER(c_int)), ("ns_dim", c_int), ("ns_hidden", c_int), ("merge", c_int)]
 
 
 MLP_FIELDS = ("w1", "b1", "w2", "b2")
@@ -64,8 +65,8 @@ SIGNATURES = {
                                        c_int, c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
     "onetrans_tokenize_workspace_bytes": (c_size_t, [POINTER(Config), POINTER(TokenizerConfig), c_int]),
     "onetrans_tokenize": (c_int, [POINTER(Config), POINTER(TokenizerConfig), POINTER(MlpWeights), c_void_p,
-                                  POINTER(MlpWeights), POINTER(c_void_p), c_void_p, c_int, c_void_p, c_void_p,
-                                  c_size_t, c_void_p]),
+                                  POINTER(MlpWeights), POINTER(c_void_p), POINTER(c_void_p), c_void_p, c_int,
+                                  c_void_p, c_void_p, c_size_t, c_void_p]),
     "onetrans_timing_enable": (c_int, [c_int]),
     "onetrans_timing_read": (c_int, [POINTER(ctypes.c_double), POINTER(ctypes.c_longlong)]),
     "onetrans_status_string": (c_char_p, [c_int]),

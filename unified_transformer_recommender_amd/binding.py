@@ -198,18 +198,22 @@ def onetrans_append_events(model: Model, cache: KVCache, x_new: torch.Tensor,
 class Tokenizer:
     """Device weights of the tokenizers ahead of block 1 for one model (see onetrans_tokenize).
 
-    ``seq_mlps``: one mapping per behaviour type (merge order) with w1 [hidden][D_i], b1 [hidden],
-    w2 [d][hidden], b2 [d]; ``sep`` [n_seq][d]; ``ns_mlp``: the Auto-Split MLP (w1 [hidden][ns_dim],
+    ``seq_mlps``: one mapping per behaviour type (intent order) with w1 [hidden][D_i], b1 [hidden],
+    w2 [d][hidden], b2 [d]; ``seq_vec`` [n_seq][d]: the [SEP] rows (merge "intent") or the
+    behaviour-type embeddings (merge "time"); ``ns_mlp``: the Auto-Split MLP (w1 [hidden][ns_dim],
     b1, w2 [l_ns * d][hidden], b2) or None when l_ns = 0. All contiguous, storage dtype, on device.
     """
 
-    def __init__(self, model: Model, seq_lens: Sequence[int], seq_mlps, sep: torch.Tensor, ns_mlp=None):
+    def __init__(self, model: Model, seq_lens: Sequence[int], seq_mlps, seq_vec: torch.Tensor, ns_mlp=None,
+                 merge: str = "intent"):
         self.model = model
         self.seq_lens = tuple(int(v) for v in seq_lens)
         n = len(self.seq_lens)
         if len(seq_mlps) != n:
             raise ValueError("one MLP per behaviour type")
-        self._tensors = [sep]
+        self.merge = merge
+        merge_code = {"intent": L.MERGE_INTENT, "time": L.MERGE_TIME}[merge]
+        self._tensors = [seq_vec]
         self._mlps = (L.MlpWeights * n)()
         dims, hidden = [], []
         for i, p in enumerate(seq_mlps):
@@ -226,9 +230,9 @@ class Tokenizer:
         self._len = (ctypes.c_int * n)(*self.seq_lens)
         self._dim = (ctypes.c_int * n)(*dims)
         self._hid = (ctypes.c_int * n)(*hidden)
-        self.tc = L.TokenizerConfig(n, self._len, self._dim, self._hid, ns_dim, ns_hidden)
-        self.sep = sep
-        self.l_s = sum(self.seq_lens) + n
+        self.tc = L.TokenizerConfig(n, self._len, self._dim, self._hid, ns_dim, ns_hidden, merge_code)
+        self.seq_vec = seq_vec
+        self.l_s = sum(self.seq_lens) + (n if merge == "intent" else 0)
 
     def _fill(self, c, p):
         for f in L.MLP_FIELDS:
@@ -247,8 +251,9 @@ class Tokenizer:
 
 def onetrans_tokenize(tok: Tokenizer, events: Sequence[torch.Tensor], ns_feat: Optional[torch.Tensor],
                       x0: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
-                      stream=None) -> torch.Tensor:
-    """events[i] [B][L_i][D_i], ns_feat [B][ns_dim] -> X(0) [B][L_S + l_ns][d] (storage dtype)."""
+                      stream=None, times: Optional[Sequence[torch.Tensor]] = None) -> torch.Tensor:
+    """events[i] [B][L_i][D_i], ns_feat [B][ns_dim] (times[i] int64 [B][L_i] for the time merge)
+    -> X(0) [B][L_S + l_ns][d] (storage dtype)."""
     m = tok.model
     B = int(ns_feat.shape[0]) if ns_feat is not None else int(events[0].shape[0])
     for i, e in enumerate(events):
@@ -262,8 +267,16 @@ def onetrans_tokenize(tok: Tokenizer, events: Sequence[torch.Tensor], ns_feat: O
     if ws is None:
         ws = tok.workspace(B)
     ev = (ctypes.c_void_p * len(events))(*[e.data_ptr() for e in events])
-    st = L.lib().onetrans_tokenize(ctypes.byref(m.cfg), ctypes.byref(tok.tc), tok._mlps, tok.sep.data_ptr(),
-                                   ctypes.byref(tok._ns) if tok._ns is not None else None, ev, _ptr(ns_feat), B,
+    tm = None
+    if tok.merge == "time":
+        if times is None or len(times) != len(events):
+            raise ValueError("the time merge needs one int64 [B][L_i] timestamp tensor per behaviour type")
+        for i, t in enumerate(times):
+            if t.dtype != torch.int64 or not t.is_contiguous() or tuple(t.shape) != (B, tok.seq_lens[i]):
+                raise ValueError(f"times[{i}]: need a contiguous int64 tensor [B][L_i]")
+        tm = (ctypes.c_void_p * len(times))(*[t.data_ptr() for t in times])
+    st = L.lib().onetrans_tokenize(ctypes.byref(m.cfg), ctypes.byref(tok.tc), tok._mlps, tok.seq_vec.data_ptr(),
+                                   ctypes.byref(tok._ns) if tok._ns is not None else None, ev, tm, _ptr(ns_feat), B,
                                    x0.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev, stream))
     L.check(st, "onetrans_tokenize")
     return x0

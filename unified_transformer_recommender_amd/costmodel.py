@@ -172,21 +172,22 @@ def append_cache_bytes(d, n_blocks, l_old, d_l, store_bytes):
 
 # --- tokenizers ahead of block 1 ([en] 7.5.0) ---------------------------------------------------
 
-def tokenize_work(d, l_ns, seq_lens, seq_dims, seq_hidden, ns_dim, ns_hidden, store_bytes):
+def tokenize_work(d, l_ns, seq_lens, seq_dims, seq_hidden, ns_dim, ns_hidden, store_bytes, merge="intent"):
     """Per-sample algorithmic flops and HBM bytes of the two grouped linear launches.
 
     flops: 2 m n k over every layer of every MLP. bytes: what each launch must read and write
     once: launch 1 reads the raw events / NS features and the first-layer weights and writes the
     hidden activations; launch 2 reads those and the second-layer weights and writes the non-[SEP]
-    rows of X(0). Weights are counted once per launch, so per sample they are divided by the batch
-    by the caller (returned separately)."""
+    rows of X(0) (with the timestamp-aware merge also each event's int32 row index). Weights are
+    counted once per launch, so per sample they are divided by the batch by the caller (returned
+    separately)."""
     flops = 0.0
     act = 0.0        # per-sample activation bytes over both launches
     wts = 0.0        # weight bytes over both launches (once per launch, not per sample)
     for L, D, H in zip(seq_lens, seq_dims, seq_hidden):
         flops += 2.0 * L * (D * H + H * d)
-        act += store_bytes * L * (D + H + H + d)
-        wts += store_bytes * (H * D + H + d * H + d)
+        act += store_bytes * L * (D + H + H + d) + (4 * L if merge == "time" else 0)
+        wts += store_bytes * (H * D + H + d * H + d) + (store_bytes * d if merge == "time" else 0)
     if l_ns > 0:
         flops += 2.0 * (ns_dim * ns_hidden + ns_hidden * l_ns * d)
         act += store_bytes * (ns_dim + 2 * ns_hidden + l_ns * d)

@@ -303,7 +303,8 @@ struct AttnArgs {
 };
 
 // ---------------------------------------------------------------------------------------------
-// Grouped linear layer of the tokenizers: per group, y = act(x W^T + b) over m rows.
+// Grouped linear layer of the tokenizers: per group, y = act(x W^T + b) or x W^T + b + b_add over
+// m rows.
 // Input row r at x + r * x_ld elements; output row r at
 //   y + (r / y_rps) * y_ss + (r % y_rps) * y_rs elements
 // (y_rps rows per sample, so a group can write its rows straight into X(0)).
@@ -317,10 +318,21 @@ struct LinGroup {
   int m, n, k;
   int gelu;                // exact erf GELU after the bias
   int tile0;
+  const int *y_row;        // or null: output row r goes to row y_row[r] (instead of r % y_rps) of its sample
+  const void *b_add;       // or null: a second bias [n] added with b (groups without GELU only)
 };
 struct LinArgs {
   LinGroup g[LIN_MAX_GROUPS];
   int n_groups;
+};
+
+// Timestamp-aware merge: merged row of every event, per sample (one workgroup each). Event l of
+// type i has key (t[i][b][l], i, l); its row is the number of the sample's events with a smaller key.
+struct RankArgs {
+  const long long *t[LIN_MAX_GROUPS];   // [batch][len[i]] timestamps of type i
+  int *pos[LIN_MAX_GROUPS];             // [batch][len[i]] merged row of each event
+  int len[LIN_MAX_GROUPS];
+  int n_seq, total;                     // total = sum of len
 };
 
 // [SEP] rows: row j of sep [n_sep][d] to row sep_row[j] of each sample (sample_stride elements).

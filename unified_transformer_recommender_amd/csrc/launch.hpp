@@ -22,6 +22,8 @@ hipError_t launch_lin(int dtype, const LinArgs &a, int grid, hipStream_t s);
 int lin_rows_per_tile();
 int lin_features_per_tile();
 hipError_t launch_sep(int dtype, const SepArgs &a, hipStream_t s);
+hipError_t launch_rank(const RankArgs &a, int batch, hipStream_t s);
+constexpr int RANK_MAX_EVENTS = 8192;   // timestamps of one sample staged in LDS (64 KB)
 
 constexpr int ATTN_WAVES = 8;                    // waves per attention workgroup
 constexpr int ATTN_QBLOCK = 32 * ATTN_WAVES;     // forward-mode queries per attention workgroup

@@ -382,9 +382,11 @@ inline HeadView cache_view(const Dims &D, const onetrans_kv_cache *c, void *base
 
 // ---- tokenizers (section 7.5.0) ----------------------------------------------------------------
 // Workspace: the hidden activations of every MLP, [batch * rows][hidden] each, storage dtype.
+// With the timestamp-aware merge also the merged row of every event, int32 [batch * len] per type.
 struct TokPlan {
-  int l_s, T;
-  size_t hid[LIN_MAX_GROUPS];
+  int l_s, T, events;
+  bool by_time;
+  size_t hid[LIN_MAX_GROUPS], pos[LIN_MAX_GROUPS];
   size_t total;
 };
 
@@ -392,8 +394,10 @@ int check_tok(const onetrans_config *cfg, const onetrans_tokenizer_config *tc, i
   int rc;
   if ((rc = check_cfg(cfg, D))) return rc;
   if (!tc || !tc->seq_len || !tc->seq_dim || !tc->seq_hidden) return ONETRANS_ERR_INVALID_ARG;
+  if (tc->merge != ONETRANS_MERGE_INTENT && tc->merge != ONETRANS_MERGE_TIME) return ONETRANS_ERR_INVALID_ARG;
   if (batch < 1 || tc->n_seq < 1) return ONETRANS_ERR_SHAPE;
   if (tc->n_seq > LIN_MAX_GROUPS - 1) return ONETRANS_ERR_UNSUPPORTED;
+  P.by_time = tc->merge == ONETRANS_MERGE_TIME;
   auto width_ok = [](int w) { return w >= 64 && w % 64 == 0; };
   long long l_s = 0, tiles1 = 0, tiles2 = 0;
   const long long rt = lin_rows_per_tile(), nt = lin_features_per_tile();
@@ -404,7 +408,7 @@ int check_tok(const onetrans_config *cfg, const onetrans_tokenizer_config *tc, i
     if (!width_ok(tc->seq_dim[i]) || !width_ok(tc->seq_hidden[i])) return ONETRANS_ERR_UNSUPPORTED;
     const long long m = (long long)batch * L;
     if (m > (1LL << 30)) return ONETRANS_ERR_SHAPE;
-    l_s += L + 1;
+    l_s += L + (P.by_time ? 0 : 1);
     tiles1 += (m + rt - 1) / rt * (tc->seq_hidden[i] / nt);
     tiles2 += (m + rt - 1) / rt * (D.d / nt);
     P.hid[i] = off;
@@ -417,7 +421,15 @@ int check_tok(const onetrans_config *cfg, const onetrans_tokenizer_config *tc, i
     P.hid[tc->n_seq] = off;
     off += al((size_t)batch * tc->ns_hidden * D.esz);
   }
-  if (l_s + D.lns > (1 << 24) || tiles1 >= (1LL << 31) || tiles2 >= (1LL << 31)) return ONETRANS_ERR_SHAPE;
+  if (l_s < 1 || l_s + D.lns > (1 << 24) || tiles1 >= (1LL << 31) || tiles2 >= (1LL << 31)) return ONETRANS_ERR_SHAPE;
+  if (P.by_time) {
+    if (l_s > RANK_MAX_EVENTS) return ONETRANS_ERR_UNSUPPORTED;
+    for (int i = 0; i < tc->n_seq; ++i) {
+      P.pos[i] = off;
+      off += al((size_t)batch * tc->seq_len[i] * 4);
+    }
+  }
+  P.events = (int)(P.by_time ? l_s : l_s - tc->n_seq);
   P.l_s = (int)l_s;
   P.T = P.l_s + D.lns;
   P.total = off > 0 ? off : 256;
@@ -749,20 +761,20 @@ size_t onetrans_tokenize_workspace_bytes(const onetrans_config *cfg, const onetr
 }
 
 int onetrans_tokenize(const onetrans_config *cfg, const onetrans_tokenizer_config *tc,
-                      const onetrans_mlp_weights *seq_mlp, const void *sep, const onetrans_mlp_weights *ns_mlp,
-                      const void *const *events, const void *ns_feat, int batch, void *x0, void *ws,
-                      size_t ws_bytes, hipStream_t stream) {
+                      const onetrans_mlp_weights *seq_mlp, const void *seq_vec, const onetrans_mlp_weights *ns_mlp,
+                      const void *const *events, const void *const *times, const void *ns_feat, int batch,
+                      void *x0, void *ws, size_t ws_bytes, hipStream_t stream) {
   Dims D;
   TokPlan P;
   int rc;
   if ((rc = check_tok(cfg, tc, batch, D, P))) return rc;
-  if (!seq_mlp || !sep || !events || !x0 || !ws) return ONETRANS_ERR_INVALID_ARG;
-  if (misaligned(sep) || misaligned(x0) || misaligned(ws)) return ONETRANS_ERR_ALIGNMENT;
+  if (!seq_mlp || !seq_vec || !events || !x0 || !ws || (P.by_time && !times)) return ONETRANS_ERR_INVALID_ARG;
+  if (misaligned(seq_vec) || misaligned(x0) || misaligned(ws)) return ONETRANS_ERR_ALIGNMENT;
   const int n_seq = tc->n_seq;
   for (int i = 0; i < n_seq; ++i) {
     if ((rc = check_mlp(&seq_mlp[i]))) return rc;
-    if (tc->seq_len[i] > 0 && !events[i]) return ONETRANS_ERR_INVALID_ARG;
-    if (misaligned(events[i])) return ONETRANS_ERR_ALIGNMENT;
+    if (tc->seq_len[i] > 0 && (!events[i] || (P.by_time && !times[i]))) return ONETRANS_ERR_INVALID_ARG;
+    if (misaligned(events[i]) || (P.by_time && ((uintptr_t)times[i] & 7u))) return ONETRANS_ERR_ALIGNMENT;
   }
   if (D.lns > 0) {
     if ((rc = check_mlp(ns_mlp))) return rc;
@@ -784,21 +796,34 @@ int onetrans_tokenize(const onetrans_config *cfg, const onetrans_tokenizer_confi
     tiles += (g.m + rt - 1) / rt * (g.n / nt);
   };
   SepArgs sa{};
-  sa.sep = sep;
+  sa.sep = seq_vec;
   sa.x0 = x0;
   sa.sample_stride = sample;
   sa.d = D.d;
   sa.n_sep = n_seq;
   sa.batch = batch;
-  int off = 0;   // first row of sequence i inside the S-tokens
+  RankArgs ra{};
+  ra.n_seq = n_seq;
+  ra.total = P.l_s;
+  int off = 0;   // first row of sequence i inside the S-tokens (intent order)
   for (int i = 0; i < n_seq; ++i) {
     const int L = tc->seq_len[i], h = tc->seq_hidden[i], m = batch * L;
     const onetrans_mlp_weights &p = seq_mlp[i];
-    // MLP_i, layer 1: events -> hidden (GELU); layer 2: hidden -> rows off..off+L-1 of each sample
+    // MLP_i, layer 1: events -> hidden (GELU); layer 2: hidden -> rows off..off+L-1 of each sample,
+    // or, merged by time, to each event's ranked row plus the type embedding
     add(l1, tiles1, LinGroup{events[i], tc->seq_dim[i], p.w1, p.b1, w + P.hid[i], h, 0, 1, m, h, tc->seq_dim[i], 1, 0});
-    add(l2, tiles2, LinGroup{w + P.hid[i], h, p.w2, p.b2, x + (size_t)off * d * D.esz, sample, d, L, m, D.d, h, 0, 0});
-    sa.sep_row[i] = off + L;
-    off += L + 1;
+    if (P.by_time) {
+      int *pos = (int *)(w + P.pos[i]);
+      ra.t[i] = (const long long *)times[i];
+      ra.pos[i] = pos;
+      ra.len[i] = L;
+      add(l2, tiles2, LinGroup{w + P.hid[i], h, p.w2, p.b2, x, sample, d, L, m, D.d, h, 0, 0, pos,
+                               (const char *)seq_vec + (size_t)i * d * D.esz});
+    } else {
+      add(l2, tiles2, LinGroup{w + P.hid[i], h, p.w2, p.b2, x + (size_t)off * d * D.esz, sample, d, L, m, D.d, h, 0, 0});
+      sa.sep_row[i] = off + L;
+      off += L + 1;
+    }
   }
   if (D.lns > 0) {
     // Auto-Split: one row per sample, its l_ns * d outputs are the sample's NS rows in order
@@ -808,11 +833,13 @@ int onetrans_tokenize(const onetrans_config *cfg, const onetrans_tokenizer_confi
     add(l2, tiles2, LinGroup{w + P.hid[n_seq], h, ns_mlp->w2, ns_mlp->b2, x + (size_t)P.l_s * d * D.esz, sample, 0, 1,
                              batch, D.lns * D.d, h, 0, 0});
   }
+  if (P.by_time && timed(ONETRANS_K_MERGE, stream, [&] { return launch_rank(ra, batch, stream); }) != hipSuccess)
+    return ONETRANS_ERR_HIP;
   if (tiles1 > 0 && timed(ONETRANS_K_LIN, stream, [&] { return launch_lin(D.dt, l1, tiles1, stream); }) != hipSuccess)
     return ONETRANS_ERR_HIP;
   if (tiles2 > 0 && timed(ONETRANS_K_LIN, stream, [&] { return launch_lin(D.dt, l2, tiles2, stream); }) != hipSuccess)
     return ONETRANS_ERR_HIP;
-  if (timed(ONETRANS_K_SEP, stream, [&] { return launch_sep(D.dt, sa, stream); }) != hipSuccess)
+  if (!P.by_time && timed(ONETRANS_K_MERGE, stream, [&] { return launch_sep(D.dt, sa, stream); }) != hipSuccess)
     return ONETRANS_ERR_HIP;
   return ONETRANS_OK;
 }

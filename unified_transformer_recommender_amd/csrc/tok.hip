@@ -7,7 +7,9 @@
 // once per layer for every MLP together:
 //   launch 1: H_i = GELU(E_i W1_i^T + b1_i) for every sequence type, and the same for NS;
 //   launch 2: rows of X(0) = H_i W2_i^T + b2_i, written straight into their merged positions;
-// plus a copy of the [SEP] rows into theirs. GELU: the shared erf-form evaluations (bf16: the fitted
+// plus a copy of the [SEP] rows into theirs. With the timestamp-aware merge, rank_kernel first finds
+// every event's row in time order, and launch 2 writes each row there and adds its type's embedding
+// instead. GELU: the shared erf-form evaluations (bf16: the fitted
 // sigmoid form, whose error is below the bf16 rounding of the hidden activation it produces).
 //
 // Work unit: one workgroup of LIN_NW waves computes a tile of LIN_NW * 32 rows by LIN_NT output
@@ -52,7 +54,8 @@ __device__ __forceinline__ int xcd_tile(int b, int n) {
   return b < 8 * per ? (b % 8) * per + b / 8 : b;
 }
 
-template <typename T>
+// MAP: some group of the launch has a row map and a second bias (layer 2 of the time merge).
+template <typename T, bool MAP>
 __global__ __launch_bounds__(LIN_NW * 64, 2) void lin_kernel(const LinArgs a) {
   using MM = Mma<T>;
   using TS = TileStage<T>;
@@ -110,25 +113,30 @@ __global__ __launch_bounds__(LIN_NW * 64, 2) void lin_kernel(const LinArgs a) {
   };
   constexpr int PER_CHUNK = 6;   // direct-to-LDS loads per wave and chunk
 
-  // bias of this lane's accumulator rows, loaded before the first direct-to-LDS load so that it
-  // is not counted among the loads the chunk waits below leave outstanding
-  const T *bias = (const T *)G.b + n0;
-  float bv[NTT][16];
+  // bias (plus the second bias) of this lane's accumulator rows, loaded before the first
+  // direct-to-LDS load so that they are not counted among the loads the chunk waits below leave
+  // outstanding
+  float bv[NTT][16] = {};
+  auto load_bias = [&](const void *src, float (&out)[NTT][16]) {
+    const T *bias = (const T *)src + n0;
 #pragma unroll
-  for (int t = 0; t < NTT; ++t)
+    for (int t = 0; t < NTT; ++t)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const T *bp = bias + t * 32 + 8 * j + 4 * g;   // acc_row(4 j + i, g) = 8 j + 4 g + i
-      if constexpr (ESZ == 2) {
-        const bf16x4 b4 = *(const bf16x4 *)bp;
+      for (int j = 0; j < 4; ++j) {
+        const T *bp = bias + t * 32 + 8 * j + 4 * g;   // acc_row(4 j + i, g) = 8 j + 4 g + i
+        if constexpr (ESZ == 2) {
+          const bf16x4 b4 = *(const bf16x4 *)bp;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bv[t][4 * j + i] = (float)b4[i];
-      } else {
-        const f32x4 b4 = *(const f32x4 *)bp;
+          for (int i = 0; i < 4; ++i) out[t][4 * j + i] += (float)b4[i];
+        } else {
+          const f32x4 b4 = *(const f32x4 *)bp;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bv[t][4 * j + i] = b4[i];
+          for (int i = 0; i < 4; ++i) out[t][4 * j + i] += b4[i];
+        }
       }
-    }
+  };
+  load_bias(G.b, bv);
+  if (MAP && G.b_add) load_bias(G.b_add, bv);   // only on layers without activation
   asm volatile("" ::: "memory");
 
   f32x16 acc[NTT];
@@ -194,8 +202,8 @@ __global__ __launch_bounds__(LIN_NW * 64, 2) void lin_kernel(const LinArgs a) {
       const int m = m0 + tok;
       const u32x4 piece = TS::get(stg, k, lane);
       if (m < G.m) {
-        T *dst = (T *)G.y + (long long)(m / G.y_rps) * G.y_ss + (long long)(m % G.y_rps) * G.y_rs + n0 + t * 32 +
-                 TS::feature(lane);
+        const int r = MAP && G.y_row ? G.y_row[m] : m % G.y_rps;
+        T *dst = (T *)G.y + (long long)(m / G.y_rps) * G.y_ss + (long long)r * G.y_rs + n0 + t * 32 + TS::feature(lane);
         st16(dst, piece);
       }
     }
@@ -219,16 +227,88 @@ __global__ __launch_bounds__(256) void sep_kernel(const SepArgs a) {
   st16(dst, ld16(src));
 }
 
+// One workgroup per sample. The sample's timestamps go to LDS; an event's row is the number of the
+// sample's events with a smaller key (time, type, position). When every type's timestamps are
+// non-decreasing (the usual case: a behaviour log is chronological), that count is, per other type
+// j, a binary search: the events of an earlier type j < i at times <= t, of a later type at times
+// < t, plus the event's own position. Otherwise the workgroup counts by comparing with every event
+// (O(n^2), exact for any order). Either way the rows are a permutation of 0..total-1.
+__global__ __launch_bounds__(256) void rank_kernel(const RankArgs a) {
+  extern __shared__ long long s_t[];
+  __shared__ int s_unsorted;
+  const long long b = blockIdx.x;
+  if (threadIdx.x == 0) s_unsorted = 0;
+  int off = 0;
+  for (int i = 0; i < a.n_seq; ++i) {
+    const long long *src = a.t[i] + b * a.len[i];
+    for (int l = threadIdx.x; l < a.len[i]; l += 256) s_t[off + l] = src[l];
+    off += a.len[i];
+  }
+  __syncthreads();
+  off = 0;
+  int bad = 0;
+  for (int i = 0; i < a.n_seq; ++i) {
+    for (int l = 1 + threadIdx.x; l < a.len[i]; l += 256) bad |= s_t[off + l - 1] > s_t[off + l];
+    off += a.len[i];
+  }
+  if (bad) atomicOr(&s_unsorted, 1);
+  __syncthreads();
+  const bool sorted = s_unsorted == 0;
+  off = 0;
+  for (int i = 0; i < a.n_seq; ++i) {
+    for (int l = threadIdx.x; l < a.len[i]; l += 256) {
+      const int e = off + l;
+      const long long t = s_t[e];
+      int r = 0;
+      if (sorted) {
+        r = l;
+        int o = 0;
+        for (int j = 0; j < a.n_seq; ++j) {
+          if (j != i) {
+            // first position in type j whose time is > t (j < i) or >= t (j > i)
+            int lo = 0, hi = a.len[j];
+            while (lo < hi) {
+              const int mid = (lo + hi) >> 1;
+              const long long v = s_t[o + mid];
+              if (j < i ? v <= t : v < t) lo = mid + 1;
+              else hi = mid;
+            }
+            r += lo;
+          }
+          o += a.len[j];
+        }
+      } else {
+        for (int u = 0; u < a.total; ++u) {
+          const long long v = s_t[u];
+          r += (v < t) | ((v == t) & (u < e));
+        }
+      }
+      a.pos[i][b * a.len[i] + l] = r;
+    }
+    off += a.len[i];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_rank(const RankArgs &a, int batch, hipStream_t s) {
+  hipLaunchKernelGGL(rank_kernel, dim3(batch), dim3(256), (size_t)a.total * sizeof(long long), s, a);
+  return hipGetLastError();
+}
 
 int lin_rows_per_tile() { return LIN_NW * 32; }
 int lin_features_per_tile() { return LIN_NT; }
 
 hipError_t launch_lin(int dtype, const LinArgs &a, int grid, hipStream_t s) {
-  if (dtype == 1)
-    hipLaunchKernelGGL(lin_kernel<bf16>, dim3(grid), dim3(LIN_NW * 64), 0, s, a);
-  else
-    hipLaunchKernelGGL(lin_kernel<float>, dim3(grid), dim3(LIN_NW * 64), 0, s, a);
+  bool map = false;
+  for (int i = 0; i < a.n_groups; ++i) map |= a.g[i].y_row != nullptr || a.g[i].b_add != nullptr;
+  if (dtype == 1) {
+    if (map) hipLaunchKernelGGL((lin_kernel<bf16, true>), dim3(grid), dim3(LIN_NW * 64), 0, s, a);
+    else hipLaunchKernelGGL((lin_kernel<bf16, false>), dim3(grid), dim3(LIN_NW * 64), 0, s, a);
+  } else {
+    if (map) hipLaunchKernelGGL((lin_kernel<float, true>), dim3(grid), dim3(LIN_NW * 64), 0, s, a);
+    else hipLaunchKernelGGL((lin_kernel<float, false>), dim3(grid), dim3(LIN_NW * 64), 0, s, a);
+  }
   return hipGetLastError();
 }
 
