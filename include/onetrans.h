@@ -110,6 +110,10 @@ size_t onetrans_kv_cache_bytes(const onetrans_config *cfg, int n_users, int capa
 /* Monolithic forward of the block stack (sections 7.5.1-7.5.2) over `batch` independent samples.
  *   x0  [batch][l_s + l_ns][d] storage dtype: S rows then NS rows of each sample.
  *   out [batch][q_last + l_ns][d] fp32: final block rows (tail S rows then NS rows).
+ * A batch of 64 or more samples runs as two halves, the second on a stream the library creates
+ * once per device (default priority); it forks from and joins back into `stream` with events, so
+ * the call is still ordered on `stream` alone. Concurrent calls from several host threads on one
+ * device are not supported (they share that stream's fork/join events).
  * Errors: INVALID_ARG, SHAPE, UNSUPPORTED, WORKSPACE, ALIGNMENT, HIP. */
 int onetrans_forward(const onetrans_config *cfg, const onetrans_block_weights *blk /* host [n_blocks] */,
                      const void *x0, int batch, int l_s, void *out, void *ws, size_t ws_bytes,
@@ -222,6 +226,12 @@ int onetrans_tokenize(const onetrans_config *cfg, const onetrans_tokenizer_confi
                       const onetrans_mlp_weights *ns_mlp, const void *const *events,
                       const void *const *times, const void *ns_feat, int batch, void *x0, void *ws,
                       size_t ws_bytes, hipStream_t stream);
+
+/* Streams of onetrans_forward: 2 (default) splits batches of 64 or more samples into two halves on
+ * two streams; 1 runs every batch on the caller's stream alone (one kernel at a time, as a
+ * per-kernel profile needs). Results are identical either way; the workspace size does not change.
+ * Process-wide setting. Returns INVALID_ARG for other values. */
+int onetrans_set_forward_streams(int n);
 
 /* Kernel classes of the per-launch timing below. */
 typedef enum {

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert "onetrans_forward" in names and "onetrans_tokenize" in names and len(names) == 12
+    assert "onetrans_forward" in names and "onetrans_tokenize" in names and len(names) == 13
     lib = L.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -254,6 +254,20 @@ def test_tokenize_validation_errors():
     assert call(tc=_tok_cfg(merge=3)) == L.ERR_INVALID_ARG
     # an empty sequence needs no event buffer
     assert call(tc=_tok_cfg(lens=(15, 0)), events=(ctypes.c_void_p * 2)(FAKE, None), wsb=64) == L.ERR_WORKSPACE
+
+
+def test_forward_workspace_covers_the_split():
+    """Batches of 64+ run as two halves: the workspace holds two half-batch layouts, which also covers
+    the single-stream layout of the whole batch."""
+    lib = L.lib()
+    c = _cfg()
+    one = lambda B: lib.onetrans_workspace_bytes(ctypes.byref(c), L.OP_FORWARD, B, 120, 0, 0)
+    assert one(64) == 2 * one(32)
+    assert one(65) == 2 * one(33)
+    assert one(65) >= one(63)
+    assert lib.onetrans_set_forward_streams(3) == L.ERR_INVALID_ARG
+    assert lib.onetrans_set_forward_streams(0) == L.ERR_INVALID_ARG
+    assert lib.onetrans_set_forward_streams(2) == L.OK
 
 
 def test_status_strings():

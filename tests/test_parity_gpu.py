@@ -271,3 +271,28 @@ def test_gpu_two_stage_matches_gpu_forward():
     fw = ob.onetrans_forward(mdl, dev(x0, mdl)).cpu().numpy()
     ns = fw[:, -w.model.l_ns:].reshape(sc.shape)
     assert rel_err(sc, ns) <= 1e-5
+
+
+def test_forward_two_streams_equal_one_stream():
+    """A batch of 64+ runs as two halves on two streams: bit-identical to one stream, and correct on
+    both sides of the split (samples 34 and 35 of 70)."""
+    w = replace(synth.test_workload("tiny3_fwd", "bf16"), batch=70)
+    say(f"[forward two streams] {w.key} B={w.batch}")
+    mdl = model(w)
+    x = synth.forward_batch(w)
+    xd = dev(x, mdl)
+    try:
+        ob.set_forward_streams(1)
+        one = ob.onetrans_forward(mdl, xd)
+        torch.cuda.synchronize()
+        ob.set_forward_streams(2)
+        two = ob.onetrans_forward(mdl, xd)
+        torch.cuda.synchronize()
+    finally:
+        ob.set_forward_streams(2)
+    assert torch.equal(one, two)
+    got = two.cpu().numpy()
+    for b in (0, 34, 35, 69):
+        e = rel_err(got[b], O.forward(x[b], weights(w.model), w.model, w.s_queries))
+        say(f"  sample {b}: err {e:.3e}")
+        assert e <= TOL["bf16"], (b, e)

@@ -282,6 +282,11 @@ def onetrans_tokenize(tok: Tokenizer, events: Sequence[torch.Tensor], ns_feat: O
     return x0
 
 
+def set_forward_streams(n: int) -> None:
+    """Streams of onetrans_forward: 2 (default) splits batches of 64+ samples over two streams, 1 does not."""
+    L.check(L.lib().onetrans_set_forward_streams(int(n)), "onetrans_set_forward_streams")
+
+
 def timing_enable(on: bool = True) -> None:
     """Bracket every library kernel launch with hipEvents on its stream (tracing aid)."""
     L.check(L.lib().onetrans_timing_enable(1 if on else 0), "onetrans_timing_enable")

@@ -442,43 +442,37 @@ int check_mlp(const onetrans_mlp_weights *m) {
   return ONETRANS_OK;
 }
 
-}  // namespace
+// ---- forward over two streams -------------------------------------------------------------------
+// Batches of at least FORWARD_SPLIT_MIN samples run as two halves on the caller's stream and a
+// library-owned stream of the same device (default priority), forked and joined with events. The
+// workspace is always sized for the split (it also holds the whole batch's single-stream layout).
+constexpr int FORWARD_SPLIT_MIN = 64;
+int g_forward_streams = 2;
+inline int ws_parts(int batch) { return batch >= FORWARD_SPLIT_MIN ? 2 : 1; }
+inline int forward_parts(int batch) { return g_forward_streams == 2 ? ws_parts(batch) : 1; }
 
-extern "C" {
+struct Side {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+Side g_side[64];
 
-size_t onetrans_workspace_bytes(const onetrans_config *cfg, int op, int n_seq, int l_s, int n_cand, int d_l) {
-  Dims D;
-  if (check_cfg(cfg, D)) return 0;
-  size_t n, tin, rq;
-  bool kv;
-  if (!ws_dims(cfg, D, op, n_seq, l_s, n_cand, d_l, n, tin, rq, kv)) return 0;
-  if ((op == ONETRANS_OP_FORWARD || op == ONETRANS_OP_PREFILL) && check_schedule(cfg, l_s)) return 0;
-  return ws_layout(D, n, tin, rq, kv).total;
+int side_streams(Side *&out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+  Side &sd = g_side[dev];
+  if (!sd.s) {
+    if (hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) != hipSuccess) return 1;
+    if (hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) != hipSuccess) return 1;
+    if (hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) != hipSuccess) return 1;
+  }
+  out = &sd;
+  return 0;
 }
 
-size_t onetrans_kv_cache_bytes(const onetrans_config *cfg, int n_users, int capacity) {
-  Dims D;
-  if (check_cfg(cfg, D) || n_users < 1 || capacity < 1) return 0;
-  return (size_t)n_users * D.N * D.H * (size_t)capacity * D.dh * D.esz;
-}
-
-int onetrans_forward(const onetrans_config *cfg, const onetrans_block_weights *blk, const void *x0, int batch,
-                     int l_s, void *out, void *ws, size_t ws_bytes, hipStream_t stream) {
-  Dims D;
+int forward_run(const Dims &D, const onetrans_config *cfg, const onetrans_block_weights *blk, const void *x0,
+                int batch, int l_s, void *out, char *w, const Ws &L, hipStream_t stream) {
   int rc;
-  if ((rc = check_cfg(cfg, D))) return rc;
-  if (batch < 1 || l_s < 1) return ONETRANS_ERR_SHAPE;
-  if ((rc = check_schedule(cfg, l_s))) return rc;
-  if ((rc = check_weights(blk, D))) return rc;
-  if (!x0 || !out) return ONETRANS_ERR_INVALID_ARG;
-  if (misaligned(x0) || misaligned(out)) return ONETRANS_ERR_ALIGNMENT;
-  size_t n, tin, rq;
-  bool kv;
-  ws_dims(cfg, D, ONETRANS_OP_FORWARD, batch, l_s, 0, 0, n, tin, rq, kv);
-  const Ws L = ws_layout(D, n, tin, rq, kv);
-  if ((rc = check_ws(D, L, ws, ws_bytes))) return rc;
-
-  char *w = (char *)ws;
   const int d = D.d, H = D.H, dh = D.dh;
   int s = l_s;
   RowView x{const_cast<void *>(x0), (long long)(l_s + D.lns) * d, 0, d};
@@ -518,6 +512,67 @@ int onetrans_forward(const onetrans_config *cfg, const onetrans_block_weights *b
     x_f32 = 1;
     s = q;
   }
+  return ONETRANS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t onetrans_workspace_bytes(const onetrans_config *cfg, int op, int n_seq, int l_s, int n_cand, int d_l) {
+  Dims D;
+  if (check_cfg(cfg, D)) return 0;
+  size_t n, tin, rq;
+  bool kv;
+  if (!ws_dims(cfg, D, op, n_seq, l_s, n_cand, d_l, n, tin, rq, kv)) return 0;
+  if ((op == ONETRANS_OP_FORWARD || op == ONETRANS_OP_PREFILL) && check_schedule(cfg, l_s)) return 0;
+  if (op == ONETRANS_OP_FORWARD) {
+    const int parts = ws_parts(n_seq);
+    return ws_layout(D, (n_seq + parts - 1) / parts, tin, rq, kv).total * parts;
+  }
+  return ws_layout(D, n, tin, rq, kv).total;
+}
+
+size_t onetrans_kv_cache_bytes(const onetrans_config *cfg, int n_users, int capacity) {
+  Dims D;
+  if (check_cfg(cfg, D) || n_users < 1 || capacity < 1) return 0;
+  return (size_t)n_users * D.N * D.H * (size_t)capacity * D.dh * D.esz;
+}
+
+int onetrans_forward(const onetrans_config *cfg, const onetrans_block_weights *blk, const void *x0, int batch,
+                     int l_s, void *out, void *ws, size_t ws_bytes, hipStream_t stream) {
+  Dims D;
+  int rc;
+  if ((rc = check_cfg(cfg, D))) return rc;
+  if (batch < 1 || l_s < 1) return ONETRANS_ERR_SHAPE;
+  if ((rc = check_schedule(cfg, l_s))) return rc;
+  if ((rc = check_weights(blk, D))) return rc;
+  if (!x0 || !out) return ONETRANS_ERR_INVALID_ARG;
+  if (misaligned(x0) || misaligned(out)) return ONETRANS_ERR_ALIGNMENT;
+  size_t n, tin, rq;
+  bool kv;
+  ws_dims(cfg, D, ONETRANS_OP_FORWARD, batch, l_s, 0, 0, n, tin, rq, kv);
+  const int wp = ws_parts(batch), parts = forward_parts(batch);
+  if (misaligned(ws)) return ONETRANS_ERR_ALIGNMENT;
+  if (!ws) return ONETRANS_ERR_INVALID_ARG;
+  if (ws_bytes < ws_layout(D, (batch + wp - 1) / wp, tin, rq, kv).total * wp) return ONETRANS_ERR_WORKSPACE;
+  const int b0 = (batch + parts - 1) / parts;
+  const Ws L = ws_layout(D, b0, tin, rq, kv);
+  if (parts == 1) return forward_run(D, cfg, blk, x0, batch, l_s, out, (char *)ws, L, stream);
+  // Two halves of the batch on two streams (samples are independent): each half's small late
+  // blocks and launch gaps overlap the other half's kernels. The halves join back into `stream`.
+  Side *sd = nullptr;
+  if (side_streams(sd)) return ONETRANS_ERR_HIP;
+  const size_t in_row = (size_t)(l_s + D.lns) * D.d * D.esz;
+  const size_t out_row = (size_t)(cfg->s_queries[D.N - 1] + D.lns) * D.d * 4;
+  if (hipEventRecord(sd->fork, stream) != hipSuccess || hipStreamWaitEvent(sd->s, sd->fork, 0) != hipSuccess)
+    return ONETRANS_ERR_HIP;
+  if ((rc = forward_run(D, cfg, blk, x0, b0, l_s, out, (char *)ws, L, stream))) return rc;
+  if ((rc = forward_run(D, cfg, blk, (const char *)x0 + b0 * in_row, batch - b0, l_s, (char *)out + b0 * out_row,
+                        (char *)ws + L.total, L, sd->s)))
+    return rc;
+  if (hipEventRecord(sd->join, sd->s) != hipSuccess || hipStreamWaitEvent(stream, sd->join, 0) != hipSuccess)
+    return ONETRANS_ERR_HIP;
   return ONETRANS_OK;
 }
 
@@ -859,6 +914,12 @@ const char *onetrans_status_string(int status) {
 }
 
 const char *onetrans_version(void) { return "onetrans-gfx950 0.1"; }
+
+int onetrans_set_forward_streams(int n) {
+  if (n != 1 && n != 2) return ONETRANS_ERR_INVALID_ARG;
+  g_forward_streams = n;
+  return ONETRANS_OK;
+}
 
 int onetrans_timing_enable(int on) {
   g_timing = on != 0;
