@@ -457,9 +457,17 @@ struct Side {
 };
 Side g_side[64];
 
-int side_streams(Side *&out) {
+// The side stream of the current device, created on first use. Returns 1 on a HIP error, and -1
+// when `stream` belongs to another device than the current one (the caller then stays on one
+// stream: the side stream and its events live on the current device).
+int side_streams(hipStream_t stream, Side *&out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+  if (stream) {
+    hipDevice_t sdev = 0;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return 1;
+    if ((int)sdev != dev) return -1;
+  }
   Side &sd = g_side[dev];
   if (!sd.s) {
     if (hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) != hipSuccess) return 1;
@@ -558,11 +566,12 @@ int onetrans_forward(const onetrans_config *cfg, const onetrans_block_weights *b
   if (ws_bytes < ws_layout(D, (batch + wp - 1) / wp, tin, rq, kv).total * wp) return ONETRANS_ERR_WORKSPACE;
   const int b0 = (batch + parts - 1) / parts;
   const Ws L = ws_layout(D, b0, tin, rq, kv);
-  if (parts == 1) return forward_run(D, cfg, blk, x0, batch, l_s, out, (char *)ws, L, stream);
+  Side *sd = nullptr;
+  const int side = parts == 2 ? side_streams(stream, sd) : -1;
+  if (side > 0) return ONETRANS_ERR_HIP;
+  if (side < 0) return forward_run(D, cfg, blk, x0, batch, l_s, out, (char *)ws, ws_layout(D, batch, tin, rq, kv), stream);
   // Two halves of the batch on two streams (samples are independent): each half's small late
   // blocks and launch gaps overlap the other half's kernels. The halves join back into `stream`.
-  Side *sd = nullptr;
-  if (side_streams(sd)) return ONETRANS_ERR_HIP;
   const size_t in_row = (size_t)(l_s + D.lns) * D.d * D.esz;
   const size_t out_row = (size_t)(cfg->s_queries[D.N - 1] + D.lns) * D.d * 4;
   if (hipEventRecord(sd->fork, stream) != hipSuccess || hipStreamWaitEvent(sd->s, sd->fork, 0) != hipSuccess)
