@@ -46,8 +46,9 @@ def parse():
     p.add_argument("--dtype", default=None, choices=[None, "bf16", "f32"])
     p.add_argument("--no-trace", action="store_true", help="no per-kernel events in the timed region")
     p.add_argument("--streams", type=int, default=2, choices=[1, 2],
-                   help="streams of onetrans_forward: 2 runs a batch as two concurrent halves (per-kernel "
-                        "timing then comes from a separate one-stream pass); 1 runs everything on one stream")
+                   help="streams of the batched calls: 2 runs a forward batch / an append's users as two "
+                        "concurrent halves (per-kernel timing then comes from a separate one-stream pass); 1 "
+                        "runs everything on one stream")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline (0: skip)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain elementwise copy of MIB MiB (fp32 negate: reads and writes MIB MiB "
@@ -238,7 +239,7 @@ def main():
     host_w = synth.make_weights(m)
     sched = w.s_queries if w.kind != "append" else (w.l_old,) * m.n_blocks
     model = ob.Model.from_host(m, sched, host_w, device=dev)
-    ob.set_forward_streams(a.streams)
+    ob.set_streams(a.streams)
 
     def up(x):
         return torch.from_numpy(np.ascontiguousarray(x)).to(dev, dtype=model.torch_dtype)
@@ -312,7 +313,7 @@ def main():
 
     # timed region. With two forward streams a launch's duration overlaps the other half's kernels,
     # so the per-kernel table (and the roofline) comes from a separate one-stream pass.
-    trace_in = not a.no_trace and not (w.kind == "forward" and a.streams == 2)
+    trace_in = not a.no_trace and not (w.kind in ("forward", "append") and a.streams == 2)
     ob.timing_enable(trace_in)
     total_ms = 0.0
     if w.kind == "append":
@@ -343,7 +344,7 @@ def main():
     ms_step = total_ms / a.steps
     if not trace_in:
         # per-kernel table from a separate traced pass (one stream) after the timed region
-        ob.set_forward_streams(1)
+        ob.set_streams(1)
         ob.timing_enable(True)
         for _ in range(a.steps):
             if w.kind == "append":
@@ -352,7 +353,7 @@ def main():
         torch.cuda.synchronize()
         ob.timing_enable(False)
         timing = ob.timing_read()
-        ob.set_forward_streams(a.streams)
+        ob.set_streams(a.streams)
     value = n_units / (ms_step * 1e-3)
 
     flops_unit = sum(classes.values())
@@ -419,7 +420,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "trace_in_timed_region": trace_in,
-        "forward_streams": a.streams if w.kind == "forward" else 1,
+        "streams": a.streams if w.kind in ("forward", "append") else 1,
         "kernel_table": "timed region" if trace_in else "separate one-stream pass",
         "setup_s": round(t_setup, 1),
         **extra,

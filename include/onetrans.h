@@ -156,6 +156,8 @@ int onetrans_score_candidates(const onetrans_config *cfg, const onetrans_block_w
  * append, so appending could not equal recomputation. cfg->s_queries is not read by this call.
  * Ragged users (cache->user_len set): L_old is user_len[u] for user u, and user_len[u] advances by
  * d_l (the lengths are read and advanced on the host at enqueue time).
+ * 16 or more users run as two halves on two streams, forked from and joined back into `stream`
+ * (see onetrans_forward for the stream's lifetime and thread-safety).
  *   x_new   [n_users][d_l][d] storage dtype.
  *   out_new [n_users][d_l][d] fp32 final rows of the new events, or NULL.
  * Errors: as forward, plus CACHE_CAPACITY (L_old + d_l > capacity for some user), UNSUPPORTED
@@ -227,11 +229,11 @@ int onetrans_tokenize(const onetrans_config *cfg, const onetrans_tokenizer_confi
                       const void *const *times, const void *ns_feat, int batch, void *x0, void *ws,
                       size_t ws_bytes, hipStream_t stream);
 
-/* Streams of onetrans_forward: 2 (default) splits batches of 64 or more samples into two halves on
- * two streams; 1 runs every batch on the caller's stream alone (one kernel at a time, as a
- * per-kernel profile needs). Results are identical either way; the workspace size does not change.
- * Process-wide setting. Returns INVALID_ARG for other values. */
-int onetrans_set_forward_streams(int n);
+/* Streams of the batched calls: 2 (default) runs a forward of 64 or more samples, and an append
+ * over 16 or more users, as two halves on two streams; 1 runs every call on the caller's stream
+ * alone (one kernel at a time, as a per-kernel profile needs). Results are identical either way;
+ * workspace sizes do not change. Process-wide setting. Returns INVALID_ARG for other values. */
+int onetrans_set_streams(int n);
 
 /* Kernel classes of the per-launch timing below. */
 typedef enum {

@@ -282,17 +282,57 @@ def test_forward_two_streams_equal_one_stream():
     x = synth.forward_batch(w)
     xd = dev(x, mdl)
     try:
-        ob.set_forward_streams(1)
+        ob.set_streams(1)
         one = ob.onetrans_forward(mdl, xd)
         torch.cuda.synchronize()
-        ob.set_forward_streams(2)
+        ob.set_streams(2)
         two = ob.onetrans_forward(mdl, xd)
         torch.cuda.synchronize()
     finally:
-        ob.set_forward_streams(2)
+        ob.set_streams(2)
     assert torch.equal(one, two)
     got = two.cpu().numpy()
     for b in (0, 34, 35, 69):
         e = rel_err(got[b], O.forward(x[b], weights(w.model), w.model, w.s_queries))
         say(f"  sample {b}: err {e:.3e}")
         assert e <= TOL["bf16"], (b, e)
+
+
+@pytest.mark.parametrize("ragged", [False, True])
+def test_append_two_streams_equal_one_stream(ragged):
+    """An append over 16+ users runs as two halves on two streams: the new rows and every cache row
+    are bit-identical to one stream; users on both sides of the split (8 and 9 of 17) match the
+    oracle."""
+    w = replace(synth.test_workload("tiny3_append", "bf16"), n_users=17, input_seed=2118)
+    m, ws = w.model, weights(w.model)
+    lens = [(5 * u) % (w.l_old + 1) for u in range(w.n_users)] if ragged else None
+    say(f"[append two streams] {w.key} users={w.n_users} ragged={ragged}")
+    mdl = model(w, s_queries=(w.l_old,) * m.n_blocks)
+    seq = synth.user_sequences(w)
+    old = np.ascontiguousarray(seq[:, : w.l_old])
+    new = np.ascontiguousarray(seq[:, w.l_old:])
+    res = []
+    try:
+        for n_streams in (1, 2):
+            ob.set_streams(n_streams)
+            cache = ob.KVCache(mdl, w.n_users, w.l_old + w.d_l, user_len=lens)
+            ob.onetrans_prefill_user(mdl, dev(old, mdl), cache)
+            out_new = torch.empty((w.n_users, w.d_l, m.d_model), dtype=torch.float32, device=mdl.device)
+            ob.onetrans_append_events(mdl, cache, dev(new, mdl), out_new)
+            torch.cuda.synchronize()
+            res.append((out_new.clone(), cache.k.clone(), cache.v.clone(), cache.lengths, cache.user_lengths))
+    finally:
+        ob.set_streams(2)
+    (o1, k1, v1, l1, u1), (o2, k2, v2, l2, u2) = res
+    assert torch.equal(o1, o2) and torch.equal(k1, k2) and torch.equal(v1, v2)
+    assert l1 == l2 and u1 == u2
+    for u in (8, 9):
+        n_old = lens[u] if ragged else w.l_old
+        if n_old:
+            oc, _ = O.prefill_user(old[u, :n_old], ws, m, (n_old,) * m.n_blocks)
+            _, ref_new = O.append_events(oc, new[u], ws, m)
+        else:
+            _, ref_new = O.prefill_user(new[u], ws, m, (w.d_l,) * m.n_blocks)
+        e = rel_err(o2[u].cpu().numpy(), ref_new)
+        say(f"  user {u} (L_old {n_old}): {e:.3e}")
+        assert e <= TOL["bf16"], (u, e)

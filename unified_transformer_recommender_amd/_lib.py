@@ -67,7 +67,7 @@ SIGNATURES = {
     "onetrans_tokenize": (c_int, [POINTER(Config), POINTER(TokenizerConfig), POINTER(MlpWeights), c_void_p,
                                   POINTER(MlpWeights), POINTER(c_void_p), POINTER(c_void_p), c_void_p, c_int,
                                   c_void_p, c_void_p, c_size_t, c_void_p]),
-    "onetrans_set_forward_streams": (c_int, [c_int]),
+    "onetrans_set_streams": (c_int, [c_int]),
     "onetrans_timing_enable": (c_int, [c_int]),
     "onetrans_timing_read": (c_int, [POINTER(ctypes.c_double), POINTER(ctypes.c_longlong)]),
     "onetrans_status_string": (c_char_p, [c_int]),

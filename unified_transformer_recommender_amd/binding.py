@@ -282,9 +282,10 @@ def onetrans_tokenize(tok: Tokenizer, events: Sequence[torch.Tensor], ns_feat: O
     return x0
 
 
-def set_forward_streams(n: int) -> None:
-    """Streams of onetrans_forward: 2 (default) splits batches of 64+ samples over two streams, 1 does not."""
-    L.check(L.lib().onetrans_set_forward_streams(int(n)), "onetrans_set_forward_streams")
+def set_streams(n: int) -> None:
+    """Streams of the batched calls: 2 (default) splits a forward of 64+ samples and an append over 16+
+    users into two halves on two streams; 1 does not."""
+    L.check(L.lib().onetrans_set_streams(int(n)), "onetrans_set_streams")
 
 
 def timing_enable(on: bool = True) -> None:

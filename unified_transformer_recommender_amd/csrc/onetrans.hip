@@ -442,14 +442,18 @@ int check_mlp(const onetrans_mlp_weights *m) {
   return ONETRANS_OK;
 }
 
-// ---- forward over two streams -------------------------------------------------------------------
-// Batches of at least FORWARD_SPLIT_MIN samples run as two halves on the caller's stream and a
-// library-owned stream of the same device (default priority), forked and joined with events. The
-// workspace is always sized for the split (it also holds the whole batch's single-stream layout).
+// ---- batches over two streams ---------------------------------------------------------------------
+// A forward batch of at least FORWARD_SPLIT_MIN samples, and an append over at least
+// APPEND_SPLIT_MIN users, run as two halves on the caller's stream and a library-owned stream of
+// the same device (default priority), forked and joined with events. The workspace is always sized
+// for the split (two half layouts also hold the whole batch's single-stream layout).
 constexpr int FORWARD_SPLIT_MIN = 64;
-int g_forward_streams = 2;
+constexpr int APPEND_SPLIT_MIN = 16;
+int g_streams = 2;
 inline int ws_parts(int batch) { return batch >= FORWARD_SPLIT_MIN ? 2 : 1; }
-inline int forward_parts(int batch) { return g_forward_streams == 2 ? ws_parts(batch) : 1; }
+inline int forward_parts(int batch) { return g_streams == 2 ? ws_parts(batch) : 1; }
+inline int append_ws_parts(int users) { return users >= APPEND_SPLIT_MIN ? 2 : 1; }
+inline int append_parts(int users) { return g_streams == 2 ? append_ws_parts(users) : 1; }
 
 struct Side {
   hipStream_t s = nullptr;
@@ -523,6 +527,58 @@ int forward_run(const Dims &D, const onetrans_config *cfg, const onetrans_block_
   return ONETRANS_OK;
 }
 
+// The append launch sequence for `n_users` users of `cache` (a view whose first user is the call's
+// first user), with workspace `w` laid out as L. l_old: cached rows (0 for ragged users, whose own
+// lengths come from cache->user_len).
+int append_run(const Dims &D, const onetrans_block_weights *blk, const onetrans_kv_cache *cache, const void *x_new,
+               int n_users, int d_l, void *out_new, char *w, const Ws &L, int l_old, hipStream_t stream) {
+  int rc;
+  const bool ragged = cache->user_len != nullptr;
+  if (ragged && (rc = upload_user_len(cache, n_users, w, L, stream))) return rc;
+  // ragged users: positions are relative to each user's own cached length, which the QKV kernel
+  // adds to the cache rows it writes and the attention to its query positions and key count
+  const int *shift = ragged ? (const int *)(w + L.seq) : nullptr;
+  const int d = D.d;
+  RowView x{const_cast<void *>(x_new), (long long)d_l * d, l_old, d};
+  int x_f32 = D.dt == ONETRANS_F32;
+  void *stats = nullptr;   // (mean, rstd) rows of x when the previous block wrote them
+  for (int n = 0; n < D.N; ++n) {
+    const bool last = n + 1 == D.N;
+    Step st{};
+    st.n_seq = n_users;
+    st.s = l_old + d_l;
+    st.q = d_l;
+    st.kv_t0 = l_old;
+    st.kv_n = d_l;
+    st.ns = 0;
+    st.in_t0 = l_old;
+    st.in_n = d_l;
+    st.x = x;
+    st.x_f32 = x_f32;
+    st.kS = cache_view(D, cache, cache->k, n);
+    st.vS = cache_view(D, cache, cache->v, n);
+    st.kN = st.kS;
+    st.vN = st.vS;
+    st.stage2 = 0;
+    st.n_pre = l_old + d_l;
+    st.kp = st.kS.base;
+    st.vp = st.vS.base;
+    st.pre_sb = st.kS.sb;
+    st.pre_sh = st.kS.sh;
+    st.out = RowView{last && out_new ? out_new : (void *)(w + L.x[n & 1]), (long long)d_l * d, l_old, d};
+    st.kv_shift = shift;
+    st.seq_shift = shift;
+    st.stats_in = stats;
+    st.stats_out = last ? nullptr : (void *)(w + L.st[n & 1]);
+    st.need_out = !last || out_new != nullptr;
+    if ((rc = run_step(D, blk[n], st, w, L, stream))) return rc;
+    x = RowView{w + L.x[n & 1], (long long)d_l * d, l_old, d};
+    stats = st.stats_out;
+    x_f32 = 1;
+  }
+  return ONETRANS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -534,8 +590,8 @@ size_t onetrans_workspace_bytes(const onetrans_config *cfg, int op, int n_seq, i
   bool kv;
   if (!ws_dims(cfg, D, op, n_seq, l_s, n_cand, d_l, n, tin, rq, kv)) return 0;
   if ((op == ONETRANS_OP_FORWARD || op == ONETRANS_OP_PREFILL) && check_schedule(cfg, l_s)) return 0;
-  if (op == ONETRANS_OP_FORWARD) {
-    const int parts = ws_parts(n_seq);
+  if (op == ONETRANS_OP_FORWARD || op == ONETRANS_OP_APPEND) {
+    const int parts = op == ONETRANS_OP_FORWARD ? ws_parts(n_seq) : append_ws_parts(n_seq);
     return ws_layout(D, (n_seq + parts - 1) / parts, tin, rq, kv).total * parts;
   }
   return ws_layout(D, n, tin, rq, kv).total;
@@ -759,52 +815,37 @@ int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weig
   size_t n, tin, rq;
   bool kv;
   ws_dims(cfg, D, ONETRANS_OP_APPEND, n_users, 0, 0, d_l, n, tin, rq, kv);
-  const Ws L = ws_layout(D, n, tin, rq, kv);
-  if ((rc = check_ws(D, L, ws, ws_bytes))) return rc;
-
-  char *w = (char *)ws;
-  if (ragged && (rc = upload_user_len(cache, n_users, w, L, stream))) return rc;
-  // ragged users: positions are relative to each user's own cached length, which the QKV kernel
-  // adds to the cache rows it writes and the attention to its query positions and key count
+  const int wp = append_ws_parts(n_users), parts = append_parts(n_users);
+  if (misaligned(ws)) return ONETRANS_ERR_ALIGNMENT;
+  if (!ws) return ONETRANS_ERR_INVALID_ARG;
+  if (ws_bytes < ws_layout(D, (n_users + wp - 1) / wp, tin, rq, kv).total * wp) return ONETRANS_ERR_WORKSPACE;
   const int l_old = ragged ? 0 : cache->layer_len[0];
-  const int *shift = ragged ? (const int *)(w + L.seq) : nullptr;
-  const int d = D.d;
-  RowView x{const_cast<void *>(x_new), (long long)d_l * d, l_old, d};
-  int x_f32 = D.dt == ONETRANS_F32;
-  void *stats = nullptr;   // (mean, rstd) rows of x when the previous block wrote them
-  for (int n = 0; n < D.N; ++n) {
-    const bool last = n + 1 == D.N;
-    Step st{};
-    st.n_seq = n_users;
-    st.s = l_old + d_l;
-    st.q = d_l;
-    st.kv_t0 = l_old;
-    st.kv_n = d_l;
-    st.ns = 0;
-    st.in_t0 = l_old;
-    st.in_n = d_l;
-    st.x = x;
-    st.x_f32 = x_f32;
-    st.kS = cache_view(D, cache, cache->k, n);
-    st.vS = cache_view(D, cache, cache->v, n);
-    st.kN = st.kS;
-    st.vN = st.vS;
-    st.stage2 = 0;
-    st.n_pre = l_old + d_l;
-    st.kp = st.kS.base;
-    st.vp = st.vS.base;
-    st.pre_sb = st.kS.sb;
-    st.pre_sh = st.kS.sh;
-    st.out = RowView{last && out_new ? out_new : (void *)(w + L.x[n & 1]), (long long)d_l * d, l_old, d};
-    st.kv_shift = shift;
-    st.seq_shift = shift;
-    st.stats_in = stats;
-    st.stats_out = last ? nullptr : (void *)(w + L.st[n & 1]);
-    st.need_out = !last || out_new != nullptr;
-    if ((rc = run_step(D, blk[n], st, w, L, stream))) return rc;
-    x = RowView{w + L.x[n & 1], (long long)d_l * d, l_old, d};
-    stats = st.stats_out;
-    x_f32 = 1;
+  Side *sd = nullptr;
+  const int side = parts == 2 ? side_streams(stream, sd) : -1;
+  if (side > 0) return ONETRANS_ERR_HIP;
+  if (side < 0) {
+    if ((rc = append_run(D, blk, cache, x_new, n_users, d_l, out_new, (char *)ws, ws_layout(D, n_users, tin, rq, kv),
+                         l_old, stream)))
+      return rc;
+  } else {
+    // two halves of the users on two streams (users are independent), joined back into `stream`
+    const int u0 = (n_users + 1) / 2;
+    const Ws L = ws_layout(D, u0, tin, rq, kv);
+    onetrans_kv_cache hb = *cache;   // the second half's users
+    const size_t user_bytes = (size_t)D.N * D.H * cache->capacity * D.dh * D.esz;
+    hb.k = (char *)cache->k + u0 * user_bytes;
+    hb.v = (char *)cache->v + u0 * user_bytes;
+    hb.n_users = cache->n_users - u0;
+    hb.user_len = ragged ? cache->user_len + u0 : nullptr;
+    if (hipEventRecord(sd->fork, stream) != hipSuccess || hipStreamWaitEvent(sd->s, sd->fork, 0) != hipSuccess)
+      return ONETRANS_ERR_HIP;
+    if ((rc = append_run(D, blk, cache, x_new, u0, d_l, out_new, (char *)ws, L, l_old, stream))) return rc;
+    const size_t in_user = (size_t)d_l * D.d * D.esz, out_user = (size_t)d_l * D.d * 4;
+    if ((rc = append_run(D, blk, &hb, (const char *)x_new + u0 * in_user, n_users - u0, d_l,
+                         out_new ? (char *)out_new + u0 * out_user : nullptr, (char *)ws + L.total, L, l_old, sd->s)))
+      return rc;
+    if (hipEventRecord(sd->join, sd->s) != hipSuccess || hipStreamWaitEvent(stream, sd->join, 0) != hipSuccess)
+      return ONETRANS_ERR_HIP;
   }
   if (ragged) {
     int longest = 0;
@@ -924,9 +965,9 @@ const char *onetrans_status_string(int status) {
 
 const char *onetrans_version(void) { return "onetrans-gfx950 0.1"; }
 
-int onetrans_set_forward_streams(int n) {
+int onetrans_set_streams(int n) {
   if (n != 1 && n != 2) return ONETRANS_ERR_INVALID_ARG;
-  g_forward_streams = n;
+  g_streams = n;
   return ONETRANS_OK;
 }
 
