@@ -313,7 +313,7 @@ def main():
 
     # timed region. With two forward streams a launch's duration overlaps the other half's kernels,
     # so the per-kernel table (and the roofline) comes from a separate one-stream pass.
-    trace_in = not a.no_trace and not (w.kind in ("forward", "append") and a.streams == 2)
+    trace_in = not a.no_trace and a.streams == 1
     ob.timing_enable(trace_in)
     total_ms = 0.0
     if w.kind == "append":
@@ -420,7 +420,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "trace_in_timed_region": trace_in,
-        "streams": a.streams if w.kind in ("forward", "append") else 1,
+        "streams": a.streams,
         "kernel_table": "timed region" if trace_in else "separate one-stream pass",
         "setup_s": round(t_setup, 1),
         **extra,

@@ -141,8 +141,9 @@ int onetrans_prefill_user(const onetrans_config *cfg, const onetrans_block_weigh
  * token-specific FFN.
  *   x_ns   [n_users][n_cand][l_ns][d] storage dtype.
  *   out_ns [n_users][n_cand][l_ns][d] fp32 final NS rows.
- * The cache is read only. Errors: as forward, plus SHAPE if n_users > cache->n_users or a
- * layer_len is out of range. */
+ * The cache is read only. 16 or more users run as two halves on two streams, forked from and
+ * joined back into `stream` (see onetrans_forward). Errors: as forward, plus SHAPE if
+ * n_users > cache->n_users or a layer_len is out of range. */
 int onetrans_score_candidates(const onetrans_config *cfg, const onetrans_block_weights *blk,
                               const onetrans_kv_cache *cache, const void *x_ns, int n_users,
                               int n_cand, void *out_ns, void *ws, size_t ws_bytes,
@@ -229,8 +230,8 @@ int onetrans_tokenize(const onetrans_config *cfg, const onetrans_tokenizer_confi
                       const void *const *times, const void *ns_feat, int batch, void *x0, void *ws,
                       size_t ws_bytes, hipStream_t stream);
 
-/* Streams of the batched calls: 2 (default) runs a forward of 64 or more samples, and an append
- * over 16 or more users, as two halves on two streams; 1 runs every call on the caller's stream
+/* Streams of the batched calls: 2 (default) runs a forward of 64 or more samples, and an append or
+ * a Stage II call over 16 or more users, as two halves on two streams; 1 runs every call on the caller's stream
  * alone (one kernel at a time, as a per-kernel profile needs). Results are identical either way;
  * workspace sizes do not change. Process-wide setting. Returns INVALID_ARG for other values. */
 int onetrans_set_streams(int n);

@@ -336,3 +336,38 @@ def test_append_two_streams_equal_one_stream(ragged):
         e = rel_err(o2[u].cpu().numpy(), ref_new)
         say(f"  user {u} (L_old {n_old}): {e:.3e}")
         assert e <= TOL["bf16"], (u, e)
+
+
+@pytest.mark.parametrize("ragged", [False, True])
+def test_score_two_streams_equal_one_stream(ragged):
+    """Stage II over 16+ users runs as two halves on two streams: bit-identical to one stream, and
+    users on both sides of the split (8 and 9 of 17) match the oracle."""
+    w = replace(synth.test_workload("tiny3_two_stage", "bf16"), n_users=17, n_cand=3, input_seed=2119)
+    m, ws = w.model, weights(w.model)
+    say(f"[score two streams] {w.key} users={w.n_users} ragged={ragged}")
+    sched = (w.l_s,) * m.n_blocks if ragged else w.s_queries
+    lens = [(7 * u) % (w.l_s + 1) for u in range(w.n_users)] if ragged else None
+    mdl = model(w, s_queries=sched)
+    xs = synth.user_sequences(w)
+    xn = synth.candidate_batch(w)
+    cache = ob.KVCache(mdl, w.n_users, w.l_s, user_len=lens)
+    ob.onetrans_prefill_user(mdl, dev(xs, mdl), cache)
+    res = []
+    try:
+        for n_streams in (1, 2):
+            ob.set_streams(n_streams)
+            res.append(ob.onetrans_score_candidates(mdl, cache, dev(xn, mdl)))
+            torch.cuda.synchronize()
+    finally:
+        ob.set_streams(2)
+    assert torch.equal(res[0], res[1])
+    got = res[1].cpu().numpy()
+    for u in (8, 9):
+        n_old = lens[u] if ragged else w.l_s
+        if ragged and n_old == 0:
+            continue
+        oc, _ = O.prefill_user(xs[u, :n_old], ws, m, (n_old,) * m.n_blocks if ragged else w.s_queries)
+        for c in range(w.n_cand):
+            e = rel_err(got[u, c], O.score_candidate(oc, xn[u, c], ws, m))
+            say(f"  user {u} cand {c}: {e:.3e}")
+            assert e <= TOL["bf16"], (u, c, e)

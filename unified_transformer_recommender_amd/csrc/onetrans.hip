@@ -443,8 +443,8 @@ int check_mlp(const onetrans_mlp_weights *m) {
 }
 
 // ---- batches over two streams ---------------------------------------------------------------------
-// A forward batch of at least FORWARD_SPLIT_MIN samples, and an append over at least
-// APPEND_SPLIT_MIN users, run as two halves on the caller's stream and a library-owned stream of
+// A forward batch of at least FORWARD_SPLIT_MIN samples, and an append or a Stage II call over at
+// least APPEND_SPLIT_MIN users, run as two halves on the caller's stream and a library-owned stream of
 // the same device (default priority), forked and joined with events. The workspace is always sized
 // for the split (two half layouts also hold the whole batch's single-stream layout).
 constexpr int FORWARD_SPLIT_MIN = 64;
@@ -579,6 +579,61 @@ int append_run(const Dims &D, const onetrans_block_weights *blk, const onetrans_
   return ONETRANS_OK;
 }
 
+// The Stage II launch sequence for `n_users` users of `cache` (a view whose first user is the
+// call's first user), with workspace `w` laid out as L.
+int score_run(const Dims &D, const onetrans_block_weights *blk, const onetrans_kv_cache *cache, const void *x_ns,
+              int n_users, int n_cand, void *out_ns, char *w, const Ws &L, hipStream_t stream) {
+  int rc;
+  const bool ragged = cache->user_len != nullptr;
+  if (ragged && (rc = upload_user_len(cache, n_users, w, L, stream))) return rc;
+  const int d = D.d, H = D.H, dh = D.dh, ns = D.lns;
+  const int nseq = n_users * n_cand;
+  // ragged users: positions are relative to each user's own cached length (the attention adds it)
+  RowView x{const_cast<void *>(x_ns), (long long)ns * d, ragged ? 0 : cache->layer_len[0], d};
+  int x_f32 = D.dt == ONETRANS_F32;
+  void *stats = nullptr;   // (mean, rstd) rows of x when the previous block wrote them
+  for (int n = 0; n < D.N; ++n) {
+    const int s = ragged ? 0 : cache->layer_len[n];
+    Step st{};
+    st.n_seq = nseq;
+    st.s = s;
+    st.q = 0;
+    st.kv_t0 = 0;
+    st.kv_n = 0;
+    st.ns = ns;
+    st.in_t0 = s;
+    st.in_n = ns;
+    x.t_off = s;
+    st.x = x;
+    st.x_f32 = x_f32;
+    st.kN = HeadView{w + L.k, (long long)H * ns * dh, (long long)ns * dh, s};
+    st.vN = HeadView{w + L.v, (long long)H * ns * dh, (long long)ns * dh, s};
+    st.kS = st.kN;
+    st.vS = st.vN;
+    const HeadView cv = cache_view(D, cache, cache->k, n);
+    st.stage2 = 1;
+    st.n_grp = n_users;
+    st.n_cand = n_cand;
+    st.n_pre = s;
+    st.kp = cv.base;
+    st.vp = cache_view(D, cache, cache->v, n).base;
+    st.pre_sb = cv.sb;
+    st.pre_sh = cv.sh;
+    st.own_sb = st.kN.sb;
+    st.own_sh = st.kN.sh;
+    st.seq_shift = ragged ? (const int *)(w + L.seq) : nullptr;
+    st.out = RowView{n + 1 == D.N ? out_ns : (void *)(w + L.x[n & 1]), (long long)ns * d, s, d};
+    st.need_out = true;
+    st.stats_in = stats;
+    st.stats_out = n + 1 == D.N ? nullptr : (void *)(w + L.st[n & 1]);
+    if ((rc = run_step(D, blk[n], st, w, L, stream))) return rc;
+    x = RowView{w + L.x[n & 1], (long long)ns * d, 0, d};
+    stats = st.stats_out;
+    x_f32 = 1;
+  }
+  return ONETRANS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -590,9 +645,10 @@ size_t onetrans_workspace_bytes(const onetrans_config *cfg, int op, int n_seq, i
   bool kv;
   if (!ws_dims(cfg, D, op, n_seq, l_s, n_cand, d_l, n, tin, rq, kv)) return 0;
   if ((op == ONETRANS_OP_FORWARD || op == ONETRANS_OP_PREFILL) && check_schedule(cfg, l_s)) return 0;
-  if (op == ONETRANS_OP_FORWARD || op == ONETRANS_OP_APPEND) {
+  if (op == ONETRANS_OP_FORWARD || op == ONETRANS_OP_APPEND || op == ONETRANS_OP_SCORE) {
     const int parts = op == ONETRANS_OP_FORWARD ? ws_parts(n_seq) : append_ws_parts(n_seq);
-    return ws_layout(D, (n_seq + parts - 1) / parts, tin, rq, kv).total * parts;
+    const size_t per = op == ONETRANS_OP_SCORE ? (size_t)n_cand : 1;   // sequences per user
+    return ws_layout(D, (size_t)((n_seq + parts - 1) / parts) * per, tin, rq, kv).total * parts;
   }
   return ws_layout(D, n, tin, rq, kv).total;
 }
@@ -735,56 +791,34 @@ int onetrans_score_candidates(const onetrans_config *cfg, const onetrans_block_w
   size_t n, tin, rq;
   bool kv;
   ws_dims(cfg, D, ONETRANS_OP_SCORE, n_users, 0, n_cand, 0, n, tin, rq, kv);
-  const Ws L = ws_layout(D, n, tin, rq, kv);
-  if ((rc = check_ws(D, L, ws, ws_bytes))) return rc;
-
-  char *w = (char *)ws;
-  if (ragged && (rc = upload_user_len(cache, n_users, w, L, stream))) return rc;
-  const int d = D.d, H = D.H, dh = D.dh, ns = D.lns;
-  const int nseq = n_users * n_cand;
-  // ragged users: positions are relative to each user's own cached length (the attention adds it)
-  RowView x{const_cast<void *>(x_ns), (long long)ns * d, ragged ? 0 : cache->layer_len[0], d};
-  int x_f32 = D.dt == ONETRANS_F32;
-  void *stats = nullptr;   // (mean, rstd) rows of x when the previous block wrote them
-  for (int n = 0; n < D.N; ++n) {
-    const int s = ragged ? 0 : cache->layer_len[n];
-    Step st{};
-    st.n_seq = nseq;
-    st.s = s;
-    st.q = 0;
-    st.kv_t0 = 0;
-    st.kv_n = 0;
-    st.ns = ns;
-    st.in_t0 = s;
-    st.in_n = ns;
-    x.t_off = s;
-    st.x = x;
-    st.x_f32 = x_f32;
-    st.kN = HeadView{w + L.k, (long long)H * ns * dh, (long long)ns * dh, s};
-    st.vN = HeadView{w + L.v, (long long)H * ns * dh, (long long)ns * dh, s};
-    st.kS = st.kN;
-    st.vS = st.vN;
-    const HeadView cv = cache_view(D, cache, cache->k, n);
-    st.stage2 = 1;
-    st.n_grp = n_users;
-    st.n_cand = n_cand;
-    st.n_pre = s;
-    st.kp = cv.base;
-    st.vp = cache_view(D, cache, cache->v, n).base;
-    st.pre_sb = cv.sb;
-    st.pre_sh = cv.sh;
-    st.own_sb = st.kN.sb;
-    st.own_sh = st.kN.sh;
-    st.seq_shift = ragged ? (const int *)(w + L.seq) : nullptr;
-    st.out = RowView{n + 1 == D.N ? out_ns : (void *)(w + L.x[n & 1]), (long long)ns * d, s, d};
-    st.need_out = true;
-    st.stats_in = stats;
-    st.stats_out = n + 1 == D.N ? nullptr : (void *)(w + L.st[n & 1]);
-    if ((rc = run_step(D, blk[n], st, w, L, stream))) return rc;
-    x = RowView{w + L.x[n & 1], (long long)ns * d, 0, d};
-    stats = st.stats_out;
-    x_f32 = 1;
-  }
+  const int wp = append_ws_parts(n_users), parts = append_parts(n_users);
+  if (misaligned(ws)) return ONETRANS_ERR_ALIGNMENT;
+  if (!ws) return ONETRANS_ERR_INVALID_ARG;
+  const int uh = (n_users + wp - 1) / wp;
+  if (ws_bytes < ws_layout(D, (size_t)uh * n_cand, tin, rq, kv).total * wp) return ONETRANS_ERR_WORKSPACE;
+  Side *sd = nullptr;
+  const int side = parts == 2 ? side_streams(stream, sd) : -1;
+  if (side > 0) return ONETRANS_ERR_HIP;
+  if (side < 0)
+    return score_run(D, blk, cache, x_ns, n_users, n_cand, out_ns, (char *)ws, ws_layout(D, n, tin, rq, kv), stream);
+  // two halves of the users on two streams (users are independent), joined back into `stream`
+  const int u0 = (n_users + 1) / 2;
+  const Ws L = ws_layout(D, (size_t)u0 * n_cand, tin, rq, kv);
+  onetrans_kv_cache hb = *cache;   // the second half's users
+  const size_t user_bytes = (size_t)D.N * D.H * cache->capacity * D.dh * D.esz;
+  hb.k = (char *)cache->k + u0 * user_bytes;
+  hb.v = (char *)cache->v + u0 * user_bytes;
+  hb.n_users = cache->n_users - u0;
+  hb.user_len = cache->user_len ? cache->user_len + u0 : nullptr;
+  const size_t in_user = (size_t)n_cand * D.lns * D.d * D.esz, out_user = (size_t)n_cand * D.lns * D.d * 4;
+  if (hipEventRecord(sd->fork, stream) != hipSuccess || hipStreamWaitEvent(sd->s, sd->fork, 0) != hipSuccess)
+    return ONETRANS_ERR_HIP;
+  if ((rc = score_run(D, blk, cache, x_ns, u0, n_cand, out_ns, (char *)ws, L, stream))) return rc;
+  if ((rc = score_run(D, blk, &hb, (const char *)x_ns + u0 * in_user, n_users - u0, n_cand,
+                      (char *)out_ns + u0 * out_user, (char *)ws + L.total, L, sd->s)))
+    return rc;
+  if (hipEventRecord(sd->join, sd->s) != hipSuccess || hipStreamWaitEvent(stream, sd->join, 0) != hipSuccess)
+    return ONETRANS_ERR_HIP;
   return ONETRANS_OK;
 }
 
