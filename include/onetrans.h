@@ -129,6 +129,8 @@ int onetrans_forward(const onetrans_config *cfg, const onetrans_block_weights *b
  * <= t, so the first user_len[u] rows of every block, in the cache and in out_s, are exactly those
  * of user u's own sequence (the padding rows hold values no later call reads). Needs an
  * unpyramided schedule (every s_queries[n] = l_s), otherwise UNSUPPORTED.
+ * 16 or more users run as two halves on two streams, forked from and joined back into `stream`
+ * (see onetrans_forward).
  * Errors: as forward, plus CACHE_CAPACITY (capacity < l_s or n_users > cache->n_users), SHAPE (a
  * user_len outside [0, l_s]). */
 int onetrans_prefill_user(const onetrans_config *cfg, const onetrans_block_weights *blk,
@@ -230,8 +232,8 @@ int onetrans_tokenize(const onetrans_config *cfg, const onetrans_tokenizer_confi
                       const void *const *times, const void *ns_feat, int batch, void *x0, void *ws,
                       size_t ws_bytes, hipStream_t stream);
 
-/* Streams of the batched calls: 2 (default) runs a forward of 64 or more samples, and an append or
- * a Stage II call over 16 or more users, as two halves on two streams; 1 runs every call on the caller's stream
+/* Streams of the batched calls: 2 (default) runs a forward of 64 or more samples, and a Stage I,
+ * Stage II or append call over 16 or more users, as two halves on two streams; 1 runs every call on the caller's stream
  * alone (one kernel at a time, as a per-kernel profile needs). Results are identical either way;
  * workspace sizes do not change. Process-wide setting. Returns INVALID_ARG for other values. */
 int onetrans_set_streams(int n);

@@ -324,8 +324,10 @@ def test_append_two_streams_equal_one_stream(ragged):
     finally:
         ob.set_streams(2)
     (o1, k1, v1, l1, u1), (o2, k2, v2, l2, u2) = res
-    assert torch.equal(o1, o2) and torch.equal(k1, k2) and torch.equal(v1, v2)
-    assert l1 == l2 and u1 == u2
+    assert torch.equal(o1, o2) and l1 == l2 and u1 == u2
+    for u in range(w.n_users):    # each user's valid rows (rows past them are never written)
+        rows = u1[u] if ragged else l1[0]
+        assert torch.equal(k1[u, :, :, :rows], k2[u, :, :, :rows]) and torch.equal(v1[u, :, :, :rows], v2[u, :, :, :rows])
     for u in (8, 9):
         n_old = lens[u] if ragged else w.l_old
         if n_old:
@@ -371,3 +373,28 @@ def test_score_two_streams_equal_one_stream(ragged):
             e = rel_err(got[u, c], O.score_candidate(oc, xn[u, c], ws, m))
             say(f"  user {u} cand {c}: {e:.3e}")
             assert e <= TOL["bf16"], (u, c, e)
+
+
+def test_prefill_two_streams_equal_one_stream():
+    """Stage I over 16+ users runs as two halves on two streams: cache and final rows bit-identical
+    to one stream (pyramided schedule)."""
+    w = replace(synth.test_workload("tiny3_two_stage", "bf16"), n_users=17, input_seed=2120)
+    m = w.model
+    say(f"[prefill two streams] {w.key} users={w.n_users}")
+    mdl = model(w)
+    xs = dev(synth.user_sequences(w), mdl)
+    res = []
+    try:
+        for n_streams in (1, 2):
+            ob.set_streams(n_streams)
+            cache = ob.KVCache(mdl, w.n_users, w.l_s)
+            out = torch.empty((w.n_users, w.s_queries[-1], m.d_model), dtype=torch.float32, device=mdl.device)
+            ob.onetrans_prefill_user(mdl, xs, cache, out)
+            torch.cuda.synchronize()
+            res.append((out.clone(), cache.k.clone(), cache.v.clone(), cache.lengths))
+    finally:
+        ob.set_streams(2)
+    (o1, k1, v1, l1), (o2, k2, v2, l2) = res
+    assert torch.equal(o1, o2) and l1 == l2
+    for n, rows in enumerate(l1):   # rows past a block's length are never written
+        assert torch.equal(k1[:, n, :, :rows], k2[:, n, :, :rows]) and torch.equal(v1[:, n, :, :rows], v2[:, n, :, :rows])

@@ -443,8 +443,8 @@ int check_mlp(const onetrans_mlp_weights *m) {
 }
 
 // ---- batches over two streams ---------------------------------------------------------------------
-// A forward batch of at least FORWARD_SPLIT_MIN samples, and an append or a Stage II call over at
-// least APPEND_SPLIT_MIN users, run as two halves on the caller's stream and a library-owned stream of
+// A forward batch of at least FORWARD_SPLIT_MIN samples, and a Stage I, Stage II or append call
+// over at least APPEND_SPLIT_MIN users, run as two halves on the caller's stream and a library-owned stream of
 // the same device (default priority), forked and joined with events. The workspace is always sized
 // for the split (two half layouts also hold the whole batch's single-stream layout).
 constexpr int FORWARD_SPLIT_MIN = 64;
@@ -634,6 +634,55 @@ int score_run(const Dims &D, const onetrans_block_weights *blk, const onetrans_k
   return ONETRANS_OK;
 }
 
+// The Stage I launch sequence for `n_users` users of `cache` (a view whose first user is the
+// call's first user), with workspace `w` laid out as L. Writes no host state.
+int prefill_run(const Dims &D, const onetrans_config *cfg, const onetrans_block_weights *blk, const void *x_s,
+                int n_users, int l_s, const onetrans_kv_cache *cache, void *out_s, char *w, const Ws &L,
+                hipStream_t stream) {
+  int rc;
+  const int d = D.d;
+  int s = l_s;
+  RowView x{const_cast<void *>(x_s), (long long)l_s * d, 0, d};
+  int x_f32 = D.dt == ONETRANS_F32;
+  void *stats = nullptr;   // (mean, rstd) rows of x when the previous block wrote them
+  for (int n = 0; n < D.N; ++n) {
+    const int q = cfg->s_queries[n];
+    const int p0 = s - q;
+    const bool last = n + 1 == D.N;
+    Step st{};
+    st.n_seq = n_users;
+    st.s = s;
+    st.q = q;
+    st.kv_t0 = 0;
+    st.kv_n = s;
+    st.ns = 0;
+    st.in_t0 = 0;
+    st.in_n = s;
+    st.x = x;
+    st.x_f32 = x_f32;
+    st.kS = cache_view(D, cache, cache->k, n);
+    st.vS = cache_view(D, cache, cache->v, n);
+    st.kN = st.kS;
+    st.vN = st.vS;
+    st.stage2 = 0;
+    st.n_pre = s;
+    st.kp = st.kS.base;
+    st.vp = st.vS.base;
+    st.pre_sb = st.kS.sb;
+    st.pre_sh = st.kS.sh;
+    st.out = RowView{last ? out_s : (void *)(w + L.x[n & 1]), (long long)q * d, p0, d};
+    st.need_out = !last || out_s != nullptr;
+    st.stats_in = stats;
+    st.stats_out = last ? nullptr : (void *)(w + L.st[n & 1]);
+    if ((rc = run_step(D, blk[n], st, w, L, stream))) return rc;
+    x = RowView{w + L.x[n & 1], (long long)q * d, 0, d};
+    stats = st.stats_out;
+    x_f32 = 1;
+    s = q;
+  }
+  return ONETRANS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -645,7 +694,7 @@ size_t onetrans_workspace_bytes(const onetrans_config *cfg, int op, int n_seq, i
   bool kv;
   if (!ws_dims(cfg, D, op, n_seq, l_s, n_cand, d_l, n, tin, rq, kv)) return 0;
   if ((op == ONETRANS_OP_FORWARD || op == ONETRANS_OP_PREFILL) && check_schedule(cfg, l_s)) return 0;
-  if (op == ONETRANS_OP_FORWARD || op == ONETRANS_OP_APPEND || op == ONETRANS_OP_SCORE) {
+  if (op == ONETRANS_OP_FORWARD || op == ONETRANS_OP_APPEND || op == ONETRANS_OP_SCORE || op == ONETRANS_OP_PREFILL) {
     const int parts = op == ONETRANS_OP_FORWARD ? ws_parts(n_seq) : append_ws_parts(n_seq);
     const size_t per = op == ONETRANS_OP_SCORE ? (size_t)n_cand : 1;   // sequences per user
     return ws_layout(D, (size_t)((n_seq + parts - 1) / parts) * per, tin, rq, kv).total * parts;
@@ -719,51 +768,38 @@ int onetrans_prefill_user(const onetrans_config *cfg, const onetrans_block_weigh
   size_t n, tin, rq;
   bool kv;
   ws_dims(cfg, D, ONETRANS_OP_PREFILL, n_users, l_s, 0, 0, n, tin, rq, kv);
-  const Ws L = ws_layout(D, n, tin, rq, kv);
-  if ((rc = check_ws(D, L, ws, ws_bytes))) return rc;
-
-  char *w = (char *)ws;
-  const int d = D.d;
-  int s = l_s;
-  RowView x{const_cast<void *>(x_s), (long long)l_s * d, 0, d};
-  int x_f32 = D.dt == ONETRANS_F32;
-  void *stats = nullptr;   // (mean, rstd) rows of x when the previous block wrote them
-  for (int n = 0; n < D.N; ++n) {
-    const int q = cfg->s_queries[n];
-    const int p0 = s - q;
-    const bool last = n + 1 == D.N;
-    Step st{};
-    st.n_seq = n_users;
-    st.s = s;
-    st.q = q;
-    st.kv_t0 = 0;
-    st.kv_n = s;
-    st.ns = 0;
-    st.in_t0 = 0;
-    st.in_n = s;
-    st.x = x;
-    st.x_f32 = x_f32;
-    st.kS = cache_view(D, cache, cache->k, n);
-    st.vS = cache_view(D, cache, cache->v, n);
-    st.kN = st.kS;
-    st.vN = st.vS;
-    st.stage2 = 0;
-    st.n_pre = s;
-    st.kp = st.kS.base;
-    st.vp = st.vS.base;
-    st.pre_sb = st.kS.sb;
-    st.pre_sh = st.kS.sh;
-    st.out = RowView{last ? out_s : (void *)(w + L.x[n & 1]), (long long)q * d, p0, d};
-    st.need_out = !last || out_s != nullptr;
-    st.stats_in = stats;
-    st.stats_out = last ? nullptr : (void *)(w + L.st[n & 1]);
-    if ((rc = run_step(D, blk[n], st, w, L, stream))) return rc;
-    x = RowView{w + L.x[n & 1], (long long)q * d, 0, d};
-    stats = st.stats_out;
-    x_f32 = 1;
-    s = q;
+  const int wp = append_ws_parts(n_users), parts = append_parts(n_users);
+  if (misaligned(ws)) return ONETRANS_ERR_ALIGNMENT;
+  if (!ws) return ONETRANS_ERR_INVALID_ARG;
+  if (ws_bytes < ws_layout(D, (n_users + wp - 1) / wp, tin, rq, kv).total * wp) return ONETRANS_ERR_WORKSPACE;
+  Side *sd = nullptr;
+  const int side = parts == 2 ? side_streams(stream, sd) : -1;
+  if (side > 0) return ONETRANS_ERR_HIP;
+  if (side < 0) {
+    if ((rc = prefill_run(D, cfg, blk, x_s, n_users, l_s, cache, out_s, (char *)ws, ws_layout(D, n_users, tin, rq, kv),
+                          stream)))
+      return rc;
+  } else {
+    // two halves of the users on two streams (users are independent), joined back into `stream`
+    const int u0 = (n_users + 1) / 2;
+    const Ws L = ws_layout(D, u0, tin, rq, kv);
+    onetrans_kv_cache hb = *cache;   // the second half's users
+    const size_t user_bytes = (size_t)D.N * D.H * cache->capacity * D.dh * D.esz;
+    hb.k = (char *)cache->k + u0 * user_bytes;
+    hb.v = (char *)cache->v + u0 * user_bytes;
+    hb.n_users = cache->n_users - u0;
+    hb.user_len = cache->user_len ? cache->user_len + u0 : nullptr;
+    const size_t in_user = (size_t)l_s * D.d * D.esz, out_user = (size_t)cfg->s_queries[D.N - 1] * D.d * 4;
+    if (hipEventRecord(sd->fork, stream) != hipSuccess || hipStreamWaitEvent(sd->s, sd->fork, 0) != hipSuccess)
+      return ONETRANS_ERR_HIP;
+    if ((rc = prefill_run(D, cfg, blk, x_s, u0, l_s, cache, out_s, (char *)ws, L, stream))) return rc;
+    if ((rc = prefill_run(D, cfg, blk, (const char *)x_s + u0 * in_user, n_users - u0, l_s, &hb,
+                          out_s ? (char *)out_s + u0 * out_user : nullptr, (char *)ws + L.total, L, sd->s)))
+      return rc;
+    if (hipEventRecord(sd->join, sd->s) != hipSuccess || hipStreamWaitEvent(stream, sd->join, 0) != hipSuccess)
+      return ONETRANS_ERR_HIP;
   }
-  s = l_s;
+  int s = l_s;
   for (int n = 0; n < D.N; ++n) {
     cache->layer_len[n] = s;
     s = cfg->s_queries[n];
