@@ -13,9 +13,11 @@ are measured for the design notes, not as the headline.
 
 Timing: W untimed warm-up steps, then K timed steps between a device synchronisation on both
 sides (one GPU, so no barrier is needed). Inputs and weights are resident in HBM before the
-timed region starts. Per-kernel device time comes from hipEvents the library records around each
-launch on the call's stream during the timed region. The CPU baseline times the fp64 oracle on a
-bounded sample of the same workload on the host cores.
+timed region starts. The library runs large batches as two concurrent halves on two streams
+(--streams 2, the default), so per-kernel device time comes from a separate pass after the timed
+region with one stream, from hipEvents the library records around each launch (--streams 1 times
+and traces the same single-stream run). The CPU baseline times the fp64 oracle on a bounded sample
+of the same workload on the host cores.
 """
 
 from __future__ import annotations
