@@ -135,6 +135,7 @@ def bench_tokenize(a):
     t_setup = time.time()
     one = replace(m, n_blocks=1)
     model = ob.Model.from_host(one, (w.l_s,), synth.make_weights(one), device=dev)
+    ob.set_streams(a.streams)
     tw = synth.tokenizer_weights(w)
     up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev, dtype=model.torch_dtype)
     tok = ob.Tokenizer(model, w.seq_lens, [{k: up(v) for k, v in p.items()} for p in tw["seq"]], up(tw["sep"]),
