@@ -47,7 +47,7 @@ def parse():
                             "tokenize_s_time"])
     p.add_argument("--dtype", default=None, choices=[None, "bf16", "f32"])
     p.add_argument("--no-trace", action="store_true", help="no per-kernel events in the timed region")
-    p.add_argument("--streams", type=int, default=2, choices=[1, 2],
+    p.add_argument("--streams", type=int, default=2, choices=[1, 2, 4],
                    help="streams of the batched calls: 2 runs a forward batch / an append's users as two "
                         "concurrent halves (per-kernel timing then comes from a separate one-stream pass); 1 "
                         "runs everything on one stream")

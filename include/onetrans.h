@@ -232,10 +232,13 @@ int onetrans_tokenize(const onetrans_config *cfg, const onetrans_tokenizer_confi
                       const void *const *times, const void *ns_feat, int batch, void *x0, void *ws,
                       size_t ws_bytes, hipStream_t stream);
 
-/* Streams of the batched calls: 2 (default) runs a forward of 64 or more samples, and a Stage I,
- * Stage II or append call over 16 or more users, as two halves on two streams; 1 runs every call on the caller's stream
- * alone (one kernel at a time, as a per-kernel profile needs). Results are identical either way;
- * workspace sizes do not change. Process-wide setting. Returns INVALID_ARG for other values. */
+/* Streams of the batched calls. 2 (default): a forward of 64 or more samples, and a Stage I,
+ * Stage II or append call over 16 or more users, run as two parts on two streams. 4: up to four
+ * parts (from 128 samples or 32 users). 1: every call on the caller's stream alone (one kernel at a
+ * time, as a per-kernel profile needs). Parts are contiguous ranges of samples or users; results
+ * are identical in every setting and workspace sizes do not depend on it. Process-wide setting.
+ * Returns INVALID_ARG for other values. */
+
 int onetrans_set_streams(int n);
 
 /* Kernel classes of the per-launch timing below. */

@@ -265,7 +265,9 @@ def test_forward_workspace_covers_the_split():
     assert one(64) == 2 * one(32)
     assert one(65) == 2 * one(33)
     assert one(65) >= one(63)
+    assert one(128) == 4 * one(32) and one(130) == 4 * one(33)     # four parts from 128 samples
     assert lib.onetrans_set_streams(3) == L.ERR_INVALID_ARG
+    assert lib.onetrans_set_streams(4) == L.OK
     assert lib.onetrans_set_streams(0) == L.ERR_INVALID_ARG
     assert lib.onetrans_set_streams(2) == L.OK
 

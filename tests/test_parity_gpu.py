@@ -274,25 +274,24 @@ def test_gpu_two_stage_matches_gpu_forward():
 
 
 def test_forward_two_streams_equal_one_stream():
-    """A batch of 64+ runs as two halves on two streams: bit-identical to one stream, and correct on
-    both sides of the split (samples 34 and 35 of 70)."""
-    w = replace(synth.test_workload("tiny3_fwd", "bf16"), batch=70)
-    say(f"[forward two streams] {w.key} B={w.batch}")
+    """A batch of 64+ (128+) runs as two (four) parts on as many streams: bit-identical to one
+    stream, and correct on both sides of the part boundaries (33 samples per part of 130)."""
+    w = replace(synth.test_workload("tiny3_fwd", "bf16"), batch=130)
+    say(f"[forward two and four streams] {w.key} B={w.batch}")
     mdl = model(w)
     x = synth.forward_batch(w)
     xd = dev(x, mdl)
+    outs = []
     try:
-        ob.set_streams(1)
-        one = ob.onetrans_forward(mdl, xd)
-        torch.cuda.synchronize()
-        ob.set_streams(2)
-        two = ob.onetrans_forward(mdl, xd)
-        torch.cuda.synchronize()
+        for n_streams in (1, 2, 4):
+            ob.set_streams(n_streams)
+            outs.append(ob.onetrans_forward(mdl, xd))
+            torch.cuda.synchronize()
     finally:
         ob.set_streams(2)
-    assert torch.equal(one, two)
-    got = two.cpu().numpy()
-    for b in (0, 34, 35, 69):
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    got = outs[2].cpu().numpy()
+    for b in (0, 32, 33, 64, 65, 129):
         e = rel_err(got[b], O.forward(x[b], weights(w.model), w.model, w.s_queries))
         say(f"  sample {b}: err {e:.3e}")
         assert e <= TOL["bf16"], (b, e)
@@ -300,10 +299,10 @@ def test_forward_two_streams_equal_one_stream():
 
 @pytest.mark.parametrize("ragged", [False, True])
 def test_append_two_streams_equal_one_stream(ragged):
-    """An append over 16+ users runs as two halves on two streams: the new rows and every cache row
-    are bit-identical to one stream; users on both sides of the split (8 and 9 of 17) match the
-    oracle."""
-    w = replace(synth.test_workload("tiny3_append", "bf16"), n_users=17, input_seed=2118)
+    """An append over 16+ (32+) users runs as two (four) parts on as many streams: the new rows and
+    every written cache row are bit-identical to one stream; users on both sides of a part boundary
+    (8 and 9 of 33) match the oracle."""
+    w = replace(synth.test_workload("tiny3_append", "bf16"), n_users=33, input_seed=2118)
     m, ws = w.model, weights(w.model)
     lens = [(5 * u) % (w.l_old + 1) for u in range(w.n_users)] if ragged else None
     say(f"[append two streams] {w.key} users={w.n_users} ragged={ragged}")
@@ -313,7 +312,7 @@ def test_append_two_streams_equal_one_stream(ragged):
     new = np.ascontiguousarray(seq[:, w.l_old:])
     res = []
     try:
-        for n_streams in (1, 2):
+        for n_streams in (1, 2, 4):
             ob.set_streams(n_streams)
             cache = ob.KVCache(mdl, w.n_users, w.l_old + w.d_l, user_len=lens)
             ob.onetrans_prefill_user(mdl, dev(old, mdl), cache)
@@ -323,11 +322,13 @@ def test_append_two_streams_equal_one_stream(ragged):
             res.append((out_new.clone(), cache.k.clone(), cache.v.clone(), cache.lengths, cache.user_lengths))
     finally:
         ob.set_streams(2)
-    (o1, k1, v1, l1, u1), (o2, k2, v2, l2, u2) = res
-    assert torch.equal(o1, o2) and l1 == l2 and u1 == u2
-    for u in range(w.n_users):    # each user's valid rows (rows past them are never written)
-        rows = u1[u] if ragged else l1[0]
-        assert torch.equal(k1[u, :, :, :rows], k2[u, :, :, :rows]) and torch.equal(v1[u, :, :, :rows], v2[u, :, :, :rows])
+    (o1, k1, v1, l1, u1) = res[0]
+    for (o2, k2, v2, l2, u2) in res[1:]:
+        assert torch.equal(o1, o2) and l1 == l2 and u1 == u2
+        for u in range(w.n_users):    # each user's valid rows (rows past them are never written)
+            rows = u1[u] if ragged else l1[0]
+            assert torch.equal(k1[u, :, :, :rows], k2[u, :, :, :rows])
+            assert torch.equal(v1[u, :, :, :rows], v2[u, :, :, :rows])
     for u in (8, 9):
         n_old = lens[u] if ragged else w.l_old
         if n_old:
@@ -342,9 +343,9 @@ def test_append_two_streams_equal_one_stream(ragged):
 
 @pytest.mark.parametrize("ragged", [False, True])
 def test_score_two_streams_equal_one_stream(ragged):
-    """Stage II over 16+ users runs as two halves on two streams: bit-identical to one stream, and
-    users on both sides of the split (8 and 9 of 17) match the oracle."""
-    w = replace(synth.test_workload("tiny3_two_stage", "bf16"), n_users=17, n_cand=3, input_seed=2119)
+    """Stage II over 16+ (32+) users runs as two (four) parts on as many streams: bit-identical to
+    one stream, and users on both sides of a part boundary (8 and 9 of 33) match the oracle."""
+    w = replace(synth.test_workload("tiny3_two_stage", "bf16"), n_users=33, n_cand=3, input_seed=2119)
     m, ws = w.model, weights(w.model)
     say(f"[score two streams] {w.key} users={w.n_users} ragged={ragged}")
     sched = (w.l_s,) * m.n_blocks if ragged else w.s_queries
@@ -356,14 +357,14 @@ def test_score_two_streams_equal_one_stream(ragged):
     ob.onetrans_prefill_user(mdl, dev(xs, mdl), cache)
     res = []
     try:
-        for n_streams in (1, 2):
+        for n_streams in (1, 2, 4):
             ob.set_streams(n_streams)
             res.append(ob.onetrans_score_candidates(mdl, cache, dev(xn, mdl)))
             torch.cuda.synchronize()
     finally:
         ob.set_streams(2)
-    assert torch.equal(res[0], res[1])
-    got = res[1].cpu().numpy()
+    assert torch.equal(res[0], res[1]) and torch.equal(res[0], res[2])
+    got = res[2].cpu().numpy()
     for u in (8, 9):
         n_old = lens[u] if ragged else w.l_s
         if ragged and n_old == 0:
@@ -376,16 +377,16 @@ def test_score_two_streams_equal_one_stream(ragged):
 
 
 def test_prefill_two_streams_equal_one_stream():
-    """Stage I over 16+ users runs as two halves on two streams: cache and final rows bit-identical
-    to one stream (pyramided schedule)."""
-    w = replace(synth.test_workload("tiny3_two_stage", "bf16"), n_users=17, input_seed=2120)
+    """Stage I over 16+ (32+) users runs as two (four) parts on as many streams: cache and final rows
+    bit-identical to one stream (pyramided schedule)."""
+    w = replace(synth.test_workload("tiny3_two_stage", "bf16"), n_users=33, input_seed=2120)
     m = w.model
     say(f"[prefill two streams] {w.key} users={w.n_users}")
     mdl = model(w)
     xs = dev(synth.user_sequences(w), mdl)
     res = []
     try:
-        for n_streams in (1, 2):
+        for n_streams in (1, 2, 4):
             ob.set_streams(n_streams)
             cache = ob.KVCache(mdl, w.n_users, w.l_s)
             out = torch.empty((w.n_users, w.s_queries[-1], m.d_model), dtype=torch.float32, device=mdl.device)
@@ -394,7 +395,9 @@ def test_prefill_two_streams_equal_one_stream():
             res.append((out.clone(), cache.k.clone(), cache.v.clone(), cache.lengths))
     finally:
         ob.set_streams(2)
-    (o1, k1, v1, l1), (o2, k2, v2, l2) = res
-    assert torch.equal(o1, o2) and l1 == l2
-    for n, rows in enumerate(l1):   # rows past a block's length are never written
-        assert torch.equal(k1[:, n, :, :rows], k2[:, n, :, :rows]) and torch.equal(v1[:, n, :, :rows], v2[:, n, :, :rows])
+    (o1, k1, v1, l1) = res[0]
+    for (o2, k2, v2, l2) in res[1:]:
+        assert torch.equal(o1, o2) and l1 == l2
+        for n, rows in enumerate(l1):   # rows past a block's length are never written
+            assert torch.equal(k1[:, n, :, :rows], k2[:, n, :, :rows])
+            assert torch.equal(v1[:, n, :, :rows], v2[:, n, :, :rows])

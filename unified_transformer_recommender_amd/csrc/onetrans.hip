@@ -17,6 +17,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "onetrans.h"
@@ -442,28 +443,31 @@ int check_mlp(const onetrans_mlp_weights *m) {
   return ONETRANS_OK;
 }
 
-// ---- batches over two streams ---------------------------------------------------------------------
-// A forward batch of at least FORWARD_SPLIT_MIN samples, and a Stage I, Stage II or append call
-// over at least APPEND_SPLIT_MIN users, run as two halves on the caller's stream and a library-owned stream of
-// the same device (default priority), forked and joined with events. The workspace is always sized
-// for the split (two half layouts also hold the whole batch's single-stream layout).
-constexpr int FORWARD_SPLIT_MIN = 64;
-constexpr int APPEND_SPLIT_MIN = 16;
-int g_streams = 2;
-inline int ws_parts(int batch) { return batch >= FORWARD_SPLIT_MIN ? 2 : 1; }
-inline int forward_parts(int batch) { return g_streams == 2 ? ws_parts(batch) : 1; }
-inline int append_ws_parts(int users) { return users >= APPEND_SPLIT_MIN ? 2 : 1; }
-inline int append_parts(int users) { return g_streams == 2 ? append_ws_parts(users) : 1; }
+// ---- batches over several streams ---------------------------------------------------------------
+// Samples (forward) and users (Stage I, Stage II, append) are independent, so a call can run as
+// up to four contiguous parts, part 0 on the caller's stream and part i on a library-owned stream
+// of the same device (default priority), forked from and joined back into the caller's stream with
+// events. The late pyramid blocks and the append / Stage II launches are small, and every kernel
+// ends in a partial wave; parts in flight together fill those tails and the launch gaps.
+// The workspace is always sized for the largest split the call's size allows (WsParts parts), which
+// also holds every smaller split (halving a part never needs more bytes).
+constexpr int MAX_PARTS = 4;
+constexpr int FORWARD_PART_MIN = 32;   // samples per part
+constexpr int USER_PART_MIN = 8;       // users per part
+int g_streams = 2;                     // 1, 2 or 4
+inline int ws_parts_for(int n, int min_part) { return n >= 4 * min_part ? 4 : n >= 2 * min_part ? 2 : 1; }
+inline int parts_for(int n, int min_part) { return std::min(g_streams, ws_parts_for(n, min_part)); }
 
 struct Side {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipStream_t s[MAX_PARTS - 1] = {};
+  hipEvent_t fork = nullptr;
+  hipEvent_t join[MAX_PARTS - 1] = {};
 };
 Side g_side[64];
 
-// The side stream of the current device, created on first use. Returns 1 on a HIP error, and -1
-// when `stream` belongs to another device than the current one (the caller then stays on one
-// stream: the side stream and its events live on the current device).
+// The side streams of the current device, created on first use. Returns 1 on a HIP error, and -1
+// when `stream` belongs to another device than the current one (the call then stays on one stream:
+// the side streams and their events live on the current device).
 int side_streams(hipStream_t stream, Side *&out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
@@ -473,13 +477,52 @@ int side_streams(hipStream_t stream, Side *&out) {
     if ((int)sdev != dev) return -1;
   }
   Side &sd = g_side[dev];
-  if (!sd.s) {
-    if (hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) != hipSuccess) return 1;
+  if (!sd.fork) {
+    for (int i = 0; i < MAX_PARTS - 1; ++i) {
+      if (hipStreamCreateWithFlags(&sd.s[i], hipStreamNonBlocking) != hipSuccess) return 1;
+      if (hipEventCreateWithFlags(&sd.join[i], hipEventDisableTiming) != hipSuccess) return 1;
+    }
     if (hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) != hipSuccess) return 1;
-    if (hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) != hipSuccess) return 1;
   }
   out = &sd;
   return 0;
+}
+
+// Runs run(first, count, part, stream) over `parts` contiguous ranges of [0, n) (ceil(n / parts)
+// each, the last one shorter), each on its own stream, and joins them back into `stream`.
+template <class F>
+int over_streams(int n, int parts, hipStream_t stream, F &&run) {
+  Side *sd = nullptr;
+  if (parts > 1) {
+    const int side = side_streams(stream, sd);
+    if (side > 0) return ONETRANS_ERR_HIP;
+    if (side < 0) parts = 1;
+  }
+  if (parts == 1) return run(0, n, 0, stream);
+  if (hipEventRecord(sd->fork, stream) != hipSuccess) return ONETRANS_ERR_HIP;
+  for (int i = 1; i < parts; ++i)
+    if (hipStreamWaitEvent(sd->s[i - 1], sd->fork, 0) != hipSuccess) return ONETRANS_ERR_HIP;
+  const int per = (n + parts - 1) / parts;
+  int rc;
+  for (int i = 0; i < parts && i * per < n; ++i)
+    if ((rc = run(i * per, std::min(per, n - i * per), i, i == 0 ? stream : sd->s[i - 1]))) return rc;
+  for (int i = 1; i < parts; ++i)
+    if (hipEventRecord(sd->join[i - 1], sd->s[i - 1]) != hipSuccess ||
+        hipStreamWaitEvent(stream, sd->join[i - 1], 0) != hipSuccess)
+      return ONETRANS_ERR_HIP;
+  return ONETRANS_OK;
+}
+
+// The users [first, ...) of a cache: layout [user][block][head][capacity][d_head], so a pointer
+// offset (and the matching slice of user_len); layer_len stays shared.
+onetrans_kv_cache user_view(const Dims &D, const onetrans_kv_cache *c, int first) {
+  onetrans_kv_cache v = *c;
+  const size_t user_bytes = (size_t)D.N * D.H * c->capacity * D.dh * D.esz;
+  v.k = (char *)c->k + first * user_bytes;
+  v.v = (char *)c->v + first * user_bytes;
+  v.n_users = c->n_users - first;
+  v.user_len = c->user_len ? c->user_len + first : nullptr;
+  return v;
 }
 
 int forward_run(const Dims &D, const onetrans_config *cfg, const onetrans_block_weights *blk, const void *x0,
@@ -694,12 +737,9 @@ size_t onetrans_workspace_bytes(const onetrans_config *cfg, int op, int n_seq, i
   bool kv;
   if (!ws_dims(cfg, D, op, n_seq, l_s, n_cand, d_l, n, tin, rq, kv)) return 0;
   if ((op == ONETRANS_OP_FORWARD || op == ONETRANS_OP_PREFILL) && check_schedule(cfg, l_s)) return 0;
-  if (op == ONETRANS_OP_FORWARD || op == ONETRANS_OP_APPEND || op == ONETRANS_OP_SCORE || op == ONETRANS_OP_PREFILL) {
-    const int parts = op == ONETRANS_OP_FORWARD ? ws_parts(n_seq) : append_ws_parts(n_seq);
-    const size_t per = op == ONETRANS_OP_SCORE ? (size_t)n_cand : 1;   // sequences per user
-    return ws_layout(D, (size_t)((n_seq + parts - 1) / parts) * per, tin, rq, kv).total * parts;
-  }
-  return ws_layout(D, n, tin, rq, kv).total;
+  const int parts = ws_parts_for(n_seq, op == ONETRANS_OP_FORWARD ? FORWARD_PART_MIN : USER_PART_MIN);
+  const size_t per = op == ONETRANS_OP_SCORE ? (size_t)n_cand : 1;   // sequences per user
+  return ws_layout(D, (size_t)((n_seq + parts - 1) / parts) * per, tin, rq, kv).total * parts;
 }
 
 size_t onetrans_kv_cache_bytes(const onetrans_config *cfg, int n_users, int capacity) {
@@ -721,29 +761,17 @@ int onetrans_forward(const onetrans_config *cfg, const onetrans_block_weights *b
   size_t n, tin, rq;
   bool kv;
   ws_dims(cfg, D, ONETRANS_OP_FORWARD, batch, l_s, 0, 0, n, tin, rq, kv);
-  const int wp = ws_parts(batch), parts = forward_parts(batch);
+  const int wp = ws_parts_for(batch, FORWARD_PART_MIN), parts = parts_for(batch, FORWARD_PART_MIN);
   if (misaligned(ws)) return ONETRANS_ERR_ALIGNMENT;
   if (!ws) return ONETRANS_ERR_INVALID_ARG;
   if (ws_bytes < ws_layout(D, (batch + wp - 1) / wp, tin, rq, kv).total * wp) return ONETRANS_ERR_WORKSPACE;
-  const int b0 = (batch + parts - 1) / parts;
-  const Ws L = ws_layout(D, b0, tin, rq, kv);
-  Side *sd = nullptr;
-  const int side = parts == 2 ? side_streams(stream, sd) : -1;
-  if (side > 0) return ONETRANS_ERR_HIP;
-  if (side < 0) return forward_run(D, cfg, blk, x0, batch, l_s, out, (char *)ws, ws_layout(D, batch, tin, rq, kv), stream);
-  // Two halves of the batch on two streams (samples are independent): each half's small late
-  // blocks and launch gaps overlap the other half's kernels. The halves join back into `stream`.
+  const size_t part_bytes = ws_layout(D, (batch + parts - 1) / parts, tin, rq, kv).total;
   const size_t in_row = (size_t)(l_s + D.lns) * D.d * D.esz;
   const size_t out_row = (size_t)(cfg->s_queries[D.N - 1] + D.lns) * D.d * 4;
-  if (hipEventRecord(sd->fork, stream) != hipSuccess || hipStreamWaitEvent(sd->s, sd->fork, 0) != hipSuccess)
-    return ONETRANS_ERR_HIP;
-  if ((rc = forward_run(D, cfg, blk, x0, b0, l_s, out, (char *)ws, L, stream))) return rc;
-  if ((rc = forward_run(D, cfg, blk, (const char *)x0 + b0 * in_row, batch - b0, l_s, (char *)out + b0 * out_row,
-                        (char *)ws + L.total, L, sd->s)))
-    return rc;
-  if (hipEventRecord(sd->join, sd->s) != hipSuccess || hipStreamWaitEvent(stream, sd->join, 0) != hipSuccess)
-    return ONETRANS_ERR_HIP;
-  return ONETRANS_OK;
+  return over_streams(batch, parts, stream, [&](int first, int count, int part, hipStream_t st) {
+    return forward_run(D, cfg, blk, (const char *)x0 + first * in_row, count, l_s, (char *)out + first * out_row,
+                       (char *)ws + part * part_bytes, ws_layout(D, count, tin, rq, kv), st);
+  });
 }
 
 int onetrans_prefill_user(const onetrans_config *cfg, const onetrans_block_weights *blk, const void *x_s,
@@ -768,37 +796,19 @@ int onetrans_prefill_user(const onetrans_config *cfg, const onetrans_block_weigh
   size_t n, tin, rq;
   bool kv;
   ws_dims(cfg, D, ONETRANS_OP_PREFILL, n_users, l_s, 0, 0, n, tin, rq, kv);
-  const int wp = append_ws_parts(n_users), parts = append_parts(n_users);
+  const int wp = ws_parts_for(n_users, USER_PART_MIN), parts = parts_for(n_users, USER_PART_MIN);
   if (misaligned(ws)) return ONETRANS_ERR_ALIGNMENT;
   if (!ws) return ONETRANS_ERR_INVALID_ARG;
   if (ws_bytes < ws_layout(D, (n_users + wp - 1) / wp, tin, rq, kv).total * wp) return ONETRANS_ERR_WORKSPACE;
-  Side *sd = nullptr;
-  const int side = parts == 2 ? side_streams(stream, sd) : -1;
-  if (side > 0) return ONETRANS_ERR_HIP;
-  if (side < 0) {
-    if ((rc = prefill_run(D, cfg, blk, x_s, n_users, l_s, cache, out_s, (char *)ws, ws_layout(D, n_users, tin, rq, kv),
-                          stream)))
-      return rc;
-  } else {
-    // two halves of the users on two streams (users are independent), joined back into `stream`
-    const int u0 = (n_users + 1) / 2;
-    const Ws L = ws_layout(D, u0, tin, rq, kv);
-    onetrans_kv_cache hb = *cache;   // the second half's users
-    const size_t user_bytes = (size_t)D.N * D.H * cache->capacity * D.dh * D.esz;
-    hb.k = (char *)cache->k + u0 * user_bytes;
-    hb.v = (char *)cache->v + u0 * user_bytes;
-    hb.n_users = cache->n_users - u0;
-    hb.user_len = cache->user_len ? cache->user_len + u0 : nullptr;
-    const size_t in_user = (size_t)l_s * D.d * D.esz, out_user = (size_t)cfg->s_queries[D.N - 1] * D.d * 4;
-    if (hipEventRecord(sd->fork, stream) != hipSuccess || hipStreamWaitEvent(sd->s, sd->fork, 0) != hipSuccess)
-      return ONETRANS_ERR_HIP;
-    if ((rc = prefill_run(D, cfg, blk, x_s, u0, l_s, cache, out_s, (char *)ws, L, stream))) return rc;
-    if ((rc = prefill_run(D, cfg, blk, (const char *)x_s + u0 * in_user, n_users - u0, l_s, &hb,
-                          out_s ? (char *)out_s + u0 * out_user : nullptr, (char *)ws + L.total, L, sd->s)))
-      return rc;
-    if (hipEventRecord(sd->join, sd->s) != hipSuccess || hipStreamWaitEvent(stream, sd->join, 0) != hipSuccess)
-      return ONETRANS_ERR_HIP;
-  }
+  const size_t part_bytes = ws_layout(D, (n_users + parts - 1) / parts, tin, rq, kv).total;
+  const size_t in_user = (size_t)l_s * D.d * D.esz, out_user = (size_t)cfg->s_queries[D.N - 1] * D.d * 4;
+  rc = over_streams(n_users, parts, stream, [&](int first, int count, int part, hipStream_t st) {
+    const onetrans_kv_cache view = user_view(D, cache, first);
+    return prefill_run(D, cfg, blk, (const char *)x_s + first * in_user, count, l_s, &view,
+                       out_s ? (char *)out_s + first * out_user : nullptr, (char *)ws + part * part_bytes,
+                       ws_layout(D, count, tin, rq, kv), st);
+  });
+  if (rc) return rc;
   int s = l_s;
   for (int n = 0; n < D.N; ++n) {
     cache->layer_len[n] = s;
@@ -827,35 +837,19 @@ int onetrans_score_candidates(const onetrans_config *cfg, const onetrans_block_w
   size_t n, tin, rq;
   bool kv;
   ws_dims(cfg, D, ONETRANS_OP_SCORE, n_users, 0, n_cand, 0, n, tin, rq, kv);
-  const int wp = append_ws_parts(n_users), parts = append_parts(n_users);
+  const int wp = ws_parts_for(n_users, USER_PART_MIN), parts = parts_for(n_users, USER_PART_MIN);
   if (misaligned(ws)) return ONETRANS_ERR_ALIGNMENT;
   if (!ws) return ONETRANS_ERR_INVALID_ARG;
-  const int uh = (n_users + wp - 1) / wp;
-  if (ws_bytes < ws_layout(D, (size_t)uh * n_cand, tin, rq, kv).total * wp) return ONETRANS_ERR_WORKSPACE;
-  Side *sd = nullptr;
-  const int side = parts == 2 ? side_streams(stream, sd) : -1;
-  if (side > 0) return ONETRANS_ERR_HIP;
-  if (side < 0)
-    return score_run(D, blk, cache, x_ns, n_users, n_cand, out_ns, (char *)ws, ws_layout(D, n, tin, rq, kv), stream);
-  // two halves of the users on two streams (users are independent), joined back into `stream`
-  const int u0 = (n_users + 1) / 2;
-  const Ws L = ws_layout(D, (size_t)u0 * n_cand, tin, rq, kv);
-  onetrans_kv_cache hb = *cache;   // the second half's users
-  const size_t user_bytes = (size_t)D.N * D.H * cache->capacity * D.dh * D.esz;
-  hb.k = (char *)cache->k + u0 * user_bytes;
-  hb.v = (char *)cache->v + u0 * user_bytes;
-  hb.n_users = cache->n_users - u0;
-  hb.user_len = cache->user_len ? cache->user_len + u0 : nullptr;
+  if (ws_bytes < ws_layout(D, (size_t)((n_users + wp - 1) / wp) * n_cand, tin, rq, kv).total * wp)
+    return ONETRANS_ERR_WORKSPACE;
+  const size_t part_bytes = ws_layout(D, (size_t)((n_users + parts - 1) / parts) * n_cand, tin, rq, kv).total;
   const size_t in_user = (size_t)n_cand * D.lns * D.d * D.esz, out_user = (size_t)n_cand * D.lns * D.d * 4;
-  if (hipEventRecord(sd->fork, stream) != hipSuccess || hipStreamWaitEvent(sd->s, sd->fork, 0) != hipSuccess)
-    return ONETRANS_ERR_HIP;
-  if ((rc = score_run(D, blk, cache, x_ns, u0, n_cand, out_ns, (char *)ws, L, stream))) return rc;
-  if ((rc = score_run(D, blk, &hb, (const char *)x_ns + u0 * in_user, n_users - u0, n_cand,
-                      (char *)out_ns + u0 * out_user, (char *)ws + L.total, L, sd->s)))
-    return rc;
-  if (hipEventRecord(sd->join, sd->s) != hipSuccess || hipStreamWaitEvent(stream, sd->join, 0) != hipSuccess)
-    return ONETRANS_ERR_HIP;
-  return ONETRANS_OK;
+  return over_streams(n_users, parts, stream, [&](int first, int count, int part, hipStream_t st) {
+    const onetrans_kv_cache view = user_view(D, cache, first);
+    return score_run(D, blk, &view, (const char *)x_ns + first * in_user, count, n_cand,
+                     (char *)out_ns + first * out_user, (char *)ws + part * part_bytes,
+                     ws_layout(D, (size_t)count * n_cand, tin, rq, kv), st);
+  });
 }
 
 int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weights *blk, onetrans_kv_cache *cache,
@@ -885,38 +879,20 @@ int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weig
   size_t n, tin, rq;
   bool kv;
   ws_dims(cfg, D, ONETRANS_OP_APPEND, n_users, 0, 0, d_l, n, tin, rq, kv);
-  const int wp = append_ws_parts(n_users), parts = append_parts(n_users);
+  const int wp = ws_parts_for(n_users, USER_PART_MIN), parts = parts_for(n_users, USER_PART_MIN);
   if (misaligned(ws)) return ONETRANS_ERR_ALIGNMENT;
   if (!ws) return ONETRANS_ERR_INVALID_ARG;
   if (ws_bytes < ws_layout(D, (n_users + wp - 1) / wp, tin, rq, kv).total * wp) return ONETRANS_ERR_WORKSPACE;
   const int l_old = ragged ? 0 : cache->layer_len[0];
-  Side *sd = nullptr;
-  const int side = parts == 2 ? side_streams(stream, sd) : -1;
-  if (side > 0) return ONETRANS_ERR_HIP;
-  if (side < 0) {
-    if ((rc = append_run(D, blk, cache, x_new, n_users, d_l, out_new, (char *)ws, ws_layout(D, n_users, tin, rq, kv),
-                         l_old, stream)))
-      return rc;
-  } else {
-    // two halves of the users on two streams (users are independent), joined back into `stream`
-    const int u0 = (n_users + 1) / 2;
-    const Ws L = ws_layout(D, u0, tin, rq, kv);
-    onetrans_kv_cache hb = *cache;   // the second half's users
-    const size_t user_bytes = (size_t)D.N * D.H * cache->capacity * D.dh * D.esz;
-    hb.k = (char *)cache->k + u0 * user_bytes;
-    hb.v = (char *)cache->v + u0 * user_bytes;
-    hb.n_users = cache->n_users - u0;
-    hb.user_len = ragged ? cache->user_len + u0 : nullptr;
-    if (hipEventRecord(sd->fork, stream) != hipSuccess || hipStreamWaitEvent(sd->s, sd->fork, 0) != hipSuccess)
-      return ONETRANS_ERR_HIP;
-    if ((rc = append_run(D, blk, cache, x_new, u0, d_l, out_new, (char *)ws, L, l_old, stream))) return rc;
-    const size_t in_user = (size_t)d_l * D.d * D.esz, out_user = (size_t)d_l * D.d * 4;
-    if ((rc = append_run(D, blk, &hb, (const char *)x_new + u0 * in_user, n_users - u0, d_l,
-                         out_new ? (char *)out_new + u0 * out_user : nullptr, (char *)ws + L.total, L, l_old, sd->s)))
-      return rc;
-    if (hipEventRecord(sd->join, sd->s) != hipSuccess || hipStreamWaitEvent(stream, sd->join, 0) != hipSuccess)
-      return ONETRANS_ERR_HIP;
-  }
+  const size_t part_bytes = ws_layout(D, (n_users + parts - 1) / parts, tin, rq, kv).total;
+  const size_t in_user = (size_t)d_l * D.d * D.esz, out_user = (size_t)d_l * D.d * 4;
+  rc = over_streams(n_users, parts, stream, [&](int first, int count, int part, hipStream_t st) {
+    const onetrans_kv_cache view = user_view(D, cache, first);
+    return append_run(D, blk, &view, (const char *)x_new + first * in_user, count, d_l,
+                      out_new ? (char *)out_new + first * out_user : nullptr, (char *)ws + part * part_bytes,
+                      ws_layout(D, count, tin, rq, kv), l_old, st);
+  });
+  if (rc) return rc;
   if (ragged) {
     int longest = 0;
     for (int u = 0; u < n_users; ++u) longest = max(longest, cache->user_len[u] += d_l);
@@ -1048,7 +1024,7 @@ const char *onetrans_status_string(int status) {
 const char *onetrans_version(void) { return "onetrans-gfx950 0.1"; }
 
 int onetrans_set_streams(int n) {
-  if (n != 1 && n != 2) return ONETRANS_ERR_INVALID_ARG;
+  if (n != 1 && n != 2 && n != 4) return ONETRANS_ERR_INVALID_ARG;
   g_streams = n;
   return ONETRANS_OK;
 }
