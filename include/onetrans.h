@@ -238,7 +238,6 @@ int onetrans_tokenize(const onetrans_config *cfg, const onetrans_tokenizer_confi
  * time, as a per-kernel profile needs). Parts are contiguous ranges of samples or users; results
  * are identical in every setting and workspace sizes do not depend on it. Process-wide setting.
  * Returns INVALID_ARG for other values. */
-
 int onetrans_set_streams(int n);
 
 /* Kernel classes of the per-launch timing below. */
