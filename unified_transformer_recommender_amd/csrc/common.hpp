@@ -245,6 +245,7 @@ struct QkvArgs {
   const void *wq, *wk, *wv;   // [G][d][d] storage dtype
   const void *gamma, *beta;   // norm1 [d]
   RowView stats;           // per-row (mean, rstd) of x from the previous block's tail, fp32; base null if absent
+  int tg;                  // token groups of 32 per wave (1, or 2 where the kernel supports it)
   int layer;
   float eps;
   float q_scale;           // queries are stored multiplied by this (log2(e) / sqrt(d_head))

@@ -9,7 +9,11 @@ namespace ot {
 
 // dtype: 0 = fp32 storage, 1 = bf16 storage. in_f32: block input rows are fp32 (1) or storage (0).
 hipError_t launch_qkv(int dtype, int in_f32, const QkvArgs &a, int grid, hipStream_t s);
-int qkv_tokens_per_tile(int dtype, int d_model);
+// Token groups of 32 per wave the QKV kernel supports for a dtype / d_model (QkvArgs::tg may be
+// that or 1), and the tokens per workgroup tile for a token-group count.
+int qkv_max_groups(int dtype, int d_model);
+int qkv_tokens_per_tile(int tg);
+constexpr int QKV_SMALL_LAUNCH = 128;   // below this many two-group tiles, one group per wave
 
 hipError_t launch_attn(int dtype, int d_head, int stage2, const AttnArgs &a, hipStream_t s);
 

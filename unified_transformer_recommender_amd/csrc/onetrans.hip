@@ -224,9 +224,8 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
   {
     QkvArgs qa;
     memset(&qa, 0, sizeof(qa));
-    const int bm = qkv_tokens_per_tile(D.dt, d);
     const int no_q = 0x7fffffff;
-    int nj = 0;
+    int nj = 0, bm = 0;
     long long tiles = 0;
     auto add_job = [&](RowSet rs, int q_from, HeadView k, HeadView v) {
       const long long m = (long long)rs.n_seq * rs.rows;
@@ -241,8 +240,17 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
       j.tile_start = (int)tiles;
       tiles += (long long)j.m_tiles * rs.n_groups;
     };
-    if (st.kv_n > 0) add_job(RowSet{st.n_seq, st.kv_n, 1, st.kv_t0, 0, 0}, st.need_out ? p0 : no_q, st.kS, st.vS);
-    if (st.ns > 0) add_job(RowSet{st.n_seq, 1, st.ns, st.s, 1, 1}, st.need_out ? st.s : no_q, st.kN, st.vN);
+    auto add_jobs = [&](int tg) {
+      nj = 0;
+      tiles = 0;
+      bm = qkv_tokens_per_tile(tg);
+      qa.tg = tg;
+      if (st.kv_n > 0) add_job(RowSet{st.n_seq, st.kv_n, 1, st.kv_t0, 0, 0}, st.need_out ? p0 : no_q, st.kS, st.vS);
+      if (st.ns > 0) add_job(RowSet{st.n_seq, 1, st.ns, st.s, 1, 1}, st.need_out ? st.s : no_q, st.kN, st.vN);
+    };
+    // two token groups per wave, unless that leaves fewer workgroups than half the GPU's CUs
+    add_jobs(qkv_max_groups(D.dt, d));
+    if (qa.tg == 2 && tiles < QKV_SMALL_LAUNCH) add_jobs(1);
     qa.n_jobs = nj;
     qa.d_model = d;
     qa.d_head = dh;

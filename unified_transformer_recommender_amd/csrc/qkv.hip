@@ -38,15 +38,17 @@ constexpr int QKV_NB = 2;                 // weight-chunk ring slots; loads run 
 // Token groups of 32 per wave: with two, every weight fragment read from LDS feeds two MFMAs
 // (half the LDS operand traffic and half the weight stream per token). The normalised rows of
 // both groups stay in registers, which bounds it to bf16 at d <= 256.
+// A launch with fewer than QKV_SMALL_LAUNCH two-group tiles (half the GPU's CUs) runs one token
+// group per wave instead: twice the workgroups, each with half the work, since the workgroups'
+// latency, not the LDS traffic, bounds such a launch.
 template <typename T, int D>
 constexpr int qkv_tg() { return (sizeof(T) == 2 && D <= 256) ? 2 : 1; }
 
-template <typename T, typename TI, int D, bool LAYER>
+template <typename T, typename TI, int D, bool LAYER, int TG>
 __global__ __launch_bounds__(QKV_NW * 64, 2) void qkv_kernel(const QkvArgs a) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int NW = QKV_NW;
-  constexpr int TG = qkv_tg<T, D>();
   constexpr int EPC = 16 / (int)sizeof(T);
   constexpr int DT = D / 32;                    // 32-feature chunks per projection
   constexpr int KC = D / M::KSTEP;
@@ -307,13 +309,21 @@ __global__ __launch_bounds__(QKV_NW * 64, 2) void qkv_kernel(const QkvArgs a) {
   }
 }
 
+template <typename T, typename TI, int D, int TG>
+hipError_t launch_dlt(const QkvArgs &a, int grid, hipStream_t s) {
+  if (a.layer)
+    hipLaunchKernelGGL((qkv_kernel<T, TI, D, true, TG>), dim3(grid), dim3(QKV_NW * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((qkv_kernel<T, TI, D, false, TG>), dim3(grid), dim3(QKV_NW * 64), 0, s, a);
+  return hipGetLastError();
+}
+
 template <typename T, typename TI, int D>
 hipError_t launch_dl(const QkvArgs &a, int grid, hipStream_t s) {
-  if (a.layer)
-    hipLaunchKernelGGL((qkv_kernel<T, TI, D, true>), dim3(grid), dim3(QKV_NW * 64), 0, s, a);
-  else
-    hipLaunchKernelGGL((qkv_kernel<T, TI, D, false>), dim3(grid), dim3(QKV_NW * 64), 0, s, a);
-  return hipGetLastError();
+  if constexpr (qkv_tg<T, D>() == 2) {
+    if (a.tg == 2) return launch_dlt<T, TI, D, 2>(a, grid, s);
+  }
+  return launch_dlt<T, TI, D, 1>(a, grid, s);
 }
 
 template <typename T, typename TI>
@@ -332,10 +342,12 @@ hipError_t launch_d(const QkvArgs &a, int grid, hipStream_t s) {
 
 }  // namespace
 
-int qkv_tokens_per_tile(int dtype, int d_model) {
-  if (dtype == 1) return QKV_NW * 32 * (d_model <= 256 ? qkv_tg<bf16, 256>() : qkv_tg<bf16, 512>());
-  return QKV_NW * 32 * qkv_tg<float, 256>();
+int qkv_max_groups(int dtype, int d_model) {
+  if (dtype == 1) return d_model <= 256 ? qkv_tg<bf16, 256>() : qkv_tg<bf16, 512>();
+  return qkv_tg<float, 256>();
 }
+
+int qkv_tokens_per_tile(int tg) { return QKV_NW * 32 * tg; }
 
 hipError_t launch_qkv(int dtype, int in_f32, const QkvArgs &a, int grid, hipStream_t s) {
   if (grid == 0) return hipSuccess;
