@@ -110,10 +110,12 @@ size_t onetrans_kv_cache_bytes(const onetrans_config *cfg, int n_users, int capa
 /* Monolithic forward of the block stack (sections 7.5.1-7.5.2) over `batch` independent samples.
  *   x0  [batch][l_s + l_ns][d] storage dtype: S rows then NS rows of each sample.
  *   out [batch][q_last + l_ns][d] fp32: final block rows (tail S rows then NS rows).
- * A batch of 64 or more samples runs as two halves, the second on a stream the library creates
- * once per device (default priority); it forks from and joins back into `stream` with events, so
- * the call is still ordered on `stream` alone. Concurrent calls from several host threads on one
- * device are not supported (they share that stream's fork/join events).
+ * A batch of 64 or more samples runs as two halves (onetrans_set_streams), the second on a stream
+ * the library creates once per device (default priority, kept until the process ends); it forks
+ * from and joins back into `stream` with events, so the call is still ordered on `stream` alone.
+ * When `stream` belongs to another device than the current one the call stays on `stream`.
+ * Concurrent calls from several host threads on one device are not supported (they share those
+ * streams' fork/join events).
  * Errors: INVALID_ARG, SHAPE, UNSUPPORTED, WORKSPACE, ALIGNMENT, HIP. */
 int onetrans_forward(const onetrans_config *cfg, const onetrans_block_weights *blk /* host [n_blocks] */,
                      const void *x0, int batch, int l_s, void *out, void *ws, size_t ws_bytes,
