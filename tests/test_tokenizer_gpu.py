@@ -126,6 +126,16 @@ def test_tokenize_time_merge_full_size_sampled():
     _case(w, samples=w.parity_subset)
 
 
+def test_tokenize_d512_model():
+    """The OneTransL-shaped model (d = 512, 16 NS tokens): output tiles of 512-wide rows, hidden widths
+    up to 512, a 2 x 8192-wide Auto-Split output per sample."""
+    base = synth.tok_workload("tok_mid", "bf16")
+    w = replace(base, key="tok_l", model=synth.workload("onetrans_l").model, seq_lens=(20, 33, 0),
+                seq_dims=(128, 64, 64), seq_hidden=(256, 512, 64), ns_dim=256, ns_hidden=512, batch=3)
+    _case(w)
+    _case(replace(w, merge="time"))
+
+
 def test_tokenize_full_size_sampled():
     w = synth.tok_workload("tokenize_s")
     _case(w, samples=w.parity_subset)
