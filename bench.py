@@ -82,6 +82,30 @@ def blas_threads() -> int:
     return len(os.sched_getaffinity(0))
 
 
+def host_info() -> dict:
+    """CPU model (from /proc/cpuinfo) and the BLAS library NumPy calls (vendor, version, threads)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            i = libs[0]
+            blas = f"{i.get('internal_api')} {i.get('version')} ({i.get('threading_layer', 'threads')}, " \
+                   f"{i.get('num_threads')} threads, {i.get('architecture')})"
+    except Exception:
+        pass
+    return {"cpu_model": model, "blas": blas}
+
+
 def roofline_entry(name, work, ms, launches, peak, unit, bound):
     achieved = work / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
     return {"kernel": name, "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
@@ -191,7 +215,7 @@ def bench_tokenize(a):
         cpu_s = time.perf_counter() - t0
         cpu = {"value": round(done / cpu_s, 4), "unit": "samples/s", "cores": blas_threads(), "kind": "oracle",
                "sample": f"{done} samples of the same workload, one at a time (input generation included)",
-               "seconds": round(cpu_s, 2)}
+               "seconds": round(cpu_s, 2), **host_info()}
     kernels = {k: {"ms_per_step": round(ms / a.steps, 4), "launches_per_step": n // a.steps}
                for k, (ms, n) in timing.items() if n}
     print(json.dumps({
@@ -398,7 +422,8 @@ def main():
             units = done
         cpu_s = time.perf_counter() - t0 if w.kind != "append" else t_app
         cpu = {"value": round(units / cpu_s, 4), "unit": "candidates/s" if w.kind != "append" else "users/s",
-               "cores": blas_threads(), "kind": "oracle", "sample": sample, "seconds": round(cpu_s, 2)}
+               "cores": blas_threads(), "kind": "oracle", "sample": sample, "seconds": round(cpu_s, 2),
+               **host_info()}
 
     unit = "candidates/s" if w.kind != "append" else "user appends/s"
     line = {

@@ -18,8 +18,10 @@
  *     aligned. The caller owns all memory (inputs, outputs, weights, workspace, K/V cache); the
  *     library never allocates or frees device memory.
  *   - Calls are asynchronous on `stream` (NULL = the null stream). Buffers must stay alive until
- *     the stream has passed the call. Argument validation happens on the host before anything is
- *     enqueued; a call that returns an error other than ONETRANS_ERR_HIP has enqueued nothing.
+ *     the stream has passed the call. Argument validation (shapes, launch sizes, workspace, cache
+ *     capacity) happens on the host before anything is enqueued; a call that returns an error
+ *     other than ONETRANS_ERR_HIP has enqueued nothing and changed no host state (layer_len,
+ *     user_len). A call whose launch grids would not fit a 32-bit int returns SHAPE.
  *     Device faults surface at the caller's synchronisation or as ONETRANS_ERR_HIP of a later call.
  *   - Storage dtype (config.dtype) applies to X(0) / x_s / x_ns / x_new, all weights and norm
  *     parameters, and the K/V cache. Arithmetic accumulates in fp32; the residual stream between
@@ -90,8 +92,10 @@ typedef struct {
                              by prefill_user (s_n) and advanced by append_events (+d_l) */
   int *user_len;          /* host [n_users] or NULL. Ragged users: when set, user u's valid rows are
                              the first user_len[u] rows of every block (an unpyramided cache) and
-                             the calls below read and advance it per user; layer_len then holds the
-                             largest user_len. NULL: every user has layer_len[n] rows. */
+                             the calls below read and advance it per user. layer_len then bounds
+                             them: prefill_user sets it to l_s (the padded length), append_events
+                             raises it to the largest user_len if that is larger. NULL: every user
+                             has layer_len[n] rows. */
 } onetrans_kv_cache;
 
 /* Workspace bytes needed by one call of `op`.

@@ -4,8 +4,9 @@ TEST INFRASTRUCTURE. Only tests, the smoke check and the benchmark's CPU-baselin
 module; the HIP product path shares no code with it.
 
 Source: fun-rec-mdbook (English), chapter 7.5 "OneTrans", section 7.5.0 "Unified Tokenization"
-(the equations for the aligned sequences, S-tokens, NS-tokens and X(0)); the Chinese edition's
-section 2.1 names the Auto-Split tokenizer as the one that saves kernel launches.
+(the equations for the aligned sequences, S-tokens, NS-tokens and X(0)); the paper-daily deep
+reading of the OneTrans paper, section 2.1 "Unified Tokenization", recommends the Auto-Split
+tokenizer because one MLP instead of one per feature group saves kernel launches.
 
 What is computed, per sample and independently:
 

@@ -103,6 +103,23 @@ def test_forward_validation_errors():
     assert _fwd(_cfg(norm=L.LAYERNORM), nb) == L.ERR_INVALID_ARG
 
 
+def test_launch_sizes_checked_before_enqueue():
+    """Calls whose launch grids would not fit a 32-bit int fail validation (SHAPE) on the host, before
+    the workspace check and before any HIP call, and advance no cache length."""
+    lib = L.lib()
+    c, b = _cfg(), _blocks(2)
+    assert _fwd(c, b, B=1 << 21) == L.ERR_SHAPE                    # 2^21 x 136 rows x 8 heads > 2^31
+    assert _fwd(c, b, B=1 << 20, wsb=1024) == L.ERR_WORKSPACE       # fits: 2^20 x 136 x 8 < 2^31
+    kc = _cache(n_users=1 << 20, lens=(120, 120))
+    assert lib.onetrans_score_candidates(ctypes.byref(c), b, ctypes.byref(kc), FAKE, 1 << 20, 64, FAKE, FAKE,
+                                         1 << 40, None) == L.ERR_SHAPE
+    flat = _cfg(sq=(120, 120))
+    kc = _cache(n_users=1 << 22, cap=200, lens=(120, 120))
+    assert lib.onetrans_append_events(ctypes.byref(flat), b, ctypes.byref(kc), FAKE, 1 << 22, 64, None, FAKE,
+                                      1 << 40, None) == L.ERR_SHAPE
+    assert list(kc._keep) == [120, 120]
+
+
 def _cache(n_users=2, cap=200, lens=(120, 100)):
     ll = (ctypes.c_int * len(lens))(*lens)
     kc = L.KVCache(FAKE, FAKE, n_users, cap, ll)

@@ -74,10 +74,9 @@ def test_d128_shape_both_norms(norm):
     _forward_case(w)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_two_stage_small(dtype):
-    w = synth.test_workload("tiny3_two_stage", dtype)
-    say(f"[two_stage] {w.key} dtype={dtype}")
+def _two_stage_case(w):
+    dtype = w.model.dtype
+    say(f"[two_stage] {w.key} dtype={dtype} d={w.model.d_model} norm={w.model.norm}")
     mdl = model(w)
     m, ws = w.model, weights(w.model)
     xs = synth.user_sequences(w)
@@ -87,7 +86,11 @@ def test_two_stage_small(dtype):
     ob.onetrans_prefill_user(mdl, dev(xs, mdl), cache, out_s)
     out = ob.onetrans_score_candidates(mdl, cache, dev(xn, mdl))
     torch.cuda.synchronize()
-    assert cache.lengths == [32, 32, 20]
+    expect_len, s = [], w.l_s
+    for q in w.s_queries:
+        expect_len.append(s)
+        s = q
+    assert cache.lengths == expect_len
     for u in range(w.n_users):
         rc, rs = O.prefill_user(xs[u], ws, m, w.s_queries)
         assert rel_err(out_s[u].cpu().numpy(), rs) <= TOL[dtype]
@@ -99,10 +102,9 @@ def test_two_stage_small(dtype):
             assert e <= TOL[dtype]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_append_small(dtype):
-    w = synth.test_workload("tiny3_append", dtype)
-    say(f"[append] {w.key} dtype={dtype}")
+def _append_case(w):
+    dtype = w.model.dtype
+    say(f"[append] {w.key} dtype={dtype} d={w.model.d_model} norm={w.model.norm}")
     m, ws = w.model, weights(w.model)
     mdl = model(w, s_queries=(w.l_old,) * m.n_blocks)
     old, new = synth.append_batch(w)
@@ -123,6 +125,40 @@ def test_append_small(dtype):
         e = rel_err(sc[u, 0].cpu().numpy(), O.score_candidate(nc, xn[u, 0], ws, m))
         say(f"  user {u}: score err {e:.3e}")
         assert e <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_two_stage_small(dtype):
+    _two_stage_case(synth.test_workload("tiny3_two_stage", dtype))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_append_small(dtype):
+    _append_case(synth.test_workload("tiny3_append", dtype))
+
+
+def _wide_layernorm_model(d):
+    """The OneTransS-like widths at d (d_head 32, d_ff = 4 d) with LayerNorm, 3 blocks, bf16."""
+    return replace(synth.workload("onetrans_s").model, name=f"ln{d}", n_blocks=3, d_model=d, n_heads=d // 32,
+                   d_ff=4 * d, norm="layer", norm_eps=1e-5, dtype="bf16", weight_seed=1200 + d)
+
+
+@pytest.mark.parametrize("d", [256, 512])
+def test_layernorm_bf16_wide_forward(d):
+    """bf16 LayerNorm at d >= 256: block 1's norm 1 takes the row statistics in the QKV kernel (one
+    pass about the row's first element), blocks 2 and 3 read the (mean, rstd) that the previous
+    block's post kernel wrote; pyramid with ragged tiles and a batch of 5."""
+    base = synth.workload("onetrans_s")
+    w = replace(base, model=_wide_layernorm_model(d), l_s=203, s_queries=(203, 131, 5), seq_lens=(60, 70, 70),
+                batch=5, key=f"ln{d}_fwd")
+    _forward_case(w)
+
+
+def test_layernorm_bf16_d256_two_stage_and_append():
+    """The same LayerNorm statistics handoff on Stage I / Stage II and on append (d = 256)."""
+    m = _wide_layernorm_model(256)
+    _two_stage_case(replace(synth.test_workload("tiny3_two_stage"), model=m, key="ln256_two_stage"))
+    _append_case(replace(synth.test_workload("tiny3_append"), model=m, key="ln256_append"))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

@@ -166,3 +166,50 @@ def test_time_merge_is_a_sorted_permutation():
     np.testing.assert_array_equal(x[:w.l_s], rows[idx])
     assert sorted(idx) == list(range(w.l_s))
     assert np.all(np.diff(t_all[idx]) >= 0)
+
+
+# --- the batched form used as the expectation of the GPU tokenizer tests ------------------------
+
+def test_tokenize_batch_hand_worked_two_samples():
+    # Two samples, two types, identity-like MLPs (MLP(x) = [x, 0] in the linear regime), so X(0)
+    # is written out by hand. Intent merge: [A events; SEP_A; B events; SEP_B; NS rows]. The Auto-
+    # Split MLP is the identity on its 4 features (linear regime again), so NS row j of a sample is
+    # its feature pair j. Samples differ in every entry, so a swapped sample, a shifted row or a
+    # mixed-up time fails.
+    ident = _identity_mlp()
+    ns_mlp = {"w1": np.eye(4), "b1": np.full(4, 40.0), "w2": np.eye(4), "b2": np.full(4, -40.0)}
+    tw = {"seq": [ident, ident], "sep": np.array([[0.0, 7.0], [0.0, 8.0]]), "ns": ns_mlp}
+    ev = [np.array([[[1.0], [2.0]], [[3.0], [4.0]]]),          # type A: [B=2][L=2][1]
+          np.array([[[5.0]], [[6.0]]])]                        # type B: [B=2][L=1][1]
+    ns = np.array([[0.1, 0.2, 0.3, 0.4], [0.5, 0.6, 0.7, 0.8]])
+    got = oracle.tokenize_batch(ev, ns, tw, 2)
+    expect = [[[1, 0], [2, 0], [0, 7], [5, 0], [0, 8], [0.1, 0.2], [0.3, 0.4]],
+              [[3, 0], [4, 0], [0, 7], [6, 0], [0, 8], [0.5, 0.6], [0.7, 0.8]]]
+    np.testing.assert_allclose(got, expect, atol=1e-12)
+    # timestamp-aware: sample 0 has B's event first (time 0 < 1 < 2), sample 1 last (time 9)
+    times = [np.array([[1, 2], [1, 2]]), np.array([[0], [9]])]
+    got = oracle.tokenize_batch(ev, ns, tw, 2, times=times)
+    expect = [[[5, 8], [1, 7], [2, 7], [0.1, 0.2], [0.3, 0.4]],
+              [[3, 7], [4, 7], [6, 8], [0.5, 0.6], [0.7, 0.8]]]
+    np.testing.assert_allclose(got, expect, atol=1e-12)
+
+
+@pytest.mark.parametrize("key", ["tok_mid", "tok_mid_time"])
+def test_tokenize_batch_is_per_sample_tokenize(key):
+    # Every sample of the batched form equals the (pinned) single-sample form on that sample's own
+    # events, features and times, and permuting the batch permutes the result.
+    w = synth.tok_workload(key)
+    tw = synth.tokenizer_weights(w)
+    samples = [0, 3, 1]
+    ev, ns = synth.tokenizer_batch(w, samples)
+    times = synth.tokenizer_times_batch(w, samples) if w.merge == "time" else None
+    got = oracle.tokenize_batch(ev, ns, tw, w.model.l_ns, times=times)
+    for i, b in enumerate(samples):
+        e1, n1 = synth.tokenizer_sample(w, b)
+        t1 = synth.tokenizer_times(w, b) if times is not None else None
+        np.testing.assert_array_equal(got[i], oracle.tokenize(e1, n1, tw, w.model.l_ns, times=t1))
+    assert not np.array_equal(got[0], got[1])
+    perm = [2, 0, 1]
+    got_p = oracle.tokenize_batch([e[perm] for e in ev], ns[perm], tw, w.model.l_ns,
+                                  times=None if times is None else [t[perm] for t in times])
+    np.testing.assert_array_equal(got_p, got[perm])

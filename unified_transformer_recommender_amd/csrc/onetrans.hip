@@ -107,6 +107,15 @@ int check_schedule(const onetrans_config *c, int l_s) {
   return ONETRANS_OK;
 }
 
+// Launch sizes of a call over n_seq sequences of at most `rows` block rows each: every kernel's
+// grid (QKV and post tiles: at most one per row; attention: query blocks x sequences x heads, at
+// most rows x sequences x heads) must fit a 32-bit int. Checked before anything is enqueued, so a
+// call that fails here has launched nothing.
+int check_size(const Dims &D, long long n_seq, long long rows) {
+  if (n_seq * rows * D.H > 0x7fffffffLL) return ONETRANS_ERR_SHAPE;
+  return ONETRANS_OK;
+}
+
 int check_weights(const onetrans_block_weights *blk, const Dims &D) {
   if (!blk) return ONETRANS_ERR_INVALID_ARG;
   for (int n = 0; n < D.N; ++n) {
@@ -269,7 +278,6 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
     qa.q_scale = 1.4426950408889634f / sqrtf((float)dh);
     qa.trash = ws + L.trash;
     qa.kv_shift = st.kv_shift;
-    if (tiles > 0x7fffffffLL) return ONETRANS_ERR_UNSUPPORTED;
     const hipError_t e = timed(ONETRANS_K_QKV, stream, [&] { return launch_qkv(D.dt, st.x_f32, qa, (int)tiles, stream); });
     if (e != hipSuccess) return ONETRANS_ERR_HIP;
   }
@@ -346,7 +354,6 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
     if (D.dt == ONETRANS_BF16 && d >= 256 && st.stats_out) pa.stats = RowView{st.stats_out, st.out.sb / d * 2, st.out.t_off, 2};
     pa.layer = D.layer;
     pa.eps = D.eps;
-    if (tiles > 0x7fffffffLL) return ONETRANS_ERR_UNSUPPORTED;
     const hipError_t e = timed(ONETRANS_K_POST, stream, [&] { return launch_post(D.dt, st.x_f32, pa, (int)tiles, stream); });
     if (e != hipSuccess) return ONETRANS_ERR_HIP;
   }
@@ -766,6 +773,7 @@ int onetrans_forward(const onetrans_config *cfg, const onetrans_block_weights *b
   if ((rc = check_weights(blk, D))) return rc;
   if (!x0 || !out) return ONETRANS_ERR_INVALID_ARG;
   if (misaligned(x0) || misaligned(out)) return ONETRANS_ERR_ALIGNMENT;
+  if ((rc = check_size(D, batch, (long long)l_s + D.lns))) return rc;
   size_t n, tin, rq;
   bool kv;
   ws_dims(cfg, D, ONETRANS_OP_FORWARD, batch, l_s, 0, 0, n, tin, rq, kv);
@@ -795,6 +803,7 @@ int onetrans_prefill_user(const onetrans_config *cfg, const onetrans_block_weigh
   if (misaligned(x_s) || (out_s && misaligned(out_s))) return ONETRANS_ERR_ALIGNMENT;
   if ((rc = check_cache(cache))) return rc;
   if (n_users > cache->n_users || l_s > cache->capacity) return ONETRANS_ERR_CACHE_CAPACITY;
+  if ((rc = check_size(D, n_users, l_s))) return rc;
   if (cache->user_len) {
     // ragged users: padding rows behind each user's sequence are only harmless without pruning
     for (int n = 0; n < D.N; ++n)
@@ -842,6 +851,7 @@ int onetrans_score_candidates(const onetrans_config *cfg, const onetrans_block_w
     if (cache->layer_len[n] < 0 || cache->layer_len[n] > cache->capacity) return ONETRANS_ERR_SHAPE;
   const bool ragged = cache->user_len != nullptr;
   if (ragged && (rc = check_user_len(cache, n_users, cache->capacity))) return rc;
+  if ((rc = check_size(D, (long long)n_users * n_cand, D.lns))) return rc;
   size_t n, tin, rq;
   bool kv;
   ws_dims(cfg, D, ONETRANS_OP_SCORE, n_users, 0, n_cand, 0, n, tin, rq, kv);
@@ -884,6 +894,7 @@ int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weig
   } else if ((long long)cache->layer_len[0] + d_l > cache->capacity) {
     return ONETRANS_ERR_CACHE_CAPACITY;
   }
+  if ((rc = check_size(D, n_users, d_l))) return rc;
   size_t n, tin, rq;
   bool kv;
   ws_dims(cfg, D, ONETRANS_OP_APPEND, n_users, 0, 0, d_l, n, tin, rq, kv);
