@@ -51,7 +51,8 @@ typedef enum {
   ONETRANS_ERR_WORKSPACE = -4,      /* ws_bytes smaller than onetrans_workspace_bytes() */
   ONETRANS_ERR_CACHE_CAPACITY = -5, /* cache too small for the rows to be written */
   ONETRANS_ERR_ALIGNMENT = -6,      /* a device pointer is not 16-byte aligned */
-  ONETRANS_ERR_HIP = -7             /* a HIP runtime call or kernel launch failed */
+  ONETRANS_ERR_HIP = -7,            /* a HIP runtime call or kernel launch failed */
+  ONETRANS_ERR_SCRATCH = -8         /* the call needs more than ONETRANS_SCRATCH_BYTES of scratch */
 } onetrans_status;
 
 typedef enum { ONETRANS_F32 = 0, ONETRANS_BF16 = 1 } onetrans_dtype;
@@ -156,6 +157,29 @@ int onetrans_score_candidates(const onetrans_config *cfg, const onetrans_block_w
                               const onetrans_kv_cache *cache, const void *x_ns, int n_users,
                               int n_cand, void *out_ns, void *ws, size_t ws_bytes,
                               hipStream_t stream);
+
+/* Allocation-free Stage II, for callers that cannot allocate device memory or create streams:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments, validation, work and results as onetrans_score_candidates, minus the workspace: the
+ * workspace lives in a static device array of the library, ONETRANS_SCRATCH_BYTES (64 MiB) per GPU,
+ * which each GPU the library runs on holds until the process ends. Its device address is looked up
+ * once per device (hipGetSymbolAddress, on the first call with that device current); after that the
+ * call makes no allocation of any kind: no hipMalloc / hipFree, no stream or event creation (the
+ * whole call runs on `stream`, never split over side streams, and the per-launch timing is not
+ * recorded for it).
+ *   Size limit: the call needs the workspace of one part, at most
+ *   onetrans_workspace_bytes(cfg, ONETRANS_OP_SCORE, n_users, 0, n_cand, 0) bytes (about
+ *   64 KiB per candidate at d = 256 with 16 NS tokens, 128 KiB at d = 512): up to 1019 candidates
+ *   per call at d = 256 with 16 NS tokens. A larger call returns ONETRANS_ERR_SCRATCH before anything is enqueued.
+ *   Sharing: every call on one GPU uses that GPU's one array. Each call writes every scratch byte
+ *   it reads before reading it (nothing has to start at zero), but calls that overlap in time on
+ *   one GPU (two streams, two host threads) race on the array; order them on one stream.
+ *   `stream` must belong to the current device (NULL = its null stream), otherwise INVALID_ARG.
+ * Errors: as onetrans_score_candidates (without WORKSPACE), plus SCRATCH. */
+#define ONETRANS_SCRATCH_BYTES (64u << 20)
+int onetrans_score_candidates_noalloc(const onetrans_config *cfg, const onetrans_block_weights *blk,
+                                      const onetrans_kv_cache *cache, const void *x_ns, int n_users,
+                                      int n_cand, void *out_ns, hipStream_t stream);
 
 /* Cross-request append (section 7.5.3): `d_l` new S rows per user at positions L_old..L_old+d_l-1
  * behind the L_old cached rows. Only the new rows are computed (shared S parameters, keys = cached

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert "onetrans_forward" in names and "onetrans_tokenize" in names and len(names) == 13
+    assert "onetrans_forward" in names and "onetrans_tokenize" in names and len(names) == 14
     lib = L.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -293,3 +293,19 @@ def test_status_strings():
     for s in range(-7, 1):
         assert L.status_string(s) not in ("", "unknown status")
     assert L.status_string(-99) == "unknown status"
+
+
+def test_noalloc_score_validation():
+    """The allocation-free Stage II validates like onetrans_score_candidates and refuses a call past
+    its static scratch (SCRATCH) on the host, before any HIP call."""
+    lib = L.lib()
+    c, b = _cfg(), _blocks(2)
+    kc = _cache()
+    f = lib.onetrans_score_candidates_noalloc
+    assert f(ctypes.byref(c), b, ctypes.byref(kc), FAKE, 3, 4, FAKE, None) == L.ERR_SHAPE       # users > cache
+    assert f(ctypes.byref(c), b, ctypes.byref(kc), None, 2, 4, FAKE, None) == L.ERR_INVALID_ARG
+    assert f(ctypes.byref(c), b, ctypes.byref(kc), FAKE, 2, 4, FAKE + 4, None) == L.ERR_ALIGNMENT
+    assert f(ctypes.byref(_cfg(lns=0)), b, ctypes.byref(kc), FAKE, 2, 4, FAKE, None) == L.ERR_SHAPE
+    per = lib.onetrans_workspace_bytes(ctypes.byref(c), L.OP_SCORE, 1, 0, 1, 0)
+    assert f(ctypes.byref(c), b, ctypes.byref(kc), FAKE, 2, L.SCRATCH_BYTES // per, FAKE, None) == L.ERR_SCRATCH
+    assert "scratch" in L.status_string(L.ERR_SCRATCH)

@@ -16,6 +16,8 @@ ERR_WORKSPACE = -4
 ERR_CACHE_CAPACITY = -5
 ERR_ALIGNMENT = -6
 ERR_HIP = -7
+ERR_SCRATCH = -8
+SCRATCH_BYTES = 64 << 20     # ONETRANS_SCRATCH_BYTES
 
 F32, BF16 = 0, 1
 RMSNORM, LAYERNORM = 0, 1
@@ -61,6 +63,8 @@ SIGNATURES = {
                                       POINTER(KVCache), c_void_p, c_void_p, c_size_t, c_void_p]),
     "onetrans_score_candidates": (c_int, [POINTER(Config), POINTER(BlockWeights), POINTER(KVCache), c_void_p,
                                           c_int, c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "onetrans_score_candidates_noalloc": (c_int, [POINTER(Config), POINTER(BlockWeights), POINTER(KVCache),
+                                                  c_void_p, c_int, c_int, c_void_p, c_void_p]),
     "onetrans_append_events": (c_int, [POINTER(Config), POINTER(BlockWeights), POINTER(KVCache), c_void_p,
                                        c_int, c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
     "onetrans_tokenize_workspace_bytes": (c_size_t, [POINTER(Config), POINTER(TokenizerConfig), c_int]),

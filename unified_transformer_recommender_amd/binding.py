@@ -180,6 +180,19 @@ def onetrans_score_candidates(model: Model, cache: KVCache, x_ns: torch.Tensor,
     return out_ns
 
 
+def onetrans_score_candidates_noalloc(model: Model, cache: KVCache, x_ns: torch.Tensor, out_ns: torch.Tensor,
+                                      stream=None) -> torch.Tensor:
+    """Stage II without a workspace argument (the library's static device scratch): x_ns [U][C][l_ns][d]
+    -> out_ns [U][C][l_ns][d] fp32, both given by the caller; nothing is allocated here either."""
+    _check_input(model, x_ns, 4, "x_ns")
+    U, C, _, d = x_ns.shape
+    st = L.lib().onetrans_score_candidates_noalloc(ctypes.byref(model.cfg), model.blocks, ctypes.byref(cache.c),
+                                                   x_ns.data_ptr(), U, C, out_ns.data_ptr(),
+                                                   _stream(x_ns.device, stream))
+    L.check(st, "onetrans_score_candidates_noalloc")
+    return out_ns
+
+
 def onetrans_append_events(model: Model, cache: KVCache, x_new: torch.Tensor,
                            out_new: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
                            stream=None) -> Optional[torch.Tensor]:

@@ -49,9 +49,12 @@ hipEvent_t take_event() {
 }
 
 // Runs `launch` (returning hipError_t); with timing on, brackets it with events on `s`.
+// Set while an allocation-free call runs: no timing events are created or recorded for it.
+thread_local bool t_untimed = false;
+
 template <class F>
 hipError_t timed(int cls, hipStream_t s, F &&launch) {
-  if (!g_timing) return launch();
+  if (!g_timing || t_untimed) return launch();
   hipEvent_t a = take_event(), b = take_event();
   if (!a || !b) return hipErrorOutOfMemory;
   if (hipEventRecord(a, s) != hipSuccess) return hipErrorInvalidValue;
@@ -394,6 +397,48 @@ int upload_user_len(const onetrans_kv_cache *c, int n_users, char *ws, const Ws 
 inline HeadView cache_view(const Dims &D, const onetrans_kv_cache *c, void *base, int n) {
   const long long per_head = (long long)c->capacity * D.dh;
   return HeadView{(char *)base + (size_t)n * D.H * per_head * D.esz, (long long)D.N * D.H * per_head, per_head, 0};
+}
+
+// Arguments of a Stage II call (everything but the workspace).
+int check_score(const onetrans_config *cfg, const onetrans_block_weights *blk, const onetrans_kv_cache *cache,
+                const void *x_ns, int n_users, int n_cand, const void *out_ns, Dims &D) {
+  int rc;
+  if ((rc = check_cfg(cfg, D))) return rc;
+  if (n_users < 1 || n_cand < 1) return ONETRANS_ERR_SHAPE;
+  if (D.lns < 1) return ONETRANS_ERR_SHAPE;
+  if ((rc = check_weights(blk, D))) return rc;
+  if (!x_ns || !out_ns) return ONETRANS_ERR_INVALID_ARG;
+  if (misaligned(x_ns) || misaligned(out_ns)) return ONETRANS_ERR_ALIGNMENT;
+  if ((rc = check_cache(cache))) return rc;
+  if (n_users > cache->n_users) return ONETRANS_ERR_SHAPE;
+  for (int n = 0; n < D.N; ++n)
+    if (cache->layer_len[n] < 0 || cache->layer_len[n] > cache->capacity) return ONETRANS_ERR_SHAPE;
+  if (cache->user_len && (rc = check_user_len(cache, n_users, cache->capacity))) return rc;
+  return check_size(D, (long long)n_users * n_cand, D.lns);
+}
+
+// ---- allocation-free Stage II: a library-owned device scratch ----------------------------------
+// Stage II's workspace (block outputs, row statistics, Q/K/V/O of the candidates' NS rows, the
+// ragged users' lengths) lives in this array instead of a caller buffer. It is in every GPU's copy
+// of the library's device code and stays until the process ends. Host code never uses the array's
+// name as an address (on the host it only stands for the symbol): the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and kernels receive it as
+// their workspace pointer.
+static __device__ __align__(256) unsigned char scratch[ONETRANS_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+void *g_scratch[MAX_DEVICES];   // device address of `scratch` per device (null until first use)
+
+// The current device's scratch address, looked up on the first call on that device.
+int scratch_ptr(int dev, void *&out) {
+  if (dev < 0 || dev >= MAX_DEVICES) return ONETRANS_ERR_HIP;
+  if (!g_scratch[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ONETRANS_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  out = g_scratch[dev];
+  return ONETRANS_OK;
 }
 
 // ---- tokenizers (section 7.5.0) ----------------------------------------------------------------
@@ -839,19 +884,7 @@ int onetrans_score_candidates(const onetrans_config *cfg, const onetrans_block_w
                               void *out_ns, void *ws, size_t ws_bytes, hipStream_t stream) {
   Dims D;
   int rc;
-  if ((rc = check_cfg(cfg, D))) return rc;
-  if (n_users < 1 || n_cand < 1) return ONETRANS_ERR_SHAPE;
-  if (D.lns < 1) return ONETRANS_ERR_SHAPE;
-  if ((rc = check_weights(blk, D))) return rc;
-  if (!x_ns || !out_ns) return ONETRANS_ERR_INVALID_ARG;
-  if (misaligned(x_ns) || misaligned(out_ns)) return ONETRANS_ERR_ALIGNMENT;
-  if ((rc = check_cache(cache))) return rc;
-  if (n_users > cache->n_users) return ONETRANS_ERR_SHAPE;
-  for (int n = 0; n < D.N; ++n)
-    if (cache->layer_len[n] < 0 || cache->layer_len[n] > cache->capacity) return ONETRANS_ERR_SHAPE;
-  const bool ragged = cache->user_len != nullptr;
-  if (ragged && (rc = check_user_len(cache, n_users, cache->capacity))) return rc;
-  if ((rc = check_size(D, (long long)n_users * n_cand, D.lns))) return rc;
+  if ((rc = check_score(cfg, blk, cache, x_ns, n_users, n_cand, out_ns, D))) return rc;
   size_t n, tin, rq;
   bool kv;
   ws_dims(cfg, D, ONETRANS_OP_SCORE, n_users, 0, n_cand, 0, n, tin, rq, kv);
@@ -868,6 +901,33 @@ int onetrans_score_candidates(const onetrans_config *cfg, const onetrans_block_w
                      (char *)out_ns + first * out_user, (char *)ws + part * part_bytes,
                      ws_layout(D, (size_t)count * n_cand, tin, rq, kv), st);
   });
+}
+
+int onetrans_score_candidates_noalloc(const onetrans_config *cfg, const onetrans_block_weights *blk,
+                                      const onetrans_kv_cache *cache, const void *x_ns, int n_users, int n_cand,
+                                      void *out_ns, hipStream_t stream) {
+  Dims D;
+  int rc;
+  if ((rc = check_score(cfg, blk, cache, x_ns, n_users, n_cand, out_ns, D))) return rc;
+  // one part on the caller's stream: the whole call's workspace in the scratch
+  size_t n, tin, rq;
+  bool kv;
+  ws_dims(cfg, D, ONETRANS_OP_SCORE, n_users, 0, n_cand, 0, n, tin, rq, kv);
+  const Ws L = ws_layout(D, n, tin, rq, kv);
+  if (L.total > (size_t)ONETRANS_SCRATCH_BYTES) return ONETRANS_ERR_SCRATCH;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ONETRANS_ERR_HIP;
+  if (stream) {
+    hipDevice_t sdev = 0;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return ONETRANS_ERR_HIP;
+    if ((int)sdev != dev) return ONETRANS_ERR_INVALID_ARG;   // the scratch address is per device
+  }
+  void *w = nullptr;
+  if ((rc = scratch_ptr(dev, w))) return rc;
+  t_untimed = true;
+  rc = score_run(D, blk, cache, x_ns, n_users, n_cand, out_ns, (char *)w, L, stream);
+  t_untimed = false;
+  return rc;
 }
 
 int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weights *blk, onetrans_kv_cache *cache,
@@ -1036,6 +1096,7 @@ const char *onetrans_status_string(int status) {
     case ONETRANS_ERR_CACHE_CAPACITY: return "kv cache capacity exceeded";
     case ONETRANS_ERR_ALIGNMENT: return "device pointer not 16-byte aligned";
     case ONETRANS_ERR_HIP: return "HIP runtime error";
+    case ONETRANS_ERR_SCRATCH: return "call needs more than the library's static scratch (ONETRANS_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
