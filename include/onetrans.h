@@ -29,8 +29,7 @@
  *   - Weight matrices are (out, in) row-major, like torch.nn.Linear: y = W x. Each matrix is
  *     stored as [1 + l_ns][rows][cols]: index 0 is the shared S set, 1 + j is NS token j.
  *   - No exceptions cross the boundary; every entry point returns an onetrans_status.
- *   - Supported shapes: d_head = d_model / n_heads in {16, 32}; d_model in {64, 128, 256, 512}
- *     (fp32 storage: up to 256);
+ *   - Supported shapes: d_head = d_model / n_heads in {16, 32}; d_model in {64, 128, 256, 512};
  *     d_ff a multiple of 64, at most 2048; 0 <= l_ns <= 32 (>= 1 for score_candidates).
  */
 #ifndef ONETRANS_H_

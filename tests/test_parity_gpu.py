@@ -292,6 +292,34 @@ def test_onetrans_l_forward_bf16_full_batch():
     _forward_case(w, samples=w.parity_subset)
 
 
+def test_onetrans_l_forward_f32_mode():
+    """fp32 mode of the OneTransL shape (d = 512): the fp32 QKV kernel with one workgroup per CU
+    and the 16-token-tile fp32 post kernel, over the whole 8-block pyramid 2048 -> 32."""
+    w = replace(synth.workload("onetrans_l", "f32"), batch=4)
+    _forward_case(w, samples=(0, 3))
+
+
+def _f32_wide_model(norm):
+    return replace(synth.workload("onetrans_l").model, name=f"f32w_{norm}", n_blocks=3, norm=norm,
+                   norm_eps=1e-6 if norm == "rms" else 1e-5, dtype="f32", weight_seed=1250)
+
+
+@pytest.mark.parametrize("norm", ["rms", "layer"])
+def test_f32_d512_ragged_tiles(norm):
+    """fp32 at d = 512 with both norms: 3 blocks, a pyramid with ragged 64-token post tiles and 128-
+    token QKV tiles (203 -> 131 -> 5 S rows, 16 NS rows), batch 5."""
+    base = synth.workload("onetrans_l")
+    w = replace(base, model=_f32_wide_model(norm), l_s=203, s_queries=(203, 131, 5), seq_lens=(60, 70, 70),
+                batch=5, key=f"f32_d512_{norm}")
+    _forward_case(w)
+
+
+def test_f32_d512_two_stage_and_append():
+    m = _f32_wide_model("rms")
+    _two_stage_case(replace(synth.test_workload("tiny3_two_stage"), model=m, key="f32_d512_two_stage"))
+    _append_case(replace(synth.test_workload("tiny3_append"), model=m, key="f32_d512_append"))
+
+
 # --- GPU-side invariants ----------------------------------------------------------------------
 
 def test_gpu_two_stage_matches_gpu_forward():

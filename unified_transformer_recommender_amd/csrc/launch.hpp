@@ -20,6 +20,9 @@ hipError_t launch_attn(int dtype, int d_head, int stage2, const AttnArgs &a, hip
 // Fused post-attention kernel; tokens per workgroup tile for a dtype / d_model.
 hipError_t launch_post(int dtype, int resid_f32, const PostArgs &a, int grid, hipStream_t s);
 int post_tokens_per_tile(int dtype, int d_model);
+// fp32 storage at d = 512: the post-attention kernel on 16x16x4 MFMA tiles (16 tokens per wave).
+hipError_t launch_post_f32w(int d_model, const PostArgs &a, int grid, hipStream_t s);
+int post_f32w_tokens_per_tile();
 
 // Tokenizer kernels: grouped linear layer (rows / output features per workgroup) and [SEP] copy.
 hipError_t launch_lin(int dtype, const LinArgs &a, int grid, hipStream_t s);

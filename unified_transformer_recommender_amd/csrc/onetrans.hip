@@ -94,7 +94,6 @@ int check_cfg(const onetrans_config *c, Dims &D) {
   if (D.dh != 16 && D.dh != 32) return ONETRANS_ERR_UNSUPPORTED;
   if ((D.d != 64 && D.d != 128 && D.d != 256 && D.d != 512) || D.dff % 64 || D.dff > POST_MAX_DFF)
     return ONETRANS_ERR_UNSUPPORTED;
-  if (D.dt == ONETRANS_F32 && D.d > 256) return ONETRANS_ERR_UNSUPPORTED;
   if (D.lns > 32) return ONETRANS_ERR_UNSUPPORTED;
   return ONETRANS_OK;
 }

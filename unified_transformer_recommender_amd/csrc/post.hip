@@ -419,7 +419,7 @@ hipError_t launch_d(const PostArgs &a, int grid, hipStream_t s) {
     case 256: return launch_dl<T, TR, 256>(a, grid, s);
     case 512:
       if constexpr (sizeof(T) == 2) return launch_dl<T, TR, 512>(a, grid, s);
-      return hipErrorInvalidValue;   // fp32 storage at d = 512 is not supported
+      return launch_post_f32w(512, a, grid, s);   // fp32: the 16-token-tile kernel
     default:
       return hipErrorInvalidValue;
   }
@@ -429,6 +429,7 @@ hipError_t launch_d(const PostArgs &a, int grid, hipStream_t s) {
 
 int post_tokens_per_tile(int dtype, int d_model) {
   if (dtype == 1) return (d_model == 128 ? post_nw<bf16, 128>() : post_nw<bf16, 256>()) * 32;
+  if (d_model >= 512) return post_f32w_tokens_per_tile();
   return post_nw<float, 256>() * 32;
 }
 

@@ -44,8 +44,13 @@ constexpr int QKV_NB = 2;                 // weight-chunk ring slots; loads run 
 template <typename T, int D>
 constexpr int qkv_tg() { return (sizeof(T) == 2 && D <= 256) ? 2 : 1; }
 
+// Workgroups per CU the register budget is set for: two (256 registers per lane), except fp32 at
+// d = 512, whose normalised row alone takes 256 registers per lane (one workgroup, 512 registers).
+template <typename T, int D>
+constexpr int qkv_wgs_per_cu() { return (sizeof(T) == 4 && D >= 512) ? 1 : 2; }
+
 template <typename T, typename TI, int D, bool LAYER, int TG>
-__global__ __launch_bounds__(QKV_NW * 64, 2) void qkv_kernel(const QkvArgs a) {
+__global__ __launch_bounds__(QKV_NW * 64, (qkv_wgs_per_cu<T, D>())) void qkv_kernel(const QkvArgs a) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int NW = QKV_NW;
@@ -332,9 +337,7 @@ hipError_t launch_d(const QkvArgs &a, int grid, hipStream_t s) {
     case 64: return launch_dl<T, TI, 64>(a, grid, s);
     case 128: return launch_dl<T, TI, 128>(a, grid, s);
     case 256: return launch_dl<T, TI, 256>(a, grid, s);
-    case 512:
-      if constexpr (sizeof(T) == 2) return launch_dl<T, TI, 512>(a, grid, s);
-      return hipErrorInvalidValue;
+    case 512: return launch_dl<T, TI, 512>(a, grid, s);
     default:
       return hipErrorInvalidValue;
   }
