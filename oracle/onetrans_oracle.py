@@ -38,7 +38,9 @@ Readings of points the pages leave open (each listed in the design notes):
   * Stage II attends, per NS query j, over [cached S keys of that block; own NS keys <= j]
     in ONE softmax (the pages' "cross-attention then self-attention" is the two key
     segments of the same causal row);
-  * cross-request append is defined for an unpyramided stack only.
+  * cross-request append on a pyramided stack is recomputation of the longer sequence: the
+    leading blocks that keep every row grow with the sequence, and from the first block that
+    prunes on, each block keeps the same number of tail rows as before (see grown_schedule).
 """
 
 from __future__ import annotations
@@ -293,3 +295,33 @@ def append_events(cache: List[Dict[str, np.ndarray]], x_new: np.ndarray, weights
         yh = norm(y, p.norm2_g, p.norm2_b, m.norm, m.norm_eps)
         x = y + mixed_linear(gelu(mixed_linear(yh, p.w1, rows, s, p.b1)), p.w2, rows, s, p.b2)
     return new_cache, x
+
+
+def grown_schedule(l_s: int, s_queries: Sequence[int], d_l: int) -> Tuple[int, ...]:
+    """Pyramid of a user sequence of l_s rows after d_l more rows are appended ([en] 7.5.2 keeps a
+    fixed number of tail rows per block; [en] 7.5.3 appends events at the end).
+
+    Reading: a leading block that keeps every row of its input (q_n = s_n) keeps every row of the
+    longer sequence too; from the first block that prunes (q_n < s_n) on, every block keeps the
+    same count of tail rows as before.
+    """
+    out, s, pruned = [], l_s, False
+    for q in s_queries:
+        pruned = pruned or q < s
+        out.append(q if pruned else q + d_l)
+        s = q
+    return tuple(out)
+
+
+def append_recompute(x_s_old: np.ndarray, x_new: np.ndarray, weights, m, s_queries: Sequence[int]
+                     ) -> Tuple[List[Dict[str, np.ndarray]], np.ndarray]:
+    """Cross-request append on any cache, pyramided or not: the cache and final rows that Stage I of
+    the concatenated sequence produces ([en] 7.5.3: appending equals recomputing), under the grown
+    pyramid. x_s_old: the user's l_s earlier rows (prefilled with s_queries). Returns (cache, final
+    rows of the new events that the last block keeps: the last min(d_l, q_last) rows)."""
+    x_old = np.asarray(x_s_old, F64)
+    x_new = np.asarray(x_new, F64)
+    d_l = x_new.shape[0]
+    sched = grown_schedule(x_old.shape[0], s_queries, d_l)
+    cache, final = prefill_user(np.concatenate([x_old, x_new]), weights, m, sched)
+    return cache, final[final.shape[0] - min(d_l, sched[-1]):]

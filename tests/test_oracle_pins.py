@@ -198,6 +198,93 @@ def test_append_refuses_pyramided_cache():
         O.append_events(cache, np.zeros((2, w.model.d_model), np.float32), ws, w.model)
 
 
+# --- cross-request append on a pyramided cache ------------------------------------------------
+
+def test_grown_schedule_hand_examples():
+    # leading blocks that keep every row grow with the sequence; from the first pruning block on the
+    # kept counts stay (the OneTransS schedule after appending 32 rows to 1158)
+    assert O.grown_schedule(1158, (1158, 955, 719, 484, 248, 12), 32) == (1190, 955, 719, 484, 248, 12)
+    assert O.grown_schedule(24, (24, 24, 24), 8) == (32, 32, 32)          # no pyramid: everything grows
+    assert O.grown_schedule(24, (24, 24, 8), 8) == (32, 32, 8)            # only the last block prunes
+    assert O.grown_schedule(24, (20, 20, 8), 8) == (20, 20, 8)            # block 1 prunes: nothing grows
+    assert O.grown_schedule(100, (100, 60, 60, 30), 10) == (110, 60, 60, 30)
+
+
+def test_append_recompute_equals_incremental_append_without_pyramid():
+    """On an unpyramided cache the recomputation of the longer sequence equals the incremental
+    append (new rows only, against the cached keys), cache rows and new final rows both."""
+    w = synth.test_workload("tiny3_append")
+    m, ws = w.model, synth.make_weights(w.model)
+    old, new = synth.append_rows(w, 1)
+    flat = (w.l_old,) * m.n_blocks
+    rc_cache, rc_out = O.append_recompute(old, new, ws, m, flat)
+    inc_cache, inc_out = O.append_events(O.prefill_user(old, ws, m, flat)[0], new, ws, m)
+    for a, b in zip(rc_cache, inc_cache):
+        assert _rel(a["k"], b["k"]) < 1e-12 and _rel(a["v"], b["v"]) < 1e-12
+    assert _rel(rc_out, inc_out) < 1e-12
+
+
+def _pyramid_route(old, new, ws, m, sched):
+    """Append by the exact route, built from oracle pieces: blocks up to the first pruning block n*
+    keep their cached rows and compute only the new rows; block n*'s kept outputs of the old
+    sequence (its window) are extended by the new rows' outputs and cut to the block's kept count;
+    the blocks after n* run as Stage I over that window."""
+    L = old.shape[0]
+    s, n_star = L, None
+    for n, q in enumerate(sched):
+        if q < s:
+            n_star = n
+            break
+        s = q
+    old_cache, _ = O.prefill_user(old, ws, m, sched)
+    head = n_star + 1 if n_star is not None else m.n_blocks
+    # blocks 0..n*: the cached rows of each are the whole sequence so far (no pruning before n*)
+    head_cache, head_out = O.append_events(old_cache[:head], new, ws[:head], m)
+    if n_star is None or n_star == m.n_blocks - 1:
+        d_l = new.shape[0]
+        q_last = sched[-1] if n_star is not None else L + d_l
+        return head_cache, head_out[d_l - min(d_l, q_last):]
+    # block n*'s kept outputs of the old sequence: Stage I of the first n* + 1 blocks
+    _, window_old = O.prefill_user(old, ws[:head], m, sched[:head])
+    q_star = sched[n_star]
+    window = np.concatenate([window_old, head_out])[-q_star:]
+    tail_cache, final = O.prefill_user(window, ws[head:], m, sched[head:])
+    d_l = new.shape[0]
+    return head_cache + tail_cache, final[final.shape[0] - min(d_l, sched[-1]):]
+
+
+@pytest.mark.parametrize("sched_old,d_l", [((24, 20, 8), 8), ((24, 24, 8), 8), ((24, 20, 4), 8), ((24, 20, 8), 3),
+                                           ((24, 24, 24), 8)])
+def test_pyramided_append_route_equals_recompute(sched_old, d_l):
+    """The route the device follows reaches exactly the recomputation of the longer sequence: the
+    blocks up to the first pruning block keep every old row's keys/values (causal mask, window
+    start 0), and the block after it sees old rows whose values did not change, so only the blocks
+    from there on need their (slid) windows recomputed. Covers a first pruning block in the middle,
+    only the last block pruning, more new rows than final rows, and no pyramid."""
+    w = synth.test_workload("tiny3_append")
+    m, ws = w.model, synth.make_weights(w.model)
+    old = synth.user_sequence(w, 0)[:24]
+    new = synth.append_rows(w, 1)[1][:d_l] + 0.5
+    rc_cache, rc_out = O.append_recompute(old, new, ws, m, sched_old)
+    rt_cache, rt_out = _pyramid_route(old, new, ws, m, sched_old)
+    grown = O.grown_schedule(24, sched_old, d_l)
+    s = 24 + d_l
+    for n, (a, b) in enumerate(zip(rt_cache, rc_cache)):
+        assert a["k"].shape[0] == b["k"].shape[0] == s, (n, a["k"].shape, s)
+        assert _rel(a["k"], b["k"]) < 1e-12 and _rel(a["v"], b["v"]) < 1e-12, n
+        s = grown[n]
+    assert rt_out.shape == rc_out.shape == (min(d_l, grown[-1]), m.d_model)
+    assert _rel(rt_out, rc_out) < 1e-12
+    # the old rows of the blocks up to the first pruning block are untouched by the append
+    old_cache, _ = O.prefill_user(old, ws, m, sched_old)
+    assert _rel(rc_cache[0]["k"][:24], old_cache[0]["k"]) < 1e-12
+    if sched_old[0] == 24 and sched_old[1] < 24:
+        assert _rel(rc_cache[1]["k"][:24], old_cache[1]["k"]) < 1e-12
+        # ...while the block after the first pruning block sees a slid window: its rows change
+        assert rc_cache[2]["k"].shape == old_cache[2]["k"].shape
+        assert _rel(rc_cache[2]["k"], old_cache[2]["k"]) > 1e-6
+
+
 # --- P6 / P7: closed forms of the mask ---------------------------------------------------------
 
 def test_equal_scores_give_mean_of_visible_values():
