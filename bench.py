@@ -43,8 +43,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="onetrans_s",
-                   choices=["onetrans_s", "two_stage", "append", "append_ragged", "onetrans_l", "tokenize_s",
-                            "tokenize_s_time"])
+                   choices=["onetrans_s", "two_stage", "append", "append_ragged", "append_pyramid", "onetrans_l",
+                            "tokenize_s", "tokenize_s_time"])
     p.add_argument("--dtype", default=None, choices=[None, "bf16", "f32"])
     p.add_argument("--no-trace", action="store_true", help="no per-kernel events in the timed region")
     p.add_argument("--streams", type=int, default=2, choices=[1, 2, 4],
@@ -264,7 +264,10 @@ def main():
     peak = PEAK_BF16_TFLOPS if m.dtype == "bf16" else PEAK_FP32_TFLOPS
     t_setup = time.time()
     host_w = synth.make_weights(m)
-    sched = w.s_queries if w.kind != "append" else (w.l_old,) * m.n_blocks
+    # append workloads: the schedule the cached rows were prefilled with (the plain append caches
+    # are unpyramided; append_pyramid keeps the OneTransS pyramid over its 1158 cached rows)
+    pyramid_append = w.kind == "append" and w.s_queries[0] == w.l_old and len(set(w.s_queries)) > 1
+    sched = w.s_queries if w.kind != "append" or pyramid_append else (w.l_old,) * m.n_blocks
     model = ob.Model.from_host(m, sched, host_w, device=dev)
     ob.set_streams(a.streams)
 
@@ -303,21 +306,29 @@ def main():
         xn = up(np.stack([synth.candidate_tokens(w, u, 0) for u in range(w.n_users)])[:, None])
         # ragged users: user u's cached rows are the first lens[u] rows (the rest of `old` pads)
         lens = synth.user_cached_lengths(w) if w.l_old_min else None
-        pristine = ob.KVCache(model, w.n_users, w.l_s, user_len=lens)
+        pristine = ob.KVCache(model, w.n_users, w.l_s, user_len=lens, x_tail=pyramid_append)
         ob.onetrans_prefill_user(model, xo, pristine)
-        cache = ob.KVCache(model, w.n_users, w.l_s, user_len=lens)
-        out_new = torch.empty((w.n_users, w.d_l, m.d_model), dtype=torch.float32, device=dev)
-        out = torch.empty((w.n_users, 1, m.l_ns, m.d_model), dtype=torch.float32, device=dev)
-        ws1 = model.workspace(ob.L.OP_APPEND, w.n_users, d_l=w.d_l)
-        ws2 = model.workspace(ob.L.OP_SCORE, w.n_users, n_cand=1)
+        cache = ob.KVCache(model, w.n_users, w.l_s, user_len=lens, x_tail=pyramid_append)
         n_units = w.n_users
         classes = {}
-        for l_old in (lens or [w.l_old]):   # per-user work, averaged over the users
-            ap = cm.append_classes(m.d_model, m.d_ff, m.n_blocks, l_old, w.d_l, store_bytes)
-            sc = cm.score_classes(m.d_model, m.d_ff, m.l_ns, l_old + w.d_l, (l_old + w.d_l,) * m.n_blocks,
-                                  store_bytes)
-            for k in sc:
-                classes[k] = classes.get(k, 0.0) + (ap[k] + sc[k]) / len(lens or [w.l_old])
+        if pyramid_append:
+            grown = cm.grown_schedule(w.l_old, sched, w.d_l)
+            q_final = min(w.d_l, grown[-1])
+            ap = cm.pyramid_append_classes(m.d_model, m.d_ff, w.l_old, w.d_l, sched, store_bytes, out_rows=q_final)
+            sc = cm.score_classes(m.d_model, m.d_ff, m.l_ns, w.l_old + w.d_l, grown, store_bytes)
+            classes = {k: ap[k] + sc[k] for k in sc}
+        else:
+            q_final = w.d_l
+            for l_old in (lens or [w.l_old]):   # per-user work, averaged over the users
+                ap = cm.append_classes(m.d_model, m.d_ff, m.n_blocks, l_old, w.d_l, store_bytes)
+                sc = cm.score_classes(m.d_model, m.d_ff, m.l_ns, l_old + w.d_l, (l_old + w.d_l,) * m.n_blocks,
+                                      store_bytes)
+                for k in sc:
+                    classes[k] = classes.get(k, 0.0) + (ap[k] + sc[k]) / len(lens or [w.l_old])
+        out_new = torch.empty((w.n_users, q_final, m.d_model), dtype=torch.float32, device=dev)
+        out = torch.empty((w.n_users, 1, m.l_ns, m.d_model), dtype=torch.float32, device=dev)
+        ws1 = model.workspace(ob.L.OP_APPEND, w.n_users, l_s=pristine.append_window(), d_l=w.d_l)
+        ws2 = model.workspace(ob.L.OP_SCORE, w.n_users, n_cand=1)
         restore_ms = []
 
         def step():
@@ -407,6 +418,17 @@ def main():
                 done += 1
             sample = f"Stage I of user 0 plus Stage II of {done} of its candidates, both timed"
             units = done
+        elif pyramid_append:
+            # the oracle's definition: Stage I of the longer sequence under the grown pyramid
+            t_app = 0.0
+            while done < min(64, w.n_users) and (time.perf_counter() - t0 < a.cpu_seconds or done < 2):
+                o, nw = synth.append_rows(w, done)
+                t1 = time.perf_counter()
+                O.append_recompute(o, nw, host_w, m, sched)
+                t_app += time.perf_counter() - t1
+                done += 1
+            sample = f"{done} users' appends, each recomputed as the oracle defines it"
+            units = done
         else:
             t_app = 0.0
             ul = synth.user_cached_lengths(w)
@@ -453,7 +475,7 @@ def main():
         "setup_s": round(t_setup, 1),
         **extra,
     }
-    if w.kind == "append":
+    if w.kind == "append" and not pyramid_append:
         byts = sum(cm.append_cache_bytes(m.d_model, m.n_blocks, l_old, w.d_l, store_bytes)
                    for l_old in (synth.user_cached_lengths(w)))
         line["cache_GB/s"] = round(byts / (ms_step * 1e-3) / 1e9, 1)

@@ -46,7 +46,7 @@ typedef enum {
   ONETRANS_OK = 0,
   ONETRANS_ERR_INVALID_ARG = -1,    /* null pointer, bad enum, non-positive size */
   ONETRANS_ERR_SHAPE = -2,          /* inconsistent sizes or pyramid schedule */
-  ONETRANS_ERR_UNSUPPORTED = -3,    /* valid but not implemented (d_head, dims, pyramided append) */
+  ONETRANS_ERR_UNSUPPORTED = -3,    /* valid but not implemented (d_head, dims, ragged + pyramid) */
   ONETRANS_ERR_WORKSPACE = -4,      /* ws_bytes smaller than onetrans_workspace_bytes() */
   ONETRANS_ERR_CACHE_CAPACITY = -5, /* cache too small for the rows to be written */
   ONETRANS_ERR_ALIGNMENT = -6,      /* a device pointer is not 16-byte aligned */
@@ -96,13 +96,24 @@ typedef struct {
                              them: prefill_user sets it to l_s (the padded length), append_events
                              raises it to the largest user_len if that is larger. NULL: every user
                              has layer_len[n] rows. */
+  int q_last;             /* host: S rows the last block keeps (its output rows). prefill_user sets
+                             it to s_queries[n_blocks - 1]; append_events advances it with the
+                             sequence when the last block keeps every row (q_last equal to
+                             layer_len[n_blocks - 1]). 0 is read as layer_len[n_blocks - 1]. */
+  void *x_tail;           /* device or NULL: [n_users][capacity][d_model] fp32. For a pyramid that
+                             prunes before its last block: the input rows of the block after the
+                             first pruning block, each at its position in the user's sequence.
+                             prefill_user writes them (when set), append_events reads and extends
+                             them; an append to such a cache needs it. */
 } onetrans_kv_cache;
 
 /* Workspace bytes needed by one call of `op`.
  *   FORWARD: n_seq = batch, l_s = S rows per sample (n_cand, d_l ignored)
  *   PREFILL: n_seq = users, l_s = S rows per user
  *   SCORE:   n_seq = users, n_cand = candidates per user (l_s ignored)
- *   APPEND:  n_seq = users, d_l = appended rows per user
+ *   APPEND:  n_seq = users, d_l = appended rows per user; l_s = 0 for a cache whose pyramid
+ *            prunes no block before the last, else the rows of the block after the first pruning
+ *            block (layer_len[n* + 1]): that block onwards is recomputed over its window
  * Returns 0 for an invalid configuration. */
 size_t onetrans_workspace_bytes(const onetrans_config *cfg, int op, int n_seq, int l_s, int n_cand,
                                 int d_l);
@@ -127,7 +138,10 @@ int onetrans_forward(const onetrans_config *cfg, const onetrans_block_weights *b
 
 /* Stage I (section 7.5.3): run the S rows of `n_users` users through every block (pyramid
  * included, no NS rows: S rows never attend to NS rows) and write each block's K/V rows into the
- * cache: block n gets s_n rows at positions 0..s_n-1. Sets cache->layer_len[n] = s_n.
+ * cache: block n gets s_n rows at positions 0..s_n-1. Sets cache->layer_len[n] = s_n and
+ * cache->q_last = s_queries[n_blocks - 1]. With cache->x_tail set and a schedule that prunes
+ * before its last block, the outputs of the first pruning block (the next block's input rows) are
+ * also written there, at their positions in the sequence, for a later append_events.
  *   x_s   [n_users][l_s][d] storage dtype.
  *   out_s [n_users][q_last][d] fp32 final S rows, or NULL.
  * Ragged users (cache->user_len set by the caller, 0 <= user_len[u] <= l_s): user u's sequence is
@@ -181,19 +195,30 @@ int onetrans_score_candidates_noalloc(const onetrans_config *cfg, const onetrans
                                       int n_cand, void *out_ns, hipStream_t stream);
 
 /* Cross-request append (section 7.5.3): `d_l` new S rows per user at positions L_old..L_old+d_l-1
- * behind the L_old cached rows. Only the new rows are computed (shared S parameters, keys = cached
- * rows plus new rows up to themselves); their K/V are written at offset L_old of every block and
- * layer_len[n] becomes L_old + d_l. Needs an unpyramided cache (every layer_len equal), otherwise
- * UNSUPPORTED: with a tail-count pyramid the key window of later blocks would slide with every
- * append, so appending could not equal recomputation. cfg->s_queries is not read by this call.
- * Ragged users (cache->user_len set): L_old is user_len[u] for user u, and user_len[u] advances by
- * d_l (the lengths are read and advanced on the host at enqueue time).
+ * behind the L_old cached rows. The result equals Stage I of the user's longer sequence under the
+ * grown pyramid: a leading block that keeps every row keeps every row of the longer sequence too,
+ * and from the first block that prunes on, each block keeps the same count of tail rows as before.
+ *   Unpyramided cache (every layer_len equal, the last block keeps every row): only the new rows
+ *   are computed (shared S parameters, keys = cached rows plus new rows up to themselves); their
+ *   K/V go to offset L_old of every block and layer_len[n] becomes L_old + d_l.
+ *   Pyramided cache: the blocks up to and including the first pruning block n* compute the new
+ *   rows only, as above (the old rows' keys, values and outputs do not change: those blocks'
+ *   windows start at the sequence's first row). The block after n* sees a window that slid by d_l
+ *   rows, so blocks n* + 1 onwards are recomputed over their windows, reading their input rows
+ *   from cache->x_tail (which prefill_user wrote and this call extends); their layer_len stay.
+ *   When only the last block prunes, no block is recomputed.
+ * cfg->s_queries is not read by this call: the pyramid comes from layer_len and q_last.
+ * Ragged users (cache->user_len set; unpyramided caches only): L_old is user_len[u] for user u,
+ * and user_len[u] advances by d_l (the lengths are read and advanced on the host at enqueue time).
  * 16 or more users run as two halves on two streams, forked from and joined back into `stream`
  * (see onetrans_forward for the stream's lifetime and thread-safety).
  *   x_new   [n_users][d_l][d] storage dtype.
- *   out_new [n_users][d_l][d] fp32 final rows of the new events, or NULL.
- * Errors: as forward, plus CACHE_CAPACITY (L_old + d_l > capacity for some user), UNSUPPORTED
- * (pyramided cache), SHAPE (a user_len outside [0, capacity]). */
+ *   out_new [n_users][min(d_l, q_last')][d] fp32, or NULL: the final rows of the new events that
+ *           the last block keeps (q_last' = q_last after the call; d_l rows without pyramid).
+ * Errors: as forward, plus CACHE_CAPACITY (L_old + d_l > capacity for some user), WORKSPACE (ws
+ * sized without the recomputed window, see onetrans_workspace_bytes), INVALID_ARG (a cache that
+ * prunes before its last block without x_tail), UNSUPPORTED (ragged users on a pyramided cache),
+ * SHAPE (a user_len outside [0, capacity], or layer_len / q_last that no pyramid produces). */
 int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weights *blk,
                            onetrans_kv_cache *cache, const void *x_new, int n_users, int d_l,
                            void *out_new, void *ws, size_t ws_bytes, hipStream_t stream);

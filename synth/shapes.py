@@ -127,6 +127,14 @@ WORKLOADS = {
                     "128 users with 579..1158 cached rows (uniform), append 32 new rows, 1 candidate/user; bf16",
         model=_ONETRANS_S, kind="append", l_s=1190, s_queries=(1190,) * 6, n_users=128, n_cand=1,
         l_old=1158, d_l=32, l_old_min=579, input_seed=2005, parity_subset=(0, 1, 64, 127)),
+    "append_pyramid": Workload(
+        key="append_pyramid",
+        description="Cross-request append on the OneTransS-shaped model with its pyramid: 128 users whose 1158 "
+                    "cached rows were prefilled with the schedule 1158->955->719->484->248->12, append 32 new rows "
+                    "(the schedule grows to 1190->955->...->12: blocks 3-6 are recomputed over their slid windows), "
+                    "1 candidate/user; bf16",
+        model=_ONETRANS_S, kind="append", l_s=1190, s_queries=(1158, 955, 719, 484, 248, 12), n_users=128, n_cand=1,
+        l_old=1158, d_l=32, input_seed=2006, parity_subset=(0, 127)),
     "onetrans_l": Workload(
         key="onetrans_l",
         description="OneTransL-shaped forward: 8 blocks, d=512, 16 heads, FFN 2048; L_S=2048, L_NS=16; "

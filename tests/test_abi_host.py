@@ -149,9 +149,28 @@ def test_serving_validation_errors():
                                          1 << 40, None) == L.ERR_SHAPE
     assert lib.onetrans_score_candidates(ctypes.byref(c), b, ctypes.byref(kc), FAKE, 2, 4, FAKE, FAKE, 64,
                                          None) == L.ERR_WORKSPACE
-    # append: pyramided cache, capacity
+    # append: a cache that prunes before its last block needs x_tail; a pyramid that grows is no state
+    # prefill produces; the workspace must cover the recomputed window (100 rows here, not d_l = 8)
     assert lib.onetrans_append_events(ctypes.byref(c), b, ctypes.byref(kc), FAKE, 2, 8, None, FAKE, 1 << 40,
-                                      None) == L.ERR_UNSUPPORTED
+                                      None) == L.ERR_INVALID_ARG
+    kt = _cache()
+    kt.x_tail = FAKE
+    small = lib.onetrans_workspace_bytes(ctypes.byref(c), L.OP_APPEND, 2, 0, 0, 8)
+    need = lib.onetrans_workspace_bytes(ctypes.byref(c), L.OP_APPEND, 2, 100, 0, 8)
+    assert 0 < small < need
+    assert lib.onetrans_append_events(ctypes.byref(c), b, ctypes.byref(kt), FAKE, 2, 8, None, FAKE, small,
+                                      None) == L.ERR_WORKSPACE
+    kt.x_tail = FAKE + 8
+    assert lib.onetrans_append_events(ctypes.byref(c), b, ctypes.byref(kt), FAKE, 2, 8, None, FAKE, need,
+                                      None) == L.ERR_ALIGNMENT
+    grows = _cache(lens=(100, 120))
+    assert lib.onetrans_append_events(ctypes.byref(c), b, ctypes.byref(grows), FAKE, 2, 8, None, FAKE, 1 << 40,
+                                      None) == L.ERR_SHAPE
+    grows = _cache(lens=(100, 100))
+    grows.q_last = 150
+    assert lib.onetrans_append_events(ctypes.byref(c), b, ctypes.byref(grows), FAKE, 2, 8, None, FAKE, 1 << 40,
+                                      None) == L.ERR_SHAPE
+    assert list(kt._keep) == [120, 100]              # nothing advanced on error
     full = _cache(cap=128, lens=(124, 124))
     assert lib.onetrans_append_events(ctypes.byref(c), b, ctypes.byref(full), FAKE, 2, 8, None, FAKE, 1 << 40,
                                       None) == L.ERR_CACHE_CAPACITY
@@ -190,6 +209,11 @@ def test_ragged_user_validation_errors():
     # score: lengths within the cache
     assert lib.onetrans_score_candidates(ctypes.byref(flat), b, ctypes.byref(_ragged_cache((10, 201))), FAKE, 2, 4,
                                          FAKE, FAKE, 1 << 40, None) == L.ERR_SHAPE
+    # ragged users need an unpyramided cache (also when only the last block prunes)
+    kr = _ragged_cache((100, 110))
+    kr.q_last = 60
+    assert lib.onetrans_append_events(ctypes.byref(flat), b, ctypes.byref(kr), FAKE, 2, 8, None, FAKE, 1 << 40,
+                                      None) == L.ERR_UNSUPPORTED
 
 
 def _tok_cfg(lens=(15, 15), dims=(64, 128), hid=(128, 64), ns_dim=192, ns_hidden=128, merge=L.MERGE_INTENT):

@@ -465,3 +465,87 @@ def test_prefill_two_streams_equal_one_stream():
         for n, rows in enumerate(l1):   # rows past a block's length are never written
             assert torch.equal(k1[:, n, :, :rows], k2[:, n, :, :rows])
             assert torch.equal(v1[:, n, :, :rows], v2[:, n, :, :rows])
+
+
+# --- cross-request append on a pyramided cache ------------------------------------------------
+
+def _pyramid_append_case(w, sched_old, steps, users=None, check=None):
+    """Prefill the old rows with `sched_old`, append the new rows in `steps` chunks, then score one
+    candidate per user; every cache row, the final new-event rows of the last append and the scores
+    are compared with the oracle's recomputation of the longer sequence."""
+    m, ws = w.model, weights(w.model)
+    dtype = m.dtype
+    old, new = synth.append_batch(w, users)
+    n_users = old.shape[0]
+    l_old = old.shape[1]
+    say(f"[pyramid append] {w.key} dtype={dtype} U={n_users} L_old={l_old} sched={sched_old} steps={steps}")
+    mdl = model(w, s_queries=sched_old)
+    cap = l_old + sum(steps)
+    cache = ob.KVCache(mdl, n_users, cap, x_tail=True)
+    ob.onetrans_prefill_user(mdl, dev(old, mdl), cache)
+    done, sched = 0, tuple(sched_old)
+    for dl in steps:
+        grown = O.grown_schedule(l_old + done, sched, dl)
+        out_new = torch.empty((n_users, min(dl, grown[-1]), m.d_model), dtype=torch.float32, device=mdl.device)
+        ob.onetrans_append_events(mdl, cache, dev(np.ascontiguousarray(new[:, done:done + dl]), mdl), out_new)
+        done += dl
+        sched = grown
+    xn = np.stack([synth.candidate_tokens(w, u, 0) for u in range(n_users)])[:, None]
+    sc = ob.onetrans_score_candidates(mdl, cache, dev(xn, mdl))
+    torch.cuda.synchronize()
+    expect_len = [l_old + done] + list(sched[:-1])
+    assert cache.lengths == expect_len and cache.q_last == sched[-1], (cache.lengths, cache.q_last, sched)
+    last = steps[-1]
+    for u in (range(n_users) if check is None else check):
+        rc, _ = O.prefill_user(np.concatenate([old[u], new[u, :done]]), ws, m, sched)
+        _, ref_out = O.append_recompute(np.concatenate([old[u], new[u, :done - last]]), new[u, done - last:done], ws,
+                                        m, O.grown_schedule(l_old, sched_old, done - last) if done > last else sched_old)
+        e_out = rel_err(out_new[u].cpu().numpy(), ref_out)
+        e_kv = 0.0
+        for n, (k, v) in enumerate(cache_to_host(cache, u, m.n_blocks, cache.lengths)):
+            e_kv = max(e_kv, rel_err(k, rc[n]["k"]), rel_err(v, rc[n]["v"]))
+        e_sc = rel_err(sc[u, 0].cpu().numpy(), O.score_candidate(rc, xn[u, 0], ws, m))
+        say(f"  user {u}: new rows {e_out:.3e} cache {e_kv:.3e} score {e_sc:.3e}")
+        assert max(e_out, e_kv, e_sc) <= TOL[dtype], (u, e_out, e_kv, e_sc)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("sched_old,steps", [((24, 20, 8), (8,)),       # first pruning block 2 of 3
+                                             ((24, 24, 8), (8,)),       # only the last block prunes
+                                             ((24, 20, 4), (8,)),       # more new rows than final rows
+                                             ((24, 6, 2), (8,)),        # window smaller than the append
+                                             ((24, 20, 8), (4, 3, 1))]) # three appends in a row
+def test_pyramid_append_small(dtype, sched_old, steps):
+    _pyramid_append_case(replace(synth.test_workload("tiny3_append", dtype), n_users=3, input_seed=2140),
+                         sched_old, steps)
+
+
+def test_pyramid_append_onetrans_s_shape():
+    """The OneTransS pyramid on 16 users: 1158 cached rows, 32 appended; blocks 3-6 recomputed."""
+    w = synth.workload("append_pyramid")
+    _pyramid_append_case(w, w.s_queries, (w.d_l,), users=range(16), check=(0, 15))
+
+
+def test_pyramid_append_two_streams_equal_one_stream():
+    w = replace(synth.test_workload("tiny3_append", "bf16"), n_users=33, input_seed=2141)
+    m = w.model
+    mdl = model(w, s_queries=(24, 20, 8))
+    old, new = synth.append_batch(w)
+    res = []
+    try:
+        for n_streams in (1, 2, 4):
+            ob.set_streams(n_streams)
+            cache = ob.KVCache(mdl, w.n_users, 32, x_tail=True)
+            ob.onetrans_prefill_user(mdl, dev(old, mdl), cache)
+            out_new = torch.empty((w.n_users, 8, m.d_model), dtype=torch.float32, device=mdl.device)
+            ob.onetrans_append_events(mdl, cache, dev(new, mdl), out_new)
+            torch.cuda.synchronize()
+            res.append((out_new.clone(), cache.k.clone(), cache.v.clone(), cache.lengths))
+    finally:
+        ob.set_streams(2)
+    (o1, k1, v1, l1) = res[0]
+    for (o2, k2, v2, l2) in res[1:]:
+        assert torch.equal(o1, o2) and l1 == l2
+        for n, rows in enumerate(l1):
+            assert torch.equal(k1[:, n, :, :rows], k2[:, n, :, :rows])
+            assert torch.equal(v1[:, n, :, :rows], v2[:, n, :, :rows])

@@ -39,7 +39,8 @@ class BlockWeights(ctypes.Structure):
 
 class KVCache(ctypes.Structure):
     _fields_ = [("k", c_void_p), ("v", c_void_p), ("n_users", c_int), ("capacity", c_int),
-                ("layer_len", POINTER(c_int)), ("user_len", POINTER(c_int))]
+                ("layer_len", POINTER(c_int)), ("user_len", POINTER(c_int)), ("q_last", c_int),
+                ("x_tail", c_void_p)]
 
 
 class TokenizerConfig(ctypes.Structure):

@@ -90,9 +90,10 @@ class KVCache:
 
     `user_len` (one int per user) makes the users ragged: user u's valid rows are its first
     user_len[u] rows of every block, and prefill / append / score read (and append advances) these
-    per-user lengths."""
+    per-user lengths. `x_tail=True` allocates the fp32 rows [user][capacity][d] that an append to a
+    cache whose pyramid prunes before its last block recomputes from (prefill writes them)."""
 
-    def __init__(self, model: Model, n_users: int, capacity: int, user_len=None):
+    def __init__(self, model: Model, n_users: int, capacity: int, user_len=None, x_tail: bool = False):
         nbytes = int(L.lib().onetrans_kv_cache_bytes(ctypes.byref(model.cfg), n_users, capacity))
         if nbytes == 0:
             raise ValueError("invalid cache shape")
@@ -106,8 +107,10 @@ class KVCache:
             if len(user_len) != n_users:
                 raise ValueError("user_len needs one length per user")
             self.user_len = (ctypes.c_int * n_users)(*[int(x) for x in user_len])
+        self.x_tail = (torch.empty((n_users, capacity, model.d_model), dtype=torch.float32, device=model.device)
+                       if x_tail else None)
         self.c = L.KVCache(self.k.data_ptr(), self.v.data_ptr(), n_users, capacity, self.layer_len,
-                           self.user_len)
+                           self.user_len, 0, _ptr(self.x_tail))
 
     @property
     def lengths(self):
@@ -117,11 +120,27 @@ class KVCache:
     def user_lengths(self):
         return None if self.user_len is None else list(self.user_len)
 
+    @property
+    def q_last(self) -> int:
+        """S rows the last block keeps (its final rows), as the library maintains it."""
+        return int(self.c.q_last) or self.layer_len[len(self.layer_len) - 1]
+
+    def append_window(self) -> int:
+        """Rows of the block after the first pruning block (recomputed by an append), or 0."""
+        lens = self.lengths + [self.q_last]
+        for n in range(len(lens) - 2):
+            if lens[n + 1] < lens[n]:
+                return lens[n + 1]
+        return 0
+
     def copy_(self, other: "KVCache") -> "KVCache":
         self.k.copy_(other.k)
         self.v.copy_(other.v)
+        if self.x_tail is not None and other.x_tail is not None:
+            self.x_tail.copy_(other.x_tail)
         for i, n in enumerate(other.layer_len):
             self.layer_len[i] = n
+        self.c.q_last = other.c.q_last
         if self.user_len is not None and other.user_len is not None:
             for i, n in enumerate(other.user_len):
                 self.user_len[i] = n
@@ -196,11 +215,12 @@ def onetrans_score_candidates_noalloc(model: Model, cache: KVCache, x_ns: torch.
 def onetrans_append_events(model: Model, cache: KVCache, x_new: torch.Tensor,
                            out_new: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
                            stream=None) -> Optional[torch.Tensor]:
-    """Cross-request append: x_new [U][dL][d] -> cache extended by dL rows per block (+ out_new fp32)."""
+    """Cross-request append: x_new [U][dL][d] -> cache extended by dL rows per block (+ out_new fp32,
+    [U][min(dL, q_last after the append)][d]: the final rows of the new events)."""
     _check_input(model, x_new, 3, "x_new")
     U, dl, _ = x_new.shape
     if ws is None:
-        ws = model.workspace(L.OP_APPEND, U, d_l=dl)
+        ws = model.workspace(L.OP_APPEND, U, l_s=cache.append_window(), d_l=dl)
     st = L.lib().onetrans_append_events(ctypes.byref(model.cfg), model.blocks, ctypes.byref(cache.c),
                                         x_new.data_ptr(), U, dl, _ptr(out_new), ws.data_ptr(), ws.numel(),
                                         _stream(x_new.device, stream))

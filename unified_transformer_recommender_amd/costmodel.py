@@ -164,6 +164,43 @@ def append_classes(d, d_ff, n_blocks, l_old, d_l, store_bytes):
     return tot
 
 
+def grown_schedule(l_s: int, s_queries: Sequence[int], d_l: int) -> Tuple[int, ...]:
+    """Pyramid of a cached sequence of l_s rows after d_l rows are appended: leading blocks that
+    keep every row keep every row of the longer sequence; from the first pruning block on the kept
+    counts stay (the library derives the same from a cache's lengths)."""
+    out, s, pruned = [], l_s, False
+    for q in s_queries:
+        pruned = pruned or q < s
+        out.append(q if pruned else q + d_l)
+        s = q
+    return tuple(out)
+
+
+def pyramid_append_classes(d, d_ff, l_old, d_l, s_queries, store_bytes, out_rows=None):
+    """Per-user append to a cache prefilled with s_queries over l_old rows: the new rows through
+    the blocks up to the first pruning block n*, then Stage I of blocks n* + 1 .. over their windows
+    (which slid by d_l rows). out_rows: queries of the last recomputed block (its kept rows, or
+    fewer when only the final rows of the new events are wanted). Without pruning before the last
+    block this is the plain append."""
+    s, n_star = l_old, None
+    for n, q in enumerate(s_queries):
+        if q < s:
+            n_star = n
+            break
+        s = q
+    n_blocks = len(s_queries)
+    head = n_blocks if n_star is None or n_star == n_blocks - 1 else n_star + 1
+    tot = append_classes(d, d_ff, head, l_old, d_l, store_bytes)
+    if head < n_blocks:
+        win = s_queries[n_star]
+        tail = list(s_queries[head:])
+        if out_rows is not None:
+            tail[-1] = min(tail[-1], out_rows)
+        for k, v in prefill_classes(d, d_ff, win, tail, 4).items():
+            tot[k] = tot.get(k, 0.0) + v
+    return tot
+
+
 def append_cache_bytes(d, n_blocks, l_old, d_l, store_bytes):
     """K/V cache bytes one user's append must read (every cached row of every block, K and V)
     plus the new rows it writes: the HBM floor of the append path."""

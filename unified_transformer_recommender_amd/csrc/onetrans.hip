@@ -188,8 +188,9 @@ bool ws_dims(const onetrans_config *c, const Dims &D, int op, int n_seq, int l_s
       n = (size_t)n_seq * n_cand; tin = rq = D.lns; kv = true;
       return true;
     case ONETRANS_OP_APPEND:
-      if (n_seq < 1 || d_l < 1) return false;
-      n = n_seq; tin = rq = d_l; kv = false;
+      // l_s > 0: the recomputed window of a pyramided cache (Stage I over l_s rows per user)
+      if (n_seq < 1 || d_l < 1 || l_s < 0) return false;
+      n = n_seq; tin = rq = std::max(d_l, l_s); kv = false;
       return true;
     default:
       return false;
@@ -373,7 +374,7 @@ int check_ws(const Dims &D, const Ws &L, void *ws, size_t ws_bytes) {
 int check_cache(const onetrans_kv_cache *c) {
   if (!c || !c->k || !c->v || !c->layer_len) return ONETRANS_ERR_INVALID_ARG;
   if (c->n_users < 1 || c->capacity < 1) return ONETRANS_ERR_INVALID_ARG;
-  if (misaligned(c->k) || misaligned(c->v)) return ONETRANS_ERR_ALIGNMENT;
+  if (misaligned(c->k) || misaligned(c->v) || (c->x_tail && misaligned(c->x_tail))) return ONETRANS_ERR_ALIGNMENT;
   return ONETRANS_OK;
 }
 
@@ -581,6 +582,7 @@ onetrans_kv_cache user_view(const Dims &D, const onetrans_kv_cache *c, int first
   v.v = (char *)c->v + first * user_bytes;
   v.n_users = c->n_users - first;
   v.user_len = c->user_len ? c->user_len + first : nullptr;
+  v.x_tail = c->x_tail ? (char *)c->x_tail + first * (size_t)c->capacity * D.d * 4 : nullptr;
   return v;
 }
 
@@ -629,11 +631,20 @@ int forward_run(const Dims &D, const onetrans_config *cfg, const onetrans_block_
   return ONETRANS_OK;
 }
 
-// The append launch sequence for `n_users` users of `cache` (a view whose first user is the call's
-// first user), with workspace `w` laid out as L. l_old: cached rows (0 for ragged users, whose own
-// lengths come from cache->user_len).
+// Rows of user-major [user][capacity][d] fp32 x_tail, addressed by position in the sequence.
+inline RowView tail_rows(const Dims &D, const onetrans_kv_cache *c, int t_off) {
+  return RowView{c->x_tail, (long long)c->capacity * D.d, t_off, D.d};
+}
+
+// The append launch sequence over blocks [0, n_head) for `n_users` users of `cache` (a view whose
+// first user is the call's first user), with workspace `w` laid out as L. l_old: cached rows (0
+// for ragged users, whose own lengths come from cache->user_len). Every block computes the d_l new
+// rows; their K/V go to offset l_old. When n_head == N the last block keeps q_final of the new rows
+// as queries (its last q_final rows; out_new [U][q_final][d]); otherwise the outputs of block
+// n_head - 1 for the new rows go to x_tail at their positions (the recomputed blocks' input).
 int append_run(const Dims &D, const onetrans_block_weights *blk, const onetrans_kv_cache *cache, const void *x_new,
-               int n_users, int d_l, void *out_new, char *w, const Ws &L, int l_old, hipStream_t stream) {
+               int n_users, int d_l, void *out_new, char *w, const Ws &L, int l_old, int n_head, int q_final,
+               hipStream_t stream) {
   int rc;
   const bool ragged = cache->user_len != nullptr;
   if (ragged && (rc = upload_user_len(cache, n_users, w, L, stream))) return rc;
@@ -644,12 +655,14 @@ int append_run(const Dims &D, const onetrans_block_weights *blk, const onetrans_
   RowView x{const_cast<void *>(x_new), (long long)d_l * d, l_old, d};
   int x_f32 = D.dt == ONETRANS_F32;
   void *stats = nullptr;   // (mean, rstd) rows of x when the previous block wrote them
-  for (int n = 0; n < D.N; ++n) {
-    const bool last = n + 1 == D.N;
+  for (int n = 0; n < n_head; ++n) {
+    const bool last = n + 1 == D.N;        // the stack's last block
+    const bool to_tail = n + 1 == n_head && !last;
+    const int q = last ? q_final : d_l;
     Step st{};
     st.n_seq = n_users;
     st.s = l_old + d_l;
-    st.q = d_l;
+    st.q = q;
     st.kv_t0 = l_old;
     st.kv_n = d_l;
     st.ns = 0;
@@ -667,12 +680,17 @@ int append_run(const Dims &D, const onetrans_block_weights *blk, const onetrans_
     st.vp = st.vS.base;
     st.pre_sb = st.kS.sb;
     st.pre_sh = st.kS.sh;
-    st.out = RowView{last && out_new ? out_new : (void *)(w + L.x[n & 1]), (long long)d_l * d, l_old, d};
+    if (to_tail)
+      st.out = tail_rows(D, cache, 0);
+    else if (last)
+      st.out = RowView{out_new, (long long)q * d, l_old + d_l - q, d};
+    else
+      st.out = RowView{w + L.x[n & 1], (long long)d_l * d, l_old, d};
     st.kv_shift = shift;
     st.seq_shift = shift;
     st.stats_in = stats;
-    st.stats_out = last ? nullptr : (void *)(w + L.st[n & 1]);
-    st.need_out = !last || out_new != nullptr;
+    st.stats_out = last || to_tail ? nullptr : (void *)(w + L.st[n & 1]);
+    st.need_out = !last || (out_new != nullptr && q > 0);
     if ((rc = run_step(D, blk[n], st, w, L, stream))) return rc;
     x = RowView{w + L.x[n & 1], (long long)d_l * d, l_old, d};
     stats = st.stats_out;
@@ -736,21 +754,24 @@ int score_run(const Dims &D, const onetrans_block_weights *blk, const onetrans_k
   return ONETRANS_OK;
 }
 
-// The Stage I launch sequence for `n_users` users of `cache` (a view whose first user is the
-// call's first user), with workspace `w` laid out as L. Writes no host state.
-int prefill_run(const Dims &D, const onetrans_config *cfg, const onetrans_block_weights *blk, const void *x_s,
-                int n_users, int l_s, const onetrans_kv_cache *cache, void *out_s, char *w, const Ws &L,
-                hipStream_t stream) {
+// The Stage I launch sequence over blocks [n0, N) for `n_users` users of `cache` (a view whose
+// first user is the call's first user), with workspace `w` laid out as L. Block n0's input rows are
+// `x` (s rows per user at block positions 0..s-1; x_f32: fp32 rather than the storage dtype). Block
+// n keeps q[n] tail rows as the next block's input and writes the K/V of all its rows into the
+// cache; the last block keeps q_final rows and writes them to `out` ([U][q_final][d], or nothing
+// if null). Block tail_block (-1: none; its positions must be the sequence's) also writes its kept
+// rows to x_tail, from where the next block reads them. Writes no host state.
+int stack_run(const Dims &D, const onetrans_block_weights *blk, RowView x, int x_f32, int s, int n_users,
+              const onetrans_kv_cache *cache, int n0, const int *q_of, int q_final, int tail_block, void *out,
+              char *w, const Ws &L, hipStream_t stream) {
   int rc;
   const int d = D.d;
-  int s = l_s;
-  RowView x{const_cast<void *>(x_s), (long long)l_s * d, 0, d};
-  int x_f32 = D.dt == ONETRANS_F32;
   void *stats = nullptr;   // (mean, rstd) rows of x when the previous block wrote them
-  for (int n = 0; n < D.N; ++n) {
-    const int q = cfg->s_queries[n];
-    const int p0 = s - q;
+  for (int n = n0; n < D.N; ++n) {
     const bool last = n + 1 == D.N;
+    const bool to_tail = n == tail_block && !last;
+    const int q = last ? q_final : q_of[n];
+    const int p0 = s - q;
     Step st{};
     st.n_seq = n_users;
     st.s = s;
@@ -772,17 +793,31 @@ int prefill_run(const Dims &D, const onetrans_config *cfg, const onetrans_block_
     st.vp = st.vS.base;
     st.pre_sb = st.kS.sb;
     st.pre_sh = st.kS.sh;
-    st.out = RowView{last ? out_s : (void *)(w + L.x[n & 1]), (long long)q * d, p0, d};
-    st.need_out = !last || out_s != nullptr;
+    if (to_tail)
+      st.out = tail_rows(D, cache, 0);
+    else
+      st.out = RowView{last ? out : (void *)(w + L.x[n & 1]), (long long)q * d, p0, d};
+    st.need_out = !last || out != nullptr;
     st.stats_in = stats;
-    st.stats_out = last ? nullptr : (void *)(w + L.st[n & 1]);
+    st.stats_out = last || to_tail ? nullptr : (void *)(w + L.st[n & 1]);
     if ((rc = run_step(D, blk[n], st, w, L, stream))) return rc;
-    x = RowView{w + L.x[n & 1], (long long)q * d, 0, d};
+    // the next block's row t is this block's position p0 + t
+    x = to_tail ? tail_rows(D, cache, -p0) : RowView{w + L.x[n & 1], (long long)q * d, 0, d};
     stats = st.stats_out;
     x_f32 = 1;
     s = q;
   }
   return ONETRANS_OK;
+}
+
+// First block of a schedule that prunes (keeps fewer rows than its input has), or -1.
+int first_pruning_block(const int *q, int N, int l_s) {
+  int s = l_s;
+  for (int n = 0; n < N; ++n) {
+    if (q[n] < s) return n;
+    s = q[n];
+  }
+  return -1;
 }
 
 }  // namespace
@@ -863,11 +898,15 @@ int onetrans_prefill_user(const onetrans_config *cfg, const onetrans_block_weigh
   if (ws_bytes < ws_layout(D, (n_users + wp - 1) / wp, tin, rq, kv).total * wp) return ONETRANS_ERR_WORKSPACE;
   const size_t part_bytes = ws_layout(D, (n_users + parts - 1) / parts, tin, rq, kv).total;
   const size_t in_user = (size_t)l_s * D.d * D.esz, out_user = (size_t)cfg->s_queries[D.N - 1] * D.d * 4;
+  // the first pruning block's kept rows go to x_tail too (when a later block exists to read them)
+  const int n_star = first_pruning_block(cfg->s_queries, D.N, l_s);
+  const int tail_block = cache->x_tail && n_star >= 0 && n_star < D.N - 1 ? n_star : -1;
   rc = over_streams(n_users, parts, stream, [&](int first, int count, int part, hipStream_t st) {
     const onetrans_kv_cache view = user_view(D, cache, first);
-    return prefill_run(D, cfg, blk, (const char *)x_s + first * in_user, count, l_s, &view,
-                       out_s ? (char *)out_s + first * out_user : nullptr, (char *)ws + part * part_bytes,
-                       ws_layout(D, count, tin, rq, kv), st);
+    RowView x{const_cast<char *>((const char *)x_s + first * in_user), (long long)l_s * D.d, 0, D.d};
+    return stack_run(D, blk, x, D.dt == ONETRANS_F32, l_s, count, &view, 0, cfg->s_queries, cfg->s_queries[D.N - 1],
+                     tail_block, out_s ? (char *)out_s + first * out_user : nullptr, (char *)ws + part * part_bytes,
+                     ws_layout(D, count, tin, rq, kv), st);
   });
   if (rc) return rc;
   int s = l_s;
@@ -875,6 +914,7 @@ int onetrans_prefill_user(const onetrans_config *cfg, const onetrans_block_weigh
     cache->layer_len[n] = s;
     s = cfg->s_queries[n];
   }
+  cache->q_last = cfg->s_queries[D.N - 1];
   return ONETRANS_OK;
 }
 
@@ -941,11 +981,21 @@ int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weig
   if (misaligned(x_new) || (out_new && misaligned(out_new))) return ONETRANS_ERR_ALIGNMENT;
   if ((rc = check_cache(cache))) return rc;
   if (n_users > cache->n_users) return ONETRANS_ERR_SHAPE;
-  for (int n = 0; n < D.N; ++n) {
+  for (int n = 0; n < D.N; ++n)
     if (cache->layer_len[n] < 0 || cache->layer_len[n] > cache->capacity) return ONETRANS_ERR_SHAPE;
-    if (cache->layer_len[n] != cache->layer_len[0]) return ONETRANS_ERR_UNSUPPORTED;
+  // the cache's pyramid: block n has s_n = layer_len[n] rows and keeps q_n = layer_len[n + 1]
+  // (the last block: q_last); n_star = the first block that prunes
+  const int q_last = cache->q_last > 0 ? cache->q_last : cache->layer_len[D.N - 1];
+  int n_star = -1;
+  for (int n = 0; n < D.N; ++n) {
+    const int qn = n + 1 < D.N ? cache->layer_len[n + 1] : q_last;
+    if (qn > cache->layer_len[n]) return ONETRANS_ERR_SHAPE;   // no pyramid grows
+    if (qn < cache->layer_len[n] && n_star < 0) n_star = n;
   }
   const bool ragged = cache->user_len != nullptr;
+  const bool recompute = n_star >= 0 && n_star < D.N - 1;   // blocks n_star + 1 .. run again
+  if (ragged && n_star >= 0) return ONETRANS_ERR_UNSUPPORTED;
+  if (recompute && !cache->x_tail) return ONETRANS_ERR_INVALID_ARG;
   if (ragged) {
     if ((rc = check_user_len(cache, n_users, cache->capacity))) return rc;
     for (int u = 0; u < n_users; ++u)
@@ -953,30 +1003,50 @@ int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weig
   } else if ((long long)cache->layer_len[0] + d_l > cache->capacity) {
     return ONETRANS_ERR_CACHE_CAPACITY;
   }
-  if ((rc = check_size(D, n_users, d_l))) return rc;
+  const int window = recompute ? cache->layer_len[n_star + 1] : 0;   // rows of block n_star + 1
+  if ((rc = check_size(D, n_users, std::max(d_l, window)))) return rc;
   size_t n, tin, rq;
   bool kv;
-  ws_dims(cfg, D, ONETRANS_OP_APPEND, n_users, 0, 0, d_l, n, tin, rq, kv);
+  ws_dims(cfg, D, ONETRANS_OP_APPEND, n_users, window, 0, d_l, n, tin, rq, kv);
   const int wp = ws_parts_for(n_users, USER_PART_MIN), parts = parts_for(n_users, USER_PART_MIN);
   if (misaligned(ws)) return ONETRANS_ERR_ALIGNMENT;
   if (!ws) return ONETRANS_ERR_INVALID_ARG;
   if (ws_bytes < ws_layout(D, (n_users + wp - 1) / wp, tin, rq, kv).total * wp) return ONETRANS_ERR_WORKSPACE;
   const int l_old = ragged ? 0 : cache->layer_len[0];
+  const int l_new = l_old + d_l;
+  // the last block's kept rows after the append: it grows with the sequence unless it prunes
+  const bool last_prunes = n_star >= 0;    // n_star <= N - 1: the last block keeps a fixed count
+  const int q_last_new = last_prunes ? q_last : q_last + d_l;
+  const int q_final = std::min(d_l, q_last_new);   // final rows of the new events
+  const int n_head = recompute ? n_star + 1 : D.N;
+  // the recomputed blocks' schedule: block n keeps layer_len[n + 1] rows
+  std::vector<int> q_of(D.N);
+  for (int b = 0; b + 1 < D.N; ++b) q_of[b] = cache->layer_len[b + 1];
+  q_of[D.N - 1] = q_last;
   const size_t part_bytes = ws_layout(D, (n_users + parts - 1) / parts, tin, rq, kv).total;
-  const size_t in_user = (size_t)d_l * D.d * D.esz, out_user = (size_t)d_l * D.d * 4;
+  const size_t in_user = (size_t)d_l * D.d * D.esz, out_user = (size_t)q_final * D.d * 4;
   rc = over_streams(n_users, parts, stream, [&](int first, int count, int part, hipStream_t st) {
     const onetrans_kv_cache view = user_view(D, cache, first);
-    return append_run(D, blk, &view, (const char *)x_new + first * in_user, count, d_l,
-                      out_new ? (char *)out_new + first * out_user : nullptr, (char *)ws + part * part_bytes,
-                      ws_layout(D, count, tin, rq, kv), l_old, st);
+    char *w = (char *)ws + part * part_bytes;
+    const Ws Lp = ws_layout(D, count, tin, rq, kv);
+    void *out = out_new ? (char *)out_new + first * out_user : nullptr;
+    int r = append_run(D, blk, &view, (const char *)x_new + first * in_user, count, d_l, out, w, Lp, l_old, n_head,
+                       q_final, st);
+    if (r || !recompute) return r;
+    // blocks n_star + 1 .. over their slid windows: block n_star + 1 reads the last `window` rows of
+    // the sequence from x_tail (the old rows written by prefill, the new ones by the blocks above)
+    return stack_run(D, blk, tail_rows(D, &view, -(l_new - window)), 1, window, count, &view, n_star + 1, q_of.data(),
+                     q_final, -1, out, w, Lp, st);
   });
   if (rc) return rc;
   if (ragged) {
     int longest = 0;
     for (int u = 0; u < n_users; ++u) longest = max(longest, cache->user_len[u] += d_l);
-    for (int n = 0; n < D.N; ++n) cache->layer_len[n] = max(cache->layer_len[n], longest);
+    for (int b = 0; b < D.N; ++b) cache->layer_len[b] = max(cache->layer_len[b], longest);
+    cache->q_last = cache->layer_len[D.N - 1];
   } else {
-    for (int n = 0; n < D.N; ++n) cache->layer_len[n] = l_old + d_l;
+    for (int b = 0; b < n_head; ++b) cache->layer_len[b] = l_new;
+    cache->q_last = q_last_new;
   }
   return ONETRANS_OK;
 }
