@@ -56,7 +56,9 @@ def test_workspace_and_cache_sizes():
     got = lib.onetrans_workspace_bytes(ctypes.byref(c), L.OP_FORWARD, B, l_s, 0, 0)
     d, T, R = 256, 136, 116
     al = lambda n: (n + 255) // 256 * 256
-    expect = 2 * al(B * R * d * 4) + 2 * al(B * R * 8) + al(B * R * d * 2) + 2 * al(B * T * d * 2) + al(B * R * d * 2) + al(16) + al(B * 4)
+    part = al(B * R * 8 * d * 4)          # partial sums of split post launches (8 splits; at most 32 MiB)
+    expect = (2 * al(B * R * d * 4) + 2 * al(B * R * 8) + al(B * R * d * 2) + 2 * al(B * T * d * 2) + al(B * R * d * 2)
+              + al(16) + al(B * 4) + part)
     assert got == expect
     assert lib.onetrans_kv_cache_bytes(ctypes.byref(c), 3, 200) == 3 * 2 * 8 * 200 * 32 * 2
     assert lib.onetrans_workspace_bytes(ctypes.byref(c), L.OP_SCORE, 2, 0, 5, 0) > 0
@@ -301,8 +303,10 @@ def test_forward_workspace_covers_the_split():
     """Batches of 64+ run as two halves: the workspace holds two half-batch layouts, which also covers
     the single-stream layout of the whole batch."""
     lib = L.lib()
-    c = _cfg()
-    one = lambda B: lib.onetrans_workspace_bytes(ctypes.byref(c), L.OP_FORWARD, B, 120, 0, 0)
+    # 416 query rows per sample: no call of 10+ samples is small enough for split post launches, so
+    # every layout below is the same per-sample layout
+    c = _cfg(sq=(400, 200))
+    one = lambda B: lib.onetrans_workspace_bytes(ctypes.byref(c), L.OP_FORWARD, B, 400, 0, 0)
     assert one(64) == 2 * one(32)
     assert one(65) == 2 * one(33)
     assert one(65) >= one(63)
@@ -330,6 +334,12 @@ def test_noalloc_score_validation():
     assert f(ctypes.byref(c), b, ctypes.byref(kc), None, 2, 4, FAKE, None) == L.ERR_INVALID_ARG
     assert f(ctypes.byref(c), b, ctypes.byref(kc), FAKE, 2, 4, FAKE + 4, None) == L.ERR_ALIGNMENT
     assert f(ctypes.byref(_cfg(lns=0)), b, ctypes.byref(kc), FAKE, 2, 4, FAKE, None) == L.ERR_SHAPE
-    per = lib.onetrans_workspace_bytes(ctypes.byref(c), L.OP_SCORE, 1, 0, 1, 0)
-    assert f(ctypes.byref(c), b, ctypes.byref(kc), FAKE, 2, L.SCRATCH_BYTES // per, FAKE, None) == L.ERR_SCRATCH
+    # the scratch holds about 1000 candidates of this shape (d = 256, 16 NS tokens): 2 users x 600 do not fit
+    assert lib.onetrans_workspace_bytes(ctypes.byref(c), L.OP_SCORE, 1, 0, 1000, 0) <= L.SCRATCH_BYTES
+    assert f(ctypes.byref(c), b, ctypes.byref(kc), FAKE, 2, 600, FAKE, None) == L.ERR_SCRATCH
+    # ...and the candidates that fit form one range (the split post launches' partials buffer only
+    # exists for small calls and never pushes a smaller call past the scratch)
+    need = [lib.onetrans_workspace_bytes(ctypes.byref(c), L.OP_SCORE, 1, 0, n, 0) for n in range(1, 1100, 7)]
+    fits = [x <= L.SCRATCH_BYTES for x in need]
+    assert fits == sorted(fits, reverse=True)
     assert "scratch" in L.status_string(L.ERR_SCRATCH)

@@ -322,13 +322,208 @@ __global__ __launch_bounds__(ATTN_WAVES * 64) void attn_kernel(const AttnArgs a)
   }
 }
 
+// Launches with at most 32 query rows per (sequence or user, head): an append's new rows, the
+// last pyramid blocks, Stage II of one or two candidates per user. One workgroup per (sequence or
+// user, head) whose waves split the KEYS: wave w takes a contiguous range of 32-key subtiles of the
+// prefix for the same 32 query lanes, streams them through its own LDS tile (loads of subtile i + 1
+// in flight while subtile i is computed; no workgroup barrier in the key loop); in Stage II the last
+// wave also folds in the candidates' own NS keys. The eight partial softmax states (m, l, o) are
+// merged exactly at the end:
+//   o = sum_w 2^(m_w - M) o_w / sum_w 2^(m_w - M) l_w,   M = max_w m_w.
+template <typename T, int DH, bool STAGE2>
+__global__ __launch_bounds__(ATTN_WAVES * 64) void attn_split_kernel(const AttnArgs a) {
+  using M = Mma<T>;
+  using frag = typename M::frag;
+  constexpr int EPC = 16 / (int)sizeof(T);
+  constexpr int NWA = ATTN_WAVES;
+  constexpr int LDK = DH + EPC;      // padded K row (elements)
+  constexpr int LDW = 32 + EPC;      // padded V^T row (keys)
+  constexpr int CPK = DH / EPC;      // 16-byte pieces per key row
+  constexpr int NPL = (32 * CPK + 63) / 64;   // K (and V) pieces per lane per subtile
+  using TS = TileStage<T>;
+  // LDS: per-wave K / V^T tiles during the key loop; after a barrier the same bytes hold the merge
+  // (every wave's m, l and o) and the output staging tile
+  constexpr int TILE_BYTES = NWA * (32 * LDK + DH * LDW) * (int)sizeof(T);
+  constexpr int MERGE_BYTES = NWA * (2 * 32 + 16 * 64) * 4 + TS::SIZE * (int)sizeof(T);
+  __shared__ __attribute__((aligned(16))) unsigned char smem[TILE_BYTES > MERGE_BYTES ? TILE_BYTES : MERGE_BYTES];
+  T (*sK)[32 * LDK] = (T (*)[32 * LDK])smem;
+  T (*sV)[DH * LDW] = (T (*)[DH * LDW])(smem + NWA * 32 * LDK * sizeof(T));
+  float (*s_o)[16][64] = (float (*)[16][64])smem;
+  float (*s_m)[32] = (float (*)[32])(smem + NWA * 16 * 64 * 4);
+  float (*s_l)[32] = (float (*)[32])(smem + NWA * (16 * 64 + 32) * 4);
+  T *stage = (T *)(smem + NWA * (16 * 64 + 64) * 4);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, lc = lane & 31;
+  const int H = a.n_heads;
+  const int pair = blockIdx.x;
+  const int h = pair % H, grp = pair / H;
+  // this lane's query: forward, row lc of sequence grp; Stage II, NS row qi of candidate cslot
+  int z, qi, cslot = 0, cpw = 0;
+  bool valid;
+  if constexpr (!STAGE2) {
+    z = grp;
+    qi = lc;
+    valid = qi < a.R;
+  } else {
+    cpw = 32 / a.R;
+    cslot = lc / a.R;
+    qi = lc - cslot * a.R;
+    valid = cslot < cpw && cslot < a.n_cand;
+    z = grp * a.n_cand + (valid ? cslot : 0);
+  }
+  const int shift = a.seq_shift ? a.seq_shift[grp] : 0;
+  const int p0 = a.p0 + shift, n_pre = a.n_pre + shift;
+  const int qpos = p0 + qi;
+
+  frag qf[DH / M::KSTEP];
+  {
+    const T *qrow = (const T *)a.q + z * a.q_sb + h * a.q_sh + (long long)(valid ? qi : 0) * DH + g * M::KPL;
+#pragma unroll
+    for (int kk = 0; kk < DH / M::KSTEP; ++kk) qf[kk] = valid ? *(const frag *)(qrow + kk * M::KSTEP) : M::zero();
+  }
+  // prefix keys 0..n_keys-1 (forward: up to the last query's position), split in whole subtiles
+  const int n_keys = STAGE2 ? n_pre : min(n_pre, p0 + a.R);
+  const int n_sub = (n_keys + 31) / 32;
+  const int per = (n_sub + NWA - 1) / NWA;
+  const int sub0 = min(n_sub, wave * per), sub1 = min(n_sub, sub0 + per);
+  const T *kp = (const T *)a.k_pre + grp * a.pre_sb + h * a.pre_sh;
+  const T *vp = (const T *)a.v_pre + grp * a.pre_sb + h * a.pre_sh;
+
+  SoftmaxState st;
+  st.m = -1e30f;
+  st.lsum = 0.0f;
+  st.o = f32x16{};
+  T *kw = sK[wave];
+  T *vw = sV[wave];
+  u32x4 pk[NPL], pv[NPL];
+  auto load = [&](int sub) {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int ch = lane + 64 * i;
+      const int key = ch / CPK, c0 = (ch - key * CPK) * EPC;
+      const int kg = sub * 32 + key;
+      pk[i] = u32x4{0, 0, 0, 0};
+      pv[i] = u32x4{0, 0, 0, 0};
+      if (ch < 32 * CPK && kg < n_keys) {
+        pk[i] = ld16(kp + (long long)kg * DH + c0);
+        pv[i] = ld16(vp + (long long)kg * DH + c0);
+      }
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int ch = lane + 64 * i;
+      if (ch < 32 * CPK) {
+        const int key = ch / CPK, c0 = (ch - key * CPK) * EPC;
+        st16(&kw[key * LDK + c0], pk[i]);
+        const T *ve = (const T *)&pv[i];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) vw[(c0 + e) * LDW + key] = ve[e];
+      }
+    }
+  };
+  if (sub0 < sub1) load(sub0);
+  for (int sub = sub0; sub < sub1; ++sub) {
+    wait_lgkm0();                              // this wave's reads of the previous subtile are done
+    store();
+    if (sub + 1 < sub1) load(sub + 1);
+    wait_lgkm0();                              // the tile is in LDS (only this wave reads it)
+    f32x16 s = score_tile<T, DH>(&kw[lc * LDK + g * M::KPL], qf);
+    const int kb = sub * 32;
+    if ((!STAGE2 && kb + 31 > p0) || kb + 32 > n_keys) {
+      const int lim = (STAGE2 ? n_keys - 1 : min(qpos, n_keys - 1)) - kb - 4 * g;
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (acc_row(v, 0) > lim) s[v] = NEG_INF;
+    }
+    softmax_pv<T, DH>(s, st, lc < DH ? &vw[lc * LDW] : nullptr, g);
+  }
+
+  // ---- Stage II: the candidates' own NS keys (block-diagonal causal), on the last wave --------
+  if constexpr (STAGE2) {
+    if (wave == NWA - 1) {
+      const int n_own = min(cpw, a.n_cand) * a.R;
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        const int ch = lane + 64 * i;
+        const int ks = ch / CPK, c0 = (ch - ks * CPK) * EPC;
+        const int kc = ks / a.R, j2 = ks - kc * a.R;
+        pk[i] = u32x4{0, 0, 0, 0};
+        pv[i] = u32x4{0, 0, 0, 0};
+        if (ch < 32 * CPK && ks < n_own) {
+          const long long off = (long long)(grp * a.n_cand + kc) * a.own_sb + h * a.own_sh + (long long)j2 * DH + c0;
+          pk[i] = ld16((const T *)a.k_own + off);
+          pv[i] = ld16((const T *)a.v_own + off);
+        }
+      }
+      wait_lgkm0();
+      store();
+      wait_lgkm0();
+      f32x16 s = score_tile<T, DH>(&kw[lc * LDK + g * M::KPL], qf);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int ks = acc_row(v, g);
+        const int kc = ks / a.R, j2 = ks - kc * a.R;
+        if (!(ks < n_own && kc == cslot && j2 <= qi)) s[v] = NEG_INF;
+      }
+      softmax_pv<T, DH>(s, st, lc < DH ? &vw[lc * LDW] : nullptr, g);
+    }
+  }
+
+  // ---- merge the waves' partial states ------------------------------------------------------
+  const float lt = st.lsum + other_half(st.lsum);
+  __syncthreads();                             // every wave is done with its tiles
+  if (g == 0) {
+    s_m[wave][lc] = st.m;
+    s_l[wave][lc] = lt;
+  }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) s_o[wave][v][lane] = st.o[v];
+  __syncthreads();
+  if (wave != 0) return;
+  float mx = s_m[0][lc];
+#pragma unroll
+  for (int w = 1; w < NWA; ++w) mx = fmaxf(mx, s_m[w][lc]);
+  float l = 0.0f;
+  f32x16 o = f32x16{};
+#pragma unroll
+  for (int w = 0; w < NWA; ++w) {
+    const float sc = __builtin_amdgcn_exp2f(s_m[w][lc] - mx);
+    l += sc * s_l[w][lc];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o[v] += sc * s_o[w][v][lane];
+  }
+  const float inv = valid ? 1.0f / l : 0.0f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) o[v] *= inv;
+  TS::put(stage, o, lc, g);
+#pragma unroll
+  for (int k = 0; k < TS::NI; ++k) {
+    const int tok = TS::token(k, lane);
+    const int tz = __shfl(z, tok, 64), tq = __shfl(qi, tok, 64);
+    const bool tv = __shfl((int)valid, tok, 64) != 0;
+    const u32x4 piece = TS::get(stage, k, lane);
+    const int f = TS::feature(lane);
+    if (tv && f < DH) st16((T *)a.o + tz * a.o_sb + (long long)tq * a.d_model + h * DH + f, piece);
+  }
+}
+
 template <typename T, int DH>
 hipError_t launch_dh(int stage2, const AttnArgs &a, hipStream_t s) {
-  dim3 gd(a.n_qblocks * a.n_seq_grp * a.n_heads), bd(ATTN_WAVES * 64);
-  if (stage2)
-    hipLaunchKernelGGL((attn_kernel<T, DH, true>), gd, bd, 0, s, a);
-  else
-    hipLaunchKernelGGL((attn_kernel<T, DH, false>), gd, bd, 0, s, a);
+  dim3 bd(ATTN_WAVES * 64);
+  const dim3 split_grid(a.n_seq_grp * a.n_heads);
+  if (stage2) {
+    if (a.n_cand * a.R <= 32)   // every candidate of a user in the 32 query lanes of one wave
+      hipLaunchKernelGGL((attn_split_kernel<T, DH, true>), split_grid, bd, 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_kernel<T, DH, true>), dim3(a.n_qblocks * a.n_seq_grp * a.n_heads), bd, 0, s, a);
+  } else if (a.R <= 32) {
+    hipLaunchKernelGGL((attn_split_kernel<T, DH, false>), split_grid, bd, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((attn_kernel<T, DH, false>), dim3(a.n_qblocks * a.n_seq_grp * a.n_heads), bd, 0, s, a);
+  }
   return hipGetLastError();
 }
 

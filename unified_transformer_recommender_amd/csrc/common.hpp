@@ -246,6 +246,8 @@ struct QkvArgs {
   const void *gamma, *beta;   // norm1 [d]
   RowView stats;           // per-row (mean, rstd) of x from the previous block's tail, fp32; base null if absent
   int tg;                  // token groups of 32 per wave (1, or 2 where the kernel supports it)
+  int n_split;             // workgroups per token tile, each taking a contiguous range of the
+                           // tile's weight chunks (1: one workgroup does all of them)
   int layer;
   float eps;
   float q_scale;           // queries are stored multiplied by this (log2(e) / sqrt(d_head))
@@ -275,6 +277,10 @@ struct PostArgs {
   RowView stats;           // where to write per-row (mean, rstd) of X' for the next block's norm 1; base null: none
   int layer;
   float eps;
+  int n_split;             // workgroups per token tile, each over a contiguous range of the FFN's
+                           // hidden chunks (1: one workgroup does the whole FFN)
+  RowView part;            // n_split > 1: partial X' rows of split s at part.base + s * part_split
+  long long part_split;    // elements (fp32; compact rows by (sequence, position)); a reduce launch adds them
 };
 
 // ---------------------------------------------------------------------------------------------

@@ -14,12 +14,19 @@ hipError_t launch_qkv(int dtype, int in_f32, const QkvArgs &a, int grid, hipStre
 int qkv_max_groups(int dtype, int d_model);
 int qkv_tokens_per_tile(int tg);
 constexpr int QKV_SMALL_LAUNCH = 128;   // below this many two-group tiles, one group per wave
+// Chunk ranges per token tile (QkvArgs::n_split) at most, for a launch with too few tiles.
+int qkv_max_split(int d_model);
+constexpr int QKV_SPLIT_TARGET = 512;   // workgroups a split launch aims at (two per CU)
 
 hipError_t launch_attn(int dtype, int d_head, int stage2, const AttnArgs &a, hipStream_t s);
 
 // Fused post-attention kernel; tokens per workgroup tile for a dtype / d_model.
 hipError_t launch_post(int dtype, int resid_f32, const PostArgs &a, int grid, hipStream_t s);
 int post_tokens_per_tile(int dtype, int d_model);
+// Sum of a split post launch's partial rows (PostArgs::n_split > 1) into `out`, plus row statistics.
+hipError_t launch_post_reduce(const PostArgs &a, int rows, hipStream_t s);
+constexpr int POST_MAX_SPLIT = 8;        // hidden-chunk ranges per token tile at most
+constexpr long long POST_SPLIT_BYTES = 32ll << 20;   // partials buffer at most (fp32, POST_MAX_SPLIT copies)
 // fp32 storage at d = 512: the post-attention kernel on 16x16x4 MFMA tiles (16 tokens per wave).
 hipError_t launch_post_f32w(int d_model, const PostArgs &a, int grid, hipStream_t s);
 int post_f32w_tokens_per_tile();

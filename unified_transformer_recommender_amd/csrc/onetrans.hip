@@ -137,13 +137,23 @@ int check_weights(const onetrans_block_weights *blk, const Dims &D) {
 
 // ---- workspace -------------------------------------------------------------------------------
 struct Ws {
-  size_t x[2], st[2], q, k, v, o, trash, seq, total;
+  size_t x[2], st[2], q, k, v, o, trash, seq, part, total;
+  size_t part_rows;   // rows per split of the partial-sum buffer (0: no split post launches)
 };
 
 inline size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
 
-// n: sequences; tin: max block input rows; rq: max query rows; kv: K/V buffers needed
-Ws ws_layout(const Dims &D, size_t n, size_t tin, size_t rq, bool kv) {
+// Split post launches (the FFN's hidden chunks over several workgroups per token tile, partial sums
+// reduced afterwards) are used by a whole call or not at all, so that a call's results do not depend
+// on how it is split over streams: when the call's n_call sequences of rq query rows need at most
+// POST_SPLIT_BYTES of partials.
+inline bool post_split_call(const Dims &D, size_t n_call, size_t rq) {
+  return n_call * rq * POST_MAX_SPLIT * D.d * 4 <= (size_t)POST_SPLIT_BYTES;
+}
+
+// n: sequences; tin: max block input rows; rq: max query rows; kv: K/V buffers needed;
+// n_call: sequences of the whole call (n is one part of it)
+Ws ws_layout(const Dims &D, size_t n, size_t tin, size_t rq, bool kv, size_t n_call) {
   Ws w{};
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -168,6 +178,9 @@ Ws ws_layout(const Dims &D, size_t n, size_t tin, size_t rq, bool kv) {
   w.trash = take(16);
   // per-sequence row offsets of ragged cached users (int32)
   w.seq = take(n * 4);
+  // partial sums of post launches split over the FFN's hidden chunks (small launches only)
+  w.part_rows = post_split_call(D, n_call, rq) ? n * rq : 0;
+  w.part = take(w.part_rows * POST_MAX_SPLIT * d * 4);
   w.total = off;
   return w;
 }
@@ -260,9 +273,13 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
       if (st.kv_n > 0) add_job(RowSet{st.n_seq, st.kv_n, 1, st.kv_t0, 0, 0}, st.need_out ? p0 : no_q, st.kS, st.vS);
       if (st.ns > 0) add_job(RowSet{st.n_seq, 1, st.ns, st.s, 1, 1}, st.need_out ? st.s : no_q, st.kN, st.vN);
     };
-    // two token groups per wave, unless that leaves fewer workgroups than half the GPU's CUs
+    // two token groups per wave, unless that leaves fewer workgroups than half the GPU's CUs; a
+    // launch that still has few tiles splits each tile's weight chunks over several workgroups
     add_jobs(qkv_max_groups(D.dt, d));
     if (qa.tg == 2 && tiles < QKV_SMALL_LAUNCH) add_jobs(1);
+    qa.n_split = 1;
+    if (tiles > 0 && tiles < QKV_SPLIT_TARGET)
+      qa.n_split = (int)std::min<long long>(qkv_max_split(d), (QKV_SPLIT_TARGET + tiles - 1) / tiles);
     qa.n_jobs = nj;
     qa.d_model = d;
     qa.d_head = dh;
@@ -357,7 +374,24 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
     if (D.dt == ONETRANS_BF16 && d >= 256 && st.stats_out) pa.stats = RowView{st.stats_out, st.out.sb / d * 2, st.out.t_off, 2};
     pa.layer = D.layer;
     pa.eps = D.eps;
-    const hipError_t e = timed(ONETRANS_K_POST, stream, [&] { return launch_post(D.dt, st.x_f32, pa, (int)tiles, stream); });
+    // a small call splits the FFN's hidden chunks over up to POST_MAX_SPLIT workgroups per tile (the
+    // 32-token-tile kernels; partial sums in the workspace, then one reduce launch)
+    pa.n_split = 1;
+    const long long rows = (long long)st.n_seq * R;
+    const bool splittable = (D.dt == ONETRANS_BF16 || d <= 256) && L.part_rows > 0 && rows <= (long long)L.part_rows;
+    if (splittable) {
+      const int nc = D.dff / 32;
+      while (pa.n_split < POST_MAX_SPLIT && nc % (pa.n_split * 2) == 0) pa.n_split *= 2;
+    }
+    if (pa.n_split > 1) {
+      // compact rows, whatever the layout of `out` (x_tail's rows are `capacity` apart): the launch's
+      // R query rows per sequence from position p0, n_seq * R <= part_rows
+      pa.part = RowView{ws + L.part, (long long)R * d, p0, d};
+      pa.part_split = (long long)L.part_rows * d;
+    }
+    hipError_t e = timed(ONETRANS_K_POST, stream, [&] { return launch_post(D.dt, st.x_f32, pa, (int)tiles, stream); });
+    if (e == hipSuccess && pa.n_split > 1)
+      e = timed(ONETRANS_K_POST, stream, [&] { return launch_post_reduce(pa, (int)rows, stream); });
     if (e != hipSuccess) return ONETRANS_ERR_HIP;
   }
   return ONETRANS_OK;
@@ -833,7 +867,7 @@ size_t onetrans_workspace_bytes(const onetrans_config *cfg, int op, int n_seq, i
   if ((op == ONETRANS_OP_FORWARD || op == ONETRANS_OP_PREFILL) && check_schedule(cfg, l_s)) return 0;
   const int parts = ws_parts_for(n_seq, op == ONETRANS_OP_FORWARD ? FORWARD_PART_MIN : USER_PART_MIN);
   const size_t per = op == ONETRANS_OP_SCORE ? (size_t)n_cand : 1;   // sequences per user
-  return ws_layout(D, (size_t)((n_seq + parts - 1) / parts) * per, tin, rq, kv).total * parts;
+  return ws_layout(D, (size_t)((n_seq + parts - 1) / parts) * per, tin, rq, kv, (size_t)n_seq * per).total * parts;
 }
 
 size_t onetrans_kv_cache_bytes(const onetrans_config *cfg, int n_users, int capacity) {
@@ -859,13 +893,13 @@ int onetrans_forward(const onetrans_config *cfg, const onetrans_block_weights *b
   const int wp = ws_parts_for(batch, FORWARD_PART_MIN), parts = parts_for(batch, FORWARD_PART_MIN);
   if (misaligned(ws)) return ONETRANS_ERR_ALIGNMENT;
   if (!ws) return ONETRANS_ERR_INVALID_ARG;
-  if (ws_bytes < ws_layout(D, (batch + wp - 1) / wp, tin, rq, kv).total * wp) return ONETRANS_ERR_WORKSPACE;
-  const size_t part_bytes = ws_layout(D, (batch + parts - 1) / parts, tin, rq, kv).total;
+  if (ws_bytes < ws_layout(D, (batch + wp - 1) / wp, tin, rq, kv, batch).total * wp) return ONETRANS_ERR_WORKSPACE;
+  const size_t part_bytes = ws_layout(D, (batch + parts - 1) / parts, tin, rq, kv, batch).total;
   const size_t in_row = (size_t)(l_s + D.lns) * D.d * D.esz;
   const size_t out_row = (size_t)(cfg->s_queries[D.N - 1] + D.lns) * D.d * 4;
   return over_streams(batch, parts, stream, [&](int first, int count, int part, hipStream_t st) {
     return forward_run(D, cfg, blk, (const char *)x0 + first * in_row, count, l_s, (char *)out + first * out_row,
-                       (char *)ws + part * part_bytes, ws_layout(D, count, tin, rq, kv), st);
+                       (char *)ws + part * part_bytes, ws_layout(D, count, tin, rq, kv, batch), st);
   });
 }
 
@@ -895,8 +929,8 @@ int onetrans_prefill_user(const onetrans_config *cfg, const onetrans_block_weigh
   const int wp = ws_parts_for(n_users, USER_PART_MIN), parts = parts_for(n_users, USER_PART_MIN);
   if (misaligned(ws)) return ONETRANS_ERR_ALIGNMENT;
   if (!ws) return ONETRANS_ERR_INVALID_ARG;
-  if (ws_bytes < ws_layout(D, (n_users + wp - 1) / wp, tin, rq, kv).total * wp) return ONETRANS_ERR_WORKSPACE;
-  const size_t part_bytes = ws_layout(D, (n_users + parts - 1) / parts, tin, rq, kv).total;
+  if (ws_bytes < ws_layout(D, (n_users + wp - 1) / wp, tin, rq, kv, n_users).total * wp) return ONETRANS_ERR_WORKSPACE;
+  const size_t part_bytes = ws_layout(D, (n_users + parts - 1) / parts, tin, rq, kv, n_users).total;
   const size_t in_user = (size_t)l_s * D.d * D.esz, out_user = (size_t)cfg->s_queries[D.N - 1] * D.d * 4;
   // the first pruning block's kept rows go to x_tail too (when a later block exists to read them)
   const int n_star = first_pruning_block(cfg->s_queries, D.N, l_s);
@@ -906,7 +940,7 @@ int onetrans_prefill_user(const onetrans_config *cfg, const onetrans_block_weigh
     RowView x{const_cast<char *>((const char *)x_s + first * in_user), (long long)l_s * D.d, 0, D.d};
     return stack_run(D, blk, x, D.dt == ONETRANS_F32, l_s, count, &view, 0, cfg->s_queries, cfg->s_queries[D.N - 1],
                      tail_block, out_s ? (char *)out_s + first * out_user : nullptr, (char *)ws + part * part_bytes,
-                     ws_layout(D, count, tin, rq, kv), st);
+                     ws_layout(D, count, tin, rq, kv, n_users), st);
   });
   if (rc) return rc;
   int s = l_s;
@@ -930,15 +964,16 @@ int onetrans_score_candidates(const onetrans_config *cfg, const onetrans_block_w
   const int wp = ws_parts_for(n_users, USER_PART_MIN), parts = parts_for(n_users, USER_PART_MIN);
   if (misaligned(ws)) return ONETRANS_ERR_ALIGNMENT;
   if (!ws) return ONETRANS_ERR_INVALID_ARG;
-  if (ws_bytes < ws_layout(D, (size_t)((n_users + wp - 1) / wp) * n_cand, tin, rq, kv).total * wp)
+  const size_t n_call = (size_t)n_users * n_cand;
+  if (ws_bytes < ws_layout(D, (size_t)((n_users + wp - 1) / wp) * n_cand, tin, rq, kv, n_call).total * wp)
     return ONETRANS_ERR_WORKSPACE;
-  const size_t part_bytes = ws_layout(D, (size_t)((n_users + parts - 1) / parts) * n_cand, tin, rq, kv).total;
+  const size_t part_bytes = ws_layout(D, (size_t)((n_users + parts - 1) / parts) * n_cand, tin, rq, kv, n_call).total;
   const size_t in_user = (size_t)n_cand * D.lns * D.d * D.esz, out_user = (size_t)n_cand * D.lns * D.d * 4;
   return over_streams(n_users, parts, stream, [&](int first, int count, int part, hipStream_t st) {
     const onetrans_kv_cache view = user_view(D, cache, first);
     return score_run(D, blk, &view, (const char *)x_ns + first * in_user, count, n_cand,
                      (char *)out_ns + first * out_user, (char *)ws + part * part_bytes,
-                     ws_layout(D, (size_t)count * n_cand, tin, rq, kv), st);
+                     ws_layout(D, (size_t)count * n_cand, tin, rq, kv, n_call), st);
   });
 }
 
@@ -952,7 +987,7 @@ int onetrans_score_candidates_noalloc(const onetrans_config *cfg, const onetrans
   size_t n, tin, rq;
   bool kv;
   ws_dims(cfg, D, ONETRANS_OP_SCORE, n_users, 0, n_cand, 0, n, tin, rq, kv);
-  const Ws L = ws_layout(D, n, tin, rq, kv);
+  const Ws L = ws_layout(D, n, tin, rq, kv, n);
   if (L.total > (size_t)ONETRANS_SCRATCH_BYTES) return ONETRANS_ERR_SCRATCH;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return ONETRANS_ERR_HIP;
@@ -1011,7 +1046,7 @@ int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weig
   const int wp = ws_parts_for(n_users, USER_PART_MIN), parts = parts_for(n_users, USER_PART_MIN);
   if (misaligned(ws)) return ONETRANS_ERR_ALIGNMENT;
   if (!ws) return ONETRANS_ERR_INVALID_ARG;
-  if (ws_bytes < ws_layout(D, (n_users + wp - 1) / wp, tin, rq, kv).total * wp) return ONETRANS_ERR_WORKSPACE;
+  if (ws_bytes < ws_layout(D, (n_users + wp - 1) / wp, tin, rq, kv, n_users).total * wp) return ONETRANS_ERR_WORKSPACE;
   const int l_old = ragged ? 0 : cache->layer_len[0];
   const int l_new = l_old + d_l;
   // the last block's kept rows after the append: it grows with the sequence unless it prunes
@@ -1023,12 +1058,12 @@ int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weig
   std::vector<int> q_of(D.N);
   for (int b = 0; b + 1 < D.N; ++b) q_of[b] = cache->layer_len[b + 1];
   q_of[D.N - 1] = q_last;
-  const size_t part_bytes = ws_layout(D, (n_users + parts - 1) / parts, tin, rq, kv).total;
+  const size_t part_bytes = ws_layout(D, (n_users + parts - 1) / parts, tin, rq, kv, n_users).total;
   const size_t in_user = (size_t)d_l * D.d * D.esz, out_user = (size_t)q_final * D.d * 4;
   rc = over_streams(n_users, parts, stream, [&](int first, int count, int part, hipStream_t st) {
     const onetrans_kv_cache view = user_view(D, cache, first);
     char *w = (char *)ws + part * part_bytes;
-    const Ws Lp = ws_layout(D, count, tin, rq, kv);
+    const Ws Lp = ws_layout(D, count, tin, rq, kv, n_users);
     void *out = out_new ? (char *)out_new + first * out_user : nullptr;
     int r = append_run(D, blk, &view, (const char *)x_new + first * in_user, count, d_l, out, w, Lp, l_old, n_head,
                        q_final, st);

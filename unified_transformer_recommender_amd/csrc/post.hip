@@ -67,7 +67,7 @@ __device__ __forceinline__ bf16x8 natural_kfrag(bf16x8 f) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
-template <typename T, typename TR, int D, bool LAYER>
+template <typename T, typename TR, int D, bool LAYER, bool SPLIT>
 __global__ __launch_bounds__((post_nw<T, D>() * 64), (post_wgs_per_cu<T, D>())) void post_kernel(const PostArgs a) {
   using M = Mma<T>;
   using frag = typename M::frag;
@@ -94,11 +94,14 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64), (post_wgs_per_cu<T, D>())) 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lc = lane & 31;
   const int DFF = a.d_ff;
-  const int NC = DFF / 32;                      // hidden chunks
+  // workgroup -> (token tile, split): split s of n_split takes hidden chunks [hc0, hc0 + NC)
+  const int nsp = SPLIT ? a.n_split : 1;
+  const int bid = blockIdx.x / nsp, split = blockIdx.x - bid * nsp;
+  const int NC = DFF / 32 / nsp;                // hidden chunks of this workgroup (the host splits evenly)
+  const int hc0 = split * NC;
   const int NCH = DT + 2 * NC;                  // chunks in the stream
 
   // ---- job / group / token tile --------------------------------------------------------------
-  const int bid = blockIdx.x;
   const PostJob &jb = (a.n_jobs > 1 && bid >= a.job[1].tile_start) ? a.job[1] : a.job[0];
   const int local = bid - jb.tile_start;
   const int tm = local % jb.m_tiles, grp = local / jb.m_tiles;
@@ -111,9 +114,10 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64), (post_wgs_per_cu<T, D>())) 
   const int t = jb.rs.t0 + grp * jb.rs.t_step + (r - b * jb.rs.rows);
 
   const T *wo = (const T *)a.wo + (size_t)wg * D * D;
-  const T *w1 = (const T *)a.w1 + (size_t)wg * DFF * D;
-  const T *w2 = (const T *)a.w2 + (size_t)wg * D * DFF;
-  const T *b1 = (const T *)a.b1 + (size_t)wg * DFF;
+  // this split's hidden units start at 32 hc0: W1 rows, W2 columns and b1 entries from there
+  const T *w1 = (const T *)a.w1 + (size_t)wg * DFF * D + (size_t)(32 * hc0) * D;
+  const T *w2 = (const T *)a.w2 + (size_t)wg * D * DFF + 32 * hc0;
+  const T *b1 = (const T *)a.b1 + (size_t)wg * DFF + 32 * hc0;
   const T *b2 = (const T *)a.b2 + (size_t)wg * D;
 
   // ---- weight chunk stream --------------------------------------------------------------------
@@ -190,7 +194,7 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64), (post_wgs_per_cu<T, D>())) 
   for (int i = 0; i < NB - 1; ++i) issue(i);
 
   float *s_gm = svec, *s_bt = svec + D, *s_b2 = svec + 2 * D, *s_b1 = svec + 3 * D;
-  for (int i = tid; i < 3 * D + DFF; i += NW * 64) {
+  for (int i = tid; i < 3 * D + 32 * NC; i += NW * 64) {
     float v;
     if (i < D) v = to_f32(((const T *)a.gamma)[i]);
     else if (i < 2 * D) v = LAYER ? to_f32(((const T *)a.beta)[i - D]) : 0.0f;
@@ -276,7 +280,9 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64), (post_wgs_per_cu<T, D>())) 
         float y = (acc[ti][v] - mean) * rstd * s_gm[f];
         if constexpr (LAYER) y += s_bt[f];
         yh[v] = y;
-        acc[ti][v] += s_b2[f];
+        // split 0 carries Y + b2, the other splits only their part of the FFN
+        if (!SPLIT || split == 0) acc[ti][v] += s_b2[f];
+        else acc[ti][v] = 0.0f;
       }
       if constexpr (BF) {
 #pragma unroll
@@ -351,7 +357,7 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64), (post_wgs_per_cu<T, D>())) 
   }
 
   // ---- statistics of X' for the next block's norm 1 (exact two-pass over the registers) --------
-  if (a.stats.base != nullptr) {
+  if (!SPLIT && a.stats.base != nullptr) {
     float mean = 0.0f;
     if constexpr (LAYER) {
       float s = 0.0f;
@@ -388,7 +394,9 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64), (post_wgs_per_cu<T, D>())) 
       const int tok = TS::token(k, lane);
       const int tb = __shfl(b, tok, 64), tt = __shfl(t, tok, 64);
       rv[k] = __shfl((int)valid, tok, 64) != 0;
-      rowp[k] = (float *)a.out.base + tb * a.out.sb + (long long)(tt - a.out.t_off) * a.out.rs + TS::feature(lane);
+      const RowView &ov = SPLIT ? a.part : a.out;
+      rowp[k] = (float *)ov.base + (SPLIT ? split * a.part_split : 0) + tb * ov.sb + (long long)(tt - ov.t_off) * ov.rs +
+                TS::feature(lane);
     }
 #pragma unroll
     for (int ti = 0; ti < DT; ++ti) {
@@ -402,13 +410,86 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64), (post_wgs_per_cu<T, D>())) 
   }
 }
 
-template <typename T, typename TR, int D>
-hipError_t launch_dl(const PostArgs &a, int grid, hipStream_t s) {
+// Sum of the n_split partial X' rows of a split post launch into `out` (fixed order, so results do
+// not depend on timing), plus the row statistics for the next block's norm 1 when requested. One
+// wave per row, in the job order of the post launch.
+template <int D>
+__global__ __launch_bounds__(256) void post_reduce_kernel(const PostArgs a, int total) {
+  constexpr int PER = D / 64;                   // features per lane
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= total) return;
+  const int m0 = a.job[0].rs.n_seq * a.job[0].rs.rows * a.job[0].rs.n_groups;
+  const PostJob &jb = (a.n_jobs > 1 && row >= m0) ? a.job[1] : a.job[0];
+  const int local = row >= m0 ? row - m0 : row;
+  const int M_rows = jb.rs.n_seq * jb.rs.rows;
+  const int grp = local / M_rows, r = local - grp * M_rows;
+  const int b = r / jb.rs.rows;
+  const int t = jb.rs.t0 + grp * jb.rs.t_step + (r - b * jb.rs.rows);
+  const long long po = b * a.part.sb + (long long)(t - a.part.t_off) * a.part.rs + PER * lane;
+  float x[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) x[e] = 0.0f;
+  for (int sp = 0; sp < a.n_split; ++sp) {
+    const float *p = (const float *)a.part.base + sp * a.part_split + po;
+    if constexpr (PER >= 4) {
+#pragma unroll
+      for (int e = 0; e < PER; e += 4) {
+        const f32x4 v = *(const f32x4 *)(p + e);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x[e + q] += v[q];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < PER; ++e) x[e] += p[e];
+    }
+  }
+  float *o = (float *)a.out.base + b * a.out.sb + (long long)(t - a.out.t_off) * a.out.rs + PER * lane;
+  if constexpr (PER >= 4) {
+#pragma unroll
+    for (int e = 0; e < PER; e += 4) *(f32x4 *)(o + e) = f32x4{x[e], x[e + 1], x[e + 2], x[e + 3]};
+  } else {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o[e] = x[e];
+  }
+  if (a.stats.base != nullptr) {
+    float mean = 0.0f;
+    if (a.layer) {
+      float sm = 0.0f;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) sm += x[e];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) sm += __shfl_xor(sm, off, 64);
+      mean = sm * (1.0f / D);
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const float c = x[e] - mean;
+      ss += c * c;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    if (lane == 0) {
+      float *sp = (float *)a.stats.base + b * a.stats.sb + (long long)(t - a.stats.t_off) * a.stats.rs;
+      sp[0] = mean;
+      sp[1] = 1.0f / sqrtf(ss * (1.0f / D) + a.eps);
+    }
+  }
+}
+
+template <typename T, typename TR, int D, bool SPLIT>
+hipError_t launch_dls(const PostArgs &a, int grid, hipStream_t s) {
   if (a.layer)
-    hipLaunchKernelGGL((post_kernel<T, TR, D, true>), dim3(grid), dim3(post_nw<T, D>() * 64), 0, s, a);
+    hipLaunchKernelGGL((post_kernel<T, TR, D, true, SPLIT>), dim3(grid), dim3(post_nw<T, D>() * 64), 0, s, a);
   else
-    hipLaunchKernelGGL((post_kernel<T, TR, D, false>), dim3(grid), dim3(post_nw<T, D>() * 64), 0, s, a);
+    hipLaunchKernelGGL((post_kernel<T, TR, D, false, SPLIT>), dim3(grid), dim3(post_nw<T, D>() * 64), 0, s, a);
   return hipGetLastError();
+}
+
+template <typename T, typename TR, int D>
+hipError_t launch_dl(const PostArgs &a, int tiles, hipStream_t s) {
+  if (a.n_split > 1) return launch_dls<T, TR, D, true>(a, tiles * a.n_split, s);
+  return launch_dls<T, TR, D, false>(a, tiles, s);
 }
 
 template <typename T, typename TR>
@@ -431,6 +512,19 @@ int post_tokens_per_tile(int dtype, int d_model) {
   if (dtype == 1) return (d_model == 128 ? post_nw<bf16, 128>() : post_nw<bf16, 256>()) * 32;
   if (d_model >= 512) return post_f32w_tokens_per_tile();
   return post_nw<float, 256>() * 32;
+}
+
+hipError_t launch_post_reduce(const PostArgs &a, int rows, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const dim3 gd((rows + 3) / 4), bd(256);
+  switch (a.d_model) {
+    case 64: hipLaunchKernelGGL((post_reduce_kernel<64>), gd, bd, 0, s, a, rows); break;
+    case 128: hipLaunchKernelGGL((post_reduce_kernel<128>), gd, bd, 0, s, a, rows); break;
+    case 256: hipLaunchKernelGGL((post_reduce_kernel<256>), gd, bd, 0, s, a, rows); break;
+    case 512: hipLaunchKernelGGL((post_reduce_kernel<512>), gd, bd, 0, s, a, rows); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_post(int dtype, int resid_f32, const PostArgs &a, int grid, hipStream_t s) {

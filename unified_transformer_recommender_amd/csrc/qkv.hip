@@ -79,7 +79,9 @@ __global__ __launch_bounds__(QKV_NW * 64, (qkv_wgs_per_cu<T, D>())) void qkv_ker
   // ---- job / group / token tile --------------------------------------------------------------
   // The workgroup's tile is NW * TG * 32 rows of one parameter group; wave w holds token groups
   // w * TG .. w * TG + TG - 1 of it, and the lane's token lc of each.
-  const int bid = blockIdx.x;
+  // workgroup -> (token tile, chunk range): the n_split workgroups of a tile split its chunk stream
+  const int nsp = a.n_split > 1 ? a.n_split : 1;
+  const int bid = blockIdx.x / nsp, split = blockIdx.x - bid * nsp;
   const QkvJob &jb = (a.n_jobs > 1 && bid >= a.job[1].tile_start) ? a.job[1] : a.job[0];
   const int local = bid - jb.tile_start;
   const int tm = local % jb.m_tiles, grp = local / jb.m_tiles;
@@ -99,6 +101,11 @@ __global__ __launch_bounds__(QKV_NW * 64, (qkv_wgs_per_cu<T, D>())) void qkv_ker
     any_q = any_q || lane_q[tg];
   }
   const bool tile_q = __syncthreads_or(any_q);   // does any token of this workgroup issue a query?
+  // this workgroup's chunks [c0, c1) of the stream K 0..DT-1, V, then Q (Q only if tile_q)
+  const int per_split = (3 * DT + nsp - 1) / nsp;
+  const int c0 = split * per_split;
+  const int c1 = min(tile_q ? 3 * DT : 2 * DT, c0 + per_split);
+  if (c0 >= c1) return;                          // uniform over the workgroup: no later barrier is missed
   // Output pieces this lane stores (one per store instruction): the piece's token within its
   // group, and whether it is written at all. Every store instruction is issued; a lane with
   // nothing to write sends its piece to a trash slot, so the number of outstanding vector-memory
@@ -119,7 +126,6 @@ __global__ __launch_bounds__(QKV_NW * 64, (qkv_wgs_per_cu<T, D>())) void qkv_ker
   T *stg = stage[wave];
 
   // ---- weight chunk stream: K chunks 0..DT-1, V chunks, then (if any query row) Q chunks -------
-  const int n_chunks = tile_q ? 3 * DT : 2 * DT;
   const T *wk = (const T *)a.wk + (size_t)wg * D * D;
   const T *wv = (const T *)a.wv + (size_t)wg * D * D;
   const T *wq = (const T *)a.wq + (size_t)wg * D * D;
@@ -140,7 +146,7 @@ __global__ __launch_bounds__(QKV_NW * 64, (qkv_wgs_per_cu<T, D>())) void qkv_ker
 #pragma unroll
     for (int j = 0; j < LPW; ++j) dma16s(base, off[j], dst + (uint32_t)((j * NW + wave_s) * 64 * 16));
   };
-  issue(0);                                      // n_chunks >= 2 * DT >= 2
+  issue(c0);
 
   for (int i = tid; i < D; i += NW * 64) {
     s_gm[i] = to_f32(((const T *)a.gamma)[i]);
@@ -263,16 +269,16 @@ __global__ __launch_bounds__(QKV_NW * 64, (qkv_wgs_per_cu<T, D>())) void qkv_ker
 
   // ---- chunk loop ----------------------------------------------------------------------------
   // Before the barrier of chunk i this wave waits for its own loads of chunk i: after those it
-  // has issued only the NS stores of chunk i - 1 (for chunk 0: nothing that is still in flight,
+  // has issued only the NS stores of chunk i - 1 (for the first chunk: nothing that is still in flight,
   // the rows above were consumed), and operations complete in issue order. After the barrier
   // every wave has also finished reading chunk i - 1, so its slot takes chunk i + 1.
   T *trash = (T *)a.trash;
-  for (int i = 0; i < n_chunks; ++i) {
-    if (i == 0) wait_vm<0>();
+  for (int i = c0; i < c1; ++i) {
+    if (i == c0) wait_vm<0>();
     else wait_vm<NS>();
     wait_lgkm0();
     bare_barrier();
-    if (i + 1 < n_chunks) issue(i + 1);
+    if (i + 1 < c1) issue(i + 1);
     const T *base = lds[i % NB];
     f32x16 acc[TG];
 #pragma unroll
@@ -315,7 +321,8 @@ __global__ __launch_bounds__(QKV_NW * 64, (qkv_wgs_per_cu<T, D>())) void qkv_ker
 }
 
 template <typename T, typename TI, int D, int TG>
-hipError_t launch_dlt(const QkvArgs &a, int grid, hipStream_t s) {
+hipError_t launch_dlt(const QkvArgs &a, int tiles, hipStream_t s) {
+  const int grid = tiles * (a.n_split > 1 ? a.n_split : 1);
   if (a.layer)
     hipLaunchKernelGGL((qkv_kernel<T, TI, D, true, TG>), dim3(grid), dim3(QKV_NW * 64), 0, s, a);
   else
@@ -351,6 +358,8 @@ int qkv_max_groups(int dtype, int d_model) {
 }
 
 int qkv_tokens_per_tile(int tg) { return QKV_NW * 32 * tg; }
+
+int qkv_max_split(int d_model) { return d_model / 32; }   // chunk ranges of at least three chunks
 
 hipError_t launch_qkv(int dtype, int in_f32, const QkvArgs &a, int grid, hipStream_t s) {
   if (grid == 0) return hipSuccess;
