@@ -24,6 +24,32 @@ def test_traffic_record_ignored_after_kernel_change(tmp_path):
 
 
 def test_kernel_classes_match_source_files():
-    for k, (sym, src) in profsummary.KERNELS.items():
+    for k, (syms, src) in profsummary.KERNELS.items():
         assert os.path.exists(os.path.join(profsummary.CSRC, src))
-        assert profsummary.classify("void ot::(anonymous namespace)::" + sym + "<bf16>") == k
+        for sym in syms:
+            assert profsummary.classify("void ot::(anonymous namespace)::" + sym + "<bf16>") == k
+            assert sym in open(os.path.join(profsummary.CSRC, src)).read() or sym == "post_f32w_kernel"
+    assert profsummary.classify("__amd_rocclr_copyBuffer") is None
+
+
+def test_mfma_summary_weights_by_duration(tmp_path):
+    """Duration-weighted MfmaUtil / VALUBusy and executed flops from a counters table laid out as
+    rocprofv3 writes it (one row per dispatch and counter)."""
+    import sqlite3
+    db = os.path.join(tmp_path, "run_results.db")
+    c = sqlite3.connect(db)
+    c.execute("create table counters_collection (dispatch_id int, kernel_name text, counter_name text, "
+              "value real, duration real)")
+    rows = [(1, "attn_kernel<bf16>", "MfmaUtil", 10.0, 100.0), (1, "attn_kernel<bf16>", "VALUBusy", 50.0, 100.0),
+            (1, "attn_kernel<bf16>", "SQ_INSTS_VALU_MFMA_MOPS_BF16", 2.0, 100.0),
+            (2, "attn_split_kernel<bf16>", "MfmaUtil", 40.0, 300.0), (2, "attn_split_kernel<bf16>", "VALUBusy", 10.0, 300.0),
+            (2, "attn_split_kernel<bf16>", "SQ_INSTS_VALU_MFMA_MOPS_BF16", 4.0, 300.0),
+            (3, "qkv_kernel<bf16>", "MfmaUtil", 99.0, 1.0)]
+    c.executemany("insert into counters_collection values (?,?,?,?,?)", rows)
+    c.commit()
+    m = profsummary.mfma_summary(db, "attn")
+    assert m["dispatches"] == 2
+    assert abs(m["MfmaUtil"] - (10 * 100 + 40 * 300) / 400) < 1e-9
+    assert abs(m["VALUBusy"] - (50 * 100 + 10 * 300) / 400) < 1e-9
+    assert m["mfma_flops_per_dispatch"] == 512.0 * 3.0
+    assert profsummary.mfma_summary(db, "post") is None
