@@ -9,7 +9,9 @@ from .onetrans_oracle import (rms_norm, layer_norm, norm, gelu, weight_group, bl
                               forward, forward_batch, prefill_user, score_candidate,
                               append_events, append_recompute, grown_schedule, BlockTrace)
 from .tokenizer_oracle import mlp, s_tokens, s_tokens_by_time, ns_tokens, tokenize, tokenize_batch
+from .onetrans_backward import backward, backward_batch
 
-__all__ = ["mlp", "s_tokens", "s_tokens_by_time", "ns_tokens", "tokenize", "tokenize_batch","rms_norm", "layer_norm", "norm", "gelu", "weight_group", "block_forward", "forward",
+__all__ = ["mlp", "s_tokens", "s_tokens_by_time", "ns_tokens", "tokenize", "tokenize_batch",
+           "rms_norm", "layer_norm", "norm", "gelu", "weight_group", "block_forward", "forward",
            "forward_batch", "prefill_user", "score_candidate", "append_events", "append_recompute",
-           "grown_schedule", "BlockTrace"]
+           "grown_schedule", "BlockTrace", "backward", "backward_batch"]

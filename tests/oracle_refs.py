@@ -51,48 +51,69 @@ def torch_encoder_layer_stack(x0: np.ndarray, weights, m) -> np.ndarray:
     return x[0].numpy()
 
 
-def torch_functional_forward(x0: np.ndarray, weights, m, s_queries) -> np.ndarray:
-    """Mixed-parameter stack written with torch library calls (F.rms_norm / F.layer_norm,
-    F.linear, F.scaled_dot_product_attention with an explicit bottom-right causal mask, F.gelu).
-
-    Row t of a block with s S rows uses parameter set 0 if t < s, else 1 + (t - s).
-    """
-    x = _t(x0)
+def _functional_stack(x, params, m, s_queries):
+    """The mixed-parameter stack in torch over tensors (x [L_S + l_ns][d], params[n][field])."""
     d, H = m.d_model, m.n_heads
     dh = d // H
     s = x.shape[0] - m.l_ns
 
     def nrm(z, g, b):
         if m.norm == "rms":
-            return F.rms_norm(z, (d,), weight=_t(g), eps=m.norm_eps)
-        return F.layer_norm(z, (d,), weight=_t(g), bias=_t(b), eps=m.norm_eps)
+            return F.rms_norm(z, (d,), weight=g, eps=m.norm_eps)
+        return F.layer_norm(z, (d,), weight=g, bias=b, eps=m.norm_eps)
 
     def lin(z, W, rows, b=None):
         out = []
         for i, t in enumerate(rows):
             gi = 0 if t < s else 1 + (t - s)
-            out.append(F.linear(z[i:i + 1], _t(W[gi]), None if b is None else _t(b[gi])))
+            out.append(F.linear(z[i:i + 1], W[gi], None if b is None else b[gi]))
         return torch.cat(out)
 
-    for n, p in enumerate(weights):
+    for n, p in enumerate(params):
         T = x.shape[0]
         q_keep = s_queries[n]
         rows = list(range(T))
         tail = list(range(s - q_keep, T))
-        xh = nrm(x, p.norm1_g, p.norm1_b)
-        k = lin(xh, p.wk, rows)
-        v = lin(xh, p.wv, rows)
-        q = lin(xh[tail], p.wq, tail)
+        xh = nrm(x, p["norm1_g"], p["norm1_b"])
+        k = lin(xh, p["wk"], rows)
+        v = lin(xh, p["wv"], rows)
+        q = lin(xh[tail], p["wq"], tail)
         R = len(tail)
         mask = torch.arange(T)[None, :] <= torch.tensor(tail)[:, None]
         o = F.scaled_dot_product_attention(q.view(R, H, dh).transpose(0, 1), k.view(T, H, dh).transpose(0, 1),
                                            v.view(T, H, dh).transpose(0, 1), attn_mask=mask)
         o = o.transpose(0, 1).reshape(R, d)
-        y = x[tail] + lin(o, p.wo, tail)
-        hid = F.gelu(lin(nrm(y, p.norm2_g, p.norm2_b), p.w1, tail, p.b1), approximate="none")
-        x = y + lin(hid, p.w2, tail, p.b2)
+        y = x[tail] + lin(o, p["wo"], tail)
+        hid = F.gelu(lin(nrm(y, p["norm2_g"], p["norm2_b"]), p["w1"], tail, p["b1"]), approximate="none")
+        x = y + lin(hid, p["w2"], tail, p["b2"])
         s = q_keep
-    return x.numpy()
+    return x
+
+
+_FIELDS = ("norm1_g", "norm1_b", "norm2_g", "norm2_b", "wq", "wk", "wv", "wo", "w1", "b1", "w2", "b2")
+
+
+def torch_functional_forward(x0: np.ndarray, weights, m, s_queries) -> np.ndarray:
+    """Mixed-parameter stack written with torch library calls (F.rms_norm / F.layer_norm,
+    F.linear, F.scaled_dot_product_attention with an explicit bottom-right causal mask, F.gelu).
+
+    Row t of a block with s S rows uses parameter set 0 if t < s, else 1 + (t - s).
+    """
+    params = [{f: _t(getattr(p, f)) for f in _FIELDS} for p in weights]
+    with torch.no_grad():
+        return _functional_stack(_t(x0), params, m, s_queries).numpy()
+
+
+def torch_functional_grads(x0: np.ndarray, weights, m, s_queries, d_out: np.ndarray):
+    """torch.autograd (fp64) gradients of L = sum(d_out * stack(x0)) through the same torch-functional
+    stack: (dL/dx0, [{field: dL/dparam} per block])."""
+    x = _t(x0).requires_grad_(True)
+    params = [{f: _t(getattr(p, f)).requires_grad_(True) for f in _FIELDS} for p in weights]
+    out = _functional_stack(x, params, m, s_queries)
+    (out * _t(d_out)).sum().backward()
+    grads = [{f: (p[f].grad.numpy() if p[f].grad is not None else np.zeros(p[f].shape)) for f in _FIELDS}
+             for p in params]
+    return x.grad.numpy(), grads
 
 
 def gelu_scalar(z: float) -> float:
