@@ -223,6 +223,43 @@ int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weig
                            onetrans_kv_cache *cache, const void *x_new, int n_users, int d_l,
                            void *out_new, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---- Training step (section 7.5.3, closing paragraph: mixed-precision training with activation
+ * recomputation; paper-daily deep reading, section 4.3, system-efficiency table) ---------------
+ *
+ * The gradients of one training step of the block stack over a batch, for a loss whose gradient
+ * with respect to the stack's final rows (the last block's kept rows, q_last + l_ns per sample)
+ * is d_out. The call runs the forward over the batch keeping only each block's input rows (fp32),
+ * then walks the blocks backwards, recomputing each block's internals from its input (activation
+ * recomputation) before its backward: the norms, the mixed Q/K/V/O and FFN products, and the
+ * causal attention with the pyramid's tail queries, with its probabilities recomputed from the
+ * kept per-query log-sum-exp (never stored). Products take storage-dtype operands and accumulate
+ * in fp32; every gradient is accumulated and written in fp32.
+ * Parameter gradients are sums over the batch, kept per weight set: index 0 of a [1 + l_ns][..]
+ * gradient is the shared S set (every S row of every sample), 1 + j is NS token j's own set. */
+typedef struct {          /* one per block, device, fp32, shapes as onetrans_block_weights */
+  float *norm1_g, *norm1_b;        /* [d]; *_b may be NULL (RMSNorm: written as zeros when set) */
+  float *norm2_g, *norm2_b;        /* [d] */
+  float *wq, *wk, *wv, *wo;        /* [1+l_ns][d][d] */
+  float *w1, *b1;                  /* [1+l_ns][d_ff][d], [1+l_ns][d_ff] */
+  float *w2, *b2;                  /* [1+l_ns][d][d_ff], [1+l_ns][d] */
+} onetrans_block_grads;
+
+/* Workspace bytes of onetrans_backward for `batch` samples of l_s S rows (0: invalid config or
+ * schedule). */
+size_t onetrans_backward_workspace_bytes(const onetrans_config *cfg, int batch, int l_s);
+
+/* One training step's gradients (see above).
+ *   x0     [batch][l_s + l_ns][d] storage dtype: X(0)
+ *   d_out  [batch][q_last + l_ns][d] fp32: dL/d(final rows), q_last = s_queries[n_blocks - 1]
+ *   out    [batch][q_last + l_ns][d] fp32 or NULL: the forward's final rows
+ *   dx0    [batch][l_s + l_ns][d] fp32 or NULL: dL/dX(0)
+ *   grads  host [n_blocks]: every gradient buffer is overwritten (not accumulated into)
+ * Runs on `stream` alone. Errors: as onetrans_forward (INVALID_ARG also for a null gradient
+ * pointer other than *_b, ALIGNMENT for a misaligned one). */
+int onetrans_backward(const onetrans_config *cfg, const onetrans_block_weights *blk, const void *x0, int batch,
+                      int l_s, const float *d_out, float *out, float *dx0, const onetrans_block_grads *grads,
+                      void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* ---- Tokenizers ahead of block 1 (section 7.5.0, "Unified Tokenization") -------------------
  *
  * S-tokens: n_seq behaviour sequences (types), given in intent order (highest intent first).
@@ -301,7 +338,12 @@ typedef enum {
   ONETRANS_K_POST = 2,       /* fused W^O + residual + pre-norm 2 + mixed FFN + residual */
   ONETRANS_K_LIN = 3,        /* tokenizer linear layers (grouped MLP layers) */
   ONETRANS_K_MERGE = 4,      /* tokenizer merge: [SEP] rows, or time-order ranks */
-  ONETRANS_K_COUNT = 5
+  ONETRANS_K_BWD_GEMM = 5,   /* training step: recomputed and backward products, weight gradients
+                                (with their split-sum reductions) */
+  ONETRANS_K_BWD_ATTN = 6,   /* training step: attention backward (dK/dV and dQ) */
+  ONETRANS_K_BWD_ROWS = 7,   /* training step: norms and their backward, conversions, column sums,
+                                weight transposes, zero fills */
+  ONETRANS_K_COUNT = 8
 } onetrans_kernel_class;
 
 /* Per-launch device timing (tracing aid). While enabled, the library brackets every kernel launch

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert "onetrans_forward" in names and "onetrans_tokenize" in names and len(names) == 14
+    assert "onetrans_forward" in names and "onetrans_tokenize" in names and len(names) == 16
     lib = L.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -343,3 +343,61 @@ def test_noalloc_score_validation():
     fits = [x <= L.SCRATCH_BYTES for x in need]
     assert fits == sorted(fits, reverse=True)
     assert "scratch" in L.status_string(L.ERR_SCRATCH)
+
+
+def _grads(N, base=0x200000):
+    g = (L.BlockGrads * N)()
+    for i in range(N):
+        for j, f in enumerate(L.WEIGHT_FIELDS):
+            setattr(g[i], f, base + (i * 16 + j) * 4096)
+    return g
+
+
+def _bwd(c, blocks, grads, x0=FAKE, B=2, l_s=120, d_out=FAKE, out=None, dx0=FAKE, ws=FAKE, wsb=1 << 40):
+    return L.lib().onetrans_backward(ctypes.byref(c) if c is not None else None, blocks, x0, B, l_s, d_out, out, dx0,
+                                     grads, ws, wsb, None)
+
+
+def test_backward_validation_errors():
+    """The training step validates like the forward, plus its gradient pointers, before enqueueing anything."""
+    lib = L.lib()
+    c, b, g = _cfg(), _blocks(2), _grads(2)
+    need = lib.onetrans_backward_workspace_bytes(ctypes.byref(c), 2, 120)
+    assert need > 0
+    assert lib.onetrans_backward_workspace_bytes(ctypes.byref(c), 2, 60) == 0      # schedule longer than l_s
+    assert lib.onetrans_backward_workspace_bytes(None, 2, 120) == 0
+    assert _bwd(c, b, g, wsb=need - 1) == L.ERR_WORKSPACE
+    assert _bwd(None, b, g) == L.ERR_INVALID_ARG
+    assert _bwd(c, None, g) == L.ERR_INVALID_ARG
+    assert _bwd(c, b, None) == L.ERR_INVALID_ARG
+    assert _bwd(c, b, g, x0=None) == L.ERR_INVALID_ARG
+    assert _bwd(c, b, g, d_out=None) == L.ERR_INVALID_ARG
+    assert _bwd(c, b, g, ws=None) == L.ERR_INVALID_ARG
+    assert _bwd(c, b, g, d_out=FAKE + 4) == L.ERR_ALIGNMENT
+    assert _bwd(c, b, g, out=FAKE + 4) == L.ERR_ALIGNMENT
+    assert _bwd(c, b, g, dx0=FAKE + 4) == L.ERR_ALIGNMENT
+    assert _bwd(c, b, g, B=0) == L.ERR_SHAPE
+    assert _bwd(c, b, g, l_s=60) == L.ERR_SHAPE
+    assert _bwd(_cfg(d=256, H=4), b, g) == L.ERR_UNSUPPORTED
+    ng = _grads(2)
+    ng[1].wq = None
+    assert _bwd(c, b, ng) == L.ERR_INVALID_ARG
+    ng = _grads(2)
+    ng[0].b1 = FAKE + 8
+    assert _bwd(c, b, ng) == L.ERR_ALIGNMENT
+    ng = _grads(2)
+    ng[0].norm1_b = None                                                            # optional under RMSNorm
+    assert _bwd(c, b, ng, wsb=need - 1) == L.ERR_WORKSPACE
+    # launch sizes: rows x heads beyond 2^31, and feature-major tiles beyond 32-bit offsets
+    assert _bwd(c, b, g, B=1 << 21) == L.ERR_SHAPE
+    assert _bwd(c, b, g, B=1 << 17, wsb=1024) == L.ERR_SHAPE
+    assert _bwd(c, b, g, B=1 << 15, wsb=1024) == L.ERR_WORKSPACE
+
+
+def test_backward_workspace_grows_with_batch():
+    lib = L.lib()
+    c = _cfg()
+    sizes = [lib.onetrans_backward_workspace_bytes(ctypes.byref(c), B, 120) for B in (1, 2, 8, 64)]
+    assert all(a < b for a, b in zip(sizes, sizes[1:]))
+    # the checkpoints alone: block 1's input rows, fp32
+    assert sizes[1] - sizes[0] >= (100 + 16) * 256 * 4

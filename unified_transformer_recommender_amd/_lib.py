@@ -22,7 +22,7 @@ SCRATCH_BYTES = 64 << 20     # ONETRANS_SCRATCH_BYTES
 F32, BF16 = 0, 1
 RMSNORM, LAYERNORM = 0, 1
 OP_FORWARD, OP_PREFILL, OP_SCORE, OP_APPEND = 0, 1, 2, 3
-KERNEL_CLASSES = ("qkv", "attn", "post", "lin", "merge")
+KERNEL_CLASSES = ("qkv", "attn", "post", "lin", "merge", "bwd_gemm", "bwd_attn", "bwd_rows")
 MERGE_INTENT, MERGE_TIME = 0, 1
 
 WEIGHT_FIELDS = ("norm1_g", "norm1_b", "norm2_g", "norm2_b", "wq", "wk", "wv", "wo", "w1", "b1", "w2", "b2")
@@ -34,6 +34,10 @@ class Config(ctypes.Structure):
 
 
 class BlockWeights(ctypes.Structure):
+    _fields_ = [(f, c_void_p) for f in WEIGHT_FIELDS]
+
+
+class BlockGrads(ctypes.Structure):
     _fields_ = [(f, c_void_p) for f in WEIGHT_FIELDS]
 
 
@@ -72,6 +76,9 @@ SIGNATURES = {
     "onetrans_tokenize": (c_int, [POINTER(Config), POINTER(TokenizerConfig), POINTER(MlpWeights), c_void_p,
                                   POINTER(MlpWeights), POINTER(c_void_p), POINTER(c_void_p), c_void_p, c_int,
                                   c_void_p, c_void_p, c_size_t, c_void_p]),
+    "onetrans_backward_workspace_bytes": (c_size_t, [POINTER(Config), c_int, c_int]),
+    "onetrans_backward": (c_int, [POINTER(Config), POINTER(BlockWeights), c_void_p, c_int, c_int, c_void_p,
+                                  c_void_p, c_void_p, POINTER(BlockGrads), c_void_p, c_size_t, c_void_p]),
     "onetrans_set_streams": (c_int, [c_int]),
     "onetrans_timing_enable": (c_int, [c_int]),
     "onetrans_timing_read": (c_int, [POINTER(ctypes.c_double), POINTER(ctypes.c_longlong)]),

@@ -168,6 +168,45 @@ def onetrans_forward(model: Model, x0: torch.Tensor, out: Optional[torch.Tensor]
     return out
 
 
+def weight_shapes(model: Model) -> dict:
+    """Shape of every per-block parameter (and of its fp32 gradient)."""
+    d, f, G = model.d_model, model.d_ff, 1 + model.l_ns
+    return {"norm1_g": (d,), "norm1_b": (d,), "norm2_g": (d,), "norm2_b": (d,), "wq": (G, d, d), "wk": (G, d, d),
+            "wv": (G, d, d), "wo": (G, d, d), "w1": (G, f, d), "b1": (G, f), "w2": (G, d, f), "b2": (G, d)}
+
+
+def onetrans_backward(model: Model, x0: torch.Tensor, d_out: torch.Tensor, want_out: bool = False,
+                      want_dx0: bool = True, grads=None, ws: Optional[torch.Tensor] = None, stream=None):
+    """One training step's gradients: x0 [B][L_S + l_ns][d] (storage dtype) and d_out [B][q_last + l_ns][d]
+    fp32 -> (out or None, dx0 or None, grads), grads a list (one per block) of {field: fp32 tensor}
+    summed over the batch. `grads` may be given (that structure, preallocated) to be overwritten."""
+    _check_input(model, x0, 3, "x0")
+    B, T, d = x0.shape
+    l_s = T - model.l_ns
+    R = model.s_queries[-1] + model.l_ns
+    if d_out.dtype != torch.float32 or not d_out.is_contiguous() or tuple(d_out.shape) != (B, R, d):
+        raise ValueError("d_out: need a contiguous fp32 tensor [B][q_last + l_ns][d]")
+    dev = x0.device
+    out = torch.empty((B, R, d), dtype=torch.float32, device=dev) if want_out else None
+    dx0 = torch.empty((B, T, d), dtype=torch.float32, device=dev) if want_dx0 else None
+    if grads is None:
+        grads = [{f: torch.empty(s, dtype=torch.float32, device=dev) for f, s in weight_shapes(model).items()}
+                 for _ in range(model.n_blocks)]
+    gs = (L.BlockGrads * model.n_blocks)()
+    for i, g in enumerate(grads):
+        for f in L.WEIGHT_FIELDS:
+            setattr(gs[i], f, _ptr(g.get(f)))
+    if ws is None:
+        n = int(L.lib().onetrans_backward_workspace_bytes(ctypes.byref(model.cfg), B, l_s))
+        if n == 0:
+            raise ValueError("invalid configuration for a backward workspace")
+        ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    st = L.lib().onetrans_backward(ctypes.byref(model.cfg), model.blocks, x0.data_ptr(), B, l_s, d_out.data_ptr(),
+                                   _ptr(out), _ptr(dx0), gs, ws.data_ptr(), ws.numel(), _stream(dev, stream))
+    L.check(st, "onetrans_backward")
+    return out, dx0, grads
+
+
 def onetrans_prefill_user(model: Model, x_s: torch.Tensor, cache: KVCache, out_s: Optional[torch.Tensor] = None,
                           ws: Optional[torch.Tensor] = None, stream=None) -> Optional[torch.Tensor]:
     """Stage I: x_s [U][L_S][d] -> cache K/V per block (and optionally out_s [U][q_last][d] fp32)."""

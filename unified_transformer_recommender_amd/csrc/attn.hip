@@ -306,6 +306,7 @@ __global__ __launch_bounds__(ATTN_WAVES * 64) void attn_kernel(const AttnArgs a)
   // ---- normalise and store O[b][i][h*dh + c] through the wave's LDS staging tile ---------------
   const float lt = st.lsum + other_half(st.lsum);
   const float inv = valid ? 1.0f / lt : 0.0f;
+  if (a.lse && valid && g == 0) a.lse[((long long)z * H + h) * a.R + qi] = st.m + log2f(lt);
   f32x16 o = st.o;
 #pragma unroll
   for (int v = 0; v < 16; ++v) o[v] *= inv;
@@ -496,6 +497,7 @@ __global__ __launch_bounds__(ATTN_WAVES * 64) void attn_split_kernel(const AttnA
     for (int v = 0; v < 16; ++v) o[v] += sc * s_o[w][v][lane];
   }
   const float inv = valid ? 1.0f / l : 0.0f;
+  if (a.lse && valid && g == 0) a.lse[((long long)z * a.n_heads + h) * a.R + qi] = mx + log2f(l);
 #pragma unroll
   for (int v = 0; v < 16; ++v) o[v] *= inv;
   TS::put(stage, o, lc, g);

@@ -307,6 +307,8 @@ struct AttnArgs {
   void *o; long long o_sb;
   const int *seq_shift;    // [n_seq_grp] or null: sequence z's query positions and prefix keys
                            // start seq_shift[z] rows later (ragged cached lengths)
+  float *lse;              // or null: base-2 log-sum-exp of each query's scores (log2(e) S, the
+                           // softmax's log normaliser), at lse[(z * n_heads + h) * R + i]
 };
 
 // ---------------------------------------------------------------------------------------------

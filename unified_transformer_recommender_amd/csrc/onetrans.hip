@@ -23,6 +23,7 @@
 #include "onetrans.h"
 #include "common.hpp"
 #include "launch.hpp"
+#include "bwd.hpp"
 
 using namespace ot;
 
@@ -232,6 +233,8 @@ struct Step {
   const int *kv_shift; // device [n_seq] or null: K/V rows of sequence b go kv_shift[b] rows later
   const int *seq_shift;   // device [n_grp] or null: attention positions / prefix keys of sequence
                           // (or user) z start seq_shift[z] rows later
+  float *lse;             // or null: per-query base-2 log-sum-exp of the attention scores
+  bool no_post;           // stop after the attention (the training step's recomputation)
 };
 
 int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, char *ws, const Ws &L,
@@ -322,6 +325,7 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
     a.o = ob;
     a.o_sb = (long long)R * d;
     a.seq_shift = st.seq_shift;
+    a.lse = st.lse;
     if (st.stage2) {
       a.n_seq_grp = st.n_grp;
       a.n_cand = st.n_cand;
@@ -338,6 +342,7 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
     if (timed(ONETRANS_K_ATTN, stream, [&] { return launch_attn(D.dt, dh, st.stage2, a, stream); }) != hipSuccess)
       return ONETRANS_ERR_HIP;
   }
+  if (st.no_post) return ONETRANS_OK;
 
   // W^O + residual + norm2 + mixed FFN + residual, fused, over the query rows:
   // tail S rows use parameter set 0, NS token j uses set 1 + j
@@ -854,6 +859,629 @@ int first_pruning_block(const int *q, int N, int l_s) {
   return -1;
 }
 
+
+// ---- training step (fun-rec-mdbook 7.5.3, closing paragraph: mixed precision with activation
+// recomputation) ----------------------------------------------------------------------------------
+//
+// Forward over the batch keeping only each block's input rows (fp32 checkpoints), then per block,
+// last to first, with s S rows in, q kept, T = s + l_ns rows, R = q + l_ns query rows, p0 = s - q:
+//   recompute  xh^T = Norm1(X) (feature-major), Q/K/V and O with each query's log-sum-exp (the
+//              forward's QKV and attention kernels), Y = X[tail] + O Wo^T, yh = Norm2(Y),
+//              hpre = yh W1^T + b1 and hid^T = GELU(hpre)
+//   backward   dhpre = (dOut W2) * GELU'(hpre); dW2 += dOut^T hid, db2 += dOut; dW1 += dhpre^T yh,
+//              db1 += dhpre; dYh = dhpre W1; dY = Norm2'(dYh) + dOut; dO = dY Wo; dWo += dY^T O;
+//              attention backward -> dK, dV, dQ; dWq/k/v += d{Q,K,V}^T Xh;
+//              dXh = dK Wk + dV Wv + dQ Wq; dX = Norm1'(dXh) + dY on the tail rows
+// Every mixed product runs as an S-rows job (set 0) and an NS job (set 1 + j for NS token j). Weight
+// gradients are contractions over tokens of feature-major copies (tokens of a set contiguous).
+
+inline long long pad64(long long n) { return (n + 63) / 64 * 64; }
+
+// Element (b, t) of a row buffer at base + (b * sb + (t - t_off) * rs) * esz bytes.
+struct RowBuf {
+  char *base;
+  size_t esz;
+  long long sb;
+  int rs, t_off;
+};
+inline Mat2 rows_S(const RowBuf &r, int t0, int cnt) {
+  return Mat2{r.base + (long long)(t0 - r.t_off) * r.rs * (long long)r.esz, 0, r.sb, cnt, r.rs};
+}
+inline Mat2 rows_N(const RowBuf &r, int s) {
+  return Mat2{r.base + (long long)(s - r.t_off) * r.rs * (long long)r.esz, r.rs, r.sb, 1, 0};
+}
+inline RowView view(const RowBuf &r) { return RowView{r.base, r.sb, r.t_off, r.rs}; }
+
+// Row n of weight set w at base + (w * set + n * rs) * esz bytes.
+struct WBuf {
+  const char *base;
+  size_t esz;
+  long long set;
+  int rs;
+};
+inline Mat2 w_set(const WBuf &w, int set0) { return Mat2{w.base + set0 * w.set * (long long)w.esz, w.set, 0, 0x7fffffff, w.rs}; }
+
+// Feature-major copy of F features: S tokens at S + f * ldS + token, NS token j at N + (j F + f) ldN + b.
+struct FeatBuf {
+  char *S, *N;
+  long long ldS, ldN;
+  int F;
+};
+inline MatT featT_S(const FeatBuf &f) { return MatT{f.S, 0, f.ldS}; }
+inline MatT featT_N(const FeatBuf &f) { return MatT{f.N, (long long)f.F * f.ldN, f.ldN}; }
+inline Mat2 feat_S(const FeatBuf &f) { return Mat2{f.S, 0, 0, 0x7fffffff, (int)f.ldS}; }
+inline Mat2 feat_N(const FeatBuf &f) { return Mat2{f.N, (long long)f.F * f.ldN, 0, 0x7fffffff, (int)f.ldN}; }
+
+struct GemmPlan {
+  GemmArgs a;
+  long long tiles;
+  long long part_elems;   // PARTIAL jobs: fp32 partial elements (splits included)
+  long long rsum_elems;
+};
+inline void plan_init(GemmPlan &P) {
+  memset(&P.a, 0, sizeof(P.a));
+  P.tiles = P.part_elems = P.rsum_elems = 0;
+}
+inline void plan_add(GemmPlan &P, GemmJob j) {
+  if (j.m <= 0 || j.n_groups <= 0) return;
+  j.m_tiles = (j.m + gemm_tokens_per_tile() - 1) / gemm_tokens_per_tile();
+  j.n_tiles = j.n_feat / gemm_features_per_tile();
+  j.tile0 = (int)P.tiles;
+  P.tiles += (long long)j.n_split * j.n_groups * j.m_tiles * j.n_tiles;
+  P.a.job[P.a.n_jobs++] = j;
+}
+
+// Split of a weight-gradient contraction over `chunks` 128-byte chunks per row: enough workgroups
+// for the GPU (about 1024 per job), at least 8 chunks per split.
+inline int wgrad_split(long long chunks, long long tiles) {
+  long long s = (1024 + tiles - 1) / tiles;
+  s = std::min(s, chunks / 8);
+  return (int)std::max(1LL, std::min(s, 256LL));
+}
+
+// dW[set][m][n] (+ row sums) = sum over the set's tokens of A^T B, for the S set (one group) and
+// the NS sets (l_ns groups); partials and row-sum partials at running offsets of part / rsum.
+struct WgradOut {
+  float *w, *b;   // gradient destinations (set 0 first), b may be null
+};
+void wgrad_jobs(GemmPlan &P, RedArgs *R, const Dims &D, const FeatBuf &A, const FeatBuf &Bf, long long tokS,
+                int B, WgradOut dst, float *part, float *rsum) {
+  const int m = A.F, n = Bf.F;
+  const int kc = (int)(128 / D.esz);
+  for (int ns = 0; ns < 2; ++ns) {
+    const int groups = ns ? D.lns : 1;
+    if (groups == 0 || (ns ? B : tokS) == 0) continue;
+    GemmJob j;
+    memset(&j, 0, sizeof(j));
+    j.a = ns ? feat_N(A) : feat_S(A);
+    j.b = ns ? feat_N(Bf) : feat_S(Bf);
+    j.m = m;
+    j.n_feat = n;
+    j.k_len = (int)(ns ? A.ldN : A.ldS);
+    j.n_groups = groups;
+    const long long base_tiles = (long long)groups * ((m + 127) / 128) * (n / 64);
+    j.n_split = wgrad_split(j.k_len / kc, base_tiles);
+    j.epi = EPI_PARTIAL;
+    j.out = Mat2{part ? part + P.part_elems : nullptr, (long long)m * n, 0, 0x7fffffff, n};
+    j.part_split = (long long)groups * m * n;
+    if (dst.b) {
+      j.rowsum = rsum ? rsum + P.rsum_elems : nullptr;
+      j.rowsum_split = (long long)groups * m;
+    }
+    const long long pe = (long long)j.n_split * groups * m * n, re = dst.b ? (long long)j.n_split * groups * m : 0;
+    if (R && part) {
+      RedJob &r = R->job[R->n_jobs++];
+      r.src = part + P.part_elems;
+      r.split = j.part_split;
+      r.n_split = j.n_split;
+      r.dst = dst.w + (ns ? (long long)m * n : 0);
+      r.count = (long long)groups * m * n;
+      r.start = R->total;
+      R->total += (r.count + 3) / 4 * 4;
+      if (dst.b) {
+        RedJob &rb = R->job[R->n_jobs++];
+        rb.src = rsum + P.rsum_elems;
+        rb.split = j.rowsum_split;
+        rb.n_split = j.n_split;
+        rb.dst = dst.b + (ns ? m : 0);
+        rb.count = (long long)groups * m;
+        rb.start = R->total;
+        R->total += (rb.count + 3) / 4 * 4;
+      }
+    }
+    P.part_elems += (pe + 63) / 64 * 64;
+    P.rsum_elems += (re + 63) / 64 * 64;
+    plan_add(P, j);
+  }
+}
+
+struct TrainWs {
+  Ws fw;                      // the forward kernels' buffers (q, k, v, o, trash)
+  std::vector<size_t> ckpt;   // [N]: block n's input rows (n >= 1), fp32 [B][T_n][d]
+  size_t lse, dvec, y, yh, hpre, dhpre, dyh, dy32, dyt, dout_t, d_o, dqkv, dxh, dx32;
+  size_t xhT, dkT, dvT, dqT, oT, dyT, yhT, dhpreT, hidT, doutT;
+  size_t woT, w1T, w2T, wcT;
+  size_t part, rsum, colpart;
+  long long ldS_all, ldS_tail, ldN;   // block-0 (largest) feature-major row lengths
+  size_t total;
+};
+
+// S rows of block n (s_n) and the schedule's kept rows.
+inline int block_s(const onetrans_config *cfg, int l_s, int n) { return n == 0 ? l_s : cfg->s_queries[n - 1]; }
+
+TrainWs train_layout(const Dims &D, const onetrans_config *cfg, int B, int l_s) {
+  TrainWs w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += al(bytes);
+    return o;
+  };
+  const size_t d = D.d, es = D.esz, L = D.lns, dff = D.dff, G = 1 + L;
+  const size_t T0 = (size_t)l_s + L, R0 = (size_t)cfg->s_queries[0] + L;
+  const size_t rowsT = (size_t)B * T0, rowsR = (size_t)B * R0;
+  w.fw = Ws{};
+  w.fw.q = take(rowsR * d * es);
+  w.fw.k = take(rowsT * d * es);
+  w.fw.v = take(rowsT * d * es);
+  w.fw.o = take(rowsR * d * es);
+  w.fw.trash = take(16);
+  w.fw.part_rows = 0;
+  w.ckpt.assign(D.N, 0);
+  for (int n = 1; n < D.N; ++n) w.ckpt[n] = take((size_t)B * (block_s(cfg, l_s, n) + L) * d * 4);
+  w.lse = take(rowsR * D.H * 4);
+  w.dvec = take(rowsR * D.H * 4);
+  w.y = take(rowsR * d * 4);
+  w.yh = take(rowsR * d * es);
+  w.hpre = take(rowsR * dff * es);
+  w.dhpre = take(rowsR * dff * es);
+  w.dyh = take(rowsR * d * 4);
+  w.dy32 = take(rowsR * d * 4);
+  w.dyt = take(rowsR * d * es);
+  w.dout_t = take(rowsR * d * es);
+  w.d_o = take(rowsR * d * es);
+  w.dqkv = take(rowsT * 3 * d * es);
+  w.dxh = take(rowsT * d * 4);
+  w.dx32 = take((D.N > 1 ? rowsR : 0) * d * 4);
+  w.ldS_all = pad64((long long)B * l_s);
+  w.ldS_tail = pad64((long long)B * cfg->s_queries[0]);
+  w.ldN = pad64(B);
+  auto feat = [&](size_t F, long long ldS) { return take(F * (size_t)ldS * es + L * F * (size_t)w.ldN * es); };
+  w.xhT = feat(d, w.ldS_all);
+  w.dkT = feat(d, w.ldS_all);
+  w.dvT = feat(d, w.ldS_all);
+  w.dqT = feat(d, w.ldS_all);
+  w.oT = feat(d, w.ldS_tail);
+  w.dyT = feat(d, w.ldS_tail);
+  w.yhT = feat(d, w.ldS_tail);
+  w.doutT = feat(d, w.ldS_tail);
+  w.dhpreT = feat(dff, w.ldS_tail);
+  w.hidT = feat(dff, w.ldS_tail);
+  w.woT = take(G * d * d * es);
+  w.w1T = take(G * d * dff * es);
+  w.w2T = take(G * dff * d * es);
+  w.wcT = take(G * d * 3 * d * es);
+  // the weight-gradient launches' partials and the norms' column partials: the largest block
+  long long part = 0, rsum = 0, tiles32 = 0;
+  for (int n = 0; n < D.N; ++n) {
+    const int s = block_s(cfg, l_s, n), q = cfg->s_queries[n];
+    const long long ldA = pad64((long long)B * s), ldQ = pad64((long long)B * q);
+    FeatBuf fd{nullptr, nullptr, ldA, w.ldN, D.d}, fq{nullptr, nullptr, ldQ, w.ldN, D.d},
+        ff{nullptr, nullptr, ldQ, w.ldN, D.dff};
+    GemmPlan P1, P2;
+    plan_init(P1);
+    plan_init(P2);
+    float dummy;
+    wgrad_jobs(P1, nullptr, D, fq, ff, (long long)B * q, B, WgradOut{&dummy, &dummy}, nullptr, nullptr);   // dW2
+    wgrad_jobs(P1, nullptr, D, ff, fq, (long long)B * q, B, WgradOut{&dummy, &dummy}, nullptr, nullptr);   // dW1
+    for (int i = 0; i < 3; ++i)
+      wgrad_jobs(P2, nullptr, D, fd, fd, (long long)B * s, B, WgradOut{&dummy, nullptr}, nullptr, nullptr);
+    wgrad_jobs(P2, nullptr, D, fq, fq, (long long)B * q, B, WgradOut{&dummy, nullptr}, nullptr, nullptr);   // dWo
+    part = std::max({part, P1.part_elems, P2.part_elems});
+    rsum = std::max({rsum, P1.rsum_elems, P2.rsum_elems});
+    const long long t32 = ((long long)B * s + 31) / 32 + (long long)L * ((B + 31) / 32);
+    tiles32 = std::max(tiles32, t32);
+  }
+  w.part = take((size_t)part * 4);
+  w.rsum = take((size_t)rsum * 4);
+  w.colpart = take((size_t)tiles32 * 2 * d * 4);
+  w.total = off;
+  return w;
+}
+
+int check_grads(const onetrans_block_grads *g, const Dims &D) {
+  if (!g) return ONETRANS_ERR_INVALID_ARG;
+  for (int n = 0; n < D.N; ++n) {
+    const float *req[] = {g[n].norm1_g, g[n].norm2_g, g[n].wq, g[n].wk, g[n].wv, g[n].wo, g[n].w1, g[n].b1, g[n].w2, g[n].b2};
+    for (const float *p : req) {
+      if (!p) return ONETRANS_ERR_INVALID_ARG;
+      if (misaligned(p)) return ONETRANS_ERR_ALIGNMENT;
+    }
+    if (misaligned(g[n].norm1_b) || misaligned(g[n].norm2_b)) return ONETRANS_ERR_ALIGNMENT;
+  }
+  return ONETRANS_OK;
+}
+
+int train_run(const Dims &D, const onetrans_config *cfg, const onetrans_block_weights *blk, const void *x0, int B,
+              int l_s, const float *d_out, float *out, float *dx0, const onetrans_block_grads *grads, char *w,
+              const TrainWs &W, hipStream_t stream) {
+  int rc;
+  const int d = D.d, H = D.H, dh = D.dh, L = D.lns, dff = D.dff, N = D.N;
+  const size_t es = D.esz;
+  const int dt = D.dt;
+  auto hip_ok = [](hipError_t e) { return e == hipSuccess; };
+
+  // ---- forward, keeping block inputs ------------------------------------------------------------
+  auto input_of = [&](int n, RowView &x, int &x_f32) {
+    const int T = block_s(cfg, l_s, n) + L;
+    if (n == 0) {
+      x = RowView{const_cast<void *>(x0), (long long)(l_s + L) * d, 0, d};
+      x_f32 = dt == ONETRANS_F32;
+    } else {
+      x = RowView{w + W.ckpt[n], (long long)T * d, 0, d};
+      x_f32 = 1;
+    }
+  };
+  auto step_for = [&](int n, bool post) {
+    const int s = block_s(cfg, l_s, n), q = cfg->s_queries[n];
+    const int T = s + L, R = q + L, p0 = s - q;
+    Step st{};
+    st.n_seq = B;
+    st.s = s;
+    st.q = q;
+    st.kv_t0 = 0;
+    st.kv_n = s;
+    st.ns = L;
+    st.in_t0 = 0;
+    st.in_n = T;
+    input_of(n, st.x, st.x_f32);
+    st.kS = HeadView{w + W.fw.k, (long long)H * T * dh, (long long)T * dh, 0};
+    st.vS = HeadView{w + W.fw.v, (long long)H * T * dh, (long long)T * dh, 0};
+    st.kN = st.kS;
+    st.vN = st.vS;
+    st.n_pre = T;
+    st.kp = w + W.fw.k;
+    st.vp = w + W.fw.v;
+    st.pre_sb = (long long)H * T * dh;
+    st.pre_sh = (long long)T * dh;
+    st.need_out = true;
+    st.no_post = !post;
+    if (post) st.out = RowView{n + 1 == N ? (void *)out : (void *)(w + W.ckpt[n + 1]), (long long)R * d, p0, d};
+    else st.lse = (float *)(w + W.lse);
+    return st;
+  };
+  for (int n = 0; n < N; ++n) {
+    if (n + 1 == N && !out) break;   // the last block's output is not needed for the gradients
+    const Step st = step_for(n, true);
+    if ((rc = run_step(D, blk[n], st, w, W.fw, stream))) return rc;
+  }
+
+  // ---- backward -----------------------------------------------------------------------------------
+  auto tm = [&](int cls, auto &&launch) { return hip_ok(timed(cls, stream, launch)); };
+  for (int n = N - 1; n >= 0; --n) {
+    const onetrans_block_weights &wt = blk[n];
+    const onetrans_block_grads &gr = grads[n];
+    const int s = block_s(cfg, l_s, n), q = cfg->s_queries[n];
+    const int T = s + L, R = q + L, p0 = s - q;
+    const long long ldA = pad64((long long)B * s), ldQ = pad64((long long)B * q), ldN = W.ldN;
+    RowView xv;
+    int x_f32;
+    input_of(n, xv, x_f32);
+    const RowBuf X{(char *)xv.base, x_f32 ? 4u : es, xv.sb, d, 0};
+    // block-local buffers: tail rows [B][R][*] at positions p0.., all rows [B][T][*]
+    auto tail = [&](size_t off, size_t esz, int width) { return RowBuf{w + off, esz, (long long)R * width, width, p0}; };
+    const RowBuf Ob = tail(W.fw.o, es, d), Yb = tail(W.y, 4, d), YHb = tail(W.yh, es, d), HPb = tail(W.hpre, es, dff),
+                 DHPb = tail(W.dhpre, es, dff), DYHb = tail(W.dyh, 4, d), DY32 = tail(W.dy32, 4, d),
+                 DYt = tail(W.dyt, es, d), DOt = tail(W.dout_t, es, d), DOb = tail(W.d_o, es, d);
+    const RowBuf DOUT32 = n == N - 1 ? RowBuf{(char *)d_out, 4, (long long)R * d, d, p0} : tail(W.dx32, 4, d);
+    const RowBuf DQKV{w + W.dqkv, es, (long long)T * 3 * d, 3 * d, 0}, DXH{w + W.dxh, 4, (long long)T * d, d, 0};
+    auto fb = [&](size_t off, int F, long long ldS_max, long long ldS) {
+      return FeatBuf{w + off, w + off + (size_t)F * ldS_max * es, ldS, ldN, F};
+    };
+    const FeatBuf xhT = fb(W.xhT, d, W.ldS_all, ldA), dkT = fb(W.dkT, d, W.ldS_all, ldA),
+                  dvT = fb(W.dvT, d, W.ldS_all, ldA), dqT = fb(W.dqT, d, W.ldS_all, ldA),
+                  oT = fb(W.oT, d, W.ldS_tail, ldQ), dyT = fb(W.dyT, d, W.ldS_tail, ldQ),
+                  yhT = fb(W.yhT, d, W.ldS_tail, ldQ), doutT = fb(W.doutT, d, W.ldS_tail, ldQ),
+                  dhpT = fb(W.dhpreT, dff, W.ldS_tail, ldQ), hidT = fb(W.hidT, dff, W.ldS_tail, ldQ);
+    // the next lower block's d_out^T: this block's all-rows layout
+    const FeatBuf doutT_next = fb(W.doutT, d, W.ldS_tail, ldA);
+
+    // zero the padding columns of this block's feature-major buffers, and dQ of the rows before p0
+    {
+      FillArgs fa;
+      memset(&fa, 0, sizeof(fa));
+      bool full = false;
+      auto add = [&](void *base, long long g, long long ld, int groups, int rows, long long c0, long long c1) {
+        if (c1 <= c0 || rows == 0 || groups == 0) return;
+        if (fa.n_jobs == FILL_MAX_JOBS) {
+          full = true;
+          return;
+        }
+        FillJob &j = fa.job[fa.n_jobs++];
+        j = FillJob{base, g, ld, groups, rows, (int)c0, (int)c1, (int)es, fa.total};
+        fa.total += (long long)groups * rows * (c1 - c0);
+      };
+      auto pads = [&](const FeatBuf &f, long long tok) {
+        add(f.S, 0, f.ldS, 1, f.F, tok, f.ldS);
+        add(f.N, (long long)f.F * f.ldN, f.ldN, L, f.F, B, f.ldN);
+      };
+      pads(xhT, (long long)B * s);
+      pads(dkT, (long long)B * s);
+      pads(dvT, (long long)B * s);
+      pads(dqT, (long long)B * s);
+      for (const FeatBuf *f : {&oT, &dyT, &yhT, &doutT, &dhpT, &hidT}) pads(*f, (long long)B * q);
+      // dQ of the rows that issue no query: dqkv columns [2d, 3d) and the S part of dQ^T
+      add(w + W.dqkv, (long long)T * 3 * d, 3 * d, B, p0, 2 * d, 3 * d);
+      add(dqT.S, dqT.ldS, s, d, B, 0, p0);
+      if (full) return ONETRANS_ERR_SHAPE;   // (not reached: 22 regions at most)
+      if (!tm(ONETRANS_K_BWD_ROWS, [&] { return launch_fill(fa, stream); })) return ONETRANS_ERR_HIP;
+    }
+    // transposed weights: Wo^T, W1^T, W2^T and [Wk^T | Wv^T | Wq^T]
+    {
+      TrArgs ta;
+      memset(&ta, 0, sizeof(ta));
+      int tiles = 0;
+      const int G = 1 + L;
+      auto add = [&](const void *src, size_t dst_off, int rows, int cols, int dst_ld, int dst_off_col) {
+        TrJob &j = ta.job[ta.n_jobs++];
+        j = TrJob{src, w + dst_off, rows, cols, G, (long long)rows * cols, (long long)cols * dst_ld, dst_ld, dst_off_col, tiles};
+        tiles += G * ((rows + 31) / 32) * ((cols + 31) / 32);
+      };
+      add(wt.wo, W.woT, d, d, d, 0);
+      add(wt.w1, W.w1T, dff, d, dff, 0);
+      add(wt.w2, W.w2T, d, dff, d, 0);
+      add(wt.wk, W.wcT, d, d, 3 * d, 0);
+      add(wt.wv, W.wcT, d, d, 3 * d, d);
+      add(wt.wq, W.wcT, d, d, 3 * d, 2 * d);
+      if (!tm(ONETRANS_K_BWD_ROWS, [&] { return launch_transpose(dt, ta, tiles, stream); })) return ONETRANS_ERR_HIP;
+    }
+    const WBuf Wo{(const char *)wt.wo, es, (long long)d * d, d}, W1{(const char *)wt.w1, es, (long long)dff * d, d},
+        WoT{w + W.woT, es, (long long)d * d, d}, W1T{w + W.w1T, es, (long long)d * dff, dff},
+        W2T{w + W.w2T, es, (long long)dff * d, d}, WcT{w + W.wcT, es, (long long)d * 3 * d, 3 * d};
+
+    // rows launch over the S rows [t0, t0 + cnt) and the NS rows of every sample
+    auto rows_launch = [&](RowsArgs ra, int t0, int cnt, const FeatBuf *outT) {
+      long long tiles = 0;
+      ra.n_jobs = 0;
+      auto add = [&](RowSet rs, void *ot, long long g, long long ld) {
+        const long long m = (long long)rs.n_seq * rs.rows;
+        if (m == 0 || rs.n_groups == 0) return;
+        RowsJob &j = ra.job[ra.n_jobs++];
+        j.rs = rs;
+        j.m_tiles = (int)((m + 31) / 32);
+        j.tile0 = (int)tiles;
+        j.outT = ot;
+        j.tr_g = g;
+        j.tr_ld = ld;
+        tiles += (long long)j.m_tiles * rs.n_groups;
+      };
+      add(RowSet{B, cnt, 1, t0, 0, 0}, outT ? outT->S : nullptr, 0, outT ? outT->ldS : 0);
+      add(RowSet{B, 1, L, s, 1, 1}, outT ? outT->N : nullptr, outT ? (long long)outT->F * outT->ldN : 0, outT ? outT->ldN : 0);
+      ra.d = d;
+      ra.layer = D.layer;
+      ra.eps = D.eps;
+      ra.n_heads = H;
+      if (!tm(ONETRANS_K_BWD_ROWS, [&] { return launch_rows(dt, ra, (int)tiles, stream); })) return -1LL;
+      return tiles;
+    };
+    // mixed product over the S rows [t0, t0 + cnt) (set 0) and the NS rows (sets 1..l_ns)
+    auto act_gemm = [&](const RowBuf &A, const WBuf &Wb, int n_feat, int k_len, int t0, int cnt, int epi,
+                        const void *bias, const RowBuf *resid, const RowBuf *aux, const RowBuf *outb, bool out_f32,
+                        const FeatBuf *outT) {
+      GemmPlan P;
+      plan_init(P);
+      for (int ns = 0; ns < 2; ++ns) {
+        GemmJob j;
+        memset(&j, 0, sizeof(j));
+        j.a = ns ? rows_N(A, s) : rows_S(A, t0, cnt);
+        j.b = w_set(Wb, ns);
+        j.m = ns ? B : B * cnt;
+        j.n_feat = n_feat;
+        j.k_len = k_len;
+        j.n_groups = ns ? L : 1;
+        j.n_split = 1;
+        j.epi = epi;
+        if (bias) {
+          j.bias = (const char *)bias + (ns ? (long long)n_feat * es : 0);
+          j.bias_g = n_feat;
+        }
+        if (resid) {
+          j.resid = ns ? rows_N(*resid, s) : rows_S(*resid, t0, cnt);
+          j.resid_f32 = resid->esz == 4;
+        }
+        if (aux) j.aux = ns ? rows_N(*aux, s) : rows_S(*aux, t0, cnt);
+        if (outb) {
+          j.out = ns ? rows_N(*outb, s) : rows_S(*outb, t0, cnt);
+          j.out_f32 = out_f32;
+        }
+        if (outT) j.outT = ns ? featT_N(*outT) : featT_S(*outT);
+        plan_add(P, j);
+      }
+      return tm(ONETRANS_K_BWD_GEMM, [&] { return launch_gemm(dt, P.a, (int)P.tiles, stream); });
+    };
+
+    // ---- recompute ----
+    {   // xh^T = Norm1(X) over all rows
+      RowsArgs ra;
+      memset(&ra, 0, sizeof(ra));
+      ra.mode = ROWS_NORM_FWD;
+      ra.x = view(X);
+      ra.x_f32 = x_f32;
+      ra.gamma = wt.norm1_g;
+      ra.beta = wt.norm1_b;
+      if (rows_launch(ra, 0, s, &xhT) < 0) return ONETRANS_ERR_HIP;
+    }
+    {   // Q/K/V and O (with the log-sum-exp) by the forward's kernels
+      const Step st = step_for(n, false);
+      if ((rc = run_step(D, wt, st, w, W.fw, stream))) return rc;
+    }
+    // Y = X[tail] + O Wo^T (fp32)
+    if (!act_gemm(Ob, Wo, d, d, p0, q, EPI_STORE, nullptr, &X, nullptr, &Yb, true, nullptr)) return ONETRANS_ERR_HIP;
+    {   // yh = Norm2(Y): rows and feature-major
+      RowsArgs ra;
+      memset(&ra, 0, sizeof(ra));
+      ra.mode = ROWS_NORM_FWD;
+      ra.x = view(Yb);
+      ra.x_f32 = 1;
+      ra.gamma = wt.norm2_g;
+      ra.beta = wt.norm2_b;
+      ra.out_t = view(YHb);
+      if (rows_launch(ra, p0, q, &yhT) < 0) return ONETRANS_ERR_HIP;
+    }
+    // hpre = yh W1^T + b1 (rows), hid^T = GELU(hpre) (feature-major)
+    if (!act_gemm(YHb, W1, dff, d, p0, q, EPI_GELU, wt.b1, nullptr, nullptr, &HPb, false, &hidT)) return ONETRANS_ERR_HIP;
+
+    // ---- backward ----
+    if (n == N - 1) {   // the caller's d_out: storage-dtype rows and feature-major copy
+      RowsArgs ra;
+      memset(&ra, 0, sizeof(ra));
+      ra.mode = ROWS_CONVERT;
+      ra.x = view(DOUT32);
+      ra.x_f32 = 1;
+      ra.out_t = view(DOt);
+      if (rows_launch(ra, p0, q, &doutT) < 0) return ONETRANS_ERR_HIP;
+    }
+    // dhpre = (dOut W2) * GELU'(hpre): rows and feature-major
+    if (!act_gemm(DOt, W2T, dff, d, p0, q, EPI_DGELU, nullptr, nullptr, &HPb, &DHPb, false, &dhpT)) return ONETRANS_ERR_HIP;
+    {   // dW2, db2, dW1, db1
+      GemmPlan P;
+      plan_init(P);
+      RedArgs ra;
+      memset(&ra, 0, sizeof(ra));
+      float *part = (float *)(w + W.part), *rsum = (float *)(w + W.rsum);
+      wgrad_jobs(P, &ra, D, doutT, hidT, (long long)B * q, B, WgradOut{gr.w2, gr.b2}, part, rsum);
+      wgrad_jobs(P, &ra, D, dhpT, yhT, (long long)B * q, B, WgradOut{gr.w1, gr.b1}, part, rsum);
+      if (!tm(ONETRANS_K_BWD_GEMM, [&] { return launch_gemm(dt, P.a, (int)P.tiles, stream); })) return ONETRANS_ERR_HIP;
+      if (!tm(ONETRANS_K_BWD_GEMM, [&] { return launch_reduce(ra, stream); })) return ONETRANS_ERR_HIP;
+    }
+    // dYh = dhpre W1 (fp32)
+    if (!act_gemm(DHPb, W1T, d, dff, p0, q, EPI_STORE, nullptr, nullptr, nullptr, &DYHb, true, nullptr)) return ONETRANS_ERR_HIP;
+    {   // dY = Norm2'(dYh) + dOut: fp32 rows, storage rows, feature-major; dg2 / db2 column partials
+      RowsArgs ra;
+      memset(&ra, 0, sizeof(ra));
+      ra.mode = ROWS_NORM_BWD;
+      ra.x = view(Yb);
+      ra.x_f32 = 1;
+      ra.dy = view(DYHb);
+      ra.res = view(DOUT32);
+      ra.res_from = 0;
+      ra.gamma = wt.norm2_g;
+      ra.beta = wt.norm2_b;
+      ra.out_f32 = view(DY32);
+      ra.out_t = view(DYt);
+      ra.colpart = (float *)(w + W.colpart);
+      const long long tiles = rows_launch(ra, p0, q, &dyT);
+      if (tiles < 0) return ONETRANS_ERR_HIP;
+      if (!tm(ONETRANS_K_BWD_ROWS, [&] {
+            return launch_colsum(ra.colpart, (int)tiles, d, gr.norm2_g, D.layer ? gr.norm2_b : nullptr, stream);
+          }))
+        return ONETRANS_ERR_HIP;
+    }
+    // dO = dY Wo (storage rows)
+    if (!act_gemm(DYt, WoT, d, d, p0, q, EPI_STORE, nullptr, nullptr, nullptr, &DOb, false, nullptr)) return ONETRANS_ERR_HIP;
+    {   // D = rowsum(dO * O) per head, and O^T
+      RowsArgs ra;
+      memset(&ra, 0, sizeof(ra));
+      ra.mode = ROWS_DOT;
+      ra.x = view(Ob);
+      ra.x_f32 = 0;
+      ra.dy = view(DOb);
+      ra.dvec = (float *)(w + W.dvec);
+      ra.d_sb = (long long)H * R;
+      ra.d_R = R;
+      ra.d_p0 = p0;
+      if (dt == ONETRANS_F32) ra.x_f32 = 1;
+      if (rows_launch(ra, p0, q, &oT) < 0) return ONETRANS_ERR_HIP;
+    }
+    {   // attention backward
+      AttnBwdArgs a;
+      memset(&a, 0, sizeof(a));
+      a.n_seq = B;
+      a.n_heads = H;
+      a.d_model = d;
+      a.T = T;
+      a.s = s;
+      a.R = R;
+      a.p0 = p0;
+      a.q = w + W.fw.q;
+      a.q_sb = (long long)H * R * dh;
+      a.k = w + W.fw.k;
+      a.v = w + W.fw.v;
+      a.kv_sb = (long long)H * T * dh;
+      a.dout = w + W.d_o;
+      a.lse = (const float *)(w + W.lse);
+      a.dvec = (const float *)(w + W.dvec);
+      a.dqkv = w + W.dqkv;
+      const FeatBuf *tf[3] = {&dkT, &dvT, &dqT};
+      for (int i = 0; i < 3; ++i) {
+        a.tS[i] = tf[i]->S;
+        a.tN[i] = tf[i]->N;
+      }
+      a.tS_ld = ldA;
+      a.tN_g = (long long)d * ldN;
+      a.tN_ld = ldN;
+      a.n_kblocks = (T + 32 * ATTB_WAVES - 1) / (32 * ATTB_WAVES);
+      a.n_qblocks = (R + 32 * ATTB_WAVES - 1) / (32 * ATTB_WAVES);
+      if (!tm(ONETRANS_K_BWD_ATTN, [&] { return launch_attn_bwd(dt, dh, a, stream); })) return ONETRANS_ERR_HIP;
+    }
+    {   // dWq, dWk, dWv (over every S row; dQ is zero before p0) and dWo
+      GemmPlan P;
+      plan_init(P);
+      RedArgs ra;
+      memset(&ra, 0, sizeof(ra));
+      float *part = (float *)(w + W.part);
+      wgrad_jobs(P, &ra, D, dqT, xhT, (long long)B * s, B, WgradOut{gr.wq, nullptr}, part, nullptr);
+      wgrad_jobs(P, &ra, D, dkT, xhT, (long long)B * s, B, WgradOut{gr.wk, nullptr}, part, nullptr);
+      wgrad_jobs(P, &ra, D, dvT, xhT, (long long)B * s, B, WgradOut{gr.wv, nullptr}, part, nullptr);
+      wgrad_jobs(P, &ra, D, dyT, oT, (long long)B * q, B, WgradOut{gr.wo, nullptr}, part, nullptr);
+      if (!tm(ONETRANS_K_BWD_GEMM, [&] { return launch_gemm(dt, P.a, (int)P.tiles, stream); })) return ONETRANS_ERR_HIP;
+      if (!tm(ONETRANS_K_BWD_GEMM, [&] { return launch_reduce(ra, stream); })) return ONETRANS_ERR_HIP;
+    }
+    // dXh = [dK | dV | dQ] [Wk; Wv; Wq] over all rows (fp32)
+    if (!act_gemm(DQKV, WcT, d, 3 * d, 0, s, EPI_STORE, nullptr, nullptr, nullptr, &DXH, true, nullptr)) return ONETRANS_ERR_HIP;
+    {   // dX = Norm1'(dXh) + dY on the tail rows: the lower block's d_out (fp32 rows, storage rows,
+        // feature-major), or dX(0); dg1 / db1 column partials
+      RowsArgs ra;
+      memset(&ra, 0, sizeof(ra));
+      ra.mode = ROWS_NORM_BWD;
+      ra.x = view(X);
+      ra.x_f32 = x_f32;
+      ra.dy = view(DXH);
+      ra.res = view(DY32);
+      ra.res_from = p0;
+      ra.gamma = wt.norm1_g;
+      ra.beta = wt.norm1_b;
+      ra.colpart = (float *)(w + W.colpart);
+      const FeatBuf *ot = nullptr;
+      if (n > 0) {
+        ra.out_f32 = RowView{w + W.dx32, (long long)T * d, 0, d};
+        ra.out_t = RowView{w + W.dout_t, (long long)T * d, 0, d};
+        ot = &doutT_next;
+      } else if (dx0) {
+        ra.out_f32 = RowView{dx0, (long long)T * d, 0, d};
+      }
+      const long long tiles = rows_launch(ra, 0, s, ot);
+      if (tiles < 0) return ONETRANS_ERR_HIP;
+      if (!tm(ONETRANS_K_BWD_ROWS, [&] {
+            return launch_colsum(ra.colpart, (int)tiles, d, gr.norm1_g, D.layer ? gr.norm1_b : nullptr, stream);
+          }))
+        return ONETRANS_ERR_HIP;
+    }
+    if (!D.layer) {   // RMSNorm has no shift: its gradient slots, when given, are zero
+      FillArgs fa;
+      memset(&fa, 0, sizeof(fa));
+      for (float *p : {gr.norm1_b, gr.norm2_b})
+        if (p) {
+          FillJob &j = fa.job[fa.n_jobs++];
+          j = FillJob{p, 0, d, 1, 1, 0, d, 4, fa.total};
+          fa.total += d;
+        }
+      if (fa.n_jobs && !tm(ONETRANS_K_BWD_ROWS, [&] { return launch_fill(fa, stream); })) return ONETRANS_ERR_HIP;
+    }
+  }
+  return ONETRANS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -868,6 +1496,34 @@ size_t onetrans_workspace_bytes(const onetrans_config *cfg, int op, int n_seq, i
   const int parts = ws_parts_for(n_seq, op == ONETRANS_OP_FORWARD ? FORWARD_PART_MIN : USER_PART_MIN);
   const size_t per = op == ONETRANS_OP_SCORE ? (size_t)n_cand : 1;   // sequences per user
   return ws_layout(D, (size_t)((n_seq + parts - 1) / parts) * per, tin, rq, kv, (size_t)n_seq * per).total * parts;
+}
+
+size_t onetrans_backward_workspace_bytes(const onetrans_config *cfg, int batch, int l_s) {
+  Dims D;
+  if (check_cfg(cfg, D) || batch < 1 || l_s < 1 || check_schedule(cfg, l_s)) return 0;
+  return train_layout(D, cfg, batch, l_s).total;
+}
+
+int onetrans_backward(const onetrans_config *cfg, const onetrans_block_weights *blk, const void *x0, int batch,
+                      int l_s, const float *d_out, float *out, float *dx0, const onetrans_block_grads *grads,
+                      void *ws, size_t ws_bytes, hipStream_t stream) {
+  Dims D;
+  int rc;
+  if ((rc = check_cfg(cfg, D))) return rc;
+  if (batch < 1 || l_s < 1) return ONETRANS_ERR_SHAPE;
+  if ((rc = check_schedule(cfg, l_s))) return rc;
+  if ((rc = check_weights(blk, D))) return rc;
+  if ((rc = check_grads(grads, D))) return rc;
+  if (!x0 || !d_out || !ws) return ONETRANS_ERR_INVALID_ARG;
+  if (misaligned(x0) || misaligned(d_out) || misaligned(out) || misaligned(dx0) || misaligned(ws))
+    return ONETRANS_ERR_ALIGNMENT;
+  if ((rc = check_size(D, batch, (long long)l_s + D.lns))) return rc;
+  // a weight-gradient tile spans 128 feature-major rows of every token of a set: byte offsets
+  // within it are 32-bit
+  if (128LL * pad64((long long)batch * l_s) * 4 >= (1LL << 32)) return ONETRANS_ERR_SHAPE;
+  const TrainWs W = train_layout(D, cfg, batch, l_s);
+  if (ws_bytes < W.total) return ONETRANS_ERR_WORKSPACE;
+  return train_run(D, cfg, blk, x0, batch, l_s, d_out, out, dx0, grads, (char *)ws, W, stream);
 }
 
 size_t onetrans_kv_cache_bytes(const onetrans_config *cfg, int n_users, int capacity) {
