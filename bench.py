@@ -44,7 +44,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="onetrans_s",
                    choices=["onetrans_s", "two_stage", "append", "append_ragged", "append_pyramid", "onetrans_l",
-                            "tokenize_s", "tokenize_s_time"])
+                            "train_s", "tokenize_s", "tokenize_s_time"])
     p.add_argument("--dtype", default=None, choices=[None, "bf16", "f32"])
     p.add_argument("--no-trace", action="store_true", help="no per-kernel events in the timed region")
     p.add_argument("--streams", type=int, default=2, choices=[1, 2, 4],
@@ -285,6 +285,19 @@ def main():
 
         def step():
             ob.onetrans_forward(model, x0, out, wsp)
+    elif w.kind == "train":
+        x0 = up(synth.forward_batch(w))
+        d_out = torch.from_numpy(synth.grad_out_batch(w)).to(dev)
+        out = torch.empty((w.batch, w.s_queries[-1] + m.l_ns, m.d_model), dtype=torch.float32, device=dev)
+        dx0 = torch.empty((w.batch, w.l_s + m.l_ns, m.d_model), dtype=torch.float32, device=dev)
+        grads = ob.grad_buffers(model)
+        wsp = ob.backward_workspace(model, w.batch, w.l_s)
+        n_units = w.batch
+        classes = cm.train_classes(m.d_model, m.d_ff, m.l_ns, w.l_s, w.s_queries)
+        extra["workspace_GiB"] = round(wsp.numel() / 2**30, 2)
+
+        def step():
+            ob.onetrans_backward(model, x0, d_out, grads=grads, ws=wsp, out=out, dx0=dx0)
     elif w.kind == "two_stage":
         xs = up(synth.user_sequences(w))
         xn = up(synth.candidate_batch(w))
@@ -411,6 +424,12 @@ def main():
                 done += 1
             sample = f"{done} samples of the same workload, one at a time"
             units = done
+        elif w.kind == "train":
+            while done < 16 and (time.perf_counter() - t0 < a.cpu_seconds or done < 1):
+                O.backward(synth.forward_sample(w, done), host_w, m, w.s_queries, synth.grad_out_sample(w, done))
+                done += 1
+            sample = f"{done} samples' forward and backward, one at a time"
+            units = done
         elif w.kind == "two_stage":
             cache_o, _ = O.prefill_user(synth.user_sequence(w, 0), host_w, m, w.s_queries)
             while done < 2048 and (time.perf_counter() - t0 < a.cpu_seconds or done < 4):
@@ -443,13 +462,17 @@ def main():
             sample = f"{done} users' appends (their Stage I prefill runs untimed)"
             units = done
         cpu_s = time.perf_counter() - t0 if w.kind != "append" else t_app
-        cpu = {"value": round(units / cpu_s, 4), "unit": "candidates/s" if w.kind != "append" else "users/s",
+        cpu = {"value": round(units / cpu_s, 4),
+               "unit": {"append": "users/s", "train": "samples/s"}.get(w.kind, "candidates/s"),
                "cores": blas_threads(), "kind": "oracle", "sample": sample, "seconds": round(cpu_s, 2),
                **host_info()}
 
-    unit = "candidates/s" if w.kind != "append" else "user appends/s"
+    unit = {"append": "user appends/s", "train": "training samples/s"}.get(w.kind, "candidates/s")
+    metric = METRIC if w.key == "onetrans_s" else f"{unit} at 1 GPU ({w.key})"
+    if w.kind == "train":
+        metric = f"{unit} at 1 GPU ({w.key}: forward keeping block inputs + backward with recomputation)"
     line = {
-        "metric": METRIC if w.key == "onetrans_s" else f"{unit} at 1 GPU ({w.key})",
+        "metric": metric,
         "value": round(value, 2),
         "unit": unit,
         "n_gpus": 1,

@@ -25,7 +25,7 @@ from .shapes import (ModelShape, Workload, WORKLOADS, TEST_SHAPES, linear_pyrami
 from .gen import (round_bf16, bf16_bits, BlockWeights, make_weights, sep_vectors,
                   forward_sample, forward_batch, user_sequence, user_sequences,
                   candidate_tokens, candidate_batch, append_rows, append_batch,
-                  user_cached_lengths)
+                  user_cached_lengths, grad_out_sample, grad_out_batch)
 
 from .tokenizer import (TokWorkload, TOK_WORKLOADS, tok_workload, tokenizer_weights, tokenizer_sample,
                         tokenizer_batch, tokenizer_times, tokenizer_times_batch)
@@ -36,5 +36,5 @@ __all__ = [
     "ModelShape", "Workload", "WORKLOADS", "TEST_SHAPES", "linear_pyramid", "workload",
     "test_workload", "round_bf16", "bf16_bits", "BlockWeights", "make_weights", "sep_vectors",
     "forward_sample", "forward_batch", "user_sequence", "user_sequences", "candidate_tokens",
-    "candidate_batch", "append_rows", "append_batch", "user_cached_lengths",
+    "candidate_batch", "append_rows", "append_batch", "user_cached_lengths", "grad_out_sample", "grad_out_batch",
 ]

@@ -181,3 +181,14 @@ def append_batch(w: Workload, users: Optional[Sequence[int]] = None):
     us = range(w.n_users) if users is None else users
     s = np.stack([user_sequence(w, u) for u in us])
     return s[:, : w.l_old], s[:, w.l_old:]
+
+
+def grad_out_sample(w: Workload, b: int) -> np.ndarray:
+    """Training step: the loss gradient of sample b's final rows, [q_last + L_NS][d] fp32, N(0,1)."""
+    rng = _rng(w.input_seed, (3, b))
+    return _normal(rng, (w.s_queries[-1] + w.model.l_ns, w.model.d_model))
+
+
+def grad_out_batch(w: Workload, samples: Optional[Sequence[int]] = None) -> np.ndarray:
+    idx = range(w.batch) if samples is None else samples
+    return np.stack([grad_out_sample(w, b) for b in idx])

@@ -56,7 +56,7 @@ class Workload:
     key: str
     description: str
     model: ModelShape
-    kind: str                          # "forward", "two_stage" or "append"
+    kind: str                          # "forward", "two_stage", "append" or "train"
     l_s: int
     s_queries: Tuple[int, ...]         # q_n per block
     seq_lens: Tuple[int, ...] = ()     # behaviour sequences in merge order (each followed by [SEP])
@@ -135,6 +135,14 @@ WORKLOADS = {
                     "1 candidate/user; bf16",
         model=_ONETRANS_S, kind="append", l_s=1190, s_queries=(1158, 955, 719, 484, 248, 12), n_users=128, n_cand=1,
         l_old=1158, d_l=32, input_seed=2006, parity_subset=(0, 127)),
+    "train_s": Workload(
+        key="train_s",
+        description="Training step on the OneTransS-shaped model: the forward over the batch keeping each "
+                    "block's input rows, then the backward with activation recomputation (gradients of "
+                    "X(0) and of every parameter, per weight set); batch 256, L_S=1190, pyramid 1190->12; "
+                    "bf16 storage, fp32 accumulation and gradients",
+        model=_ONETRANS_S, kind="train", l_s=1190, s_queries=_S_PYR, seq_lens=(187, 200, 800),
+        batch=256, input_seed=2007, parity_subset=(0, 255)),
     "onetrans_l": Workload(
         key="onetrans_l",
         description="OneTransL-shaped forward: 8 blocks, d=512, 16 heads, FFN 2048; L_S=2048, L_NS=16; "

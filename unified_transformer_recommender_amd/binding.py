@@ -175,11 +175,25 @@ def weight_shapes(model: Model) -> dict:
             "wv": (G, d, d), "wo": (G, d, d), "w1": (G, f, d), "b1": (G, f), "w2": (G, d, f), "b2": (G, d)}
 
 
+def backward_workspace(model: Model, batch: int, l_s: int) -> torch.Tensor:
+    n = int(L.lib().onetrans_backward_workspace_bytes(ctypes.byref(model.cfg), batch, l_s))
+    if n == 0:
+        raise ValueError("invalid configuration for a backward workspace")
+    return torch.empty(n, dtype=torch.uint8, device=model.device)
+
+
+def grad_buffers(model: Model) -> list:
+    """One {field: fp32 tensor} per block, shaped like the parameters."""
+    return [{f: torch.empty(s, dtype=torch.float32, device=model.device) for f, s in weight_shapes(model).items()}
+            for _ in range(model.n_blocks)]
+
+
 def onetrans_backward(model: Model, x0: torch.Tensor, d_out: torch.Tensor, want_out: bool = False,
-                      want_dx0: bool = True, grads=None, ws: Optional[torch.Tensor] = None, stream=None):
+                      want_dx0: bool = True, grads=None, ws: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None, dx0: Optional[torch.Tensor] = None, stream=None):
     """One training step's gradients: x0 [B][L_S + l_ns][d] (storage dtype) and d_out [B][q_last + l_ns][d]
     fp32 -> (out or None, dx0 or None, grads), grads a list (one per block) of {field: fp32 tensor}
-    summed over the batch. `grads` may be given (that structure, preallocated) to be overwritten."""
+    summed over the batch. Preallocated `grads` (grad_buffers), `out`, `dx0` and `ws` are overwritten."""
     _check_input(model, x0, 3, "x0")
     B, T, d = x0.shape
     l_s = T - model.l_ns
@@ -187,20 +201,18 @@ def onetrans_backward(model: Model, x0: torch.Tensor, d_out: torch.Tensor, want_
     if d_out.dtype != torch.float32 or not d_out.is_contiguous() or tuple(d_out.shape) != (B, R, d):
         raise ValueError("d_out: need a contiguous fp32 tensor [B][q_last + l_ns][d]")
     dev = x0.device
-    out = torch.empty((B, R, d), dtype=torch.float32, device=dev) if want_out else None
-    dx0 = torch.empty((B, T, d), dtype=torch.float32, device=dev) if want_dx0 else None
+    if out is None and want_out:
+        out = torch.empty((B, R, d), dtype=torch.float32, device=dev)
+    if dx0 is None and want_dx0:
+        dx0 = torch.empty((B, T, d), dtype=torch.float32, device=dev)
     if grads is None:
-        grads = [{f: torch.empty(s, dtype=torch.float32, device=dev) for f, s in weight_shapes(model).items()}
-                 for _ in range(model.n_blocks)]
+        grads = grad_buffers(model)
     gs = (L.BlockGrads * model.n_blocks)()
     for i, g in enumerate(grads):
         for f in L.WEIGHT_FIELDS:
             setattr(gs[i], f, _ptr(g.get(f)))
     if ws is None:
-        n = int(L.lib().onetrans_backward_workspace_bytes(ctypes.byref(model.cfg), B, l_s))
-        if n == 0:
-            raise ValueError("invalid configuration for a backward workspace")
-        ws = torch.empty(n, dtype=torch.uint8, device=dev)
+        ws = backward_workspace(model, B, l_s)
     st = L.lib().onetrans_backward(ctypes.byref(model.cfg), model.blocks, x0.data_ptr(), B, l_s, d_out.data_ptr(),
                                    _ptr(out), _ptr(dx0), gs, ws.data_ptr(), ws.numel(), _stream(dev, stream))
     L.check(st, "onetrans_backward")

@@ -230,3 +230,37 @@ def tokenize_work(d, l_ns, seq_lens, seq_dims, seq_hidden, ns_dim, ns_hidden, st
         act += store_bytes * (ns_dim + 2 * ns_hidden + l_ns * d)
         wts += store_bytes * (ns_hidden * ns_dim + ns_hidden + l_ns * d * ns_hidden + l_ns * d)
     return flops, act, wts
+
+
+# --- training step (forward keeping block inputs + backward with activation recomputation) ------
+
+TRAIN_CLASSES = ("qkv", "attn", "post", "bwd_gemm", "bwd_attn", "bwd_rows")
+
+
+def train_classes(d, d_ff, l_ns, l_s, s_queries):
+    """Per-sample algorithmic flops of one training step by kernel class.
+
+    The forward runs every block once (qkv, attn, post); the backward recomputes each block's Q/K/V
+    and attention (qkv, attn again), then W^O and the FFN's first product (bwd_gemm), and runs the
+    backward products: for q query rows and t block rows, the FFN's dHidden, dW2, dW1, dYh
+    (4 x 2 q d d_ff), W^O's dO and dWo (2 x 2 q d^2), dWq (2 q d^2), dWk and dWv (2 x 2 t d^2) and
+    dXh (2 t d 2d + 2 q d^2). Attention backward: dV, dP, dQ, dK (4 x 2 d per visible pair) plus
+    the recomputed scores (2 d per pair); the dQ kernel's second pass over the scores and dP is
+    implementation overhead and not counted. Row kernels (norms, conversions, sums) count no flops."""
+    tot = {k: 0.0 for k in TRAIN_CLASSES}
+    s = l_s
+    for q in s_queries:
+        t, r = s + l_ns, q + l_ns
+        pairs = visible_pairs(s - q, r)
+        fq = 2.0 * d * d * (2 * t + r)
+        fa = 4.0 * d * pairs
+        tot["qkv"] += 2 * fq
+        tot["attn"] += 2 * fa
+        tot["post"] += 2.0 * d * d * r + 4.0 * d * d_ff * r
+        tot["bwd_gemm"] += (2.0 * d * d * r + 2.0 * d * d_ff * r          # recomputed W^O and W1
+                            + 8.0 * r * d * d_ff + 4.0 * r * d * d        # FFN and W^O backward
+                            + 2.0 * r * d * d + 4.0 * t * d * d           # dWq, dWk, dWv
+                            + 4.0 * t * d * d + 2.0 * r * d * d)          # dXh
+        tot["bwd_attn"] += 10.0 * d * pairs
+        s = q
+    return tot

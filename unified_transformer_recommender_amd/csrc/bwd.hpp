@@ -100,7 +100,8 @@ struct TrArgs {
 hipError_t launch_transpose(int dtype, const TrArgs &a, int grid, hipStream_t s);
 
 // Zero fill of up to FILL_MAX_JOBS strided regions: for row i < rows of group j < groups, elements
-// [c0, c1) of base + j * g + i * ld (bytes per element: esz).
+// [c0, c1) of base + j * g + i * ld (bytes per element: esz). start: the job's first segment
+// (groups * rows segments per job) in the launch; total: segments of the launch.
 constexpr int FILL_MAX_JOBS = 32;
 struct FillJob {
   void *base; long long g, ld;
@@ -146,8 +147,11 @@ struct RowsArgs {
 hipError_t launch_rows(int dtype, const RowsArgs &a, int grid, hipStream_t s);
 
 // Column sums of the NORM_BWD partials: dst_g[f] = sum_tiles colpart[tile][0][f], dst_b likewise
-// with [1] (dst_b may be null).
-hipError_t launch_colsum(const float *colpart, int n_tiles, int d, float *dst_g, float *dst_b, hipStream_t s);
+// with [1] (dst_b may be null). More than COLSUM_PER tiles are first summed in ranges of that many
+// into scratch ([ceil(n_tiles / COLSUM_PER)][2][d] floats).
+constexpr int COLSUM_PER = 64;
+hipError_t launch_colsum(const float *colpart, int n_tiles, int d, float *dst_g, float *dst_b, float *scratch,
+                         hipStream_t s);
 
 // ---------------------------------------------------------------------------------------------
 // Attention backward for one block (per head, base 2 as in the forward: queries stored multiplied

@@ -291,55 +291,6 @@ __global__ __launch_bounds__(256) void reduce_kernel(const RedArgs a) {
   }
 }
 
-// ---- weight transposes (32 x 32 tiles through LDS) --------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void transpose_kernel(const TrArgs a) {
-  __shared__ T tile[32][33];
-  const int b = blockIdx.x;
-  int ji = 0;
-#pragma unroll
-  for (int i = 1; i < TR_MAX_JOBS; ++i)
-    if (i < a.n_jobs && b >= a.job[i].tile0) ji = i;
-  const TrJob &J = a.job[ji];
-  const int rt = (J.rows + 31) / 32, ct = (J.cols + 31) / 32;
-  int local = b - J.tile0;
-  const int tc = local % ct;
-  local /= ct;
-  const int tr = local % rt;
-  const int set = local / rt;
-  const T *src = (const T *)J.src + set * J.src_set;
-  T *dst = (T *)J.dst + set * J.dst_set;
-  const int x = threadIdx.x & 31, y0 = threadIdx.x >> 5;
-  for (int y = y0; y < 32; y += 8) {
-    const int r = tr * 32 + y, c = tc * 32 + x;
-    if (r < J.rows && c < J.cols) tile[y][x] = src[(long long)r * J.cols + c];
-  }
-  __syncthreads();
-  for (int y = y0; y < 32; y += 8) {
-    const int c = tc * 32 + y, r = tr * 32 + x;
-    if (r < J.rows && c < J.cols) dst[(long long)c * J.dst_ld + J.dst_off + r] = tile[x][y];
-  }
-}
-
-// ---- zero fills -------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void fill_kernel(const FillArgs a) {
-  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (e >= a.total) return;
-  int ji = 0;
-#pragma unroll
-  for (int i = 1; i < FILL_MAX_JOBS; ++i)
-    if (i < a.n_jobs && e >= a.job[i].start) ji = i;
-  const FillJob &J = a.job[ji];
-  const long long x = e - J.start;
-  const int w = J.c1 - J.c0;
-  const long long row = x / w;
-  const int c = J.c0 + (int)(x - row * w);
-  const int i = (int)(row % J.rows), jg = (int)(row / J.rows);
-  char *p = (char *)J.base + ((long long)jg * J.g + (long long)i * J.ld + c) * J.esz;
-  if (J.esz == 2) *(uint16_t *)p = 0;
-  else *(uint32_t *)p = 0;
-}
-
 }  // namespace
 
 int gemm_tokens_per_tile() { return GM_NW * 32; }
@@ -356,19 +307,6 @@ hipError_t launch_reduce(const RedArgs &a, hipStream_t s) {
   if (a.total == 0) return hipSuccess;
   const long long groups = (a.total + 3) / 4;
   hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose(int dtype, const TrArgs &a, int grid, hipStream_t s) {
-  if (grid == 0) return hipSuccess;
-  if (dtype == 1) hipLaunchKernelGGL(transpose_kernel<bf16>, dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(transpose_kernel<float>, dim3(grid), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_fill(const FillArgs &a, hipStream_t s) {
-  if (a.total == 0) return hipSuccess;
-  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((a.total + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -1001,7 +1001,7 @@ struct TrainWs {
   size_t lse, dvec, y, yh, hpre, dhpre, dyh, dy32, dyt, dout_t, d_o, dqkv, dxh, dx32;
   size_t xhT, dkT, dvT, dqT, oT, dyT, yhT, dhpreT, hidT, doutT;
   size_t woT, w1T, w2T, wcT;
-  size_t part, rsum, colpart;
+  size_t part, rsum, colpart, colsum2;
   long long ldS_all, ldS_tail, ldN;   // block-0 (largest) feature-major row lengths
   size_t total;
 };
@@ -1085,6 +1085,7 @@ TrainWs train_layout(const Dims &D, const onetrans_config *cfg, int B, int l_s) 
   w.part = take((size_t)part * 4);
   w.rsum = take((size_t)rsum * 4);
   w.colpart = take((size_t)tiles32 * 2 * d * 4);
+  w.colsum2 = take((size_t)((tiles32 + COLSUM_PER - 1) / COLSUM_PER) * 2 * d * 4);
   w.total = off;
   return w;
 }
@@ -1199,7 +1200,7 @@ int train_run(const Dims &D, const onetrans_config *cfg, const onetrans_block_we
         }
         FillJob &j = fa.job[fa.n_jobs++];
         j = FillJob{base, g, ld, groups, rows, (int)c0, (int)c1, (int)es, fa.total};
-        fa.total += (long long)groups * rows * (c1 - c0);
+        fa.total += (long long)groups * rows;
       };
       auto pads = [&](const FeatBuf &f, long long tok) {
         add(f.S, 0, f.ldS, 1, f.F, tok, f.ldS);
@@ -1373,7 +1374,8 @@ int train_run(const Dims &D, const onetrans_config *cfg, const onetrans_block_we
       const long long tiles = rows_launch(ra, p0, q, &dyT);
       if (tiles < 0) return ONETRANS_ERR_HIP;
       if (!tm(ONETRANS_K_BWD_ROWS, [&] {
-            return launch_colsum(ra.colpart, (int)tiles, d, gr.norm2_g, D.layer ? gr.norm2_b : nullptr, stream);
+            return launch_colsum(ra.colpart, (int)tiles, d, gr.norm2_g, D.layer ? gr.norm2_b : nullptr,
+                                 (float *)(w + W.colsum2), stream);
           }))
         return ONETRANS_ERR_HIP;
     }
@@ -1463,7 +1465,8 @@ int train_run(const Dims &D, const onetrans_config *cfg, const onetrans_block_we
       const long long tiles = rows_launch(ra, 0, s, ot);
       if (tiles < 0) return ONETRANS_ERR_HIP;
       if (!tm(ONETRANS_K_BWD_ROWS, [&] {
-            return launch_colsum(ra.colpart, (int)tiles, d, gr.norm1_g, D.layer ? gr.norm1_b : nullptr, stream);
+            return launch_colsum(ra.colpart, (int)tiles, d, gr.norm1_g, D.layer ? gr.norm1_b : nullptr,
+                                 (float *)(w + W.colsum2), stream);
           }))
         return ONETRANS_ERR_HIP;
     }
@@ -1474,7 +1477,7 @@ int train_run(const Dims &D, const onetrans_config *cfg, const onetrans_block_we
         if (p) {
           FillJob &j = fa.job[fa.n_jobs++];
           j = FillJob{p, 0, d, 1, 1, 0, d, 4, fa.total};
-          fa.total += d;
+          fa.total += 1;
         }
       if (fa.n_jobs && !tm(ONETRANS_K_BWD_ROWS, [&] { return launch_fill(fa, stream); })) return ONETRANS_ERR_HIP;
     }

@@ -1,5 +1,6 @@
-// Row-wise kernels of the training step (fun-rec-mdbook 7.5.1: pre-norm RMSNorm / LayerNorm; the
-// backward of each norm and of the attention softmax's row term).
+// Row-wise and data-movement kernels of the training step (fun-rec-mdbook 7.5.1: pre-norm RMSNorm /
+// LayerNorm; the backward of each norm and of the attention softmax's row term), plus the weight
+// transposes and zero fills the backward products need.
 //
 // One workgroup takes 32 consecutive rows of one row set (a wave takes 8 of them, one row at a
 // time; a lane holds E = d / 64 consecutive features). Feature-major outputs are staged in LDS as a
@@ -208,19 +209,74 @@ __global__ __launch_bounds__(256) void rows_kernel(const RowsArgs a) {
   }
 }
 
-// Column sums of per-tile partials: one workgroup per 64 columns of one kind (g or b).
-__global__ __launch_bounds__(256) void colsum_kernel(const float *part, int n_tiles, int d, float *dst_g, float *dst_b) {
+// Column sums of per-tile partials [n_tiles][2][d]: workgroup (p, group) adds tiles
+// [p * per, (p + 1) * per) for 64 columns of one kind (g or b) and writes the sum to
+// out[p][kind][c]; with one range that is the final column sum. Fixed order, no atomics.
+__global__ __launch_bounds__(256) void colsum_kernel(const float *part, int n_tiles, int per, int d, float *out_g,
+                                                     float *out_b, long long out_split) {
   __shared__ float s[4][64];
-  const int groups = d / 64;
-  const int kind = blockIdx.x / groups, c0 = (blockIdx.x - kind * groups) * 64;
-  float *dst = kind == 0 ? dst_g : dst_b;
+  const int groups = 2 * (d / 64);
+  const int gi = blockIdx.x % groups, p = blockIdx.x / groups;
+  const int kind = gi / (d / 64), c0 = (gi - kind * (d / 64)) * 64;
+  float *dst = kind == 0 ? out_g : out_b;
   if (!dst) return;
   const int c = c0 + (threadIdx.x & 63), ph = threadIdx.x >> 6;
+  const int t0 = p * per, t1 = min(n_tiles, t0 + per);
   float acc = 0.0f;
-  for (int t = ph; t < n_tiles; t += 4) acc += part[((long long)t * 2 + kind) * d + c];
+  for (int t = t0 + ph; t < t1; t += 4) acc += part[((long long)t * 2 + kind) * d + c];
   s[ph][threadIdx.x & 63] = acc;
   __syncthreads();
-  if (ph == 0) dst[c] = (s[0][threadIdx.x] + s[1][threadIdx.x]) + (s[2][threadIdx.x] + s[3][threadIdx.x]);
+  if (ph == 0)
+    dst[p * out_split + c] = (s[0][threadIdx.x] + s[1][threadIdx.x]) + (s[2][threadIdx.x] + s[3][threadIdx.x]);
+}
+
+// ---- weight transposes (32 x 32 tiles through LDS) --------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const TrArgs a) {
+  __shared__ T tile[32][33];
+  const int b = blockIdx.x;
+  int ji = 0;
+#pragma unroll
+  for (int i = 1; i < TR_MAX_JOBS; ++i)
+    if (i < a.n_jobs && b >= a.job[i].tile0) ji = i;
+  const TrJob &J = a.job[ji];
+  const int rt = (J.rows + 31) / 32, ct = (J.cols + 31) / 32;
+  int local = b - J.tile0;
+  const int tc = local % ct;
+  local /= ct;
+  const int tr = local % rt;
+  const int set = local / rt;
+  const T *src = (const T *)J.src + set * J.src_set;
+  T *dst = (T *)J.dst + set * J.dst_set;
+  const int x = threadIdx.x & 31, y0 = threadIdx.x >> 5;
+  for (int y = y0; y < 32; y += 8) {
+    const int r = tr * 32 + y, c = tc * 32 + x;
+    if (r < J.rows && c < J.cols) tile[y][x] = src[(long long)r * J.cols + c];
+  }
+  __syncthreads();
+  for (int y = y0; y < 32; y += 8) {
+    const int c = tc * 32 + y, r = tr * 32 + x;
+    if (r < J.rows && c < J.cols) dst[(long long)c * J.dst_ld + J.dst_off + r] = tile[x][y];
+  }
+}
+
+// ---- zero fills ----------------------------------------------------------------------------------
+// One workgroup per contiguous segment (row i of group j of a job): its elements [c0, c1), written
+// by consecutive threads (coalesced; 4-byte stores for 4-byte elements, 2-byte otherwise).
+__global__ __launch_bounds__(256) void fill_kernel(const FillArgs a) {
+  const long long seg = blockIdx.x;
+  int ji = 0;
+#pragma unroll
+  for (int i = 1; i < FILL_MAX_JOBS; ++i)
+    if (i < a.n_jobs && seg >= a.job[i].start) ji = i;
+  const FillJob &J = a.job[ji];
+  const long long x = seg - J.start;
+  const int i = (int)(x % J.rows), jg = (int)(x / J.rows);
+  char *row = (char *)J.base + ((long long)jg * J.g + (long long)i * J.ld) * J.esz;
+  for (int c = J.c0 + (int)threadIdx.x; c < J.c1; c += 256) {
+    if (J.esz == 2) *(uint16_t *)(row + (long long)c * 2) = 0;
+    else *(uint32_t *)(row + (long long)c * 4) = 0;
+  }
 }
 
 template <typename T, int E>
@@ -252,8 +308,31 @@ hipError_t launch_rows(int dtype, const RowsArgs &a, int grid, hipStream_t s) {
   return dtype == 1 ? launch_t<bf16>(a, grid, s) : launch_t<float>(a, grid, s);
 }
 
-hipError_t launch_colsum(const float *colpart, int n_tiles, int d, float *dst_g, float *dst_b, hipStream_t s) {
-  hipLaunchKernelGGL(colsum_kernel, dim3(2 * (d / 64)), dim3(256), 0, s, colpart, n_tiles, d, dst_g, dst_b);
+hipError_t launch_colsum(const float *colpart, int n_tiles, int d, float *dst_g, float *dst_b, float *scratch,
+                         hipStream_t s) {
+  const int groups = 2 * (d / 64);
+  if (n_tiles > COLSUM_PER) {
+    // first level: ranges of COLSUM_PER tiles into scratch [ranges][2][d], then their sum
+    const int ranges = (n_tiles + COLSUM_PER - 1) / COLSUM_PER;
+    hipLaunchKernelGGL(colsum_kernel, dim3(groups * ranges), dim3(256), 0, s, colpart, n_tiles, COLSUM_PER, d,
+                       scratch, scratch + d, 2LL * d);
+    colpart = scratch;
+    n_tiles = ranges;
+  }
+  hipLaunchKernelGGL(colsum_kernel, dim3(groups), dim3(256), 0, s, colpart, n_tiles, n_tiles, d, dst_g, dst_b, 0LL);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(int dtype, const TrArgs &a, int grid, hipStream_t s) {
+  if (grid == 0) return hipSuccess;
+  if (dtype == 1) hipLaunchKernelGGL(transpose_kernel<bf16>, dim3(grid), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(transpose_kernel<float>, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill(const FillArgs &a, hipStream_t s) {
+  if (a.total == 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)a.total), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

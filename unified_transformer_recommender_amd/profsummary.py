@@ -34,6 +34,9 @@ KERNELS = {
     "attn": (("attn_kernel", "attn_split_kernel"), "attn.hip"),
     "post": (("post_kernel", "post_reduce_kernel", "post_f32w_kernel"), "post.hip"),
     "lin": (("lin_kernel",), "tok.hip"),
+    "bwd_gemm": (("gemm_kernel", "reduce_kernel"), "gemm.hip"),
+    "bwd_attn": (("attn_dkdv_kernel", "attn_dq_kernel"), "attn_bwd.hip"),
+    "bwd_rows": (("rows_kernel", "colsum_kernel", "transpose_kernel", "fill_kernel"), "rows.hip"),
 }
 COPY_KERNEL = "neg"
 MFMA_COUNTERS = ("MfmaUtil", "VALUBusy")
