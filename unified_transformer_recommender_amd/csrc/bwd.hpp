@@ -38,6 +38,8 @@ struct MatT {
 //   STORE   out(j, r)[n] = C (+ bias[j][n]) (+ resid(j, r)[n]); fp32 or storage dtype; plus outT
 //   GELU    out = C + bias (storage dtype, the pre-activation); outT = GELU(C + bias)
 //   DGELU   v = C * GELU'(aux(j, r)[n]); out = v (storage dtype) and outT = v
+//           (GELU: the erf form with fp32 storage; with bf16 storage the fitted form the bf16
+//           forward evaluates, and its exact derivative)
 //   PARTIAL out(j, r)[n] at out.base + split * part_split: the split's fp32 partial sum; with
 //           rowsum set, the workgroups of feature tile 0 also write sum_k A(j, r)[k] over their
 //           range to rowsum[split * rowsum_split + j * m + r]

@@ -20,14 +20,25 @@
 namespace ot {
 namespace {
 
-constexpr int GM_NW = 4;       // waves per workgroup, 32 token rows each
-constexpr int GM_NT = 64;      // feature rows per workgroup
 constexpr int GM_CB = 128;     // bytes of k per row and chunk
 constexpr int GM_NB = 2;       // chunk buffers
-constexpr int GM_W_BYTES = GM_NT * GM_CB;
-constexpr int GM_X_BYTES = GM_NW * 32 * GM_CB;
-constexpr int GM_STAGE_BYTES = GM_W_BYTES + GM_X_BYTES;
-static_assert(GM_NT == 64 && GM_NW == 4, "direct-to-LDS load split: 2 feature and 4 token loads per wave");
+constexpr int GM_TOK = 128;    // token-operand rows per workgroup (both layouts)
+
+// Wave layouts of a 4-wave workgroup: WGM x WGN waves, each computing TM x TN accumulator tiles of
+// 32 x 32 (TM token tiles, TN feature tiles). Narrow: 4 x 1 waves of 1 x 2 tiles (128 tokens x 64
+// features; every feature fragment read feeds one MFMA). Wide: 2 x 2 waves of 2 x 2 tiles
+// (128 x 128; every fragment read feeds two MFMAs).
+template <int TM_, int TN_, int WGM_, int WGN_>
+struct Layout {
+  static constexpr int TM = TM_, TN = TN_, WGM = WGM_, WGN = WGN_;
+  static constexpr int FR = 32 * TN * WGN;   // feature rows per workgroup
+  static constexpr int TR = 32 * TM * WGM;   // token rows per workgroup
+  static constexpr int STAGE = (FR + TR) * GM_CB;
+  static constexpr int LOADS = (FR + TR) * 8 / 256;   // 16-byte direct loads per thread and chunk
+  static_assert(WGM * WGN == 4 && TR == GM_TOK, "4 waves, 128 token rows");
+};
+using Narrow = Layout<1, 2, 4, 1>;
+using Wide = Layout<2, 2, 2, 2>;
 
 __device__ __forceinline__ uint32_t slot_byte(int r, int p) { return (uint32_t)(r * 8 + (p ^ (r & 7))) * 16u; }
 
@@ -43,20 +54,39 @@ __device__ __forceinline__ int xcd_tile(int b, int n) {
 }
 
 // Derivative of the erf-form GELU, Phi(x) + x phi(x), with Phi from Abramowitz & Stegun 7.1.26 in
-// the same form as gelu_as (|error| of Phi <= 1.5e-7 / 2).
-__device__ __forceinline__ float gelu_grad(float x) {
+// the same form as gelu_as (|error| of Phi <= 1.5e-7 / 2). fp32 storage.
+__device__ __forceinline__ float gelu_grad_as(float x) {
   constexpr float p = 0.3275911f * 0.70710678118654752f;
   constexpr float a1 = 0.5f * 0.254829592f, a2 = 0.5f * -0.284496736f, a3 = 0.5f * 1.421413741f,
                   a4 = 0.5f * -1.453152027f, a5 = 0.5f * 1.061405429f;
   constexpr float neg_half_log2e = -0.72134752044448170f;
   constexpr float inv_sqrt_2pi = 0.3989422804014327f;
   const float ax = fabsf(x);
-  const float t = 1.0f / fmaf(p, ax, 1.0f);
+  const float t = __builtin_amdgcn_rcpf(fmaf(p, ax, 1.0f));
   const float q = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, a5, a4), a3), a2), a1);   // 0.5 erfc(|x| / sqrt 2) / e
   const float e = __builtin_amdgcn_exp2f(x * x * neg_half_log2e);              // exp(-x^2 / 2)
   const float tail = q * e;
   const float cdf = x >= 0.0f ? 1.0f - tail : tail;
   return fmaf(x * inv_sqrt_2pi, e, cdf);
+}
+
+// Derivative of the bf16 paths' GELU x sigma(z), z = x (A1 + A3 x^2) (gelu_fit, the function the
+// bf16 forward evaluates): sigma(z) (1 + x (1 - sigma(z)) (A1 + 3 A3 x^2)), with
+// 1 - sigma(z) = e^-z sigma(z).
+__device__ __forceinline__ float gelu_grad_fit(float x) {
+  constexpr float L = -1.4426950408889634f;   // -log2(e)
+  const float x2 = x * x;
+  const float e = __builtin_amdgcn_exp2f(x * fmaf(x2, GELU_FIT_A3 * L, GELU_FIT_A1 * L));   // e^-z
+  const float sg = __builtin_amdgcn_rcpf(1.0f + e);
+  const float dz = fmaf(3.0f * GELU_FIT_A3, x2, GELU_FIT_A1);
+  return sg * fmaf(x * e * sg, dz, 1.0f);
+}
+
+template <typename T> __device__ __forceinline__ float gelu_of(float x) {
+  return sizeof(T) == 2 ? gelu_fit(x) : gelu_as(x);
+}
+template <typename T> __device__ __forceinline__ float gelu_grad_of(float x) {
+  return sizeof(T) == 2 ? gelu_grad_fit(x) : gelu_grad_as(x);
 }
 
 // Four consecutive values of a row (storage dtype or fp32) as floats.
@@ -70,16 +100,17 @@ __device__ __forceinline__ f32x4 load4(const T *p) {
   }
 }
 
-template <typename T>
-__global__ __launch_bounds__(GM_NW * 64, 2) void gemm_kernel(const GemmArgs a) {
+template <typename T, typename LY>
+__global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
   using MM = Mma<T>;
   constexpr int ESZ = (int)sizeof(T);
   constexpr int KC = GM_CB / ESZ;             // k elements per chunk
   constexpr int EPP = 16 / ESZ;               // elements per 16-byte piece
   constexpr int SPP = EPP / MM::KPL;          // MFMA k-steps per piece (bf16: 1, fp32: 4)
-  constexpr int NTT = GM_NT / 32;             // accumulator tiles per wave
-  static_assert(GM_NW * TileStage<float>::SIZE * 4 <= GM_NB * GM_STAGE_BYTES, "staging fits in the ring");
-  __shared__ __attribute__((aligned(16))) char ring[GM_NB * GM_STAGE_BYTES];
+  constexpr int TM = LY::TM, TN = LY::TN;
+  static_assert(4 * TileStage<float>::SIZE * 4 + 4 * 32 * (32 + 16 / ESZ) * ESZ <= GM_NB * LY::STAGE,
+                "row-major and feature-major staging fit in the ring");
+  __shared__ __attribute__((aligned(16))) char ring[GM_NB * LY::STAGE];
 
   const int tile = xcd_tile((int)blockIdx.x, (int)gridDim.x);
   int ji = 0;
@@ -94,52 +125,54 @@ __global__ __launch_bounds__(GM_NW * 64, 2) void gemm_kernel(const GemmArgs a) {
   local /= J.m_tiles;
   const int j = local % J.n_groups;
   const int split = local / J.n_groups;
-  const int n0 = nt * GM_NT;
-  const int mw0 = mt * (GM_NW * 32);
-  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int n0 = nt * LY::FR;
+  const int mw0 = mt * LY::TR;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
   const int lc = lane & 31, g = lane >> 5;
-  const int m0 = mw0 + wave * 32;
+  const int wm = wave % LY::WGM, wn = wave / LY::WGM;
+  const int m0 = mw0 + wm * 32 * TM;          // this wave's first token row
+  const int f0 = wn * 32 * TN;                // this wave's first feature row within the tile
 
   const int n_all = J.k_len / KC;
   const int per = (n_all + J.n_split - 1) / J.n_split;
   const int c_lo = min(n_all, split * per), c_hi = min(n_all, c_lo + per);
   const int n_chunks = c_hi - c_lo;
 
-  // direct-to-LDS sources: feature rows n0.. of the tile, token rows of this wave (clamped to the
-  // last row in the ragged tail, whose results are never stored); byte offsets from the first row
+  // direct-to-LDS loads: instruction i of wave w covers stage slots [(4 i + w) 64, + 64); slot s
+  // holds piece (s % 8) ^ (row & 7) of stage row s / 8 (feature rows first, then token rows; a
+  // token row past the end re-reads the last row, whose results are never stored)
   const long long wrow0 = row_off(J.b, j, n0), xrow0 = row_off(J.a, j, mw0);
   const char *wsrc = (const char *)J.b.base + (wrow0 + (long long)c_lo * KC) * ESZ;
   const char *xsrc = (const char *)J.a.base + (xrow0 + (long long)c_lo * KC) * ESZ;
-  uint32_t w_off[2], x_off[4];
+  uint32_t off[LY::LOADS];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int s = (2 * wave + i) * 64 + lane, r = s / 8, p = (s % 8) ^ (r & 7);
-    w_off[i] = (uint32_t)((row_off(J.b, j, n0 + r) - wrow0) * ESZ + p * 16);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int s = i * 64 + lane, r = s / 8, p = (s % 8) ^ (r & 7);
-    const int row = min(m0 + r, J.m - 1);
-    x_off[i] = (uint32_t)((row_off(J.a, j, row) - xrow0) * ESZ + p * 16);
+  for (int i = 0; i < LY::LOADS; ++i) {
+    const int s = (4 * i + wave) * 64 + lane, r = s / 8, p = (s % 8) ^ (r & 7);
+    if (r < LY::FR) {
+      off[i] = (uint32_t)((row_off(J.b, j, n0 + r) - wrow0) * ESZ + p * 16);
+    } else {
+      const int row = min(mw0 + r - LY::FR, J.m - 1);
+      off[i] = (uint32_t)((row_off(J.a, j, row) - xrow0) * ESZ + p * 16);
+    }
   }
   const uint32_t ring_lds = lds_addr(ring);
   auto issue = [&](int c) {
-    const uint32_t st = ring_lds + (uint32_t)((c % GM_NB) * GM_STAGE_BYTES);
+    const uint32_t st = ring_lds + (uint32_t)((c % GM_NB) * LY::STAGE);
     const uint32_t cb = (uint32_t)c * GM_CB;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      dma16s(wsrc, w_off[i] + cb, __builtin_amdgcn_readfirstlane(st + (uint32_t)((2 * wave + i) * 1024)));
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      dma16s(xsrc, x_off[i] + cb, __builtin_amdgcn_readfirstlane(st + GM_W_BYTES + (uint32_t)(wave * 4096 + i * 1024)));
+    for (int i = 0; i < LY::LOADS; ++i) {
+      const bool feat = (4 * i + wave) * 8 < LY::FR;   // wave-uniform: 8 rows per instruction
+      dma16s(feat ? (const void *)wsrc : (const void *)xsrc, off[i] + cb,
+             __builtin_amdgcn_readfirstlane(st + (uint32_t)((4 * i + wave) * 1024)));
+    }
   };
 
   // bias of this lane's accumulator rows, loaded before the first direct-to-LDS load
-  float bv[NTT][16] = {};
+  float bv[TN][16] = {};
   if (J.bias) {
-    const T *bias = (const T *)J.bias + j * J.bias_g + n0;
+    const T *bias = (const T *)J.bias + j * J.bias_g + n0 + f0;
 #pragma unroll
-    for (int t = 0; t < NTT; ++t)
+    for (int t = 0; t < TN; ++t)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const f32x4 b4 = load4<T>(bias + t * 32 + 8 * jj + 4 * g);   // acc_row(4 jj + i, g) = 8 jj + 4 g + i
@@ -147,13 +180,15 @@ __global__ __launch_bounds__(GM_NW * 64, 2) void gemm_kernel(const GemmArgs a) {
         for (int i = 0; i < 4; ++i) bv[t][4 * jj + i] = b4[i];
       }
   }
-  const bool rowsum = J.epi == EPI_PARTIAL && J.rowsum && nt == 0;
-  float rsum = 0.0f;
+  const bool rowsum = J.epi == EPI_PARTIAL && J.rowsum && nt == 0 && wn == 0;
+  float rsum[TM] = {};
   asm volatile("" ::: "memory");
 
-  f32x16 acc[NTT];
+  f32x16 acc[TM][TN];
 #pragma unroll
-  for (int t = 0; t < NTT; ++t) acc[t] = f32x16{};
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int t = 0; t < TN; ++t) acc[i][t] = f32x16{};
 
   if (n_chunks > 0) issue(0);
   for (int c = 0; c < n_chunks; ++c) {
@@ -162,105 +197,130 @@ __global__ __launch_bounds__(GM_NW * 64, 2) void gemm_kernel(const GemmArgs a) {
     bare_barrier();
     if (c + 1 < n_chunks) issue(c + 1);
 
-    const char *st = ring + (c % GM_NB) * GM_STAGE_BYTES;
-    const char *xs = st + GM_W_BYTES + wave * 4096;
-    u32x4 xb[4], wa[4][NTT];
+    const char *st = ring + (c % GM_NB) * LY::STAGE;
+    const char *xs = st + LY::FR * GM_CB;
+    u32x4 xb[4][TM], wa[4][TN];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      xb[q] = *(const u32x4 *)(xs + slot_byte(lc, 4 * g + q));
 #pragma unroll
-      for (int t = 0; t < NTT; ++t) wa[q][t] = *(const u32x4 *)(st + slot_byte(t * 32 + lc, 4 * g + q));
+      for (int i = 0; i < TM; ++i) xb[q][i] = *(const u32x4 *)(xs + slot_byte(wm * 32 * TM + i * 32 + lc, 4 * g + q));
+#pragma unroll
+      for (int t = 0; t < TN; ++t) wa[q][t] = *(const u32x4 *)(st + slot_byte(f0 + t * 32 + lc, 4 * g + q));
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int t = 0; t < NTT; ++t) {
-        if constexpr (ESZ == 2) {
-          acc[t] = MM::mma(__builtin_bit_cast(bf16x8, wa[q][t]), __builtin_bit_cast(bf16x8, xb[q]), acc[t]);
-        } else {
-          const f32x4 af = __builtin_bit_cast(f32x4, wa[q][t]), bf = __builtin_bit_cast(f32x4, xb[q]);
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-          for (int e = 0; e < SPP; ++e) acc[t] = MM::mma(af[e], bf[e], acc[t]);
+        for (int t = 0; t < TN; ++t) {
+          if constexpr (ESZ == 2) {
+            acc[i][t] = MM::mma(__builtin_bit_cast(bf16x8, wa[q][t]), __builtin_bit_cast(bf16x8, xb[q][i]), acc[i][t]);
+          } else {
+            const f32x4 af = __builtin_bit_cast(f32x4, wa[q][t]), bf = __builtin_bit_cast(f32x4, xb[q][i]);
+#pragma unroll
+            for (int e = 0; e < SPP; ++e) acc[i][t] = MM::mma(af[e], bf[e], acc[i][t]);
+          }
         }
-      }
-    sched_lds_mfma<4 * (1 + NTT), 4 * NTT * SPP, 6>();
+    sched_lds_mfma<4 * (TM + TN), 4 * TM * TN * SPP, 6>();
     if (rowsum) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if constexpr (ESZ == 2) {
-          const bf16x8 v = __builtin_bit_cast(bf16x8, xb[q]);
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) rsum += (float)v[e];
-        } else {
-          const f32x4 v = __builtin_bit_cast(f32x4, xb[q]);
-          rsum += (v[0] + v[1]) + (v[2] + v[3]);
+        for (int i = 0; i < TM; ++i) {
+          if constexpr (ESZ == 2) {
+            const bf16x8 v = __builtin_bit_cast(bf16x8, xb[q][i]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) rsum[i] += (float)v[e];
+          } else {
+            const f32x4 v = __builtin_bit_cast(f32x4, xb[q][i]);
+            rsum[i] += (v[0] + v[1]) + (v[2] + v[3]);
+          }
         }
-      }
     }
   }
 
   // ---- epilogue ----------------------------------------------------------------------------
   wait_lgkm0();
   bare_barrier();   // every wave is done with the ring; it becomes the staging area
-  if (rowsum) {
-    const float other = __shfl_xor(rsum, 32, 64);
-    if (g == 0 && m0 + lc < J.m) J.rowsum[split * J.rowsum_split + (long long)j * J.m + m0 + lc] = rsum + other;
-  }
-  const bool tok_ok = m0 + lc < J.m;
-  const int my_row = min(m0 + lc, J.m - 1);
 #pragma unroll
-  for (int t = 0; t < NTT; ++t) {
-    f32x16 v = acc[t];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) v[e] += bv[t][e];
-    const int nb = n0 + t * 32;
-    if (J.epi == EPI_STORE && J.resid.base) {
-      const long long ro = row_off(J.resid, j, my_row) + nb + 4 * g;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const f32x4 r4 = J.resid_f32 ? load4<float>((const float *)J.resid.base + ro + 8 * jj)
-                                     : load4<T>((const T *)J.resid.base + ro + 8 * jj);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[4 * jj + i] += r4[i];
-      }
+  for (int i = 0; i < TM; ++i) {
+    const int mi = m0 + i * 32;               // first token row of this accumulator tile
+    if (rowsum) {
+      const float other = __shfl_xor(rsum[i], 32, 64);
+      if (g == 0 && mi + lc < J.m) J.rowsum[split * J.rowsum_split + (long long)j * J.m + mi + lc] = rsum[i] + other;
     }
-    if (J.epi == EPI_DGELU) {
-      const long long ro = row_off(J.aux, j, my_row) + nb + 4 * g;
+    const int my_row = min(mi + lc, J.m - 1);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const f32x4 h4 = load4<T>((const T *)J.aux.base + ro + 8 * jj);
+    for (int t = 0; t < TN; ++t) {
+      f32x16 v = acc[i][t];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[4 * jj + i] *= gelu_grad(h4[i]);
+      for (int e = 0; e < 16; ++e) v[e] += bv[t][e];
+      const int nb = n0 + f0 + t * 32;
+      if (J.epi == EPI_STORE && J.resid.base) {
+        const long long ro = row_off(J.resid, j, my_row) + nb + 4 * g;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const f32x4 r4 = J.resid_f32 ? load4<float>((const float *)J.resid.base + ro + 8 * jj)
+                                       : load4<T>((const T *)J.resid.base + ro + 8 * jj);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[4 * jj + e] += r4[e];
+        }
       }
-    }
-    // feature-major copy: lanes of a half-wave write 32 consecutive tokens of one feature
-    if (J.outT.base && tok_ok) {
-      T *dst = (T *)J.outT.base + j * J.outT.g + m0 + lc;
+      if (J.epi == EPI_DGELU) {
+        const long long ro = row_off(J.aux, j, my_row) + nb + 4 * g;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float y = J.epi == EPI_GELU ? gelu_as(v[e]) : v[e];
-        dst[(long long)(nb + acc_row(e, g)) * J.outT.ld] = from_f32<T>(y);
+        for (int jj = 0; jj < 4; ++jj) {
+          const f32x4 h4 = load4<T>((const T *)J.aux.base + ro + 8 * jj);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[4 * jj + e] *= gelu_grad_of<T>(h4[e]);
+        }
       }
-    }
-    // row-major output through the wave's LDS staging tile
-    if (J.out.base) {
-      const long long split_off = J.epi == EPI_PARTIAL ? split * J.part_split : 0;
-      auto store_rows = [&](auto tag) {
-        using U = decltype(tag);
-        using TS = TileStage<U>;
-        U *stg = reinterpret_cast<U *>(ring) + wave * TS::SIZE;
-        TS::put(stg, v, lc, g);
-        wait_lgkm0();
+      // feature-major copy through the wave's transposed staging tile [32 features][32 tokens]:
+      // each 16-byte store holds consecutive tokens of one feature
+      if (J.outT.base) {
+        constexpr int EPC = 16 / ESZ, LDT = 32 + EPC, PPF = 32 / EPC;
+        T *stT = reinterpret_cast<T *>(ring + 4 * TileStage<float>::SIZE * 4) + wave * 32 * LDT;
 #pragma unroll
-        for (int k = 0; k < TS::NI; ++k) {
-          const int m = m0 + TS::token(k, lane);
-          const u32x4 piece = TS::get(stg, k, lane);
-          if (m < J.m) st16((U *)J.out.base + split_off + row_off(J.out, j, m) + nb + TS::feature(lane), piece);
+        for (int e = 0; e < 16; ++e) {
+          const float y = J.epi == EPI_GELU ? gelu_of<T>(v[e]) : v[e];
+          stT[acc_row(e, g) * LDT + lc] = from_f32<T>(y);
         }
         wait_lgkm0();
-      };
-      if (J.epi == EPI_PARTIAL || J.out_f32) store_rows(0.0f);
-      else store_rows(T{});
+        T *dst = (T *)J.outT.base + j * J.outT.g + mi;
+#pragma unroll
+        for (int k = 0; k < 32 * PPF / 64; ++k) {
+          const int idx = k * 64 + lane, f = idx / PPF, r = (idx - f * PPF) * EPC;
+          const u32x4 piece = *(const u32x4 *)(stT + f * LDT + r);
+          T *d = dst + (long long)(nb + f) * J.outT.ld + r;
+          if (mi + r + EPC <= J.m) {
+            st16(d, piece);
+          } else {
+            const T *pe = (const T *)&piece;
+            for (int e = 0; e < EPC && mi + r + e < J.m; ++e) d[e] = pe[e];
+          }
+        }
+        wait_lgkm0();
+      }
+      // row-major output through the wave's LDS staging tile
+      if (J.out.base) {
+        const long long split_off = J.epi == EPI_PARTIAL ? split * J.part_split : 0;
+        auto store_rows = [&](auto tag) {
+          using U = decltype(tag);
+          using TS = TileStage<U>;
+          U *stg = reinterpret_cast<U *>(ring) + wave * TS::SIZE;
+          TS::put(stg, v, lc, g);
+          wait_lgkm0();
+#pragma unroll
+          for (int k = 0; k < TS::NI; ++k) {
+            const int m = mi + TS::token(k, lane);
+            const u32x4 piece = TS::get(stg, k, lane);
+            if (m < J.m) st16((U *)J.out.base + split_off + row_off(J.out, j, m) + nb + TS::feature(lane), piece);
+          }
+          wait_lgkm0();
+        };
+        if (J.epi == EPI_PARTIAL || J.out_f32) store_rows(0.0f);
+        else store_rows(T{});
+      }
     }
   }
 }
@@ -293,13 +353,30 @@ __global__ __launch_bounds__(256) void reduce_kernel(const RedArgs a) {
 
 }  // namespace
 
-int gemm_tokens_per_tile() { return GM_NW * 32; }
-int gemm_features_per_tile() { return GM_NT; }
+int gemm_tokens_per_tile() { return GM_TOK; }
+int gemm_features_per_tile() { return Narrow::FR; }
 
+// The plan counts Narrow tiles (64 features); when every job's feature rows are a multiple of 128
+// the launch uses the Wide layout with its own tile numbering.
 hipError_t launch_gemm(int dtype, const GemmArgs &a, int grid, hipStream_t s) {
   if (grid == 0) return hipSuccess;
-  if (dtype == 1) hipLaunchKernelGGL(gemm_kernel<bf16>, dim3(grid), dim3(GM_NW * 64), 0, s, a);
-  else hipLaunchKernelGGL(gemm_kernel<float>, dim3(grid), dim3(GM_NW * 64), 0, s, a);
+  bool wide = true;
+  for (int i = 0; i < a.n_jobs; ++i) wide &= a.job[i].n_feat % Wide::FR == 0;
+  if (wide) {
+    GemmArgs w = a;
+    long long tiles = 0;
+    for (int i = 0; i < w.n_jobs; ++i) {
+      GemmJob &J = w.job[i];
+      J.n_tiles = J.n_feat / Wide::FR;
+      J.tile0 = (int)tiles;
+      tiles += (long long)J.n_split * J.n_groups * J.m_tiles * J.n_tiles;
+    }
+    if (dtype == 1) hipLaunchKernelGGL((gemm_kernel<bf16, Wide>), dim3((unsigned)tiles), dim3(256), 0, s, w);
+    else hipLaunchKernelGGL((gemm_kernel<float, Wide>), dim3((unsigned)tiles), dim3(256), 0, s, w);
+  } else {
+    if (dtype == 1) hipLaunchKernelGGL((gemm_kernel<bf16, Narrow>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((gemm_kernel<float, Narrow>), dim3(grid), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
