@@ -7,15 +7,18 @@
 //   dK = dS^T Qs / log2(e),  dQ = dS K / sqrt(dh)
 // The probabilities are recomputed, never stored. Two kernels, each owning its outputs (no atomics):
 //   attn_dkdv_kernel: a workgroup per (sequence, head, 32 * ATTB_WAVES keys); a wave keeps its 32
-//     keys' K and V fragments in registers and walks the query tiles that can see them. Scores are
+//     keys' K and V fragments in registers and walks the 64-query tiles that can see them. Scores are
 //     formed as S = Qs K^T with queries as accumulator rows, so that P and dS (per lane: 16
 //     queries of one key) are already the B operand of dV^T += dO^T P and dK^T += Qs^T dS, whose
 //     contraction index is a permutation of the tile's 32 queries; dO^T and Qs^T are read from
 //     transposed LDS copies with the same permutation.
 //   attn_dq_kernel: a workgroup per (sequence, head, 32 * ATTB_WAVES queries); a wave keeps its 32
-//     queries' Qs and dO fragments in registers and walks the key tiles they can see, forming
+//     queries' Qs and dO fragments in registers and walks the 64-key tiles they can see, forming
 //     S^T = K Qs^T (keys as rows, one query per lane column, its lse and D in the lane), and
 //     dQ^T += K^T dS^T with K^T from a transposed LDS copy.
+// Both stage their shared tiles in two LDS buffers: the next tile's global loads are issued into
+// registers before the current tile is computed and written to the other buffer after it, so one
+// workgroup barrier per tile separates the two and the loads' latency hides behind the math.
 
 #include "bwd.hpp"
 
@@ -81,6 +84,16 @@ __device__ __forceinline__ void store_grad(const AttnBwdArgs &a, T *stg, const f
     const int c = acc_row(v, g);
     if (c < DH) dst[(long long)(h * DH + c) * ld] = from_f32<T>(acc[v]);
   }
+  // dK's call also writes the zero dQ^T of S keys before p0 (positions that issue no query): the
+  // weight gradient of W_Q contracts over every S token
+  if (which == 0 && tok_pos < a.p0) {
+    T *dq0 = (T *)a.tS[2] + (long long)b * a.s + tok_pos;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int c = acc_row(v, g);
+      if (c < DH) dq0[(long long)(h * DH + c) * ld] = from_f32<T>(0.0f);
+    }
+  }
 }
 
 template <typename T, int DH>
@@ -90,16 +103,20 @@ __global__ __launch_bounds__(ATTB_WAVES * 64) void attn_dkdv_kernel(const AttnBw
   using TS = TileStage<T>;
   constexpr int NW = ATTB_WAVES;
   constexpr int EPC = 16 / (int)sizeof(T);
-  constexpr int LDQ = DH + EPC;       // padded row of a [32][DH] tile
-  constexpr int LDT = 32 + EPC;       // padded row of a [DH][32] transposed tile
+  constexpr int QT = 64;              // queries per shared tile (two 32-query halves)
+  constexpr int LDQ = DH + EPC;       // padded row of a [QT][DH] tile
+  constexpr int LDT = QT + EPC;       // padded row of a [DH][QT] transposed tile
   constexpr int CPR = DH / EPC;       // 16-byte pieces per row
+  constexpr int NPT = (2 * QT * CPR + NW * 64 - 1) / (NW * 64);   // pieces per thread and tile
   constexpr int NK = DH / M::KSTEP;   // k-steps over the head dimension
   constexpr int MC = 32 / M::KSTEP;   // k-steps over 32 queries
-  __shared__ __attribute__((aligned(16))) T sQ[32 * LDQ];
-  __shared__ __attribute__((aligned(16))) T sO[32 * LDQ];
-  __shared__ __attribute__((aligned(16))) T sQt[DH * LDT];
-  __shared__ __attribute__((aligned(16))) T sOt[DH * LDT];
-  __shared__ float sL[32], sD[32];
+  // double-buffered tiles: Q and dO rows, their transposes, lse and D
+  __shared__ __attribute__((aligned(16))) T sQ[2][QT * LDQ];
+  __shared__ __attribute__((aligned(16))) T sO[2][QT * LDQ];
+  __shared__ __attribute__((aligned(16))) T sQt[2][DH * LDT];
+  __shared__ __attribute__((aligned(16))) T sOt[2][DH * LDT];
+  __shared__ __attribute__((aligned(16))) float sL[2][QT];
+  __shared__ __attribute__((aligned(16))) float sD[2][QT];
   __shared__ __attribute__((aligned(16))) T stage[NW][TS::SIZE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -125,59 +142,118 @@ __global__ __launch_bounds__(ATTB_WAVES * 64) void attn_dkdv_kernel(const AttnBw
   const float *lbase = a.lse + ((long long)b * H + h) * a.R;
   const float *dbase = a.dvec + ((long long)b * H + h) * a.R;
 
+  // a tile's global loads into registers (rows past R: zeros, lse +inf so that P = 0) ...
+  u32x4 reg[NPT];
+  float rl = 0.0f, rd = 0.0f;
+  auto gload = [&](int qt) {
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) {
+      const int ch = tid + k * NW * 64;
+      const int which = ch / (QT * CPR), rem = ch - which * (QT * CPR);
+      const int row = rem / CPR, c0 = (rem - row * CPR) * EPC;
+      const int i = qt + row;
+      reg[k] = u32x4{0, 0, 0, 0};
+      if (ch < 2 * QT * CPR && i < a.R)
+        reg[k] = which == 0 ? ld16(qbase + (long long)i * DH + c0) : ld16(obase + (long long)i * a.d_model + c0);
+    }
+    if (tid < QT) {
+      const int i = qt + tid;
+      rl = i < a.R ? lbase[i] : __builtin_inff();
+      rd = i < a.R ? dbase[i] : 0.0f;
+    }
+  };
+  // ... and from registers into LDS buffer `buf`, rows and transposes
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) {
+      const int ch = tid + k * NW * 64;
+      if (ch < 2 * QT * CPR) {
+        const int which = ch / (QT * CPR), rem = ch - which * (QT * CPR);
+        const int row = rem / CPR, c0 = (rem - row * CPR) * EPC;
+        T *rt = which == 0 ? sQ[buf] : sO[buf];
+        T *tt = which == 0 ? sQt[buf] : sOt[buf];
+        st16(&rt[row * LDQ + c0], reg[k]);
+        const T *ve = (const T *)&reg[k];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) tt[(c0 + e) * LDT + row] = ve[e];
+      }
+    }
+    if (tid < QT) {
+      sL[buf][tid] = rl;
+      sD[buf][tid] = rd;
+    }
+  };
+
   f32x16 dk = f32x16{}, dv = f32x16{};
   // first query that sees any key of the workgroup: position p0 + i >= kb * 32 * NW
   const int i_lo = max(0, kb * 32 * NW - a.p0);
-  for (int qt = (i_lo / 32) * 32; qt < a.R; qt += 32) {
+  const int qt0 = (i_lo / 32) * 32;
+  if (qt0 < a.R) {
+    gload(qt0);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int qt = qt0, it = 0; qt < a.R; qt += QT, ++it) {
+    const int buf = it & 1;
+    const bool more = qt + QT < a.R;
+    if (more) gload(qt + QT);   // in flight while this tile is computed
+#pragma unroll
+    for (int sub = 0; sub < QT / 32; ++sub) {
+      const int q0 = qt + sub * 32;
+      // (wave-uniform) no key of the wave, no query in this half, or every query of the half
+      // before the wave's first key
+      if (kw0 >= a.T || q0 >= a.R || kw0 > a.p0 + q0 + 31) continue;
+      // the accumulators start at -lse and -D of their query rows (acc_row(4 j + e, g) =
+      // 8 j + 4 g + e), so the products come out as exp2 arguments and dP - D
+      f32x16 s, dp;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 l4 = *(const f32x4 *)&sL[buf][sub * 32 + 8 * j + 4 * g];
+        const f32x4 d4 = *(const f32x4 *)&sD[buf][sub * 32 + 8 * j + 4 * g];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s[4 * j + e] = -l4[e];
+          dp[4 * j + e] = -d4[e];
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        const frag qa = *(const frag *)(&sQ[buf][(sub * 32 + lc) * LDQ + kk * M::KSTEP + g * M::KPL]);
+        const frag oa = *(const frag *)(&sO[buf][(sub * 32 + lc) * LDQ + kk * M::KSTEP + g * M::KPL]);
+        s = M::mma(qa, kf[kk], s);
+        dp = M::mma(oa, vf[kk], dp);
+      }
+      // query q0 + acc_row(v, g) sees key iff key <= p0 + q0 + acc_row(v, g): only the tiles that
+      // cross the diagonal need the mask (rows past R have lse = +inf, so P = 0 there; keys past
+      // T have zero K and V and their columns are never stored)
+      float p[16], ds[16];
+      if (kw0 + 31 <= a.p0 + q0) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          p[v] = __builtin_amdgcn_exp2f(s[v]);
+          ds[v] = p[v] * dp[v];
+        }
+      } else {
+        const int lim = key - a.p0 - q0;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          p[v] = acc_row(v, g) >= lim ? __builtin_amdgcn_exp2f(s[v]) : 0.0f;
+          ds[v] = p[v] * dp[v];
+        }
+      }
+      const T *ot_row = &sOt[buf][(lc < DH ? lc : 0) * LDT + sub * 32];
+      const T *qt_row = &sQt[buf][(lc < DH ? lc : 0) * LDT + sub * 32];
+#pragma unroll
+      for (int mc = 0; mc < MC; ++mc) {
+        const frag oa = lc < DH ? TrFrag<T>::load(ot_row, mc, g) : M::zero();
+        const frag qa = lc < DH ? TrFrag<T>::load(qt_row, mc, g) : M::zero();
+        dv = M::mma(oa, TrFrag<T>::from_acc(p, mc), dv);
+        dk = M::mma(qa, TrFrag<T>::from_acc(ds, mc), dk);
+      }
+    }
+    // the other buffer was last read in the previous iteration, before the barrier below it
+    if (more) lstore(buf ^ 1);
     __syncthreads();
-    for (int ch = tid; ch < 2 * 32 * CPR; ch += NW * 64) {
-      const int which = ch / (32 * CPR), rem = ch - which * (32 * CPR);
-      const int row = rem / CPR, c0 = (rem - row * CPR) * EPC;
-      const int i = qt + row;
-      u32x4 v = {0, 0, 0, 0};
-      if (i < a.R) v = which == 0 ? ld16(qbase + (long long)i * DH + c0) : ld16(obase + (long long)i * a.d_model + c0);
-      T *rt = which == 0 ? sQ : sO;
-      T *tt = which == 0 ? sQt : sOt;
-      st16(&rt[row * LDQ + c0], v);
-      const T *ve = (const T *)&v;
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) tt[(c0 + e) * LDT + row] = ve[e];
-    }
-    if (tid < 32) {
-      const int i = qt + tid;
-      sL[tid] = i < a.R ? lbase[i] : __builtin_inff();
-      sD[tid] = i < a.R ? dbase[i] : 0.0f;
-    }
-    __syncthreads();
-    // (wave-uniform) no key of the wave exists, or its first key lies past the tile's last query
-    if (kw0 >= a.T || kw0 > a.p0 + qt + 31) continue;
-    f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      const frag qa = *(const frag *)(&sQ[lc * LDQ + kk * M::KSTEP + g * M::KPL]);
-      const frag oa = *(const frag *)(&sO[lc * LDQ + kk * M::KSTEP + g * M::KPL]);
-      s = M::mma(qa, kf[kk], s);
-      dp = M::mma(oa, vf[kk], dp);
-    }
-    // query qt + acc_row(v, g) sees key iff key <= p0 + qt + acc_row(v, g)
-    const int lim = key - a.p0 - qt;
-    float p[16], ds[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = acc_row(v, g);
-      const bool vis = key_ok && r >= lim;
-      p[v] = vis ? __builtin_amdgcn_exp2f(s[v] - sL[r]) : 0.0f;
-      ds[v] = p[v] * (dp[v] - sD[r]);
-    }
-    const T *ot_row = &sOt[(lc < DH ? lc : 0) * LDT];
-    const T *qt_row = &sQt[(lc < DH ? lc : 0) * LDT];
-#pragma unroll
-    for (int mc = 0; mc < MC; ++mc) {
-      const frag oa = lc < DH ? TrFrag<T>::load(ot_row, mc, g) : M::zero();
-      const frag qa = lc < DH ? TrFrag<T>::load(qt_row, mc, g) : M::zero();
-      dv = M::mma(oa, TrFrag<T>::from_acc(p, mc), dv);
-      dk = M::mma(qa, TrFrag<T>::from_acc(ds, mc), dk);
-    }
   }
 #pragma unroll
   for (int v = 0; v < 16; ++v) dk[v] *= LN2;
@@ -192,15 +268,16 @@ __global__ __launch_bounds__(ATTB_WAVES * 64) void attn_dq_kernel(const AttnBwdA
   using TS = TileStage<T>;
   constexpr int NW = ATTB_WAVES;
   constexpr int EPC = 16 / (int)sizeof(T);
-  constexpr int KT = 64;              // keys per shared tile
+  constexpr int KT = 64;              // keys per shared tile (two 32-key halves)
   constexpr int LDK = DH + EPC;
   constexpr int LDT = KT + EPC;
   constexpr int CPR = DH / EPC;
+  constexpr int NPT = (2 * KT * CPR + NW * 64 - 1) / (NW * 64);
   constexpr int NK = DH / M::KSTEP;
   constexpr int MC = 32 / M::KSTEP;
-  __shared__ __attribute__((aligned(16))) T sK[KT * LDK];
-  __shared__ __attribute__((aligned(16))) T sV[KT * LDK];
-  __shared__ __attribute__((aligned(16))) T sKt[DH * LDT];
+  __shared__ __attribute__((aligned(16))) T sK[2][KT * LDK];
+  __shared__ __attribute__((aligned(16))) T sV[2][KT * LDK];
+  __shared__ __attribute__((aligned(16))) T sKt[2][DH * LDT];
   __shared__ __attribute__((aligned(16))) T stage[NW][TS::SIZE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -235,51 +312,84 @@ __global__ __launch_bounds__(ATTB_WAVES * 64) void attn_dq_kernel(const AttnBwdA
   const int wave_last = min(a.R, qw0 + 32) - 1;
   const int wave_max = qw0 < a.R ? a.p0 + wave_last : -1;
 
-  f32x16 dq = f32x16{};
-  for (int k0 = 0; k0 < n_keys; k0 += KT) {
-    __syncthreads();
-    for (int ch = tid; ch < 2 * KT * CPR; ch += NW * 64) {
+  u32x4 reg[NPT];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) {
+      const int ch = tid + k * NW * 64;
       const int which = ch / (KT * CPR), rem = ch - which * (KT * CPR);
       const int row = rem / CPR, c0 = (rem - row * CPR) * EPC;
       const int kg = k0 + row;
-      u32x4 v = {0, 0, 0, 0};
-      if (kg < n_keys) v = ld16((which == 0 ? kbase : vbase) + (long long)kg * DH + c0);
-      st16(&(which == 0 ? sK : sV)[row * LDK + c0], v);
-      if (which == 0) {
-        const T *ve = (const T *)&v;
+      reg[k] = u32x4{0, 0, 0, 0};
+      if (ch < 2 * KT * CPR && kg < n_keys) reg[k] = ld16((which == 0 ? kbase : vbase) + (long long)kg * DH + c0);
+    }
+  };
+  auto lstore = [&](int buf) {
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) sKt[(c0 + e) * LDT + row] = ve[e];
+    for (int k = 0; k < NPT; ++k) {
+      const int ch = tid + k * NW * 64;
+      if (ch < 2 * KT * CPR) {
+        const int which = ch / (KT * CPR), rem = ch - which * (KT * CPR);
+        const int row = rem / CPR, c0 = (rem - row * CPR) * EPC;
+        st16(&(which == 0 ? sK[buf] : sV[buf])[row * LDK + c0], reg[k]);
+        if (which == 0) {
+          const T *ve = (const T *)&reg[k];
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) sKt[buf][(c0 + e) * LDT + row] = ve[e];
+        }
       }
     }
-    __syncthreads();
+  };
+
+  f32x16 dq = f32x16{};
+  if (n_keys > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int k0 = 0, it = 0; k0 < n_keys; k0 += KT, ++it) {
+    const int buf = it & 1;
+    const bool more = k0 + KT < n_keys;
+    if (more) gload(k0 + KT);   // in flight while this tile is computed
 #pragma unroll
     for (int sub = 0; sub < KT / 32; ++sub) {
       const int kb = k0 + sub * 32;
-      if (kb >= n_keys || kb > wave_max) break;
-      f32x16 s = f32x16{}, dp = f32x16{};
+      if (kb >= n_keys || kb > wave_max) continue;   // wave-uniform
+      // accumulators start at -lse and -D of the lane's query
+      f32x16 s, dp;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        s[v] = -lse;
+        dp[v] = -dd;
+      }
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        const frag ka = *(const frag *)(&sK[(sub * 32 + lc) * LDK + kk * M::KSTEP + g * M::KPL]);
-        const frag va = *(const frag *)(&sV[(sub * 32 + lc) * LDK + kk * M::KSTEP + g * M::KPL]);
+        const frag ka = *(const frag *)(&sK[buf][(sub * 32 + lc) * LDK + kk * M::KSTEP + g * M::KPL]);
+        const frag va = *(const frag *)(&sV[buf][(sub * 32 + lc) * LDK + kk * M::KSTEP + g * M::KPL]);
         s = M::mma(ka, qf[kk], s);
         dp = M::mma(va, of[kk], dp);
       }
-      // key kb + acc_row(v, g) is visible iff it is at most min(qpos, n_keys - 1)
-      const int lim = min(qpos, n_keys - 1) - kb;
+      // key kb + acc_row(v, g) is visible iff it is at most qpos: only tiles that cross the
+      // diagonal need the mask (queries past R have lse = +inf, so P = 0; keys past n_keys have
+      // zero K rows, so they add nothing to dQ)
       float ds[16];
+      if (kb + 31 <= a.p0 + qw0) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const bool vis = q_ok && acc_row(v, g) <= lim;
-        const float p = vis ? __builtin_amdgcn_exp2f(s[v] - lse) : 0.0f;
-        ds[v] = p * (dp[v] - dd);
+        for (int v = 0; v < 16; ++v) ds[v] = __builtin_amdgcn_exp2f(s[v]) * dp[v];
+      } else {
+        const int lim = qpos - kb;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) ds[v] = acc_row(v, g) <= lim ? __builtin_amdgcn_exp2f(s[v]) * dp[v] : 0.0f;
       }
-      const T *kt_row = &sKt[(lc < DH ? lc : 0) * LDT + sub * 32];
+      const T *kt_row = &sKt[buf][(lc < DH ? lc : 0) * LDT + sub * 32];
 #pragma unroll
       for (int mc = 0; mc < MC; ++mc) {
         const frag ka = lc < DH ? TrFrag<T>::load(kt_row, mc, g) : M::zero();
         dq = M::mma(ka, TrFrag<T>::from_acc(ds, mc), dq);
       }
     }
+    if (more) lstore(buf ^ 1);
+    __syncthreads();
   }
   const float scale = 1.0f / sqrtf((float)DH);
 #pragma unroll

@@ -164,6 +164,7 @@ hipError_t launch_colsum(const float *colpart, int n_tiles, int d, float *dst_g,
 // Queries: q[b][h][i][dh] at positions p0 + i (i < R). Keys/values: k, v [b][h][t][dh] (t < T).
 // dO [b][i][d] rows. Outputs: dK, dV, dQ rows of dqkv [b][t][3d] (columns 0, d, 2d), and their
 // feature-major copies: position t < s is S token b * s + t, t >= s is NS group t - s token b.
+// The dQ copy holds zeros at the S positions before p0 (they issue no query; written with dK).
 // ---------------------------------------------------------------------------------------------
 struct AttnBwdArgs {
   int n_seq, n_heads, d_model;

@@ -1211,10 +1211,7 @@ int train_run(const Dims &D, const onetrans_config *cfg, const onetrans_block_we
       pads(dvT, (long long)B * s);
       pads(dqT, (long long)B * s);
       for (const FeatBuf *f : {&oT, &dyT, &yhT, &doutT, &dhpT, &hidT}) pads(*f, (long long)B * q);
-      // dQ of the rows that issue no query: dqkv columns [2d, 3d) and the S part of dQ^T
-      add(w + W.dqkv, (long long)T * 3 * d, 3 * d, B, p0, 2 * d, 3 * d);
-      add(dqT.S, dqT.ldS, s, d, B, 0, p0);
-      if (full) return ONETRANS_ERR_SHAPE;   // (not reached: 22 regions at most)
+      if (full) return ONETRANS_ERR_SHAPE;   // (not reached: 20 regions at most)
       if (!tm(ONETRANS_K_BWD_ROWS, [&] { return launch_fill(fa, stream); })) return ONETRANS_ERR_HIP;
     }
     // transposed weights: Wo^T, W1^T, W2^T and [Wk^T | Wv^T | Wq^T]
@@ -1439,8 +1436,30 @@ int train_run(const Dims &D, const onetrans_config *cfg, const onetrans_block_we
       if (!tm(ONETRANS_K_BWD_GEMM, [&] { return launch_gemm(dt, P.a, (int)P.tiles, stream); })) return ONETRANS_ERR_HIP;
       if (!tm(ONETRANS_K_BWD_GEMM, [&] { return launch_reduce(ra, stream); })) return ONETRANS_ERR_HIP;
     }
-    // dXh = [dK | dV | dQ] [Wk; Wv; Wq] over all rows (fp32)
-    if (!act_gemm(DQKV, WcT, d, 3 * d, 0, s, EPI_STORE, nullptr, nullptr, nullptr, &DXH, true, nullptr)) return ONETRANS_ERR_HIP;
+    // dXh = [dK | dV | dQ] [Wk; Wv; Wq] over all rows (fp32); the S rows before p0 issue no query,
+    // so their contraction stops after [dK | dV] (their dQ columns are never written)
+    {
+      GemmPlan P;
+      plan_init(P);
+      for (int part = 0; part < 3; ++part) {
+        GemmJob j;
+        memset(&j, 0, sizeof(j));
+        const bool ns = part == 2;
+        const int t0 = part == 0 ? 0 : p0, cnt = part == 0 ? p0 : q;
+        j.a = ns ? rows_N(DQKV, s) : rows_S(DQKV, t0, cnt);
+        j.b = w_set(WcT, ns);
+        j.m = ns ? B : B * cnt;
+        j.n_feat = d;
+        j.k_len = part == 0 ? 2 * d : 3 * d;
+        j.n_groups = ns ? L : 1;
+        j.n_split = 1;
+        j.epi = EPI_STORE;
+        j.out = ns ? rows_N(DXH, s) : rows_S(DXH, t0, cnt);
+        j.out_f32 = 1;
+        plan_add(P, j);
+      }
+      if (!tm(ONETRANS_K_BWD_GEMM, [&] { return launch_gemm(dt, P.a, (int)P.tiles, stream); })) return ONETRANS_ERR_HIP;
+    }
     {   // dX = Norm1'(dXh) + dY on the tail rows: the lower block's d_out (fp32 rows, storage rows,
         // feature-major), or dX(0); dg1 / db1 column partials
       RowsArgs ra;
