@@ -21,24 +21,40 @@ namespace ot {
 namespace {
 
 constexpr int GM_CB = 128;     // bytes of k per row and chunk
-constexpr int GM_NB = 2;       // chunk buffers
 constexpr int GM_TOK = 128;    // token-operand rows per workgroup (both layouts)
 
 // Wave layouts of a 4-wave workgroup: WGM x WGN waves, each computing TM x TN accumulator tiles of
 // 32 x 32 (TM token tiles, TN feature tiles). Narrow: 4 x 1 waves of 1 x 2 tiles (128 tokens x 64
 // features; every feature fragment read feeds one MFMA). Wide: 2 x 2 waves of 2 x 2 tiles
 // (128 x 128; every fragment read feeds two MFMAs).
-template <int TM_, int TN_, int WGM_, int WGN_>
+template <int TM_, int TN_, int WGM_, int WGN_, int NB_>
 struct Layout {
   static constexpr int TM = TM_, TN = TN_, WGM = WGM_, WGN = WGN_;
+  static constexpr int NB = NB_;             // chunk buffers: NB - 1 chunks in flight
   static constexpr int FR = 32 * TN * WGN;   // feature rows per workgroup
   static constexpr int TR = 32 * TM * WGM;   // token rows per workgroup
   static constexpr int STAGE = (FR + TR) * GM_CB;
   static constexpr int LOADS = (FR + TR) * 8 / 256;   // 16-byte direct loads per thread and chunk
   static_assert(WGM * WGN == 4 && TR == GM_TOK, "4 waves, 128 token rows");
+  static_assert(NB >= 2 && NB <= 4, "chunk buffers");
 };
-using Narrow = Layout<1, 2, 4, 1>;
-using Wide = Layout<2, 2, 2, 2>;
+// Two chunk buffers: measured on the OneTransS training step, three or four buffers (fewer
+// workgroups per CU) made the contractions 12-58 % slower.
+using Narrow = Layout<1, 2, 4, 1, 2>;
+using Wide = Layout<2, 2, 2, 2, 2>;
+
+// Wait until chunk c's direct loads have landed: the loads of the chunks issued after it (at most
+// NB - 2, fewer near the end) may stay outstanding.
+template <typename LY>
+__device__ __forceinline__ void wait_chunk(int after) {
+  if constexpr (LY::NB >= 4) {
+    if (after >= 2) { wait_vm<2 * LY::LOADS>(); return; }
+  }
+  if constexpr (LY::NB >= 3) {
+    if (after >= 1) { wait_vm<LY::LOADS>(); return; }
+  }
+  wait_vm<0>();
+}
 
 __device__ __forceinline__ uint32_t slot_byte(int r, int p) { return (uint32_t)(r * 8 + (p ^ (r & 7))) * 16u; }
 
@@ -108,9 +124,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
   constexpr int EPP = 16 / ESZ;               // elements per 16-byte piece
   constexpr int SPP = EPP / MM::KPL;          // MFMA k-steps per piece (bf16: 1, fp32: 4)
   constexpr int TM = LY::TM, TN = LY::TN;
-  static_assert(4 * TileStage<float>::SIZE * 4 + 4 * 32 * (32 + 16 / ESZ) * ESZ <= GM_NB * LY::STAGE,
+  static_assert(4 * TileStage<float>::SIZE * 4 + 4 * 32 * (32 + 16 / ESZ) * ESZ <= LY::NB * LY::STAGE,
                 "row-major and feature-major staging fit in the ring");
-  __shared__ __attribute__((aligned(16))) char ring[GM_NB * LY::STAGE];
+  __shared__ __attribute__((aligned(16))) char ring[LY::NB * LY::STAGE];
 
   const int tile = xcd_tile((int)blockIdx.x, (int)gridDim.x);
   int ji = 0;
@@ -157,7 +173,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
   }
   const uint32_t ring_lds = lds_addr(ring);
   auto issue = [&](int c) {
-    const uint32_t st = ring_lds + (uint32_t)((c % GM_NB) * LY::STAGE);
+    const uint32_t st = ring_lds + (uint32_t)((c % LY::NB) * LY::STAGE);
     const uint32_t cb = (uint32_t)c * GM_CB;
 #pragma unroll
     for (int i = 0; i < LY::LOADS; ++i) {
@@ -190,14 +206,16 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
 #pragma unroll
     for (int t = 0; t < TN; ++t) acc[i][t] = f32x16{};
 
-  if (n_chunks > 0) issue(0);
+#pragma unroll
+  for (int c = 0; c < LY::NB - 1; ++c)
+    if (c < n_chunks) issue(c);
   for (int c = 0; c < n_chunks; ++c) {
-    wait_vm<0>();
+    wait_chunk<LY>(min(LY::NB - 2, n_chunks - 1 - c));
     wait_lgkm0();
-    bare_barrier();
-    if (c + 1 < n_chunks) issue(c + 1);
+    bare_barrier();   // every wave's loads of chunk c have landed; chunk c - 1's buffer is free
+    if (c + LY::NB - 1 < n_chunks) issue(c + LY::NB - 1);
 
-    const char *st = ring + (c % GM_NB) * LY::STAGE;
+    const char *st = ring + (c % LY::NB) * LY::STAGE;
     const char *xs = st + LY::FR * GM_CB;
     u32x4 xb[4][TM], wa[4][TN];
 #pragma unroll

@@ -215,7 +215,7 @@ def main() -> None:
                           f"{mf['MfmaUtil']:.1f} %",
                           f"- VALUBusy (vector ALUs busy): {mf['VALUBusy']:.1f} %",
                           f"- MFMA flops executed per dispatch: {mf['mfma_flops_per_dispatch'] / 1e9:.2f} GFLOP"]
-                if alg:
+                if alg and float(alg) > 0:
                     lines.append(f"- algorithmic flops per dispatch: {float(alg) / 1e9:.2f} GFLOP "
                                  f"(executed / algorithmic = {mf['mfma_flops_per_dispatch'] / float(alg):.3f})")
                 lines.append("")
