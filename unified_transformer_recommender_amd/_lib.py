@@ -6,7 +6,9 @@ import ctypes
 import os
 from ctypes import POINTER, c_char_p, c_float, c_int, c_size_t, c_void_p
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libonetrans.so")
+# The in-tree build; ONETRANS_LIB names another build of the same sources (the host-sanitized
+# library of the CPU tests).
+LIB_PATH = os.environ.get("ONETRANS_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libonetrans.so")
 
 OK = 0
 ERR_INVALID_ARG = -1

@@ -67,5 +67,42 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """The shared AddressSanitizer runtime a process must preload to load the sanitized library."""
+    r = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return r.stdout.strip()
+
+
+def build_host_sanitized() -> str:
+    """A copy of the library whose host code (the C ABI's validation and the planner in
+    onetrans.hip) is built with AddressSanitizer and UndefinedBehaviorSanitizer; device code is
+    not instrumented. Written to _build/asan/libonetrans.so; the other objects come from build()."""
+    out_dir = os.path.join(BUILD, "asan")
+    os.makedirs(out_dir, exist_ok=True)
+    planner = os.path.join(CSRC, "onetrans.hip")
+    others = [s for s in sources() if s != planner]
+    objs = [os.path.join(BUILD, os.path.basename(s) + ".o") for s in others]
+    if not all(os.path.exists(o) for o in objs):
+        os.makedirs(BUILD, exist_ok=True)
+        with ThreadPoolExecutor(max_workers=min(8, len(others))) as ex:
+            objs = list(ex.map(_compile, others))
+    obj = os.path.join(out_dir, "onetrans.hip.o")
+    cmd = [hipcc(), *[f for f in FLAGS if f != "-O3"], "-O1", "-g", *SANITIZE, "-c", planner, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("sanitized compile failed:\n" + r.stderr)
+    lib = os.path.join(out_dir, "libonetrans.so")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *SANITIZE, "-Xarch_host", "-shared-libsan",
+           "-o", lib, *objs, obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("sanitized link failed:\n" + r.stderr)
+    return lib
+
+
 if __name__ == "__main__":
     build(verbose=True)
