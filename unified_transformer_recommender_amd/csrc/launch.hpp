@@ -27,6 +27,10 @@ int post_tokens_per_tile(int dtype, int d_model);
 hipError_t launch_post_reduce(const PostArgs &a, int rows, hipStream_t s);
 constexpr int POST_MAX_SPLIT = 8;        // hidden-chunk ranges per token tile at most
 constexpr long long POST_SPLIT_BYTES = 32ll << 20;   // partials buffer at most (fp32, POST_MAX_SPLIT copies)
+// bf16 storage at d = 512, unsplit launches: the wave-pair post-attention kernel (128 tokens per
+// workgroup tile, like post_kernel's).
+hipError_t launch_post_pair(int resid_f32, const PostArgs &a, int grid, hipStream_t s);
+int post_pair_tokens_per_tile(int d_model);
 // fp32 storage at d = 512: the post-attention kernel on 16x16x4 MFMA tiles (16 tokens per wave).
 hipError_t launch_post_f32w(int d_model, const PostArgs &a, int grid, hipStream_t s);
 int post_f32w_tokens_per_tile();

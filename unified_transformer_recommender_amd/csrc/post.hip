@@ -489,6 +489,8 @@ hipError_t launch_dls(const PostArgs &a, int grid, hipStream_t s) {
 template <typename T, typename TR, int D>
 hipError_t launch_dl(const PostArgs &a, int tiles, hipStream_t s) {
   if (a.n_split > 1) return launch_dls<T, TR, D, true>(a, tiles * a.n_split, s);
+  // bf16 at d = 512: the wave-pair kernel (same 128-token tiles, no register spills)
+  if constexpr (sizeof(T) == 2 && D == 512) return launch_post_pair(sizeof(TR) == 4, a, tiles, s);
   return launch_dls<T, TR, D, false>(a, tiles, s);
 }
 

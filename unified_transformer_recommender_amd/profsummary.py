@@ -28,15 +28,16 @@ from typing import Dict, List, Optional, Tuple
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 
-# kernel class -> (substrings of the kernel symbols, source file)
+# kernel class -> (substrings of the kernel symbols, source files)
 KERNELS = {
-    "qkv": (("qkv_kernel",), "qkv.hip"),
-    "attn": (("attn_kernel", "attn_split_kernel"), "attn.hip"),
-    "post": (("post_kernel", "post_reduce_kernel", "post_f32w_kernel"), "post.hip"),
-    "lin": (("lin_kernel",), "tok.hip"),
-    "bwd_gemm": (("gemm_kernel", "reduce_kernel"), "gemm.hip"),
-    "bwd_attn": (("attn_dkdv_kernel", "attn_dq_kernel"), "attn_bwd.hip"),
-    "bwd_rows": (("rows_kernel", "colsum_kernel", "transpose_kernel", "fill_kernel"), "rows.hip"),
+    "qkv": (("qkv_kernel",), ("qkv.hip",)),
+    "attn": (("attn_kernel", "attn_split_kernel"), ("attn.hip",)),
+    "post": (("post_kernel", "post_reduce_kernel", "post_f32w_kernel", "post_pair_kernel"),
+             ("post.hip", "post_f32w.hip", "post_pair.hip")),
+    "lin": (("lin_kernel",), ("tok.hip",)),
+    "bwd_gemm": (("gemm_kernel", "reduce_kernel"), ("gemm.hip",)),
+    "bwd_attn": (("attn_dkdv_kernel", "attn_dq_kernel"), ("attn_bwd.hip",)),
+    "bwd_rows": (("rows_kernel", "colsum_kernel", "transpose_kernel", "fill_kernel"), ("rows.hip",)),
 }
 COPY_KERNEL = "neg"
 MFMA_COUNTERS = ("MfmaUtil", "VALUBusy")
@@ -51,9 +52,9 @@ def classify(name: str) -> Optional[str]:
 
 
 def source_sha256(kernel: str) -> str:
-    """Hash of the kernel's source file together with the shared device header."""
+    """Hash of the kernel class's source files together with the shared device header."""
     h = hashlib.sha256()
-    for f in (KERNELS[kernel][1], "common.hpp"):
+    for f in (*KERNELS[kernel][1], "common.hpp"):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
