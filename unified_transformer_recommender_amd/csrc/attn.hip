@@ -87,15 +87,18 @@ __device__ __forceinline__ f32x16 score_tile(const T *krow, const typename Mma<T
   return s;
 }
 
-// One 32-key tile: fold the scores s (base-2 units, -inf where invisible) into the running state.
+// One 32-key tile: fold the scores (base-2 units, -inf where invisible) into the running state.
+// `scores()` forms the tile's masked scores from LDS; it is called once on the common path, and
+// once more on the rare rescale path instead of keeping the 16 score registers alive across the
+// tile (which lets the kernel fit 64 registers and eight waves per SIMD).
 // The probabilities are first taken against the running maximum m as it stands. Any one of them
 // above 2^RESCALE_HEADROOM makes the lane's tile sum exceed that bound too, so the tile maximum is
 // only searched (and the state rescaled, the probabilities retaken) when some lane's sum does: on
 // the first tile (m starts far below every score) and when the scores climb by more than the
 // headroom. A tile whose sum crosses the bound with no single probability above it costs one
 // needless rescale, which changes nothing in the result.
-template <typename T, int DH>
-__device__ __forceinline__ void softmax_pv(const f32x16 &s, SoftmaxState &st,
+template <typename T, int DH, typename Scores>
+__device__ __forceinline__ void softmax_pv(const Scores &scores, SoftmaxState &st,
                                            const T *vt_row /* this lane's V^T row, or null if lc >= DH */,
                                            int g) {
   using M = Mma<T>;
@@ -104,7 +107,7 @@ __device__ __forceinline__ void softmax_pv(const f32x16 &s, SoftmaxState &st,
   frag pf[MC];
   float tsum;
   // probabilities of the tile against the current maximum, as the P.V operand, and their sum
-  auto take = [&]() {
+  auto take = [&](const f32x16 &s, bool again) {
     float p[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(s[v] - st.m);
@@ -123,11 +126,18 @@ __device__ __forceinline__ void softmax_pv(const f32x16 &s, SoftmaxState &st,
         tsum += pf[mc];
       }
     }
+    // distinct (empty) markers keep the two uses of this block apart: otherwise the compiler merges
+    // their common tail after the branch and keeps the fp32 probabilities alive across it
+    if (again) asm volatile("; retake" ::); else asm volatile("; take" ::);
   };
-  take();
+  take(scores(), false);
   constexpr float BOUND = 256.0f;   // 2^RESCALE_HEADROOM
   static_assert(RESCALE_HEADROOM == 8.0f, "bound is 2^headroom");
   if (__any(!(tsum <= BOUND))) {    // wave-uniform; also catches an infinite sum
+    // rare: the scores are formed again from LDS rather than kept in registers through the
+    // common path
+    asm volatile("" ::: "memory");
+    const f32x16 s = scores();
     float mt = s[0];
 #pragma unroll
     for (int v = 1; v < 15; v += 2) mt = fmaxf(fmaxf(mt, s[v]), s[v + 1]);   // three-operand max
@@ -139,7 +149,7 @@ __device__ __forceinline__ void softmax_pv(const f32x16 &s, SoftmaxState &st,
     st.lsum *= alpha;
 #pragma unroll
     for (int v = 0; v < 16; ++v) st.o[v] *= alpha;
-    take();
+    take(s, true);
   }
   st.lsum += tsum;
 #pragma unroll
@@ -149,8 +159,10 @@ __device__ __forceinline__ void softmax_pv(const f32x16 &s, SoftmaxState &st,
   }
 }
 
+// Register budget of eight waves per SIMD (64 registers at bf16 storage, no spills): four 8-wave
+// workgroups per CU hide each other's barrier and LDS waits (measured 6 % faster than six waves).
 template <typename T, int DH, bool STAGE2>
-__global__ __launch_bounds__(ATTN_WAVES * 64) void attn_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(ATTN_WAVES * 64) __attribute__((amdgpu_waves_per_eu(8, 8))) void attn_kernel(const AttnArgs a) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int EPC = 16 / (int)sizeof(T);
@@ -167,7 +179,7 @@ __global__ __launch_bounds__(ATTN_WAVES * 64) void attn_kernel(const AttnArgs a)
   using TS = TileStage<T>;
   __shared__ __attribute__((aligned(16))) T stage[NWA][TS::SIZE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, lc = lane & 31;
   const int H = a.n_heads;
   // Work order. Workgroups are dispatched round-robin over the 8 XCDs (block b runs on XCD b % 8),
@@ -256,18 +268,21 @@ __global__ __launch_bounds__(ATTN_WAVES * 64) void attn_kernel(const AttnArgs a)
       const int kb = k0 + sub * 32;
       if (kb >= n_keys) break;
       if (!STAGE2 && kb > wave_max) break;
-      f32x16 s = score_tile<T, DH>(&sK[(sub * 32 + lc) * LDK + g * M::KPL], qf);
       const bool need_mask = STAGE2 ? (kb + 32 > n_keys) : (kb + 31 > wave_min || kb + 32 > n_keys);
-      if (need_mask) {
-        // key kb + acc_row(v, g) is visible iff it is at most min(qpos, n_keys - 1) (Stage II: no
-        // causal limit within the prefix); compare element v's constant row offset with one
-        // per-lane bound
-        const int lim = (STAGE2 ? n_keys - 1 : min(qpos, n_keys - 1)) - kb - 4 * g;
+      auto scores = [&]() {
+        f32x16 s = score_tile<T, DH>(&sK[(sub * 32 + lc) * LDK + g * M::KPL], qf);
+        if (need_mask) {
+          // key kb + acc_row(v, g) is visible iff it is at most min(qpos, n_keys - 1) (Stage II:
+          // no causal limit within the prefix); compare element v's constant row offset with one
+          // per-lane bound
+          const int lim = (STAGE2 ? n_keys - 1 : min(qpos, n_keys - 1)) - kb - 4 * g;
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (acc_row(v, 0) > lim) s[v] = NEG_INF;
-      }
-      softmax_pv<T, DH>(s, st, lc < DH ? &sVt[lc * LDV + sub * 32] : nullptr, g);
+          for (int v = 0; v < 16; ++v)
+            if (acc_row(v, 0) > lim) s[v] = NEG_INF;
+        }
+        return s;
+      };
+      softmax_pv<T, DH>(scores, st, lc < DH ? &sVt[lc * LDV + sub * 32] : nullptr, g);
     }
   }
 
@@ -292,15 +307,18 @@ __global__ __launch_bounds__(ATTN_WAVES * 64) void attn_kernel(const AttnArgs a)
       for (int e = 0; e < EPC; ++e) vw[(c0 + e) * LDW + ks] = ve[e];
     }
     __syncthreads();
-    f32x16 s = score_tile<T, DH>(&kw[lc * LDK + g * M::KPL], qf);
+    auto scores = [&]() {
+      f32x16 s = score_tile<T, DH>(&kw[lc * LDK + g * M::KPL], qf);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int ks = acc_row(v, g);
-      const int kc = ks / a.R, j2 = ks - kc * a.R;
-      const bool vis = ks < n_own && kc == cslot && j2 <= qi && c_first + kc < a.n_cand;
-      if (!vis) s[v] = NEG_INF;
-    }
-    softmax_pv<T, DH>(s, st, lc < DH ? &vw[lc * LDW] : nullptr, g);
+      for (int v = 0; v < 16; ++v) {
+        const int ks = acc_row(v, g);
+        const int kc = ks / a.R, j2 = ks - kc * a.R;
+        const bool vis = ks < n_own && kc == cslot && j2 <= qi && c_first + kc < a.n_cand;
+        if (!vis) s[v] = NEG_INF;
+      }
+      return s;
+    };
+    softmax_pv<T, DH>(scores, st, lc < DH ? &vw[lc * LDW] : nullptr, g);
   }
 
   // ---- normalise and store O[b][i][h*dh + c] through the wave's LDS staging tile ---------------
@@ -354,7 +372,7 @@ __global__ __launch_bounds__(ATTN_WAVES * 64) void attn_split_kernel(const AttnA
   float (*s_l)[32] = (float (*)[32])(smem + NWA * (16 * 64 + 32) * 4);
   T *stage = (T *)(smem + NWA * (16 * 64 + 64) * 4);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, lc = lane & 31;
   const int H = a.n_heads;
   const int pair = blockIdx.x;
@@ -431,15 +449,18 @@ __global__ __launch_bounds__(ATTN_WAVES * 64) void attn_split_kernel(const AttnA
     store();
     if (sub + 1 < sub1) load(sub + 1);
     wait_lgkm0();                              // the tile is in LDS (only this wave reads it)
-    f32x16 s = score_tile<T, DH>(&kw[lc * LDK + g * M::KPL], qf);
     const int kb = sub * 32;
-    if ((!STAGE2 && kb + 31 > p0) || kb + 32 > n_keys) {
-      const int lim = (STAGE2 ? n_keys - 1 : min(qpos, n_keys - 1)) - kb - 4 * g;
+    auto scores = [&]() {
+      f32x16 s = score_tile<T, DH>(&kw[lc * LDK + g * M::KPL], qf);
+      if ((!STAGE2 && kb + 31 > p0) || kb + 32 > n_keys) {
+        const int lim = (STAGE2 ? n_keys - 1 : min(qpos, n_keys - 1)) - kb - 4 * g;
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        if (acc_row(v, 0) > lim) s[v] = NEG_INF;
-    }
-    softmax_pv<T, DH>(s, st, lc < DH ? &vw[lc * LDW] : nullptr, g);
+        for (int v = 0; v < 16; ++v)
+          if (acc_row(v, 0) > lim) s[v] = NEG_INF;
+      }
+      return s;
+    };
+    softmax_pv<T, DH>(scores, st, lc < DH ? &vw[lc * LDW] : nullptr, g);
   }
 
   // ---- Stage II: the candidates' own NS keys (block-diagonal causal), on the last wave --------
@@ -462,14 +483,17 @@ __global__ __launch_bounds__(ATTN_WAVES * 64) void attn_split_kernel(const AttnA
       wait_lgkm0();
       store();
       wait_lgkm0();
-      f32x16 s = score_tile<T, DH>(&kw[lc * LDK + g * M::KPL], qf);
+      auto scores = [&]() {
+        f32x16 s = score_tile<T, DH>(&kw[lc * LDK + g * M::KPL], qf);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int ks = acc_row(v, g);
-        const int kc = ks / a.R, j2 = ks - kc * a.R;
-        if (!(ks < n_own && kc == cslot && j2 <= qi)) s[v] = NEG_INF;
-      }
-      softmax_pv<T, DH>(s, st, lc < DH ? &vw[lc * LDW] : nullptr, g);
+        for (int v = 0; v < 16; ++v) {
+          const int ks = acc_row(v, g);
+          const int kc = ks / a.R, j2 = ks - kc * a.R;
+          if (!(ks < n_own && kc == cslot && j2 <= qi)) s[v] = NEG_INF;
+        }
+        return s;
+      };
+      softmax_pv<T, DH>(scores, st, lc < DH ? &vw[lc * LDW] : nullptr, g);
     }
   }
 
