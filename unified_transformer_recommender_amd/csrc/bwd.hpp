@@ -37,7 +37,9 @@ struct MatT {
 // Epilogues:
 //   STORE   out(j, r)[n] = C (+ bias[j][n]) (+ resid(j, r)[n]); fp32 or storage dtype; plus outT
 //   GELU    out = C + bias (storage dtype, the pre-activation); outT = GELU(C + bias)
-//   DGELU   v = C * GELU'(aux(j, r)[n]); out = v (storage dtype) and outT = v
+//   DGELU   v = C * GELU'(Z(j, r, n)); out = v (storage dtype) and outT = v, where the
+//           pre-activation Z = sum_k A2(j, r)[k] * B2(j, n)[k] + bias(j)[n] over k in [0, k_len2) is
+//           formed by a first contraction of the same shape into registers (not read from memory)
 //           (GELU: the erf form with fp32 storage; with bf16 storage the fitted form the bf16
 //           forward evaluates, and its exact derivative)
 //   PARTIAL out(j, r)[n] at out.base + split * part_split: the split's fp32 partial sum; with
@@ -52,9 +54,9 @@ struct GemmJob {
   int n_split;
   int tile0, m_tiles, n_tiles;   // tiles = n_split * n_groups * m_tiles * n_tiles
   int epi;
-  const void *bias; long long bias_g;   // storage dtype [group][n_feat], or null
+  const void *bias; long long bias_g;   // storage dtype [group][n_feat], or null (DGELU: Z's bias)
   Mat2 resid; int resid_f32;            // STORE: rows added to C (base null: none)
-  Mat2 aux;                             // DGELU: pre-activation rows (storage dtype)
+  Mat2 a2, b2; int k_len2;              // DGELU: the pre-activation's operands (no split)
   Mat2 out; int out_f32;                // row-major output (base null: none)
   MatT outT;                            // feature-major output, storage dtype (base null: none)
   long long part_split;                 // PARTIAL: elements between splits

@@ -14,6 +14,11 @@
 //
 // Split contraction: a job may cut k into n_split contiguous chunk ranges, each workgroup writing
 // its fp32 partial; launch_reduce sums them in a fixed order (results do not depend on timing).
+//
+// The GELU-derivative product runs two contractions through the same chunk ring: first the
+// pre-activation Z = A2 B2^T + bias of its output tile, kept in registers as GELU'(Z), then the main
+// product. The FFN's pre-activation rows thus never go to memory: its output is as wide as the
+// hidden layer, and writing and re-reading it cost more than forming it again on the matrix units.
 
 #include "bwd.hpp"
 
@@ -149,40 +154,6 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
   const int m0 = mw0 + wm * 32 * TM;          // this wave's first token row
   const int f0 = wn * 32 * TN;                // this wave's first feature row within the tile
 
-  const int n_all = J.k_len / KC;
-  const int per = (n_all + J.n_split - 1) / J.n_split;
-  const int c_lo = min(n_all, split * per), c_hi = min(n_all, c_lo + per);
-  const int n_chunks = c_hi - c_lo;
-
-  // direct-to-LDS loads: instruction i of wave w covers stage slots [(4 i + w) 64, + 64); slot s
-  // holds piece (s % 8) ^ (row & 7) of stage row s / 8 (feature rows first, then token rows; a
-  // token row past the end re-reads the last row, whose results are never stored)
-  const long long wrow0 = row_off(J.b, j, n0), xrow0 = row_off(J.a, j, mw0);
-  const char *wsrc = (const char *)J.b.base + (wrow0 + (long long)c_lo * KC) * ESZ;
-  const char *xsrc = (const char *)J.a.base + (xrow0 + (long long)c_lo * KC) * ESZ;
-  uint32_t off[LY::LOADS];
-#pragma unroll
-  for (int i = 0; i < LY::LOADS; ++i) {
-    const int s = (4 * i + wave) * 64 + lane, r = s / 8, p = (s % 8) ^ (r & 7);
-    if (r < LY::FR) {
-      off[i] = (uint32_t)((row_off(J.b, j, n0 + r) - wrow0) * ESZ + p * 16);
-    } else {
-      const int row = min(mw0 + r - LY::FR, J.m - 1);
-      off[i] = (uint32_t)((row_off(J.a, j, row) - xrow0) * ESZ + p * 16);
-    }
-  }
-  const uint32_t ring_lds = lds_addr(ring);
-  auto issue = [&](int c) {
-    const uint32_t st = ring_lds + (uint32_t)((c % LY::NB) * LY::STAGE);
-    const uint32_t cb = (uint32_t)c * GM_CB;
-#pragma unroll
-    for (int i = 0; i < LY::LOADS; ++i) {
-      const bool feat = (4 * i + wave) * 8 < LY::FR;   // wave-uniform: 8 rows per instruction
-      dma16s(feat ? (const void *)wsrc : (const void *)xsrc, off[i] + cb,
-             __builtin_amdgcn_readfirstlane(st + (uint32_t)((4 * i + wave) * 1024)));
-    }
-  };
-
   // bias of this lane's accumulator rows, loaded before the first direct-to-LDS load
   float bv[TN][16] = {};
   if (J.bias) {
@@ -201,65 +172,114 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
   asm volatile("" ::: "memory");
 
   f32x16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int t = 0; t < TN; ++t) acc[i][t] = f32x16{};
+  const uint32_t ring_lds = lds_addr(ring);
 
+  // acc = sum over chunks [c_lo, c_lo + n_chunks) of A's token rows times Bw's feature rows (the
+  // chunk ring starts empty and is free again when this returns)
+  auto contract = [&](const Mat2 &A, const Mat2 &Bw, int c_lo, int n_chunks, bool rs) {
 #pragma unroll
-  for (int c = 0; c < LY::NB - 1; ++c)
-    if (c < n_chunks) issue(c);
-  for (int c = 0; c < n_chunks; ++c) {
-    wait_chunk<LY>(min(LY::NB - 2, n_chunks - 1 - c));
-    wait_lgkm0();
-    bare_barrier();   // every wave's loads of chunk c have landed; chunk c - 1's buffer is free
-    if (c + LY::NB - 1 < n_chunks) issue(c + LY::NB - 1);
-
-    const char *st = ring + (c % LY::NB) * LY::STAGE;
-    const char *xs = st + LY::FR * GM_CB;
-    u32x4 xb[4][TM], wa[4][TN];
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+      for (int t = 0; t < TN; ++t) acc[i][t] = f32x16{};
+    // direct-to-LDS loads: instruction i of wave w covers stage slots [(4 i + w) 64, + 64); slot s
+    // holds piece (s % 8) ^ (row & 7) of stage row s / 8 (feature rows first, then token rows; a
+    // token row past the end re-reads the last row, whose results are never stored)
+    const long long wrow0 = row_off(Bw, j, n0), xrow0 = row_off(A, j, mw0);
+    const char *wsrc = (const char *)Bw.base + (wrow0 + (long long)c_lo * KC) * ESZ;
+    const char *xsrc = (const char *)A.base + (xrow0 + (long long)c_lo * KC) * ESZ;
+    uint32_t off[LY::LOADS];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) xb[q][i] = *(const u32x4 *)(xs + slot_byte(wm * 32 * TM + i * 32 + lc, 4 * g + q));
-#pragma unroll
-      for (int t = 0; t < TN; ++t) wa[q][t] = *(const u32x4 *)(st + slot_byte(f0 + t * 32 + lc, 4 * g + q));
+    for (int i = 0; i < LY::LOADS; ++i) {
+      const int s = (4 * i + wave) * 64 + lane, r = s / 8, p = (s % 8) ^ (r & 7);
+      if (r < LY::FR) {
+        off[i] = (uint32_t)((row_off(Bw, j, n0 + r) - wrow0) * ESZ + p * 16);
+      } else {
+        const int row = min(mw0 + r - LY::FR, J.m - 1);
+        off[i] = (uint32_t)((row_off(A, j, row) - xrow0) * ESZ + p * 16);
+      }
     }
+    auto issue = [&](int c) {
+      const uint32_t st = ring_lds + (uint32_t)((c % LY::NB) * LY::STAGE);
+      const uint32_t cb = (uint32_t)c * GM_CB;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+      for (int i = 0; i < LY::LOADS; ++i) {
+        const bool feat = (4 * i + wave) * 8 < LY::FR;   // wave-uniform: 8 rows per instruction
+        dma16s(feat ? (const void *)wsrc : (const void *)xsrc, off[i] + cb,
+               __builtin_amdgcn_readfirstlane(st + (uint32_t)((4 * i + wave) * 1024)));
+      }
+    };
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+    for (int c = 0; c < LY::NB - 1; ++c)
+      if (c < n_chunks) issue(c);
+    for (int c = 0; c < n_chunks; ++c) {
+      wait_chunk<LY>(min(LY::NB - 2, n_chunks - 1 - c));
+      wait_lgkm0();
+      bare_barrier();   // every wave's loads of chunk c have landed; chunk c - 1's buffer is free
+      if (c + LY::NB - 1 < n_chunks) issue(c + LY::NB - 1);
+
+      const char *st = ring + (c % LY::NB) * LY::STAGE;
+      const char *xs = st + LY::FR * GM_CB;
+      u32x4 xb[4][TM], wa[4][TN];
 #pragma unroll
-        for (int t = 0; t < TN; ++t) {
-          if constexpr (ESZ == 2) {
-            acc[i][t] = MM::mma(__builtin_bit_cast(bf16x8, wa[q][t]), __builtin_bit_cast(bf16x8, xb[q][i]), acc[i][t]);
-          } else {
-            const f32x4 af = __builtin_bit_cast(f32x4, wa[q][t]), bf = __builtin_bit_cast(f32x4, xb[q][i]);
+      for (int q = 0; q < 4; ++q) {
 #pragma unroll
-            for (int e = 0; e < SPP; ++e) acc[i][t] = MM::mma(af[e], bf[e], acc[i][t]);
-          }
-        }
-    sched_lds_mfma<4 * (TM + TN), 4 * TM * TN * SPP, 6>();
-    if (rowsum) {
+        for (int i = 0; i < TM; ++i) xb[q][i] = *(const u32x4 *)(xs + slot_byte(wm * 32 * TM + i * 32 + lc, 4 * g + q));
+#pragma unroll
+        for (int t = 0; t < TN; ++t) wa[q][t] = *(const u32x4 *)(st + slot_byte(f0 + t * 32 + lc, 4 * g + q));
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          if constexpr (ESZ == 2) {
-            const bf16x8 v = __builtin_bit_cast(bf16x8, xb[q][i]);
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) rsum[i] += (float)v[e];
-          } else {
-            const f32x4 v = __builtin_bit_cast(f32x4, xb[q][i]);
-            rsum[i] += (v[0] + v[1]) + (v[2] + v[3]);
+          for (int t = 0; t < TN; ++t) {
+            if constexpr (ESZ == 2) {
+              acc[i][t] = MM::mma(__builtin_bit_cast(bf16x8, wa[q][t]), __builtin_bit_cast(bf16x8, xb[q][i]), acc[i][t]);
+            } else {
+              const f32x4 af = __builtin_bit_cast(f32x4, wa[q][t]), bf = __builtin_bit_cast(f32x4, xb[q][i]);
+#pragma unroll
+              for (int e = 0; e < SPP; ++e) acc[i][t] = MM::mma(af[e], bf[e], acc[i][t]);
+            }
           }
-        }
+      sched_lds_mfma<4 * (TM + TN), 4 * TM * TN * SPP, 6>();
+      if (rs) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+            if constexpr (ESZ == 2) {
+              const bf16x8 v = __builtin_bit_cast(bf16x8, xb[q][i]);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) rsum[i] += (float)v[e];
+            } else {
+              const f32x4 v = __builtin_bit_cast(f32x4, xb[q][i]);
+              rsum[i] += (v[0] + v[1]) + (v[2] + v[3]);
+            }
+          }
+      }
     }
+    wait_lgkm0();
+    bare_barrier();   // every wave is done with the ring
+  };
+
+  // DGELU: the gate GELU'(Z) from a first contraction (the pre-activation never goes to memory)
+  f32x16 gate[TM][TN];
+  if (J.epi == EPI_DGELU) {
+    contract(J.a2, J.b2, 0, J.k_len2 / KC, false);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) gate[i][t][e] = gelu_grad_of<T>(acc[i][t][e] + bv[t][e]);
   }
 
-  // ---- epilogue ----------------------------------------------------------------------------
-  wait_lgkm0();
-  bare_barrier();   // every wave is done with the ring; it becomes the staging area
+  const int n_all = J.k_len / KC;
+  const int per = (n_all + J.n_split - 1) / J.n_split;
+  const int c_lo = min(n_all, split * per), c_hi = min(n_all, c_lo + per);
+  contract(J.a, J.b, c_lo, c_hi - c_lo, rowsum);
+
+  // ---- epilogue (the ring becomes the staging area) -------------------------------------------
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int mi = m0 + i * 32;               // first token row of this accumulator tile
@@ -271,8 +291,10 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
       f32x16 v = acc[i][t];
+      if (J.epi != EPI_DGELU) {   // (DGELU: the bias belongs to the pre-activation)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) v[e] += bv[t][e];
+        for (int e = 0; e < 16; ++e) v[e] += bv[t][e];
+      }
       const int nb = n0 + f0 + t * 32;
       if (J.epi == EPI_STORE && J.resid.base) {
         const long long ro = row_off(J.resid, j, my_row) + nb + 4 * g;
@@ -285,13 +307,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
         }
       }
       if (J.epi == EPI_DGELU) {
-        const long long ro = row_off(J.aux, j, my_row) + nb + 4 * g;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const f32x4 h4 = load4<T>((const T *)J.aux.base + ro + 8 * jj);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[4 * jj + e] *= gelu_grad_of<T>(h4[e]);
-        }
+        for (int e = 0; e < 16; ++e) v[e] *= gate[i][t][e];
       }
       // feature-major copy through the wave's transposed staging tile [32 features][32 tokens]:
       // each 16-byte store holds consecutive tokens of one feature

@@ -18,6 +18,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <utility>
 #include <vector>
 
 #include "onetrans.h"
@@ -867,8 +868,9 @@ int first_pruning_block(const int *q, int N, int l_s) {
 // last to first, with s S rows in, q kept, T = s + l_ns rows, R = q + l_ns query rows, p0 = s - q:
 //   recompute  xh^T = Norm1(X) (feature-major), Q/K/V and O with each query's log-sum-exp (the
 //              forward's QKV and attention kernels), Y = X[tail] + O Wo^T, yh = Norm2(Y),
-//              hpre = yh W1^T + b1 and hid^T = GELU(hpre)
-//   backward   dhpre = (dOut W2) * GELU'(hpre); dW2 += dOut^T hid, db2 += dOut; dW1 += dhpre^T yh,
+//              hid^T = GELU(hpre) with hpre = yh W1^T + b1 (hpre itself is not stored)
+//   backward   dhpre = (dOut W2) * GELU'(hpre), hpre formed again in registers by the same kernel;
+//              dW2 += dOut^T hid, db2 += dOut; dW1 += dhpre^T yh,
 //              db1 += dhpre; dYh = dhpre W1; dY = Norm2'(dYh) + dOut; dO = dY Wo; dWo += dY^T O;
 //              attention backward -> dK, dV, dQ; dWq/k/v += d{Q,K,V}^T Xh;
 //              dXh = dK Wk + dV Wv + dQ Wq; dX = Norm1'(dXh) + dY on the tail rows
@@ -998,7 +1000,7 @@ void wgrad_jobs(GemmPlan &P, RedArgs *R, const Dims &D, const FeatBuf &A, const 
 struct TrainWs {
   Ws fw;                      // the forward kernels' buffers (q, k, v, o, trash)
   std::vector<size_t> ckpt;   // [N]: block n's input rows (n >= 1), fp32 [B][T_n][d]
-  size_t lse, dvec, y, yh, hpre, dhpre, dyh, dy32, dyt, dout_t, d_o, dqkv, dxh, dx32;
+  size_t lse, dvec, y, yh, dhpre, dyh, dy32, dyt, dout_t, d_o, dqkv, dxh, dx32;
   size_t xhT, dkT, dvT, dqT, oT, dyT, yhT, dhpreT, hidT, doutT;
   size_t woT, w1T, w2T, wcT;
   size_t part, rsum, colpart, colsum2;
@@ -1033,7 +1035,6 @@ TrainWs train_layout(const Dims &D, const onetrans_config *cfg, int B, int l_s) 
   w.dvec = take(rowsR * D.H * 4);
   w.y = take(rowsR * d * 4);
   w.yh = take(rowsR * d * es);
-  w.hpre = take(rowsR * dff * es);
   w.dhpre = take(rowsR * dff * es);
   w.dyh = take(rowsR * d * 4);
   w.dy32 = take(rowsR * d * 4);
@@ -1171,7 +1172,7 @@ int train_run(const Dims &D, const onetrans_config *cfg, const onetrans_block_we
     const RowBuf X{(char *)xv.base, x_f32 ? 4u : es, xv.sb, d, 0};
     // block-local buffers: tail rows [B][R][*] at positions p0.., all rows [B][T][*]
     auto tail = [&](size_t off, size_t esz, int width) { return RowBuf{w + off, esz, (long long)R * width, width, p0}; };
-    const RowBuf Ob = tail(W.fw.o, es, d), Yb = tail(W.y, 4, d), YHb = tail(W.yh, es, d), HPb = tail(W.hpre, es, dff),
+    const RowBuf Ob = tail(W.fw.o, es, d), Yb = tail(W.y, 4, d), YHb = tail(W.yh, es, d),
                  DHPb = tail(W.dhpre, es, dff), DYHb = tail(W.dyh, 4, d), DY32 = tail(W.dy32, 4, d),
                  DYt = tail(W.dyt, es, d), DOt = tail(W.dout_t, es, d), DOb = tail(W.d_o, es, d);
     const RowBuf DOUT32 = n == N - 1 ? RowBuf{(char *)d_out, 4, (long long)R * d, d, p0} : tail(W.dx32, 4, d);
@@ -1263,9 +1264,10 @@ int train_run(const Dims &D, const onetrans_config *cfg, const onetrans_block_we
       return tiles;
     };
     // mixed product over the S rows [t0, t0 + cnt) (set 0) and the NS rows (sets 1..l_ns)
+    // pre (EPI_DGELU): the pre-activation's operands, rows of pre->first times pre->second (k = d)
     auto act_gemm = [&](const RowBuf &A, const WBuf &Wb, int n_feat, int k_len, int t0, int cnt, int epi,
-                        const void *bias, const RowBuf *resid, const RowBuf *aux, const RowBuf *outb, bool out_f32,
-                        const FeatBuf *outT) {
+                        const void *bias, const RowBuf *resid, const std::pair<const RowBuf *, const WBuf *> *pre,
+                        const RowBuf *outb, bool out_f32, const FeatBuf *outT) {
       GemmPlan P;
       plan_init(P);
       for (int ns = 0; ns < 2; ++ns) {
@@ -1287,7 +1289,11 @@ int train_run(const Dims &D, const onetrans_config *cfg, const onetrans_block_we
           j.resid = ns ? rows_N(*resid, s) : rows_S(*resid, t0, cnt);
           j.resid_f32 = resid->esz == 4;
         }
-        if (aux) j.aux = ns ? rows_N(*aux, s) : rows_S(*aux, t0, cnt);
+        if (pre) {
+          j.a2 = ns ? rows_N(*pre->first, s) : rows_S(*pre->first, t0, cnt);
+          j.b2 = w_set(*pre->second, ns);
+          j.k_len2 = d;
+        }
         if (outb) {
           j.out = ns ? rows_N(*outb, s) : rows_S(*outb, t0, cnt);
           j.out_f32 = out_f32;
@@ -1326,8 +1332,8 @@ int train_run(const Dims &D, const onetrans_config *cfg, const onetrans_block_we
       ra.out_t = view(YHb);
       if (rows_launch(ra, p0, q, &yhT) < 0) return ONETRANS_ERR_HIP;
     }
-    // hpre = yh W1^T + b1 (rows), hid^T = GELU(hpre) (feature-major)
-    if (!act_gemm(YHb, W1, dff, d, p0, q, EPI_GELU, wt.b1, nullptr, nullptr, &HPb, false, &hidT)) return ONETRANS_ERR_HIP;
+    // hid^T = GELU(yh W1^T + b1) (feature-major only: the backward forms the pre-activation again)
+    if (!act_gemm(YHb, W1, dff, d, p0, q, EPI_GELU, wt.b1, nullptr, nullptr, nullptr, false, &hidT)) return ONETRANS_ERR_HIP;
 
     // ---- backward ----
     if (n == N - 1) {   // the caller's d_out: storage-dtype rows and feature-major copy
@@ -1339,8 +1345,12 @@ int train_run(const Dims &D, const onetrans_config *cfg, const onetrans_block_we
       ra.out_t = view(DOt);
       if (rows_launch(ra, p0, q, &doutT) < 0) return ONETRANS_ERR_HIP;
     }
-    // dhpre = (dOut W2) * GELU'(hpre): rows and feature-major
-    if (!act_gemm(DOt, W2T, dff, d, p0, q, EPI_DGELU, nullptr, nullptr, &HPb, &DHPb, false, &dhpT)) return ONETRANS_ERR_HIP;
+    // dhpre = (dOut W2) * GELU'(yh W1^T + b1), the pre-activation formed in registers: rows and
+    // feature-major
+    {
+      const std::pair<const RowBuf *, const WBuf *> pre{&YHb, &W1};
+      if (!act_gemm(DOt, W2T, dff, d, p0, q, EPI_DGELU, wt.b1, nullptr, &pre, &DHPb, false, &dhpT)) return ONETRANS_ERR_HIP;
+    }
     {   // dW2, db2, dW1, db1
       GemmPlan P;
       plan_init(P);
