@@ -14,9 +14,12 @@
 // query (its column) and the softmax statistics of that query stay in the lane (one cross-half
 // swap per tile). The probabilities are then already laid out as the B operand of
 // O^T += V^T P^T: the k index of that product is a permutation of the 32 keys, and the V^T
-// operand is read with the same permutation from an LDS copy of V stored transposed
-// ([d_head][key]). K/V tiles of 16 * ATTN_WAVES keys are staged in LDS once per workgroup and
-// shared by all its waves.
+// operand is read with the same permutation. K/V tiles of 16 * ATTN_WAVES keys are staged in LDS
+// once per workgroup and shared by all its waves. bf16 at d_head 32 (the OneTrans shapes): both
+// tiles row-major, brought in by direct global->LDS loads into two buffers one tile ahead (one
+// barrier per tile, no staging registers), V^T fragments read from the row-major V tile by the
+// transposing LDS read. Other storage types and head sizes stage through registers, with V
+// stored transposed ([d_head][key]).
 //
 // Online softmax in base 2: queries arrive multiplied by log2(e)/sqrt(dh), so a probability is
 // exp2 of the score minus the running maximum. For bf16 the row sums are packed bf16 dot products
@@ -53,6 +56,34 @@ template <> struct VtFrag<bf16> {
 template <> struct VtFrag<float> {
   static __device__ __forceinline__ float load(const float *row, int mc, int g) { return row[acc_row(mc, g)]; }
   static __device__ __forceinline__ float pfrag(const float *p, int mc) { return p[mc]; }
+};
+
+// P.V operand fragment k-chunk mc of this lane from a transposed V^T tile: vt_row is the lane's
+// V^T row (feature lc), or null when lc >= DH (zero rows of the product).
+template <typename T, int DH>
+struct VtRow {
+  const T *vt_row;
+  int g;
+  __device__ __forceinline__ typename Mma<T>::frag operator()(int mc) const {
+    return (DH == 32 || vt_row) ? VtFrag<T>::load(vt_row, mc, g) : Mma<T>::zero();
+  }
+};
+
+// The same fragment (bf16, d_head 32) from a row-major V tile [key][32] by the transposing LDS
+// read: in each 16-lane group, lane i receives element i % 4 of the 8-byte runs that lanes i / 4,
+// 4 + i / 4, 8 + i / 4 and 12 + i / 4 point at. Source lane s of the group holding output lanes
+// (features 16 h .. 16 h + 15, lane half g) points at V[k0 + 4 g + s / 4][16 h + 4 (s % 4)], so
+// output lane (lc, g) gets keys k0 + 4 g + 0..3 of feature lc: the first four k elements of the
+// fragment; a second read at k0 + 8 gives the other four.
+struct VRowTr {
+  const bf16 *v;   // this lane's source address for key offset 0 of subtile k-chunk 0
+  __device__ __forceinline__ bf16x8 operator()(int mc) const {
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s4 lds_s4;
+    const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(v + 16 * mc * 32));
+    const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(v + (16 * mc + 8) * 32));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
 };
 
 // The value x of the lane in the other half of the wave (lane ^ 32), by one cross-half swap.
@@ -97,10 +128,8 @@ __device__ __forceinline__ f32x16 score_tile(const T *krow, const typename Mma<T
 // the first tile (m starts far below every score) and when the scores climb by more than the
 // headroom. A tile whose sum crosses the bound with no single probability above it costs one
 // needless rescale, which changes nothing in the result.
-template <typename T, int DH, typename Scores>
-__device__ __forceinline__ void softmax_pv(const Scores &scores, SoftmaxState &st,
-                                           const T *vt_row /* this lane's V^T row, or null if lc >= DH */,
-                                           int g) {
+template <typename T, int DH, typename Scores, typename VFrag>
+__device__ __forceinline__ void softmax_pv(const Scores &scores, SoftmaxState &st, const VFrag &vfrag) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int MC = 32 / M::KSTEP;
@@ -154,15 +183,15 @@ __device__ __forceinline__ void softmax_pv(const Scores &scores, SoftmaxState &s
   st.lsum += tsum;
 #pragma unroll
   for (int mc = 0; mc < MC; ++mc) {
-    frag vf = (DH == 32 || vt_row) ? VtFrag<T>::load(vt_row, mc, g) : M::zero();
-    st.o = M::mma(vf, pf[mc], st.o);
+    st.o = M::mma(vfrag(mc), pf[mc], st.o);
   }
 }
 
-// Register budget of eight waves per SIMD (64 registers at bf16 storage, no spills): four 8-wave
+// bf16: a register budget of eight waves per SIMD (64 registers, no spills), so that four 8-wave
 // workgroups per CU hide each other's barrier and LDS waits (measured 6 % faster than six waves).
+// fp32 storage (the parity mode) keeps the compiler's own budget.
 template <typename T, int DH, bool STAGE2>
-__global__ __launch_bounds__(ATTN_WAVES * 64) __attribute__((amdgpu_waves_per_eu(8, 8))) void attn_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(ATTN_WAVES * 64, sizeof(T) == 2 ? 8 : 1) void attn_kernel(const AttnArgs a) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int EPC = 16 / (int)sizeof(T);
@@ -172,12 +201,21 @@ __global__ __launch_bounds__(ATTN_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   constexpr int LDV = KT + EPC;      // padded V^T row (keys)
   constexpr int LDW = 32 + EPC;      // padded V^T row of a wave's own-key tile
   constexpr int CPK = DH / EPC;      // 16-byte chunks per key row
-  __shared__ __attribute__((aligned(16))) T sK[KT * LDK];
-  __shared__ __attribute__((aligned(16))) T sVt[DH * LDV];
+  // bf16 at d_head 32: K and V tiles row-major ([key][32], K's 16-byte pieces XOR-swizzled) in two
+  // buffers filled by direct global->LDS loads one tile ahead; V read by the transposing LDS read.
+  // Otherwise one buffer filled through registers: K row-major with padded rows, V transposed
+  // ([d_head][key], padded rows). After the key loop the same bytes hold the output staging tiles.
+  constexpr bool TRV = sizeof(T) == 2 && DH == 32;
+  using TS = TileStage<T>;
+  constexpr int KBUF = TRV ? KT * DH : KT * LDK, VBUF = TRV ? KT * DH : DH * LDV, NBUF = TRV ? 2 : 1;
+  constexpr int TILE_BYTES = NBUF * (KBUF + VBUF) * (int)sizeof(T);
+  constexpr int STAGE_BYTES = NWA * TS::SIZE * (int)sizeof(T);
+  __shared__ __attribute__((aligned(16))) unsigned char smem[TILE_BYTES > STAGE_BYTES ? TILE_BYTES : STAGE_BYTES];
+  T *const sK = (T *)smem;                 // [NBUF][KBUF]
+  T *const sVt = sK + NBUF * KBUF;         // [NBUF][VBUF]
+  T (*stage)[TS::SIZE] = (T (*)[TS::SIZE])smem;
   __shared__ __attribute__((aligned(16))) T sKw[STAGE2 ? NWA * 32 * LDK : EPC];
   __shared__ __attribute__((aligned(16))) T sVw[STAGE2 ? NWA * DH * LDW : EPC];
-  using TS = TileStage<T>;
-  __shared__ __attribute__((aligned(16))) T stage[NWA][TS::SIZE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, lc = lane & 31;
@@ -247,42 +285,88 @@ __global__ __launch_bounds__(ATTN_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   st.lsum = 0.0f;
   st.o = f32x16{};
 
-  for (int k0 = 0; k0 < n_keys; k0 += KT) {
-    __syncthreads();
-    for (int ch = tid; ch < KT * CPK; ch += NWA * 64) {
-      const int key = ch / CPK, c0 = (ch - key * CPK) * EPC;
-      const int kg = k0 + key;
-      u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-      if (kg < n_keys) {
-        kv = ld16(kp + (long long)kg * DH + c0);
-        vv = ld16(vp + (long long)kg * DH + c0);
+  if constexpr (TRV) {
+    // thread tid loads piece tid % 4 of key row tid / 4 of a tile, K's piece into slot
+    // piece ^ ((key >> 2) & 3) (the 32 rows of a score fragment read then touch every bank once)
+    const int dkey = tid >> 2, dslot = tid & 3;
+    const uint32_t kpiece = (uint32_t)((dslot ^ ((dkey >> 2) & 3)) * 16), vpiece = (uint32_t)(dslot * 16);
+    const uint32_t kl = lds_addr(sK), vl = lds_addr(sVt);
+    auto issue = [&](int k0, int b) {
+      const uint32_t row = (uint32_t)min(k0 + dkey, n_keys - 1) * (uint32_t)(DH * sizeof(T));   // rows past the end repeat the last (masked)
+      const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(b * KBUF * (int)sizeof(T)) + (uint32_t)wave * 1024u);
+      dma16s(kp, row + kpiece, kl + dst);
+      dma16s(vp, row + vpiece, vl + dst);
+    };
+    if (n_keys > 0) issue(0, 0);
+    int buf = 0;
+    for (int k0 = 0; k0 < n_keys; k0 += KT, buf ^= 1) {
+      wait_vm<0>();     // this wave's loads of tile k0 have landed
+      wait_lgkm0();     // and its reads of the other buffer are done
+      bare_barrier();
+      if (k0 + KT < n_keys) issue(k0 + KT, buf ^ 1);
+      const T *kt = sK + buf * KBUF, *vt = sVt + buf * VBUF;
+#pragma unroll
+      for (int sub = 0; sub < KT / 32; ++sub) {
+        const int kb = k0 + sub * 32;
+        if (kb >= n_keys) break;
+        if (!STAGE2 && kb > wave_max) break;
+        const bool need_mask = STAGE2 ? (kb + 32 > n_keys) : (kb + 31 > wave_min || kb + 32 > n_keys);
+        auto scores = [&]() {
+          const int key = sub * 32 + lc, sw = (key >> 2) & 3;
+          f32x16 s = f32x16{};
+#pragma unroll
+          for (int kk = 0; kk < DH / M::KSTEP; ++kk)
+            s = M::mma(*(const frag *)(kt + key * DH + 8 * ((2 * kk + g) ^ sw)), qf[kk], s);
+          if (need_mask) {
+            const int lim = (STAGE2 ? n_keys - 1 : min(qpos, n_keys - 1)) - kb - 4 * g;
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              if (acc_row(v, 0) > lim) s[v] = NEG_INF;
+          }
+          return s;
+        };
+        const int src = (sub * 32 + 4 * g + ((lane >> 2) & 3)) * DH + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        softmax_pv<T, DH>(scores, st, VRowTr{(const bf16 *)(vt + src)});
       }
-      st16(&sK[key * LDK + c0], kv);
-      const T *ve = (const T *)&vv;
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) sVt[(c0 + e) * LDV + key] = ve[e];
     }
-    __syncthreads();
-#pragma unroll
-    for (int sub = 0; sub < KT / 32; ++sub) {
-      const int kb = k0 + sub * 32;
-      if (kb >= n_keys) break;
-      if (!STAGE2 && kb > wave_max) break;
-      const bool need_mask = STAGE2 ? (kb + 32 > n_keys) : (kb + 31 > wave_min || kb + 32 > n_keys);
-      auto scores = [&]() {
-        f32x16 s = score_tile<T, DH>(&sK[(sub * 32 + lc) * LDK + g * M::KPL], qf);
-        if (need_mask) {
-          // key kb + acc_row(v, g) is visible iff it is at most min(qpos, n_keys - 1) (Stage II:
-          // no causal limit within the prefix); compare element v's constant row offset with one
-          // per-lane bound
-          const int lim = (STAGE2 ? n_keys - 1 : min(qpos, n_keys - 1)) - kb - 4 * g;
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (acc_row(v, 0) > lim) s[v] = NEG_INF;
+  } else {
+    for (int k0 = 0; k0 < n_keys; k0 += KT) {
+      __syncthreads();
+      for (int ch = tid; ch < KT * CPK; ch += NWA * 64) {
+        const int key = ch / CPK, c0 = (ch - key * CPK) * EPC;
+        const int kg = k0 + key;
+        u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+        if (kg < n_keys) {
+          kv = ld16(kp + (long long)kg * DH + c0);
+          vv = ld16(vp + (long long)kg * DH + c0);
         }
-        return s;
-      };
-      softmax_pv<T, DH>(scores, st, lc < DH ? &sVt[lc * LDV + sub * 32] : nullptr, g);
+        st16(&sK[key * LDK + c0], kv);
+        const T *ve = (const T *)&vv;
+  #pragma unroll
+        for (int e = 0; e < EPC; ++e) sVt[(c0 + e) * LDV + key] = ve[e];
+      }
+      __syncthreads();
+  #pragma unroll
+      for (int sub = 0; sub < KT / 32; ++sub) {
+        const int kb = k0 + sub * 32;
+        if (kb >= n_keys) break;
+        if (!STAGE2 && kb > wave_max) break;
+        const bool need_mask = STAGE2 ? (kb + 32 > n_keys) : (kb + 31 > wave_min || kb + 32 > n_keys);
+        auto scores = [&]() {
+          f32x16 s = score_tile<T, DH>(&sK[(sub * 32 + lc) * LDK + g * M::KPL], qf);
+          if (need_mask) {
+            // key kb + acc_row(v, g) is visible iff it is at most min(qpos, n_keys - 1) (Stage II:
+            // no causal limit within the prefix); compare element v's constant row offset with one
+            // per-lane bound
+            const int lim = (STAGE2 ? n_keys - 1 : min(qpos, n_keys - 1)) - kb - 4 * g;
+  #pragma unroll
+            for (int v = 0; v < 16; ++v)
+              if (acc_row(v, 0) > lim) s[v] = NEG_INF;
+          }
+          return s;
+        };
+        softmax_pv<T, DH>(scores, st, VtRow<T, DH>{lc < DH ? &sVt[lc * LDV + sub * 32] : nullptr, g});
+      }
     }
   }
 
@@ -318,7 +402,7 @@ __global__ __launch_bounds__(ATTN_WAVES * 64) __attribute__((amdgpu_waves_per_eu
       }
       return s;
     };
-    softmax_pv<T, DH>(scores, st, lc < DH ? &vw[lc * LDW] : nullptr, g);
+    softmax_pv<T, DH>(scores, st, VtRow<T, DH>{lc < DH ? &vw[lc * LDW] : nullptr, g});
   }
 
   // ---- normalise and store O[b][i][h*dh + c] through the wave's LDS staging tile ---------------
@@ -328,6 +412,7 @@ __global__ __launch_bounds__(ATTN_WAVES * 64) __attribute__((amdgpu_waves_per_eu
   f32x16 o = st.o;
 #pragma unroll
   for (int v = 0; v < 16; ++v) o[v] *= inv;
+  __syncthreads();   // every wave is done with the K / V tiles the staging tiles overlay
   T *stg = stage[wave];
   TS::put(stg, o, lc, g);
 #pragma unroll
@@ -460,7 +545,7 @@ __global__ __launch_bounds__(ATTN_WAVES * 64) void attn_split_kernel(const AttnA
       }
       return s;
     };
-    softmax_pv<T, DH>(scores, st, lc < DH ? &vw[lc * LDW] : nullptr, g);
+    softmax_pv<T, DH>(scores, st, VtRow<T, DH>{lc < DH ? &vw[lc * LDW] : nullptr, g});
   }
 
   // ---- Stage II: the candidates' own NS keys (block-diagonal causal), on the last wave --------
@@ -493,7 +578,7 @@ __global__ __launch_bounds__(ATTN_WAVES * 64) void attn_split_kernel(const AttnA
         }
         return s;
       };
-      softmax_pv<T, DH>(scores, st, lc < DH ? &vw[lc * LDW] : nullptr, g);
+      softmax_pv<T, DH>(scores, st, VtRow<T, DH>{lc < DH ? &vw[lc * LDW] : nullptr, g});
     }
   }
 
