@@ -70,20 +70,10 @@ struct VtRow {
 };
 
 // The same fragment (bf16, d_head 32) from a row-major V tile [key][32] by the transposing LDS
-// read: in each 16-lane group, lane i receives element i % 4 of the 8-byte runs that lanes i / 4,
-// 4 + i / 4, 8 + i / 4 and 12 + i / 4 point at. Source lane s of the group holding output lanes
-// (features 16 h .. 16 h + 15, lane half g) points at V[k0 + 4 g + s / 4][16 h + 4 (s % 4)], so
-// output lane (lc, g) gets keys k0 + 4 g + 0..3 of feature lc: the first four k elements of the
-// fragment; a second read at k0 + 8 gives the other four.
+// read (tr_frag); v = tile + tr_src<32>(first key of the subtile, lane).
 struct VRowTr {
-  const bf16 *v;   // this lane's source address for key offset 0 of subtile k-chunk 0
-  __device__ __forceinline__ bf16x8 operator()(int mc) const {
-    typedef short s4 __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) s4 lds_s4;
-    const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(v + 16 * mc * 32));
-    const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(v + (16 * mc + 8) * 32));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-  }
+  const bf16 *v;
+  __device__ __forceinline__ bf16x8 operator()(int mc) const { return tr_frag<32>(v, mc); }
 };
 
 // The value x of the lane in the other half of the wave (lane ^ 32), by one cross-half swap.
@@ -325,8 +315,7 @@ __global__ __launch_bounds__(ATTN_WAVES * 64, sizeof(T) == 2 ? 8 : 1) void attn_
           }
           return s;
         };
-        const int src = (sub * 32 + 4 * g + ((lane >> 2) & 3)) * DH + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-        softmax_pv<T, DH>(scores, st, VRowTr{(const bf16 *)(vt + src)});
+        softmax_pv<T, DH>(scores, st, VRowTr{(const bf16 *)vt + tr_src<32>(sub * 32, lane)});
       }
     }
   } else {

@@ -16,6 +16,8 @@
 //     queries' Qs and dO fragments in registers and walks the 64-key tiles they can see, forming
 //     S^T = K Qs^T (keys as rows, one query per lane column, its lse and D in the lane), and
 //     dQ^T += K^T dS^T with K^T from a transposed LDS copy.
+// bf16 at d_head 32: the transposed operands (dO^T, Qs^T, K^T) are read from the row-major tiles by
+// the transposing LDS read, so no transposed copy is written.
 // Both stage their shared tiles in two LDS buffers: the next tile's global loads are issued into
 // registers before the current tile is computed and written to the other buffer after it, so one
 // workgroup barrier per tile separates the two and the loads' latency hides behind the math.
@@ -110,11 +112,13 @@ __global__ __launch_bounds__(ATTB_WAVES * 64) void attn_dkdv_kernel(const AttnBw
   constexpr int NPT = (2 * QT * CPR + NW * 64 - 1) / (NW * 64);   // pieces per thread and tile
   constexpr int NK = DH / M::KSTEP;   // k-steps over the head dimension
   constexpr int MC = 32 / M::KSTEP;   // k-steps over 32 queries
-  // double-buffered tiles: Q and dO rows, their transposes, lse and D
+  // double-buffered tiles: Q and dO rows, their transposes (bf16 at d_head 32: read from the rows
+  // by the transposing LDS read instead), lse and D
+  constexpr bool TRB = sizeof(T) == 2 && DH == 32;
   __shared__ __attribute__((aligned(16))) T sQ[2][QT * LDQ];
   __shared__ __attribute__((aligned(16))) T sO[2][QT * LDQ];
-  __shared__ __attribute__((aligned(16))) T sQt[2][DH * LDT];
-  __shared__ __attribute__((aligned(16))) T sOt[2][DH * LDT];
+  __shared__ __attribute__((aligned(16))) T sQt[2][TRB ? EPC : DH * LDT];
+  __shared__ __attribute__((aligned(16))) T sOt[2][TRB ? EPC : DH * LDT];
   __shared__ __attribute__((aligned(16))) float sL[2][QT];
   __shared__ __attribute__((aligned(16))) float sD[2][QT];
   __shared__ __attribute__((aligned(16))) T stage[NW][TS::SIZE];
@@ -171,11 +175,13 @@ __global__ __launch_bounds__(ATTB_WAVES * 64) void attn_dkdv_kernel(const AttnBw
         const int which = ch / (QT * CPR), rem = ch - which * (QT * CPR);
         const int row = rem / CPR, c0 = (rem - row * CPR) * EPC;
         T *rt = which == 0 ? sQ[buf] : sO[buf];
-        T *tt = which == 0 ? sQt[buf] : sOt[buf];
         st16(&rt[row * LDQ + c0], reg[k]);
-        const T *ve = (const T *)&reg[k];
+        if constexpr (!TRB) {
+          T *tt = which == 0 ? sQt[buf] : sOt[buf];
+          const T *ve = (const T *)&reg[k];
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) tt[(c0 + e) * LDT + row] = ve[e];
+          for (int e = 0; e < EPC; ++e) tt[(c0 + e) * LDT + row] = ve[e];
+        }
       }
     }
     if (tid < QT) {
@@ -241,14 +247,23 @@ __global__ __launch_bounds__(ATTB_WAVES * 64) void attn_dkdv_kernel(const AttnBw
           ds[v] = p[v] * dp[v];
         }
       }
-      const T *ot_row = &sOt[buf][(lc < DH ? lc : 0) * LDT + sub * 32];
-      const T *qt_row = &sQt[buf][(lc < DH ? lc : 0) * LDT + sub * 32];
+      if constexpr (TRB) {
+        const int src = tr_src<LDQ>(sub * 32, lane);
 #pragma unroll
-      for (int mc = 0; mc < MC; ++mc) {
-        const frag oa = lc < DH ? TrFrag<T>::load(ot_row, mc, g) : M::zero();
-        const frag qa = lc < DH ? TrFrag<T>::load(qt_row, mc, g) : M::zero();
-        dv = M::mma(oa, TrFrag<T>::from_acc(p, mc), dv);
-        dk = M::mma(qa, TrFrag<T>::from_acc(ds, mc), dk);
+        for (int mc = 0; mc < MC; ++mc) {
+          dv = M::mma(tr_frag<LDQ>((const bf16 *)sO[buf] + src, mc), TrFrag<T>::from_acc(p, mc), dv);
+          dk = M::mma(tr_frag<LDQ>((const bf16 *)sQ[buf] + src, mc), TrFrag<T>::from_acc(ds, mc), dk);
+        }
+      } else {
+        const T *ot_row = &sOt[buf][(lc < DH ? lc : 0) * LDT + sub * 32];
+        const T *qt_row = &sQt[buf][(lc < DH ? lc : 0) * LDT + sub * 32];
+#pragma unroll
+        for (int mc = 0; mc < MC; ++mc) {
+          const frag oa = lc < DH ? TrFrag<T>::load(ot_row, mc, g) : M::zero();
+          const frag qa = lc < DH ? TrFrag<T>::load(qt_row, mc, g) : M::zero();
+          dv = M::mma(oa, TrFrag<T>::from_acc(p, mc), dv);
+          dk = M::mma(qa, TrFrag<T>::from_acc(ds, mc), dk);
+        }
       }
     }
     // the other buffer was last read in the previous iteration, before the barrier below it
@@ -277,7 +292,8 @@ __global__ __launch_bounds__(ATTB_WAVES * 64) void attn_dq_kernel(const AttnBwdA
   constexpr int MC = 32 / M::KSTEP;
   __shared__ __attribute__((aligned(16))) T sK[2][KT * LDK];
   __shared__ __attribute__((aligned(16))) T sV[2][KT * LDK];
-  __shared__ __attribute__((aligned(16))) T sKt[2][DH * LDT];
+  constexpr bool TRB = sizeof(T) == 2 && DH == 32;   // K^T read from the K rows by the transposing read
+  __shared__ __attribute__((aligned(16))) T sKt[2][TRB ? EPC : DH * LDT];
   __shared__ __attribute__((aligned(16))) T stage[NW][TS::SIZE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -332,7 +348,7 @@ __global__ __launch_bounds__(ATTB_WAVES * 64) void attn_dq_kernel(const AttnBwdA
         const int which = ch / (KT * CPR), rem = ch - which * (KT * CPR);
         const int row = rem / CPR, c0 = (rem - row * CPR) * EPC;
         st16(&(which == 0 ? sK[buf] : sV[buf])[row * LDK + c0], reg[k]);
-        if (which == 0) {
+        if (!TRB && which == 0) {
           const T *ve = (const T *)&reg[k];
 #pragma unroll
           for (int e = 0; e < EPC; ++e) sKt[buf][(c0 + e) * LDT + row] = ve[e];
@@ -381,11 +397,17 @@ __global__ __launch_bounds__(ATTB_WAVES * 64) void attn_dq_kernel(const AttnBwdA
 #pragma unroll
         for (int v = 0; v < 16; ++v) ds[v] = acc_row(v, g) <= lim ? __builtin_amdgcn_exp2f(s[v]) * dp[v] : 0.0f;
       }
-      const T *kt_row = &sKt[buf][(lc < DH ? lc : 0) * LDT + sub * 32];
+      if constexpr (TRB) {
+        const bf16 *src = (const bf16 *)sK[buf] + tr_src<LDK>(sub * 32, lane);
 #pragma unroll
-      for (int mc = 0; mc < MC; ++mc) {
-        const frag ka = lc < DH ? TrFrag<T>::load(kt_row, mc, g) : M::zero();
-        dq = M::mma(ka, TrFrag<T>::from_acc(ds, mc), dq);
+        for (int mc = 0; mc < MC; ++mc) dq = M::mma(tr_frag<LDK>(src, mc), TrFrag<T>::from_acc(ds, mc), dq);
+      } else {
+        const T *kt_row = &sKt[buf][(lc < DH ? lc : 0) * LDT + sub * 32];
+#pragma unroll
+        for (int mc = 0; mc < MC; ++mc) {
+          const frag ka = lc < DH ? TrFrag<T>::load(kt_row, mc, g) : M::zero();
+          dq = M::mma(ka, TrFrag<T>::from_acc(ds, mc), dq);
+        }
       }
     }
     if (more) lstore(buf ^ 1);

@@ -111,6 +111,33 @@ __device__ __forceinline__ void sched_lds_mfma() {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Transposed bf16 MFMA fragments from a row-major LDS tile [token][ROW] (ROW elements per row,
+// features 0..31 used), by the transposing LDS read ds_read_b64_tr_b16. In each 16-lane group,
+// lane i of the read receives element i % 4 of the 8-byte runs that lanes i / 4, 4 + i / 4,
+// 8 + i / 4 and 12 + i / 4 of the group point at (measured on gfx950). Source lane s of the group
+// that holds output lanes (features 16 h .. 16 h + 15, lane half g) points at
+// tile[t0 + 4 g + s / 4][16 h + 4 (s % 4)], so output lane (lc, g) receives tokens
+// t0 + 4 g + 0..3 of feature lc. Two reads, at t0 + 16 mc and t0 + 16 mc + 8, give the fragment of
+// the 32-token k index in the accumulator-row order acc_row (tokens 16 mc + 4 g + 0..3 and
+// 16 mc + 8 + 4 g + 0..3): the order in which a lane holds probabilities or score gradients, so
+// they serve directly as the other operand.
+// ---------------------------------------------------------------------------------------------
+// Element offset of this lane's source address for the tokens starting at t0.
+template <int ROW>
+__device__ __forceinline__ int tr_src(int t0, int lane) {
+  return (t0 + 4 * (lane >> 5) + ((lane >> 2) & 3)) * ROW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+}
+// k-chunk mc of the fragment; src = tile + tr_src<ROW>(t0, lane).
+template <int ROW>
+__device__ __forceinline__ bf16x8 tr_frag(const bf16 *src, int mc) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s4 lds_s4;
+  const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(src + 16 * mc * ROW));
+  const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(src + (16 * mc + 8) * ROW));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// ---------------------------------------------------------------------------------------------
 // conversions
 // ---------------------------------------------------------------------------------------------
 __device__ __forceinline__ float to_f32(float x) { return x; }
