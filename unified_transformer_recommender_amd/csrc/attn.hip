@@ -436,11 +436,14 @@ __global__ __launch_bounds__(ATTN_WAVES * 64) void attn_split_kernel(const AttnA
   using TS = TileStage<T>;
   // LDS: per-wave K / V^T tiles during the key loop; after a barrier the same bytes hold the merge
   // (every wave's m, l and o) and the output staging tile
-  constexpr int TILE_BYTES = NWA * (32 * LDK + DH * LDW) * (int)sizeof(T);
+  // bf16 at d_head 32: V row-major ([key][32], read by the transposing LDS read); else transposed
+  constexpr bool TRV = sizeof(T) == 2 && DH == 32;
+  constexpr int VW = TRV ? 32 * DH : DH * LDW;   // elements of a wave's V tile
+  constexpr int TILE_BYTES = NWA * (32 * LDK + VW) * (int)sizeof(T);
   constexpr int MERGE_BYTES = NWA * (2 * 32 + 16 * 64) * 4 + TS::SIZE * (int)sizeof(T);
   __shared__ __attribute__((aligned(16))) unsigned char smem[TILE_BYTES > MERGE_BYTES ? TILE_BYTES : MERGE_BYTES];
   T (*sK)[32 * LDK] = (T (*)[32 * LDK])smem;
-  T (*sV)[DH * LDW] = (T (*)[DH * LDW])(smem + NWA * 32 * LDK * sizeof(T));
+  T (*sV)[VW] = (T (*)[VW])(smem + NWA * 32 * LDK * sizeof(T));
   float (*s_o)[16][64] = (float (*)[16][64])smem;
   float (*s_m)[32] = (float (*)[32])(smem + NWA * 16 * 64 * 4);
   float (*s_l)[32] = (float (*)[32])(smem + NWA * (16 * 64 + 32) * 4);
@@ -511,9 +514,13 @@ __global__ __launch_bounds__(ATTN_WAVES * 64) void attn_split_kernel(const AttnA
       if (ch < 32 * CPK) {
         const int key = ch / CPK, c0 = (ch - key * CPK) * EPC;
         st16(&kw[key * LDK + c0], pk[i]);
-        const T *ve = (const T *)&pv[i];
+        if constexpr (TRV) {
+          st16(&vw[key * DH + c0], pv[i]);
+        } else {
+          const T *ve = (const T *)&pv[i];
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) vw[(c0 + e) * LDW + key] = ve[e];
+          for (int e = 0; e < EPC; ++e) vw[(c0 + e) * LDW + key] = ve[e];
+        }
       }
     }
   };
@@ -534,7 +541,8 @@ __global__ __launch_bounds__(ATTN_WAVES * 64) void attn_split_kernel(const AttnA
       }
       return s;
     };
-    softmax_pv<T, DH>(scores, st, VtRow<T, DH>{lc < DH ? &vw[lc * LDW] : nullptr, g});
+    if constexpr (TRV) softmax_pv<T, DH>(scores, st, VRowTr{(const bf16 *)vw + tr_src<32>(0, lane)});
+    else softmax_pv<T, DH>(scores, st, VtRow<T, DH>{lc < DH ? &vw[lc * LDW] : nullptr, g});
   }
 
   // ---- Stage II: the candidates' own NS keys (block-diagonal causal), on the last wave --------
@@ -567,7 +575,8 @@ __global__ __launch_bounds__(ATTN_WAVES * 64) void attn_split_kernel(const AttnA
         }
         return s;
       };
-      softmax_pv<T, DH>(scores, st, VtRow<T, DH>{lc < DH ? &vw[lc * LDW] : nullptr, g});
+      if constexpr (TRV) softmax_pv<T, DH>(scores, st, VRowTr{(const bf16 *)vw + tr_src<32>(0, lane)});
+      else softmax_pv<T, DH>(scores, st, VtRow<T, DH>{lc < DH ? &vw[lc * LDW] : nullptr, g});
     }
   }
 
