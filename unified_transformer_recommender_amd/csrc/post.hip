@@ -13,8 +13,9 @@
 // which accumulates straight into X'^T. An accumulator tile's lane holds the k-indices
 // {4g + r + 8j}; two cross-half lane swaps (v_permlane32_swap) turn it into a natural B fragment.
 //
-// Weight streaming: chunks flow through a ring of NB = 2 LDS buffers with direct global->LDS
-// loads (each wave instruction writes 64 x 16 bytes), issued one chunk ahead; a chunk is consumed
+// Weight streaming: chunks flow through a ring of NB = 2 LDS buffers (4 in split launches) with
+// direct global->LDS loads (each wave instruction writes 64 x 16 bytes), issued NB - 1 chunks
+// ahead; a chunk is consumed
 // after the issuing waves' own partial vmcnt wait and one fence-free workgroup barrier, so the
 // next chunk's loads stay in flight across it. Within a chunk, LDS operand reads are issued a
 // few MFMAs ahead of their use. Rows are stored unpadded with their 16-byte pieces XOR-swizzled so
@@ -82,7 +83,9 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64), (post_wgs_per_cu<T, D>())) 
   constexpr int BLOCKS = CH / EPC / 64;         // 1 KB wave loads per chunk
   constexpr int LPW = BLOCKS / NW;              // wave loads per chunk per wave
   static_assert(BLOCKS % NW == 0 && LPW >= 1, "chunk must split into whole wave loads");
-  constexpr int NB = 2;                         // chunk buffers; loads run NB - 1 chunks ahead
+  // chunk buffers; loads run NB - 1 chunks ahead. A split launch (few token tiles: one workgroup per
+  // CU, each with a short chunk stream) runs four, so that chunk load latency is not exposed.
+  constexpr int NB = SPLIT ? 4 : 2;
   constexpr int PD = 4;                         // LDS operand reads in flight ahead of the MFMAs
   constexpr bool BF = sizeof(T) == 2;
   __shared__ __attribute__((aligned(16))) T lds[NB][CH];
@@ -301,12 +304,11 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64), (post_wgs_per_cu<T, D>())) 
 
   // ---- FFN: per hidden chunk c, stage A (W1 chunk c): up-projection; GELU; stage B (W2 chunk
   // c): down-projection into X'^T. Two workgroups share a CU, so the VALU work and the waits of
-  // one overlap the MFMAs of the other. With two ring slots every W1 chunk sits in slot SA and
-  // every W2 chunk in slot SB, so each LDS operand address is a fixed per-lane offset.
-  constexpr int SA = DT % NB, SB = (DT + 1) % NB;
-  static_assert(NB == 2, "fixed stage slots assume a two-slot ring");
+  // one overlap the MFMAs of the other. With two ring slots every W1 chunk sits in slot DT % 2 and
+  // every W2 chunk in the other, so each LDS operand address is a fixed per-lane offset.
   for (int c = 0; c < NC; ++c) {
     const int ia = DT + 2 * c;
+    const int SA = NB == 2 ? DT % 2 : ia % NB, SB = NB == 2 ? (DT + 1) % 2 : (ia + 1) % NB;
     arrive(ia);
     if (ia + NB - 1 < NCH) issue(ia + NB - 1);
     // the up-projection accumulators start from the bias b1 (accumulator row layout)
