@@ -21,7 +21,8 @@
 // few MFMAs ahead of their use. Rows are stored unpadded with their 16-byte pieces XOR-swizzled so
 // that 16 lanes reading 16 consecutive rows touch 16 distinct bank groups.
 //
-// Occupancy: for bf16 at d <= 256 the kernel is held to 256 registers per lane so that two
+// Occupancy: for bf16 at d < 256, and at d = 256 with RMSNorm, the kernel is held to 256 registers
+// per lane so that two
 // workgroups share a CU. Each hidden chunk then runs plainly in order (up-projection, GELU,
 // down-projection): the other workgroup's MFMAs fill this one's VALU phases, waits and activation
 // loads.
@@ -44,9 +45,10 @@ template <typename T, int D>
 constexpr int post_nw() { return (sizeof(T) == 2 && D == 128) ? 8 : 4; }
 
 // Workgroups per CU the register budget is set for: two where a lane's d-wide accumulators and
-// operand fragments fit in 256 registers (bf16, d <= 256), else one (512 registers).
-template <typename T, int D>
-constexpr int post_wgs_per_cu() { return (sizeof(T) == 2 && D <= 256) ? 2 : 1; }
+// operand fragments fit in 256 registers (bf16, d <= 256; at d = 256 only for RMSNorm: LayerNorm's
+// extra shift vector and mean pass spill at 256), else one (512 registers).
+template <typename T, int D, bool LAYER>
+constexpr int post_wgs_per_cu() { return (sizeof(T) == 2 && (D < 256 || (D == 256 && !LAYER))) ? 2 : 1; }
 
 // Row layout of a weight chunk in LDS: RP 16-byte pieces per row; piece q of row r is stored at
 // slot q ^ swz(r). `rpb` = rows sharing one 256-byte bank line.
@@ -69,7 +71,7 @@ __device__ __forceinline__ bf16x8 natural_kfrag(bf16x8 f) {
 }
 
 template <typename T, typename TR, int D, bool LAYER, bool SPLIT>
-__global__ __launch_bounds__((post_nw<T, D>() * 64), (post_wgs_per_cu<T, D>())) void post_kernel(const PostArgs a) {
+__global__ __launch_bounds__((post_nw<T, D>() * 64), (post_wgs_per_cu<T, D, LAYER>())) void post_kernel(const PostArgs a) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int NW = post_nw<T, D>();
