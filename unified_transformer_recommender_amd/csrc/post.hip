@@ -22,10 +22,9 @@
 // that 16 lanes reading 16 consecutive rows touch 16 distinct bank groups.
 //
 // Occupancy: for bf16 at d < 256, and at d = 256 with RMSNorm, the kernel is held to 256 registers
-// per lane so that two
-// workgroups share a CU. Each hidden chunk then runs plainly in order (up-projection, GELU,
-// down-projection): the other workgroup's MFMAs fill this one's VALU phases, waits and activation
-// loads.
+// per lane so that two workgroups share a CU. Each hidden chunk then runs plainly in order
+// (up-projection, GELU, down-projection): the other workgroup's MFMAs fill this one's VALU phases,
+// waits and activation loads.
 //
 // GELU is the erf form 0.5 x (1 + erf(x / sqrt 2)): gelu_as (fp32 path) and gelu_fit (bf16 path)
 // of the shared header.
