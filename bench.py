@@ -310,8 +310,10 @@ def main():
         sc = cm.score_classes(m.d_model, m.d_ff, m.l_ns, w.l_s, w.s_queries, store_bytes)
         classes = {k: (pre[k] * w.n_users + sc[k] * n_units) / n_units for k in sc}
 
-        def step():
+        def step(mark=None):   # mark: an event recorded between Stage I and Stage II
             ob.onetrans_prefill_user(model, xs, cache, None, ws1)
+            if mark is not None:
+                mark.record(stream)
             ob.onetrans_score_candidates(model, cache, xn, out, ws2)
     else:   # append: restore the pristine cache (untimed), then append + score the user's NS tokens
         old, new = synth.append_batch(w)
@@ -367,6 +369,7 @@ def main():
     trace_in = not a.no_trace and a.streams == 1
     ob.timing_enable(trace_in)
     total_ms = 0.0
+    per_step = []   # each step's own event interval (ms)
     if w.kind == "append":
         # the cache restore between steps is outside the timed intervals
         for _ in range(a.steps):
@@ -377,19 +380,32 @@ def main():
             step()
             e1.record(stream)
             torch.cuda.synchronize()
-            total_ms += e0.elapsed_time(e1)
+            per_step.append(e0.elapsed_time(e1))
+        total_ms = sum(per_step)
     else:
+        # one event between consecutive steps (recording it adds no work to the stream)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+        mids = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)] if w.kind == "two_stage" else None
         t0 = time.perf_counter()
-        e0.record(stream)
-        for _ in range(a.steps):
-            step()
-        e1.record(stream)
+        evs[0].record(stream)
+        for i in range(a.steps):
+            if mids is not None:
+                step(mids[i])
+            else:
+                step()
+            evs[i + 1].record(stream)
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) * 1e3
-        total_ms = max(e0.elapsed_time(e1), 0.0)
+        total_ms = max(evs[0].elapsed_time(evs[-1]), 0.0)
+        per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(a.steps)]
         extra["wall_ms_per_step"] = round(wall / a.steps, 4)
+        if mids is not None:
+            extra["stage_ms_per_step"] = {
+                "prefill_user": round(sum(evs[i].elapsed_time(mids[i]) for i in range(a.steps)) / a.steps, 4),
+                "score_candidates": round(sum(mids[i].elapsed_time(evs[i + 1]) for i in range(a.steps)) / a.steps, 4)}
+    q = np.percentile(np.asarray(per_step, np.float64), [10, 50, 90])
+    extra["ms_step_p10_median_p90"] = [round(float(v), 4) for v in q]
     ob.timing_enable(False)
     timing = ob.timing_read()
     ms_step = total_ms / a.steps
