@@ -51,6 +51,8 @@ def parse():
                    help="streams of the batched calls: 2 runs a forward batch / an append's users as two "
                         "concurrent halves (per-kernel timing then comes from a separate one-stream pass); 1 "
                         "runs everything on one stream")
+    p.add_argument("--separate-append", action="store_true",
+                   help="append workloads: time the append and Stage II as two calls, not the fused call")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline (0: skip)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain elementwise copy of MIB MiB (fp32 negate: reads and writes MIB MiB "
@@ -342,11 +344,21 @@ def main():
                     classes[k] = classes.get(k, 0.0) + (ap[k] + sc[k]) / len(lens or [w.l_old])
         out_new = torch.empty((w.n_users, q_final, m.d_model), dtype=torch.float32, device=dev)
         out = torch.empty((w.n_users, 1, m.l_ns, m.d_model), dtype=torch.float32, device=dev)
-        ws1 = model.workspace(ob.L.OP_APPEND, w.n_users, l_s=pristine.append_window(), d_l=w.d_l)
-        ws2 = model.workspace(ob.L.OP_SCORE, w.n_users, n_cand=1)
+        # one call for both (each block's attention reads the cache once) where it applies: no pyramid,
+        # at most 32 new rows and 32 NS rows per user
+        fused = not pyramid_append and not a.separate_append and w.d_l <= 32 and m.l_ns <= 32
+        extra["append_call"] = "append_score" if fused else "append_events + score_candidates"
+        if fused:
+            ws1 = model.workspace(ob.L.OP_APPEND_SCORE, w.n_users, n_cand=1, d_l=w.d_l)
+        else:
+            ws1 = model.workspace(ob.L.OP_APPEND, w.n_users, l_s=pristine.append_window(), d_l=w.d_l)
+            ws2 = model.workspace(ob.L.OP_SCORE, w.n_users, n_cand=1)
         restore_ms = []
 
         def step():
+            if fused:
+                ob.onetrans_append_score(model, cache, xnw, xn, out_new, out, ws1)
+                return
             ob.onetrans_append_events(model, cache, xnw, out_new, ws1)
             ob.onetrans_score_candidates(model, cache, xn, out, ws2)
 

@@ -57,7 +57,8 @@ typedef enum {
 typedef enum { ONETRANS_F32 = 0, ONETRANS_BF16 = 1 } onetrans_dtype;
 typedef enum { ONETRANS_RMSNORM = 0, ONETRANS_LAYERNORM = 1 } onetrans_norm;
 typedef enum {
-  ONETRANS_OP_FORWARD = 0, ONETRANS_OP_PREFILL = 1, ONETRANS_OP_SCORE = 2, ONETRANS_OP_APPEND = 3
+  ONETRANS_OP_FORWARD = 0, ONETRANS_OP_PREFILL = 1, ONETRANS_OP_SCORE = 2, ONETRANS_OP_APPEND = 3,
+  ONETRANS_OP_APPEND_SCORE = 4
 } onetrans_op;
 
 typedef struct {
@@ -114,6 +115,8 @@ typedef struct {
  *   APPEND:  n_seq = users, d_l = appended rows per user; l_s = 0 for a cache whose pyramid
  *            prunes no block before the last, else the rows of the block after the first pruning
  *            block (layer_len[n* + 1]): that block onwards is recomputed over its window
+ *   APPEND_SCORE: n_seq = users, d_l = appended rows per user, n_cand = candidates per user
+ *            (l_s ignored): the APPEND workspace (l_s = 0) then the SCORE one
  * Returns 0 for an invalid configuration. */
 size_t onetrans_workspace_bytes(const onetrans_config *cfg, int op, int n_seq, int l_s, int n_cand,
                                 int d_l);
@@ -222,6 +225,26 @@ int onetrans_score_candidates_noalloc(const onetrans_config *cfg, const onetrans
 int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weights *blk,
                            onetrans_kv_cache *cache, const void *x_new, int n_users, int d_l,
                            void *out_new, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Cross-request append followed by Stage II scoring of the same users (section 7.5.3: the new
+ * events extend the cached sequence, then each candidate's NS rows attend over the whole cached
+ * sequence, the new rows included). Equal, bit for bit, to onetrans_append_events(cfg, blk, cache,
+ * x_new, n_users, d_l, out_new, ...) followed by onetrans_score_candidates(cfg, blk, cache, x_ns,
+ * n_users, n_cand, out_ns, ...), but each block's attention for both query sets runs as one pass
+ * over the user's cached keys, so the cache is read once per block instead of twice.
+ *   x_new   [n_users][d_l][d] storage dtype; out_new [n_users][d_l][d] fp32 (required).
+ *   x_ns    [n_users][n_cand][l_ns][d] storage dtype; out_ns [n_users][n_cand][l_ns][d] fp32.
+ *   ws      onetrans_workspace_bytes(cfg, ONETRANS_OP_APPEND_SCORE, n_users, 0, n_cand, d_l) bytes.
+ * Supported: an unpyramided cache (every layer_len equal and q_last the same), d_l <= 32 and
+ * n_cand * l_ns <= 32; otherwise UNSUPPORTED (call the two entry points instead). Ragged users as
+ * in append_events: user u's Stage II keys are its user_len[u] + d_l rows. The cache lengths advance
+ * as in append_events. 16 or more users run as two halves on two streams (see onetrans_forward).
+ * Errors: those of the two calls it replaces, plus INVALID_ARG for a NULL out_new and UNSUPPORTED
+ * as above. */
+int onetrans_append_score(const onetrans_config *cfg, const onetrans_block_weights *blk,
+                          onetrans_kv_cache *cache, const void *x_new, int n_users, int d_l,
+                          void *out_new, const void *x_ns, int n_cand, void *out_ns, void *ws,
+                          size_t ws_bytes, hipStream_t stream);
 
 /* ---- Training step (section 7.5.3, closing paragraph: mixed-precision training with activation
  * recomputation; paper-daily deep reading, section 4.3, system-efficiency table) ---------------

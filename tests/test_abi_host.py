@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert "onetrans_forward" in names and "onetrans_tokenize" in names and len(names) == 16
+    assert "onetrans_forward" in names and "onetrans_tokenize" in names and len(names) == 17
     lib = L.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -180,6 +180,41 @@ def test_serving_validation_errors():
     assert lib.onetrans_append_events(ctypes.byref(c), b, ctypes.byref(full), FAKE, 2, 0, None, FAKE, 1 << 40,
                                       None) == L.ERR_SHAPE
 
+
+
+def test_append_score_validation_errors():
+    """The fused append + Stage II call: its own limits (d_l <= 32, n_cand * l_ns <= 32, an unpyramided
+    cache, out_new required) and the checks of the two calls it replaces, all before any HIP call;
+    no cache length advances on an error."""
+    lib = L.lib()
+    flat = _cfg(sq=(120, 120))
+    b = _blocks(2)
+
+    def call(kc, U=2, dl=8, C=2, out_new=FAKE, wsb=1 << 40, cfg=flat):
+        return lib.onetrans_append_score(ctypes.byref(cfg), b, ctypes.byref(kc), FAKE, U, dl, out_new, FAKE, C,
+                                         FAKE, FAKE, wsb, None)
+
+    kc = _cache(lens=(120, 120))
+    assert call(kc, dl=33) == L.ERR_UNSUPPORTED
+    assert call(kc, C=3) == L.ERR_UNSUPPORTED                 # 3 x 16 NS rows > 32
+    assert call(_cache(lens=(120, 100))) == L.ERR_UNSUPPORTED  # pyramided
+    pruned = _cache(lens=(120, 120))
+    pruned.q_last = 50
+    assert call(pruned) == L.ERR_UNSUPPORTED
+    assert call(kc, out_new=None) == L.ERR_INVALID_ARG
+    assert call(kc, out_new=FAKE + 4) == L.ERR_ALIGNMENT
+    assert call(kc, dl=0) == L.ERR_SHAPE
+    assert call(kc, U=3) == L.ERR_SHAPE                       # more users than the cache holds
+    assert call(_cache(cap=124, lens=(120, 120))) == L.ERR_CACHE_CAPACITY
+    need = lib.onetrans_workspace_bytes(ctypes.byref(flat), L.OP_APPEND_SCORE, 2, 0, 2, 8)
+    parts = (lib.onetrans_workspace_bytes(ctypes.byref(flat), L.OP_APPEND, 2, 0, 0, 8)
+             + lib.onetrans_workspace_bytes(ctypes.byref(flat), L.OP_SCORE, 2, 0, 2, 0))
+    assert parts <= need < parts + 256
+    assert call(kc, wsb=need - 1) == L.ERR_WORKSPACE
+    assert list(kc._keep) == [120, 120]
+    rk = _ragged_cache((100, 195))
+    assert call(rk) == L.ERR_CACHE_CAPACITY                   # 195 + 8 > 200
+    assert list(rk._keep_ul) == [100, 195]
 
 def _ragged_cache(user_len, n_users=2, cap=200, lens=(120, 120)):
     kc = _cache(n_users, cap, lens)

@@ -23,7 +23,7 @@ SCRATCH_BYTES = 64 << 20     # ONETRANS_SCRATCH_BYTES
 
 F32, BF16 = 0, 1
 RMSNORM, LAYERNORM = 0, 1
-OP_FORWARD, OP_PREFILL, OP_SCORE, OP_APPEND = 0, 1, 2, 3
+OP_FORWARD, OP_PREFILL, OP_SCORE, OP_APPEND, OP_APPEND_SCORE = 0, 1, 2, 3, 4
 KERNEL_CLASSES = ("qkv", "attn", "post", "lin", "merge", "bwd_gemm", "bwd_attn", "bwd_rows")
 MERGE_INTENT, MERGE_TIME = 0, 1
 
@@ -74,6 +74,8 @@ SIGNATURES = {
                                                   c_void_p, c_int, c_int, c_void_p, c_void_p]),
     "onetrans_append_events": (c_int, [POINTER(Config), POINTER(BlockWeights), POINTER(KVCache), c_void_p,
                                        c_int, c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "onetrans_append_score": (c_int, [POINTER(Config), POINTER(BlockWeights), POINTER(KVCache), c_void_p, c_int,
+                                      c_int, c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
     "onetrans_tokenize_workspace_bytes": (c_size_t, [POINTER(Config), POINTER(TokenizerConfig), c_int]),
     "onetrans_tokenize": (c_int, [POINTER(Config), POINTER(TokenizerConfig), POINTER(MlpWeights), c_void_p,
                                   POINTER(MlpWeights), POINTER(c_void_p), POINTER(c_void_p), c_void_p, c_int,

@@ -279,6 +279,29 @@ def onetrans_append_events(model: Model, cache: KVCache, x_new: torch.Tensor,
     return out_new
 
 
+
+def onetrans_append_score(model: Model, cache: KVCache, x_new: torch.Tensor, x_ns: torch.Tensor,
+                          out_new: Optional[torch.Tensor] = None, out_ns: Optional[torch.Tensor] = None,
+                          ws: Optional[torch.Tensor] = None, stream=None):
+    """A cross-request append then Stage II for the same users in one call: x_new [U][dL][d] and
+    x_ns [U][C][l_ns][d] -> (out_new [U][dL][d], out_ns [U][C][l_ns][d]) fp32; the cache is extended
+    by dL rows per block as onetrans_append_events does."""
+    _check_input(model, x_new, 3, "x_new")
+    _check_input(model, x_ns, 4, "x_ns")
+    U, dl, d = x_new.shape
+    C = x_ns.shape[1]
+    if out_new is None:
+        out_new = torch.empty((U, dl, d), dtype=torch.float32, device=x_new.device)
+    if out_ns is None:
+        out_ns = torch.empty((U, C, model.l_ns, d), dtype=torch.float32, device=x_ns.device)
+    if ws is None:
+        ws = model.workspace(L.OP_APPEND_SCORE, U, n_cand=C, d_l=dl)
+    st = L.lib().onetrans_append_score(ctypes.byref(model.cfg), model.blocks, ctypes.byref(cache.c),
+                                       x_new.data_ptr(), U, dl, out_new.data_ptr(), x_ns.data_ptr(), C,
+                                       out_ns.data_ptr(), ws.data_ptr(), ws.numel(), _stream(x_new.device, stream))
+    L.check(st, "onetrans_append_score")
+    return out_new, out_ns
+
 class Tokenizer:
     """Device weights of the tokenizers ahead of block 1 for one model (see onetrans_tokenize).
 

@@ -619,6 +619,229 @@ __global__ __launch_bounds__(ATTN_WAVES * 64) void attn_split_kernel(const AttnA
   }
 }
 
+// Append and Stage II together (a cross-request append followed by the scoring of the user's
+// candidates): one workgroup per (user, head) streams the user's prefix keys once, as
+// attn_split_kernel does, and folds every subtile into two query groups per wave:
+//   group A (args a): the appended rows, R <= 32 per user at positions p0 + i, causal;
+//   group B (args b): the candidates' NS rows, n_cand * R <= 32 per user, Stage II: every prefix
+//   key visible, then (last wave) the candidates' own NS keys, block-diagonal causal.
+// Both groups see the same prefix keys (the cache after the append: n_pre rows, shifted by the
+// user's own length when ragged), so the K/V tiles are loaded and staged once for both. Each
+// group's eight partial states merge exactly as in attn_split_kernel (wave 0 merges group A,
+// wave 1 group B).
+template <typename T, int DH>
+struct QGroup {
+  typename Mma<T>::frag qf[DH / Mma<T>::KSTEP];
+  SoftmaxState st;
+  int z, qi, cslot;
+  bool valid;
+};
+
+template <typename T, int DH>
+__global__ __launch_bounds__(ATTN_WAVES * 64) void attn_pair_kernel(const AttnArgs a, const AttnArgs b) {
+  using M = Mma<T>;
+  using frag = typename M::frag;
+  constexpr int EPC = 16 / (int)sizeof(T);
+  constexpr int NWA = ATTN_WAVES;
+  constexpr int LDK = DH + EPC;
+  constexpr int LDW = 32 + EPC;
+  constexpr int CPK = DH / EPC;
+  constexpr int NPL = (32 * CPK + 63) / 64;
+  using TS = TileStage<T>;
+  constexpr bool TRV = sizeof(T) == 2 && DH == 32;
+  constexpr int VW = TRV ? 32 * DH : DH * LDW;
+  constexpr int TILE_BYTES = NWA * (32 * LDK + VW) * (int)sizeof(T);
+  constexpr int GROUP_BYTES = NWA * (2 * 32 + 16 * 64) * 4;          // one group's m, l and o of every wave
+  constexpr int MERGE_BYTES = 2 * GROUP_BYTES + 2 * TS::SIZE * (int)sizeof(T);
+  __shared__ __attribute__((aligned(16))) unsigned char smem[TILE_BYTES > MERGE_BYTES ? TILE_BYTES : MERGE_BYTES];
+  T (*sK)[32 * LDK] = (T (*)[32 * LDK])smem;
+  T (*sV)[VW] = (T (*)[VW])(smem + NWA * 32 * LDK * sizeof(T));
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, lc = lane & 31;
+  const int H = a.n_heads;
+  const int pair = blockIdx.x;
+  const int h = pair % H, grp = pair / H;
+
+  QGroup<T, DH> A, B;
+  A.z = grp;
+  A.qi = lc;
+  A.cslot = 0;
+  A.valid = lc < a.R;
+  const int cpw = 32 / b.R;
+  B.cslot = lc / b.R;
+  B.qi = lc - B.cslot * b.R;
+  B.valid = B.cslot < cpw && B.cslot < b.n_cand;
+  B.z = grp * b.n_cand + (B.valid ? B.cslot : 0);
+  const int shift = a.seq_shift ? a.seq_shift[grp] : 0;
+  const int p0 = a.p0 + shift, n_keys = a.n_pre + shift;
+  const int qpos = p0 + A.qi;
+  {
+    const T *qa = (const T *)a.q + A.z * a.q_sb + h * a.q_sh + (long long)(A.valid ? A.qi : 0) * DH + g * M::KPL;
+    const T *qb = (const T *)b.q + B.z * b.q_sb + h * b.q_sh + (long long)(B.valid ? B.qi : 0) * DH + g * M::KPL;
+#pragma unroll
+    for (int kk = 0; kk < DH / M::KSTEP; ++kk) {
+      A.qf[kk] = A.valid ? *(const frag *)(qa + kk * M::KSTEP) : M::zero();
+      B.qf[kk] = B.valid ? *(const frag *)(qb + kk * M::KSTEP) : M::zero();
+    }
+  }
+  for (QGroup<T, DH> *q : {&A, &B}) {
+    q->st.m = -1e30f;   // below every score (as in the other kernels)
+    q->st.lsum = 0.0f;
+    q->st.o = f32x16{};
+  }
+  const int n_sub = (n_keys + 31) / 32;
+  const int per = (n_sub + NWA - 1) / NWA;
+  const int sub0 = min(n_sub, wave * per), sub1 = min(n_sub, sub0 + per);
+  const T *kp = (const T *)a.k_pre + grp * a.pre_sb + h * a.pre_sh;
+  const T *vp = (const T *)a.v_pre + grp * a.pre_sb + h * a.pre_sh;
+
+  T *kw = sK[wave];
+  T *vw = sV[wave];
+  u32x4 pk[NPL], pv[NPL];
+  auto load = [&](int sub) {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int ch = lane + 64 * i;
+      const int key = ch / CPK, c0 = (ch - key * CPK) * EPC;
+      const int kg = sub * 32 + key;
+      pk[i] = u32x4{0, 0, 0, 0};
+      pv[i] = u32x4{0, 0, 0, 0};
+      if (ch < 32 * CPK && kg < n_keys) {
+        pk[i] = ld16(kp + (long long)kg * DH + c0);
+        pv[i] = ld16(vp + (long long)kg * DH + c0);
+      }
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int ch = lane + 64 * i;
+      if (ch < 32 * CPK) {
+        const int key = ch / CPK, c0 = (ch - key * CPK) * EPC;
+        st16(&kw[key * LDK + c0], pk[i]);
+        if constexpr (TRV) {
+          st16(&vw[key * DH + c0], pv[i]);
+        } else {
+          const T *ve = (const T *)&pv[i];
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) vw[(c0 + e) * LDW + key] = ve[e];
+        }
+      }
+    }
+  };
+  // one group's softmax over the wave's current tile: masked scores past `lim0` (relative to the
+  // tile's first key and lane half), when `mask`
+  auto fold = [&](QGroup<T, DH> &q, bool mask, int lim0) {
+    auto scores = [&]() {
+      f32x16 s = score_tile<T, DH>(&kw[lc * LDK + g * M::KPL], q.qf);
+      if (mask) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (acc_row(v, 0) > lim0) s[v] = NEG_INF;
+      }
+      return s;
+    };
+    if constexpr (TRV) softmax_pv<T, DH>(scores, q.st, VRowTr{(const bf16 *)vw + tr_src<32>(0, lane)});
+    else softmax_pv<T, DH>(scores, q.st, VtRow<T, DH>{lc < DH ? &vw[lc * LDW] : nullptr, g});
+  };
+  if (sub0 < sub1) load(sub0);
+  for (int sub = sub0; sub < sub1; ++sub) {
+    wait_lgkm0();
+    store();
+    if (sub + 1 < sub1) load(sub + 1);
+    wait_lgkm0();
+    const int kb = sub * 32;
+    fold(A, kb + 31 > p0 || kb + 32 > n_keys, min(qpos, n_keys - 1) - kb - 4 * g);
+    fold(B, kb + 32 > n_keys, n_keys - 1 - kb - 4 * g);
+  }
+
+  // ---- group B: the candidates' own NS keys (block-diagonal causal), on the last wave ---------
+  if (wave == NWA - 1) {
+    const int n_own = min(cpw, b.n_cand) * b.R;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int ch = lane + 64 * i;
+      const int ks = ch / CPK, c0 = (ch - ks * CPK) * EPC;
+      const int kc = ks / b.R, j2 = ks - kc * b.R;
+      pk[i] = u32x4{0, 0, 0, 0};
+      pv[i] = u32x4{0, 0, 0, 0};
+      if (ch < 32 * CPK && ks < n_own) {
+        const long long off = (long long)(grp * b.n_cand + kc) * b.own_sb + h * b.own_sh + (long long)j2 * DH + c0;
+        pk[i] = ld16((const T *)b.k_own + off);
+        pv[i] = ld16((const T *)b.v_own + off);
+      }
+    }
+    wait_lgkm0();
+    store();
+    wait_lgkm0();
+    auto scores = [&]() {
+      f32x16 s = score_tile<T, DH>(&kw[lc * LDK + g * M::KPL], B.qf);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int ks = acc_row(v, g);
+        const int kc = ks / b.R, j2 = ks - kc * b.R;
+        if (!(ks < n_own && kc == B.cslot && j2 <= B.qi)) s[v] = NEG_INF;
+      }
+      return s;
+    };
+    if constexpr (TRV) softmax_pv<T, DH>(scores, B.st, VRowTr{(const bf16 *)vw + tr_src<32>(0, lane)});
+    else softmax_pv<T, DH>(scores, B.st, VtRow<T, DH>{lc < DH ? &vw[lc * LDW] : nullptr, g});
+  }
+
+  // ---- merge each group's partial states: wave 0 group A, wave 1 group B ----------------------
+  const float ltA = A.st.lsum + other_half(A.st.lsum), ltB = B.st.lsum + other_half(B.st.lsum);
+  __syncthreads();   // every wave is done with its tiles
+  for (int gi = 0; gi < 2; ++gi) {
+    const QGroup<T, DH> &q = gi ? B : A;
+    unsigned char *gb = smem + gi * GROUP_BYTES;
+    float (*s_o)[16][64] = (float (*)[16][64])gb;
+    float (*s_m)[32] = (float (*)[32])(gb + NWA * 16 * 64 * 4);
+    float (*s_l)[32] = (float (*)[32])(gb + NWA * (16 * 64 + 32) * 4);
+    if (g == 0) {
+      s_m[wave][lc] = q.st.m;
+      s_l[wave][lc] = gi ? ltB : ltA;
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s_o[wave][v][lane] = q.st.o[v];
+  }
+  __syncthreads();
+  if (wave > 1) return;
+  const QGroup<T, DH> &q = wave ? B : A;
+  const AttnArgs &ar = wave ? b : a;
+  unsigned char *gb = smem + wave * GROUP_BYTES;
+  float (*s_o)[16][64] = (float (*)[16][64])gb;
+  float (*s_m)[32] = (float (*)[32])(gb + NWA * 16 * 64 * 4);
+  float (*s_l)[32] = (float (*)[32])(gb + NWA * (16 * 64 + 32) * 4);
+  T *stage = (T *)(smem + 2 * GROUP_BYTES) + wave * TS::SIZE;
+  float mx = s_m[0][lc];
+#pragma unroll
+  for (int w = 1; w < NWA; ++w) mx = fmaxf(mx, s_m[w][lc]);
+  float l = 0.0f;
+  f32x16 o = f32x16{};
+#pragma unroll
+  for (int w = 0; w < NWA; ++w) {
+    const float sc = __builtin_amdgcn_exp2f(s_m[w][lc] - mx);
+    l += sc * s_l[w][lc];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o[v] += sc * s_o[w][v][lane];
+  }
+  const float inv = q.valid ? 1.0f / l : 0.0f;
+  if (ar.lse && q.valid && g == 0) ar.lse[((long long)q.z * ar.n_heads + h) * ar.R + q.qi] = mx + log2f(l);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) o[v] *= inv;
+  TS::put(stage, o, lc, g);
+#pragma unroll
+  for (int k = 0; k < TS::NI; ++k) {
+    const int tok = TS::token(k, lane);
+    const int tz = __shfl(q.z, tok, 64), tq = __shfl(q.qi, tok, 64);
+    const bool tv = __shfl((int)q.valid, tok, 64) != 0;
+    const u32x4 piece = TS::get(stage, k, lane);
+    const int f = TS::feature(lane);
+    if (tv && f < DH) st16((T *)ar.o + tz * ar.o_sb + (long long)tq * ar.d_model + h * DH + f, piece);
+  }
+}
+
 template <typename T, int DH>
 hipError_t launch_dh(int stage2, const AttnArgs &a, hipStream_t s) {
   dim3 bd(ATTN_WAVES * 64);
@@ -637,6 +860,19 @@ hipError_t launch_dh(int stage2, const AttnArgs &a, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_attn_pair(int dtype, int d_head, const AttnArgs &a, const AttnArgs &b, hipStream_t s) {
+  if (a.n_seq_grp * a.n_heads == 0) return hipSuccess;
+  const dim3 grid(a.n_seq_grp * a.n_heads), bd(ATTN_WAVES * 64);
+  if (dtype == 1) {
+    if (d_head == 16) hipLaunchKernelGGL((attn_pair_kernel<bf16, 16>), grid, bd, 0, s, a, b);
+    else hipLaunchKernelGGL((attn_pair_kernel<bf16, 32>), grid, bd, 0, s, a, b);
+  } else {
+    if (d_head == 16) hipLaunchKernelGGL((attn_pair_kernel<float, 16>), grid, bd, 0, s, a, b);
+    else hipLaunchKernelGGL((attn_pair_kernel<float, 32>), grid, bd, 0, s, a, b);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_attn(int dtype, int d_head, int stage2, const AttnArgs &a, hipStream_t s) {
   if (a.n_qblocks * a.n_seq_grp * a.n_heads == 0) return hipSuccess;

@@ -19,6 +19,9 @@ int qkv_max_split(int d_model);
 constexpr int QKV_SPLIT_TARGET = 512;   // workgroups a split launch aims at (two per CU)
 
 hipError_t launch_attn(int dtype, int d_head, int stage2, const AttnArgs &a, hipStream_t s);
+// Append rows (a: forward mode, R <= 32) and Stage II of the same users (b: n_cand * R <= 32) over
+// the same prefix keys (a.n_pre == b.n_pre, same K/V and seq_shift), one pass over the keys.
+hipError_t launch_attn_pair(int dtype, int d_head, const AttnArgs &a, const AttnArgs &b, hipStream_t s);
 
 // Fused post-attention kernel; tokens per workgroup tile for a dtype / d_model.
 hipError_t launch_post(int dtype, int resid_f32, const PostArgs &a, int grid, hipStream_t s);

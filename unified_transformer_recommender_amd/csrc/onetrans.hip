@@ -236,7 +236,47 @@ struct Step {
                           // (or user) z start seq_shift[z] rows later
   float *lse;             // or null: per-query base-2 log-sum-exp of the attention scores
   bool no_post;           // stop after the attention (the training step's recomputation)
+  int only;               // 0: every phase; else the phases to run (STEP_QKV | STEP_ATTN | STEP_POST)
 };
+constexpr int STEP_QKV = 1, STEP_ATTN = 2, STEP_POST = 4;
+
+// The attention arguments of a step (its Q and O in the step's workspace).
+AttnArgs step_attn_args(const Dims &D, const Step &st, char *ws, const Ws &L) {
+  const int d = D.d, H = D.H, dh = D.dh;
+  const int p0 = st.s - st.q, R = st.q + st.ns;
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.n_heads = H;
+  a.d_model = d;
+  a.R = R;
+  a.p0 = p0;
+  a.n_pre = st.n_pre;
+  a.q = ws + L.q;
+  a.q_sb = (long long)H * R * dh;
+  a.q_sh = (long long)R * dh;
+  a.k_pre = st.kp;
+  a.v_pre = st.vp;
+  a.pre_sb = st.pre_sb;
+  a.pre_sh = st.pre_sh;
+  a.o = ws + L.o;
+  a.o_sb = (long long)R * d;
+  a.seq_shift = st.seq_shift;
+  a.lse = st.lse;
+  if (st.stage2) {
+    a.n_seq_grp = st.n_grp;
+    a.n_cand = st.n_cand;
+    a.k_own = st.kN.base;
+    a.v_own = st.vN.base;
+    a.own_sb = st.own_sb;
+    a.own_sh = st.own_sh;
+    const int cpw = 32 / st.ns;
+    a.n_qblocks = (st.n_cand + ATTN_WAVES * cpw - 1) / (ATTN_WAVES * cpw);
+  } else {
+    a.n_seq_grp = st.n_seq;
+    a.n_qblocks = (R + ATTN_QBLOCK - 1) / ATTN_QBLOCK;
+  }
+  return a;
+}
 
 int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, char *ws, const Ws &L,
              hipStream_t stream) {
@@ -247,10 +287,11 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
   int rc;
 
   const HeadView q_v{qb, (long long)H * R * dh, (long long)R * dh, p0};
+  const int only = st.only ? st.only : STEP_QKV | STEP_ATTN | STEP_POST;
 
   // pre-norm 1 + mixed Q/K/V: K/V for the S rows [kv_t0, kv_t0 + kv_n) and the NS rows, Q for the
   // rows at positions >= p0 (tail S rows and NS rows)
-  {
+  if (only & STEP_QKV) {
     QkvArgs qa;
     memset(&qa, 0, sizeof(qa));
     const int no_q = 0x7fffffff;
@@ -308,42 +349,12 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
   if (!st.need_out) return ONETRANS_OK;
 
   // attention
-  {
-    AttnArgs a;
-    memset(&a, 0, sizeof(a));
-    a.n_heads = H;
-    a.d_model = d;
-    a.R = R;
-    a.p0 = p0;
-    a.n_pre = st.n_pre;
-    a.q = qb;
-    a.q_sb = q_v.sb;
-    a.q_sh = q_v.sh;
-    a.k_pre = st.kp;
-    a.v_pre = st.vp;
-    a.pre_sb = st.pre_sb;
-    a.pre_sh = st.pre_sh;
-    a.o = ob;
-    a.o_sb = (long long)R * d;
-    a.seq_shift = st.seq_shift;
-    a.lse = st.lse;
-    if (st.stage2) {
-      a.n_seq_grp = st.n_grp;
-      a.n_cand = st.n_cand;
-      a.k_own = st.kN.base;
-      a.v_own = st.vN.base;
-      a.own_sb = st.own_sb;
-      a.own_sh = st.own_sh;
-      const int cpw = 32 / st.ns;
-      a.n_qblocks = (st.n_cand + ATTN_WAVES * cpw - 1) / (ATTN_WAVES * cpw);
-    } else {
-      a.n_seq_grp = st.n_seq;
-      a.n_qblocks = (R + ATTN_QBLOCK - 1) / ATTN_QBLOCK;
-    }
+  if (only & STEP_ATTN) {
+    const AttnArgs a = step_attn_args(D, st, ws, L);
     if (timed(ONETRANS_K_ATTN, stream, [&] { return launch_attn(D.dt, dh, st.stage2, a, stream); }) != hipSuccess)
       return ONETRANS_ERR_HIP;
   }
-  if (st.no_post) return ONETRANS_OK;
+  if (st.no_post || !(only & STEP_POST)) return ONETRANS_OK;
 
   // W^O + residual + norm2 + mixed FFN + residual, fused, over the query rows:
   // tail S rows use parameter set 0, NS token j uses set 1 + j
@@ -790,6 +801,101 @@ int score_run(const Dims &D, const onetrans_block_weights *blk, const onetrans_k
     x = RowView{w + L.x[n & 1], (long long)ns * d, 0, d};
     stats = st.stats_out;
     x_f32 = 1;
+  }
+  return ONETRANS_OK;
+}
+
+// A cross-request append followed by the scoring of the same users' candidates, block by block
+// (unpyramided cache; d_l <= 32 appended rows and n_cand * l_ns <= 32 NS rows per user): per block
+// the append's QKV (its K/V into the cache), Stage II's QKV, one attention pass over the user's keys
+// for both (attn_pair_kernel: the cache is read once), then both post launches. Stage II of block
+// n needs block n's appended K/V and block n - 1's Stage II output, both ready at that point, so
+// the result equals append_run followed by score_run. Workspaces: wa laid out as La (append), wb as
+// Lb (Stage II).
+int append_score_run(const Dims &D, const onetrans_block_weights *blk, const onetrans_kv_cache *cache,
+                     const void *x_new, int n_users, int d_l, void *out_new, const void *x_ns, int n_cand,
+                     void *out_ns, char *wa, const Ws &La, char *wb, const Ws &Lb, int l_old, hipStream_t stream) {
+  int rc;
+  const bool ragged = cache->user_len != nullptr;
+  if (ragged && (rc = upload_user_len(cache, n_users, wa, La, stream))) return rc;
+  // ragged users: positions relative to each user's own (pre-append) cached length; Stage II's key
+  // count is the same user's length after the append, which the pair kernel takes from the append
+  const int *shift = ragged ? (const int *)(wa + La.seq) : nullptr;
+  const int d = D.d, H = D.H, dh = D.dh, ns = D.lns;
+  const int s_new = l_old + d_l;          // cached rows after the append (ragged: relative)
+  RowView xa{const_cast<void *>(x_new), (long long)d_l * d, l_old, d};
+  RowView xb{const_cast<void *>(x_ns), (long long)ns * d, s_new, d};
+  int xa_f32 = D.dt == ONETRANS_F32, xb_f32 = xa_f32;
+  void *sa = nullptr, *sb = nullptr;      // (mean, rstd) rows of the inputs when written
+  for (int n = 0; n < D.N; ++n) {
+    const bool last = n + 1 == D.N;
+    Step A{};
+    A.n_seq = n_users;
+    A.s = s_new;
+    A.q = d_l;
+    A.kv_t0 = l_old;
+    A.kv_n = d_l;
+    A.in_t0 = l_old;
+    A.in_n = d_l;
+    A.x = xa;
+    A.x_f32 = xa_f32;
+    A.kS = cache_view(D, cache, cache->k, n);
+    A.vS = cache_view(D, cache, cache->v, n);
+    A.kN = A.kS;
+    A.vN = A.vS;
+    A.n_pre = s_new;
+    A.kp = A.kS.base;
+    A.vp = A.vS.base;
+    A.pre_sb = A.kS.sb;
+    A.pre_sh = A.kS.sh;
+    A.out = last ? RowView{out_new, (long long)d_l * d, l_old, d} : RowView{wa + La.x[n & 1], (long long)d_l * d, l_old, d};
+    A.kv_shift = shift;
+    A.seq_shift = shift;
+    A.stats_in = sa;
+    A.stats_out = last ? nullptr : (void *)(wa + La.st[n & 1]);
+    A.need_out = true;
+    Step B{};
+    B.n_seq = n_users * n_cand;
+    B.s = s_new;
+    B.ns = ns;
+    B.in_t0 = s_new;
+    B.in_n = ns;
+    xb.t_off = s_new;
+    B.x = xb;
+    B.x_f32 = xb_f32;
+    B.kN = HeadView{wb + Lb.k, (long long)H * ns * dh, (long long)ns * dh, s_new};
+    B.vN = HeadView{wb + Lb.v, (long long)H * ns * dh, (long long)ns * dh, s_new};
+    B.kS = B.kN;
+    B.vS = B.vN;
+    B.stage2 = 1;
+    B.n_grp = n_users;
+    B.n_cand = n_cand;
+    B.n_pre = s_new;
+    B.kp = A.kp;
+    B.vp = A.vp;
+    B.pre_sb = A.pre_sb;
+    B.pre_sh = A.pre_sh;
+    B.own_sb = B.kN.sb;
+    B.own_sh = B.kN.sh;
+    B.out = RowView{last ? out_ns : (void *)(wb + Lb.x[n & 1]), (long long)ns * d, s_new, d};
+    B.stats_in = sb;
+    B.stats_out = last ? nullptr : (void *)(wb + Lb.st[n & 1]);
+    B.need_out = true;
+
+    A.only = B.only = STEP_QKV;
+    if ((rc = run_step(D, blk[n], A, wa, La, stream)) || (rc = run_step(D, blk[n], B, wb, Lb, stream))) return rc;
+    {
+      const AttnArgs aa = step_attn_args(D, A, wa, La), ab = step_attn_args(D, B, wb, Lb);
+      if (timed(ONETRANS_K_ATTN, stream, [&] { return launch_attn_pair(D.dt, dh, aa, ab, stream); }) != hipSuccess)
+        return ONETRANS_ERR_HIP;
+    }
+    A.only = B.only = STEP_POST;
+    if ((rc = run_step(D, blk[n], A, wa, La, stream)) || (rc = run_step(D, blk[n], B, wb, Lb, stream))) return rc;
+    xa = RowView{wa + La.x[n & 1], (long long)d_l * d, l_old, d};
+    xb = RowView{wb + Lb.x[n & 1], (long long)ns * d, 0, d};
+    sa = A.stats_out;
+    sb = B.stats_out;
+    xa_f32 = xb_f32 = 1;
   }
   return ONETRANS_OK;
 }
@@ -1521,6 +1627,11 @@ extern "C" {
 size_t onetrans_workspace_bytes(const onetrans_config *cfg, int op, int n_seq, int l_s, int n_cand, int d_l) {
   Dims D;
   if (check_cfg(cfg, D)) return 0;
+  if (op == ONETRANS_OP_APPEND_SCORE) {   // the append's workspace, then Stage II's
+    const size_t wa = onetrans_workspace_bytes(cfg, ONETRANS_OP_APPEND, n_seq, 0, 0, d_l);
+    const size_t wb = onetrans_workspace_bytes(cfg, ONETRANS_OP_SCORE, n_seq, 0, n_cand, 0);
+    return wa && wb ? al(wa) + wb : 0;
+  }
   size_t n, tin, rq;
   bool kv;
   if (!ws_dims(cfg, D, op, n_seq, l_s, n_cand, d_l, n, tin, rq, kv)) return 0;
@@ -1770,6 +1881,68 @@ int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weig
   } else {
     for (int b = 0; b < n_head; ++b) cache->layer_len[b] = l_new;
     cache->q_last = q_last_new;
+  }
+  return ONETRANS_OK;
+}
+
+int onetrans_append_score(const onetrans_config *cfg, const onetrans_block_weights *blk, onetrans_kv_cache *cache,
+                          const void *x_new, int n_users, int d_l, void *out_new, const void *x_ns, int n_cand,
+                          void *out_ns, void *ws, size_t ws_bytes, hipStream_t stream) {
+  Dims D;
+  int rc;
+  if ((rc = check_score(cfg, blk, cache, x_ns, n_users, n_cand, out_ns, D))) return rc;
+  if (d_l < 1) return ONETRANS_ERR_SHAPE;
+  if (!x_new || !out_new) return ONETRANS_ERR_INVALID_ARG;
+  if (misaligned(x_new) || misaligned(out_new)) return ONETRANS_ERR_ALIGNMENT;
+  // one pass over a user's keys for both query sets: at most 32 appended rows and 32 NS rows per
+  // user, and an unpyramided cache (every block holds the whole sequence)
+  if (d_l > 32 || (long long)n_cand * D.lns > 32) return ONETRANS_ERR_UNSUPPORTED;
+  const int q_last = cache->q_last > 0 ? cache->q_last : cache->layer_len[D.N - 1];
+  for (int n = 0; n < D.N; ++n) {
+    const int qn = n + 1 < D.N ? cache->layer_len[n + 1] : q_last;
+    if (qn != cache->layer_len[n]) return ONETRANS_ERR_UNSUPPORTED;
+  }
+  const bool ragged = cache->user_len != nullptr;
+  if (ragged) {
+    for (int u = 0; u < n_users; ++u)
+      if ((long long)cache->user_len[u] + d_l > cache->capacity) return ONETRANS_ERR_CACHE_CAPACITY;
+  } else if ((long long)cache->layer_len[0] + d_l > cache->capacity) {
+    return ONETRANS_ERR_CACHE_CAPACITY;
+  }
+  if ((rc = check_size(D, n_users, d_l))) return rc;
+  if (!ws) return ONETRANS_ERR_INVALID_ARG;
+  if (misaligned(ws)) return ONETRANS_ERR_ALIGNMENT;
+  const size_t wa_bytes = onetrans_workspace_bytes(cfg, ONETRANS_OP_APPEND, n_users, 0, 0, d_l);
+  if (ws_bytes < onetrans_workspace_bytes(cfg, ONETRANS_OP_APPEND_SCORE, n_users, 0, n_cand, d_l))
+    return ONETRANS_ERR_WORKSPACE;
+  size_t n, tin_a, rq_a, tin_b, rq_b;
+  bool kv_a, kv_b;
+  ws_dims(cfg, D, ONETRANS_OP_APPEND, n_users, 0, 0, d_l, n, tin_a, rq_a, kv_a);
+  ws_dims(cfg, D, ONETRANS_OP_SCORE, n_users, 0, n_cand, 0, n, tin_b, rq_b, kv_b);
+  const int parts = parts_for(n_users, USER_PART_MIN);
+  const size_t n_call_b = (size_t)n_users * n_cand;
+  const size_t pa = ws_layout(D, (n_users + parts - 1) / parts, tin_a, rq_a, kv_a, n_users).total;
+  const size_t pb = ws_layout(D, (size_t)((n_users + parts - 1) / parts) * n_cand, tin_b, rq_b, kv_b, n_call_b).total;
+  char *wb0 = (char *)ws + al(wa_bytes);
+  const int l_old = ragged ? 0 : cache->layer_len[0];
+  const size_t in_a = (size_t)d_l * D.d * D.esz, out_a = (size_t)d_l * D.d * 4;
+  const size_t in_b = (size_t)n_cand * D.lns * D.d * D.esz, out_b = (size_t)n_cand * D.lns * D.d * 4;
+  rc = over_streams(n_users, parts, stream, [&](int first, int count, int part, hipStream_t st) {
+    const onetrans_kv_cache view = user_view(D, cache, first);
+    return append_score_run(D, blk, &view, (const char *)x_new + first * in_a, count, d_l, (char *)out_new + first * out_a,
+                            (const char *)x_ns + first * in_b, n_cand, (char *)out_ns + first * out_b,
+                            (char *)ws + part * pa, ws_layout(D, count, tin_a, rq_a, kv_a, n_users), wb0 + part * pb,
+                            ws_layout(D, (size_t)count * n_cand, tin_b, rq_b, kv_b, n_call_b), l_old, st);
+  });
+  if (rc) return rc;
+  if (ragged) {
+    int longest = 0;
+    for (int u = 0; u < n_users; ++u) longest = max(longest, cache->user_len[u] += d_l);
+    for (int b = 0; b < D.N; ++b) cache->layer_len[b] = max(cache->layer_len[b], longest);
+    cache->q_last = cache->layer_len[D.N - 1];
+  } else {
+    for (int b = 0; b < D.N; ++b) cache->layer_len[b] = l_old + d_l;
+    cache->q_last = l_old + d_l;
   }
   return ONETRANS_OK;
 }
