@@ -31,7 +31,7 @@ CSRC = os.path.join(PKG, "csrc")
 # kernel class -> (substrings of the kernel symbols, source files)
 KERNELS = {
     "qkv": (("qkv_kernel",), ("qkv.hip",)),
-    "attn": (("attn_kernel", "attn_split_kernel"), ("attn.hip",)),
+    "attn": (("attn_kernel", "attn_split_kernel", "attn_pair_kernel"), ("attn.hip",)),
     "post": (("post_kernel", "post_reduce_kernel", "post_f32w_kernel", "post_pair_kernel"),
              ("post.hip", "post_f32w.hip", "post_pair.hip")),
     "lin": (("lin_kernel",), ("tok.hip",)),
