@@ -57,8 +57,11 @@ def test_workspace_and_cache_sizes():
     d, T, R = 256, 136, 116
     al = lambda n: (n + 255) // 256 * 256
     part = al(B * R * 8 * d * 4)          # partial sums of split post launches (8 splits; at most 32 MiB)
+    # bf16 rows normalised by each post launch for the next block's QKV launch, in 32-row groups of
+    # each parameter group: at most one partial group per NS token and one for the S rows
+    handoff = al((B * R + 32 * (16 + 1)) * d * 2)
     expect = (2 * al(B * R * d * 4) + 2 * al(B * R * 8) + al(B * R * d * 2) + 2 * al(B * T * d * 2) + al(B * R * d * 2)
-              + al(16) + al(B * 4) + part)
+              + al(16) + al(B * 4) + part + handoff)
     assert got == expect
     assert lib.onetrans_kv_cache_bytes(ctypes.byref(c), 3, 200) == 3 * 2 * 8 * 200 * 32 * 2
     assert lib.onetrans_workspace_bytes(ctypes.byref(c), L.OP_SCORE, 2, 0, 5, 0) > 0

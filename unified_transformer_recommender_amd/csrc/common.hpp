@@ -262,6 +262,7 @@ struct QkvJob {
   int m_tiles;             // token tiles per group
   int q_from;              // first position that issues a query
   HeadView k, v, q;        // head-split outputs
+  int xh_g0;               // first 32-row group of this job's rows in `xh`
 };
 
 struct QkvArgs {
@@ -280,6 +281,8 @@ struct QkvArgs {
   float q_scale;           // queries are stored multiplied by this (log2(e) / sqrt(d_head))
   void *trash;             // 16 bytes that masked-off output pieces are written to
   const int *kv_shift;     // [n_seq] or null: K/V row t of sequence b is stored at row t + kv_shift[b]
+  const void *xh;          // bf16: the normalised rows in fragment order (xh_piece), written by the
+                           // previous block's post-attention kernel; null: norm 1 runs here
 };
 
 // ---------------------------------------------------------------------------------------------
@@ -290,6 +293,7 @@ struct PostJob {
   RowSet rs;
   int tile_start;          // first workgroup of this job
   int m_tiles;             // token tiles per group
+  int xh_g0;               // first 32-row group of this job's rows in `xh`
 };
 
 struct PostArgs {
@@ -308,7 +312,24 @@ struct PostArgs {
                            // hidden chunks (1: one workgroup does the whole FFN)
   RowView part;            // n_split > 1: partial X' rows of split s at part.base + s * part_split
   long long part_split;    // elements (fp32; compact rows by (sequence, position)); a reduce launch adds them
+  void *xh;                // bf16, n_split == 1: where to write the next block's norm-1 output of X'
+                           // in fragment order (xh_piece); null: none
+  const void *xh_gamma, *xh_beta;   // the next block's norm-1 parameters [d]
+  int out_from;            // X' rows at output positions (t - out.t_off) below this are not stored:
+                           // the next block reads them only through `xh` (0: store every row)
 };
+
+// Normalised rows handed from a block's post-attention kernel to the next block's QKV kernel
+// (bf16). Both launches enumerate a parameter group's rows in the same order r (a block's output
+// rows are the next block's input rows); rows 32 G .. 32 G + 31 of group grp of a job form row
+// group xh_g0 + grp * ceil(M / 32) + G, where M is the job's rows per group. A row group stores,
+// for each 16-feature k-chunk kc, the 64 lanes' MFMA B fragments in lane order: lane (g, lc)
+// holds features 16 kc + 8 g .. 16 kc + 8 g + 7 of row 32 G + lc. One wave reads a k-chunk of its
+// 32 rows as one contiguous 1 KB load. Returns the index of the 16-byte piece.
+__device__ __forceinline__ size_t xh_piece(int xh_g0, int grp, int m_rows, int G, int kcs, int kc, int lane) {
+  const int per_grp = (m_rows + 31) >> 5;
+  return ((size_t)(xh_g0 + grp * per_grp + G) * kcs + kc) * 64 + lane;
+}
 
 // ---------------------------------------------------------------------------------------------
 // Attention launch.

@@ -141,7 +141,13 @@ int check_weights(const onetrans_block_weights *blk, const Dims &D) {
 struct Ws {
   size_t x[2], st[2], q, k, v, o, trash, seq, part, total;
   size_t part_rows;   // rows per split of the partial-sum buffer (0: no split post launches)
+  size_t xh;          // normalised rows handed from a post launch to the next block's QKV launch
+  bool has_xh;
 };
+
+// Block chains that hand each block's normalised input from the previous block's post-attention
+// kernel to its QKV kernel: bf16 storage at the widths the single-wave post kernel serves.
+inline bool handoff_dims(const Dims &D) { return D.dt == ONETRANS_BF16 && D.d <= 256; }
 
 inline size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
 
@@ -154,8 +160,8 @@ inline bool post_split_call(const Dims &D, size_t n_call, size_t rq) {
 }
 
 // n: sequences; tin: max block input rows; rq: max query rows; kv: K/V buffers needed;
-// n_call: sequences of the whole call (n is one part of it)
-Ws ws_layout(const Dims &D, size_t n, size_t tin, size_t rq, bool kv, size_t n_call) {
+// n_call: sequences of the whole call (n is one part of it); xh: room for the normalised-row handoff
+Ws ws_layout(const Dims &D, size_t n, size_t tin, size_t rq, bool kv, size_t n_call, bool xh = false) {
   Ws w{};
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -183,6 +189,10 @@ Ws ws_layout(const Dims &D, size_t n, size_t tin, size_t rq, bool kv, size_t n_c
   // partial sums of post launches split over the FFN's hidden chunks (small launches only)
   w.part_rows = post_split_call(D, n_call, rq) ? n * rq : 0;
   w.part = take(w.part_rows * POST_MAX_SPLIT * d * 4);
+  // a block's n * rq query rows in 32-row groups per parameter group: the S rows' groups plus at
+  // most one partial group for each of the l_ns NS groups and the S group; bf16
+  w.has_xh = xh && handoff_dims(D);
+  w.xh = w.has_xh ? take((n * rq + 32 * (size_t)(D.lns + 1)) * d * 2) : 0;
   w.total = off;
   return w;
 }
@@ -237,6 +247,12 @@ struct Step {
   float *lse;             // or null: per-query base-2 log-sum-exp of the attention scores
   bool no_post;           // stop after the attention (the training step's recomputation)
   int only;               // 0: every phase; else the phases to run (STEP_QKV | STEP_ATTN | STEP_POST)
+  const void *xh_in;      // or null: the block input's normalised rows, handed over by the previous post launch
+  void *xh_out;           // or null: where the post launch may hand over the next block's normalised rows
+  const void *xh_gamma, *xh_beta;   // the next block's norm-1 parameters
+  int xh_keep;            // with xh_out: the first output row the next block reads as a residual
+                          // (its first query row); the rows before it are read only through xh_out
+  bool *xh_written;       // set when the post launch wrote xh_out
 };
 constexpr int STEP_QKV = 1, STEP_ATTN = 2, STEP_POST = 4;
 
@@ -296,7 +312,7 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
     memset(&qa, 0, sizeof(qa));
     const int no_q = 0x7fffffff;
     int nj = 0, bm = 0;
-    long long tiles = 0;
+    long long tiles = 0, groups = 0;
     auto add_job = [&](RowSet rs, int q_from, HeadView k, HeadView v) {
       const long long m = (long long)rs.n_seq * rs.rows;
       if (m == 0 || rs.n_groups == 0) return;
@@ -309,10 +325,13 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
       j.m_tiles = (int)((m + bm - 1) / bm);
       j.tile_start = (int)tiles;
       tiles += (long long)j.m_tiles * rs.n_groups;
+      j.xh_g0 = (int)groups;
+      groups += (m + 31) / 32 * rs.n_groups;
     };
     auto add_jobs = [&](int tg) {
       nj = 0;
       tiles = 0;
+      groups = 0;
       bm = qkv_tokens_per_tile(tg);
       qa.tg = tg;
       if (st.kv_n > 0) add_job(RowSet{st.n_seq, st.kv_n, 1, st.kv_t0, 0, 0}, st.need_out ? p0 : no_q, st.kS, st.vS);
@@ -343,6 +362,7 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
     qa.q_scale = 1.4426950408889634f / sqrtf((float)dh);
     qa.trash = ws + L.trash;
     qa.kv_shift = st.kv_shift;
+    qa.xh = st.xh_in;
     const hipError_t e = timed(ONETRANS_K_QKV, stream, [&] { return launch_qkv(D.dt, st.x_f32, qa, (int)tiles, stream); });
     if (e != hipSuccess) return ONETRANS_ERR_HIP;
   }
@@ -363,7 +383,7 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
     memset(&pa, 0, sizeof(pa));
     const int bm = post_tokens_per_tile(D.dt, d);
     int nj = 0;
-    long long tiles = 0;
+    long long tiles = 0, groups = 0;
     auto add_job = [&](RowSet rs) {
       const long long m = (long long)rs.n_seq * rs.rows;
       if (m == 0 || rs.n_groups == 0) return;
@@ -372,6 +392,8 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
       j.m_tiles = (int)((m + bm - 1) / bm);
       j.tile_start = (int)tiles;
       tiles += (long long)j.m_tiles * rs.n_groups;
+      j.xh_g0 = (int)groups;
+      groups += (m + 31) / 32 * rs.n_groups;
     };
     if (st.q > 0) add_job(RowSet{st.n_seq, st.q, 1, p0, 0, 0});
     if (st.ns > 0) add_job(RowSet{st.n_seq, 1, st.ns, st.s, 1, 1});
@@ -406,7 +428,16 @@ int run_step(const Dims &D, const onetrans_block_weights &w, const Step &st, cha
       pa.part = RowView{ws + L.part, (long long)R * d, p0, d};
       pa.part_split = (long long)L.part_rows * d;
     }
+    // hand the next block's normalised rows over (the whole-FFN launches of the single-wave kernel);
+    // the next block's row groups are this launch's: its input rows are these query rows, in order
+    if (st.xh_out && pa.n_split == 1 && handoff_dims(D)) {
+      pa.xh = st.xh_out;
+      pa.xh_gamma = st.xh_gamma;
+      pa.xh_beta = st.xh_beta;
+      pa.out_from = st.xh_keep;
+    }
     hipError_t e = timed(ONETRANS_K_POST, stream, [&] { return launch_post(D.dt, st.x_f32, pa, (int)tiles, stream); });
+    if (e == hipSuccess && pa.xh && st.xh_written) *st.xh_written = true;
     if (e == hipSuccess && pa.n_split > 1)
       e = timed(ONETRANS_K_POST, stream, [&] { return launch_post_reduce(pa, (int)rows, stream); });
     if (e != hipSuccess) return ONETRANS_ERR_HIP;
@@ -645,6 +676,7 @@ int forward_run(const Dims &D, const onetrans_config *cfg, const onetrans_block_
   RowView x{const_cast<void *>(x0), (long long)(l_s + D.lns) * d, 0, d};
   int x_f32 = D.dt == ONETRANS_F32;
   void *stats = nullptr;   // (mean, rstd) rows of x when the previous block wrote them
+  bool handed = false;     // the previous block's post launch wrote x's normalised rows to L.xh
   for (int n = 0; n < D.N; ++n) {
     const int q = cfg->s_queries[n];
     const int T = s + D.lns, R = q + D.lns, p0 = s - q;
@@ -673,9 +705,20 @@ int forward_run(const Dims &D, const onetrans_config *cfg, const onetrans_block_
     st.need_out = true;
     st.stats_in = stats;
     st.stats_out = n + 1 == D.N ? nullptr : (void *)(w + L.st[n & 1]);
+    // one handoff buffer: the next block's QKV launch reads it before its post launch rewrites it
+    bool wrote = false;
+    st.xh_in = handed ? w + L.xh : nullptr;
+    if (L.has_xh && n + 1 < D.N) {
+      st.xh_out = w + L.xh;
+      st.xh_gamma = blk[n + 1].norm1_g;
+      st.xh_beta = blk[n + 1].norm1_b;
+      st.xh_keep = q - cfg->s_queries[n + 1];
+      st.xh_written = &wrote;
+    }
     if ((rc = run_step(D, blk[n], st, w, L, stream))) return rc;
     x = RowView{w + L.x[n & 1], (long long)R * d, 0, d};
     stats = st.stats_out;
+    handed = wrote;
     x_f32 = 1;
     s = q;
   }
@@ -1638,7 +1681,8 @@ size_t onetrans_workspace_bytes(const onetrans_config *cfg, int op, int n_seq, i
   if ((op == ONETRANS_OP_FORWARD || op == ONETRANS_OP_PREFILL) && check_schedule(cfg, l_s)) return 0;
   const int parts = ws_parts_for(n_seq, op == ONETRANS_OP_FORWARD ? FORWARD_PART_MIN : USER_PART_MIN);
   const size_t per = op == ONETRANS_OP_SCORE ? (size_t)n_cand : 1;   // sequences per user
-  return ws_layout(D, (size_t)((n_seq + parts - 1) / parts) * per, tin, rq, kv, (size_t)n_seq * per).total * parts;
+  return ws_layout(D, (size_t)((n_seq + parts - 1) / parts) * per, tin, rq, kv, (size_t)n_seq * per,
+                   op == ONETRANS_OP_FORWARD).total * parts;
 }
 
 size_t onetrans_backward_workspace_bytes(const onetrans_config *cfg, int batch, int l_s) {
@@ -1692,13 +1736,13 @@ int onetrans_forward(const onetrans_config *cfg, const onetrans_block_weights *b
   const int wp = ws_parts_for(batch, FORWARD_PART_MIN), parts = parts_for(batch, FORWARD_PART_MIN);
   if (misaligned(ws)) return ONETRANS_ERR_ALIGNMENT;
   if (!ws) return ONETRANS_ERR_INVALID_ARG;
-  if (ws_bytes < ws_layout(D, (batch + wp - 1) / wp, tin, rq, kv, batch).total * wp) return ONETRANS_ERR_WORKSPACE;
-  const size_t part_bytes = ws_layout(D, (batch + parts - 1) / parts, tin, rq, kv, batch).total;
+  if (ws_bytes < ws_layout(D, (batch + wp - 1) / wp, tin, rq, kv, batch, true).total * wp) return ONETRANS_ERR_WORKSPACE;
+  const size_t part_bytes = ws_layout(D, (batch + parts - 1) / parts, tin, rq, kv, batch, true).total;
   const size_t in_row = (size_t)(l_s + D.lns) * D.d * D.esz;
   const size_t out_row = (size_t)(cfg->s_queries[D.N - 1] + D.lns) * D.d * 4;
   return over_streams(batch, parts, stream, [&](int first, int count, int part, hipStream_t st) {
     return forward_run(D, cfg, blk, (const char *)x0 + first * in_row, count, l_s, (char *)out + first * out_row,
-                       (char *)ws + part * part_bytes, ws_layout(D, count, tin, rq, kv, batch), st);
+                       (char *)ws + part * part_bytes, ws_layout(D, count, tin, rq, kv, batch, true), st);
   });
 }
 

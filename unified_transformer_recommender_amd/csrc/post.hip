@@ -94,6 +94,8 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64), (post_wgs_per_cu<T, D, LAYE
   __shared__ __attribute__((aligned(16))) float stage[NW][TS::SIZE];
   // per-feature / per-hidden-unit vectors of this parameter set, fp32: gamma, beta, b2 [d], b1 [d_ff]
   __shared__ __attribute__((aligned(16))) float svec[3 * D + POST_MAX_DFF];
+  // the next block's norm-1 gamma / beta, fp32, when this launch hands over normalised rows
+  __shared__ __attribute__((aligned(16))) float s_xg[D], s_xb[D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lc = lane & 31;
@@ -206,6 +208,12 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64), (post_wgs_per_cu<T, D, LAYE
     else v = to_f32(b1[i - 3 * D]);
     svec[i] = v;
   }
+  const bool hand = BF && !SPLIT && a.xh != nullptr;
+  if (hand)
+    for (int i = tid; i < D; i += NW * 64) {
+      s_xg[i] = to_f32(((const T *)a.xh_gamma)[i]);
+      s_xb[i] = LAYER ? to_f32(((const T *)a.xh_beta)[i]) : 0.0f;
+    }
 
   frag ofr[KC];
   {
@@ -359,8 +367,9 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64), (post_wgs_per_cu<T, D, LAYE
     }
   }
 
-  // ---- statistics of X' for the next block's norm 1 (exact two-pass over the registers) --------
-  if (!SPLIT && a.stats.base != nullptr) {
+  // ---- statistics of X' for the next block's norm 1 (exact two-pass over the registers), and
+  // that norm's output in the next QKV launch's fragment order --------------------------------
+  if (!SPLIT && (a.stats.base != nullptr || hand)) {
     float mean = 0.0f;
     if constexpr (LAYER) {
       float s = 0.0f;
@@ -380,10 +389,31 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64), (post_wgs_per_cu<T, D, LAYE
         ss += c * c;
       }
     ss += __shfl_xor(ss, 32, 64);
-    if (g == 0 && valid) {
+    const float rstd = 1.0f / sqrtf(ss * (1.0f / D) + a.eps);
+    if (a.stats.base != nullptr && g == 0 && valid) {
       float *sp = (float *)a.stats.base + b * a.stats.sb + (long long)(t - a.stats.t_off) * a.stats.rs;
       sp[0] = mean;
-      sp[1] = 1.0f / sqrtf(ss * (1.0f / D) + a.eps);
+      sp[1] = rstd;
+    }
+    if constexpr (BF && !SPLIT) {
+      if (hand) {
+        // the same arithmetic as the QKV kernel's norm of a stored X' row, so the fragments are
+        // those it would form itself
+        u32x4 *dst = (u32x4 *)a.xh + xh_piece(jb.xh_g0, grp, M_rows, (tm * NW + wave), KC, 0, lane);
+#pragma unroll
+        for (int ti = 0; ti < DT; ++ti)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            frag fr;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int f = 32 * ti + acc_row(8 * h + e, g);
+              fr[e] = (bf16)((acc[ti][8 * h + e] - mean) * rstd * s_xg[f] + s_xb[f]);
+            }
+            const u32x4 piece = __builtin_bit_cast(u32x4, natural_kfrag(fr));
+            if (valid) st16(dst + (2 * ti + h) * 64, piece);
+          }
+      }
     }
   }
 
@@ -396,7 +426,7 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64), (post_wgs_per_cu<T, D, LAYE
     for (int k = 0; k < TS::NI; ++k) {
       const int tok = TS::token(k, lane);
       const int tb = __shfl(b, tok, 64), tt = __shfl(t, tok, 64);
-      rv[k] = __shfl((int)valid, tok, 64) != 0;
+      rv[k] = __shfl((int)valid, tok, 64) != 0 && (SPLIT || tt - a.out.t_off >= a.out_from);
       const RowView &ov = SPLIT ? a.part : a.out;
       rowp[k] = (float *)ov.base + (SPLIT ? split * a.part_split : 0) + tb * ov.sb + (long long)(tt - ov.t_off) * ov.rs +
                 TS::feature(lane);

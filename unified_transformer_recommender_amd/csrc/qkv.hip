@@ -162,6 +162,24 @@ __global__ __launch_bounds__(QKV_NW * 64, (qkv_wgs_per_cu<T, D>())) void qkv_ker
   // registers. LayerNorm statistics are taken about the row's first element, which keeps the
   // one-pass variance free of cancellation. Token groups are normalised one after the other.
   frag xfr[TG][KC];
+  bool handed = false;
+  if constexpr (BF) {
+    // rows normalised by the previous block's post-attention kernel, already in fragment order:
+    // one contiguous 1 KB wave load per k-chunk. A row group wholly past the job's rows (the last
+    // tile's spare waves) reads the job's last group instead; its results are never stored.
+    if (a.xh != nullptr) {
+      handed = true;
+      const int last = ((M_rows + 31) >> 5) - 1;
+#pragma unroll
+      for (int tg = 0; tg < TG; ++tg) {
+        const int G = min((tm * NW + wave) * TG + tg, last);
+        const frag *src = (const frag *)a.xh + xh_piece(jb.xh_g0, grp, M_rows, G, KC, 0, lane);
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) xfr[tg][kc] = src[kc * 64];
+      }
+    }
+  }
+  if (!handed) {
 #pragma unroll
   for (int tg = 0; tg < TG; ++tg) {
     asm volatile("" ::: "memory");               // one group's row in flight at a time
@@ -265,6 +283,7 @@ __global__ __launch_bounds__(QKV_NW * 64, (qkv_wgs_per_cu<T, D>())) void qkv_ker
         }
       }
     }
+  }
   }
 
   // ---- chunk loop ----------------------------------------------------------------------------
