@@ -161,6 +161,40 @@ def test_layernorm_bf16_d256_two_stage_and_append():
     _append_case(replace(synth.test_workload("tiny3_append"), model=m, key="ln256_append"))
 
 
+# Calls whose query rows exceed the split-post bound (rows * 8 * d * 4 bytes of partials > 32 MiB)
+# run every post launch over the whole FFN, and each hands the next block its normalised input rows
+# as bf16 fragments (the QKV kernel then neither reads the fp32 rows nor normalises). Odd batches
+# leave partial 32-row groups in every parameter group; block 2 of the d = 256 case has enough tiles
+# for two token groups per wave, block 3 runs one.
+_HANDOFF_CASES = {
+    "d256_layer": dict(d=256, norm="layer", batch=31, l_s=1099, sq=(1099, 1000, 9), seq=(400, 400, 296),
+                       samples=(0, 17, 30)),
+    "d256_rms": dict(d=256, norm="rms", batch=31, l_s=1099, sq=(1099, 1000, 9), seq=(400, 400, 296),
+                     samples=(0, 30)),
+    "d128_layer": dict(d=128, norm="layer", batch=19, l_s=500, sq=(500, 300, 4), seq=(160, 170, 167),
+                       samples=(0, 9, 18)),
+    "d128_rms": dict(d=128, norm="rms", batch=19, l_s=500, sq=(500, 300, 4), seq=(160, 170, 167),
+                     samples=(0, 18)),
+    "d64_layer": dict(d=64, norm="layer", batch=37, l_s=460, sq=(460, 250, 3), seq=(150, 150, 157),
+                      samples=(0, 20, 36)),
+}
+
+
+@pytest.mark.parametrize("key", sorted(_HANDOFF_CASES))
+def test_forward_normalised_row_handoff(key):
+    c = _HANDOFF_CASES[key]
+    d, lns = c["d"], 16
+    rows = c["batch"] * (c["sq"][0] + lns)
+    assert rows * 8 * d * 4 > 32 << 20, "the call must be too large for split post launches"
+    base = synth.workload("onetrans_s")
+    m = replace(base.model, name=f"handoff_{key}", n_blocks=len(c["sq"]), d_model=d, n_heads=d // 32, d_ff=4 * d,
+                norm=c["norm"], norm_eps=1e-6 if c["norm"] == "rms" else 1e-5, dtype="bf16",
+                weight_seed=1300 + d + (c["norm"] == "layer"))
+    w = replace(base, model=m, l_s=c["l_s"], s_queries=c["sq"], seq_lens=c["seq"], batch=c["batch"],
+                key=f"handoff_{key}")
+    _forward_case(w, samples=c["samples"])
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_ragged_users_prefill_append_score(dtype):
     """Users with different cached lengths in one call (cache.user_len): padded prefill, append
