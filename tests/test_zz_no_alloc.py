@@ -84,7 +84,7 @@ def test_noalloc_full_user_at_onetrans_s_shape_then_ragged():
 def test_noalloc_refuses_calls_past_the_scratch():
     w = synth.workload("two_stage")
     mdl, cache = _prefilled(replace(w, n_users=1))
-    n_cand = 2048                                  # about twice what fits (1019 candidates at this shape)
+    n_cand = 2048                                  # about twice what fits (903 candidates at this shape)
     assert mdl.workspace_bytes(L.OP_SCORE, 1, n_cand=n_cand) > L.SCRATCH_BYTES
     xn = torch.zeros((1, n_cand, w.model.l_ns, w.model.d_model), dtype=mdl.torch_dtype, device=mdl.device)
     out = torch.empty((1, n_cand, w.model.l_ns, w.model.d_model), dtype=torch.float32, device=mdl.device)

@@ -806,6 +806,7 @@ int score_run(const Dims &D, const onetrans_block_weights *blk, const onetrans_k
   RowView x{const_cast<void *>(x_ns), (long long)ns * d, ragged ? 0 : cache->layer_len[0], d};
   int x_f32 = D.dt == ONETRANS_F32;
   void *stats = nullptr;   // (mean, rstd) rows of x when the previous block wrote them
+  bool handed = false;     // the previous block's post launch wrote x's normalised rows to L.xh
   for (int n = 0; n < D.N; ++n) {
     const int s = ragged ? 0 : cache->layer_len[n];
     Step st{};
@@ -840,9 +841,21 @@ int score_run(const Dims &D, const onetrans_block_weights *blk, const onetrans_k
     st.need_out = true;
     st.stats_in = stats;
     st.stats_out = n + 1 == D.N ? nullptr : (void *)(w + L.st[n & 1]);
+    // the NS rows are every row of the next block and all of its query rows: each is handed over
+    // and kept as a residual
+    bool wrote = false;
+    st.xh_in = handed ? w + L.xh : nullptr;
+    if (L.has_xh && n + 1 < D.N) {
+      st.xh_out = w + L.xh;
+      st.xh_gamma = blk[n + 1].norm1_g;
+      st.xh_beta = blk[n + 1].norm1_b;
+      st.xh_keep = 0;
+      st.xh_written = &wrote;
+    }
     if ((rc = run_step(D, blk[n], st, w, L, stream))) return rc;
     x = RowView{w + L.x[n & 1], (long long)ns * d, 0, d};
     stats = st.stats_out;
+    handed = wrote;
     x_f32 = 1;
   }
   return ONETRANS_OK;
@@ -1682,7 +1695,7 @@ size_t onetrans_workspace_bytes(const onetrans_config *cfg, int op, int n_seq, i
   const int parts = ws_parts_for(n_seq, op == ONETRANS_OP_FORWARD ? FORWARD_PART_MIN : USER_PART_MIN);
   const size_t per = op == ONETRANS_OP_SCORE ? (size_t)n_cand : 1;   // sequences per user
   return ws_layout(D, (size_t)((n_seq + parts - 1) / parts) * per, tin, rq, kv, (size_t)n_seq * per,
-                   op == ONETRANS_OP_FORWARD).total * parts;
+                   op == ONETRANS_OP_FORWARD || op == ONETRANS_OP_SCORE).total * parts;
 }
 
 size_t onetrans_backward_workspace_bytes(const onetrans_config *cfg, int batch, int l_s) {
@@ -1808,15 +1821,16 @@ int onetrans_score_candidates(const onetrans_config *cfg, const onetrans_block_w
   if (misaligned(ws)) return ONETRANS_ERR_ALIGNMENT;
   if (!ws) return ONETRANS_ERR_INVALID_ARG;
   const size_t n_call = (size_t)n_users * n_cand;
-  if (ws_bytes < ws_layout(D, (size_t)((n_users + wp - 1) / wp) * n_cand, tin, rq, kv, n_call).total * wp)
+  if (ws_bytes < ws_layout(D, (size_t)((n_users + wp - 1) / wp) * n_cand, tin, rq, kv, n_call, true).total * wp)
     return ONETRANS_ERR_WORKSPACE;
-  const size_t part_bytes = ws_layout(D, (size_t)((n_users + parts - 1) / parts) * n_cand, tin, rq, kv, n_call).total;
+  const size_t part_bytes =
+      ws_layout(D, (size_t)((n_users + parts - 1) / parts) * n_cand, tin, rq, kv, n_call, true).total;
   const size_t in_user = (size_t)n_cand * D.lns * D.d * D.esz, out_user = (size_t)n_cand * D.lns * D.d * 4;
   return over_streams(n_users, parts, stream, [&](int first, int count, int part, hipStream_t st) {
     const onetrans_kv_cache view = user_view(D, cache, first);
     return score_run(D, blk, &view, (const char *)x_ns + first * in_user, count, n_cand,
                      (char *)out_ns + first * out_user, (char *)ws + part * part_bytes,
-                     ws_layout(D, (size_t)count * n_cand, tin, rq, kv, n_call), st);
+                     ws_layout(D, (size_t)count * n_cand, tin, rq, kv, n_call, true), st);
   });
 }
 
@@ -1830,7 +1844,7 @@ int onetrans_score_candidates_noalloc(const onetrans_config *cfg, const onetrans
   size_t n, tin, rq;
   bool kv;
   ws_dims(cfg, D, ONETRANS_OP_SCORE, n_users, 0, n_cand, 0, n, tin, rq, kv);
-  const Ws L = ws_layout(D, n, tin, rq, kv, n);
+  const Ws L = ws_layout(D, n, tin, rq, kv, n, true);
   if (L.total > (size_t)ONETRANS_SCRATCH_BYTES) return ONETRANS_ERR_SCRATCH;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return ONETRANS_ERR_HIP;
