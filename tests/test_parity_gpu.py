@@ -195,6 +195,21 @@ def test_forward_normalised_row_handoff(key):
     _forward_case(w, samples=c["samples"])
 
 
+@pytest.mark.parametrize("d,n_cand", [(128, 130), (256, 65)])
+def test_score_normalised_row_handoff(d, n_cand):
+    """Stage II calls above the split-post bound (4 users x n_cand candidates x 16 NS rows), so each
+    block's post launch hands the next block its normalised NS rows; bf16 LayerNorm, every
+    candidate against the oracle."""
+    lns = 16
+    assert 4 * n_cand * lns * 8 * d * 4 > 32 << 20, "the call must be too large for split post launches"
+    base = synth.workload("onetrans_s")
+    m = replace(base.model, name=f"score_handoff_{d}", n_blocks=3, d_model=d, n_heads=d // 32, d_ff=4 * d,
+                norm="layer", norm_eps=1e-5, dtype="bf16", weight_seed=1400 + d)
+    w = replace(synth.test_workload("tiny3_two_stage"), model=m, l_s=150, s_queries=(150, 90, 20),
+                seq_lens=(49, 49, 49), n_users=4, n_cand=n_cand, input_seed=2140 + d, key=f"score_handoff_{d}")
+    _two_stage_case(w)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_ragged_users_prefill_append_score(dtype):
     """Users with different cached lengths in one call (cache.user_len): padded prefill, append
