@@ -195,18 +195,20 @@ def test_forward_normalised_row_handoff(key):
     _forward_case(w, samples=c["samples"])
 
 
-@pytest.mark.parametrize("d,n_cand", [(128, 130), (256, 65)])
-def test_score_normalised_row_handoff(d, n_cand):
-    """Stage II calls above the split-post bound (4 users x n_cand candidates x 16 NS rows), so each
-    block's post launch hands the next block its normalised NS rows; bf16 LayerNorm, every
-    candidate against the oracle."""
-    lns = 16
-    assert 4 * n_cand * lns * 8 * d * 4 > 32 << 20, "the call must be too large for split post launches"
+@pytest.mark.parametrize("d,n_users", [(128, 40), (256, 20)])
+def test_two_stage_normalised_row_handoff(d, n_users):
+    """Stage I (n_users x 220 rows) and Stage II (n_users x 13 candidates x 16 NS rows) calls above
+    the split-post bound, so each block's post launch hands the next block its normalised rows in
+    both stages; bf16 LayerNorm with a pyramid, every user's cache and candidate against the oracle."""
+    lns, l_s, n_cand = 16, 220, 13
+    for rows in (n_users * l_s, n_users * n_cand * lns):
+        assert rows * 8 * d * 4 > 32 << 20, "the calls must be too large for split post launches"
     base = synth.workload("onetrans_s")
-    m = replace(base.model, name=f"score_handoff_{d}", n_blocks=3, d_model=d, n_heads=d // 32, d_ff=4 * d,
+    m = replace(base.model, name=f"two_stage_handoff_{d}", n_blocks=3, d_model=d, n_heads=d // 32, d_ff=4 * d,
                 norm="layer", norm_eps=1e-5, dtype="bf16", weight_seed=1400 + d)
-    w = replace(synth.test_workload("tiny3_two_stage"), model=m, l_s=150, s_queries=(150, 90, 20),
-                seq_lens=(49, 49, 49), n_users=4, n_cand=n_cand, input_seed=2140 + d, key=f"score_handoff_{d}")
+    w = replace(synth.test_workload("tiny3_two_stage"), model=m, l_s=l_s, s_queries=(l_s, 130, 20),
+                seq_lens=(72, 72, 73), n_users=n_users, n_cand=n_cand, input_seed=2140 + d,
+                key=f"two_stage_handoff_{d}")
     _two_stage_case(w)
 
 

@@ -969,6 +969,7 @@ int stack_run(const Dims &D, const onetrans_block_weights *blk, RowView x, int x
   int rc;
   const int d = D.d;
   void *stats = nullptr;   // (mean, rstd) rows of x when the previous block wrote them
+  bool handed = false;     // the previous block's post launch wrote x's normalised rows to L.xh
   for (int n = n0; n < D.N; ++n) {
     const bool last = n + 1 == D.N;
     const bool to_tail = n == tail_block && !last;
@@ -1002,10 +1003,23 @@ int stack_run(const Dims &D, const onetrans_block_weights *blk, RowView x, int x
     st.need_out = !last || out != nullptr;
     st.stats_in = stats;
     st.stats_out = last || to_tail ? nullptr : (void *)(w + L.st[n & 1]);
+    // normalised-row handoff to the next block; rows that go to x_tail are all kept (the caller's
+    // buffer), otherwise the rows before the next block's first query row are not stored
+    bool wrote = false;
+    st.xh_in = handed ? w + L.xh : nullptr;
+    if (L.has_xh && !last) {
+      const int q_next = n + 2 == D.N ? q_final : q_of[n + 1];
+      st.xh_out = w + L.xh;
+      st.xh_gamma = blk[n + 1].norm1_g;
+      st.xh_beta = blk[n + 1].norm1_b;
+      st.xh_keep = to_tail ? 0 : q - q_next;
+      st.xh_written = &wrote;
+    }
     if ((rc = run_step(D, blk[n], st, w, L, stream))) return rc;
     // the next block's row t is this block's position p0 + t
     x = to_tail ? tail_rows(D, cache, -p0) : RowView{w + L.x[n & 1], (long long)q * d, 0, d};
     stats = st.stats_out;
+    handed = wrote;
     x_f32 = 1;
     s = q;
   }
@@ -1694,8 +1708,8 @@ size_t onetrans_workspace_bytes(const onetrans_config *cfg, int op, int n_seq, i
   if ((op == ONETRANS_OP_FORWARD || op == ONETRANS_OP_PREFILL) && check_schedule(cfg, l_s)) return 0;
   const int parts = ws_parts_for(n_seq, op == ONETRANS_OP_FORWARD ? FORWARD_PART_MIN : USER_PART_MIN);
   const size_t per = op == ONETRANS_OP_SCORE ? (size_t)n_cand : 1;   // sequences per user
-  return ws_layout(D, (size_t)((n_seq + parts - 1) / parts) * per, tin, rq, kv, (size_t)n_seq * per,
-                   op == ONETRANS_OP_FORWARD || op == ONETRANS_OP_SCORE).total * parts;
+  return ws_layout(D, (size_t)((n_seq + parts - 1) / parts) * per, tin, rq, kv, (size_t)n_seq * per, true).total *
+         parts;
 }
 
 size_t onetrans_backward_workspace_bytes(const onetrans_config *cfg, int batch, int l_s) {
@@ -1785,8 +1799,9 @@ int onetrans_prefill_user(const onetrans_config *cfg, const onetrans_block_weigh
   const int wp = ws_parts_for(n_users, USER_PART_MIN), parts = parts_for(n_users, USER_PART_MIN);
   if (misaligned(ws)) return ONETRANS_ERR_ALIGNMENT;
   if (!ws) return ONETRANS_ERR_INVALID_ARG;
-  if (ws_bytes < ws_layout(D, (n_users + wp - 1) / wp, tin, rq, kv, n_users).total * wp) return ONETRANS_ERR_WORKSPACE;
-  const size_t part_bytes = ws_layout(D, (n_users + parts - 1) / parts, tin, rq, kv, n_users).total;
+  if (ws_bytes < ws_layout(D, (n_users + wp - 1) / wp, tin, rq, kv, n_users, true).total * wp)
+    return ONETRANS_ERR_WORKSPACE;
+  const size_t part_bytes = ws_layout(D, (n_users + parts - 1) / parts, tin, rq, kv, n_users, true).total;
   const size_t in_user = (size_t)l_s * D.d * D.esz, out_user = (size_t)cfg->s_queries[D.N - 1] * D.d * 4;
   // the first pruning block's kept rows go to x_tail too (when a later block exists to read them)
   const int n_star = first_pruning_block(cfg->s_queries, D.N, l_s);
@@ -1796,7 +1811,7 @@ int onetrans_prefill_user(const onetrans_config *cfg, const onetrans_block_weigh
     RowView x{const_cast<char *>((const char *)x_s + first * in_user), (long long)l_s * D.d, 0, D.d};
     return stack_run(D, blk, x, D.dt == ONETRANS_F32, l_s, count, &view, 0, cfg->s_queries, cfg->s_queries[D.N - 1],
                      tail_block, out_s ? (char *)out_s + first * out_user : nullptr, (char *)ws + part * part_bytes,
-                     ws_layout(D, count, tin, rq, kv, n_users), st);
+                     ws_layout(D, count, tin, rq, kv, n_users, true), st);
   });
   if (rc) return rc;
   int s = l_s;
@@ -1903,7 +1918,8 @@ int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weig
   const int wp = ws_parts_for(n_users, USER_PART_MIN), parts = parts_for(n_users, USER_PART_MIN);
   if (misaligned(ws)) return ONETRANS_ERR_ALIGNMENT;
   if (!ws) return ONETRANS_ERR_INVALID_ARG;
-  if (ws_bytes < ws_layout(D, (n_users + wp - 1) / wp, tin, rq, kv, n_users).total * wp) return ONETRANS_ERR_WORKSPACE;
+  if (ws_bytes < ws_layout(D, (n_users + wp - 1) / wp, tin, rq, kv, n_users, true).total * wp)
+    return ONETRANS_ERR_WORKSPACE;
   const int l_old = ragged ? 0 : cache->layer_len[0];
   const int l_new = l_old + d_l;
   // the last block's kept rows after the append: it grows with the sequence unless it prunes
@@ -1915,12 +1931,12 @@ int onetrans_append_events(const onetrans_config *cfg, const onetrans_block_weig
   std::vector<int> q_of(D.N);
   for (int b = 0; b + 1 < D.N; ++b) q_of[b] = cache->layer_len[b + 1];
   q_of[D.N - 1] = q_last;
-  const size_t part_bytes = ws_layout(D, (n_users + parts - 1) / parts, tin, rq, kv, n_users).total;
+  const size_t part_bytes = ws_layout(D, (n_users + parts - 1) / parts, tin, rq, kv, n_users, true).total;
   const size_t in_user = (size_t)d_l * D.d * D.esz, out_user = (size_t)q_final * D.d * 4;
   rc = over_streams(n_users, parts, stream, [&](int first, int count, int part, hipStream_t st) {
     const onetrans_kv_cache view = user_view(D, cache, first);
     char *w = (char *)ws + part * part_bytes;
-    const Ws Lp = ws_layout(D, count, tin, rq, kv, n_users);
+    const Ws Lp = ws_layout(D, count, tin, rq, kv, n_users, true);
     void *out = out_new ? (char *)out_new + first * out_user : nullptr;
     int r = append_run(D, blk, &view, (const char *)x_new + first * in_user, count, d_l, out, w, Lp, l_old, n_head,
                        q_final, st);
