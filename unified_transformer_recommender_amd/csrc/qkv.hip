@@ -148,11 +148,16 @@ __global__ __launch_bounds__(QKV_NW * 64, (qkv_wgs_per_cu<T, D>())) void qkv_ker
   };
   issue(c0);
 
-  for (int i = tid; i < D; i += NW * 64) {
-    s_gm[i] = to_f32(((const T *)a.gamma)[i]);
-    s_bt[i] = LAYER ? to_f32(((const T *)a.beta)[i]) : 0.0f;
+  // handed-over rows are normalised already: no norm parameters to stage, and their loads go out
+  // right behind the first chunk's
+  const bool from_xh = BF && a.xh != nullptr;
+  if (!from_xh) {
+    for (int i = tid; i < D; i += NW * 64) {
+      s_gm[i] = to_f32(((const T *)a.gamma)[i]);
+      s_bt[i] = LAYER ? to_f32(((const T *)a.beta)[i]) : 0.0f;
+    }
+    __syncthreads();                             // gamma / beta staged
   }
-  __syncthreads();                               // gamma / beta staged
 
   // ---- norm1 of this lane's tokens -> bf16 B fragments (k = 16 kc + 8 g + e) -----------------
   // A lane holds half of its token's row (the other half sits in lane +- 32). For bf16 storage at
@@ -167,7 +172,7 @@ __global__ __launch_bounds__(QKV_NW * 64, (qkv_wgs_per_cu<T, D>())) void qkv_ker
     // rows normalised by the previous block's post-attention kernel, already in fragment order:
     // one contiguous 1 KB wave load per k-chunk. A row group wholly past the job's rows (the last
     // tile's spare waves) reads the job's last group instead; its results are never stored.
-    if (a.xh != nullptr) {
+    if (from_xh) {
       handed = true;
       const int last = ((M_rows + 31) >> 5) - 1;
 #pragma unroll
@@ -293,7 +298,16 @@ __global__ __launch_bounds__(QKV_NW * 64, (qkv_wgs_per_cu<T, D>())) void qkv_ker
   // every wave has also finished reading chunk i - 1, so its slot takes chunk i + 1.
   T *trash = (T *)a.trash;
   for (int i = c0; i < c1; ++i) {
-    if (i == c0) wait_vm<0>();
+    // first chunk: its loads are done; with handed-over rows their TG * KC loads, issued after
+    // the chunk's, may still be in flight (the MFMAs wait for each fragment as they use it)
+    if (i == c0) {
+      if constexpr (BF) {
+        if (from_xh) wait_vm<TG * KC>();
+        else wait_vm<0>();
+      } else {
+        wait_vm<0>();
+      }
+    }
     else wait_vm<NS>();
     wait_lgkm0();
     bare_barrier();
