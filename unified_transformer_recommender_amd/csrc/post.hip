@@ -21,6 +21,11 @@
 // few MFMAs ahead of their use. Rows are stored unpadded with their 16-byte pieces XOR-swizzled so
 // that 16 lanes reading 16 consecutive rows touch 16 distinct bank groups.
 //
+// Epilogue: X' rows (fp32) through a per-wave LDS staging tile, the (mean, rstd) of each row for
+// the next block's norm 1, and, where the launch hands over, that norm's output in bf16 as the next
+// QKV launch's B fragments (xh_piece order); X' rows the next block reads only through those
+// fragments are then not stored.
+//
 // Occupancy: for bf16 at d < 256, and at d = 256 with RMSNorm, the kernel is held to 256 registers
 // per lane so that two workgroups share a CU. Each hidden chunk then runs plainly in order
 // (up-projection, GELU, down-projection): the other workgroup's MFMAs fill this one's VALU phases,

@@ -6,7 +6,9 @@
 // each lane owns one token of each of its wave's token groups (two groups of 32 for bf16 at
 // d <= 256: every weight fragment read from LDS then feeds two MFMAs). A lane loads its token's
 // input row, forms the norm statistics with one cross-half shuffle (or reads them from the
-// previous block's post kernel), and keeps the normalised row as bf16 B fragments in registers.
+// previous block's post kernel), and keeps the normalised row as bf16 B fragments in registers;
+// where the previous block's post kernel handed the normalised rows over (bf16, xh_piece order),
+// the lane loads those fragments instead, one contiguous 1 KB wave load per k-chunk.
 // The projection weights stream through LDS in chunks of 32 output features x d (direct
 // global->LDS loads by all four waves, XOR-swizzled rows, double-buffered): with d_head = 32 a
 // chunk is exactly one head, and each accumulator tile is written into the head-major Q/K/V (or
