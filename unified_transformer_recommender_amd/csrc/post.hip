@@ -204,21 +204,51 @@ __global__ __launch_bounds__((post_nw<T, D>() * 64), (post_wgs_per_cu<T, D, LAYE
 #pragma unroll
   for (int i = 0; i < NB - 1; ++i) issue(i);
 
+  // Per-feature vectors into LDS. Every thread's loads are issued together and waited for once (a
+  // plain strided loop waits for each 2-byte load before the next: one memory round trip per
+  // element, in front of the first chunk).
   float *s_gm = svec, *s_bt = svec + D, *s_b2 = svec + 2 * D, *s_b1 = svec + 3 * D;
-  for (int i = tid; i < 3 * D + 32 * NC; i += NW * 64) {
-    float v;
-    if (i < D) v = to_f32(((const T *)a.gamma)[i]);
-    else if (i < 2 * D) v = LAYER ? to_f32(((const T *)a.beta)[i - D]) : 0.0f;
-    else if (i < 3 * D) v = to_f32(b2[i - 2 * D]);
-    else v = to_f32(b1[i - 3 * D]);
-    svec[i] = v;
-  }
   const bool hand = BF && !SPLIT && a.xh != nullptr;
-  if (hand)
-    for (int i = tid; i < D; i += NW * 64) {
-      s_xg[i] = to_f32(((const T *)a.xh_gamma)[i]);
-      s_xb[i] = LAYER ? to_f32(((const T *)a.xh_beta)[i]) : 0.0f;
+  {
+    constexpr int NT = NW * 64;
+    constexpr int SV = (3 * D + POST_MAX_DFF + NT - 1) / NT;   // svec elements per thread, at most
+    constexpr int XV = (D + NT - 1) / NT;                      // next-block norm elements per thread
+    const int nsv = 3 * D + 32 * NC;
+    float sv[SV], xg[XV], xb[XV];
+    // every load is issued (elements without a source read gamma[0] and are discarded), so no
+    // branch separates them
+    const T *const g0 = (const T *)a.gamma;
+#pragma unroll
+    for (int k = 0; k < SV; ++k) {
+      const int i = tid + k * NT;
+      const T *src = g0;
+      bool use = true;
+      if (i < D) src = g0 + i;
+      else if (i < 2 * D) { if (LAYER) src = (const T *)a.beta + (i - D); else use = false; }
+      else if (i < 3 * D) src = b2 + (i - 2 * D);
+      else if (i < nsv) src = b1 + (i - 3 * D);
+      else use = false;
+      const float v = to_f32(*src);
+      sv[k] = use ? v : 0.0f;
     }
+#pragma unroll
+    for (int k = 0; k < XV; ++k) {
+      const int i = min(tid + k * NT, D - 1);
+      const float vg = to_f32(*(hand ? (const T *)a.xh_gamma + i : g0));
+      const float vb = to_f32(*(hand && LAYER ? (const T *)a.xh_beta + i : g0));
+      xg[k] = vg;
+      xb[k] = LAYER ? vb : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < SV; ++k)
+      if (tid + k * NT < nsv) svec[tid + k * NT] = sv[k];
+#pragma unroll
+    for (int k = 0; k < XV; ++k)
+      if (hand && tid + k * NT < D) {
+        s_xg[tid + k * NT] = xg[k];
+        s_xb[tid + k * NT] = xb[k];
+      }
+  }
 
   frag ofr[KC];
   {

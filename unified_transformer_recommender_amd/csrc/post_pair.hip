@@ -182,14 +182,31 @@ __global__ __launch_bounds__(2 * PairCfg<D>::NP * 64, PairCfg<D>::WAVES_PER_SIMD
   // prologue: start the weight stream, then the per-token loads
   issue(0);
 
+  // Per-feature vectors into LDS: every thread's loads issued together and waited for once
+  // (elements without a source read gamma[0] and are discarded, so no branch separates the loads).
   float *s_gm = svec, *s_bt = svec + D, *s_b2 = svec + 2 * D, *s_b1 = svec + 3 * D;
-  for (int i = tid; i < 3 * D + DFF; i += NW * 64) {
-    float v;
-    if (i < D) v = to_f32(((const T *)a.gamma)[i]);
-    else if (i < 2 * D) v = LAYER ? to_f32(((const T *)a.beta)[i - D]) : 0.0f;
-    else if (i < 3 * D) v = to_f32(b2[i - 2 * D]);
-    else v = to_f32(b1[i - 3 * D]);
-    svec[i] = v;
+  {
+    constexpr int NT = NW * 64;
+    constexpr int SV = (3 * D + POST_MAX_DFF + NT - 1) / NT;
+    const int nsv = 3 * D + DFF;
+    const T *const g0 = (const T *)a.gamma;
+    float sv[SV];
+#pragma unroll
+    for (int k = 0; k < SV; ++k) {
+      const int i = tid + k * NT;
+      const T *src = g0;
+      bool use = true;
+      if (i < D) src = g0 + i;
+      else if (i < 2 * D) { if (LAYER) src = (const T *)a.beta + (i - D); else use = false; }
+      else if (i < 3 * D) src = b2 + (i - 2 * D);
+      else if (i < nsv) src = b1 + (i - 3 * D);
+      else use = false;
+      const float v = to_f32(*src);
+      sv[k] = use ? v : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < SV; ++k)
+      if (tid + k * NT < nsv) svec[tid + k * NT] = sv[k];
   }
 
   // O rows of this lane's tokens; the B fragments of W^O chunk i are O[k = 32 i + 16 kk + 8 g ..]
