@@ -212,6 +212,35 @@ def test_two_stage_normalised_row_handoff(d, n_users):
     _two_stage_case(w)
 
 
+def test_ragged_score_normalised_row_handoff():
+    """Stage II over ragged cached users (each user's keys end at its own length) in a call above
+    the split-post bound (4 users x 130 candidates x 16 NS rows at d = 128), so the normalised NS
+    rows are handed over between blocks; bf16 LayerNorm, every candidate against the oracle run on
+    that user's own rows."""
+    d, lns, n_cand, cap = 128, 16, 130, 150
+    assert 4 * n_cand * lns * 8 * d * 4 > 32 << 20, "the call must be too large for split post launches"
+    base = synth.workload("onetrans_s")
+    m = replace(base.model, name="ragged_score_handoff", n_blocks=3, d_model=d, n_heads=d // 32, d_ff=4 * d,
+                norm="layer", norm_eps=1e-5, dtype="bf16", weight_seed=1611)
+    w = replace(synth.test_workload("tiny3_two_stage"), model=m, l_s=cap, s_queries=(cap,) * 3,
+                seq_lens=(49, 49, 49), n_users=4, n_cand=n_cand, input_seed=2171, key="ragged_score_handoff")
+    ws = weights(m)
+    lens = [150, 3, 97, 41]
+    say(f"[ragged score handoff] lens={lens} candidates={n_cand}")
+    mdl = model(w)
+    xs = synth.user_sequences(w)                # rows past a user's length pad
+    xn = synth.candidate_batch(w)
+    cache = ob.KVCache(mdl, w.n_users, cap, user_len=lens)
+    ob.onetrans_prefill_user(mdl, dev(xs, mdl), cache)
+    sc = ob.onetrans_score_candidates(mdl, cache, dev(xn, mdl))
+    torch.cuda.synchronize()
+    for u, n in enumerate(lens):
+        rc, _ = O.prefill_user(xs[u, :n], ws, m, (n,) * m.n_blocks)
+        e = max(rel_err(sc[u, c].cpu().numpy(), O.score_candidate(rc, xn[u, c], ws, m)) for c in range(n_cand))
+        say(f"  user {u} (L {n}): worst candidate {e:.3e}")
+        assert e <= TOL["bf16"], (u, e)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_ragged_users_prefill_append_score(dtype):
     """Users with different cached lengths in one call (cache.user_len): padded prefill, append
