@@ -177,6 +177,11 @@ _HANDOFF_CASES = {
                      samples=(0, 18)),
     "d64_layer": dict(d=64, norm="layer", batch=37, l_s=460, sq=(460, 250, 3), seq=(150, 150, 157),
                       samples=(0, 20, 36)),
+    # d = 512: the wave-pair post kernel hands over, each half of a pair its own 16 k-chunks
+    "d512_layer": dict(d=512, norm="layer", batch=11, l_s=211, sq=(211, 150, 7), seq=(69, 69, 70),
+                       samples=(0, 10)),
+    "d512_rms": dict(d=512, norm="rms", batch=11, l_s=211, sq=(211, 150, 7), seq=(69, 69, 70),
+                     samples=(0, 10)),
 }
 
 

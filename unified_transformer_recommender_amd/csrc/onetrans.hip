@@ -146,8 +146,9 @@ struct Ws {
 };
 
 // Block chains that hand each block's normalised input from the previous block's post-attention
-// kernel to its QKV kernel: bf16 storage at the widths the single-wave post kernel serves.
-inline bool handoff_dims(const Dims &D) { return D.dt == ONETRANS_BF16 && D.d <= 256; }
+// kernel to its QKV kernel: bf16 storage (the single-wave post kernel at d <= 256, the wave-pair
+// kernel at d = 512).
+inline bool handoff_dims(const Dims &D) { return D.dt == ONETRANS_BF16; }
 
 inline size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
 

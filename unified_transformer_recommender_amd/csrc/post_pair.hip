@@ -82,6 +82,8 @@ __global__ __launch_bounds__(2 * PairCfg<D>::NP * 64, PairCfg<D>::WAVES_PER_SIMD
   __shared__ float nx[NW][G][32];
   // gamma, beta, b2 [d] and b1 [d_ff] of this parameter set, fp32
   __shared__ __attribute__((aligned(16))) float svec[3 * D + POST_MAX_DFF];
+  // the next block's norm-1 gamma / beta, fp32, when this launch hands over normalised rows
+  __shared__ __attribute__((aligned(16))) float s_xg[D], s_xb[D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lc = lane & 31;
@@ -208,6 +210,12 @@ __global__ __launch_bounds__(2 * PairCfg<D>::NP * 64, PairCfg<D>::WAVES_PER_SIMD
     for (int k = 0; k < SV; ++k)
       if (tid + k * NT < nsv) svec[tid + k * NT] = sv[k];
   }
+  const bool hand = a.xh != nullptr;
+  if (hand)
+    for (int i = tid; i < D; i += NW * 64) {   // D / (NW * 64) = 1 at d = 512
+      s_xg[i] = to_f32(((const T *)a.xh_gamma)[i]);
+      s_xb[i] = LAYER ? to_f32(((const T *)a.xh_beta)[i]) : 0.0f;
+    }
 
   // O rows of this lane's tokens; the B fragments of W^O chunk i are O[k = 32 i + 16 kk + 8 g ..]
   const T *orow[G];
@@ -390,8 +398,9 @@ __global__ __launch_bounds__(2 * PairCfg<D>::NP * 64, PairCfg<D>::WAVES_PER_SIMD
     }
   }
 
-  // ---- statistics of X' for the next block's norm 1 (exact two-pass over the pair's halves) ----
-  if (a.stats.base != nullptr) {
+  // ---- statistics of X' for the next block's norm 1 (exact two-pass over the pair's halves), and
+  // that norm's output in the next QKV launch's fragment order (this half's 16 k-chunks) -------
+  if (a.stats.base != nullptr || hand) {
     float mean[G], ss[G];
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) mean[gi] = 0.0f;
@@ -422,13 +431,36 @@ __global__ __launch_bounds__(2 * PairCfg<D>::NP * 64, PairCfg<D>::WAVES_PER_SIMD
       ss[gi] = s;
     }
     pair_sum(ss);
-    if (hf == 0 && g == 0) {
+    float rstd[G];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) rstd[gi] = 1.0f / sqrtf(ss[gi] * (1.0f / D) + a.eps);
+    if (a.stats.base != nullptr && hf == 0 && g == 0) {
 #pragma unroll
       for (int gi = 0; gi < G; ++gi) {
         if (!valid[gi]) continue;
         float *sp = (float *)a.stats.base + tb[gi] * a.stats.sb + (long long)(tt[gi] - a.stats.t_off) * a.stats.rs;
         sp[0] = mean[gi];
-        sp[1] = 1.0f / sqrtf(ss[gi] * (1.0f / D) + a.eps);
+        sp[1] = rstd[gi];
+      }
+    }
+    if (hand) {
+      // the same arithmetic as the QKV kernel's norm of a stored X' row; k-chunk hf * HD / 16 + 2 ti + h
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        u32x4 *dst = (u32x4 *)a.xh + xh_piece(jb.xh_g0, grp, M_rows, (tm * NP + pair) * G + gi, D / 16, 0, lane);
+#pragma unroll
+        for (int ti = 0; ti < HT; ++ti)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            frag fr;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int f = hf * HD + 32 * ti + acc_row(8 * h + e, g);
+              fr[e] = (bf16)((acc[gi][ti][8 * h + e] - mean[gi]) * rstd[gi] * s_xg[f] + s_xb[f]);
+            }
+            const u32x4 piece = __builtin_bit_cast(u32x4, natural_kfrag2(fr));
+            if (valid[gi]) st16(dst + (hf * (HD / 16) + 2 * ti + h) * 64, piece);
+          }
       }
     }
   }
@@ -449,7 +481,7 @@ __global__ __launch_bounds__(2 * PairCfg<D>::NP * 64, PairCfg<D>::WAVES_PER_SIMD
       for (int k = 0; k < TS::NI; ++k) {
         const int tok = TS::token(k, lane);
         const int b = __shfl(tb[gi], tok, 64), t = __shfl(tt[gi], tok, 64);
-        rv[k] = __shfl((int)valid[gi], tok, 64) != 0;
+        rv[k] = __shfl((int)valid[gi], tok, 64) != 0 && t - a.out.t_off >= a.out_from;
         rowp[k] = (float *)a.out.base + b * a.out.sb + (long long)(t - a.out.t_off) * a.out.rs + hf * HD +
                   TS::feature(lane);
       }
