@@ -185,8 +185,8 @@ int onetrans_score_candidates(const onetrans_config *cfg, const onetrans_block_w
  * recorded for it).
  *   Size limit: the call needs the workspace of one part, at most
  *   onetrans_workspace_bytes(cfg, ONETRANS_OP_SCORE, n_users, 0, n_cand, 0) bytes (about
- *   72 KiB per candidate at d = 256 with 16 NS tokens, 128 KiB at d = 512): up to 903 candidates
- *   per call at d = 256 with 16 NS tokens. A larger call returns ONETRANS_ERR_SCRATCH before anything is enqueued.
+ *   72 KiB per candidate at d = 256 with 16 NS tokens, 144 KiB at d = 512): up to 903 candidates
+ *   per call at d = 256 with 16 NS tokens, 450 at d = 512. A larger call returns ONETRANS_ERR_SCRATCH before anything is enqueued.
  *   Sharing: every call on one GPU uses that GPU's one array. Each call writes every scratch byte
  *   it reads before reading it (nothing has to start at zero), but calls that overlap in time on
  *   one GPU (two streams, two host threads) race on the array; order them on one stream.
